@@ -1,0 +1,223 @@
+/*
+ * kvq.h — C ABI of libkvq: pair-norm-selected mixed-precision key-cache
+ * quantization, per-token value quantization and single-token decode
+ * attention over the quantized cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the method (web pages; cited by title and section):
+ *   [PN-Mix]  "PN-Mix: Pair-Norm Guided Mixed-Precision Key Cache Quantization
+ *             for Efficient Long-Output LLM Inference" — abstract; podcast
+ *             transcript.  Saliency of a RoPE channel pair is the product of
+ *             the query pair norm and the key pair norm; the salient pairs are
+ *             chosen once at prefill, reused for all of decoding, and stored
+ *             at a higher precision than the remaining low-bit key channels.
+ *   [PM-KVQ]  pith.science review of "PM-KVQ" — supporting_citations (KIVI):
+ *             keys quantized per channel, values per token, with a window of
+ *             recent tokens kept at 16 bits; key_machinery: the cache is kept
+ *             at 16 bits first and shrunk later.
+ *   [MixKVQ]  "MixKVQ: Query-Aware Mixed-Precision KV Cache Quantization for
+ *             Long-Context Reasoning" — abstract and AI summary: per-token
+ *             low-bit value quantization; channel-level mixed precision.
+ *   [SemKV]   "SemKV: Semantic Mixed-Precision KV Cache Quantization ..." —
+ *             abstract: an affine (scale + zero point) quantizer.
+ *   [Dual-QK] "Dual-QK: Sharp Queries and Flat Keys for Prunable 2-bit KV
+ *             Caches" — abstract: decode cost is dominated by key/value
+ *             reads, which low-bit storage reduces.
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless marked (host).  Every device
+ *     pointer must be 16-byte aligned (else KVQ_EALIGN).
+ *   - A call validates its arguments on the host first; a validation error
+ *     returns before anything is enqueued and leaves every buffer untouched.
+ *   - A call enqueues kernels on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream) and returns without synchronizing, except
+ *     kvq_check.  No call allocates or frees memory.  A failed launch returns
+ *     KVQ_EHIP.
+ *   - All memory is owned by the caller.  The library keeps no state besides
+ *     its loaded code objects; calls on different caches may run concurrently.
+ *   - 16-bit inputs (KVQ_FP16 or KVQ_BF16, `io_dtype`) are contiguous,
+ *     row-major, last dimension = channel.  Inputs must be finite with
+ *     |x| <= 32752 (so that every scale below stays finite).
+ *
+ * Shapes: B = batch, Hq = query heads, Hkv = KV heads, G = Hq / Hkv (query
+ * heads sharing one KV head; 1 <= G <= 16), D = head_dim = 128, 64 RoPE pairs.
+ * Pair j owns channels j and j + 64 (rotate-half RoPE pairing).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvq_status;
+enum {
+  KVQ_OK = 0,
+  KVQ_EINVAL = -1,    /* bad size, null pointer or inconsistent layout */
+  KVQ_ENOTSUP = -2,   /* a valid but unimplemented layout option */
+  KVQ_EALIGN = -3,    /* a device pointer is not 16-byte aligned */
+  KVQ_ECAPACITY = -4, /* T exceeds max_tokens, or workspace too small */
+  KVQ_EHIP = -5       /* the HIP runtime reported an error */
+};
+enum { KVQ_FP16 = 0, KVQ_BF16 = 1 };
+
+/* Host struct, read only.  Fixes the shape and the bit allocation. */
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim; /* head_dim must be 128 */
+  int32_t group;       /* 32: token group of a key channel, channel group of
+                          a value token */
+  int32_t n_pairs_hi;  /* salient pairs, 0..8 (ranks 0 .. n_pairs_hi-1) */
+  int32_t bits_hi;     /* 4 (4-bit codes) or 16 (raw 16-bit values) */
+  int32_t n_pairs_lo1; /* pairs stored at 1 bit; must be 0 in this version */
+  int32_t bits_lo;     /* 2: bits of every non-salient key channel */
+  int32_t bits_v;      /* 2: bits of every value */
+  int32_t residual;    /* R: recent tokens kept at 16 bits; multiple of 32,
+                          32 <= R */
+  int32_t max_tokens;  /* capacity per sequence, 1 <= max_tokens <= 2^20 */
+  int32_t io_dtype;    /* KVQ_FP16 | KVQ_BF16 */
+} kvq_layout;
+
+/* Device buffers of one cache, all caller-allocated with the sizes returned
+ * by kvq_cache_sizes, index order as listed there.
+ *
+ * Let RS = R + 32 (ring slots), NG = max(0, max_tokens - R) / 32 (capacity in
+ * quantized groups).  With T tokens held, n_q(T) = 32 * floor(max(0, T-R)/32)
+ * tokens are quantized (groups 0 .. n_q/32 - 1, positions [32g, 32g+32)) and
+ * the n_r = T - n_q most recent tokens (R <= n_r <= R + 31 once T >= R) sit
+ * in the ring at slot = position mod RS.
+ *
+ * Token order inside a group record ("tile order"): record index
+ * e = 16*T + r (T in {0,1}, r in 0..15) holds token 8*(r/4) + 4*T + r%4.
+ * Position swap pi(c) = (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1).
+ * A 2-bit code at position p occupies bits [2p, 2p+2) of a little-endian
+ * 32-bit word (of a 16-bit half-word for v_codes).
+ *
+ *  k_lo    [B][Hkv][NG][256] u32: word ((T*4 + kq)*16 + r)*2 + u holds,
+ *          for the token at tile index 16T + r, channels 16w .. 16w+15 with
+ *          w = 2kq + u, channel 16w + c at position pi(c).  The stored digit
+ *          is the 2-bit code of a 2-bit channel, the low two bits of the code
+ *          of a 4-bit channel, and 0 for a 16-bit channel.
+ *  k_hi    bits_hi == 4: [B][Hkv][NG][32] u32: word 16T + r (token at tile
+ *          index 16T+r) holds the high two bits (code >> 2) of the d-th
+ *          salient channel (ascending channel order, d < 2*n_pairs_hi) at
+ *          position pi(d).  bits_hi == 16: [B][Hkv][NG][32][2*n_pairs_hi]
+ *          16-bit raw values, tile order, salient channels ascending.
+ *          Zero bytes when n_pairs_hi == 0.
+ *  k_meta  [B][Hkv][NG][2][128] fp16: scale s[c] then zero z[c] per channel,
+ *          natural channel order; 0 for 16-bit channels.
+ *  v_codes [B][Hkv][NG][256] u32: word (j*4 + kq)*16 + c holds channel
+ *          32j + c in bits 0..15 and channel 32j + 16 + c in bits 16..31;
+ *          token 8*kq + i of the group at position pi(i) of that half.
+ *  v_meta  [B][Hkv][NG][2][4][32] fp16: scale s[j][t] then zero z[j][t] of
+ *          channel group j (channels 32j .. 32j+31) of token t.
+ *  ring_k  [B][Hkv][RS][128] io dtype, slot-major.
+ *  ring_v  [B][Hkv][RS/32][128][32] io dtype: slot block, channel, slot%32.
+ *  pairs   [B][Hkv][64] int32: pair id at each saliency rank (rank 0 first).
+ *  len     [B][Hkv] int32: tokens held (T).
+ *  sums    [B][Hkv][2][64] uint64: fixed-point saliency sums per pair id,
+ *          [0] query side, [1] key side (see kvq_select_pairs).
+ *  err     [1] int32: sticky error word, 0 = none; bit 0 = an append found
+ *          the cache full.
+ */
+typedef struct {
+  void *k_lo, *k_hi, *k_meta, *v_codes, *v_meta, *ring_k, *ring_v;
+  int32_t *pairs;
+  int32_t *len;
+  uint64_t *sums;
+  int32_t *err;
+} kvq_cache;
+
+#define KVQ_NBUF 11
+
+/* Bytes of each cache buffer, in kvq_cache field order (host only, no GPU).
+ * Returns KVQ_EINVAL / KVQ_ENOTSUP for a layout the library rejects. */
+kvq_status kvq_cache_sizes(const kvq_layout *L, size_t sizes[KVQ_NBUF] /*host*/);
+
+/* Workspace bytes kvq_decode_attn needs for `n_splits` token splits per
+ * (sequence, KV head): B*Hq*n_splits*130 floats of partial results. */
+kvq_status kvq_workspace_bytes(const kvq_layout *L, int32_t n_splits,
+                               size_t *bytes /*host*/);
+
+/* Pair selection, once per sequence at prefill ([PN-Mix] abstract and
+ * transcript: score = query pair norm x key pair norm; chosen once at
+ * prefill).  Per (b, kv head) and pair j, with norms in fp32
+ * n = sqrt(a*a + b*b) of the pair's two channel values (IEEE, correctly
+ * rounded) and u(n) = floor(n * 2^24) as an unsigned 64-bit integer:
+ *   sums[0][j] = sum over the G query heads of the KV head and the n_qry
+ *                selection queries of u(|q^(j)|),
+ *   sums[1][j] = sum over the T prefill keys of u(|k^(j)|),
+ *   S_j = (double)sums[0][j] * (double)sums[1][j].
+ * S_j is the product of the query-side and key-side norm sums, which ranks
+ * pairs exactly like the mean of |q^(j)| |k^(j)| over all query/key
+ * combinations.  pairs[] = pair ids by descending S_j, ties to the lower id.
+ *   q_sel [B][Hq][n_qry][128] post-RoPE selection queries, 1 <= n_qry <= 1024
+ *   k     [B][Hkv][T][128]   post-RoPE prefill keys, 1 <= T <= max_tokens
+ * Writes cache->sums and cache->pairs only. */
+kvq_status kvq_select_pairs(const kvq_layout *L, const void *q_sel,
+                            int32_t n_qry, const void *k, int32_t T,
+                            kvq_cache *cache, void *stream);
+
+/* Key quantization at prefill ([PN-Mix] abstract: salient pairs at higher
+ * precision; [PM-KVQ] supporting_citations: keys per channel; [SemKV]
+ * abstract: affine quantizer).  Requires cache->pairs from kvq_select_pairs.
+ * For each group of 32 tokens and each channel at b bits (L = 2^b - 1),
+ * values x_0..x_31 widened exactly to fp32:
+ *   z = fp16(min x);  s = fp16(fp32(max x - z) / L)   (IEEE fp32, RNE)
+ *   s == 0: every code 0; else r = 1.0f / s and
+ *   code_i = clamp(rint((x_i - z) * r), 0, L)  (fp32, ties to even)
+ * Channels of the n_pairs_hi top-ranked pairs use bits_hi, others bits_lo.
+ * Fills groups [0, n_q(T)/32), copies positions [n_q(T), T) into ring_k and
+ * sets len[b][h] = T.   k: [B][Hkv][T][128], 1 <= T <= max_tokens. */
+kvq_status kvq_quant_keys(const kvq_layout *L, const void *k, int32_t T,
+                          kvq_cache *cache, void *stream);
+
+/* Value quantization at prefill ([MixKVQ] abstract, [PM-KVQ]
+ * supporting_citations: per-token values).  Same quantizer as the keys over
+ * each token's channel groups [32j, 32j+32) at bits_v bits.  Fills groups
+ * [0, n_q(T)/32), copies positions [n_q(T), T) into ring_v, sets len = T. */
+kvq_status kvq_quant_values(const kvq_layout *L, const void *v, int32_t T,
+                            kvq_cache *cache, void *stream);
+
+/* One decode-step append ([PM-KVQ] key_machinery and supporting_citations:
+ * new tokens are held at 16 bits first and quantized later).  Per (b, kv
+ * head): T = len; if T == max_tokens, sets err bit 0 and changes nothing.
+ * Otherwise writes k_new/v_new to ring slot T mod RS, sets len = T + 1, and
+ * when n_q(T+1) > n_q(T) quantizes the group of positions [n_q(T),
+ * n_q(T)+32) from the ring exactly as kvq_quant_keys / kvq_quant_values
+ * would, with the prefill pair ranking.
+ *   k_new, v_new: [B][Hkv][128] io dtype. */
+kvq_status kvq_append(const kvq_layout *L, const void *k_new,
+                      const void *v_new, kvq_cache *cache, void *stream);
+
+/* Single-token decode attention over the quantized cache ([Dual-QK]
+ * abstract and [PN-Mix] abstract: decode reads the low-bit cache).  For
+ * each query head h of KV head h/G:
+ *   logit_t = sm_scale * sum_c q[h][c] * k^[t][c],  o = softmax(logit) . v^
+ * over all T tokens, where k^, v^ are the dequantized codes z + s*code for
+ * quantized tokens and channels and the raw 16-bit values for ring tokens
+ * and 16-bit channels.  The token axis is cut into n_splits ranges per
+ * (b, kv head) (1 <= n_splits <= 1024), each reduced with an online softmax;
+ * a log-sum-exp combine merges them.  Computation is fp32 with fp16 matrix
+ * operands.
+ *   q   [B][Hq][128] io dtype;  out [B][Hq][128] io dtype
+ *   workspace: >= kvq_workspace_bytes(L, n_splits) bytes, else
+ *   KVQ_ECAPACITY. */
+kvq_status kvq_decode_attn(const kvq_layout *L, const void *q,
+                           const kvq_cache *cache, float sm_scale,
+                           int32_t n_splits, void *workspace, size_t ws_bytes,
+                           void *out, void *stream);
+
+/* Synchronizes `stream`, then copies cache->err to *host_err (tests and
+ * debugging only). */
+kvq_status kvq_check(const kvq_cache *cache, int32_t *host_err /*host*/,
+                     void *stream);
+
+/* Static text for a status code. */
+const char *kvq_status_str(kvq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,213 @@
+"""CPU oracle of the quantized-KV decode path (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the GPU library
+(``decode_attention_select_amd``) and neither imports the other; both read
+their inputs from ``kvq_synth``.
+
+The arithmetic lives in ``kvq_oracle.c`` (plain loops, IEEE fp32/fp64, built
+with ``-O2 -ffp-contract=off``); this module builds it with gcc and wraps it
+with numpy.  ``oracle.brute`` holds independent brute-force checks used to pin
+the oracle itself.
+
+Pinned by (see tests/test_oracle_*.py): 16-bit conversions against numpy and
+torch casts over every bit pattern; the quantizer against nearest-level
+search, its error bound, min/max codes, idempotence and constant groups; the
+selection against an exhaustive mean over all query/key combinations, planted
+outliers, RoPE invariance and token-order invariance; packing against an
+independent bit-level unpacker; attention against textbook softmax attention
+(all-16-bit cache), T = 1, q = 0 and a brute-force pass over the dequantized
+cache.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+GS = 32
+D = 128
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (IEEE arithmetic, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
+                               "-ffp-contract=off", "-fno-fast-math",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        _lib = ctypes.CDLL(_LIB)
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _bf(io_dtype: str) -> int:
+    return 1 if io_dtype == "bf16" else 0
+
+
+def n_quant(T: int, R: int) -> int:
+    """Quantized tokens held when T tokens are cached with residual R."""
+    return int(_load().orc_n_quant(int(T), int(R)))
+
+
+def half_to_f64(bits) -> np.ndarray:
+    lib = _load()
+    lib.orc_half_to_f64.restype = ctypes.c_double
+    b = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.orc_half_to_f64(ctypes.c_uint16(int(x))) for x in b])
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    lib = _load()
+    lib.orc_bf16_to_f64.restype = ctypes.c_double
+    b = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.orc_bf16_to_f64(ctypes.c_uint16(int(x))) for x in b])
+
+
+def f32_to_half(x) -> np.ndarray:
+    lib = _load()
+    lib.orc_f32_to_half.restype = ctypes.c_uint16
+    lib.orc_f32_to_half.argtypes = [ctypes.c_float]
+    a = np.asarray(x, dtype=np.float32).ravel()
+    return np.array([lib.orc_f32_to_half(float(v)) for v in a], dtype=np.uint16)
+
+
+def quant_group(x, bits: int):
+    """Quantize one group of 32 values (fp32-exact) at `bits` bits.
+    Returns (codes uint8[32], s_bits, z_bits)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.shape == (GS,)
+    s = np.zeros(1, np.uint16)
+    z = np.zeros(1, np.uint16)
+    c = np.zeros(GS, np.uint8)
+    lib.orc_quant_group(_p(x), ctypes.c_int((1 << bits) - 1), _p(s), _p(z), _p(c))
+    return c, int(s[0]), int(z[0])
+
+
+def select(q_sel, k, T: int, n_kv_heads: int, io_dtype: str):
+    """Pair ranking.  q_sel [B][Hq][n_qry][128], k [B][Hkv][Tstride][128]
+    bits.  Returns (sums uint64 [B][Hkv][2][64], pairs int32 [B][Hkv][64])."""
+    q_sel = np.ascontiguousarray(q_sel, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    B, Hq, n_qry, _ = q_sel.shape
+    Hkv = n_kv_heads
+    sums = np.zeros((B, Hkv, 2, 64), np.uint64)
+    pairs = np.zeros((B, Hkv, 64), np.int32)
+    rc = _load().orc_select(B, Hq, Hkv, _bf(io_dtype), _p(q_sel), n_qry, _p(k),
+                            k.shape[2], int(T), _p(sums), _p(pairs))
+    assert rc == 0
+    return sums, pairs
+
+
+class Quantized:
+    """Logical (unpacked) quantized cache of the oracle."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def quantize(k, v, T: int, pairs, *, residual: int, n_pairs_hi: int,
+             bits_hi: int, io_dtype: str, ng: int | None = None) -> Quantized:
+    """Quantize keys and values of the first T tokens (k, v
+    [B][Hkv][Tstride][128] bits) with the given rank table."""
+    lib = _load()
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32)
+    B, Hkv, Tstride, _ = k.shape
+    nq = n_quant(T, residual)
+    NG = ng if ng is not None else max(nq // GS, 1)
+    kc = np.zeros((B, Hkv, NG, D, GS), np.uint8)
+    ks = np.zeros((B, Hkv, NG, D), np.uint16)
+    kz = np.zeros((B, Hkv, NG, D), np.uint16)
+    vc = np.zeros((B, Hkv, NG, GS, D), np.uint8)
+    vs = np.zeros((B, Hkv, NG, GS, 4), np.uint16)
+    vz = np.zeros((B, Hkv, NG, GS, 4), np.uint16)
+    rc = lib.orc_quant_keys(B, Hkv, _bf(io_dtype), _p(k), Tstride, int(T),
+                            int(residual), int(n_pairs_hi), int(bits_hi),
+                            _p(pairs), NG, _p(kc), _p(ks), _p(kz))
+    assert rc == 0
+    rc = lib.orc_quant_values(B, Hkv, _bf(io_dtype), _p(v), Tstride, int(T),
+                              int(residual), 2, NG, _p(vc), _p(vs), _p(vz))
+    assert rc == 0
+    return Quantized(k=k, v=v, T=int(T), R=int(residual), n_hi=int(n_pairs_hi),
+                     bits_hi=int(bits_hi), io_dtype=io_dtype, pairs=pairs,
+                     NG=NG, nq=nq, kcodes=kc, ks=ks, kz=kz, vcodes=vc, vs=vs,
+                     vz=vz)
+
+
+def attention(qz: Quantized, q, sm_scale: float, with_lse: bool = False):
+    """Decode attention over the oracle's quantized cache.  q [B][Hq][128]
+    bits.  Returns fp64 [B][Hq][128] (and lse [B][Hq] if asked)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    B, Hq, _ = q.shape
+    Hkv = qz.k.shape[1]
+    out = np.zeros((B, Hq, D), np.float64)
+    lse = np.zeros((B, Hq), np.float64)
+    rc = _load().orc_attention(
+        B, Hq, Hkv, _bf(qz.io_dtype), _p(q), _p(qz.k), _p(qz.v), qz.k.shape[2],
+        qz.T, qz.R, qz.n_hi, qz.bits_hi, _p(qz.pairs), qz.NG, _p(qz.kcodes),
+        _p(qz.ks), _p(qz.kz), _p(qz.vcodes), _p(qz.vs), _p(qz.vz),
+        ctypes.c_double(float(np.float32(sm_scale))), _p(out), _p(lse))
+    assert rc == 0
+    return (out, lse) if with_lse else out
+
+
+def k_hi_words(n_pairs_hi: int, bits_hi: int) -> int:
+    """Bytes of the salient-key section of one group record."""
+    if n_pairs_hi == 0:
+        return 0
+    return 128 if bits_hi == 4 else 32 * 2 * n_pairs_hi * 2
+
+
+def pack(qz: Quantized) -> dict:
+    """Byte records of the oracle's quantized cache (layout of include/kvq.h)
+    for groups [0, n_q/32); plus the live ring slots."""
+    lib = _load()
+    B, Hkv, Tstride, _ = qz.k.shape
+    NG = qz.NG
+    k_lo = np.zeros((B, Hkv, NG, 256), np.uint32)
+    k_hi = np.zeros((B, Hkv, NG, max(k_hi_words(qz.n_hi, qz.bits_hi), 1)), np.uint8)
+    k_meta = np.zeros((B, Hkv, NG, 256), np.uint16)
+    v_codes = np.zeros((B, Hkv, NG, 256), np.uint32)
+    v_meta = np.zeros((B, Hkv, NG, 256), np.uint16)
+    RS = qz.R + GS
+    ring_k = np.zeros((B, Hkv, RS, D), np.uint16)
+    ring_v = np.zeros((B, Hkv, RS // GS, D, GS), np.uint16)
+    lib.orc_pack_keys(B, Hkv, _p(qz.k), Tstride, qz.T, qz.R, qz.n_hi,
+                      qz.bits_hi, _p(qz.pairs), NG, _p(qz.kcodes), _p(qz.ks),
+                      _p(qz.kz), _p(k_lo), _p(k_hi), _p(k_meta))
+    lib.orc_pack_values(B, Hkv, qz.T, qz.R, NG, _p(qz.vcodes), _p(qz.vs),
+                        _p(qz.vz), _p(v_codes), _p(v_meta))
+    lib.orc_ring(B, Hkv, _p(qz.k), _p(qz.v), Tstride, qz.T, qz.R, _p(ring_k),
+                 _p(ring_v))
+    if k_hi_words(qz.n_hi, qz.bits_hi) == 0:
+        k_hi = k_hi[..., :0]
+    return dict(k_lo=k_lo, k_hi=k_hi, k_meta=k_meta, v_codes=v_codes,
+                v_meta=v_meta, ring_k=ring_k, ring_v=ring_v)
+
+
+def live_ring_slots(T: int, R: int) -> np.ndarray:
+    """Ring slots that hold tokens when T tokens are cached."""
+    RS = R + GS
+    return np.array([p % RS for p in range(n_quant(T, R), T)], dtype=np.int64)

@@ -1,0 +1,434 @@
+/*
+ * kvq_oracle.c — CPU oracle of the quantized-KV decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library.  It shares no code, header, table
+ * or helper with the GPU library and must never be used as a fallback for it.
+ *
+ * Plain loops, one step at a time, in the order the method states them:
+ *   - pair saliency (PN-Mix, abstract and transcript): per RoPE pair, the
+ *     query pair norm times the key pair norm, aggregated over the prefill
+ *     queries of the head group and the prefill keys; salient pairs chosen
+ *     once at prefill;
+ *   - mixed-precision keys (PN-Mix, abstract): salient pairs at a higher bit
+ *     width, the rest at 2 bits, per channel over groups of 32 tokens
+ *     (PM-KVQ review, supporting_citations: per-channel keys, per-token
+ *     values, recent tokens at 16 bits);
+ *   - affine quantizer with scale and zero point (SemKV, abstract);
+ *   - per-token 2-bit values (MixKVQ, abstract);
+ *   - decode attention: the textbook softmax(scale * q.k) . v over the
+ *     dequantized cache, unsplit, in fp64.
+ * Floating point follows IEEE binary32 / binary64 exactly (build with
+ * -ffp-contract=off, never -ffast-math).  16-bit conversions are written out
+ * here from the IEEE formats.
+ *
+ * Readings of points the pages leave open (each listed in the design notes):
+ *   saliency sums in fixed point u(n) = floor(n * 2^24) of fp32 norms;
+ *   z = fp16(min), s = fp16((max - z) / L), codes rint((x - z) * (1/s));
+ *   K groups = 32 tokens of one channel; V groups = 32 channels of one token;
+ *   n_q(T) = 32 * floor(max(0, T - R) / 32) quantized tokens, the rest raw.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define D 128
+#define NPAIR 64
+#define GS 32
+
+/* ---------------------------------------------------------------- 16-bit */
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double orc_half_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int f = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24); /* subnormal: f * 2^-24 */
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+  return sign ? -v : v;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+double orc_bf16_to_f64(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static double to_f64(uint16_t h, int bf16) {
+  return bf16 ? orc_bf16_to_f64(h) : orc_half_to_f64(h);
+}
+
+/* binary32 -> binary16, round to nearest, ties to even; overflow -> inf. */
+uint16_t orc_f32_to_half(float x) {
+  double a = fabs((double)x);
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return sign | 0x7e00;
+  if (a >= 65520.0) return sign | 0x7c00; /* rounds past the largest half */
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: integer multiple of 2^-24 (rint = ties to even) */
+    double m = rint(a * ldexp(1.0, 24));
+    return sign | (uint16_t)m; /* m == 1024 is the smallest normal */
+  }
+  int e;
+  frexp(a, &e); /* a = f * 2^e, f in [0.5, 1) -> a in [2^(e-1), 2^e) */
+  int ue = e - 1; /* a in [2^ue, 2^(ue+1)) */
+  double m = rint(ldexp(a, 10 - ue)); /* 11-bit significand in [1024, 2048] */
+  if (m == 2048.0) {
+    m = 1024.0;
+    ue += 1;
+  }
+  return sign | (uint16_t)(((ue + 15) << 10) | ((int)m - 1024));
+}
+
+/* ---------------------------------------------------------- pair saliency */
+
+/* Fixed-point pair norm: fp32 sqrt(a*a + b*b), scaled by 2^24, truncated. */
+static uint64_t norm_fixed(double a, double b) {
+  float af = (float)a, bf = (float)b;
+  float s = af * af + bf * bf;
+  float n = sqrtf(s);
+  return (uint64_t)floor((double)n * 16777216.0);
+}
+
+/* q_sel [B][Hq][n_qry][128], k [B][Hkv][Tstride][128] (first T used).
+ * sums [B][Hkv][2][64]: [0] query side, [1] key side.  pairs [B][Hkv][64]. */
+int orc_select(int B, int Hq, int Hkv, int bf16, const uint16_t *q_sel,
+               int n_qry, const uint16_t *k, int Tstride, int T,
+               uint64_t *sums, int32_t *pairs) {
+  if (Hq % Hkv) return -1;
+  int G = Hq / Hkv;
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++) {
+      uint64_t *qs = sums + ((size_t)(b * Hkv + kh) * 2 + 0) * NPAIR;
+      uint64_t *ks = sums + ((size_t)(b * Hkv + kh) * 2 + 1) * NPAIR;
+      for (int j = 0; j < NPAIR; j++) qs[j] = ks[j] = 0;
+      for (int g = 0; g < G; g++) {
+        int h = kh * G + g;
+        for (int t = 0; t < n_qry; t++) {
+          const uint16_t *row = q_sel + (((size_t)b * Hq + h) * n_qry + t) * D;
+          for (int j = 0; j < NPAIR; j++)
+            qs[j] += norm_fixed(to_f64(row[j], bf16), to_f64(row[j + NPAIR], bf16));
+        }
+      }
+      for (int t = 0; t < T; t++) {
+        const uint16_t *row = k + (((size_t)b * Hkv + kh) * Tstride + t) * D;
+        for (int j = 0; j < NPAIR; j++)
+          ks[j] += norm_fixed(to_f64(row[j], bf16), to_f64(row[j + NPAIR], bf16));
+      }
+      /* rank: descending score, ties to the lower pair id */
+      double S[NPAIR];
+      int used[NPAIR];
+      for (int j = 0; j < NPAIR; j++) {
+        S[j] = (double)qs[j] * (double)ks[j];
+        used[j] = 0;
+      }
+      int32_t *pr = pairs + (size_t)(b * Hkv + kh) * NPAIR;
+      for (int r = 0; r < NPAIR; r++) {
+        int best = -1;
+        for (int j = 0; j < NPAIR; j++)
+          if (!used[j] && (best < 0 || S[j] > S[best])) best = j;
+        used[best] = 1;
+        pr[r] = best;
+      }
+    }
+  return 0;
+}
+
+/* Bits of channel c given the rank table of its (b, kv head). */
+int orc_channel_bits(const int32_t *pr, int n_hi, int bits_hi, int bits_lo,
+                     int c) {
+  int j = c % NPAIR;
+  for (int r = 0; r < n_hi; r++)
+    if (pr[r] == j) return bits_hi;
+  return bits_lo;
+}
+
+/* ------------------------------------------------------------- quantizer */
+
+/* Affine min/max quantizer of one group of 32 values at L = 2^b - 1 levels.
+ * x are exact widenings of 16-bit inputs.  Writes fp16 bits of s and z. */
+void orc_quant_group(const float *x, int L, uint16_t *s_bits, uint16_t *z_bits,
+                     uint8_t *codes) {
+  float mn = x[0], mx = x[0];
+  for (int i = 1; i < GS; i++) {
+    if (x[i] < mn) mn = x[i];
+    if (x[i] > mx) mx = x[i];
+  }
+  uint16_t zb = orc_f32_to_half(mn);
+  float z = (float)orc_half_to_f64(zb);
+  float diff = mx - z;
+  uint16_t sb = 0;
+  if (diff > 0.0f) sb = orc_f32_to_half(diff / (float)L);
+  *z_bits = zb;
+  *s_bits = sb;
+  if (sb == 0) {
+    for (int i = 0; i < GS; i++) codes[i] = 0;
+    return;
+  }
+  float s = (float)orc_half_to_f64(sb);
+  float r = 1.0f / s;
+  for (int i = 0; i < GS; i++) {
+    float t = (x[i] - z) * r;
+    float q = rintf(t);
+    if (q < 0.0f) q = 0.0f;
+    if (q > (float)L) q = (float)L;
+    codes[i] = (uint8_t)q;
+  }
+}
+
+/* Quantized tokens for T held tokens and residual R. */
+int orc_n_quant(int T, int R) {
+  int over = T - R;
+  return over > 0 ? (over / GS) * GS : 0;
+}
+
+/* Keys.  k [B][Hkv][Tstride][128].  Outputs (logical, for NG group slots):
+ * codes [B][Hkv][NG][128][32] (channel, token), s/z [B][Hkv][NG][128] fp16
+ * bits.  16-bit channels get s = z = 0 and codes 0.  Fills groups
+ * [0, n_q(T)/32). */
+int orc_quant_keys(int B, int Hkv, int bf16, const uint16_t *k, int Tstride,
+                   int T, int R, int n_hi, int bits_hi, const int32_t *pairs,
+                   int NG, uint8_t *codes, uint16_t *s, uint16_t *z) {
+  int ng = orc_n_quant(T, R) / GS;
+  if (ng > NG) return -1;
+  float x[GS];
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++) {
+      const int32_t *pr = pairs + (size_t)(b * Hkv + kh) * NPAIR;
+      for (int g = 0; g < ng; g++)
+        for (int c = 0; c < D; c++) {
+          size_t slot = ((size_t)(b * Hkv + kh) * NG + g) * D + c;
+          int bits = orc_channel_bits(pr, n_hi, bits_hi, 2, c);
+          if (bits == 16) {
+            memset(codes + slot * GS, 0, GS);
+            s[slot] = z[slot] = 0;
+            continue;
+          }
+          for (int i = 0; i < GS; i++)
+            x[i] = (float)to_f64(k[(((size_t)b * Hkv + kh) * Tstride + g * GS + i) * D + c], bf16);
+          orc_quant_group(x, (1 << bits) - 1, s + slot, z + slot, codes + slot * GS);
+        }
+    }
+  return 0;
+}
+
+/* Values.  v [B][Hkv][Tstride][128].  codes [B][Hkv][NG][32][128] (token,
+ * channel), s/z [B][Hkv][NG][32][4] fp16 bits (token, channel group). */
+int orc_quant_values(int B, int Hkv, int bf16, const uint16_t *v, int Tstride,
+                     int T, int R, int bits_v, int NG, uint8_t *codes,
+                     uint16_t *s, uint16_t *z) {
+  int ng = orc_n_quant(T, R) / GS;
+  if (ng > NG) return -1;
+  float x[GS];
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++)
+      for (int g = 0; g < ng; g++)
+        for (int t = 0; t < GS; t++)
+          for (int j = 0; j < D / GS; j++) {
+            size_t tok = ((size_t)(b * Hkv + kh) * NG + g) * GS + t;
+            const uint16_t *row = v + (((size_t)b * Hkv + kh) * Tstride + g * GS + t) * D;
+            for (int i = 0; i < GS; i++) x[i] = (float)to_f64(row[j * GS + i], bf16);
+            orc_quant_group(x, (1 << bits_v) - 1, s + tok * 4 + j, z + tok * 4 + j,
+                            codes + tok * D + j * GS);
+          }
+  return 0;
+}
+
+/* ------------------------------------------------------------- attention */
+
+/* Decode attention, unsplit, fp64.  q [B][Hq][128] bits; k, v raw inputs
+ * [B][Hkv][Tstride][128] (used for ring tokens and 16-bit channels); the
+ * logical codes / metadata from orc_quant_keys / orc_quant_values.
+ * out [B][Hq][128] fp64.  Optional lse [B][Hq] (natural log of the softmax
+ * denominator of the scaled logits, for split checks). */
+int orc_attention(int B, int Hq, int Hkv, int bf16, const uint16_t *q,
+                  const uint16_t *k, const uint16_t *v, int Tstride, int T,
+                  int R, int n_hi, int bits_hi, const int32_t *pairs, int NG,
+                  const uint8_t *kcodes, const uint16_t *ks, const uint16_t *kz,
+                  const uint8_t *vcodes, const uint16_t *vs, const uint16_t *vz,
+                  double sm_scale, double *out, double *lse) {
+  if (Hq % Hkv) return -1;
+  int G = Hq / Hkv;
+  int nq = orc_n_quant(T, R);
+  double *logit = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+  double *kh_row = (double *)malloc(sizeof(double) * D);
+  if (!logit || !kh_row) return -2;
+  for (int b = 0; b < B; b++)
+    for (int h = 0; h < Hq; h++) {
+      int kh = h / G;
+      const int32_t *pr = pairs + (size_t)(b * Hkv + kh) * NPAIR;
+      double qv[D];
+      for (int c = 0; c < D; c++) qv[c] = to_f64(q[((size_t)b * Hq + h) * D + c], bf16);
+      /* logits */
+      double m = -INFINITY;
+      for (int t = 0; t < T; t++) {
+        const uint16_t *raw = k + (((size_t)b * Hkv + kh) * Tstride + t) * D;
+        for (int c = 0; c < D; c++) {
+          int bits = orc_channel_bits(pr, n_hi, bits_hi, 2, c);
+          if (t >= nq || bits == 16) {
+            kh_row[c] = to_f64(raw[c], bf16);
+          } else {
+            size_t slot = ((size_t)(b * Hkv + kh) * NG + t / GS) * D + c;
+            kh_row[c] = orc_half_to_f64(kz[slot]) +
+                        orc_half_to_f64(ks[slot]) * (double)kcodes[slot * GS + t % GS];
+          }
+        }
+        double acc = 0.0;
+        for (int c = 0; c < D; c++) acc += qv[c] * kh_row[c];
+        logit[t] = sm_scale * acc;
+        if (logit[t] > m) m = logit[t];
+      }
+      /* softmax-weighted values */
+      double l = 0.0, o[D];
+      for (int c = 0; c < D; c++) o[c] = 0.0;
+      for (int t = 0; t < T; t++) {
+        double p = exp(logit[t] - m);
+        l += p;
+        const uint16_t *raw = v + (((size_t)b * Hkv + kh) * Tstride + t) * D;
+        for (int c = 0; c < D; c++) {
+          double vv;
+          if (t >= nq) {
+            vv = to_f64(raw[c], bf16);
+          } else {
+            size_t tok = ((size_t)(b * Hkv + kh) * NG + t / GS) * GS + t % GS;
+            vv = orc_half_to_f64(vz[tok * 4 + c / GS]) +
+                 orc_half_to_f64(vs[tok * 4 + c / GS]) * (double)vcodes[tok * D + c];
+          }
+          o[c] += p * vv;
+        }
+      }
+      for (int c = 0; c < D; c++) out[((size_t)b * Hq + h) * D + c] = o[c] / l;
+      if (lse) lse[(size_t)b * Hq + h] = m + log(l);
+    }
+  free(logit);
+  free(kh_row);
+  return 0;
+}
+
+/* ------------------------------------------------------------ byte layout */
+
+/* Token of record index e = 16*T + r inside a group ("tile order"). */
+static int tile_token(int e) {
+  int T = e / 16, r = e % 16;
+  return 8 * (r / 4) + 4 * T + r % 4;
+}
+
+/* Position of element c inside its 4-aligned block: bits 0 and 1 swapped. */
+static int pos_swap(int c) { return (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1); }
+
+/* Packs the logical key codes of groups [0, ng) into the byte records.
+ * k_lo [..][NG][256] u32, k_hi (4-bit: [..][NG][32] u32; 16-bit:
+ * [..][NG][32][2*n_hi] u16 raw), k_meta [..][NG][2][128] u16. */
+int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
+                  int n_hi, int bits_hi, const int32_t *pairs, int NG,
+                  const uint8_t *codes, const uint16_t *s, const uint16_t *z,
+                  uint32_t *k_lo, void *k_hi, uint16_t *k_meta) {
+  int ng = orc_n_quant(T, R) / GS;
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++) {
+      const int32_t *pr = pairs + (size_t)(b * Hkv + kh) * NPAIR;
+      int hil[16], nh = 0; /* salient channels, ascending */
+      for (int c = 0; c < D; c++)
+        if (orc_channel_bits(pr, n_hi, bits_hi, 2, c) != 2) hil[nh++] = c;
+      for (int g = 0; g < ng; g++) {
+        size_t grp = (size_t)(b * Hkv + kh) * NG + g;
+        const uint8_t *cg = codes + grp * D * GS;
+        uint32_t *lo = k_lo + grp * 256;
+        memset(lo, 0, 256 * 4);
+        for (int e = 0; e < 32; e++) {
+          int t = tile_token(e), Tt = e / 16, r = e % 16;
+          for (int c = 0; c < D; c++) {
+            int w = c / 16, kq = w / 2, u = w % 2;
+            int bits = orc_channel_bits(pr, n_hi, bits_hi, 2, c);
+            uint32_t digit = bits == 16 ? 0u : (uint32_t)(cg[c * GS + t] & 3);
+            size_t word = ((size_t)(Tt * 4 + kq) * 16 + r) * 2 + u;
+            lo[word] |= digit << (2 * pos_swap(c % 16));
+          }
+        }
+        if (nh && bits_hi == 4) {
+          uint32_t *hi = (uint32_t *)k_hi + grp * 32;
+          memset(hi, 0, 32 * 4);
+          for (int e = 0; e < 32; e++) {
+            int t = tile_token(e);
+            for (int d = 0; d < nh; d++)
+              hi[e] |= (uint32_t)(cg[hil[d] * GS + t] >> 2) << (2 * pos_swap(d));
+          }
+        } else if (nh && bits_hi == 16) {
+          uint16_t *hi = (uint16_t *)k_hi + grp * 32 * nh;
+          for (int e = 0; e < 32; e++) {
+            int t = tile_token(e);
+            for (int d = 0; d < nh; d++)
+              hi[e * nh + d] = k[(((size_t)b * Hkv + kh) * Tstride + g * GS + t) * D + hil[d]];
+          }
+        }
+        uint16_t *meta = k_meta + grp * 256;
+        for (int c = 0; c < D; c++) {
+          meta[c] = s[grp * D + c];
+          meta[D + c] = z[grp * D + c];
+        }
+      }
+    }
+  return 0;
+}
+
+/* Packs the logical value codes: v_codes [..][NG][256] u32,
+ * v_meta [..][NG][2][4][32] u16. */
+int orc_pack_values(int B, int Hkv, int T, int R, int NG, const uint8_t *codes,
+                    const uint16_t *s, const uint16_t *z, uint32_t *v_codes,
+                    uint16_t *v_meta) {
+  int ng = orc_n_quant(T, R) / GS;
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++)
+      for (int g = 0; g < ng; g++) {
+        size_t grp = (size_t)(b * Hkv + kh) * NG + g;
+        const uint8_t *cg = codes + grp * GS * D; /* [token][channel] */
+        uint32_t *vc = v_codes + grp * 256;
+        memset(vc, 0, 256 * 4);
+        for (int j = 0; j < 4; j++)
+          for (int kq = 0; kq < 4; kq++)
+            for (int c = 0; c < 16; c++) {
+              uint32_t w = 0;
+              for (int i = 0; i < 8; i++) {
+                int t = 8 * kq + i;
+                w |= (uint32_t)cg[t * D + 32 * j + c] << (2 * pos_swap(i));
+                w |= (uint32_t)cg[t * D + 32 * j + 16 + c] << (16 + 2 * pos_swap(i));
+              }
+              vc[(j * 4 + kq) * 16 + c] = w;
+            }
+        uint16_t *meta = v_meta + grp * 256;
+        for (int j = 0; j < 4; j++)
+          for (int t = 0; t < GS; t++) {
+            meta[j * 32 + t] = s[(grp * GS + t) * 4 + j];
+            meta[128 + j * 32 + t] = z[(grp * GS + t) * 4 + j];
+          }
+      }
+  return 0;
+}
+
+/* Ring contents for positions [n_q(T), T): ring_k [..][RS][128],
+ * ring_v [..][RS/32][128][32]; other slots are left as they are. */
+int orc_ring(int B, int Hkv, const uint16_t *k, const uint16_t *v, int Tstride,
+             int T, int R, uint16_t *ring_k, uint16_t *ring_v) {
+  int RS = R + GS;
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++)
+      for (int p = orc_n_quant(T, R); p < T; p++) {
+        int slot = p % RS;
+        const size_t src = (((size_t)b * Hkv + kh) * Tstride + p) * D;
+        uint16_t *rk = ring_k + ((size_t)(b * Hkv + kh) * RS + slot) * D;
+        uint16_t *rv = ring_v + (size_t)(b * Hkv + kh) * RS * D;
+        for (int c = 0; c < D; c++) {
+          rk[c] = k[src + c];
+          rv[((size_t)(slot / GS) * D + c) * GS + slot % GS] = v[src + c];
+        }
+      }
+  return 0;
+}
