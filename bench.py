@@ -1,0 +1,194 @@
+"""Decode-step benchmark of the quantized-KV path on one MI355X.
+
+One step = one kvq_decode_attn call (split-K decode attention over the packed
+cache plus the split merge) for every query head of the workload, with the
+cache already resident in HBM.  Every timed step reads the next of N cache
+replicas (N * cache bytes >= 512 MiB) so that the 256 MB Infinity Cache cannot
+serve it.  The default workload is the Llama-3-8B-shaped GQA layer at 32K
+context (batch 1, 32 query / 8 KV heads, bf16, 6 salient pairs at 4 bits,
+residual 128).
+
+Prints one JSON line (rank 0, one GPU):
+  value = effective HBM GB/s = algorithmic bytes per step / step time.
+Algorithmic bytes per step: for every (sequence, KV head), the n_q quantized
+tokens at 35 B of key codes (6 pairs x 4 bits + 116 channels x 2 bits) +
+16 B key scale/zero + 32 B value codes + 16 B value scale/zero, the n_r ring
+tokens at 256 B key + 256 B value, plus the query and the output.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(w, T: int) -> int:
+    R = w.residual
+    nq = 32 * (max(0, T - R) // 32)
+    nr = T - nq
+    n_hi_ch = 2 * w.n_pairs_hi
+    if w.bits_hi == 16:
+        k_code_bits = n_hi_ch * 16 + (128 - n_hi_ch) * 2
+        k_meta = (128 - n_hi_ch) * 4 / 32
+    else:
+        k_code_bits = n_hi_ch * w.bits_hi + (128 - n_hi_ch) * 2
+        k_meta = 128 * 4 / 32
+    per_tok = k_code_bits / 8 + k_meta + 32 + 16
+    bh = w.batch * w.n_kv_heads
+    return int(round(bh * (nq * per_tok + nr * 512) + 2 * w.batch * w.n_q_heads * 128 * 2))
+
+
+def layout_bytes(cache, w, T: int) -> int:
+    """Bytes the packed layout actually holds for T tokens (read per step)."""
+    R = w.residual
+    nq = 32 * (max(0, T - R) // 32)
+    nr = T - nq
+    ng = nq // 32
+    bh = w.batch * w.n_kv_heads
+    khi = cache.sizes[1] // max(1, bh * cache_ng(cache, w))
+    per_grp = 1024 + khi + 512 + 1024 + 512
+    return bh * (ng * per_grp + nr * 512) + 2 * w.batch * w.n_q_heads * 128 * 2
+
+
+def cache_ng(cache, w):
+    return max(cache.layout.max_tokens - w.residual, 0) // 32
+
+
+def default_splits(w) -> int:
+    # about 4 waves per CU in flight: 256 CUs * 4 / (sequences * KV heads)
+    return max(1, min(1024, math.ceil(1024 / (w.batch * w.n_kv_heads))))
+
+
+def cpu_baseline(w, data, min_s: float = 10.0):
+    """The oracle's decode step (all query heads, unsplit fp64) timed on this
+    host, single thread, repeated until about `min_s` seconds have passed."""
+    import oracle
+    from tests._gpu_case import SM_SCALE
+    T = w.tokens
+    _, pairs = oracle.select(data["q_sel"], data["k"], T, w.n_kv_heads, w.io_dtype)
+    qz = oracle.quantize(data["k"], data["v"], T, pairs, residual=w.residual,
+                         n_pairs_hi=w.n_pairs_hi, bits_hi=w.bits_hi, io_dtype=w.io_dtype)
+    q = data["q_dec"][:, :, 0]
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attention(qz, q, SM_SCALE)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_s:
+            break
+    per_step_s = el / n
+    return {"value": round(per_step_s * 1e6, 1), "unit": "us/step", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d full decode steps (all %d query heads, %d tokens), fp64, 1 thread"
+                      % (n, w.batch * w.n_q_heads, T),
+            "gbs_equiv": round(algorithmic_bytes(w, T) / per_step_s / 1e9, 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3-8b-32k")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--replica-mib", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kvq_synth
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import SM_SCALE, dev
+
+    w = kvq_synth.workload(args.workload)
+    S = args.splits or w.n_splits or default_splits(w)
+    T = w.tokens
+    data = kvq_synth.generate(w)
+    layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads, n_pairs_hi=w.n_pairs_hi,
+                             bits_hi=w.bits_hi, residual=w.residual, max_tokens=T,
+                             io_dtype=w.io_dtype)
+    base = kvq.Cache(layout)
+    kvq.kvq_select_pairs(layout, dev(data["q_sel"]), w.n_qry, dev(data["k"][:, :, :T]), T,
+                         base.struct)
+    kvq.kvq_quant_keys(layout, dev(data["k"][:, :, :T]), T, base.struct)
+    kvq.kvq_quant_values(layout, dev(data["v"][:, :, :T]), T, base.struct)
+    torch.cuda.synchronize()
+
+    n_rep = max(1, math.ceil(args.replica_mib * 2 ** 20 / base.nbytes()))
+    replicas = [base]
+    for _ in range(n_rep - 1):
+        r = kvq.Cache.__new__(kvq.Cache)
+        r.layout, r.sizes = base.layout, base.sizes
+        r.bufs = {k: v.clone() for k, v in base.bufs.items()}
+        r.struct = kvq.kvq_cache(*[r.bufs[n].data_ptr() for n in kvq.BUF_NAMES])
+        replicas.append(r)
+    q = dev(data["q_dec"][:, :, 0])
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    ws = torch.empty(kvq.kvq_workspace_bytes(layout, S), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kvq.kvq_decode_attn(layout, q, replicas[i % n_rep].struct, SM_SCALE, S, ws, out,
+                            stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+
+    alg = algorithmic_bytes(w, T)
+    gbs = alg / (ev_ms * 1e-3) / 1e9
+    res = {
+        "metric": "quantized-KV decode attn: us/step, effective HBM GB/s, % of 8 TB/s peak",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ev_ms, 5),
+        "us_per_step": round(ev_ms * 1e3, 3),
+        "wall_ms_per_step": round(wall_ms, 5),
+        "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16-mfma/fp32-acc, bf16 io",
+        "data": "synthetic (seeded N(0,1) + outlier key pairs, RoPE)",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "context": T, "io_dtype": w.io_dtype,
+                   "salient_pairs": w.n_pairs_hi, "salient_bits": w.bits_hi,
+                   "residual": w.residual, "n_splits": S, "cache_replicas": n_rep},
+        "algorithmic_bytes_per_step": alg,
+        "layout_bytes_per_step": layout_bytes(base, w, T),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, data)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

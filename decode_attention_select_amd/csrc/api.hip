@@ -1,0 +1,184 @@
+// api.hip — the C ABI of libkvq (declared in include/kvq.h): argument
+// validation, buffer sizes and launch dispatch.  No call allocates or
+// synchronizes (except kvq_check).
+#include <string.h>
+
+#include "common.h"
+#include "internal.h"
+
+using namespace kvq;
+
+namespace {
+
+kvq_status check_layout(const kvq_layout* L) {
+  if (!L) return KVQ_EINVAL;
+  if (L->batch < 1 || L->n_q_heads < 1 || L->n_kv_heads < 1) return KVQ_EINVAL;
+  if (L->n_q_heads % L->n_kv_heads) return KVQ_EINVAL;
+  if (L->head_dim != D || L->group != GS) return KVQ_EINVAL;
+  if (L->n_q_heads / L->n_kv_heads > 16) return KVQ_ENOTSUP;
+  if (L->n_pairs_hi < 0 || L->n_pairs_hi > 8) return KVQ_EINVAL;
+  if (L->bits_hi != 4 && L->bits_hi != 16) return KVQ_ENOTSUP;
+  if (L->n_pairs_lo1 != 0) return KVQ_ENOTSUP;
+  if (L->bits_lo != 2 || L->bits_v != 2) return KVQ_ENOTSUP;
+  if (L->residual < GS || L->residual % GS) return KVQ_EINVAL;
+  if (L->max_tokens < 1 || L->max_tokens > (1 << 20)) return KVQ_EINVAL;
+  if (L->io_dtype != KVQ_FP16 && L->io_dtype != KVQ_BF16) return KVQ_EINVAL;
+  return KVQ_OK;
+}
+
+Geo make_geo(const kvq_layout* L) {
+  Geo g;
+  g.B = L->batch;
+  g.Hq = L->n_q_heads;
+  g.Hkv = L->n_kv_heads;
+  g.G = g.Hq / g.Hkv;
+  g.R = L->residual;
+  g.RS = g.R + GS;
+  g.NG = L->max_tokens > g.R ? (L->max_tokens - g.R) / GS : 0;
+  g.n_hi = L->n_pairs_hi;
+  g.bits_hi = L->bits_hi;
+  g.nh = 2 * g.n_hi;
+  g.bf16 = L->io_dtype == KVQ_BF16;
+  g.max_tokens = L->max_tokens;
+  g.khi_bytes = g.n_hi == 0 ? 0 : (g.bits_hi == 4 ? 32 * 4 : GS * g.nh * 2);
+  return g;
+}
+
+bool aligned(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+kvq_status check_ptr(const void* p) {
+  if (!p) return KVQ_EINVAL;
+  return aligned(p) ? KVQ_OK : KVQ_EALIGN;
+}
+
+kvq_status check_cache(const Geo& g, const kvq_cache* c, bool need_groups) {
+  if (!c) return KVQ_EINVAL;
+  const void* ptrs[] = {c->ring_k, c->ring_v, c->pairs, c->len, c->sums, c->err};
+  for (const void* p : ptrs)
+    if (kvq_status s = check_ptr(p)) return s;
+  if (need_groups && g.NG > 0) {
+    const void* gp[] = {c->k_lo, c->k_meta, c->v_codes, c->v_meta};
+    for (const void* p : gp)
+      if (kvq_status s = check_ptr(p)) return s;
+    if (g.khi_bytes)
+      if (kvq_status s = check_ptr(c->k_hi)) return s;
+  }
+  return KVQ_OK;
+}
+
+kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_cache_sizes(const kvq_layout* L, size_t sizes[KVQ_NBUF]) {
+  if (kvq_status s = check_layout(L)) return s;
+  if (!sizes) return KVQ_EINVAL;
+  const Geo g = make_geo(L);
+  const size_t bh = (size_t)g.B * g.Hkv, grp = bh * g.NG;
+  const size_t el = 2;  // bytes of a 16-bit value
+  sizes[0] = grp * GROUP_WORDS * 4;  // k_lo
+  sizes[1] = grp * g.khi_bytes;      // k_hi
+  sizes[2] = grp * 2 * D * 2;        // k_meta
+  sizes[3] = grp * GROUP_WORDS * 4;  // v_codes
+  sizes[4] = grp * 2 * D * 2;        // v_meta
+  sizes[5] = bh * g.RS * D * el;     // ring_k
+  sizes[6] = bh * g.RS * D * el;     // ring_v
+  sizes[7] = bh * NPAIR * 4;         // pairs
+  sizes[8] = bh * 4;                 // len
+  sizes[9] = bh * 2 * NPAIR * 8;     // sums
+  sizes[10] = 4;                     // err
+  return KVQ_OK;
+}
+
+kvq_status kvq_workspace_bytes(const kvq_layout* L, int32_t n_splits, size_t* bytes) {
+  if (kvq_status s = check_layout(L)) return s;
+  if (!bytes || n_splits < 1 || n_splits > 1024) return KVQ_EINVAL;
+  *bytes = (size_t)L->batch * L->n_q_heads * n_splits * (4 + D) * sizeof(float);
+  return KVQ_OK;
+}
+
+kvq_status kvq_select_pairs(const kvq_layout* L, const void* q_sel, int32_t n_qry, const void* k,
+                            int32_t T, kvq_cache* cache, void* stream) {
+  if (kvq_status s = check_layout(L)) return s;
+  const Geo g = make_geo(L);
+  if (n_qry < 1 || n_qry > 1024 || T < 1) return KVQ_EINVAL;
+  if (T > g.max_tokens) return KVQ_ECAPACITY;
+  if (kvq_status s = check_ptr(q_sel)) return s;
+  if (kvq_status s = check_ptr(k)) return s;
+  if (kvq_status s = check_cache(g, cache, false)) return s;
+  return hip_status(launch_select(g, q_sel, n_qry, k, T, cache, (hipStream_t)stream));
+}
+
+kvq_status kvq_quant_keys(const kvq_layout* L, const void* k, int32_t T, kvq_cache* cache,
+                          void* stream) {
+  if (kvq_status s = check_layout(L)) return s;
+  const Geo g = make_geo(L);
+  if (T < 1) return KVQ_EINVAL;
+  if (T > g.max_tokens) return KVQ_ECAPACITY;
+  if (kvq_status s = check_ptr(k)) return s;
+  if (kvq_status s = check_cache(g, cache, true)) return s;
+  return hip_status(launch_quant_keys(g, k, T, cache, (hipStream_t)stream));
+}
+
+kvq_status kvq_quant_values(const kvq_layout* L, const void* v, int32_t T, kvq_cache* cache,
+                            void* stream) {
+  if (kvq_status s = check_layout(L)) return s;
+  const Geo g = make_geo(L);
+  if (T < 1) return KVQ_EINVAL;
+  if (T > g.max_tokens) return KVQ_ECAPACITY;
+  if (kvq_status s = check_ptr(v)) return s;
+  if (kvq_status s = check_cache(g, cache, true)) return s;
+  return hip_status(launch_quant_values(g, v, T, cache, (hipStream_t)stream));
+}
+
+kvq_status kvq_append(const kvq_layout* L, const void* k_new, const void* v_new,
+                      kvq_cache* cache, void* stream) {
+  if (kvq_status s = check_layout(L)) return s;
+  const Geo g = make_geo(L);
+  if (kvq_status s = check_ptr(k_new)) return s;
+  if (kvq_status s = check_ptr(v_new)) return s;
+  if (kvq_status s = check_cache(g, cache, true)) return s;
+  return hip_status(launch_append(g, k_new, v_new, cache, (hipStream_t)stream));
+}
+
+kvq_status kvq_decode_attn(const kvq_layout* L, const void* q, const kvq_cache* cache,
+                           float sm_scale, int32_t n_splits, void* workspace, size_t ws_bytes,
+                           void* out, void* stream) {
+  if (kvq_status s = check_layout(L)) return s;
+  const Geo g = make_geo(L);
+  size_t need = 0;
+  if (kvq_status s = kvq_workspace_bytes(L, n_splits, &need)) return s;
+  if (ws_bytes < need) return KVQ_ECAPACITY;
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_EINVAL;
+  if (kvq_status s = check_ptr(q)) return s;
+  if (kvq_status s = check_ptr(out)) return s;
+  if (kvq_status s = check_ptr(workspace)) return s;
+  if (kvq_status s = check_cache(g, cache, true)) return s;
+  return hip_status(launch_decode(g, q, cache, sm_scale, n_splits, (float*)workspace, out,
+                                  (hipStream_t)stream));
+}
+
+kvq_status kvq_check(const kvq_cache* cache, int32_t* host_err, void* stream) {
+  if (!cache || !cache->err || !host_err) return KVQ_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return KVQ_EHIP;
+  if (hipMemcpy(host_err, cache->err, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return KVQ_EHIP;
+  return KVQ_OK;
+}
+
+const char* kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument";
+    case KVQ_ENOTSUP: return "unsupported layout option";
+    case KVQ_EALIGN: return "device pointer not 16-byte aligned";
+    case KVQ_ECAPACITY: return "capacity or workspace too small";
+    case KVQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

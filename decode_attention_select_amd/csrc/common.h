@@ -1,0 +1,100 @@
+// common.h — shared definitions of libkvq's HIP sources (gfx950 only).
+//
+// Byte layout of the cache (the contract with every caller) is documented in
+// include/kvq.h; the helpers below compute its indices.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int D = 128;     // head dim
+constexpr int NPAIR = 64;  // RoPE pairs: pair j = channels j, j + 64
+constexpr int GS = 32;     // group: 32 tokens (keys) or 32 channels (values)
+constexpr int GROUP_WORDS = 256;  // u32 words of k_lo / v_codes per group
+
+// Shape and bit allocation, resolved on the host and passed by value.
+struct Geo {
+  int B, Hq, Hkv, G;
+  int R, RS;           // residual tokens, ring slots (R + 32)
+  int NG;              // quantized-group capacity per (b, kv head)
+  int n_hi, bits_hi;   // salient pairs and their bits (4 or 16)
+  int nh;              // salient channels = 2 * n_hi
+  int bf16;            // io dtype is bfloat16
+  int max_tokens;
+  int khi_bytes;       // bytes of the salient section per group
+};
+
+// Quantized tokens for T held tokens: 32 * floor(max(0, T - R) / 32).
+__host__ __device__ inline int n_quant(int T, int R) {
+  int over = T - R;
+  return over > 0 ? (over / GS) * GS : 0;
+}
+
+// Record index e = 16*T + r inside a group holds token 8*(r/4) + 4*T + r%4.
+__host__ __device__ inline int tile_token(int e) {
+  int T = e >> 4, r = e & 15;
+  return 8 * (r >> 2) + 4 * T + (r & 3);
+}
+
+// Code position of element c: bits 0 and 1 of c exchanged.  With that order
+// the nibble split (w & 0x33333333, (w >> 2) & 0x33333333) of a word yields
+// adjacent element pairs in each byte.
+__host__ __device__ inline int pos_swap(int c) {
+  return (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1);
+}
+
+// 16-bit input -> fp32 (exact for both dtypes).
+__device__ inline float in_to_f32(uint16_t bits, int bf16) {
+  if (bf16) return __uint_as_float((uint32_t)bits << 16);
+  return (float)__builtin_bit_cast(_Float16, bits);
+}
+
+// fp32 -> fp16 bits, round to nearest even.
+__device__ inline uint16_t f32_to_half_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+__device__ inline float half_bits_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Affine min/max quantizer of one group of 32 values (exact fp32 widenings of
+// 16-bit inputs) at L = 2^b - 1 levels:
+//   z = fp16(min);  s = fp16((max - z) / L), 0 when max - z <= 0;
+//   code = clamp(rint((x - z) * (1/s)), 0, L), all 0 when s == 0.
+// Every step is one IEEE fp32 operation (correctly rounded division and
+// rint, ties to even), so results are bit-identical to any IEEE
+// implementation of the same steps.
+__device__ inline void quantize_group(const float (&x)[GS], int L,
+                                      uint16_t& s_bits, uint16_t& z_bits,
+                                      uint8_t (&codes)[GS]) {
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < GS; i++) {
+    mn = x[i] < mn ? x[i] : mn;
+    mx = x[i] > mx ? x[i] : mx;
+  }
+  z_bits = f32_to_half_bits(mn);
+  const float z = half_bits_to_f32(z_bits);
+  const float diff = __fsub_rn(mx, z);
+  s_bits = diff > 0.0f ? f32_to_half_bits(__fdiv_rn(diff, (float)L)) : (uint16_t)0;
+  if (s_bits == 0) {
+#pragma unroll
+    for (int i = 0; i < GS; i++) codes[i] = 0;
+    return;
+  }
+  const float r = __fdiv_rn(1.0f, half_bits_to_f32(s_bits));
+#pragma unroll
+  for (int i = 0; i < GS; i++) {
+    float q = rintf(__fmul_rn(__fsub_rn(x[i], z), r));
+    q = q < 0.0f ? 0.0f : q;
+    q = q > (float)L ? (float)L : q;
+    codes[i] = (uint8_t)q;
+  }
+}
+
+}  // namespace kvq

@@ -1,0 +1,17 @@
+// internal.h — launchers shared between libkvq's translation units.
+#pragma once
+
+#include "common.h"
+
+namespace kvq {
+
+hipError_t launch_select(const Geo& g, const void* q_sel, int n_qry, const void* k, int T,
+                         kvq_cache* c, hipStream_t st);
+hipError_t launch_quant_keys(const Geo& g, const void* k, int T, kvq_cache* c, hipStream_t st);
+hipError_t launch_quant_values(const Geo& g, const void* v, int T, kvq_cache* c, hipStream_t st);
+hipError_t launch_append(const Geo& g, const void* k_new, const void* v_new, kvq_cache* c,
+                         hipStream_t st);
+hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float sm_scale,
+                         int n_splits, float* partials, void* out, hipStream_t st);
+
+}  // namespace kvq

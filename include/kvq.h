@@ -136,7 +136,7 @@ typedef struct {
 kvq_status kvq_cache_sizes(const kvq_layout *L, size_t sizes[KVQ_NBUF] /*host*/);
 
 /* Workspace bytes kvq_decode_attn needs for `n_splits` token splits per
- * (sequence, KV head): B*Hq*n_splits*130 floats of partial results. */
+ * (sequence, KV head): B*Hq*n_splits*132 floats of partial results. */
 kvq_status kvq_workspace_bytes(const kvq_layout *L, int32_t n_splits,
                                size_t *bytes /*host*/);
 

@@ -1,0 +1,142 @@
+"""Shared set-up of GPU parity cases: one seeded workload run through the HIP
+library (via the C-ABI binding) and through the CPU oracle on the same data."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import kvq_synth
+import oracle
+from decode_attention_select_amd import kvq
+
+SM_SCALE = float(np.float32(1.0 / math.sqrt(128.0)))
+
+
+def dev(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bit array -> contiguous int16 tensor on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def host(t: torch.Tensor, dtype) -> np.ndarray:
+    return t.cpu().numpy().view(dtype)
+
+
+class Case:
+    """GPU cache after prefill of `T` tokens, and the oracle's view of it."""
+
+    def __init__(self, w: kvq_synth.Workload, T: int | None = None,
+                 max_tokens: int | None = None, data: dict | None = None):
+        self.w = w
+        self.T = w.tokens if T is None else T
+        self.d = kvq_synth.generate(w) if data is None else data
+        self.max_tokens = max_tokens or max(w.max_tokens, self.T)
+        self.layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads,
+                                      n_pairs_hi=w.n_pairs_hi, bits_hi=w.bits_hi,
+                                      residual=w.residual, max_tokens=self.max_tokens,
+                                      io_dtype=w.io_dtype)
+        self.cache = kvq.Cache(self.layout)
+        self.NG = max(self.max_tokens - w.residual, 0) // 32
+        # selection always looks at the workload's prefill (once, at prefill)
+        Tsel = w.tokens
+        self.k_sel = dev(self.d["k"][:, :, :Tsel])
+        self.q_sel = dev(self.d["q_sel"])
+        kvq.kvq_select_pairs(self.layout, self.q_sel, w.n_qry, self.k_sel, Tsel, self.cache.struct)
+        k = dev(self.d["k"][:, :, :self.T])
+        v = dev(self.d["v"][:, :, :self.T])
+        kvq.kvq_quant_keys(self.layout, k, self.T, self.cache.struct)
+        kvq.kvq_quant_values(self.layout, v, self.T, self.cache.struct)
+        torch.cuda.synchronize()
+
+    # ----------------------------------------------------------- oracle side
+    def oracle_select(self):
+        return oracle.select(self.d["q_sel"], self.d["k"], self.w.tokens,
+                             self.w.n_kv_heads, self.w.io_dtype)
+
+    def oracle_quant(self, T=None, pairs=None):
+        if pairs is None:
+            pairs = self.oracle_select()[1]
+        return oracle.quantize(self.d["k"], self.d["v"], self.T if T is None else T, pairs,
+                               residual=self.w.residual, n_pairs_hi=self.w.n_pairs_hi,
+                               bits_hi=self.w.bits_hi, io_dtype=self.w.io_dtype,
+                               ng=max(self.NG, 1))
+
+    # -------------------------------------------------------------- GPU side
+    def gpu_bytes(self) -> dict:
+        B, H, NG = self.w.batch, self.w.n_kv_heads, self.NG
+        c = self.cache
+        RS = self.w.residual + 32
+        out = {
+            "k_lo": host(c["k_lo"], np.uint32).reshape(B, H, NG, 256),
+            "k_hi": (host(c["k_hi"], np.uint8).reshape(B, H, NG, -1) if c.sizes[1]
+                     else np.zeros((B, H, NG, 0), np.uint8)),
+            "k_meta": host(c["k_meta"], np.uint16).reshape(B, H, NG, 256),
+            "v_codes": host(c["v_codes"], np.uint32).reshape(B, H, NG, 256),
+            "v_meta": host(c["v_meta"], np.uint16).reshape(B, H, NG, 256),
+            "ring_k": host(c["ring_k"], np.uint16).reshape(B, H, RS, 128),
+            "ring_v": host(c["ring_v"], np.uint16).reshape(B, H, RS // 32, 128, 32),
+            "pairs": host(c["pairs"], np.int32).reshape(B, H, 64),
+            "len": host(c["len"], np.int32).reshape(B, H),
+            "sums": host(c["sums"], np.uint64).reshape(B, H, 2, 64),
+        }
+        return out
+
+    def decode(self, q_bits: np.ndarray, n_splits: int, partials: bool = False):
+        """q_bits [B][Hq][128] -> GPU output widened to fp64; with `partials`
+        also the fp32 per-split records [B][Hq][S][132] (m, l, -, -, o[128])."""
+        ws = torch.empty(kvq.kvq_workspace_bytes(self.layout, n_splits), dtype=torch.uint8,
+                         device="cuda")
+        out = torch.empty((self.w.batch, self.w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+        kvq.kvq_decode_attn(self.layout, dev(q_bits), self.cache.struct, SM_SCALE, n_splits,
+                            ws, out)
+        torch.cuda.synchronize()
+        o = kvq_synth.bits_to_f64(host(out, np.uint16), self.w.io_dtype)
+        if not partials:
+            return o
+        part = host(ws, np.float32).reshape(self.w.batch, self.w.n_q_heads, n_splits, 132)
+        return o, part
+
+
+def half_ulp(x: np.ndarray, io_dtype: str) -> np.ndarray:
+    """Half a unit in the last place of the 16-bit output dtype at |x|: the
+    rounding error of storing an exact result in that dtype."""
+    mant = 7 if io_dtype == "bf16" else 10
+    emin = -126 if io_dtype == "bf16" else -14
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** emin)))
+    return 2.0 ** (e - mant - 1)
+
+
+def check_output(got, ref, io_dtype, atol):
+    """|got - ref| <= atol + half an output ulp, elementwise; returns the
+    largest excess of the arithmetic error over `atol` budget usage."""
+    err = np.abs(got - ref)
+    bound = atol + half_ulp(ref, io_dtype)
+    assert np.all(err <= bound), "max err %.3g (bound there %.3g)" % (
+        err.max(), bound.flat[np.argmax(err - bound)])
+    return float(err.max())
+
+
+def single_split_fp32(part: np.ndarray) -> np.ndarray:
+    """fp32 attention result from a one-split partial: o / l."""
+    assert part.shape[2] == 1
+    return part[:, :, 0, 4:].astype(np.float64) / part[:, :, 0, 1:2].astype(np.float64)
+
+
+def compare_cache(case: Case, qz, ng: int):
+    """Asserts the GPU cache bytes equal the oracle's packing for groups
+    [0, ng) and the live ring slots."""
+    g = case.gpu_bytes()
+    o = oracle.pack(qz)
+    for name in ("k_lo", "k_meta", "v_codes", "v_meta"):
+        a, b = g[name][:, :, :ng], o[name][:, :, :ng]
+        assert np.array_equal(a, b), "%s differs at %s" % (name, np.argwhere(a != b)[:5])
+    if o["k_hi"].shape[-1]:
+        a, b = g["k_hi"][:, :, :ng], o["k_hi"][:, :, :ng]
+        assert np.array_equal(a, b), "k_hi differs at %s" % np.argwhere(a != b)[:5]
+    slots = oracle.live_ring_slots(qz.T, qz.R)
+    assert np.array_equal(g["ring_k"][:, :, slots], o["ring_k"][:, :, slots])
+    rv_g = g["ring_v"].reshape(*g["ring_v"].shape[:2], -1, 128, 32)
+    for s in slots:
+        assert np.array_equal(rv_g[:, :, s // 32, :, s % 32], o["ring_v"][:, :, s // 32, :, s % 32])
+    assert np.all(g["len"] == qz.T)

@@ -1,0 +1,168 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on
+the same seeded inputs.  Indices, sums, codes, scales, zero points and ring
+bytes must match bit for bit; attention outputs within max-abs 2e-3 (the
+accuracy target for fp16/bf16 I/O with fp32 accumulation).  The bound is
+checked strictly on the fp32 result (one split: o / l straight from the
+workspace); the 16-bit output may differ from it by its own rounding, half an
+ulp of the output dtype, which alone exceeds 2e-3 in bf16 once |o| >= 0.5."""
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth
+import oracle
+from tests._gpu_case import SM_SCALE, Case, check_output, compare_cache, half_ulp, single_split_fp32
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+
+SMALL = [
+    kvq_synth.WORKLOADS[0],  # tiny: fp16, 8 pairs @4-bit, R = 32, T = 512
+    kvq_synth.Workload("gqa4-ragged", 2, 8, 2, 1000, n_qry=16, io_dtype="bf16",
+                       outliers="pct2x10", n_pairs_hi=6, residual=128, seed=21),
+    kvq_synth.Workload("raw16-salient", 1, 8, 2, 700, n_qry=8, io_dtype="bf16",
+                       n_pairs_hi=6, bits_hi=16, residual=64, seed=22),
+    kvq_synth.Workload("no-salient-g1", 1, 3, 3, 333, n_qry=8, io_dtype="fp16",
+                       n_pairs_hi=0, residual=32, seed=23),
+    kvq_synth.Workload("g16", 1, 16, 1, 300, n_qry=4, io_dtype="bf16",
+                       n_pairs_hi=8, residual=32, seed=24),
+]
+
+
+def _ids(w):
+    return w.name
+
+
+@pytest.mark.parametrize("w", SMALL, ids=_ids)
+def test_select_bit_exact(w):
+    case = Case(w)
+    sums, pairs = case.oracle_select()
+    g = case.gpu_bytes()
+    bad = np.argwhere(g["sums"] != sums)
+    if len(bad):
+        i = tuple(bad[0])
+        print("sums mismatch at %d places, first %s gpu %d oracle %d" % (
+            len(bad), i, g["sums"][i], sums[i]))
+    assert np.array_equal(g["sums"], sums)
+    assert np.array_equal(g["pairs"], pairs)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=_ids)
+def test_quant_bit_exact(w):
+    case = Case(w)
+    qz = case.oracle_quant()
+    assert qz.nq > 0
+    compare_cache(case, qz, qz.nq // 32)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=_ids)
+@pytest.mark.parametrize("n_splits", [1, 3, 64])
+def test_decode_matches_oracle(w, n_splits):
+    case = Case(w)
+    qz = case.oracle_quant()
+    q = case.d["q_dec"][:, :, 0]
+    ref = oracle.attention(qz, q, SM_SCALE)
+    got, part = case.decode(q, n_splits, partials=True)
+    err = check_output(got, ref, w.io_dtype, ATOL)
+    msg = "%s S=%d max|err| %.3g max|o| %.3g" % (w.name, n_splits, err, np.abs(ref).max())
+    if n_splits == 1:
+        e32 = np.max(np.abs(single_split_fp32(part) - ref))
+        msg += " fp32 max|err| %.3g" % e32
+        assert e32 <= ATOL
+    print(msg)
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 127, 160, 161, 193])
+def test_decode_edge_lengths(T):
+    # T < R (ring only), T = 1, and lengths either side of group boundaries
+    w = kvq_synth.Workload("edge", 1, 4, 1, 200, n_qry=8, io_dtype="bf16", n_pairs_hi=6,
+                           residual=128, seed=30)
+    case = Case(w, T=T)
+    qz = case.oracle_quant()
+    if qz.nq:
+        compare_cache(case, qz, qz.nq // 32)
+    q = case.d["q_dec"][:, :, 0]
+    ref = oracle.attention(qz, q, SM_SCALE)
+    for S in (1, 5):
+        got, part = case.decode(q, S, partials=True)
+        check_output(got, ref, w.io_dtype, ATOL)
+        if S == 1:
+            assert np.max(np.abs(single_split_fp32(part) - ref)) <= ATOL
+
+
+def test_all_sixteen_bit_mode_matches_textbook():
+    # residual window over every token: the kernel reproduces plain attention
+    w = kvq_synth.Workload("hp", 1, 8, 2, 250, n_qry=8, io_dtype="bf16", residual=256, seed=31)
+    case = Case(w)
+    q = case.d["q_dec"][:, :, 0]
+    out, part = case.decode(q, 1, partials=True)
+    out32 = single_split_fp32(part)
+    qf = kvq_synth.bits_to_f64(q, "bf16")
+    K = kvq_synth.bits_to_f64(case.d["k"][:, :, :250], "bf16")
+    V = kvq_synth.bits_to_f64(case.d["v"][:, :, :250], "bf16")
+    for h in range(8):
+        lg = SM_SCALE * (K[0, h // 4] @ qf[0, h])
+        p = np.exp(lg - lg.max())
+        ref = (p / p.sum()) @ V[0, h // 4]
+        assert np.max(np.abs(out32[0, h] - ref)) <= 1e-4
+        check_output(out[0, h], ref, "bf16", 1e-4)
+
+
+def test_split_counts_agree():
+    w = SMALL[1]
+    case = Case(w)
+    q = case.d["q_dec"][:, :, 0]
+    outs = [case.decode(q, S) for S in (1, 7, 32, 256)]
+    for o in outs[1:]:
+        # the fp32 results differ only by rounding order; stored in bf16 they
+        # may land one output ulp apart
+        assert np.all(np.abs(o - outs[0]) <= 2 * half_ulp(outs[0], "bf16") + 5e-4)
+
+
+def test_deterministic():
+    case = Case(SMALL[1])
+    q = case.d["q_dec"][:, :, 0]
+    a, b = case.decode(q, 16), case.decode(q, 16)
+    assert np.array_equal(a, b)
+
+
+def test_append_equals_prefill():
+    # prefill T0, then n appends == prefill of T0 + n (same rank table)
+    w = kvq_synth.Workload("app", 2, 8, 2, 200, n_qry=8, n_app=75, io_dtype="bf16",
+                           n_pairs_hi=6, residual=64, seed=32)
+    case = Case(w, T=w.tokens, max_tokens=w.max_tokens)
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    kn = dev(np.ascontiguousarray(case.d["k"][:, :, w.tokens:]))
+    vn = dev(np.ascontiguousarray(case.d["v"][:, :, w.tokens:]))
+    q = case.d["q_dec"][:, :, 0]
+    for i in range(w.n_app):
+        kvq.kvq_append(case.layout, kn[:, :, i].contiguous(), vn[:, :, i].contiguous(),
+                       case.cache.struct)
+        if i in (0, 40, w.n_app - 1):
+            T = w.tokens + i + 1
+            qz = case.oracle_quant(T=T)
+            ref = oracle.attention(qz, q, SM_SCALE)
+            check_output(case.decode(q, 8), ref, w.io_dtype, ATOL)
+            _, part = case.decode(q, 1, partials=True)
+            assert np.max(np.abs(single_split_fp32(part) - ref)) <= ATOL
+    torch.cuda.synchronize()
+    T = w.tokens + w.n_app
+    qz = case.oracle_quant(T=T)
+    compare_cache(case, qz, qz.nq // 32)
+    assert kvq.kvq_check(case.cache.struct) == 0
+
+
+def test_append_at_capacity_sets_error():
+    w = kvq_synth.Workload("cap", 1, 4, 1, 96, n_qry=4, io_dtype="bf16", residual=32, seed=33)
+    case = Case(w, T=96, max_tokens=96)
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    before = case.gpu_bytes()
+    z = dev(np.zeros((1, 1, 128), np.uint16))
+    kvq.kvq_append(case.layout, z, z, case.cache.struct)
+    assert kvq.kvq_check(case.cache.struct) == 1
+    after = case.gpu_bytes()
+    for k in before:
+        assert np.array_equal(before[k], after[k])
