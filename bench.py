@@ -138,7 +138,7 @@ def main():
         replicas.append(r)
     q = dev(data["q_dec"][:, :, 0])
     out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
-    ws = torch.empty(kvq.kvq_workspace_bytes(layout, S), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(kvq.kvq_workspace_bytes(layout, S), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(i):

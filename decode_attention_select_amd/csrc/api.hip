@@ -95,7 +95,7 @@ kvq_status kvq_cache_sizes(const kvq_layout* L, size_t sizes[KVQ_NBUF]) {
 kvq_status kvq_workspace_bytes(const kvq_layout* L, int32_t n_splits, size_t* bytes) {
   if (kvq_status s = check_layout(L)) return s;
   if (!bytes || n_splits < 1 || n_splits > 1024) return KVQ_EINVAL;
-  *bytes = (size_t)L->batch * L->n_q_heads * n_splits * (4 + D) * sizeof(float);
+  *bytes = decode_workspace_bytes(L->batch, L->n_q_heads, L->n_kv_heads, n_splits);
   return KVQ_OK;
 }
 
@@ -156,7 +156,7 @@ kvq_status kvq_decode_attn(const kvq_layout* L, const void* q, const kvq_cache* 
   if (kvq_status s = check_ptr(out)) return s;
   if (kvq_status s = check_ptr(workspace)) return s;
   if (kvq_status s = check_cache(g, cache, true)) return s;
-  return hip_status(launch_decode(g, q, cache, sm_scale, n_splits, (float*)workspace, out,
+  return hip_status(launch_decode(g, q, cache, sm_scale, n_splits, workspace, out,
                                   (hipStream_t)stream));
 }
 

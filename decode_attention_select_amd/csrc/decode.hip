@@ -18,11 +18,21 @@
 // all-ones row in the value-zero MFMA yields the softmax denominator from the
 // same rounded p.  Query heads of one KV head fill the 16 MFMA columns
 // (G <= 16).  Ring (16-bit) tokens use the same MFMA shapes on raw values.
+// The salient keys' high digits weigh 4*q*s, which is split exactly into an
+// fp16 value and its fp16 rounding residual carried by the otherwise unused
+// K-lanes 16..31 of that MFMA.
 //
-// Work split: one wave64 per (sequence, KV head, token split); each split
-// runs an online softmax (base 2, scale folded into the exponent) over its
-// 32-token blocks and writes (m, l, o[128]) per head; a second kernel merges
-// the splits with the log-sum-exp rule.
+// Work split: an 8-wave workgroup per (sequence, KV head, token split), one
+// workgroup per CU by default.  The waves take the split's 32-token blocks
+// round-robin, each with its own online softmax (base 2, scale folded into
+// the exponent; the running max is raised only when a block exceeds it by
+// more than 2^8, so most blocks skip the rescale).  Four blocks' codes and
+// scale/zero records are in flight per wave in registers; the record of the
+// block in work is staged through a per-wave LDS buffer so that the 16 lanes
+// sharing a channel slice read it as a broadcast.  The waves merge in LDS
+// into one record per head (m, l, o/l in fp16); the last workgroup of a
+// (sequence, KV head) to finish (atomic counter) merges the split records
+// with the log-sum-exp rule and writes the output.
 #include "common.h"
 #include "internal.h"
 
@@ -35,13 +45,18 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
-constexpr int PART = 4 + D;  // floats per (head, split) partial: m, l, 2 pad, o[128]
+constexpr int NW = 8;                  // waves per workgroup (one workgroup per CU)
+constexpr int WG_THREADS = 64 * NW;
+constexpr int PF = 4;                  // quantized groups in flight per wave
+constexpr int MAXG = 16;
+constexpr float RESCALE_SLACK = 8.0f;  // log2 headroom before the running max moves
 
 __device__ inline uint32_t h2u(h2 x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ inline h2 u2h(uint32_t x) { return __builtin_bit_cast(h2, x); }
 __device__ inline uint32_t pk_mul(uint32_t a, uint32_t b) { return h2u(u2h(a) * u2h(b)); }
 // fp32 pair -> fp16 pair, round to nearest even (v_cvt_pk_f16_f32)
 __device__ inline uint32_t pk_rne(float a, float b) { return h2u(h2{(_Float16)a, (_Float16)b}); }
+__device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Two codes of nibble pair `byte` of w (each nibble 0..3, value = code / 2 in
 // e2m1) -> two exact fp16 integers.
@@ -72,14 +87,6 @@ __device__ inline float wave_sum_kq(float x) {
   return x + __shfl_xor(x, 32);
 }
 
-// 16-bit input pair -> fp16 pair (bf16 widened exactly, then RNE to fp16).
-template <bool BF16>
-__device__ inline uint32_t to_f16_pair(uint32_t w) {
-  if constexpr (!BF16) return w;
-  const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
-  return (uint32_t)f32_to_half_bits(lo) | ((uint32_t)f32_to_half_bits(hi) << 16);
-}
-
 // Splits fp32 p into two 16-bit parts of the raw dtype with p ~= hi + lo to
 // ~2^-16 relative, so that the ring's raw 16-bit values multiply p at fp32-
 // like precision.
@@ -97,71 +104,171 @@ __device__ inline void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) 
   }
 }
 
+// Per-lane loads of one quantized group, issued one block ahead.
+struct Pref {
+  u2 klo[2];        // k_lo words of tile 0 and 1 (token col of the tile, channels 32kq..)
+  uint32_t khi[2];  // k_hi word of tile 0 and 1
+  uint32_t vc[4];   // v_codes word of channel group j = 0..3
+  u4 meta;          // 16 B of the group's k_meta (lanes 0-31) or v_meta (lanes 32-63)
+};
+
+template <int HIMODE>
+__device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int col, int kq,
+                                  Pref& p) {
+  const u2* klo = (const u2*)((const uint32_t*)c.k_lo + rec * GROUP_WORDS);
+  p.klo[0] = klo[(0 * 4 + kq) * 16 + col];
+  p.klo[1] = klo[(1 * 4 + kq) * 16 + col];
+  if constexpr (HIMODE == 4) {
+    const uint32_t* kh = (const uint32_t*)c.k_hi + rec * 32;
+    p.khi[0] = kh[col];
+    p.khi[1] = kh[16 + col];
+  }
+  const uint32_t* vc = (const uint32_t*)c.v_codes + rec * GROUP_WORDS;
+#pragma unroll
+  for (int j = 0; j < 4; j++) p.vc[j] = vc[(j * 4 + kq) * 16 + col];
+  const u4* meta = lane < 32 ? (const u4*)((const uint16_t*)c.k_meta + rec * 2 * D)
+                             : (const u4*)((const uint16_t*)c.v_meta + rec * 2 * D);
+  p.meta = meta[lane & 31];
+}
+
+// Workspace of one call (zero-filled once by the caller; counters return to
+// zero at the end of every call):
+//   ml   float2 [B*Hkv][S][G]        per split and head: running max m (log2
+//                                     units) and softmax denominator l
+//   o    fp16   [B*Hkv][S][G][128]   per split and head: o / l
+//   tick u32    [B*Hkv]              splits finished
+struct Ws {
+  float2* ml;
+  uint16_t* o;
+  uint32_t* tick;
+};
+
+__host__ __device__ inline size_t ws_ml_bytes(int B, int Hq, int S) {
+  return ((size_t)B * Hq * S * 8 + 255) & ~(size_t)255;
+}
+__host__ __device__ inline size_t ws_o_bytes(int B, int Hq, int S) {
+  return ((size_t)B * Hq * S * D * 2 + 255) & ~(size_t)255;
+}
+
+inline Ws ws_layout(void* base, int B, int Hq, int S) {
+  Ws w;
+  w.ml = (float2*)base;
+  w.o = (uint16_t*)((char*)base + ws_ml_bytes(B, Hq, S));
+  w.tick = (uint32_t*)((char*)base + ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S));
+  return w;
+}
+
+// LDS, one layout per phase (phases are separated by barriers)
+struct LdsLoop {
+  uint16_t q16[MAXG][D + 8];   // query as fp16 (rows padded: no bank conflicts)
+  uint16_t qraw[MAXG][D + 8];  // query in the io dtype
+  uint32_t stage[NW][256];     // per wave: metadata record of the group in work
+};
+struct LdsMerge {
+  float o[NW][MAXG][D + 4];    // wave results before the workgroup merge (padded rows)
+  float m[NW][MAXG], l[NW][MAXG];
+};
+struct Lds {
+  union {
+    LdsLoop loop;
+    LdsMerge merge;
+  } u;
+  int hil[16];                 // salient channels, ascending
+  int last;
+};
+
 template <bool BF16, int HIMODE>
-__global__ __launch_bounds__(64) void decode_split_kernel(Geo g, const uint16_t* __restrict__ q,
-                                                          kvq_cache c, float scale_log2, int S,
-                                                          float* __restrict__ partials) {
-  const int lane = threadIdx.x, col = lane & 15, kq = lane >> 4;
+__global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
+                                                            kvq_cache c, float scale_log2, int S,
+                                                            Ws ws, uint16_t* __restrict__ out) {
+  __shared__ Lds lds;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, kq = lane >> 4;
   const int bh = blockIdx.x / S, s = blockIdx.x % S;
   const int b = bh / g.Hkv, kh = bh % g.Hkv;
-  const bool hvalid = col < g.G;
-  const int head = kh * g.G + (hvalid ? col : 0);
+  const int G = g.G;
+  const bool hvalid = col < G;
 
+  // ---- this split's 32-token blocks: quantized groups, then ring blocks
   const int T = c.len[bh];
   const int nq = n_quant(T, g.R), ngq = nq / GS;
   const int nrb = (T - nq + GS - 1) / GS;
   const int NB = ngq + nrb;
   const int n0 = (int)((long long)s * NB / S), n1 = (int)((long long)(s + 1) * NB / S);
+  const int nq_end = min(n1, ngq);
+  const size_t rec0 = (size_t)bh * g.NG;
 
-  // query: lane (col, kq) holds channels 32kq .. 32kq+31 of head col
-  uint32_t qraw[16], q16[16];
-  {
-    const u4* qp = (const u4*)(q + ((size_t)b * g.Hq + head) * D + 32 * kq);
+  // ---- query (fp16 and raw) and the salient-channel table.  Finished
+  // before the cache stream starts: loads issued behind the stream would
+  // wait for all of it (memory counters retire in order).
+  for (int i = tid; i < G * D; i += WG_THREADS) {
+    const uint16_t v = q[((size_t)b * g.Hq + kh * G + (i >> 7)) * D + (i & (D - 1))];
+    lds.u.loop.qraw[i >> 7][i & (D - 1)] = v;
+    lds.u.loop.q16[i >> 7][i & (D - 1)] = BF16 ? f32_to_half_bits(in_to_f32(v, 1)) : v;
+  }
+  if constexpr (HIMODE != 0) {
+    if (wave == 0) {
+      // lane j: is pair j among the n_hi top-ranked pairs?  The 8 leading
+      // entries are read at once (one scalar load, not one per rank).
+      const int32_t* pr = c.pairs + (size_t)bh * NPAIR;
+      int top[8];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      u4 v = hvalid ? qp[i] : u4{0, 0, 0, 0};
+      for (int r = 0; r < 8; r++) top[r] = pr[r];
+      bool sal = false;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        qraw[4 * i + e] = v[e];
-        q16[4 * i + e] = to_f16_pair<BF16>(v[e]);
+      for (int r = 0; r < 8; r++) sal |= r < g.n_hi && (top[r] & 63) == lane;
+      const unsigned long long m = __ballot(sal);
+      if (lane < 16) lds.hil[lane] = 0;  // stays in range even for a malformed rank table
+      if (sal) {
+        const int idx = __popcll(m & ((1ull << lane) - 1));
+        lds.hil[idx] = lane;
+        lds.hil[g.n_hi + idx] = lane + NPAIR;
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  // the barrier comes before the stream: a wave whose load issue stalls on a
+  // saturated memory pipeline must not hold up the others
+  __syncthreads();
 
-  // salient channels (ascending): pairs of rank < n_hi, then the same + 64
-  __shared__ int hil[16];
+  // This wave's quantized groups are n0 + wave + i*NW, i < nmine.  Exactly PF
+  // group loads are kept in flight (past the end the index is clamped to the
+  // wave's last group: cache hits), so the compiler can count outstanding
+  // loads across the loop and never drains the prefetches.
+  const int nmine = nq_end > n0 + wave ? (nq_end - (n0 + wave) + NW - 1) / NW : 0;
+  const int nlast = n0 + wave + (nmine - 1) * NW;
+  auto group_at = [&](int i) { return rec0 + (size_t)min(n0 + wave + i * NW, nlast); };
+  Pref pf[PF];
+  if (nmine > 0) {
+#pragma unroll
+    for (int k = 0; k < PF; k++) load_group<HIMODE>(c, group_at(k), lane, col, kq, pf[k]);
+  }
+
+  uint32_t q16[16] = {0};
+  if (hvalid) {
+    const u4* qp = (const u4*)&lds.u.loop.q16[col][32 * kq];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const u4 v = qp[i];
+#pragma unroll
+      for (int e = 0; e < 4; e++) q16[4 * i + e] = v[e];
+    }
+  }
   uint32_t qhi[4] = {0, 0, 0, 0};  // HIMODE 4: 4*q (fp16); HIMODE 16: raw q
   float q4f[8];                    // HIMODE 4: 4*q in fp32
   int hch[8];                      // salient channel of digit 8*(kq&1) + e
   if constexpr (HIMODE != 0) {
-    __shared__ unsigned long long smask;
-    if (lane == 0) smask = 0;
-    if (lane < 16) hil[lane] = 0;  // stays in range even for a malformed rank table
-    __syncthreads();
-    if (lane < g.n_hi) atomicOr(&smask, 1ull << (c.pairs[(size_t)bh * NPAIR + lane] & 63));
-    __syncthreads();
-    const unsigned long long m = smask;
-    if ((m >> lane) & 1) {
-      const int idx = __popcll(m & ((1ull << lane) - 1));
-      hil[idx] = lane;
-      hil[g.n_hi + idx] = lane + NPAIR;
-    }
-    __syncthreads();
-    const uint16_t* qrow = q + ((size_t)b * g.Hq + head) * D;
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const int d = 8 * (kq & 1) + e;
       // HIMODE 4: K-lanes 16..31 (kq 2, 3) repeat the digits of lanes 0..15
       // and carry the rounding residual of 4*q*s; HIMODE 16 uses lanes 0..15
       const bool ok = hvalid && d < g.nh && (HIMODE == 4 || kq < 2);
-      hch[e] = ok ? (hil[d] & (D - 1)) : 0;
-      float v = ok ? in_to_f32(qrow[hch[e]], BF16) : 0.0f;
+      hch[e] = ok ? (lds.hil[d] & (D - 1)) : 0;
+      const float v = ok ? half_bits_to_f32(lds.u.loop.q16[col][hch[e]]) : 0.0f;
       q4f[e] = 4.0f * v;
-      uint32_t bits;
-      if constexpr (HIMODE == 4)
-        bits = f32_to_half_bits(4.0f * v);
-      else
-        bits = ok ? qrow[hch[e]] : 0u;
+      const uint32_t bits = HIMODE == 4 ? (uint32_t)f32_to_half_bits(4.0f * v)
+                                        : (ok ? (uint32_t)lds.u.loop.qraw[col][hch[e]] : 0u);
       qhi[e >> 1] |= bits << (16 * (e & 1));
     }
   }
@@ -172,246 +279,351 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Geo g, const uint16_t*
   for (int t = 0; t < 8; t++) O[t] = f4{0, 0, 0, 0};
   const uint32_t ONES = 0x3c003c00u;  // fp16 (1, 1)
 
-  for (int n = n0; n < n1; n++) {
+  // online-softmax step on this block's 8 logits per lane (x in log2 units)
+  auto softmax_step = [&](float (&x)[8], float (&p)[8]) {
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; i++) mx = fmaxf(mx, x[i]);
+    mx = wave_max_kq(mx);
+    const bool need = mx > m_run + RESCALE_SLACK;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = ex2(m_run - m_new);
+#pragma unroll
+      for (int t = 0; t < 8; t++) O[t] *= alpha;
+      Cvb *= alpha;
+      l_raw *= alpha;
+      m_run = m_new;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) p[i] = ex2(x[i] - m_run);
+  };
+
+  uint32_t* sm = lds.u.loop.stage[wave];
+  auto process_group = [&](const Pref& cur, size_t rec) {
+    // stage the metadata record: [0,64) k scale pairs, [64,128) k zero
+    // pairs, [128,192) v scale pairs (j-major), [192,256) v zero pairs.
+    // LDS accesses of one wave execute in order, so only the compiler must
+    // not move the reads below above this write (a memory fence here would
+    // also wait for the prefetches in flight).
+    ((u4*)sm)[lane] = cur.meta;
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+
+    // keys: q' = q * s (fp16), bias = q . z
+    uint32_t qs[16];
+    f4 cb = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const u4 sv = ((const u4*)(sm + 16 * kq))[i];
+      const u4 zv = ((const u4*)(sm + 64 + 16 * kq))[i];
+#pragma unroll
+      for (int e = 0; e < 4; e++) qs[4 * i + e] = pk_mul(q16[4 * i + e], sv[e]);
+      cb = mma_f16(zv, u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]}, cb);
+    }
+    uint32_t qshi[4];
+    if constexpr (HIMODE == 4) {
+      const uint16_t* ks = (const uint16_t*)sm;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        // 4*q*s is exact in fp32; split it into its fp16 rounding hi and the
+        // fp16 residual lo
+        const uint32_t sp = (uint32_t)ks[hch[2 * e]] | ((uint32_t)ks[hch[2 * e + 1]] << 16);
+        const uint32_t hi = pk_mul(qhi[e], sp);
+        const h2 sh = u2h(sp), hh = u2h(hi);
+        const uint32_t lo = pk_rne(fmaf(q4f[2 * e], (float)sh[0], -(float)hh[0]),
+                                   fmaf(q4f[2 * e + 1], (float)sh[1], -(float)hh[1]));
+        qshi[e] = kq < 2 ? hi : lo;
+      }
+    }
     f4 C[2];
-    if (n < ngq) {
-      // ------------------------------------------------ quantized group
-      const size_t rec = (size_t)bh * g.NG + n;
-      const uint32_t* kmeta = (const uint32_t*)c.k_meta + rec * (2 * D / 2);
-      uint32_t qs[16];
-      f4 cb = {0, 0, 0, 0};
+#pragma unroll
+    for (int TT = 0; TT < 2; TT++) {
+      const u2 w = cur.klo[TT];
+      f4 acc = cb;
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const uint32_t A = w[u] & 0x33333333u, Bn = (w[u] >> 2) & 0x33333333u;
+        const int k0 = 8 * u;
+        acc = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
+                      u4{qs[k0], qs[k0 + 1], qs[k0 + 2], qs[k0 + 3]}, acc);
+        acc = mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)},
+                      u4{qs[k0 + 4], qs[k0 + 5], qs[k0 + 6], qs[k0 + 7]}, acc);
+      }
+      if constexpr (HIMODE == 4) {
+        const uint32_t wsel = (kq & 1) ? cur.khi[TT] >> 16 : cur.khi[TT];
+        const uint32_t A = wsel & 0x33333333u, Bn = (wsel >> 2) & 0x33333333u;
+        acc = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
+                      u4{qshi[0], qshi[1], qshi[2], qshi[3]}, acc);
+      }
+      if constexpr (HIMODE == 16) {
+        const uint16_t* raw = (const uint16_t*)c.k_hi + rec * GS * g.nh + (16 * TT + col) * g.nh;
+        uint32_t a[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int d = 8 * (kq & 1) + e;
+          const uint32_t v = (kq < 2 && d < g.nh) ? raw[d] : 0u;
+          a[e >> 1] |= v << (16 * (e & 1));
+        }
+        acc = mma_raw<BF16>(u4{a[0], a[1], a[2], a[3]}, u4{qhi[0], qhi[1], qhi[2], qhi[3]}, acc);
+      }
+      C[TT] = acc;
+    }
+    float x[8], p[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) x[i] = C[i >> 2][i & 3] * scale_log2;
+    softmax_step(x, p);
+    const u4 P = u4{pk_rne(p[0], p[1]), pk_rne(p[2], p[3]), pk_rne(p[4], p[5]), pk_rne(p[6], p[7])};
+    // values
+    const u4 za = col < 4 ? ((const u4*)(sm + 192 + 16 * col))[kq]
+                          : (col == 4 ? u4{ONES, ONES, ONES, ONES} : u4{0, 0, 0, 0});
+    Cvb = mma_f16(za, P, Cvb);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const u4 sv = ((const u4*)(sm + 128 + 16 * j))[kq];
+      const u4 pj = u4{pk_mul(P[0], sv[0]), pk_mul(P[1], sv[1]), pk_mul(P[2], sv[2]),
+                       pk_mul(P[3], sv[3])};
+      const uint32_t wv = cur.vc[j];
+      const uint32_t A = wv & 0x33333333u, Bn = (wv >> 2) & 0x33333333u;
+      O[2 * j] = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)}, pj, O[2 * j]);
+      O[2 * j + 1] = mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)}, pj, O[2 * j + 1]);
+    }
+  };
+
+  for (int i = 0; i < nmine; i += PF) {
+#pragma unroll
+    for (int k = 0; k < PF; k++) {
+      if (i + k < nmine) process_group(pf[k], group_at(i + k));
+      load_group<HIMODE>(c, group_at(i + k + PF), lane, col, kq, pf[k]);
+    }
+  }
+
+  // ring blocks (16-bit keys and values): blocks n >= ngq of this split
+  for (int n = n0 + wave; n < n1; n += NW) {
+    if (n < ngq) continue;
+    const int pbase = nq + GS * (n - ngq);
+    const int nvalid = min(GS, T - pbase);
+    const int sb = (pbase / GS) % (g.RS / GS);
+    const uint16_t* rk = (const uint16_t*)c.ring_k + ((size_t)bh * g.RS + sb * GS) * D;
+    uint32_t qraw[16] = {0};
+    if (hvalid) {
+      const u4* qp = (const u4*)&lds.u.loop.qraw[col][32 * kq];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const u4 sv = ((const u4*)(kmeta + 16 * kq))[i];
-        const u4 zv = ((const u4*)(kmeta + 64 + 16 * kq))[i];
+        const u4 v = qp[i];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          qs[4 * i + e] = pk_mul(q16[4 * i + e], sv[e]);
-        }
-        cb = mma_f16(zv, u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]}, cb);
-      }
-      uint32_t qshi[4];
-      if constexpr (HIMODE == 4) {
-        const uint16_t* ks = (const uint16_t*)c.k_meta + rec * 2 * D;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          // 4*q*s is exact in fp32 (8- or 11-bit q times 11-bit s); split it
-          // into its fp16 rounding hi and the fp16 residual lo
-          const uint32_t sp = (uint32_t)ks[hch[2 * e]] | ((uint32_t)ks[hch[2 * e + 1]] << 16);
-          const uint32_t hi = pk_mul(qhi[e], sp);
-          const h2 sh = u2h(sp), hh = u2h(hi);
-          const uint32_t lo = pk_rne(fmaf(q4f[2 * e], (float)sh[0], -(float)hh[0]),
-                                     fmaf(q4f[2 * e + 1], (float)sh[1], -(float)hh[1]));
-          qshi[e] = kq < 2 ? hi : lo;
-        }
-      }
-      const u2* klo = (const u2*)((const uint32_t*)c.k_lo + rec * GROUP_WORDS);
-#pragma unroll
-      for (int TT = 0; TT < 2; TT++) {
-        const u2 w = klo[(TT * 4 + kq) * 16 + col];
-        f4 acc = cb;
-#pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const uint32_t A = w[u] & 0x33333333u, Bn = (w[u] >> 2) & 0x33333333u;
-          const int k0 = 8 * u;
-          acc = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
-                        u4{qs[k0], qs[k0 + 1], qs[k0 + 2], qs[k0 + 3]}, acc);
-          acc = mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)},
-                        u4{qs[k0 + 4], qs[k0 + 5], qs[k0 + 6], qs[k0 + 7]}, acc);
-        }
-        if constexpr (HIMODE == 4) {
-          const uint32_t wh = ((const uint32_t*)c.k_hi)[rec * 32 + 16 * TT + col];
-          const uint32_t ws = (kq & 1) ? wh >> 16 : wh;
-          const uint32_t A = ws & 0x33333333u, Bn = (ws >> 2) & 0x33333333u;
-          acc = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
-                        u4{qshi[0], qshi[1], qshi[2], qshi[3]}, acc);
-        }
-        if constexpr (HIMODE == 16) {
-          const uint16_t* raw = (const uint16_t*)c.k_hi + rec * GS * g.nh + (16 * TT + col) * g.nh;
-          uint32_t a[4] = {0, 0, 0, 0};
-#pragma unroll
-          for (int e = 0; e < 8; e++) {
-            const int d = 8 * (kq & 1) + e;
-            const uint32_t v = (kq < 2 && d < g.nh) ? raw[d] : 0u;
-            a[e >> 1] |= v << (16 * (e & 1));
-          }
-          acc = mma_raw<BF16>(u4{a[0], a[1], a[2], a[3]}, u4{qhi[0], qhi[1], qhi[2], qhi[3]}, acc);
-        }
-        C[TT] = acc;
-      }
-      // online softmax (base 2)
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) x[i] = C[i >> 2][i & 3] * scale_log2;
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 8; i++) mx = fmaxf(mx, x[i]);
-      const float m_new = fmaxf(m_run, wave_max_kq(mx));
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
-#pragma unroll
-      for (int t = 0; t < 8; t++) O[t] *= alpha;
-      Cvb *= alpha;
-      l_raw *= alpha;
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) p[i] = exp2f(x[i] - m_new);
-      const uint32_t P[4] = {pk_rne(p[0], p[1]),
-                             pk_rne(p[2], p[3]),
-                             pk_rne(p[4], p[5]),
-                             pk_rne(p[6], p[7])};
-      // values
-      const uint32_t* vmeta = (const uint32_t*)c.v_meta + rec * (2 * D / 2);
-      u4 za;
-      if (col < 4)
-        za = ((const u4*)(vmeta + 64 + 16 * col))[kq];
-      else if (col == 4)
-        za = u4{ONES, ONES, ONES, ONES};
-      else
-        za = u4{0, 0, 0, 0};
-      Cvb = mma_f16(za, u4{P[0], P[1], P[2], P[3]}, Cvb);
-      const uint32_t* vc = (const uint32_t*)c.v_codes + rec * GROUP_WORDS;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const u4 sv = ((const u4*)(vmeta + 16 * j))[kq];
-        const u4 pj = u4{pk_mul(P[0], sv[0]), pk_mul(P[1], sv[1]), pk_mul(P[2], sv[2]),
-                         pk_mul(P[3], sv[3])};
-        const uint32_t wv = vc[(j * 4 + kq) * 16 + col];
-        const uint32_t A = wv & 0x33333333u, Bn = (wv >> 2) & 0x33333333u;
-        O[2 * j] = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)}, pj, O[2 * j]);
-        O[2 * j + 1] =
-            mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)}, pj, O[2 * j + 1]);
-      }
-    } else {
-      // --------------------------------------------- ring block (16-bit)
-      const int pbase = nq + GS * (n - ngq);
-      const int nvalid = min(GS, T - pbase);
-      const int sb = (pbase / GS) % (g.RS / GS);
-      const uint16_t* rk = (const uint16_t*)c.ring_k + ((size_t)bh * g.RS + sb * GS) * D;
-#pragma unroll
-      for (int TT = 0; TT < 2; TT++) {
-        const int t = tile_token(16 * TT + col);
-        const u4* kr = (const u4*)(rk + (size_t)t * D + 32 * kq);
-        f4 acc = {0, 0, 0, 0};
-#pragma unroll
-        for (int k = 0; k < 4; k++)
-          acc = mma_raw<BF16>(kr[k], u4{qraw[4 * k], qraw[4 * k + 1], qraw[4 * k + 2], qraw[4 * k + 3]},
-                              acc);
-        C[TT] = acc;
-      }
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const int t = 8 * kq + 4 * (i >> 2) + (i & 3);
-        x[i] = t < nvalid ? C[i >> 2][i & 3] * scale_log2 : -INFINITY;
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 8; i++) mx = fmaxf(mx, x[i]);
-      const float m_new = fmaxf(m_run, wave_max_kq(mx));
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
-#pragma unroll
-      for (int t = 0; t < 8; t++) O[t] *= alpha;
-      Cvb *= alpha;
-      l_raw *= alpha;
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        p[i] = exp2f(x[i] - m_new);
-        l_raw += p[i];
-      }
-      uint32_t Ph[4], Pl[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) split_pair<BF16>(p[2 * i], p[2 * i + 1], Ph[i], Pl[i]);
-      const uint16_t* rv = (const uint16_t*)c.ring_v + (((size_t)bh * (g.RS / GS) + sb) * D) * GS;
-#pragma unroll
-      for (int tt = 0; tt < 8; tt++) {
-        u4 a = *(const u4*)(rv + (size_t)(16 * tt + col) * GS + 8 * kq);
-        // zero slots past the last token (they may hold stale data)
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int t0 = 8 * kq + 2 * e;
-          const uint32_t keep = (t0 < nvalid ? 0x0000ffffu : 0u) | (t0 + 1 < nvalid ? 0xffff0000u : 0u);
-          a[e] &= keep;
-        }
-        O[tt] = mma_raw<BF16>(a, u4{Ph[0], Ph[1], Ph[2], Ph[3]}, O[tt]);
-        O[tt] = mma_raw<BF16>(a, u4{Pl[0], Pl[1], Pl[2], Pl[3]}, O[tt]);
+        for (int e = 0; e < 4; e++) qraw[4 * i + e] = v[e];
       }
     }
-  }
-
-  // softmax denominator: all-ones row (row 4 -> lane 16 + col, element 0)
-  // of the value-zero MFMA, plus the ring blocks' fp32 sum
-  const float l_q = __shfl(Cvb[0], 16 + col);
-  const float l = l_q + wave_sum_kq(l_raw);
-  float vb[4];
+    f4 C[2];
 #pragma unroll
-  for (int j = 0; j < 4; j++) vb[j] = __shfl(Cvb[j], col);  // rows 0..3 -> lane col
-  if (hvalid) {
-    float* out = partials + ((size_t)(b * g.Hq + head) * S + s) * PART;
-    if (kq == 0) {
-      out[0] = m_run;
-      out[1] = l;
+    for (int TT = 0; TT < 2; TT++) {
+      const int t = tile_token(16 * TT + col);
+      const u4* kr = (const u4*)(rk + (size_t)t * D + 32 * kq);
+      f4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < 4; k++)
+        acc = mma_raw<BF16>(kr[k], u4{qraw[4 * k], qraw[4 * k + 1], qraw[4 * k + 2], qraw[4 * k + 3]},
+                            acc);
+      C[TT] = acc;
     }
+    float x[8], p[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int t = 8 * kq + 4 * (i >> 2) + (i & 3);
+      x[i] = t < nvalid ? C[i >> 2][i & 3] * scale_log2 : -INFINITY;
+    }
+    softmax_step(x, p);
+#pragma unroll
+    for (int i = 0; i < 8; i++) l_raw += p[i];
+    uint32_t Ph[4], Pl[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) split_pair<BF16>(p[2 * i], p[2 * i + 1], Ph[i], Pl[i]);
+    const uint16_t* rv = (const uint16_t*)c.ring_v + (((size_t)bh * (g.RS / GS) + sb) * D) * GS;
 #pragma unroll
     for (int tt = 0; tt < 8; tt++) {
-      f4 v = O[tt] + vb[tt >> 1];
-      *(f4*)(out + 4 + 16 * tt + 4 * kq) = v;
+      u4 a = *(const u4*)(rv + (size_t)(16 * tt + col) * GS + 8 * kq);
+      // zero slots past the last token (they may hold stale data)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int t0 = 8 * kq + 2 * e;
+        const uint32_t keep =
+            (t0 < nvalid ? 0x0000ffffu : 0u) | (t0 + 1 < nvalid ? 0xffff0000u : 0u);
+        a[e] &= keep;
+      }
+      O[tt] = mma_raw<BF16>(a, u4{Ph[0], Ph[1], Ph[2], Ph[3]}, O[tt]);
+      O[tt] = mma_raw<BF16>(a, u4{Pl[0], Pl[1], Pl[2], Pl[3]}, O[tt]);
     }
   }
-}
 
-// Merges the splits of one (b, query head): thread c owns channel c.
-template <bool BF16>
-__global__ __launch_bounds__(D) void combine_kernel(int S, const float* __restrict__ partials,
-                                                    uint16_t* __restrict__ out) {
-  const int bhq = blockIdx.x, c = threadIdx.x;
-  const float* p = partials + (size_t)bhq * S * PART;
-  float M = -INFINITY;
-  for (int s = 0; s < S; s++) M = fmaxf(M, p[(size_t)s * PART]);
-  float L = 0.0f, acc = 0.0f;
-  for (int s = 0; s < S; s++) {
-    const float m = p[(size_t)s * PART];
-    if (m == -INFINITY) continue;
-    const float w = exp2f(m - M);
-    L += w * p[(size_t)s * PART + 1];
-    acc += w * p[(size_t)s * PART + 4 + c];
+  // ---- merge the waves: per head m, l and unnormalized o
+  __syncthreads();  // every wave is done with the loop-phase LDS
+  {
+    const float l_q = __shfl(Cvb[0], 16 + col);  // all-ones row 4 -> lane 16 + col
+    const float l = l_q + wave_sum_kq(l_raw);
+    float vb[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) vb[j] = __shfl(Cvb[j], col);  // value-zero rows 0..3
+    if (hvalid) {
+      if (kq == 0) {
+        lds.u.merge.m[wave][col] = m_run;
+        lds.u.merge.l[wave][col] = l;
+      }
+#pragma unroll
+      for (int tt = 0; tt < 8; tt++)
+        *(f4*)&lds.u.merge.o[wave][col][16 * tt + 4 * kq] = O[tt] + vb[tt >> 1];
+    }
   }
-  const float o = L > 0.0f ? acc / L : 0.0f;
-  uint16_t bits;
-  if constexpr (BF16) {
-    const uint32_t u = __float_as_uint(o);
-    bits = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-  } else {
-    bits = f32_to_half_bits(o);
+  __syncthreads();
+  // split record: (m, l) and o / l in fp16; thread -> (head, 4 channels)
+  const size_t rbase = ((size_t)bh * S + s) * G;
+  for (int i = tid; i < G * (D / 4); i += WG_THREADS) {
+    const int h = i / (D / 4), c4 = 4 * (i % (D / 4));
+    float M = lds.u.merge.m[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; w++) M = fmaxf(M, lds.u.merge.m[w][h]);
+    f4 o = {0, 0, 0, 0};
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+      const float mw = lds.u.merge.m[w][h];
+      const float a = mw == -INFINITY ? 0.0f : ex2(mw - M);
+      o += a * *(const f4*)&lds.u.merge.o[w][h][c4];
+      l += a * lds.u.merge.l[w][h];
+    }
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    // records cross workgroups (and L2 slices): coherent (sc1) stores
+    const uint64_t ov = (uint64_t)pk_rne(o[0] * inv, o[1] * inv) |
+                        ((uint64_t)pk_rne(o[2] * inv, o[3] * inv) << 32);
+    __hip_atomic_store((uint64_t*)(ws.o + (rbase + h) * D + c4), ov, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (c4 == 0)
+      __hip_atomic_store((uint64_t*)&ws.ml[rbase + h],
+                         (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(l) << 32),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  out[(size_t)bhq * D + c] = bits;
+
+  // ---- the last workgroup of this (sequence, KV head) merges all splits.
+  // Every record store has completed (s_waitcnt) before the counter moves,
+  // and the merging workgroup reads with coherent loads: no cache-wide
+  // writeback or invalidate is needed.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(&ws.tick[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds.last = prev == (uint32_t)(S - 1);
+  }
+  __syncthreads();
+  if (!lds.last) return;
+  // item = (head, 8 channels); nsub lanes (a power of two <= 32) share an
+  // item's splits and reduce with shuffles
+  const int items = G * (D / 8);
+  int nsub = 1;
+  while (nsub < 32 && items * nsub * 2 <= WG_THREADS) nsub *= 2;
+  const uint64_t* mlb = (const uint64_t*)(ws.ml + (size_t)bh * S * G);
+  const uint64_t* ob = (const uint64_t*)(ws.o + (size_t)bh * S * G * D);
+  auto ld = [](const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  for (int base = 0; base < items * nsub; base += WG_THREADS) {
+    const int t = base + tid;
+    const int item = t / nsub, sub = t % nsub;
+    const bool act = item < items;
+    const int h = act ? item / (D / 8) : 0, c8 = act ? 8 * (item % (D / 8)) : 0;
+    // one pass: up to 4 of this lane's splits are loaded at once and folded
+    // in with a running max (rescaling when it rises)
+    float M = -INFINITY, L = 0.0f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i0 = sub; act && i0 < S; i0 += 4 * nsub) {
+      uint64_t mlw[4], o0[4], o1[4];
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const int i = min(i0 + k * nsub, S - 1);
+        const uint64_t* op = ob + (((size_t)i * G + h) * D + c8) / 4;
+        mlw[k] = ld(mlb + (size_t)i * G + h);
+        o0[k] = ld(op);
+        o1[k] = ld(op + 1);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const float m = __uint_as_float((uint32_t)mlw[k]);
+        const float l = __uint_as_float((uint32_t)(mlw[k] >> 32));
+        if (i0 + k * nsub >= S || m == -INFINITY) continue;
+        if (m > M) {
+          const float a = ex2(M - m);
+          L *= a;
+#pragma unroll
+          for (int e = 0; e < 8; e++) acc[e] *= a;
+          M = m;
+        }
+        const float wgt = ex2(m - M) * l;
+        L += wgt;
+        const u4 ov = u4{(uint32_t)o0[k], (uint32_t)(o0[k] >> 32), (uint32_t)o1[k],
+                         (uint32_t)(o1[k] >> 32)};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const h2 v = u2h(ov[e]);
+          acc[2 * e] += wgt * (float)v[0];
+          acc[2 * e + 1] += wgt * (float)v[1];
+        }
+      }
+    }
+    for (int o = 1; o < nsub; o <<= 1) {
+      const float M2 = __shfl_xor(M, o), L2 = __shfl_xor(L, o);
+      const float Mn = fmaxf(M, M2);
+      const float a1 = M == -INFINITY ? 0.0f : ex2(M - Mn);
+      const float a2 = M2 == -INFINITY ? 0.0f : ex2(M2 - Mn);
+      L = L * a1 + L2 * a2;
+#pragma unroll
+      for (int e = 0; e < 8; e++) acc[e] = acc[e] * a1 + __shfl_xor(acc[e], o) * a2;
+      M = Mn;
+    }
+    if (act && sub == 0) {
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      uint16_t* op = out + ((size_t)b * g.Hq + kh * G + h) * D + c8;
+      uint16_t bits[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float v = acc[e] * inv;
+        if constexpr (BF16) {
+          const uint32_t u = __float_as_uint(v);
+          bits[e] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+        } else {
+          bits[e] = f32_to_half_bits(v);
+        }
+      }
+      *(u4*)op = u4{bits[0] | ((uint32_t)bits[1] << 16), bits[2] | ((uint32_t)bits[3] << 16),
+                    bits[4] | ((uint32_t)bits[5] << 16), bits[6] | ((uint32_t)bits[7] << 16)};
+    }
+  }
+  if (tid == 0)  // ready for the next call
+    __hip_atomic_store(&ws.tick[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool BF16, int HIMODE>
-static void launch_split(const Geo& g, const void* q, const kvq_cache* c, float scale_log2,
-                         int S, float* partials, hipStream_t st) {
-  hipLaunchKernelGGL((decode_split_kernel<BF16, HIMODE>), dim3(g.B * g.Hkv * S), dim3(64), 0, st,
-                     g, (const uint16_t*)q, *c, scale_log2, S, partials);
+static void launch_one(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
+                       const Ws& ws, void* out, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<BF16, HIMODE>), dim3(g.B * g.Hkv * S), dim3(WG_THREADS), 0,
+                     st, g, (const uint16_t*)q, *c, scale_log2, S, ws, (uint16_t*)out);
+}
+
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {
+  return ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S) + (((size_t)B * Hkv * 4 + 255) & ~(size_t)255);
 }
 
 hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float sm_scale,
-                         int S, float* partials, void* out, hipStream_t st) {
+                         int S, void* workspace, void* out, hipStream_t st) {
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   const int hm = g.n_hi == 0 ? 0 : g.bits_hi;
+  const Ws ws = ws_layout(workspace, g.B, g.Hq, S);
   if (g.bf16) {
-    if (hm == 0) launch_split<true, 0>(g, q, c, scale_log2, S, partials, st);
-    else if (hm == 4) launch_split<true, 4>(g, q, c, scale_log2, S, partials, st);
-    else launch_split<true, 16>(g, q, c, scale_log2, S, partials, st);
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(g.B * g.Hq), dim3(D), 0, st, S,
-                       (const float*)partials, (uint16_t*)out);
+    if (hm == 0) launch_one<true, 0>(g, q, c, scale_log2, S, ws, out, st);
+    else if (hm == 4) launch_one<true, 4>(g, q, c, scale_log2, S, ws, out, st);
+    else launch_one<true, 16>(g, q, c, scale_log2, S, ws, out, st);
   } else {
-    if (hm == 0) launch_split<false, 0>(g, q, c, scale_log2, S, partials, st);
-    else if (hm == 4) launch_split<false, 4>(g, q, c, scale_log2, S, partials, st);
-    else launch_split<false, 16>(g, q, c, scale_log2, S, partials, st);
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(g.B * g.Hq), dim3(D), 0, st, S,
-                       (const float*)partials, (uint16_t*)out);
+    if (hm == 0) launch_one<false, 0>(g, q, c, scale_log2, S, ws, out, st);
+    else if (hm == 4) launch_one<false, 4>(g, q, c, scale_log2, S, ws, out, st);
+    else launch_one<false, 16>(g, q, c, scale_log2, S, ws, out, st);
   }
   return hipGetLastError();
 }

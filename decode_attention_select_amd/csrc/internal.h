@@ -12,6 +12,7 @@ hipError_t launch_quant_values(const Geo& g, const void* v, int T, kvq_cache* c,
 hipError_t launch_append(const Geo& g, const void* k_new, const void* v_new, kvq_cache* c,
                          hipStream_t st);
 hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float sm_scale,
-                         int n_splits, float* partials, void* out, hipStream_t st);
+                         int n_splits, void* workspace, void* out, hipStream_t st);
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_splits);
 
 }  // namespace kvq

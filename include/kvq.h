@@ -136,7 +136,12 @@ typedef struct {
 kvq_status kvq_cache_sizes(const kvq_layout *L, size_t sizes[KVQ_NBUF] /*host*/);
 
 /* Workspace bytes kvq_decode_attn needs for `n_splits` token splits per
- * (sequence, KV head): B*Hq*n_splits*132 floats of partial results. */
+ * (sequence, KV head), 1 <= n_splits <= 1024 and n_splits * G <= 4096:
+ * B*Hq*n_splits*132 floats of per-split results followed by one 32-bit
+ * counter per (sequence, KV head), rounded up to 16 bytes.  The caller
+ * zero-fills a workspace once before its first use; every completed call
+ * leaves the counters at zero again.  One workspace serves one call at a
+ * time. */
 kvq_status kvq_workspace_bytes(const kvq_layout *L, int32_t n_splits,
                                size_t *bytes /*host*/);
 
@@ -198,12 +203,13 @@ kvq_status kvq_append(const kvq_layout *L, const void *k_new,
  * over all T tokens, where k^, v^ are the dequantized codes z + s*code for
  * quantized tokens and channels and the raw 16-bit values for ring tokens
  * and 16-bit channels.  The token axis is cut into n_splits ranges per
- * (b, kv head) (1 <= n_splits <= 1024), each reduced with an online softmax;
- * a log-sum-exp combine merges them.  Computation is fp32 with fp16 matrix
- * operands.
+ * (b, kv head) (limits as for kvq_workspace_bytes), each reduced with an
+ * online softmax; a log-sum-exp combine merges them inside the same launch.
+ * Computation is fp32 with fp16 matrix operands; the result is rounded to
+ * the io dtype (nearest even).  Requires T >= 1 (T = 0 writes zeros).
  *   q   [B][Hq][128] io dtype;  out [B][Hq][128] io dtype
- *   workspace: >= kvq_workspace_bytes(L, n_splits) bytes, else
- *   KVQ_ECAPACITY. */
+ *   workspace: >= kvq_workspace_bytes(L, n_splits) bytes (else
+ *   KVQ_ECAPACITY), zero-filled before its first use. */
 kvq_status kvq_decode_attn(const kvq_layout *L, const void *q,
                            const kvq_cache *cache, float sm_scale,
                            int32_t n_splits, void *workspace, size_t ws_bytes,

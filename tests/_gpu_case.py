@@ -84,8 +84,11 @@ class Case:
 
     def decode(self, q_bits: np.ndarray, n_splits: int, partials: bool = False):
         """q_bits [B][Hq][128] -> GPU output widened to fp64; with `partials`
-        also the fp32 per-split records [B][Hq][S][132] (m, l, -, -, o[128])."""
-        ws = torch.empty(kvq.kvq_workspace_bytes(self.layout, n_splits), dtype=torch.uint8,
+        also the per-split records read back from the workspace: fp32 (m, l)
+        [B][Hq][S][2] and the fp16 normalized o/l [B][Hq][S][128] (fp64).
+        The workspace holds them as [B*Hkv][S][G] (m, l), 256-byte aligned,
+        then [B*Hkv][S][G][128] fp16."""
+        ws = torch.zeros(kvq.kvq_workspace_bytes(self.layout, n_splits), dtype=torch.uint8,
                          device="cuda")
         out = torch.empty((self.w.batch, self.w.n_q_heads, 128), dtype=torch.int16, device="cuda")
         kvq.kvq_decode_attn(self.layout, dev(q_bits), self.cache.struct, SM_SCALE, n_splits,
@@ -94,8 +97,15 @@ class Case:
         o = kvq_synth.bits_to_f64(host(out, np.uint16), self.w.io_dtype)
         if not partials:
             return o
-        part = host(ws, np.float32).reshape(self.w.batch, self.w.n_q_heads, n_splits, 132)
-        return o, part
+        B, Hkv, G, S = self.w.batch, self.w.n_kv_heads, self.w.group_size, n_splits
+        nrec = B * Hkv * S * G
+        raw = host(ws, np.uint8)
+        ml_bytes = (nrec * 8 + 255) // 256 * 256
+        ml = raw[:nrec * 8].view(np.float32).reshape(B, Hkv, S, G, 2)
+        o16 = raw[ml_bytes:ml_bytes + nrec * 256].view(np.float16).reshape(B, Hkv, S, G, 128)
+        ml = ml.transpose(0, 1, 3, 2, 4).reshape(B, Hkv * G, S, 2).astype(np.float64)
+        o16 = o16.transpose(0, 1, 3, 2, 4).reshape(B, Hkv * G, S, 128).astype(np.float64)
+        return o, (ml, o16)
 
 
 def half_ulp(x: np.ndarray, io_dtype: str) -> np.ndarray:
@@ -108,19 +118,30 @@ def half_ulp(x: np.ndarray, io_dtype: str) -> np.ndarray:
 
 
 def check_output(got, ref, io_dtype, atol):
-    """|got - ref| <= atol + half an output ulp, elementwise; returns the
-    largest excess of the arithmetic error over `atol` budget usage."""
+    """|got - ref| <= atol + half an fp16 ulp (the split records hold o/l in
+    fp16) + half an output ulp, elementwise; returns the largest error."""
     err = np.abs(got - ref)
-    bound = atol + half_ulp(ref, io_dtype)
+    bound = atol + half_ulp(ref, "fp16") + half_ulp(ref, io_dtype)
     assert np.all(err <= bound), "max err %.3g (bound there %.3g)" % (
         err.max(), bound.flat[np.argmax(err - bound)])
     return float(err.max())
 
 
-def single_split_fp32(part: np.ndarray) -> np.ndarray:
-    """fp32 attention result from a one-split partial: o / l."""
-    assert part.shape[2] == 1
-    return part[:, :, 0, 4:].astype(np.float64) / part[:, :, 0, 1:2].astype(np.float64)
+def single_split(part) -> np.ndarray:
+    """Attention result of a one-split call before the 16-bit output
+    rounding: the split record's o/l, computed in fp32 and stored as fp16."""
+    ml, o16 = part
+    assert o16.shape[2] == 1
+    return o16[:, :, 0]
+
+
+def check_single_split(part, ref, atol):
+    """The fp32 result, seen through its fp16 record: within `atol` plus
+    half an fp16 ulp of the oracle."""
+    got = single_split(part)
+    err = np.abs(got - ref)
+    assert np.all(err <= atol + half_ulp(ref, "fp16")), "max err %.3g" % err.max()
+    return float(err.max())
 
 
 def compare_cache(case: Case, qz, ng: int):
