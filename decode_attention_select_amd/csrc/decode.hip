@@ -58,6 +58,13 @@ __device__ inline uint32_t pk_mul(uint32_t a, uint32_t b) { return h2u(u2h(a) * 
 __device__ inline uint32_t pk_rne(float a, float b) { return h2u(h2{(_Float16)a, (_Float16)b}); }
 __device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-bit input pair -> fp16 pair (bf16 widened exactly, then RNE to fp16)
+template <bool BF16>
+__device__ inline uint32_t to_f16_pair(uint32_t w) {
+  if constexpr (!BF16) return w;
+  return pk_rne(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
 // Two codes of nibble pair `byte` of w (each nibble 0..3, value = code / 2 in
 // e2m1) -> two exact fp16 integers.
 template <int BYTE>
@@ -78,9 +85,13 @@ __device__ inline f4 mma_raw(u4 a, u4 b, f4 c) {
     return mma_f16(a, b, c);
 }
 
-__device__ inline float wave_max_kq(float x) {  // max over lanes l, l^16, l^32, l^48
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+// max over lanes l, l^16, l^32, l^48: two lane-swap VALU ops (gfx950
+// v_permlane32_swap / v_permlane16_swap), no LDS round trip
+__device__ inline float wave_max_kq(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(x, fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(x, fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])));
 }
 __device__ inline float wave_sum_kq(float x) {
   x += __shfl_xor(x, 16);
@@ -158,14 +169,17 @@ inline Ws ws_layout(void* base, int B, int Hq, int S) {
   return w;
 }
 
-// LDS, one layout per phase (phases are separated by barriers)
+// LDS, one layout per phase.  The loop phase is private to each wave (no
+// workgroup barrier before the stream); a barrier separates it from the
+// merge phase.
 struct LdsLoop {
-  uint16_t q16[MAXG][D + 8];   // query as fp16 (rows padded: no bank conflicts)
-  uint16_t qraw[MAXG][D + 8];  // query in the io dtype
-  uint32_t stage[NW][256];     // per wave: metadata record of the group in work
+  uint16_t q16[NW][MAXG][D + 8];   // per wave: query as fp16 (padded rows)
+  uint16_t qraw[NW][MAXG][D + 8];  // per wave: query in the io dtype (16-bit salient keys)
+  uint32_t stage[NW][256];         // per wave: metadata record of the group in work
+  int hil[NW][16];                 // per wave: salient channels, ascending
 };
 struct LdsMerge {
-  float o[NW][MAXG][D + 4];    // wave results before the workgroup merge (padded rows)
+  float o[NW][MAXG][D + 4];        // wave results before the workgroup merge (padded rows)
   float m[NW][MAXG], l[NW][MAXG];
 };
 struct Lds {
@@ -173,11 +187,12 @@ struct Lds {
     LdsLoop loop;
     LdsMerge merge;
   } u;
-  int hil[16];                 // salient channels, ascending
   int last;
 };
 
-template <bool BF16, int HIMODE>
+// HASQ: the cache has quantized-group storage (capacity NG >= 1); without it
+// no group address exists and the group stream is compiled out.
+template <bool BF16, int HIMODE, bool HASQ>
 __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             kvq_cache c, float scale_log2, int S,
                                                             Ws ws, uint16_t* __restrict__ out) {
@@ -189,8 +204,25 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int G = g.G;
   const bool hvalid = col < G;
 
-  // ---- this split's 32-token blocks: quantized groups, then ring blocks
+  // ---- every wave starts on its own.  Its first request is its query
+  // slice (head col, channels 32kq..32kq+31): memory counters retire in
+  // order, so anything requested behind the cache stream would wait for it.
+  u4 qv[4];
+  {
+    const u4* qg = (const u4*)(q + ((size_t)b * g.Hq + kh * G + min(col, G - 1)) * D + 32 * kq);
+#pragma unroll
+    for (int i = 0; i < 4; i++) qv[i] = qg[i];
+  }
+  // scalar loads: the length and the 8 leading ranks
   const int T = c.len[bh];
+  int top[8];
+  if constexpr (HIMODE != 0) {
+    const int32_t* pr = c.pairs + (size_t)bh * NPAIR;
+#pragma unroll
+    for (int r = 0; r < 8; r++) top[r] = pr[r];
+  }
+
+  // this split's 32-token blocks: quantized groups, then ring blocks
   const int nq = n_quant(T, g.R), ngq = nq / GS;
   const int nrb = (T - nq + GS - 1) / GS;
   const int NB = ngq + nrb;
@@ -198,77 +230,66 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int nq_end = min(n1, ngq);
   const size_t rec0 = (size_t)bh * g.NG;
 
-  // ---- query (fp16 and raw) and the salient-channel table.  Finished
-  // before the cache stream starts: loads issued behind the stream would
-  // wait for all of it (memory counters retire in order).
-  for (int i = tid; i < G * D; i += WG_THREADS) {
-    const uint16_t v = q[((size_t)b * g.Hq + kh * G + (i >> 7)) * D + (i & (D - 1))];
-    lds.u.loop.qraw[i >> 7][i & (D - 1)] = v;
-    lds.u.loop.q16[i >> 7][i & (D - 1)] = BF16 ? f32_to_half_bits(in_to_f32(v, 1)) : v;
-  }
-  if constexpr (HIMODE != 0) {
-    if (wave == 0) {
-      // lane j: is pair j among the n_hi top-ranked pairs?  The 8 leading
-      // entries are read at once (one scalar load, not one per rank).
-      const int32_t* pr = c.pairs + (size_t)bh * NPAIR;
-      int top[8];
-#pragma unroll
-      for (int r = 0; r < 8; r++) top[r] = pr[r];
-      bool sal = false;
-#pragma unroll
-      for (int r = 0; r < 8; r++) sal |= r < g.n_hi && (top[r] & 63) == lane;
-      const unsigned long long m = __ballot(sal);
-      if (lane < 16) lds.hil[lane] = 0;  // stays in range even for a malformed rank table
-      if (sal) {
-        const int idx = __popcll(m & ((1ull << lane) - 1));
-        lds.hil[idx] = lane;
-        lds.hil[g.n_hi + idx] = lane + NPAIR;
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  // the barrier comes before the stream: a wave whose load issue stalls on a
-  // saturated memory pipeline must not hold up the others
-  __syncthreads();
-
   // This wave's quantized groups are n0 + wave + i*NW, i < nmine.  Exactly PF
   // group loads are kept in flight (past the end the index is clamped to the
-  // wave's last group: cache hits), so the compiler can count outstanding
-  // loads across the loop and never drains the prefetches.
+  // wave's last group, or to group 0: cache hits, never used), so the
+  // compiler can count outstanding loads and never drains the prefetches.
   const int nmine = nq_end > n0 + wave ? (nq_end - (n0 + wave) + NW - 1) / NW : 0;
-  const int nlast = n0 + wave + (nmine - 1) * NW;
+  const int nlast = nmine > 0 ? n0 + wave + (nmine - 1) * NW : 0;
   auto group_at = [&](int i) { return rec0 + (size_t)min(n0 + wave + i * NW, nlast); };
   Pref pf[PF];
-  if (nmine > 0) {
+  if constexpr (HASQ) {
 #pragma unroll
     for (int k = 0; k < PF; k++) load_group<HIMODE>(c, group_at(k), lane, col, kq, pf[k]);
   }
 
-  uint32_t q16[16] = {0};
-  if (hvalid) {
-    const u4* qp = (const u4*)&lds.u.loop.q16[col][32 * kq];
+  // query as fp16 pairs (zero past the G heads)
+  uint32_t q16[16];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const u4 v = qp[i];
+  for (int i = 0; i < 4; i++)
 #pragma unroll
-      for (int e = 0; e < 4; e++) q16[4 * i + e] = v[e];
-    }
-  }
+    for (int e = 0; e < 4; e++) q16[4 * i + e] = hvalid ? to_f16_pair<BF16>(qv[i][e]) : 0u;
+
   uint32_t qhi[4] = {0, 0, 0, 0};  // HIMODE 4: 4*q (fp16); HIMODE 16: raw q
   float q4f[8];                    // HIMODE 4: 4*q in fp32
   int hch[8];                      // salient channel of digit 8*(kq&1) + e
   if constexpr (HIMODE != 0) {
+    // per-wave tables: this wave's query rows and the salient channels
+    // (pairs of rank < n_hi ascending, then the same + 64)
+    uint16_t(*wq)[D + 8] = lds.u.loop.q16[wave];
+    uint16_t(*wr)[D + 8] = lds.u.loop.qraw[wave];
+    int* hil = lds.u.loop.hil[wave];
+    if (hvalid) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        *(u4*)&wq[col][32 * kq + 8 * i] = u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
+        if constexpr (HIMODE == 16) *(u4*)&wr[col][32 * kq + 8 * i] = qv[i];
+      }
+    }
+    bool sal = false;
+#pragma unroll
+    for (int r = 0; r < 8; r++) sal |= r < g.n_hi && (top[r] & 63) == lane;
+    const unsigned long long m = __ballot(sal);
+    if (lane < 16) hil[lane] = 0;  // stays in range even for a malformed rank table
+    if (sal) {
+      const int idx = __popcll(m & ((1ull << lane) - 1));
+      hil[idx] = lane;
+      hil[g.n_hi + idx] = lane + NPAIR;
+    }
+    // LDS accesses of one wave execute in order: a compiler barrier suffices
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const int d = 8 * (kq & 1) + e;
       // HIMODE 4: K-lanes 16..31 (kq 2, 3) repeat the digits of lanes 0..15
       // and carry the rounding residual of 4*q*s; HIMODE 16 uses lanes 0..15
       const bool ok = hvalid && d < g.nh && (HIMODE == 4 || kq < 2);
-      hch[e] = ok ? (lds.hil[d] & (D - 1)) : 0;
-      const float v = ok ? half_bits_to_f32(lds.u.loop.q16[col][hch[e]]) : 0.0f;
+      hch[e] = ok ? (hil[d] & (D - 1)) : 0;
+      const float v = ok ? half_bits_to_f32(wq[col][hch[e]]) : 0.0f;
       q4f[e] = 4.0f * v;
       const uint32_t bits = HIMODE == 4 ? (uint32_t)f32_to_half_bits(4.0f * v)
-                                        : (ok ? (uint32_t)lds.u.loop.qraw[col][hch[e]] : 0u);
+                                        : (ok ? (uint32_t)wr[col][hch[e]] : 0u);
       qhi[e >> 1] |= bits << (16 * (e & 1));
     }
   }
@@ -312,14 +333,18 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 
     // keys: q' = q * s (fp16), bias = q . z
     uint32_t qs[16];
-    f4 cb = {0, 0, 0, 0};
+    // short independent MFMA accumulation chains (bias: 2 x 2 steps; each
+    // tile: 2 + 3 steps), summed at the end
+    f4 cb0 = {0, 0, 0, 0}, cb1 = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const u4 sv = ((const u4*)(sm + 16 * kq))[i];
       const u4 zv = ((const u4*)(sm + 64 + 16 * kq))[i];
 #pragma unroll
       for (int e = 0; e < 4; e++) qs[4 * i + e] = pk_mul(q16[4 * i + e], sv[e]);
-      cb = mma_f16(zv, u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]}, cb);
+      const u4 qb = u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
+      if (i & 1) cb1 = mma_f16(zv, qb, cb1);
+      else cb0 = mma_f16(zv, qb, cb0);
     }
     uint32_t qshi[4];
     if constexpr (HIMODE == 4) {
@@ -340,21 +365,21 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
     for (int TT = 0; TT < 2; TT++) {
       const u2 w = cur.klo[TT];
-      f4 acc = cb;
+      f4 acc[2] = {f4{0, 0, 0, 0}, f4{0, 0, 0, 0}};
 #pragma unroll
       for (int u = 0; u < 2; u++) {
         const uint32_t A = w[u] & 0x33333333u, Bn = (w[u] >> 2) & 0x33333333u;
         const int k0 = 8 * u;
-        acc = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
-                      u4{qs[k0], qs[k0 + 1], qs[k0 + 2], qs[k0 + 3]}, acc);
-        acc = mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)},
-                      u4{qs[k0 + 4], qs[k0 + 5], qs[k0 + 6], qs[k0 + 7]}, acc);
+        acc[u] = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
+                         u4{qs[k0], qs[k0 + 1], qs[k0 + 2], qs[k0 + 3]}, acc[u]);
+        acc[u] = mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)},
+                         u4{qs[k0 + 4], qs[k0 + 5], qs[k0 + 6], qs[k0 + 7]}, acc[u]);
       }
       if constexpr (HIMODE == 4) {
         const uint32_t wsel = (kq & 1) ? cur.khi[TT] >> 16 : cur.khi[TT];
         const uint32_t A = wsel & 0x33333333u, Bn = (wsel >> 2) & 0x33333333u;
-        acc = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
-                      u4{qshi[0], qshi[1], qshi[2], qshi[3]}, acc);
+        acc[1] = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
+                         u4{qshi[0], qshi[1], qshi[2], qshi[3]}, acc[1]);
       }
       if constexpr (HIMODE == 16) {
         const uint16_t* raw = (const uint16_t*)c.k_hi + rec * GS * g.nh + (16 * TT + col) * g.nh;
@@ -365,13 +390,15 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
           const uint32_t v = (kq < 2 && d < g.nh) ? raw[d] : 0u;
           a[e >> 1] |= v << (16 * (e & 1));
         }
-        acc = mma_raw<BF16>(u4{a[0], a[1], a[2], a[3]}, u4{qhi[0], qhi[1], qhi[2], qhi[3]}, acc);
+        acc[1] = mma_raw<BF16>(u4{a[0], a[1], a[2], a[3]}, u4{qhi[0], qhi[1], qhi[2], qhi[3]},
+                               acc[1]);
       }
-      C[TT] = acc;
+      C[TT] = acc[0] + acc[1];
     }
+    const f4 cb = cb0 + cb1;
     float x[8], p[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) x[i] = C[i >> 2][i & 3] * scale_log2;
+    for (int i = 0; i < 8; i++) x[i] = (C[i >> 2][i & 3] + cb[i & 3]) * scale_log2;
     softmax_step(x, p);
     const u4 P = u4{pk_rne(p[0], p[1]), pk_rne(p[2], p[3]), pk_rne(p[4], p[5]), pk_rne(p[6], p[7])};
     // values
@@ -390,11 +417,13 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     }
   };
 
-  for (int i = 0; i < nmine; i += PF) {
+  if constexpr (HASQ) {
+    for (int i = 0; i < nmine; i += PF) {
 #pragma unroll
-    for (int k = 0; k < PF; k++) {
-      if (i + k < nmine) process_group(pf[k], group_at(i + k));
-      load_group<HIMODE>(c, group_at(i + k + PF), lane, col, kq, pf[k]);
+      for (int k = 0; k < PF; k++) {
+        if (i + k < nmine) process_group(pf[k], group_at(i + k));
+        load_group<HIMODE>(c, group_at(i + k + PF), lane, col, kq, pf[k]);
+      }
     }
   }
 
@@ -405,14 +434,16 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     const int nvalid = min(GS, T - pbase);
     const int sb = (pbase / GS) % (g.RS / GS);
     const uint16_t* rk = (const uint16_t*)c.ring_k + ((size_t)bh * g.RS + sb * GS) * D;
-    uint32_t qraw[16] = {0};
-    if (hvalid) {
-      const u4* qp = (const u4*)&lds.u.loop.qraw[col][32 * kq];
+    uint32_t qraw[16];
+    {
+      // the group stream is done here: a fresh query read waits for nothing
+      const u4* qp =
+          (const u4*)(q + ((size_t)b * g.Hq + kh * G + min(col, G - 1)) * D + 32 * kq);
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const u4 v = qp[i];
 #pragma unroll
-        for (int e = 0; e < 4; e++) qraw[4 * i + e] = v[e];
+        for (int e = 0; e < 4; e++) qraw[4 * i + e] = hvalid ? v[e] : 0u;
       }
     }
     f4 C[2];
@@ -603,8 +634,14 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 template <bool BF16, int HIMODE>
 static void launch_one(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
                        const Ws& ws, void* out, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<BF16, HIMODE>), dim3(g.B * g.Hkv * S), dim3(WG_THREADS), 0,
-                     st, g, (const uint16_t*)q, *c, scale_log2, S, ws, (uint16_t*)out);
+  if (g.NG > 0)
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true>), dim3(g.B * g.Hkv * S),
+                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, ws,
+                       (uint16_t*)out);
+  else
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false>), dim3(g.B * g.Hkv * S),
+                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, ws,
+                       (uint16_t*)out);
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {
