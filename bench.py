@@ -28,6 +28,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
+# HBM bytes per launch of the decode kernel on the default workload, from the
+# FETCH_SIZE and WRITE_SIZE counters scaled by a plain copy; None when the
+# kernel has changed since they were read.
+TRAFFIC = 27595367
 
 
 def algorithmic_bytes(w, T: int) -> int:
@@ -63,15 +67,39 @@ def cache_ng(cache, w):
 
 
 def default_splits(w) -> int:
-    # about 4 waves per CU in flight: 256 CUs * 4 / (sequences * KV heads)
-    return max(1, min(1024, math.ceil(1024 / (w.batch * w.n_kv_heads))))
+    # one 8-wave workgroup per CU: 256 CUs / (sequences * KV heads)
+    return max(1, min(1024, math.ceil(256 / (w.batch * w.n_kv_heads))))
+
+
+SM_SCALE = 1.0 / math.sqrt(128.0)
+METRIC = "quantized-KV decode attn: \u00b5s/step, effective HBM GB/s, % of 8 TB/s peak"
+
+
+def dev(bits):
+    """uint16 bit array -> contiguous int16 tensor on the GPU."""
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def copy_calibration(mib: int, reps: int = 5):
+    """Plain device-to-device copies of `mib` MiB (read mib, write mib): the
+    reference dispatch for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * 2 ** 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "reps": reps}), flush=True)
 
 
 def cpu_baseline(w, data, min_s: float = 10.0):
     """The oracle's decode step (all query heads, unsplit fp64) timed on this
     host, single thread, repeated until about `min_s` seconds have passed."""
+    import numpy as np
     import oracle
-    from tests._gpu_case import SM_SCALE
     T = w.tokens
     _, pairs = oracle.select(data["q_sel"], data["k"], T, w.n_kv_heads, w.io_dtype)
     qz = oracle.quantize(data["k"], data["v"], T, pairs, residual=w.residual,
@@ -79,17 +107,17 @@ def cpu_baseline(w, data, min_s: float = 10.0):
     q = data["q_dec"][:, :, 0]
     n, t0 = 0, time.perf_counter()
     while True:
-        oracle.attention(qz, q, SM_SCALE)
+        oracle.attention(qz, q, float(np.float32(SM_SCALE)))
         n += 1
         el = time.perf_counter() - t0
         if el >= min_s:
             break
     per_step_s = el / n
-    return {"value": round(per_step_s * 1e6, 1), "unit": "us/step", "cores": 1,
-            "kind": "oracle",
-            "sample": "%d full decode steps (all %d query heads, %d tokens), fp64, 1 thread"
-                      % (n, w.batch * w.n_q_heads, T),
-            "gbs_equiv": round(algorithmic_bytes(w, T) / per_step_s / 1e9, 4)}
+    return {"value": round(algorithmic_bytes(w, T) / per_step_s / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": "%d full decode steps of the same workload (all %d query heads, %d "
+                      "tokens), fp64, 1 thread" % (n, w.batch * w.n_q_heads, T),
+            "us_per_step": round(per_step_s * 1e6, 1)}
 
 
 def main():
@@ -101,18 +129,22 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--replica-mib", type=int, default=512)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run the copy-kernel calibration of this size")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_mib:
+        copy_calibration(args.copy_mib)
+        return
 
     import numpy as np
     import torch
 
     import kvq_synth
     from decode_attention_select_amd import kvq
-    from tests._gpu_case import SM_SCALE, dev
 
     w = kvq_synth.workload(args.workload)
     S = args.splits or w.n_splits or default_splits(w)
@@ -142,8 +174,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(i):
-        kvq.kvq_decode_attn(layout, q, replicas[i % n_rep].struct, SM_SCALE, S, ws, out,
-                            stream=stream)
+        kvq.kvq_decode_attn(layout, q, replicas[i % n_rep].struct, float(np.float32(SM_SCALE)),
+                            S, ws, out, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -158,10 +190,21 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ev_ms = ev0.elapsed_time(ev1) / args.steps
 
+    # kernel duration alone: an event pair around every launch, same stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
     alg = algorithmic_bytes(w, T)
     gbs = alg / (ev_ms * 1e-3) / 1e9
+    kern_gbs = alg / (launch_ms * 1e-3) / 1e9
     res = {
-        "metric": "quantized-KV decode attn: us/step, effective HBM GB/s, % of 8 TB/s peak",
+        "metric": METRIC,
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -174,7 +217,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16-mfma/fp32-acc, bf16 io",
+        "dtype": "f16 (MFMA) / f32 accumulate",
         "data": "synthetic (seeded N(0,1) + outlier key pairs, RoPE)",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "context": T, "io_dtype": w.io_dtype,
@@ -182,8 +225,10 @@ def main():
                    "residual": w.residual, "n_splits": S, "cache_replicas": n_rep},
         "algorithmic_bytes_per_step": alg,
         "layout_bytes_per_step": layout_bytes(base, w, T),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4), "traffic": None},
+        "kernel_us_per_launch": round(launch_ms * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kern_gbs / PEAK_GBS, 4),
+                     "traffic": TRAFFIC},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, data)
