@@ -1,0 +1,150 @@
+"""The C ABI without a GPU: the built libkvq.so loads, exports every entry
+point include/kvq.h declares, reports buffer sizes by their closed forms and
+rejects bad arguments on the host before anything is enqueued.
+
+Validation cases pass stand-in device addresses that are never dereferenced:
+each call carries exactly one error, which the host checks must catch.  They
+are skipped where a GPU is present, so that a validation bug could never turn
+into a launch over those addresses."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from decode_attention_select_amd import kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, EINVAL, ENOTSUP, EALIGN, ECAPACITY = 0, -1, -2, -3, -4
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="host-validation cases run only where no GPU can be reached")
+
+
+def declared():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    return re.findall(r"^(?:kvq_status|const char \*)\s*\**(kvq_\w+)\s*\(", text, re.M)
+
+
+def test_library_exports_every_declared_entry_point():
+    names = declared()
+    assert set(names) >= {"kvq_select_pairs", "kvq_quant_keys", "kvq_quant_values",
+                          "kvq_append", "kvq_decode_attn", "kvq_cache_sizes",
+                          "kvq_workspace_bytes", "kvq_check", "kvq_status_str"}
+    lib = kvq.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in (OK, EINVAL, ENOTSUP, EALIGN, ECAPACITY, -5):
+        assert kvq.kvq_status_str(s) not in ("", "unknown status")
+    assert kvq.kvq_status_str(7) == "unknown status"
+
+
+def L32k(**kw):
+    args = dict(n_pairs_hi=6, bits_hi=4, residual=128, max_tokens=32768, io_dtype="bf16")
+    args.update(kw)
+    return kvq.make_layout(1, 32, 8, **args)
+
+
+def test_cache_sizes_closed_form():
+    # 32K layer: 1020 groups per KV head of 1024 + 128 + 512 + 1024 + 512 B
+    s = kvq.kvq_cache_sizes(L32k())
+    ng, bh = (32768 - 128) // 32, 8
+    assert s == [bh * ng * 1024, bh * ng * 128, bh * ng * 512, bh * ng * 1024, bh * ng * 512,
+                 bh * 160 * 256, bh * 160 * 256, bh * 64 * 4, bh * 4, bh * 2 * 64 * 8, 4]
+    # raw 16-bit salient channels: 32 tokens x 12 channels x 2 B per group
+    s16 = kvq.kvq_cache_sizes(L32k(bits_hi=16))
+    assert s16[1] == bh * ng * 32 * 12 * 2
+    # no salient pairs: no high-digit section; capacity inside the window: no groups
+    assert kvq.kvq_cache_sizes(L32k(n_pairs_hi=0))[1] == 0
+    assert kvq.kvq_cache_sizes(L32k(max_tokens=100))[0] == 0
+
+
+def status_of(name, *args):
+    return getattr(kvq.lib(), name)(*args)
+
+
+@pytest.mark.parametrize("bad,want", [
+    (dict(head_dim=64), EINVAL), (dict(group=16), EINVAL), (dict(n_pairs_hi=9), EINVAL),
+    (dict(bits_hi=8), ENOTSUP), (dict(n_pairs_lo1=4), ENOTSUP), (dict(bits_lo=3), ENOTSUP),
+    (dict(residual=48), EINVAL), (dict(residual=0), EINVAL), (dict(max_tokens=0), EINVAL),
+    (dict(io_dtype=5), EINVAL), (dict(n_q_heads=30), EINVAL), (dict(n_q_heads=8 * 17), ENOTSUP),
+    (dict(batch=0), EINVAL),
+])
+def test_layout_rejected(bad, want):
+    L = L32k()
+    for k, v in bad.items():
+        setattr(L, k, v)
+    sizes = (ctypes.c_size_t * kvq.NBUF)()
+    assert status_of("kvq_cache_sizes", ctypes.byref(L), sizes) == want
+    n = ctypes.c_size_t(0)
+    assert status_of("kvq_workspace_bytes", ctypes.byref(L), 4, ctypes.byref(n)) == want
+
+
+def test_workspace_bytes():
+    L = L32k()
+    assert kvq.kvq_workspace_bytes(L, 1) < kvq.kvq_workspace_bytes(L, 32)
+    rec = 32 * 32  # query heads x splits
+    want = (rec * 8 + 255) // 256 * 256 + (rec * 256 + 255) // 256 * 256 + 256
+    assert kvq.kvq_workspace_bytes(L, 32) == want
+    n = ctypes.c_size_t(0)
+    for S in (0, 1025, -1):
+        assert status_of("kvq_workspace_bytes", ctypes.byref(L), S, ctypes.byref(n)) == EINVAL
+
+
+FAKE = 1 << 20  # a 16-byte-aligned stand-in device address (never dereferenced)
+
+
+def fake_cache():
+    return kvq.kvq_cache(*[FAKE] * kvq.NBUF)
+
+
+@no_gpu
+def test_decode_validation():
+    L = L32k()
+    c = fake_cache()
+    ws = kvq.kvq_workspace_bytes(L, 8)
+    P = ctypes.c_void_p
+
+    def call(q=FAKE, scale=0.088, S=8, wsp=FAKE, wsb=ws, out=FAKE, cache=c):
+        return status_of("kvq_decode_attn", ctypes.byref(L), P(q), ctypes.byref(cache),
+                         ctypes.c_float(scale), S, P(wsp), ctypes.c_size_t(wsb), P(out), P(0))
+
+    assert call(q=0) == EINVAL
+    assert call(out=FAKE + 8) == EALIGN
+    assert call(wsp=0) == EINVAL
+    assert call(wsb=ws - 1) == ECAPACITY
+    assert call(scale=0.0) == EINVAL
+    assert call(scale=float("nan")) == EINVAL
+    assert call(S=0) == EINVAL
+    bad = fake_cache()
+    bad.v_meta = FAKE + 4
+    assert call(cache=bad) == EALIGN
+    bad = fake_cache()
+    bad.len = 0
+    assert call(cache=bad) == EINVAL
+
+
+@no_gpu
+def test_prefill_and_append_validation():
+    L = L32k()
+    c = fake_cache()
+    P = ctypes.c_void_p
+    sel = lambda n_qry=64, T=32768, q=FAKE, k=FAKE: status_of(
+        "kvq_select_pairs", ctypes.byref(L), P(q), n_qry, P(k), T, ctypes.byref(c), P(0))
+    assert sel(n_qry=0) == EINVAL
+    assert sel(n_qry=1025) == EINVAL
+    assert sel(T=0) == EINVAL
+    assert sel(T=32769) == ECAPACITY
+    assert sel(k=FAKE + 2) == EALIGN
+    for name in ("kvq_quant_keys", "kvq_quant_values"):
+        assert status_of(name, ctypes.byref(L), P(FAKE), 32769, ctypes.byref(c), P(0)) == ECAPACITY
+        assert status_of(name, ctypes.byref(L), P(FAKE), 0, ctypes.byref(c), P(0)) == EINVAL
+        assert status_of(name, ctypes.byref(L), P(0), 100, ctypes.byref(c), P(0)) == EINVAL
+    assert status_of("kvq_append", ctypes.byref(L), P(FAKE), P(0), ctypes.byref(c), P(0)) == EINVAL
+    assert status_of("kvq_append", ctypes.byref(L), P(FAKE + 1), P(FAKE), ctypes.byref(c),
+                     P(0)) == EALIGN
+    assert status_of("kvq_check", None, None, P(0)) == EINVAL

@@ -1,0 +1,111 @@
+"""GPU parity at the full sizes of the decode workloads, in the launch
+configuration the benchmark times:
+
+* the Llama-3-8B-shaped layer at 32K context (B1, 32 q / 8 kv heads, bf16):
+  selection, every cache byte and every output element against the oracle,
+  at the benchmark's split count;
+* the 128K-context layer (B1, 64 q / 8 kv heads, G = 8, 256 splits): every
+  cache byte; outputs of two sampled KV heads (16 query heads) against the
+  oracle, which computes those heads alone;
+* the streaming layer (B16, prefill 4096): 40 appends, which pack one group
+  per sequence and head, then every cache byte and every output element.
+
+Bars as in the small-case tests: bit-exact indices, sums, codes, scales,
+zero points and ring bytes; attention within 2e-3 (+ the rounding of the
+fp16 split record and of the 16-bit output)."""
+import numpy as np
+import pytest
+
+import bench
+import kvq_synth
+import oracle
+from tests._gpu_case import (SM_SCALE, Case, check_output, check_single_split, compare_cache,
+                              dev)
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+
+
+def kv_head_slice(qz, heads):
+    """The oracle's quantized cache restricted to some KV heads (a view for
+    computing only their query heads)."""
+    kw = dict(qz.__dict__)
+    for n in ("k", "v", "pairs", "kcodes", "ks", "kz", "vcodes", "vs", "vz"):
+        kw[n] = np.ascontiguousarray(getattr(qz, n)[:, heads])
+    return oracle.Quantized(**kw)
+
+
+def check_selection(case):
+    sums, pairs = case.oracle_select()
+    g = case.gpu_bytes()
+    assert np.array_equal(g["sums"], sums)
+    assert np.array_equal(g["pairs"], pairs)
+    return pairs
+
+
+@pytest.mark.timeout(400)
+def test_llama3_8b_32k_full():
+    w = kvq_synth.workload("llama3-8b-32k")
+    print("case", w.name, flush=True)
+    case = Case(w)
+    pairs = check_selection(case)
+    qz = case.oracle_quant(pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
+    q = case.d["q_dec"][:, :, 0]
+    ref = oracle.attention(qz, q, SM_SCALE)
+    S = bench.default_splits(w)
+    err = check_output(case.decode(q, S), ref, w.io_dtype, ATOL)
+    _, part = case.decode(q, 1, partials=True)
+    e32 = check_single_split(part, ref, ATOL)
+    print("%s S=%d max|err| %.3g max|o| %.3g split-record max|err| %.3g"
+          % (w.name, S, err, np.abs(ref).max(), e32))
+
+
+@pytest.mark.timeout(600)
+def test_long_128k_sampled_heads():
+    w = kvq_synth.workload("long-128k")
+    print("case", w.name, flush=True)
+    case = Case(w)
+    pairs = check_selection(case)
+    qz = case.oracle_quant(pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
+    q = case.d["q_dec"][:, :, 0]
+    got = case.decode(q, w.n_splits)
+    G = w.group_size
+    heads = [0, w.n_kv_heads - 1]
+    qh = [kh * G + i for kh in heads for i in range(G)]
+    ref = oracle.attention(kv_head_slice(qz, heads), np.ascontiguousarray(q[:, qh]), SM_SCALE)
+    err = check_output(got[:, qh], ref, w.io_dtype, ATOL)
+    _, (ml, o16) = case.decode(q, 1, partials=True)
+    e32 = check_single_split((ml[:, qh], o16[:, qh]), ref, ATOL)
+    print("%s S=%d heads %s max|err| %.3g max|o| %.3g split-record max|err| %.3g"
+          % (w.name, w.n_splits, qh, err, np.abs(ref).max(), e32))
+
+
+@pytest.mark.timeout(600)
+def test_streaming_b16_appends():
+    from decode_attention_select_amd import kvq
+    w = kvq_synth.workload("streaming-b16")
+    print("case", w.name, flush=True)
+    n_app = 40
+    case = Case(w, T=w.tokens, max_tokens=w.max_tokens)
+    pairs = check_selection(case)
+    kn = dev(np.ascontiguousarray(case.d["k"][:, :, w.tokens:w.tokens + n_app]))
+    vn = dev(np.ascontiguousarray(case.d["v"][:, :, w.tokens:w.tokens + n_app]))
+    for i in range(n_app):
+        kvq.kvq_append(case.layout, kn[:, :, i].contiguous(), vn[:, :, i].contiguous(),
+                       case.cache.struct)
+    assert kvq.kvq_check(case.cache.struct) == 0
+    T = w.tokens + n_app
+    assert oracle.n_quant(T, w.residual) > oracle.n_quant(w.tokens, w.residual)
+    qz = case.oracle_quant(T=T, pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
+    q = np.ascontiguousarray(case.d["q_dec"][:, :, n_app - 1])
+    ref = oracle.attention(qz, q, SM_SCALE)
+    S = bench.default_splits(w)
+    err = check_output(case.decode(q, S), ref, w.io_dtype, ATOL)
+    _, part = case.decode(q, 1, partials=True)
+    e32 = check_single_split(part, ref, ATOL)
+    print("%s T=%d S=%d max|err| %.3g max|o| %.3g split-record max|err| %.3g"
+          % (w.name, T, S, err, np.abs(ref).max(), e32))
