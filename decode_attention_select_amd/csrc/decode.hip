@@ -47,7 +47,7 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 constexpr int NW = 8;                  // waves per workgroup (one workgroup per CU)
 constexpr int WG_THREADS = 64 * NW;
-constexpr int PF = 4;                  // quantized groups in flight per wave
+constexpr int PF = 2;                  // quantized groups in flight per wave
 constexpr int MAXG = 16;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 headroom before the running max moves
 
@@ -57,6 +57,11 @@ __device__ inline uint32_t pk_mul(uint32_t a, uint32_t b) { return h2u(u2h(a) * 
 // fp32 pair -> fp16 pair, round to nearest even (v_cvt_pk_f16_f32)
 __device__ inline uint32_t pk_rne(float a, float b) { return h2u(h2{(_Float16)a, (_Float16)b}); }
 __device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer descriptor word 3 for raw byte-addressed buffers (gfx9 family), and
+// the cache-policy bit that makes a buffer access device-coherent (sc1).
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+constexpr int CPOL_SC1 = 16;
 
 // 16-bit input pair -> fp16 pair (bf16 widened exactly, then RNE to fp16)
 template <bool BF16>
@@ -506,38 +511,39 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     }
   }
   __syncthreads();
-  // split record: (m, l) and o / l in fp16; thread -> (head, 4 channels)
-  const size_t rbase = ((size_t)bh * S + s) * G;
-  for (int i = tid; i < G * (D / 4); i += WG_THREADS) {
-    const int h = i / (D / 4), c4 = 4 * (i % (D / 4));
+  // split record: (m, l) and o / l in fp16; thread -> (head, 8 channels).
+  // Records cross workgroups (and L2 slices): every access to them is
+  // device-coherent (sc1), so no cache-wide writeback or invalidate is needed.
+  const size_t rbh = (size_t)bh * S * G;  // first record of this (sequence, KV head)
+  const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
+      ws.o + rbh * D, 0, (int)(S * G * D * 2), BUF_RSRC_WORD3);
+  for (int i = tid; i < G * (D / 8); i += WG_THREADS) {
+    const int h = i / (D / 8), c8 = 8 * (i % (D / 8));
     float M = lds.u.merge.m[0][h];
 #pragma unroll
     for (int w = 1; w < NW; w++) M = fmaxf(M, lds.u.merge.m[w][h]);
-    f4 o = {0, 0, 0, 0};
+    f4 oa = {0, 0, 0, 0}, ob = {0, 0, 0, 0};
     float l = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; w++) {
       const float mw = lds.u.merge.m[w][h];
       const float a = mw == -INFINITY ? 0.0f : ex2(mw - M);
-      o += a * *(const f4*)&lds.u.merge.o[w][h][c4];
+      oa += a * *(const f4*)&lds.u.merge.o[w][h][c8];
+      ob += a * *(const f4*)&lds.u.merge.o[w][h][c8 + 4];
       l += a * lds.u.merge.l[w][h];
     }
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    // records cross workgroups (and L2 slices): coherent (sc1) stores
-    const uint64_t ov = (uint64_t)pk_rne(o[0] * inv, o[1] * inv) |
-                        ((uint64_t)pk_rne(o[2] * inv, o[3] * inv) << 32);
-    __hip_atomic_store((uint64_t*)(ws.o + (rbase + h) * D + c4), ov, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    if (c4 == 0)
-      __hip_atomic_store((uint64_t*)&ws.ml[rbase + h],
+    const u4 ov = u4{pk_rne(oa[0] * inv, oa[1] * inv), pk_rne(oa[2] * inv, oa[3] * inv),
+                     pk_rne(ob[0] * inv, ob[1] * inv), pk_rne(ob[2] * inv, ob[3] * inv)};
+    __builtin_amdgcn_raw_buffer_store_b128(ov, rs_o, (int)(((s * G + h) * D + c8) * 2), 0, CPOL_SC1);
+    if (c8 == 0)
+      __hip_atomic_store((uint64_t*)&ws.ml[rbh + (size_t)s * G + h],
                          (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(l) << 32),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- the last workgroup of this (sequence, KV head) merges all splits.
-  // Every record store has completed (s_waitcnt) before the counter moves,
-  // and the merging workgroup reads with coherent loads: no cache-wide
-  // writeback or invalidate is needed.
+  // Every record store has completed (s_waitcnt) before the counter moves.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
@@ -547,36 +553,31 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   }
   __syncthreads();
   if (!lds.last) return;
-  // item = (head, 8 channels); nsub lanes (a power of two <= 32) share an
-  // item's splits and reduce with shuffles
+  // item = (head, 8 channels); nsub lanes (a power of two, within one wave)
+  // share an item's splits, each loading up to 8 records at once, and
+  // reduce with shuffles
   const int items = G * (D / 8);
   int nsub = 1;
-  while (nsub < 32 && items * nsub * 2 <= WG_THREADS) nsub *= 2;
-  const uint64_t* mlb = (const uint64_t*)(ws.ml + (size_t)bh * S * G);
-  const uint64_t* ob = (const uint64_t*)(ws.o + (size_t)bh * S * G * D);
-  auto ld = [](const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  for (int base = 0; base < items * nsub; base += WG_THREADS) {
-    const int t = base + tid;
+  while (nsub < 64 && items * nsub * 2 <= WG_THREADS) nsub *= 2;
+  const uint64_t* mlb = (const uint64_t*)(ws.ml + rbh);
+  {
+    const int t = tid;
     const int item = t / nsub, sub = t % nsub;
     const bool act = item < items;
     const int h = act ? item / (D / 8) : 0, c8 = act ? 8 * (item % (D / 8)) : 0;
-    // one pass: up to 4 of this lane's splits are loaded at once and folded
-    // in with a running max (rescaling when it rises)
     float M = -INFINITY, L = 0.0f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i0 = sub; act && i0 < S; i0 += 4 * nsub) {
-      uint64_t mlw[4], o0[4], o1[4];
+    for (int i0 = sub; act && i0 < S; i0 += 8 * nsub) {
+      uint64_t mlw[8];
+      u4 ov[8];
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
+      for (int k = 0; k < 8; k++) {
         const int i = min(i0 + k * nsub, S - 1);
-        const uint64_t* op = ob + (((size_t)i * G + h) * D + c8) / 4;
-        mlw[k] = ld(mlb + (size_t)i * G + h);
-        o0[k] = ld(op);
-        o1[k] = ld(op + 1);
+        mlw[k] = __hip_atomic_load(mlb + (size_t)i * G + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ov[k] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, (int)(((i * G + h) * D + c8) * 2), 0,
+                                                      CPOL_SC1);
       }
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
+      for (int k = 0; k < 8; k++) {
         const float m = __uint_as_float((uint32_t)mlw[k]);
         const float l = __uint_as_float((uint32_t)(mlw[k] >> 32));
         if (i0 + k * nsub >= S || m == -INFINITY) continue;
@@ -589,11 +590,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         }
         const float wgt = ex2(m - M) * l;
         L += wgt;
-        const u4 ov = u4{(uint32_t)o0[k], (uint32_t)(o0[k] >> 32), (uint32_t)o1[k],
-                         (uint32_t)(o1[k] >> 32)};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          const h2 v = u2h(ov[e]);
+          const h2 v = u2h(ov[k][e]);
           acc[2 * e] += wgt * (float)v[0];
           acc[2 * e + 1] += wgt * (float)v[1];
         }

@@ -74,8 +74,9 @@ WORKLOADS = [
              outliers="pairs4x8", n_pairs_hi=6, residual=128, seed=1002),
     Workload("pareto-b4-16k", 4, 32, 8, 16384, outliers="pct2x10",
              n_pairs_hi=6, residual=128, seed=1003),
+    # 256 token partitions in all: 32 per KV head, one workgroup per CU
     Workload("long-128k", 1, 64, 8, 131072, outliers="pairs4x8",
-             n_pairs_hi=6, residual=128, n_splits=256, seed=1004),
+             n_pairs_hi=6, residual=128, n_splits=32, seed=1004),
 ]
 
 # Key bit points of the Pareto sweep: (label, n_pairs_hi, bits_hi).
