@@ -202,7 +202,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
                                                             kvq_cache c, float scale_log2, int S,
                                                             Ws ws, uint16_t* __restrict__ out) {
   __shared__ Lds lds;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is wave-uniform: keeping it in a scalar register makes every
+  // group address scalar (one 64-bit base per load, no per-lane address math)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
   const int bh = blockIdx.x / S, s = blockIdx.x % S;
   const int b = bh / g.Hkv, kh = bh % g.Hkv;
@@ -305,12 +307,12 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   for (int t = 0; t < 8; t++) O[t] = f4{0, 0, 0, 0};
   const uint32_t ONES = 0x3c003c00u;  // fp16 (1, 1)
 
-  // online-softmax step on this block's 8 logits per lane (x in log2 units)
-  auto softmax_step = [&](float (&x)[8], float (&p)[8]) {
-    float mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; i++) mx = fmaxf(mx, x[i]);
-    mx = wave_max_kq(mx);
+  // online-softmax step on this block's 8 logits per lane, given unscaled as
+  // c (the log2-unit logit is sc * c with sc > 0, so max c gives max x)
+  auto softmax_step = [&](const float (&c)[8], float sc, float (&p)[8]) {
+    const float mc = fmaxf(fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])),
+                           fmaxf(fmaxf(c[4], c[5]), fmaxf(c[6], c[7])));
+    const float mx = wave_max_kq(mc) * sc;
     const bool need = mx > m_run + RESCALE_SLACK;
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float m_new = need ? mx : m_run;
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       m_run = m_new;
     }
 #pragma unroll
-    for (int i = 0; i < 8; i++) p[i] = ex2(x[i] - m_run);
+    for (int i = 0; i < 8; i++) p[i] = ex2(fmaf(c[i], sc, -m_run));
   };
 
   uint32_t* sm = lds.u.loop.stage[wave];
@@ -336,11 +338,10 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
 
-    // keys: q' = q * s (fp16), bias = q . z
+    // keys: q' = q * s (fp16), bias = q . z (the same for every token row);
+    // each tile's accumulator starts from the bias, so no VALU adds follow
     uint32_t qs[16];
-    // short independent MFMA accumulation chains (bias: 2 x 2 steps; each
-    // tile: 2 + 3 steps), summed at the end
-    f4 cb0 = {0, 0, 0, 0}, cb1 = {0, 0, 0, 0};
+    f4 cb = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const u4 sv = ((const u4*)(sm + 16 * kq))[i];
@@ -348,8 +349,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
       for (int e = 0; e < 4; e++) qs[4 * i + e] = pk_mul(q16[4 * i + e], sv[e]);
       const u4 qb = u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
-      if (i & 1) cb1 = mma_f16(zv, qb, cb1);
-      else cb0 = mma_f16(zv, qb, cb0);
+      cb = mma_f16(zv, qb, cb);
     }
     uint32_t qshi[4];
     if constexpr (HIMODE == 4) {
@@ -370,21 +370,21 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
     for (int TT = 0; TT < 2; TT++) {
       const u2 w = cur.klo[TT];
-      f4 acc[2] = {f4{0, 0, 0, 0}, f4{0, 0, 0, 0}};
+      f4 acc = cb;
 #pragma unroll
       for (int u = 0; u < 2; u++) {
         const uint32_t A = w[u] & 0x33333333u, Bn = (w[u] >> 2) & 0x33333333u;
         const int k0 = 8 * u;
-        acc[u] = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
-                         u4{qs[k0], qs[k0 + 1], qs[k0 + 2], qs[k0 + 3]}, acc[u]);
-        acc[u] = mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)},
-                         u4{qs[k0 + 4], qs[k0 + 5], qs[k0 + 6], qs[k0 + 7]}, acc[u]);
+        acc = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
+                      u4{qs[k0], qs[k0 + 1], qs[k0 + 2], qs[k0 + 3]}, acc);
+        acc = mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)},
+                      u4{qs[k0 + 4], qs[k0 + 5], qs[k0 + 6], qs[k0 + 7]}, acc);
       }
       if constexpr (HIMODE == 4) {
         const uint32_t wsel = (kq & 1) ? cur.khi[TT] >> 16 : cur.khi[TT];
         const uint32_t A = wsel & 0x33333333u, Bn = (wsel >> 2) & 0x33333333u;
-        acc[1] = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
-                         u4{qshi[0], qshi[1], qshi[2], qshi[3]}, acc[1]);
+        acc = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
+                      u4{qshi[0], qshi[1], qshi[2], qshi[3]}, acc);
       }
       if constexpr (HIMODE == 16) {
         const uint16_t* raw = (const uint16_t*)c.k_hi + rec * GS * g.nh + (16 * TT + col) * g.nh;
@@ -395,16 +395,14 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
           const uint32_t v = (kq < 2 && d < g.nh) ? raw[d] : 0u;
           a[e >> 1] |= v << (16 * (e & 1));
         }
-        acc[1] = mma_raw<BF16>(u4{a[0], a[1], a[2], a[3]}, u4{qhi[0], qhi[1], qhi[2], qhi[3]},
-                               acc[1]);
+        acc = mma_raw<BF16>(u4{a[0], a[1], a[2], a[3]}, u4{qhi[0], qhi[1], qhi[2], qhi[3]}, acc);
       }
-      C[TT] = acc[0] + acc[1];
+      C[TT] = acc;
     }
-    const f4 cb = cb0 + cb1;
-    float x[8], p[8];
+    float cr[8], p[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) x[i] = (C[i >> 2][i & 3] + cb[i & 3]) * scale_log2;
-    softmax_step(x, p);
+    for (int i = 0; i < 8; i++) cr[i] = C[i >> 2][i & 3];
+    softmax_step(cr, scale_log2, p);
     const u4 P = u4{pk_rne(p[0], p[1]), pk_rne(p[2], p[3]), pk_rne(p[4], p[5]), pk_rne(p[6], p[7])};
     // values
     const u4 za = col < 4 ? ((const u4*)(sm + 192 + 16 * col))[kq]
@@ -463,13 +461,13 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
                             acc);
       C[TT] = acc;
     }
-    float x[8], p[8];
+    float cr[8], p[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const int t = 8 * kq + 4 * (i >> 2) + (i & 3);
-      x[i] = t < nvalid ? C[i >> 2][i & 3] * scale_log2 : -INFINITY;
+      cr[i] = t < nvalid ? C[i >> 2][i & 3] : -INFINITY;
     }
-    softmax_step(x, p);
+    softmax_step(cr, scale_log2, p);
 #pragma unroll
     for (int i = 0; i < 8; i++) l_raw += p[i];
     uint32_t Ph[4], Pl[4];
