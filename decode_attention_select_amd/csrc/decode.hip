@@ -309,12 +309,15 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 
   // online-softmax step on this block's 8 logits per lane, given unscaled as
   // c (the log2-unit logit is sc * c with sc > 0, so max c gives max x)
+  // The running max moves only when some logit exceeds it by more than the
+  // slack: a per-lane test and a ballot decide that; the cross-lane max is
+  // taken only then.
   auto softmax_step = [&](const float (&c)[8], float sc, float (&p)[8]) {
     const float mc = fmaxf(fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])),
                            fmaxf(fmaxf(c[4], c[5]), fmaxf(c[6], c[7])));
-    const float mx = wave_max_kq(mc) * sc;
-    const bool need = mx > m_run + RESCALE_SLACK;
-    if (__builtin_amdgcn_ballot_w64(need)) {
+    if (__builtin_amdgcn_ballot_w64(mc * sc > m_run + RESCALE_SLACK)) {
+      const float mx = wave_max_kq(mc) * sc;
+      const bool need = mx > m_run + RESCALE_SLACK;
       const float m_new = need ? mx : m_run;
       const float alpha = ex2(m_run - m_new);
 #pragma unroll
