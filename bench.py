@@ -120,6 +120,118 @@ def cpu_baseline(w, data, min_s: float = 10.0):
             "us_per_step": round(per_step_s * 1e6, 1)}
 
 
+def streaming_leg(args, w):
+    """Long-output decoding: after a prefill of w.tokens tokens, every step
+    appends one token per (sequence, KV head) with kvq_append and then decodes
+    the next query with kvq_decode_attn, for w.n_app steps.  NL independent
+    layer caches (together >= --replica-mib) are stepped in turn, as the
+    layers of a model are, so the 256 MB Infinity Cache cannot hold the
+    working set.  Two timed passes over the same sequence from the same
+    prefilled state: append + decode, then append alone."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import kvq_synth
+    from decode_attention_select_amd import kvq
+
+    T0, n = w.tokens, w.n_app
+    data = kvq_synth.generate(w)
+    layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads, n_pairs_hi=w.n_pairs_hi,
+                             bits_hi=w.bits_hi, residual=w.residual, max_tokens=T0 + n,
+                             io_dtype=w.io_dtype)
+    pristine = kvq.Cache(layout)
+    kvq.kvq_select_pairs(layout, dev(data["q_sel"]), w.n_qry, dev(data["k"][:, :, :T0]), T0,
+                         pristine.struct)
+    kvq.kvq_quant_keys(layout, dev(data["k"][:, :, :T0]), T0, pristine.struct)
+    kvq.kvq_quant_values(layout, dev(data["v"][:, :, :T0]), T0, pristine.struct)
+    torch.cuda.synchronize()
+    NL = max(1, math.ceil(args.replica_mib * 2 ** 20 / pristine.nbytes()))
+    layers = []
+    for _ in range(NL):
+        c = kvq.Cache.__new__(kvq.Cache)
+        c.layout, c.sizes = pristine.layout, pristine.sizes
+        c.bufs = {k: v.clone() for k, v in pristine.bufs.items()}
+        c.struct = kvq.kvq_cache(*[c.bufs[nm].data_ptr() for nm in kvq.BUF_NAMES])
+        layers.append(c)
+    kn = [dev(np.ascontiguousarray(data["k"][:, :, T0 + i])) for i in range(n)]
+    vn = [dev(np.ascontiguousarray(data["v"][:, :, T0 + i])) for i in range(n)]
+    qd = [dev(np.ascontiguousarray(data["q_dec"][:, :, i])) for i in range(n)]
+    S = args.splits or w.n_splits or default_splits(w)
+    ws = torch.zeros(kvq.kvq_workspace_bytes(layout, S), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    lib = kvq.lib()
+    L, st = ctypes.byref(layout), ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.c_void_p
+    scale = ctypes.c_float(float(np.float32(SM_SCALE)))
+    wsb = ctypes.c_size_t(ws.numel())
+    app_args = [(P(kn[i].data_ptr()), P(vn[i].data_ptr())) for i in range(n)]
+    dec_args = [P(qd[i].data_ptr()) for i in range(n)]
+    structs = [ctypes.byref(c.struct) for c in layers]
+
+    def restore():
+        torch.cuda.synchronize()
+        for c in layers:
+            for k, v in c.bufs.items():
+                v.copy_(pristine.bufs[k])
+        torch.cuda.synchronize()
+
+    def run(decode):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(n):
+            a, b = app_args[i]
+            for cs in structs:
+                assert lib.kvq_append(L, a, b, cs, st) == 0
+                if decode:
+                    assert lib.kvq_decode_attn(L, dec_args[i], cs, scale, S, P(ws.data_ptr()), wsb,
+                                               P(out.data_ptr()), st) == 0
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / (n * NL)
+
+    # warm-up: decodes leave the caches unchanged
+    for i in range(args.warmup):
+        assert lib.kvq_decode_attn(L, dec_args[0], structs[0], scale, S, P(ws.data_ptr()), wsb,
+                                   P(out.data_ptr()), st) == 0
+    step_us = run(True)
+    for c in layers:
+        assert kvq.kvq_check(c.struct) == 0
+    restore()
+    append_us = run(False)
+    decode_us = step_us - append_us
+    alg = sum(algorithmic_bytes(w, T0 + i + 1) for i in range(n)) / n
+    gbs = alg / (decode_us * 1e-6) / 1e9
+    return {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us * 1e-3, 5),
+        "us_per_step": round(step_us, 3),
+        "append_us_per_step": round(append_us, 3),
+        "decode_us_per_step": round(decode_us, 3),
+        "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 (MFMA) / f32 accumulate",
+        "data": "synthetic (seeded N(0,1) + outlier key pairs, RoPE)",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "prefill": T0, "appended": n,
+                   "io_dtype": w.io_dtype, "salient_pairs": w.n_pairs_hi,
+                   "salient_bits": w.bits_hi, "residual": w.residual, "n_splits": S,
+                   "layer_caches": NL},
+        "algorithmic_bytes_per_step": int(alg),
+        "note": "one step = kvq_append + kvq_decode_attn on one layer cache; value = "
+                "decode bytes / (step time - append time)",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +259,9 @@ def main():
     from decode_attention_select_amd import kvq
 
     w = kvq_synth.workload(args.workload)
+    if w.n_app:
+        print(json.dumps(streaming_leg(args, w)), flush=True)
+        return
     S = args.splits or w.n_splits or default_splits(w)
     T = w.tokens
     data = kvq_synth.generate(w)
