@@ -48,6 +48,7 @@ class Workload:
     outliers: str = "pairs4x8"
     n_pairs_hi: int = 6
     bits_hi: int = 4
+    n_pairs_lo1: int = 0     # lowest-ranked pairs kept at 1 bit
     residual: int = 128
     n_splits: int = 0        # 0 = library default
     seed: int = 0

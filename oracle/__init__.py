@@ -127,7 +127,8 @@ class Quantized:
 
 
 def quantize(k, v, T: int, pairs, *, residual: int, n_pairs_hi: int,
-             bits_hi: int, io_dtype: str, ng: int | None = None) -> Quantized:
+             bits_hi: int, io_dtype: str, ng: int | None = None,
+             n_pairs_lo1: int = 0) -> Quantized:
     """Quantize keys and values of the first T tokens (k, v
     [B][Hkv][Tstride][128] bits) with the given rank table."""
     lib = _load()
@@ -145,13 +146,14 @@ def quantize(k, v, T: int, pairs, *, residual: int, n_pairs_hi: int,
     vz = np.zeros((B, Hkv, NG, GS, 4), np.uint16)
     rc = lib.orc_quant_keys(B, Hkv, _bf(io_dtype), _p(k), Tstride, int(T),
                             int(residual), int(n_pairs_hi), int(bits_hi),
-                            _p(pairs), NG, _p(kc), _p(ks), _p(kz))
+                            int(n_pairs_lo1), _p(pairs), NG, _p(kc), _p(ks), _p(kz))
     assert rc == 0
     rc = lib.orc_quant_values(B, Hkv, _bf(io_dtype), _p(v), Tstride, int(T),
                               int(residual), 2, NG, _p(vc), _p(vs), _p(vz))
     assert rc == 0
     return Quantized(k=k, v=v, T=int(T), R=int(residual), n_hi=int(n_pairs_hi),
-                     bits_hi=int(bits_hi), io_dtype=io_dtype, pairs=pairs,
+                     bits_hi=int(bits_hi), n_lo1=int(n_pairs_lo1), io_dtype=io_dtype,
+                     pairs=pairs,
                      NG=NG, nq=nq, kcodes=kc, ks=ks, kz=kz, vcodes=vc, vs=vs,
                      vz=vz)
 
@@ -166,7 +168,7 @@ def attention(qz: Quantized, q, sm_scale: float, with_lse: bool = False):
     lse = np.zeros((B, Hq), np.float64)
     rc = _load().orc_attention(
         B, Hq, Hkv, _bf(qz.io_dtype), _p(q), _p(qz.k), _p(qz.v), qz.k.shape[2],
-        qz.T, qz.R, qz.n_hi, qz.bits_hi, _p(qz.pairs), qz.NG, _p(qz.kcodes),
+        qz.T, qz.R, qz.n_hi, qz.bits_hi, qz.n_lo1, _p(qz.pairs), qz.NG, _p(qz.kcodes),
         _p(qz.ks), _p(qz.kz), _p(qz.vcodes), _p(qz.vs), _p(qz.vz),
         ctypes.c_double(float(np.float32(sm_scale))), _p(out), _p(lse))
     assert rc == 0
@@ -195,7 +197,7 @@ def pack(qz: Quantized) -> dict:
     ring_k = np.zeros((B, Hkv, RS, D), np.uint16)
     ring_v = np.zeros((B, Hkv, RS // GS, D, GS), np.uint16)
     lib.orc_pack_keys(B, Hkv, _p(qz.k), Tstride, qz.T, qz.R, qz.n_hi,
-                      qz.bits_hi, _p(qz.pairs), NG, _p(qz.kcodes), _p(qz.ks),
+                      qz.bits_hi, qz.n_lo1, _p(qz.pairs), NG, _p(qz.kcodes), _p(qz.ks),
                       _p(qz.kz), _p(k_lo), _p(k_hi), _p(k_meta))
     lib.orc_pack_values(B, Hkv, qz.T, qz.R, NG, _p(qz.vcodes), _p(qz.vs),
                         _p(qz.vz), _p(v_codes), _p(v_meta))

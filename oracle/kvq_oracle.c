@@ -142,13 +142,25 @@ int orc_select(int B, int Hq, int Hkv, int bf16, const uint16_t *q_sel,
   return 0;
 }
 
-/* Bits of channel c given the rank table of its (b, kv head). */
-int orc_channel_bits(const int32_t *pr, int n_hi, int bits_hi, int bits_lo,
-                     int c) {
+/* Bits of channel c given the rank table of its (b, kv head): the pairs of
+ * the n_hi highest ranks at bits_hi, those of the n_lo1 lowest ranks at one
+ * bit, all others at bits_lo (PN-Mix, abstract: more bits for the salient
+ * pairs; the 1-bit share is the reading that gives a 1.5-bit average). */
+int orc_channel_bits(const int32_t *pr, int n_hi, int bits_hi, int n_lo1,
+                     int bits_lo, int c) {
   int j = c % NPAIR;
   for (int r = 0; r < n_hi; r++)
     if (pr[r] == j) return bits_hi;
+  for (int r = NPAIR - n_lo1; r < NPAIR; r++)
+    if (pr[r] == j) return 1;
   return bits_lo;
+}
+
+/* Channel c belongs to one of the n_hi top-ranked (salient) pairs. */
+static int orc_is_salient(const int32_t *pr, int n_hi, int c) {
+  for (int r = 0; r < n_hi; r++)
+    if (pr[r] == c % NPAIR) return 1;
+  return 0;
 }
 
 /* ------------------------------------------------------------- quantizer */
@@ -195,7 +207,7 @@ int orc_n_quant(int T, int R) {
  * bits.  16-bit channels get s = z = 0 and codes 0.  Fills groups
  * [0, n_q(T)/32). */
 int orc_quant_keys(int B, int Hkv, int bf16, const uint16_t *k, int Tstride,
-                   int T, int R, int n_hi, int bits_hi, const int32_t *pairs,
+                   int T, int R, int n_hi, int bits_hi, int n_lo1, const int32_t *pairs,
                    int NG, uint8_t *codes, uint16_t *s, uint16_t *z) {
   int ng = orc_n_quant(T, R) / GS;
   if (ng > NG) return -1;
@@ -206,7 +218,7 @@ int orc_quant_keys(int B, int Hkv, int bf16, const uint16_t *k, int Tstride,
       for (int g = 0; g < ng; g++)
         for (int c = 0; c < D; c++) {
           size_t slot = ((size_t)(b * Hkv + kh) * NG + g) * D + c;
-          int bits = orc_channel_bits(pr, n_hi, bits_hi, 2, c);
+          int bits = orc_channel_bits(pr, n_hi, bits_hi, n_lo1, 2, c);
           if (bits == 16) {
             memset(codes + slot * GS, 0, GS);
             s[slot] = z[slot] = 0;
@@ -251,7 +263,7 @@ int orc_quant_values(int B, int Hkv, int bf16, const uint16_t *v, int Tstride,
  * denominator of the scaled logits, for split checks). */
 int orc_attention(int B, int Hq, int Hkv, int bf16, const uint16_t *q,
                   const uint16_t *k, const uint16_t *v, int Tstride, int T,
-                  int R, int n_hi, int bits_hi, const int32_t *pairs, int NG,
+                  int R, int n_hi, int bits_hi, int n_lo1, const int32_t *pairs, int NG,
                   const uint8_t *kcodes, const uint16_t *ks, const uint16_t *kz,
                   const uint8_t *vcodes, const uint16_t *vs, const uint16_t *vz,
                   double sm_scale, double *out, double *lse) {
@@ -272,7 +284,7 @@ int orc_attention(int B, int Hq, int Hkv, int bf16, const uint16_t *q,
       for (int t = 0; t < T; t++) {
         const uint16_t *raw = k + (((size_t)b * Hkv + kh) * Tstride + t) * D;
         for (int c = 0; c < D; c++) {
-          int bits = orc_channel_bits(pr, n_hi, bits_hi, 2, c);
+          int bits = orc_channel_bits(pr, n_hi, bits_hi, n_lo1, 2, c);
           if (t >= nq || bits == 16) {
             kh_row[c] = to_f64(raw[c], bf16);
           } else {
@@ -328,7 +340,7 @@ static int pos_swap(int c) { return (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1); 
  * k_lo [..][NG][256] u32, k_hi (4-bit: [..][NG][32] u32; 16-bit:
  * [..][NG][32][2*n_hi] u16 raw), k_meta [..][NG][2][128] u16. */
 int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
-                  int n_hi, int bits_hi, const int32_t *pairs, int NG,
+                  int n_hi, int bits_hi, int n_lo1, const int32_t *pairs, int NG,
                   const uint8_t *codes, const uint16_t *s, const uint16_t *z,
                   uint32_t *k_lo, void *k_hi, uint16_t *k_meta) {
   int ng = orc_n_quant(T, R) / GS;
@@ -337,7 +349,7 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
       const int32_t *pr = pairs + (size_t)(b * Hkv + kh) * NPAIR;
       int hil[16], nh = 0; /* salient channels, ascending */
       for (int c = 0; c < D; c++)
-        if (orc_channel_bits(pr, n_hi, bits_hi, 2, c) != 2) hil[nh++] = c;
+        if (orc_is_salient(pr, n_hi, c)) hil[nh++] = c;
       for (int g = 0; g < ng; g++) {
         size_t grp = (size_t)(b * Hkv + kh) * NG + g;
         const uint8_t *cg = codes + grp * D * GS;
@@ -347,7 +359,7 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
           int t = tile_token(e), Tt = e / 16, r = e % 16;
           for (int c = 0; c < D; c++) {
             int w = c / 16, kq = w / 2, u = w % 2;
-            int bits = orc_channel_bits(pr, n_hi, bits_hi, 2, c);
+            int bits = orc_channel_bits(pr, n_hi, bits_hi, n_lo1, 2, c);
             uint32_t digit = bits == 16 ? 0u : (uint32_t)(cg[c * GS + t] & 3);
             size_t word = ((size_t)(Tt * 4 + kq) * 16 + r) * 2 + u;
             lo[word] |= digit << (2 * pos_swap(c % 16));

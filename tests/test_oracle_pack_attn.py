@@ -15,7 +15,8 @@ def _setup(w, T=None):
     T = w.tokens if T is None else T
     _, pairs = oracle.select(d["q_sel"], d["k"], w.tokens, w.n_kv_heads, w.io_dtype)
     qz = oracle.quantize(d["k"], d["v"], T, pairs, residual=w.residual,
-                         n_pairs_hi=w.n_pairs_hi, bits_hi=w.bits_hi, io_dtype=w.io_dtype)
+                         n_pairs_hi=w.n_pairs_hi, bits_hi=w.bits_hi, io_dtype=w.io_dtype,
+                         n_pairs_lo1=w.n_pairs_lo1)
     return d, pairs, qz
 
 
@@ -31,6 +32,12 @@ VARIANTS = [
                        bits_hi=16, residual=32, seed=6),
     kvq_synth.Workload("d", 1, 2, 1, 130, n_qry=8, io_dtype="fp16", n_pairs_hi=0,
                        residual=32, seed=7),
+    # the 1.5-bit point: 32 pairs at 2 bits, the 32 lowest-ranked at 1 bit
+    kvq_synth.Workload("e", 1, 4, 2, 170, n_qry=8, io_dtype="bf16", outliers="pct2x10",
+                       n_pairs_hi=0, n_pairs_lo1=32, residual=32, seed=8),
+    # 4-bit salient pairs, 2-bit middle, 1-bit tail
+    kvq_synth.Workload("f", 1, 4, 1, 140, n_qry=8, io_dtype="fp16", n_pairs_hi=6,
+                       n_pairs_lo1=16, residual=64, seed=9),
 ]
 
 
@@ -166,3 +173,37 @@ def test_record_sizes():
     assert 32768 - oracle.n_quant(32768, 128) == 128
     assert oracle.n_quant(100, 128) == 0
     assert 200 - oracle.n_quant(200, 64) == 72
+
+
+@pytest.mark.parametrize("w", [v for v in VARIANTS if v.n_pairs_lo1], ids=lambda w: w.name)
+def test_one_bit_pairs(w):
+    """Pairs of the n_pairs_lo1 lowest ranks get a two-level grid: s is the
+    fp16 of the group's range, every code is the nearer of z and z + s; the
+    other non-salient pairs keep four levels.  At 32 of 64 pairs the code
+    bits average 1.5 per key channel."""
+    d, pairs, qz = _setup(w)
+    ng = qz.nq // 32
+    f16 = lambda b: float(np.uint16(b).view(np.float16))
+    for b in range(w.batch):
+        for kh in range(w.n_kv_heads):
+            ranked = [int(p) for p in pairs[b, kh]]
+            one = set(ranked[64 - w.n_pairs_lo1:])
+            two = set(ranked[w.n_pairs_hi:64 - w.n_pairs_lo1])
+            bits = [1 if c % 64 in one else 2 if c % 64 in two else w.bits_hi for c in range(128)]
+            if w.n_pairs_hi == 0 and w.n_pairs_lo1 == 32:
+                assert sum(bits) == 1.5 * 128
+            for g in range(ng):
+                x = kvq_synth.bits_to_f64(d["k"][b, kh, 32 * g:32 * g + 32], w.io_dtype)
+                for c in range(128):
+                    codes = qz.kcodes[b, kh, g, c]
+                    s, z = f16(qz.ks[b, kh, g, c]), f16(qz.kz[b, kh, g, c])
+                    if bits[c] == 1:
+                        assert codes.max() <= 1
+                        assert z == f16(oracle.f32_to_half(x[:, c].min())[0])
+                        assert s == f16(oracle.f32_to_half(np.float32(x[:, c].max() - z))[0])
+                        if s > 0:
+                            q, margin = brute.nearest_level(x[:, c], s, z, 1)
+                            ok = margin > 1e-4 * s
+                            assert np.array_equal(codes[ok], q[ok])
+            lo2 = [c for c in range(128) if bits[c] == 2]
+            assert qz.kcodes[b, kh, :ng][:, lo2].max() == 3
