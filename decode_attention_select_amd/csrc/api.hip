@@ -18,7 +18,7 @@ kvq_status check_layout(const kvq_layout* L) {
   if (L->n_q_heads / L->n_kv_heads > 16) return KVQ_ENOTSUP;
   if (L->n_pairs_hi < 0 || L->n_pairs_hi > 8) return KVQ_EINVAL;
   if (L->bits_hi != 4 && L->bits_hi != 16) return KVQ_ENOTSUP;
-  if (L->n_pairs_lo1 != 0) return KVQ_ENOTSUP;
+  if (L->n_pairs_lo1 < 0 || L->n_pairs_hi + L->n_pairs_lo1 > NPAIR) return KVQ_EINVAL;
   if (L->bits_lo != 2 || L->bits_v != 2) return KVQ_ENOTSUP;
   if (L->residual < GS || L->residual % GS) return KVQ_EINVAL;
   if (L->max_tokens < 1 || L->max_tokens > (1 << 20)) return KVQ_EINVAL;
@@ -37,6 +37,7 @@ Geo make_geo(const kvq_layout* L) {
   g.NG = L->max_tokens > g.R ? (L->max_tokens - g.R) / GS : 0;
   g.n_hi = L->n_pairs_hi;
   g.bits_hi = L->bits_hi;
+  g.n_lo1 = L->n_pairs_lo1;
   g.nh = 2 * g.n_hi;
   g.bf16 = L->io_dtype == KVQ_BF16;
   g.max_tokens = L->max_tokens;

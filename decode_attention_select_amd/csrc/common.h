@@ -22,6 +22,7 @@ struct Geo {
   int R, RS;           // residual tokens, ring slots (R + 32)
   int NG;              // quantized-group capacity per (b, kv head)
   int n_hi, bits_hi;   // salient pairs and their bits (4 or 16)
+  int n_lo1;           // lowest-ranked pairs kept at 1 bit
   int nh;              // salient channels = 2 * n_hi
   int bf16;            // io dtype is bfloat16
   int max_tokens;

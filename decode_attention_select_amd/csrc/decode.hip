@@ -197,7 +197,10 @@ struct Lds {
 
 // HASQ: the cache has quantized-group storage (capacity NG >= 1); without it
 // no group address exists and the group stream is compiled out.
-template <bool BF16, int HIMODE, bool HASQ>
+// LO1: some pairs are at 1 bit.  Their scale is the whole group range, three
+// times a 2-bit channel's, so q*s is carried as an exact fp16 pair (rounded
+// value + rounding residual) through a second MFMA pass over the same codes.
+template <bool BF16, int HIMODE, bool HASQ, bool LO1>
 __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             kvq_cache c, float scale_log2, int S,
                                                             Ws ws, uint16_t* __restrict__ out) {
@@ -343,14 +346,22 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 
     // keys: q' = q * s (fp16), bias = q . z (the same for every token row);
     // each tile's accumulator starts from the bias, so no VALU adds follow
-    uint32_t qs[16];
+    uint32_t qs[16], qsl[16];
     f4 cb = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const u4 sv = ((const u4*)(sm + 16 * kq))[i];
       const u4 zv = ((const u4*)(sm + 64 + 16 * kq))[i];
 #pragma unroll
-      for (int e = 0; e < 4; e++) qs[4 * i + e] = pk_mul(q16[4 * i + e], sv[e]);
+      for (int e = 0; e < 4; e++) {
+        qs[4 * i + e] = pk_mul(q16[4 * i + e], sv[e]);
+        if constexpr (LO1) {
+          // q*s is exact in fp32: its residual after the fp16 rounding
+          const h2 a = u2h(q16[4 * i + e]), b = u2h(sv[e]), h = u2h(qs[4 * i + e]);
+          qsl[4 * i + e] = pk_rne(fmaf((float)a[0], (float)b[0], -(float)h[0]),
+                                  fmaf((float)a[1], (float)b[1], -(float)h[1]));
+        }
+      }
       const u4 qb = u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
       cb = mma_f16(zv, qb, cb);
     }
@@ -378,10 +389,14 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       for (int u = 0; u < 2; u++) {
         const uint32_t A = w[u] & 0x33333333u, Bn = (w[u] >> 2) & 0x33333333u;
         const int k0 = 8 * u;
-        acc = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
-                      u4{qs[k0], qs[k0 + 1], qs[k0 + 2], qs[k0 + 3]}, acc);
-        acc = mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)},
-                      u4{qs[k0 + 4], qs[k0 + 5], qs[k0 + 6], qs[k0 + 7]}, acc);
+        const u4 c0 = u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)};
+        const u4 c1 = u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)};
+        acc = mma_f16(c0, u4{qs[k0], qs[k0 + 1], qs[k0 + 2], qs[k0 + 3]}, acc);
+        acc = mma_f16(c1, u4{qs[k0 + 4], qs[k0 + 5], qs[k0 + 6], qs[k0 + 7]}, acc);
+        if constexpr (LO1) {
+          acc = mma_f16(c0, u4{qsl[k0], qsl[k0 + 1], qsl[k0 + 2], qsl[k0 + 3]}, acc);
+          acc = mma_f16(c1, u4{qsl[k0 + 4], qsl[k0 + 5], qsl[k0 + 6], qsl[k0 + 7]}, acc);
+        }
       }
       if constexpr (HIMODE == 4) {
         const uint32_t wsel = (kq & 1) ? cur.khi[TT] >> 16 : cur.khi[TT];
@@ -631,17 +646,24 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     __hip_atomic_store(&ws.tick[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool BF16, int HIMODE>
+template <bool BF16, int HIMODE, bool LO1>
 static void launch_one(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
                        const Ws& ws, void* out, hipStream_t st) {
   if (g.NG > 0)
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true>), dim3(g.B * g.Hkv * S),
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, LO1>), dim3(g.B * g.Hkv * S),
                        dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, ws,
                        (uint16_t*)out);
   else
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false>), dim3(g.B * g.Hkv * S),
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, LO1>), dim3(g.B * g.Hkv * S),
                        dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, ws,
                        (uint16_t*)out);
+}
+
+template <bool BF16, int HIMODE>
+static void launch_lo1(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
+                       const Ws& ws, void* out, hipStream_t st) {
+  if (g.n_lo1 > 0) launch_one<BF16, HIMODE, true>(g, q, c, scale_log2, S, ws, out, st);
+  else launch_one<BF16, HIMODE, false>(g, q, c, scale_log2, S, ws, out, st);
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {
@@ -654,13 +676,13 @@ hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float 
   const int hm = g.n_hi == 0 ? 0 : g.bits_hi;
   const Ws ws = ws_layout(workspace, g.B, g.Hq, S);
   if (g.bf16) {
-    if (hm == 0) launch_one<true, 0>(g, q, c, scale_log2, S, ws, out, st);
-    else if (hm == 4) launch_one<true, 4>(g, q, c, scale_log2, S, ws, out, st);
-    else launch_one<true, 16>(g, q, c, scale_log2, S, ws, out, st);
+    if (hm == 0) launch_lo1<true, 0>(g, q, c, scale_log2, S, ws, out, st);
+    else if (hm == 4) launch_lo1<true, 4>(g, q, c, scale_log2, S, ws, out, st);
+    else launch_lo1<true, 16>(g, q, c, scale_log2, S, ws, out, st);
   } else {
-    if (hm == 0) launch_one<false, 0>(g, q, c, scale_log2, S, ws, out, st);
-    else if (hm == 4) launch_one<false, 4>(g, q, c, scale_log2, S, ws, out, st);
-    else launch_one<false, 16>(g, q, c, scale_log2, S, ws, out, st);
+    if (hm == 0) launch_lo1<false, 0>(g, q, c, scale_log2, S, ws, out, st);
+    else if (hm == 4) launch_lo1<false, 4>(g, q, c, scale_log2, S, ws, out, st);
+    else launch_lo1<false, 16>(g, q, c, scale_log2, S, ws, out, st);
   }
   return hipGetLastError();
 }

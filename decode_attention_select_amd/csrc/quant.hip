@@ -48,10 +48,13 @@ __device__ void quant_key_group(const Geo& g, const Src& src, const int32_t* pai
   const int tid = threadIdx.x;
   if (tid < D) {
     const int c = tid, pj = c & (NPAIR - 1);
-    int sal = 0;
+    int sal = 0, one = 0;
     for (int r = 0; r < g.n_hi; r++) sal |= pairs[r] == pj;
+    for (int r = NPAIR - g.n_lo1; r < NPAIR; r++) one |= pairs[r] == pj;
     lds.salient[c] = sal;
-    const int bits = sal ? g.bits_hi : 2;
+    // salient pairs at bits_hi, the n_lo1 lowest-ranked pairs at one bit
+    // (their codes 0/1 sit in the 2-bit slots of k_lo), the rest at 2 bits
+    const int bits = sal ? g.bits_hi : (one ? 1 : 2);
     uint16_t s = 0, z = 0;
     uint8_t codes[GS];
     if (bits == 16) {

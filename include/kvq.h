@@ -70,7 +70,9 @@ typedef struct {
                           a value token */
   int32_t n_pairs_hi;  /* salient pairs, 0..8 (ranks 0 .. n_pairs_hi-1) */
   int32_t bits_hi;     /* 4 (4-bit codes) or 16 (raw 16-bit values) */
-  int32_t n_pairs_lo1; /* pairs stored at 1 bit; must be 0 in this version */
+  int32_t n_pairs_lo1; /* pairs of the lowest ranks quantized at 1 bit
+                          (codes 0/1 kept in their 2-bit slots of k_lo);
+                          n_pairs_hi + n_pairs_lo1 <= 64 */
   int32_t bits_lo;     /* 2: bits of every non-salient key channel */
   int32_t bits_v;      /* 2: bits of every value */
   int32_t residual;    /* R: recent tokens kept at 16 bits; multiple of 32,
@@ -97,8 +99,9 @@ typedef struct {
  *  k_lo    [B][Hkv][NG][256] u32: word ((T*4 + kq)*16 + r)*2 + u holds,
  *          for the token at tile index 16T + r, channels 16w .. 16w+15 with
  *          w = 2kq + u, channel 16w + c at position pi(c).  The stored digit
- *          is the 2-bit code of a 2-bit channel, the low two bits of the code
- *          of a 4-bit channel, and 0 for a 16-bit channel.
+ *          is the 2-bit code of a 2-bit channel, the code (0 or 1) of a
+ *          1-bit channel, the low two bits of the code of a 4-bit channel,
+ *          and 0 for a 16-bit channel.
  *  k_hi    bits_hi == 4: [B][Hkv][NG][32] u32: word 16T + r (token at tile
  *          index 16T+r) holds the high two bits (code >> 2) of the d-th
  *          salient channel (ascending channel order, d < 2*n_pairs_hi) at
@@ -173,7 +176,8 @@ kvq_status kvq_select_pairs(const kvq_layout *L, const void *q_sel,
  *   z = fp16(min x);  s = fp16(fp32(max x - z) / L)   (IEEE fp32, RNE)
  *   s == 0: every code 0; else r = 1.0f / s and
  *   code_i = clamp(rint((x_i - z) * r), 0, L)  (fp32, ties to even)
- * Channels of the n_pairs_hi top-ranked pairs use bits_hi, others bits_lo.
+ * Channels of the n_pairs_hi top-ranked pairs use bits_hi, those of the
+ * n_pairs_lo1 lowest-ranked pairs 1 bit (L = 1), all others bits_lo.
  * Fills groups [0, n_q(T)/32), copies positions [n_q(T), T) into ring_k and
  * sets len[b][h] = T.   k: [B][Hkv][T][128], 1 <= T <= max_tokens. */
 kvq_status kvq_quant_keys(const kvq_layout *L, const void *k, int32_t T,

@@ -34,6 +34,7 @@ class Case:
         self.max_tokens = max_tokens or max(w.max_tokens, self.T)
         self.layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads,
                                       n_pairs_hi=w.n_pairs_hi, bits_hi=w.bits_hi,
+                                      n_pairs_lo1=w.n_pairs_lo1,
                                       residual=w.residual, max_tokens=self.max_tokens,
                                       io_dtype=w.io_dtype)
         self.cache = kvq.Cache(self.layout)
@@ -60,7 +61,7 @@ class Case:
         return oracle.quantize(self.d["k"], self.d["v"], self.T if T is None else T, pairs,
                                residual=self.w.residual, n_pairs_hi=self.w.n_pairs_hi,
                                bits_hi=self.w.bits_hi, io_dtype=self.w.io_dtype,
-                               ng=max(self.NG, 1))
+                               ng=max(self.NG, 1), n_pairs_lo1=self.w.n_pairs_lo1)
 
     # -------------------------------------------------------------- GPU side
     def gpu_bytes(self) -> dict:

@@ -69,7 +69,8 @@ def status_of(name, *args):
 
 @pytest.mark.parametrize("bad,want", [
     (dict(head_dim=64), EINVAL), (dict(group=16), EINVAL), (dict(n_pairs_hi=9), EINVAL),
-    (dict(bits_hi=8), ENOTSUP), (dict(n_pairs_lo1=4), ENOTSUP), (dict(bits_lo=3), ENOTSUP),
+    (dict(bits_hi=8), ENOTSUP), (dict(n_pairs_lo1=59), EINVAL), (dict(n_pairs_lo1=-1), EINVAL),
+    (dict(bits_lo=3), ENOTSUP),
     (dict(residual=48), EINVAL), (dict(residual=0), EINVAL), (dict(max_tokens=0), EINVAL),
     (dict(io_dtype=5), EINVAL), (dict(n_q_heads=30), EINVAL), (dict(n_q_heads=8 * 17), ENOTSUP),
     (dict(batch=0), EINVAL),

@@ -29,6 +29,11 @@ SMALL = [
                        n_pairs_hi=0, residual=32, seed=23),
     kvq_synth.Workload("g16", 1, 16, 1, 300, n_qry=4, io_dtype="bf16",
                        n_pairs_hi=8, residual=32, seed=24),
+    # the 1.5-bit point (32 pairs at 2 bits, 32 at 1 bit) and a 4/2/1-bit mix
+    kvq_synth.Workload("one-bit-1p5", 1, 8, 2, 420, n_qry=8, io_dtype="bf16",
+                       outliers="pct2x10", n_pairs_hi=0, n_pairs_lo1=32, residual=64, seed=25),
+    kvq_synth.Workload("mixed-4-2-1", 2, 4, 1, 260, n_qry=8, io_dtype="fp16",
+                       n_pairs_hi=6, n_pairs_lo1=16, residual=32, seed=26),
 ]
 
 
