@@ -38,12 +38,13 @@ def algorithmic_bytes(w, T: int) -> int:
     R = w.residual
     nq = 32 * (max(0, T - R) // 32)
     nr = T - nq
-    n_hi_ch = 2 * w.n_pairs_hi
+    n_hi_ch, n_one_ch = 2 * w.n_pairs_hi, 2 * w.n_pairs_lo1
+    n_two_ch = 128 - n_hi_ch - n_one_ch
     if w.bits_hi == 16:
-        k_code_bits = n_hi_ch * 16 + (128 - n_hi_ch) * 2
+        k_code_bits = n_hi_ch * 16 + n_two_ch * 2 + n_one_ch
         k_meta = (128 - n_hi_ch) * 4 / 32
     else:
-        k_code_bits = n_hi_ch * w.bits_hi + (128 - n_hi_ch) * 2
+        k_code_bits = n_hi_ch * w.bits_hi + n_two_ch * 2 + n_one_ch
         k_meta = 128 * 4 / 32
     per_tok = k_code_bits / 8 + k_meta + 32 + 16
     bh = w.batch * w.n_kv_heads
@@ -232,6 +233,106 @@ def streaming_leg(args, w):
     }
 
 
+def pareto_leg(args, w):
+    """Bit-allocation sweep on one workload: for every point of
+    kvq_synth.PARETO_POINTS, the decode time and effective GB/s (cache
+    replicas beyond the Infinity Cache, as in the main leg) and the attention
+    error of the GPU output against plain softmax attention over the
+    unquantized 16-bit keys and values (fp64 on the host)."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import kvq_synth
+    from decode_attention_select_amd import kvq
+
+    T = w.tokens
+    data = kvq_synth.generate(w)
+    q_bits = data["q_dec"][:, :, 0]
+    # unquantized reference, every query head
+    qf = kvq_synth.bits_to_f64(q_bits, w.io_dtype)
+    G = w.group_size
+    ref = np.zeros((w.batch, w.n_q_heads, 128))
+    for b in range(w.batch):
+        for kh in range(w.n_kv_heads):
+            K = kvq_synth.bits_to_f64(data["k"][b, kh, :T], w.io_dtype)
+            V = kvq_synth.bits_to_f64(data["v"][b, kh, :T], w.io_dtype)
+            lg = (qf[b, kh * G:(kh + 1) * G] @ K.T) * SM_SCALE
+            p = np.exp(lg - lg.max(axis=1, keepdims=True))
+            ref[b, kh * G:(kh + 1) * G] = (p / p.sum(axis=1, keepdims=True)) @ V
+    points = []
+    S = args.splits or w.n_splits or default_splits(w)
+    for label, n_hi, bits_hi, n_lo1 in kvq_synth.PARETO_POINTS:
+        wp = dataclasses.replace(w, n_pairs_hi=n_hi, bits_hi=bits_hi, n_pairs_lo1=n_lo1)
+        layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads, n_pairs_hi=n_hi,
+                                 bits_hi=bits_hi, n_pairs_lo1=n_lo1, residual=w.residual,
+                                 max_tokens=T, io_dtype=w.io_dtype)
+        base = kvq.Cache(layout)
+        kvq.kvq_select_pairs(layout, dev(data["q_sel"]), w.n_qry, dev(data["k"][:, :, :T]), T,
+                             base.struct)
+        kvq.kvq_quant_keys(layout, dev(data["k"][:, :, :T]), T, base.struct)
+        kvq.kvq_quant_values(layout, dev(data["v"][:, :, :T]), T, base.struct)
+        torch.cuda.synchronize()
+        n_rep = max(1, math.ceil(args.replica_mib * 2 ** 20 / base.nbytes()))
+        reps = [base]
+        for _ in range(n_rep - 1):
+            r = kvq.Cache.__new__(kvq.Cache)
+            r.layout, r.sizes = base.layout, base.sizes
+            r.bufs = {k: v.clone() for k, v in base.bufs.items()}
+            r.struct = kvq.kvq_cache(*[r.bufs[nm].data_ptr() for nm in kvq.BUF_NAMES])
+            reps.append(r)
+        q = dev(q_bits)
+        out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+        ws = torch.zeros(kvq.kvq_workspace_bytes(layout, S), dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream()
+        sc = float(np.float32(SM_SCALE))
+        for i in range(args.warmup):
+            kvq.kvq_decode_attn(layout, q, reps[i % n_rep].struct, sc, S, ws, out, stream=stream)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(args.steps):
+            kvq.kvq_decode_attn(layout, q, reps[i % n_rep].struct, sc, S, ws, out, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+        got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype)
+        err = np.abs(got - ref)
+        alg = algorithmic_bytes(wp, T)
+        points.append({"bits": label, "salient_pairs": n_hi, "salient_bits": bits_hi,
+                       "one_bit_pairs": n_lo1, "us_per_step": round(us, 3),
+                       "GBs": round(alg / (us * 1e-6) / 1e9, 1),
+                       "algorithmic_bytes": alg, "layout_bytes": layout_bytes(base, wp, T),
+                       "max_abs_err_vs_unquantized": float(err.max()),
+                       "mean_abs_err_vs_unquantized": float(err.mean()),
+                       "rel_l2_err_vs_unquantized": float(np.linalg.norm(got - ref) /
+                                                          np.linalg.norm(ref))})
+        del reps, base
+        torch.cuda.empty_cache()
+    main_pt = [p for p in points if p["bits"] == "2.26"][0]
+    return {
+        "metric": METRIC,
+        "value": main_pt["GBs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_pt["us_per_step"] * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 (MFMA) / f32 accumulate",
+        "data": "synthetic (seeded N(0,1) + outlier key pairs, RoPE)",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "context": T, "io_dtype": w.io_dtype,
+                   "residual": w.residual, "n_splits": S},
+        "pareto": points,
+        "note": "value = the 2.26-bit point; errors are against fp64 softmax attention over "
+                "the unquantized 16-bit K/V, all query heads",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +362,9 @@ def main():
     w = kvq_synth.workload(args.workload)
     if w.n_app:
         print(json.dumps(streaming_leg(args, w)), flush=True)
+        return
+    if w.name.startswith("pareto"):
+        print(json.dumps(pareto_leg(args, w)), flush=True)
         return
     S = args.splits or w.n_splits or default_splits(w)
     T = w.tokens

@@ -81,7 +81,9 @@ WORKLOADS = [
 ]
 
 # Key bit points of the Pareto sweep: (label, n_pairs_hi, bits_hi).
-PARETO_POINTS = [("2.0", 0, 4), ("2.26", 6, 4), ("3.0", 6, 16)]
+# Bit points of the precision sweep: (label, salient pairs, their bits,
+# pairs at 1 bit).  "1.5": 32 pairs at 2 bits and the 32 lowest-ranked at 1.
+PARETO_POINTS = [("1.5", 0, 4, 32), ("2.0", 0, 4, 0), ("2.26", 6, 4, 0), ("3.0", 6, 16, 0)]
 
 
 def workload(name: str) -> Workload:
