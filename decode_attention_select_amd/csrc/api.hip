@@ -80,7 +80,10 @@ kvq_status kvq_cache_sizes(const kvq_layout* L, size_t sizes[KVQ_NBUF]) {
   const size_t bh = (size_t)g.B * g.Hkv, grp = bh * g.NG;
   const size_t el = 2;  // bytes of a 16-bit value
   sizes[0] = grp * GROUP_WORDS * 4;  // k_lo
-  sizes[1] = grp * g.khi_bytes;      // k_hi
+  // k_hi; raw 16-bit salient rows (2*nh bytes) are read 16 bytes at a time
+  // from channel 0 or 8 of a row: the last row's read ends at most 32 - 2*nh
+  // bytes past the record, so 32 bytes of tail slack keep it in the buffer
+  sizes[1] = grp * g.khi_bytes + (grp && g.bits_hi == 16 && g.nh ? 32 : 0);
   sizes[2] = grp * 2 * D * 2;        // k_meta
   sizes[3] = grp * GROUP_WORDS * 4;  // v_codes
   sizes[4] = grp * 2 * D * 2;        // v_meta

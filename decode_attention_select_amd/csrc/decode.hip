@@ -44,6 +44,8 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+// 16 bytes at a 4-byte-aligned address (raw salient rows are 2*nh bytes long)
+typedef uint32_t u4a __attribute__((ext_vector_type(4), aligned(4)));
 
 constexpr int NW = 8;                  // waves per workgroup (one workgroup per CU)
 constexpr int WG_THREADS = 64 * NW;
@@ -124,13 +126,14 @@ __device__ inline void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) 
 struct Pref {
   u2 klo[2];        // k_lo words of tile 0 and 1 (token col of the tile, channels 32kq..)
   uint32_t khi[2];  // k_hi word of tile 0 and 1
+  u4 hraw[2];       // raw salient keys (HIMODE 16): 8 values of the lane's token, tile 0 and 1
   uint32_t vc[4];   // v_codes word of channel group j = 0..3
   u4 meta;          // 16 B of the group's k_meta (lanes 0-31) or v_meta (lanes 32-63)
 };
 
 template <int HIMODE>
 __device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int col, int kq,
-                                  Pref& p) {
+                                  int nh, Pref& p) {
   const u2* klo = (const u2*)((const uint32_t*)c.k_lo + rec * GROUP_WORDS);
   p.klo[0] = klo[(0 * 4 + kq) * 16 + col];
   p.klo[1] = klo[(1 * 4 + kq) * 16 + col];
@@ -138,6 +141,16 @@ __device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int 
     const uint32_t* kh = (const uint32_t*)c.k_hi + rec * 32;
     p.khi[0] = kh[col];
     p.khi[1] = kh[16 + col];
+  }
+  if constexpr (HIMODE == 16) {
+    // salient channels 8*(kq&1) .. +7 of the lane's token (entries past nh
+    // are masked later; the buffer carries 32 bytes of tail slack)
+    const uint16_t* kh = (const uint16_t*)c.k_hi + rec * GS * nh;
+#pragma unroll
+    for (int TT = 0; TT < 2; TT++) {
+      const u4a v = *(const u4a*)(kh + (16 * TT + col) * nh + 8 * (kq & 1));
+      p.hraw[TT] = u4{v[0], v[1], v[2], v[3]};
+    }
   }
   const uint32_t* vc = (const uint32_t*)c.v_codes + rec * GROUP_WORDS;
 #pragma unroll
@@ -250,7 +263,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   Pref pf[PF];
   if constexpr (HASQ) {
 #pragma unroll
-    for (int k = 0; k < PF; k++) load_group<HIMODE>(c, group_at(k), lane, col, kq, pf[k]);
+    for (int k = 0; k < PF; k++) load_group<HIMODE>(c, group_at(k), lane, col, kq, g.nh, pf[k]);
   }
 
   // query as fp16 pairs (zero past the G heads)
@@ -405,15 +418,14 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
                       u4{qshi[0], qshi[1], qshi[2], qshi[3]}, acc);
       }
       if constexpr (HIMODE == 16) {
-        const uint16_t* raw = (const uint16_t*)c.k_hi + rec * GS * g.nh + (16 * TT + col) * g.nh;
-        uint32_t a[4] = {0, 0, 0, 0};
+        u4 a = cur.hraw[TT];
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const int d = 8 * (kq & 1) + e;
-          const uint32_t v = (kq < 2 && d < g.nh) ? raw[d] : 0u;
-          a[e >> 1] |= v << (16 * (e & 1));
+        for (int e = 0; e < 4; e++) {
+          const int d = 8 * (kq & 1) + 2 * e;
+          const uint32_t keep = kq >= 2 ? 0u : (d < g.nh ? 0x0000ffffu : 0u) | (d + 1 < g.nh ? 0xffff0000u : 0u);
+          a[e] &= keep;
         }
-        acc = mma_raw<BF16>(u4{a[0], a[1], a[2], a[3]}, u4{qhi[0], qhi[1], qhi[2], qhi[3]}, acc);
+        acc = mma_raw<BF16>(a, u4{qhi[0], qhi[1], qhi[2], qhi[3]}, acc);
       }
       C[TT] = acc;
     }
@@ -443,7 +455,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
       for (int k = 0; k < PF; k++) {
         if (i + k < nmine) process_group(pf[k], group_at(i + k));
-        load_group<HIMODE>(c, group_at(i + k + PF), lane, col, kq, pf[k]);
+        load_group<HIMODE>(c, group_at(i + k + PF), lane, col, kq, g.nh, pf[k]);
       }
     }
   }

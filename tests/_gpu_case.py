@@ -68,10 +68,11 @@ class Case:
         B, H, NG = self.w.batch, self.w.n_kv_heads, self.NG
         c = self.cache
         RS = self.w.residual + 32
+        khi = oracle.k_hi_words(self.w.n_pairs_hi, self.w.bits_hi) if NG else 0
         out = {
             "k_lo": host(c["k_lo"], np.uint32).reshape(B, H, NG, 256),
-            "k_hi": (host(c["k_hi"], np.uint8).reshape(B, H, NG, -1) if c.sizes[1]
-                     else np.zeros((B, H, NG, 0), np.uint8)),
+            "k_hi": (host(c["k_hi"], np.uint8)[:B * H * NG * khi].reshape(B, H, NG, khi)
+                     if khi else np.zeros((B, H, NG, 0), np.uint8)),
             "k_meta": host(c["k_meta"], np.uint16).reshape(B, H, NG, 256),
             "v_codes": host(c["v_codes"], np.uint32).reshape(B, H, NG, 256),
             "v_meta": host(c["v_meta"], np.uint16).reshape(B, H, NG, 256),
