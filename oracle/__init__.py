@@ -213,3 +213,30 @@ def live_ring_slots(T: int, R: int) -> np.ndarray:
     """Ring slots that hold tokens when T tokens are cached."""
     RS = R + GS
     return np.array([p % RS for p in range(n_quant(T, R), T)], dtype=np.int64)
+
+
+def shrink_code(x: int, b: int) -> int:
+    """round(x / (2^b + 1)): the b-bit code of a 2b-bit code after the shrink."""
+    return int(_load().orc_shrink_code(int(x), int(b)))
+
+
+def ers(x: int, b: int) -> int:
+    """The review's shift form of the same map, as written there."""
+    lib = _load()
+    lib.orc_ers.restype = ctypes.c_longlong
+    lib.orc_ers.argtypes = [ctypes.c_longlong, ctypes.c_int]
+    return int(lib.orc_ers(int(x), int(b)))
+
+
+def shrink(qz: Quantized, g0: int, g1: int) -> Quantized:
+    """Copy of qz with the 4-bit salient key channels of groups [g0, g1)
+    shrunk to 2 bits (code / 5 rounded, scale x 5 in fp16, zero kept)."""
+    assert qz.bits_hi == 4
+    kw = dict(qz.__dict__)
+    kw["kcodes"] = qz.kcodes.copy()
+    kw["ks"] = qz.ks.copy()
+    B, Hkv = qz.kcodes.shape[:2]
+    rc = _load().orc_shrink_keys(B, Hkv, qz.n_hi, _p(qz.pairs), qz.NG, qz.nq // GS, int(g0),
+                                 int(g1), _p(kw["kcodes"]), _p(kw["ks"]))
+    assert rc == 0
+    return Quantized(**kw)

@@ -163,6 +163,52 @@ static int orc_is_salient(const int32_t *pr, int n_hi, int c) {
   return 0;
 }
 
+/* ------------------------------------------------------ precision shrink */
+
+/* PM-KVQ review, key_machinery: the cache is kept at 2b bits first and later
+ * shrunk in place to b bits, the zero point kept and the step multiplied by
+ * 2^b + 1 (the b-bit grid then spans the same range as the 2b-bit one).  The
+ * requantized code is the nearest b-bit level to the dequantized value,
+ * round(X / (2^b + 1)); 2^b + 1 is odd, so no tie occurs.  Plain integer
+ * rounding: floor((2X + d) / 2d) with d = 2^b + 1. */
+int orc_shrink_code(int x, int b) {
+  long long d = (1LL << b) + 1;
+  return (int)((2LL * x + d) / (2 * d));
+}
+
+/* The review's integer shift form of the same map (as the review writes it):
+ * ((2^2b - 2^b + 1) * (X + 2^(b-1))) >> 3b.  Kept apart from the definition
+ * above so that tests can compare the two over every input. */
+long long orc_ers(long long x, int b) {
+  long long m = (1LL << (2 * b)) - (1LL << b) + 1;
+  return (m * (x + (1LL << (b - 1)))) >> (3 * b);
+}
+
+/* Shrinks the 4-bit salient key channels of groups [g0, g1) (clamped to the
+ * quantized groups [0, ng)) to 2 bits: code <- round(code / 5), scale <- the
+ * fp16 rounding of 5 * s (fp32 product), zero point unchanged.  Logical
+ * codes [..][NG][128][32], s [..][NG][128]. */
+int orc_shrink_keys(int B, int Hkv, int n_hi, const int32_t *pairs, int NG, int ng,
+                    int g0, int g1, uint8_t *codes, uint16_t *s) {
+  if (g1 > ng) g1 = ng;
+  if (g0 < 0) g0 = 0;
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++) {
+      const int32_t *pr = pairs + (size_t)(b * Hkv + kh) * NPAIR;
+      for (int g = g0; g < g1; g++)
+        for (int c = 0; c < D; c++) {
+          int sal = 0;
+          for (int r = 0; r < n_hi; r++) sal |= pr[r] == c % NPAIR;
+          if (!sal) continue;
+          size_t slot = ((size_t)(b * Hkv + kh) * NG + g) * D + c;
+          for (int i = 0; i < GS; i++)
+            codes[slot * GS + i] = (uint8_t)orc_shrink_code(codes[slot * GS + i], 2);
+          s[slot] = orc_f32_to_half((float)orc_half_to_f64(s[slot]) * 5.0f);
+        }
+    }
+  return 0;
+}
+
 /* ------------------------------------------------------------- quantizer */
 
 /* Affine min/max quantizer of one group of 32 values at L = 2^b - 1 levels.
