@@ -147,6 +147,18 @@ kvq_status kvq_append(const kvq_layout* L, const void* k_new, const void* v_new,
   return hip_status(launch_append(g, k_new, v_new, cache, (hipStream_t)stream));
 }
 
+kvq_status kvq_shrink(const kvq_layout* L, kvq_cache* cache, int32_t g0, int32_t g1,
+                      void* stream) {
+  if (kvq_status s = check_layout(L)) return s;
+  const Geo g = make_geo(L);
+  if (g.n_hi > 0 && g.bits_hi != 4) return KVQ_ENOTSUP;
+  if (g0 < 0 || g1 < g0) return KVQ_EINVAL;
+  if (kvq_status s = check_cache(g, cache, true)) return s;
+  if (g.NG > 0 && g1 > g.NG) g1 = g.NG;
+  if (g0 > g1) g0 = g1;
+  return hip_status(launch_shrink(g, cache, g0, g1, (hipStream_t)stream));
+}
+
 kvq_status kvq_decode_attn(const kvq_layout* L, const void* q, const kvq_cache* cache,
                            float sm_scale, int32_t n_splits, void* workspace, size_t ws_bytes,
                            void* out, void* stream) {

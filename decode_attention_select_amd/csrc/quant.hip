@@ -230,6 +230,58 @@ hipError_t launch_quant_values(const Geo& g, const void* v, int T, kvq_cache* c,
   return hipGetLastError();
 }
 
+// In-place precision shrink of the 4-bit salient key channels (PM-KVQ
+// review, key_machinery): the b-bit code of a 2b-bit code X is the review's
+// shift form ((2^2b - 2^b + 1) * (X + 2^(b-1))) >> 3b, i.e. round(X / (2^b+1)),
+// on the grid of step (2^b + 1) s with the zero point kept.  Here 2b = 4: the
+// new value z + 5 s q is held as the 4-bit code 5 q = 4 q + q under the
+// unchanged scale s, i.e. both the high and the low digit become q, so the
+// step 5 s is exact and decoding keeps its precise paths.  One 64-lane
+// workgroup per (b, kv head, group); lane e < 32 owns the token of tile
+// index e, so its key words are written by it alone.
+__device__ inline uint32_t shrink_4_to_2(uint32_t x) { return (13u * (x + 2u)) >> 6; }
+
+__global__ __launch_bounds__(64) void shrink_kernel(Geo g, kvq_cache c, int g0, int g1) {
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  const int ngq = n_quant(c.len[bh], g.R) / GS;
+  const int grp = g0 + (int)blockIdx.y;
+  if (grp >= min(g1, ngq)) return;
+  const size_t rec = (size_t)bh * g.NG + grp;
+  // salient channels, ascending: pairs of rank < n_hi, then the same + 64
+  const int32_t* pr = c.pairs + (size_t)bh * NPAIR;
+  bool sal = false;
+  for (int r = 0; r < g.n_hi; r++) sal |= pr[r] == (lane & (NPAIR - 1));
+  const unsigned long long m = __ballot(sal);
+  __shared__ int hil[16];
+  if (sal && lane < NPAIR) {
+    const int idx = __popcll(m & ((1ull << lane) - 1));
+    hil[idx] = lane;
+    hil[g.n_hi + idx] = lane + NPAIR;
+  }
+  __syncthreads();
+  if (lane < GS) {
+    const int e = lane, T = e >> 4, r = e & 15;
+    uint32_t* hi = (uint32_t*)c.k_hi + rec * 32;
+    uint32_t* lo = (uint32_t*)c.k_lo + rec * GROUP_WORDS;
+    uint32_t hw = hi[e];
+    for (int d = 0; d < g.nh; d++) {
+      const int ch = hil[d], w = ch >> 4, kq = w >> 1, u = w & 1;
+      uint32_t& lw = lo[((T * 4 + kq) * 16 + r) * 2 + u];
+      const int pl = 2 * pos_swap(ch & 15), ph = 2 * pos_swap(d);
+      const uint32_t q = shrink_4_to_2((((hw >> ph) & 3u) << 2) | ((lw >> pl) & 3u));
+      lw = (lw & ~(3u << pl)) | (q << pl);
+      hw = (hw & ~(3u << ph)) | (q << ph);
+    }
+    hi[e] = hw;
+  }
+}
+
+hipError_t launch_shrink(const Geo& g, kvq_cache* c, int g0, int g1, hipStream_t st) {
+  if (g1 <= g0 || g.nh == 0 || g.NG == 0) return hipSuccess;
+  hipLaunchKernelGGL(shrink_kernel, dim3(g.B * g.Hkv, g1 - g0), dim3(64), 0, st, g, *c, g0, g1);
+  return hipGetLastError();
+}
+
 hipError_t launch_append(const Geo& g, const void* k_new, const void* v_new, kvq_cache* c,
                          hipStream_t st) {
   hipLaunchKernelGGL(append_kernel, dim3(g.B * g.Hkv), dim3(QTHREADS), 0, st, g,

@@ -121,6 +121,11 @@ def kvq_append(layout, k_new, v_new, cache: kvq_cache, stream=None):
           ctypes.byref(cache), _stream(stream))
 
 
+def kvq_shrink(layout, cache: kvq_cache, g0: int, g1: int, stream=None):
+    _call("kvq_shrink", ctypes.byref(layout), ctypes.byref(cache), ctypes.c_int32(g0),
+          ctypes.c_int32(g1), _stream(stream))
+
+
 def kvq_decode_attn(layout, q, cache: kvq_cache, sm_scale, n_splits, workspace, out,
                     stream=None, ws_bytes=None):
     if ws_bytes is None:

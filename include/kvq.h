@@ -201,6 +201,21 @@ kvq_status kvq_quant_values(const kvq_layout *L, const void *v, int32_t T,
 kvq_status kvq_append(const kvq_layout *L, const void *k_new,
                       const void *v_new, kvq_cache *cache, void *stream);
 
+/* In-place precision shrink of the salient key channels ([PM-KVQ]
+ * key_machinery: a cache is kept at 2b bits and later shrunk in place to b
+ * bits, zero point kept, step multiplied by 2^b + 1).  For every (b, kv head)
+ * and quantized group g in [g0, min(g1, n_q(T)/32)), each 4-bit salient code
+ * X is moved to the 2-bit grid of step 5 s: q = round(X / 5) (computed as
+ * (13 (X + 2)) >> 6), held as the 4-bit code 5 q (high and low digit both q)
+ * under the unchanged scale, so it dequantizes to exactly z + 5 s q.  All
+ * other channels are untouched; decoding needs no change.  This layout keeps
+ * the 4-bit slots, so no bytes are freed.  A group must be shrunk at most once: the
+ * caller keeps the boundary (typically the oldest groups, when memory
+ * fills).  n_pairs_hi == 0 is a no-op; bits_hi == 16 returns KVQ_ENOTSUP;
+ * g0 < 0 or g1 < g0 returns KVQ_EINVAL; g1 beyond the capacity is clamped. */
+kvq_status kvq_shrink(const kvq_layout *L, kvq_cache *cache, int32_t g0,
+                      int32_t g1, void *stream);
+
 /* Single-token decode attention over the quantized cache ([Dual-QK]
  * abstract and [PN-Mix] abstract: decode reads the low-bit cache).  For
  * each query head h of KV head h/G:

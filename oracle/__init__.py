@@ -230,7 +230,8 @@ def ers(x: int, b: int) -> int:
 
 def shrink(qz: Quantized, g0: int, g1: int) -> Quantized:
     """Copy of qz with the 4-bit salient key channels of groups [g0, g1)
-    shrunk to 2 bits (code / 5 rounded, scale x 5 in fp16, zero kept)."""
+    shrunk to the 2-bit grid of step 5 s (zero kept): 4-bit code 5 * round(X/5)
+    under the unchanged scale s."""
     assert qz.bits_hi == 4
     kw = dict(qz.__dict__)
     kw["kcodes"] = qz.kcodes.copy()

@@ -185,11 +185,13 @@ long long orc_ers(long long x, int b) {
 }
 
 /* Shrinks the 4-bit salient key channels of groups [g0, g1) (clamped to the
- * quantized groups [0, ng)) to 2 bits: code <- round(code / 5), scale <- the
- * fp16 rounding of 5 * s (fp32 product), zero point unchanged.  Logical
- * codes [..][NG][128][32], s [..][NG][128]. */
+ * quantized groups [0, ng)) to the 2-bit grid with the same zero point and
+ * step 5 s: the new 2-bit code is q = round(X / 5), and the channel keeps its
+ * 4-bit slot and its scale s with the code 5 q, which dequantizes to exactly
+ * z + (5 s) q.  Logical codes [..][NG][128][32]; s is left as it is. */
 int orc_shrink_keys(int B, int Hkv, int n_hi, const int32_t *pairs, int NG, int ng,
                     int g0, int g1, uint8_t *codes, uint16_t *s) {
+  (void)s;
   if (g1 > ng) g1 = ng;
   if (g0 < 0) g0 = 0;
   for (int b = 0; b < B; b++)
@@ -202,8 +204,7 @@ int orc_shrink_keys(int B, int Hkv, int n_hi, const int32_t *pairs, int NG, int 
           if (!sal) continue;
           size_t slot = ((size_t)(b * Hkv + kh) * NG + g) * D + c;
           for (int i = 0; i < GS; i++)
-            codes[slot * GS + i] = (uint8_t)orc_shrink_code(codes[slot * GS + i], 2);
-          s[slot] = orc_f32_to_half((float)orc_half_to_f64(s[slot]) * 5.0f);
+            codes[slot * GS + i] = (uint8_t)(5 * orc_shrink_code(codes[slot * GS + i], 2));
         }
     }
   return 0;

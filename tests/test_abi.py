@@ -31,7 +31,7 @@ def test_library_exports_every_declared_entry_point():
     names = declared()
     assert set(names) >= {"kvq_select_pairs", "kvq_quant_keys", "kvq_quant_values",
                           "kvq_append", "kvq_decode_attn", "kvq_cache_sizes",
-                          "kvq_workspace_bytes", "kvq_check", "kvq_status_str"}
+                          "kvq_workspace_bytes", "kvq_check", "kvq_status_str", "kvq_shrink"}
     lib = kvq.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -149,3 +149,7 @@ def test_prefill_and_append_validation():
     assert status_of("kvq_append", ctypes.byref(L), P(FAKE + 1), P(FAKE), ctypes.byref(c),
                      P(0)) == EALIGN
     assert status_of("kvq_check", None, None, P(0)) == EINVAL
+    assert status_of("kvq_shrink", ctypes.byref(L), ctypes.byref(c), -1, 4, P(0)) == EINVAL
+    assert status_of("kvq_shrink", ctypes.byref(L), ctypes.byref(c), 5, 4, P(0)) == EINVAL
+    L16 = L32k(bits_hi=16)
+    assert status_of("kvq_shrink", ctypes.byref(L16), ctypes.byref(c), 0, 4, P(0)) == ENOTSUP

@@ -191,3 +191,22 @@ def test_workspace_reuse_sees_fresh_records(n_splits):
         kvq.kvq_decode_attn(case.layout, qd[i % 2], case.cache.struct, SM_SCALE, n_splits, ws, out)
         got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), case.w.io_dtype)
         assert np.array_equal(got, fresh[i % 2]), "call %d" % i
+
+
+@pytest.mark.parametrize("g0,g1", [(0, 3), (2, 100), (0, 1 << 20)])
+def test_shrink_matches_oracle(g0, g1):
+    # salient 4-bit codes shrunk in place to 2 bits: bytes equal the oracle's
+    # shrunk cache; decoding over it matches the oracle's attention
+    from decode_attention_select_amd import kvq
+    w = kvq_synth.Workload("shrink", 2, 8, 2, 420, n_qry=8, io_dtype="bf16",
+                           outliers="pct2x10", n_pairs_hi=6, residual=64, seed=42)
+    case = Case(w)
+    kvq.kvq_shrink(case.layout, case.cache.struct, g0, g1)
+    torch.cuda.synchronize()
+    qz = oracle.shrink(case.oracle_quant(), g0, g1)
+    compare_cache(case, qz, qz.nq // 32)
+    q = case.d["q_dec"][:, :, 0]
+    ref = oracle.attention(qz, q, SM_SCALE)
+    check_output(case.decode(q, 8), ref, w.io_dtype, ATOL)
+    _, part = case.decode(q, 1, partials=True)
+    check_single_split(part, ref, ATOL)

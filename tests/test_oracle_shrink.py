@@ -5,9 +5,11 @@ the step multiplied by 2^b + 1).
 * The shift form the review prints and the definition round(X / (2^b + 1))
   agree on every input of every transition it names (2b = 16, 8, 4) and on
   2 -> 1, against exact rational rounding.
-* On a quantized cache, every shrunk code is the nearest level of the new
-  grid to the value the old code dequantized to (brute force over levels);
-  everything outside the shrunk channels and groups is untouched.
+* On a quantized cache, every shrunk channel dequantizes to the nearest
+  level of the new grid z + 5 s q, q = 0..3, to the value its old code
+  dequantized to (brute force over levels), held as the 4-bit code 5 q under
+  the unchanged scale; everything outside the shrunk channels and groups is
+  untouched.
 * Attention over the shrunk cache equals textbook attention over its bytes.
 """
 from fractions import Fraction
@@ -70,14 +72,16 @@ def test_shrunk_codes_are_nearest_new_levels():
                         assert sh.ks[b, kh, g, c] == qz.ks[b, kh, g, c]
                         continue
                     s_old, z = _f16(qz.ks[b, kh, g, c]), _f16(qz.kz[b, kh, g, c])
-                    # the new step is 5 s (stored as its fp16 rounding)
-                    assert sh.ks[b, kh, g, c] == oracle.f32_to_half(np.float32(s_old) * 5)[0]
+                    assert sh.ks[b, kh, g, c] == qz.ks[b, kh, g, c]
                     x_hat = z + s_old * old.astype(np.float64)
                     q, _ = brute.nearest_level(x_hat, 5 * s_old, z, 3)
-                    assert np.array_equal(new, q)
-                    assert new.max() <= 3
-    # the salient channels did use more than two bits before the shrink
-    assert qz.kcodes[:, :, g0:g1].max() > 3 and sh.kcodes[:, :, g0:g1].max() <= 3
+                    assert np.array_equal(new, 5 * q)
+                    # the dequantized value is the new grid's level, exactly
+                    assert np.array_equal(z + s_old * new.astype(np.float64),
+                                          z + (5 * s_old) * q.astype(np.float64))
+    # before the shrink the codes used the whole 4-bit range
+    assert set(np.unique(qz.kcodes[:, :, g0:g1])) - {0, 5, 10, 15}
+    assert set(np.unique(sh.kcodes[:, :, g0:g1])) <= {0, 1, 2, 3, 5, 10, 15}
 
 
 def test_shrink_range_is_clamped_to_quantized_groups():
@@ -107,7 +111,7 @@ def test_attention_over_shrunk_bytes_matches_textbook():
             for g in range(sh.nq // 32):
                 codes, _, s, z = brute.unpack_keys(pk["k_lo"][b, kh, g], pk["k_hi"][b, kh, g],
                                                    pk["k_meta"][b, kh, g], sal, 4)
-                assert codes.max() <= 3  # no high digit left
+                assert set(np.unique(codes[sal])) <= {0, 5, 10, 15}
                 for c in range(128):
                     K[32 * g:32 * g + 32, c] = _f16(z[c]) + _f16(s[c]) * codes[c]
                 vc, vs, vz = brute.unpack_values(pk["v_codes"][b, kh, g], pk["v_meta"][b, kh, g])
