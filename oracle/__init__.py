@@ -241,3 +241,17 @@ def shrink(qz: Quantized, g0: int, g1: int) -> Quantized:
                                  int(g1), _p(kw["kcodes"]), _p(kw["ks"]))
     assert rc == 0
     return Quantized(**kw)
+
+
+def select_qa(q_sel, k, T: int, n_kv_heads: int, io_dtype: str):
+    """Query-aware channel score (the MixKVQ reading): returns (score
+    [B][Hkv][64] float64, pairs [B][Hkv][64] int32)."""
+    q_sel = np.ascontiguousarray(q_sel, dtype=np.uint16)
+    k = np.ascontiguousarray(np.asarray(k)[:, :, :T], dtype=np.uint16)
+    B, Hq, n_qry, _ = q_sel.shape
+    bits = np.zeros((B, n_kv_heads, 64), np.uint64)
+    pairs = np.zeros((B, n_kv_heads, 64), np.int32)
+    rc = _load().orc_select_qa(B, Hq, n_kv_heads, _bf(io_dtype), _p(q_sel), n_qry, _p(k),
+                               int(T), _p(bits), _p(pairs))
+    assert rc == 0
+    return bits.view(np.float64), pairs

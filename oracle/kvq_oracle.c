@@ -142,6 +142,61 @@ int orc_select(int B, int Hq, int Hkv, int bf16, const uint16_t *q_sel,
   return 0;
 }
 
+/* Query-aware channel score (MixKVQ, abstract and AI summary: a key
+ * channel's importance joins its intrinsic quantization difficulty with its
+ * relevance to the query; the page prints no formula, so this is a reading).
+ * Per (b, kv head) and channel c:
+ *   A_c = sum over the group's query heads and selection queries of
+ *         floor(|q_c| * 2^24)                       (relevance)
+ *   R_c = sum over the full 32-token groups of the T prefill keys of
+ *         floor(fp32(max k_c - min k_c) * 2^16)     (difficulty: the range
+ *         sets the quantization step)
+ * and per pair j the score S_j = R_j A_j + R_{j+64} A_{j+64} in IEEE double
+ * (products and sum each rounded once).  pairs = pair ids by descending S,
+ * ties to the lower id; score_bits[j] = the bits of S_j. */
+int orc_select_qa(int B, int Hq, int Hkv, int bf16, const uint16_t *q_sel,
+                  int n_qry, const uint16_t *k, int T, uint64_t *score_bits,
+                  int32_t *pairs) {
+  if (Hq % Hkv) return -1;
+  int G = Hq / Hkv, ng = T / GS;
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++) {
+      uint64_t A[D], R[D];
+      for (int c = 0; c < D; c++) {
+        A[c] = 0;
+        for (int h = kh * G; h < kh * G + G; h++)
+          for (int t = 0; t < n_qry; t++) {
+            double x = fabs(to_f64(q_sel[(((size_t)b * Hq + h) * n_qry + t) * D + c], bf16));
+            A[c] += (uint64_t)floor(x * 16777216.0);
+          }
+        R[c] = 0;
+        for (int g = 0; g < ng; g++) {
+          float mn = INFINITY, mx = -INFINITY;
+          for (int i = 0; i < GS; i++) {
+            float x = (float)to_f64(k[(((size_t)b * Hkv + kh) * T + g * GS + i) * D + c], bf16);
+            if (x < mn) mn = x;
+            if (x > mx) mx = x;
+          }
+          float r = mx - mn;
+          R[c] += (uint64_t)floor((double)r * 65536.0);
+        }
+      }
+      double S[NPAIR];
+      for (int j = 0; j < NPAIR; j++) {
+        double p0 = (double)R[j] * (double)A[j];
+        double p1 = (double)R[j + NPAIR] * (double)A[j + NPAIR];
+        S[j] = p0 + p1;
+        memcpy(&score_bits[((size_t)b * Hkv + kh) * NPAIR + j], &S[j], 8);
+      }
+      for (int j = 0; j < NPAIR; j++) {
+        int rank = 0;
+        for (int i = 0; i < NPAIR; i++) rank += (S[i] > S[j]) || (S[i] == S[j] && i < j);
+        pairs[((size_t)b * Hkv + kh) * NPAIR + rank] = j;
+      }
+    }
+  return 0;
+}
+
 /* Bits of channel c given the rank table of its (b, kv head): the pairs of
  * the n_hi highest ranks at bits_hi, those of the n_lo1 lowest ranks at one
  * bit, all others at bits_lo (PN-Mix, abstract: more bits for the salient
