@@ -115,6 +115,18 @@ kvq_status kvq_select_pairs(const kvq_layout* L, const void* q_sel, int32_t n_qr
   return hip_status(launch_select(g, q_sel, n_qry, k, T, cache, (hipStream_t)stream));
 }
 
+kvq_status kvq_select_pairs_qa(const kvq_layout* L, const void* q_sel, int32_t n_qry,
+                               const void* k, int32_t T, kvq_cache* cache, void* stream) {
+  if (kvq_status s = check_layout(L)) return s;
+  const Geo g = make_geo(L);
+  if (n_qry < 1 || n_qry > 1024 || T < 1) return KVQ_EINVAL;
+  if (T > g.max_tokens) return KVQ_ECAPACITY;
+  if (kvq_status s = check_ptr(q_sel)) return s;
+  if (kvq_status s = check_ptr(k)) return s;
+  if (kvq_status s = check_cache(g, cache, false)) return s;
+  return hip_status(launch_select_qa(g, q_sel, n_qry, k, T, cache, (hipStream_t)stream));
+}
+
 kvq_status kvq_quant_keys(const kvq_layout* L, const void* k, int32_t T, kvq_cache* cache,
                           void* stream) {
   if (kvq_status s = check_layout(L)) return s;

@@ -7,6 +7,8 @@ namespace kvq {
 
 hipError_t launch_select(const Geo& g, const void* q_sel, int n_qry, const void* k, int T,
                          kvq_cache* c, hipStream_t st);
+hipError_t launch_select_qa(const Geo& g, const void* q_sel, int n_qry, const void* k, int T,
+                            kvq_cache* c, hipStream_t st);
 hipError_t launch_quant_keys(const Geo& g, const void* k, int T, kvq_cache* c, hipStream_t st);
 hipError_t launch_quant_values(const Geo& g, const void* v, int T, kvq_cache* c, hipStream_t st);
 hipError_t launch_shrink(const Geo& g, kvq_cache* c, int g0, int g1, hipStream_t st);

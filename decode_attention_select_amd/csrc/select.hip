@@ -111,4 +111,85 @@ hipError_t launch_select(const Geo& g, const void* q_sel, int n_qry, const void*
   return hipGetLastError();
 }
 
+// Query-aware channel score (MixKVQ, abstract and AI summary: a key
+// channel's importance joins its intrinsic quantization difficulty with its
+// relevance to the query; the page gives no formula, this is a reading).
+// Per (b, kv head) and channel c:
+//   A_c = sum over the group's query heads and selection queries of
+//         floor(|q_c| * 2^24)
+//   R_c = sum over the full 32-token groups of the prefill keys of
+//         floor(fp32(max k_c - min k_c) * 2^16)
+// and per pair S_j = R_j A_j + R_{j+64} A_{j+64} in IEEE double, each
+// product and the sum rounded once (no contraction).  Ranked descending,
+// ties to the lower pair id.  sums is scratch for R, then holds [0][j] = the
+// bits of S_j and [1][j] = 0.
+constexpr int QA_GROUPS_PER_BLOCK = 16;
+
+// grid (B * Hkv, ceil(groups / 16)); thread c sums channel c's ranges over
+// the block's groups (rows of 128 channels are read coalesced)
+__global__ __launch_bounds__(D) void qa_ranges_kernel(Geo g, const uint16_t* __restrict__ k,
+                                                      int T, uint64_t* __restrict__ sums) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  const int ng = T / GS;
+  const int g0 = blockIdx.y * QA_GROUPS_PER_BLOCK, g1 = min(ng, g0 + QA_GROUPS_PER_BLOCK);
+  const uint16_t* base = k + (size_t)bh * T * D;
+  uint64_t acc = 0;
+  for (int gi = g0; gi < g1; gi++) {
+    float mn = INFINITY, mx = -INFINITY;
+    for (int i = 0; i < GS; i++) {
+      const float x = in_to_f32(base[(size_t)(gi * GS + i) * D + c], g.bf16);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    acc += (uint64_t)((double)__fsub_rn(mx, mn) * 65536.0);  // non-negative: truncation = floor
+  }
+  if (acc) atomicAdd((unsigned long long*)&sums[(size_t)bh * D + c], (unsigned long long)acc);
+}
+
+// one workgroup of 128 threads per (b, kv head)
+__global__ __launch_bounds__(D) void qa_rank_kernel(Geo g, const uint16_t* __restrict__ q_sel,
+                                                    int n_qry, uint64_t* __restrict__ sums,
+                                                    int32_t* __restrict__ pairs) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  const int b = bh / g.Hkv, kh = bh % g.Hkv;
+  uint64_t A = 0;
+  for (int h = kh * g.G; h < (kh + 1) * g.G; h++)
+    for (int t = 0; t < n_qry; t++) {
+      const float x = fabsf(in_to_f32(q_sel[(((size_t)b * g.Hq + h) * n_qry + t) * D + c], g.bf16));
+      A += (uint64_t)((double)x * 16777216.0);
+    }
+  __shared__ uint64_t As[D], Rs[D];
+  __shared__ double S[NPAIR];
+  As[c] = A;
+  Rs[c] = sums[(size_t)bh * D + c];
+  __syncthreads();
+  if (c < NPAIR)
+    S[c] = __dadd_rn(__dmul_rn((double)Rs[c], (double)As[c]),
+                     __dmul_rn((double)Rs[c + NPAIR], (double)As[c + NPAIR]));
+  __syncthreads();
+  if (c < NPAIR) {
+    const double mine = S[c];
+    int rank = 0;
+    for (int i = 0; i < NPAIR; i++) rank += (S[i] > mine) || (S[i] == mine && i < c);
+    pairs[(size_t)bh * NPAIR + rank] = c;
+    sums[(size_t)bh * D + c] = __double_as_longlong(mine);
+  } else {
+    sums[(size_t)bh * D + c] = 0;
+  }
+}
+
+hipError_t launch_select_qa(const Geo& g, const void* q_sel, int n_qry, const void* k, int T,
+                            kvq_cache* c, hipStream_t st) {
+  const int nsum = g.B * g.Hkv * 2 * NPAIR;
+  hipLaunchKernelGGL(zero_u64_kernel, dim3((nsum + 255) / 256), dim3(256), 0, st, c->sums, nsum);
+  const int ng = T / GS;
+  if (ng > 0)
+    hipLaunchKernelGGL(qa_ranges_kernel,
+                       dim3(g.B * g.Hkv, (ng + QA_GROUPS_PER_BLOCK - 1) / QA_GROUPS_PER_BLOCK),
+                       dim3(D), 0, st, g, (const uint16_t*)k, T, c->sums);
+  hipLaunchKernelGGL(qa_rank_kernel, dim3(g.B * g.Hkv), dim3(D), 0, st, g,
+                     (const uint16_t*)q_sel, n_qry, c->sums, c->pairs);
+  return hipGetLastError();
+}
+
 }  // namespace kvq

@@ -106,6 +106,11 @@ def kvq_select_pairs(layout, q_sel, n_qry, k, T, cache: kvq_cache, stream=None):
           _ptr(k), ctypes.c_int32(T), ctypes.byref(cache), _stream(stream))
 
 
+def kvq_select_pairs_qa(layout, q_sel, n_qry, k, T, cache: kvq_cache, stream=None):
+    _call("kvq_select_pairs_qa", ctypes.byref(layout), _ptr(q_sel), ctypes.c_int32(n_qry),
+          _ptr(k), ctypes.c_int32(T), ctypes.byref(cache), _stream(stream))
+
+
 def kvq_quant_keys(layout, k, T, cache: kvq_cache, stream=None):
     _call("kvq_quant_keys", ctypes.byref(layout), _ptr(k), ctypes.c_int32(T),
           ctypes.byref(cache), _stream(stream))

@@ -168,6 +168,25 @@ kvq_status kvq_select_pairs(const kvq_layout *L, const void *q_sel,
                             int32_t n_qry, const void *k, int32_t T,
                             kvq_cache *cache, void *stream);
 
+/* Alternative pair selection by a query-aware channel score ([MixKVQ]
+ * abstract and AI summary: a key channel's importance joins its intrinsic
+ * quantization difficulty with its relevance to the query; the page gives
+ * no formula, so the score below is this library's reading).  Per (b, kv
+ * head) and channel c, with fixed-point sums:
+ *   A_c = sum over the G query heads and n_qry selection queries of
+ *         floor(|q_c| * 2^24)                          (relevance)
+ *   R_c = sum over the floor(T / 32) full 32-token groups of the prefill
+ *         keys of floor(fp32(max k_c - min k_c) * 2^16) (difficulty: the
+ *         range sets the quantization step)
+ *   S_j = R_j A_j + R_{j+64} A_{j+64}  (IEEE double, no contraction)
+ * pairs[] = pair ids by descending S_j, ties to the lower id;
+ * sums[0][j] = the bits of S_j as a double, sums[1][j] = 0.  Arguments and
+ * errors as for kvq_select_pairs, which it can replace before the
+ * quantization calls. */
+kvq_status kvq_select_pairs_qa(const kvq_layout *L, const void *q_sel,
+                               int32_t n_qry, const void *k, int32_t T,
+                               kvq_cache *cache, void *stream);
+
 /* Key quantization at prefill ([PN-Mix] abstract: salient pairs at higher
  * precision; [PM-KVQ] supporting_citations: keys per channel; [SemKV]
  * abstract: affine quantizer).  Requires cache->pairs from kvq_select_pairs.

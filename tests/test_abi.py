@@ -31,7 +31,8 @@ def test_library_exports_every_declared_entry_point():
     names = declared()
     assert set(names) >= {"kvq_select_pairs", "kvq_quant_keys", "kvq_quant_values",
                           "kvq_append", "kvq_decode_attn", "kvq_cache_sizes",
-                          "kvq_workspace_bytes", "kvq_check", "kvq_status_str", "kvq_shrink"}
+                          "kvq_workspace_bytes", "kvq_check", "kvq_status_str", "kvq_shrink",
+                          "kvq_select_pairs_qa"}
     lib = kvq.lib()
     for n in names:
         assert hasattr(lib, n), n

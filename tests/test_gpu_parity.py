@@ -210,3 +210,19 @@ def test_shrink_matches_oracle(g0, g1):
     check_output(case.decode(q, 8), ref, w.io_dtype, ATOL)
     _, part = case.decode(q, 1, partials=True)
     check_single_split(part, ref, ATOL)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=_ids)
+def test_select_qa_bit_exact(w):
+    # the query-aware channel score: scores (as double bits) and ranks
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    case = Case(w)
+    kvq.kvq_select_pairs_qa(case.layout, case.q_sel, w.n_qry, case.k_sel, w.tokens,
+                            case.cache.struct)
+    torch.cuda.synchronize()
+    S, pairs = oracle.select_qa(case.d["q_sel"], case.d["k"], w.tokens, w.n_kv_heads, w.io_dtype)
+    g = case.gpu_bytes()
+    assert np.array_equal(g["sums"][:, :, 0], S.view(np.uint64))
+    assert np.all(g["sums"][:, :, 1] == 0)
+    assert np.array_equal(g["pairs"], pairs)
