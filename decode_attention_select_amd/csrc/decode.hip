@@ -165,7 +165,10 @@ __device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int 
 //   ml   float2 [B*Hkv][S][G]        per split and head: running max m (log2
 //                                     units) and softmax denominator l
 //   o    fp16   [B*Hkv][S][G][128]   per split and head: o / l
-//   tick u32    [B*Hkv]              splits finished
+//   tick u32    [B*Hkv][64]          splits finished (word 0; each counter
+//                                     on a 256-byte line of its own, so the
+//                                     splits of different KV heads never
+//                                     contend for one line)
 struct Ws {
   float2* ml;
   uint16_t* o;
@@ -175,6 +178,7 @@ struct Ws {
 __host__ __device__ inline size_t ws_ml_bytes(int B, int Hq, int S) {
   return ((size_t)B * Hq * S * 8 + 255) & ~(size_t)255;
 }
+constexpr int TICK_STRIDE = 64;  // u32 words between counters (256 bytes)
 __host__ __device__ inline size_t ws_o_bytes(int B, int Hq, int S) {
   return ((size_t)B * Hq * S * D * 2 + 255) & ~(size_t)255;
 }
@@ -245,21 +249,27 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     for (int r = 0; r < 8; r++) top[r] = pr[r];
   }
 
-  // this split's 32-token blocks: quantized groups, then ring blocks
+  // The 32-token blocks of this (sequence, KV head): the nrb ring blocks
+  // first, then the quantized groups (block n >= nrb is group n - nrb).  A
+  // ring block has the longest latency chain, so it goes to the first split
+  // and is worked on while the group stream warms up.  Split s takes blocks
+  // [n0, n1); its waves take them round-robin.
   const int nq = n_quant(T, g.R), ngq = nq / GS;
   const int nrb = (T - nq + GS - 1) / GS;
   const int NB = ngq + nrb;
   const int n0 = (int)((long long)s * NB / S), n1 = (int)((long long)(s + 1) * NB / S);
-  const int nq_end = min(n1, ngq);
   const size_t rec0 = (size_t)bh * g.NG;
+  const int first = n0 + wave;  // this wave's blocks: first + i*NW < n1
+  const int i0 = first >= nrb ? 0 : (nrb - first + NW - 1) / NW;  // its first group block
 
-  // This wave's quantized groups are n0 + wave + i*NW, i < nmine.  Exactly PF
+  // This wave's quantized groups are gfirst + i*NW, i < nmine.  Exactly PF
   // group loads are kept in flight (past the end the index is clamped to the
   // wave's last group, or to group 0: cache hits, never used), so the
   // compiler can count outstanding loads and never drains the prefetches.
-  const int nmine = nq_end > n0 + wave ? (nq_end - (n0 + wave) + NW - 1) / NW : 0;
-  const int nlast = nmine > 0 ? n0 + wave + (nmine - 1) * NW : 0;
-  auto group_at = [&](int i) { return rec0 + (size_t)min(n0 + wave + i * NW, nlast); };
+  const int gfirst = first + i0 * NW - nrb;  // >= 0
+  const int nmine = first + i0 * NW < n1 ? (n1 - (first + i0 * NW) + NW - 1) / NW : 0;
+  const int nlast = nmine > 0 ? gfirst + (nmine - 1) * NW : 0;
+  auto group_at = [&](int i) { return rec0 + (size_t)min(gfirst + i * NW, nlast); };
   Pref pf[PF];
   if constexpr (HASQ) {
 #pragma unroll
@@ -450,45 +460,37 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     }
   };
 
-  if constexpr (HASQ) {
-    for (int i = 0; i < nmine; i += PF) {
-#pragma unroll
-      for (int k = 0; k < PF; k++) {
-        if (i + k < nmine) process_group(pf[k], group_at(i + k));
-        load_group<HIMODE>(c, group_at(i + k + PF), lane, col, kq, g.nh, pf[k]);
-      }
-    }
-  }
-
-  // ring blocks (16-bit keys and values): blocks n >= ngq of this split
-  for (int n = n0 + wave; n < n1; n += NW) {
-    if (n < ngq) continue;
-    const int pbase = nq + GS * (n - ngq);
+  // ring blocks (16-bit keys and values) of this wave: blocks n < nrb.  Key
+  // and value tiles are requested together (one round trip); the query is
+  // the raw one already in registers.
+  for (int n = first; n < min(n1, nrb); n += NW) {
+    const int pbase = nq + GS * n;
     const int nvalid = min(GS, T - pbase);
     const int sb = (pbase / GS) % (g.RS / GS);
     const uint16_t* rk = (const uint16_t*)c.ring_k + ((size_t)bh * g.RS + sb * GS) * D;
-    uint32_t qraw[16];
-    {
-      // the group stream is done here: a fresh query read waits for nothing
-      const u4* qp =
-          (const u4*)(q + ((size_t)b * g.Hq + kh * G + min(col, G - 1)) * D + 32 * kq);
+    const uint16_t* rv = (const uint16_t*)c.ring_v + (((size_t)bh * (g.RS / GS) + sb) * D) * GS;
+    u4 kt[2][4], vt[8];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const u4 v = qp[i];
+    for (int TT = 0; TT < 2; TT++) {
+      const u4* kr = (const u4*)(rk + (size_t)tile_token(16 * TT + col) * D + 32 * kq);
 #pragma unroll
-        for (int e = 0; e < 4; e++) qraw[4 * i + e] = hvalid ? v[e] : 0u;
-      }
+      for (int k = 0; k < 4; k++) kt[TT][k] = kr[k];
     }
+#pragma unroll
+    for (int tt = 0; tt < 8; tt++) vt[tt] = *(const u4*)(rv + (size_t)(16 * tt + col) * GS + 8 * kq);
+    uint32_t qraw[16];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) qraw[4 * i + e] = hvalid ? qv[i][e] : 0u;
     f4 C[2];
 #pragma unroll
     for (int TT = 0; TT < 2; TT++) {
-      const int t = tile_token(16 * TT + col);
-      const u4* kr = (const u4*)(rk + (size_t)t * D + 32 * kq);
       f4 acc = {0, 0, 0, 0};
 #pragma unroll
       for (int k = 0; k < 4; k++)
-        acc = mma_raw<BF16>(kr[k], u4{qraw[4 * k], qraw[4 * k + 1], qraw[4 * k + 2], qraw[4 * k + 3]},
-                            acc);
+        acc = mma_raw<BF16>(kt[TT][k],
+                            u4{qraw[4 * k], qraw[4 * k + 1], qraw[4 * k + 2], qraw[4 * k + 3]}, acc);
       C[TT] = acc;
     }
     float cr[8], p[8];
@@ -503,10 +505,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     uint32_t Ph[4], Pl[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) split_pair<BF16>(p[2 * i], p[2 * i + 1], Ph[i], Pl[i]);
-    const uint16_t* rv = (const uint16_t*)c.ring_v + (((size_t)bh * (g.RS / GS) + sb) * D) * GS;
 #pragma unroll
     for (int tt = 0; tt < 8; tt++) {
-      u4 a = *(const u4*)(rv + (size_t)(16 * tt + col) * GS + 8 * kq);
+      u4 a = vt[tt];
       // zero slots past the last token (they may hold stale data)
 #pragma unroll
       for (int e = 0; e < 4; e++) {
@@ -517,6 +518,16 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       }
       O[tt] = mma_raw<BF16>(a, u4{Ph[0], Ph[1], Ph[2], Ph[3]}, O[tt]);
       O[tt] = mma_raw<BF16>(a, u4{Pl[0], Pl[1], Pl[2], Pl[3]}, O[tt]);
+    }
+  }
+
+  if constexpr (HASQ) {
+    for (int i = 0; i < nmine; i += PF) {
+#pragma unroll
+      for (int k = 0; k < PF; k++) {
+        if (i + k < nmine) process_group(pf[k], group_at(i + k));
+        load_group<HIMODE>(c, group_at(i + k + PF), lane, col, kq, g.nh, pf[k]);
+      }
     }
   }
 
@@ -576,7 +587,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   __syncthreads();
   if (tid == 0) {
     const uint32_t prev =
-        __hip_atomic_fetch_add(&ws.tick[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&ws.tick[(size_t)bh * TICK_STRIDE], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     lds.last = prev == (uint32_t)(S - 1);
   }
   __syncthreads();
@@ -655,7 +667,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     }
   }
   if (tid == 0)  // ready for the next call
-    __hip_atomic_store(&ws.tick[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws.tick[(size_t)bh * TICK_STRIDE], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool BF16, int HIMODE, bool LO1>
@@ -679,7 +692,7 @@ static void launch_lo1(const Geo& g, const void* q, const kvq_cache* c, float sc
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {
-  return ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S) + (((size_t)B * Hkv * 4 + 255) & ~(size_t)255);
+  return ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S) + (size_t)B * Hkv * TICK_STRIDE * 4;
 }
 
 hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float sm_scale,

@@ -141,8 +141,8 @@ kvq_status kvq_cache_sizes(const kvq_layout *L, size_t sizes[KVQ_NBUF] /*host*/)
 /* Workspace bytes kvq_decode_attn needs for `n_splits` token splits per
  * (sequence, KV head), 1 <= n_splits <= 1024: per query head and split one
  * fp32 (running max, sum) record, then one fp16 [128] normalized partial
- * output, then one 32-bit counter per (sequence, KV head); each part starts
- * on a 256-byte boundary.  The caller
+ * output, then one 32-bit counter per (sequence, KV head), each on a
+ * 256-byte line of its own; each part starts on a 256-byte boundary.  The caller
  * zero-fills a workspace once before its first use; every completed call
  * leaves the counters at zero again.  One workspace serves one call at a
  * time. */

@@ -90,7 +90,7 @@ def test_workspace_bytes():
     L = L32k()
     assert kvq.kvq_workspace_bytes(L, 1) < kvq.kvq_workspace_bytes(L, 32)
     rec = 32 * 32  # query heads x splits
-    want = (rec * 8 + 255) // 256 * 256 + (rec * 256 + 255) // 256 * 256 + 256
+    want = (rec * 8 + 255) // 256 * 256 + (rec * 256 + 255) // 256 * 256 + 8 * 256
     assert kvq.kvq_workspace_bytes(L, 32) == want
     n = ctypes.c_size_t(0)
     for S in (0, 1025, -1):
