@@ -199,6 +199,7 @@ struct LdsLoop {
   uint16_t qraw[NW][MAXG][D + 8];  // per wave: query in the io dtype (16-bit salient keys)
   uint32_t stage[NW][256];         // per wave: metadata record of the group in work
   int hil[NW][16];                 // per wave: salient channels, ascending
+  uint16_t sal_s[NW][16];          // per wave: scales of the salient channels, group in work
 };
 struct LdsMerge {
   float o[NW][MAXG][D + 4];        // wave results before the workgroup merge (padded rows)
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 
   uint32_t qhi[4] = {0, 0, 0, 0};  // HIMODE 4: 4*q (fp16); HIMODE 16: raw q
   float q4f[8];                    // HIMODE 4: 4*q in fp32
-  int hch[8];                      // salient channel of digit 8*(kq&1) + e
+  int sal_ch = 0;                  // HIMODE 4: salient channel whose scale lane%16 copies
   if constexpr (HIMODE != 0) {
     // per-wave tables: this wave's query rows and the salient channels
     // (pairs of rank < n_hi ascending, then the same + 64)
@@ -318,13 +319,14 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       // HIMODE 4: K-lanes 16..31 (kq 2, 3) repeat the digits of lanes 0..15
       // and carry the rounding residual of 4*q*s; HIMODE 16 uses lanes 0..15
       const bool ok = hvalid && d < g.nh && (HIMODE == 4 || kq < 2);
-      hch[e] = ok ? (hil[d] & (D - 1)) : 0;
-      const float v = ok ? half_bits_to_f32(wq[col][hch[e]]) : 0.0f;
+      const int ch = ok ? (hil[d] & (D - 1)) : 0;
+      const float v = ok ? half_bits_to_f32(wq[col][ch]) : 0.0f;
       q4f[e] = 4.0f * v;
       const uint32_t bits = HIMODE == 4 ? (uint32_t)f32_to_half_bits(4.0f * v)
-                                        : (ok ? (uint32_t)wr[col][hch[e]] : 0u);
+                                        : (ok ? (uint32_t)wr[col][ch] : 0u);
       qhi[e >> 1] |= bits << (16 * (e & 1));
     }
+    sal_ch = hil[lane & 15] & (D - 1);
   }
 
   float m_run = -INFINITY, l_raw = 0.0f;
@@ -390,12 +392,18 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     }
     uint32_t qshi[4];
     if constexpr (HIMODE == 4) {
-      const uint16_t* ks = (const uint16_t*)sm;
+      // the salient channels' scales, gathered once into a contiguous row
+      // (lane l copies digit l%16), then read 8 at a time
+      uint16_t* ss = lds.u.loop.sal_s[wave];
+      ss[lane & 15] = ((const uint16_t*)sm)[sal_ch];
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+      const u4 spv = *(const u4*)(ss + 8 * (kq & 1));
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         // 4*q*s is exact in fp32; split it into its fp16 rounding hi and the
         // fp16 residual lo
-        const uint32_t sp = (uint32_t)ks[hch[2 * e]] | ((uint32_t)ks[hch[2 * e + 1]] << 16);
+        const uint32_t sp = spv[e];
         const uint32_t hi = pk_mul(qhi[e], sp);
         const h2 sh = u2h(sp), hh = u2h(hi);
         const uint32_t lo = pk_rne(fmaf(q4f[2 * e], (float)sh[0], -(float)hh[0]),
