@@ -333,6 +333,122 @@ def pareto_leg(args, w):
     }
 
 
+def prefill_leg(args, w):
+    """The calls that build a cache, each timed on its own over the workload:
+    pair selection (kvq_select_pairs and the query-aware kvq_select_pairs_qa),
+    key and value quantization, and the precision shrink of every quantized
+    group.  Inputs rotate over replicas (together >= --replica-mib) so that
+    the 256 MB Infinity Cache cannot serve them.  Algorithmic bytes per call:
+      select:        queries + keys read, ranks and sums written;
+      quant_keys:    keys read; per quantized token the key codes at their
+                     bits plus scale/zero, per ring token 256 B, written;
+      quant_values:  values read; per quantized token 32 B codes + 16 B
+                     scale/zero, per ring token 256 B, written;
+      shrink:        the salient channels' 4-bit codes read and written."""
+    import numpy as np
+    import torch
+
+    import kvq_synth
+    from decode_attention_select_amd import kvq
+
+    T = w.tokens
+    data = kvq_synth.generate(w)
+    layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads, n_pairs_hi=w.n_pairs_hi,
+                             bits_hi=w.bits_hi, residual=w.residual, max_tokens=T,
+                             io_dtype=w.io_dtype)
+    cache = kvq.Cache(layout)
+    k0, v0, q0 = dev(data["k"][:, :, :T]), dev(data["v"][:, :, :T]), dev(data["q_sel"])
+    n_rep = max(1, math.ceil(args.replica_mib * 2 ** 20 / (k0.numel() * 2)))
+    ks = [k0] + [k0.clone() for _ in range(n_rep - 1)]
+    vs = [v0] + [v0.clone() for _ in range(n_rep - 1)]
+    qs = [q0] + [q0.clone() for _ in range(n_rep - 1)]
+    stream = torch.cuda.current_stream()
+    st = lambda f: (lambda i: f(i % n_rep))
+    nq = 32 * (max(0, T - w.residual) // 32)
+    nr, bh = T - nq, w.batch * w.n_kv_heads
+    kv_in = bh * T * 256
+    q_in = w.batch * w.n_q_heads * w.n_qry * 256
+    sel_out = bh * (64 * 4 + 2 * 64 * 8)
+    n_hi_ch = 2 * w.n_pairs_hi
+    if w.bits_hi == 16:
+        k_tok = (n_hi_ch * 16 + (128 - n_hi_ch) * 2) / 8 + (128 - n_hi_ch) * 4 / 32
+    else:
+        k_tok = (n_hi_ch * w.bits_hi + (128 - n_hi_ch) * 2) / 8 + 16
+    calls = [
+        ("kvq_select_pairs", q_in + kv_in + sel_out,
+         st(lambda i: kvq.kvq_select_pairs(layout, qs[i], w.n_qry, ks[i], T, cache.struct,
+                                           stream=stream))),
+        ("kvq_select_pairs_qa", q_in + kv_in + sel_out,
+         st(lambda i: kvq.kvq_select_pairs_qa(layout, qs[i], w.n_qry, ks[i], T, cache.struct,
+                                              stream=stream))),
+        ("kvq_quant_keys", kv_in + int(bh * (nq * k_tok + nr * 256)),
+         st(lambda i: kvq.kvq_quant_keys(layout, ks[i], T, cache.struct, stream=stream))),
+        ("kvq_quant_values", kv_in + bh * (nq * 48 + nr * 256),
+         st(lambda i: kvq.kvq_quant_values(layout, vs[i], T, cache.struct, stream=stream))),
+    ]
+    res_calls = []
+    for name, alg, f in calls:
+        for i in range(args.warmup):
+            f(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(args.steps):
+            f(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+        res_calls.append({"call": name, "us": round(us, 3), "algorithmic_bytes": alg,
+                          "GBs": round(alg / (us * 1e-6) / 1e9, 1)})
+    # shrink: a fresh quantization before every timed call (outside the timing),
+    # so that each call shrinks 4-bit codes of every quantized group
+    ng = nq // 32
+    sh_alg = 2 * bh * nq * n_hi_ch * 4 // 8
+    tot = 0.0
+    for i in range(args.warmup + args.steps if w.bits_hi == 4 and w.n_pairs_hi else 0):
+        kvq.kvq_quant_keys(layout, ks[i % n_rep], T, cache.struct, stream=stream)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        kvq.kvq_shrink(layout, cache.struct, 0, ng, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            tot += ev0.elapsed_time(ev1) * 1e3
+    us = tot / args.steps
+    if tot:
+        res_calls.append({"call": "kvq_shrink", "us": round(us, 3), "algorithmic_bytes": sh_alg,
+                          "GBs": round(sh_alg / (us * 1e-6) / 1e9, 1),
+                          "note": "one launch per call, timed alone; a plain event pair around "
+                                  "one launch also holds the launch latency"})
+    build = [c for c in res_calls if c["call"] in ("kvq_select_pairs", "kvq_quant_keys",
+                                                   "kvq_quant_values")]
+    b_us = sum(c["us"] for c in build)
+    b_alg = sum(c["algorithmic_bytes"] for c in build)
+    gbs = b_alg / (b_us * 1e-6) / 1e9
+    return {
+        "metric": "cache build (select + quantize keys + quantize values): \u00b5s, "
+                  "effective HBM GB/s, % of 8 TB/s peak",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(b_us * 1e-3, 5),
+        "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (min/max, codes) / u64 (saliency sums)",
+        "data": "synthetic (seeded N(0,1) + outlier key pairs, RoPE)",
+        "config": {"workload": w.name + " (cache build)", "batch": w.batch,
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "context": T,
+                   "selection_queries": w.n_qry, "io_dtype": w.io_dtype,
+                   "salient_pairs": w.n_pairs_hi, "salient_bits": w.bits_hi,
+                   "residual": w.residual, "input_replicas": n_rep},
+        "calls": res_calls,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -342,6 +458,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--replica-mib", type=int, default=512)
+    ap.add_argument("--build", action="store_true",
+                    help="time the cache-building calls on the workload instead of decode")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run the copy-kernel calibration of this size")
     args = ap.parse_args()
@@ -360,6 +478,9 @@ def main():
     from decode_attention_select_amd import kvq
 
     w = kvq_synth.workload(args.workload)
+    if args.build:
+        print(json.dumps(prefill_leg(args, w)), flush=True)
+        return
     if w.n_app:
         print(json.dumps(streaming_leg(args, w)), flush=True)
         return

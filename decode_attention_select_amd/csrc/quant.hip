@@ -8,179 +8,413 @@
 // 32 channels.  Recent tokens stay 16-bit in a ring (PM-KVQ review,
 // key_machinery and supporting_citations: 16-bit first, quantized later).
 //
-// One 256-thread block packs one 32-token group: 128 threads quantize (one
-// key channel, or one value (token, channel group) each) into a 32x128 code
-// tile in LDS, then all 256 threads assemble one 32-bit word each of the
-// layout in include/kvq.h.
+// One wave quantizes one 32-token group.  Each lane holds an 8 x 8 block of
+// the group (8 tokens x 8 channels, two 16-byte loads' worth per token row),
+// so a group is eight 16-byte loads per lane.  The min/max reductions run
+// in registers and across the four lanes of a DPP quad:
+//   keys:   lane = 4 * cb + tq  (channels 8cb..8cb+7, tokens 8tq..8tq+7);
+//           a channel's 32 tokens lie in one quad.
+//   values: lane = 16 * tq + cb; a token's 32-channel group (4 chunks of 8)
+//           lies in one quad.
+// Each quad lane computes the scale, zero and reciprocal of two of the
+// quad's eight channels (or tokens) and hands them to the others by DPP
+// broadcast, so each division runs once per quad.
 #include "common.h"
 #include "internal.h"
 
 namespace kvq {
 
-constexpr int QTHREADS = 256;
+constexpr int QWAVES = 4;                 // groups per prefill workgroup, one per wave
+constexpr int QTHREADS = 64 * QWAVES;
+constexpr int RING_ROWS = QTHREADS / 16;  // ring-fill rows per workgroup (16 B per thread)
 
-struct GroupLds {
-  uint8_t codes[GS][D];  // [token][channel]
-  int salient[D];        // 1 if channel c belongs to a salient pair
-  int hil[16];           // salient channels, ascending
-};
+// ------------------------------------------------------------ lane exchange
 
-// Source of one group's 16-bit values: src(t, c) = bits of token t (0..31 in
-// the group), channel c.
-struct DenseSrc {  // prefill input [..][T][128], group starting at token t0
-  const uint16_t* base;
-  __device__ uint16_t operator()(int t, int c) const { return base[(size_t)t * D + c]; }
+template <int CTRL>
+__device__ inline uint32_t dpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+constexpr int QUAD_XOR1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int QUAD_XOR2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+template <int K>
+struct QuadBcast {  // quad_perm [K, K, K, K]
+  static constexpr int ctrl = K | (K << 2) | (K << 4) | (K << 6);
 };
-struct RingKSrc {  // ring_k [RS][128] of one (b, kv head), group at slot s0
-  const uint16_t* base;
-  int s0;
-  __device__ uint16_t operator()(int t, int c) const { return base[(size_t)(s0 + t) * D + c]; }
-};
-struct RingVSrc {  // ring_v [RS/32][128][32] of one (b, kv head), slot block sb
-  const uint16_t* block;
-  __device__ uint16_t operator()(int t, int c) const { return block[(size_t)c * GS + t]; }
-};
+template <int K>
+__device__ inline uint32_t quad_bcast(uint32_t x) { return dpp<QuadBcast<K>::ctrl>(x); }
 
-template <class Src>
-__device__ void quant_key_group(const Geo& g, const Src& src, const int32_t* pairs,
-                                uint32_t* lo_out, void* hi_out, uint16_t* meta_out,
-                                GroupLds& lds) {
-  const int tid = threadIdx.x;
-  if (tid < D) {
-    const int c = tid, pj = c & (NPAIR - 1);
-    int sal = 0, one = 0;
-    for (int r = 0; r < g.n_hi; r++) sal |= pairs[r] == pj;
-    for (int r = NPAIR - g.n_lo1; r < NPAIR; r++) one |= pairs[r] == pj;
-    lds.salient[c] = sal;
-    // salient pairs at bits_hi, the n_lo1 lowest-ranked pairs at one bit
-    // (their codes 0/1 sit in the 2-bit slots of k_lo), the rest at 2 bits
-    const int bits = sal ? g.bits_hi : (one ? 1 : 2);
-    uint16_t s = 0, z = 0;
-    uint8_t codes[GS];
-    if (bits == 16) {
-#pragma unroll
-      for (int i = 0; i < GS; i++) codes[i] = 0;
-    } else {
-      float x[GS];
-#pragma unroll
-      for (int i = 0; i < GS; i++) x[i] = in_to_f32(src(i, c), g.bf16);
-      quantize_group(x, (1 << bits) - 1, s, z, codes);
-    }
-#pragma unroll
-    for (int i = 0; i < GS; i++) lds.codes[i][c] = codes[i];
-    meta_out[c] = s;
-    meta_out[D + c] = z;
-  }
-  __syncthreads();
-  if (tid < D && lds.salient[tid]) {
-    int idx = 0;
-    for (int c = 0; c < tid; c++) idx += lds.salient[c];
-    lds.hil[idx] = tid;
-  }
-  {
-    // low two bits of every channel's code, token-major in tile order
-    const int wi = tid, u = wi & 1, r = (wi >> 1) & 15, kq = (wi >> 5) & 3, T = wi >> 7;
-    const int t = tile_token(16 * T + r), w = 2 * kq + u;
-    uint32_t word = 0;
-#pragma unroll
-    for (int cc = 0; cc < 16; cc++)
-      word |= (uint32_t)(lds.codes[t][16 * w + cc] & 3) << (2 * pos_swap(cc));
-    lo_out[wi] = word;
-  }
-  __syncthreads();
-  if (g.nh && g.bits_hi == 4 && tid < GS) {
-    const int t = tile_token(tid);
-    uint32_t word = 0;
-    for (int d = 0; d < g.nh; d++)
-      word |= (uint32_t)(lds.codes[t][lds.hil[d]] >> 2) << (2 * pos_swap(d));
-    ((uint32_t*)hi_out)[tid] = word;
-  } else if (g.nh && g.bits_hi == 16) {
-    for (int idx = tid; idx < GS * g.nh; idx += QTHREADS) {
-      const int e = idx / g.nh, d = idx % g.nh;
-      ((uint16_t*)hi_out)[idx] = src(tile_token(e), lds.hil[d]);
-    }
-  }
-  __syncthreads();
+// min and max over the quad.  The result is the quad's min/max value;
+// only the sign of a zero minimum depends on the combining order, and the
+// caller settles that separately (sign_of_first_zero).
+__device__ inline float quad_min(float v) {
+  float p = __uint_as_float(dpp<QUAD_XOR1>(__float_as_uint(v)));
+  v = p < v ? p : v;
+  p = __uint_as_float(dpp<QUAD_XOR2>(__float_as_uint(v)));
+  return p < v ? p : v;
+}
+__device__ inline float quad_max(float v) {
+  float p = __uint_as_float(dpp<QUAD_XOR1>(__float_as_uint(v)));
+  v = p > v ? p : v;
+  p = __uint_as_float(dpp<QUAD_XOR2>(__float_as_uint(v)));
+  return p > v ? p : v;
 }
 
-template <class Src>
-__device__ void quant_value_group(const Geo& g, const Src& src, uint32_t* vc_out,
-                                  uint16_t* meta_out, GroupLds& lds) {
-  const int tid = threadIdx.x;
-  if (tid < D) {
-    const int t = tid >> 2, j = tid & 3;
-    float x[GS];
+// A sequential scan keeps the first of equal minima, so a minimum of zero
+// carries the sign of the group's first zero element.  f = this lane's
+// first zero in its eight elements (0: +0, 1: -0, 2: none), lanes of the
+// quad in element order; returns the sign bit of the quad's first zero.
+__device__ inline uint32_t sign_of_first_zero(uint32_t f) {
+  const uint32_t f0 = quad_bcast<0>(f), f1 = quad_bcast<1>(f), f2 = quad_bcast<2>(f),
+                 f3 = quad_bcast<3>(f);
+  const uint32_t s = f0 != 2 ? f0 : f1 != 2 ? f1 : f2 != 2 ? f2 : f3;
+  return s == 1 ? 0x80000000u : 0u;
+}
+
+// 16-bit element e (0..7) of a 16-byte row chunk, widened to fp32.
+__device__ inline uint16_t half_of(const uint4& v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xFFFF);
+}
+
+// Affine parameters of one group at L levels (the quantizer of common.h):
+// z = fp16(min), s = fp16((max - z) / L) or 0, r = 1 / s (0 when s == 0).
+struct QParam {
+  uint32_t sz;  // s bits | z bits << 16
+  float r;
+};
+__device__ inline QParam qparam(float mn, float mx, float L, bool raw) {
+  if (raw) return {0u, 0.0f};
+  const uint16_t zb = f32_to_half_bits(mn);
+  const float diff = __fsub_rn(mx, half_bits_to_f32(zb));
+  const uint16_t sb = diff > 0.0f ? f32_to_half_bits(__fdiv_rn(diff, L)) : (uint16_t)0;
+  const float r = sb ? __fdiv_rn(1.0f, half_bits_to_f32(sb)) : 0.0f;
+  return {(uint32_t)sb | ((uint32_t)zb << 16), r};
+}
+
+// code = clamp(rint((x - z) * r), 0, L); 0 when r == 0 (s == 0).
+__device__ inline uint32_t qcode(float x, float z, float r, float L) {
+  float q = rintf(__fmul_rn(__fsub_rn(x, z), r));
+  q = q < 0.0f ? 0.0f : q;
+  q = q > L ? L : q;
+  return (uint32_t)q;
+}
+
+// Marks the loaded words as changed, so that widened copies made before are
+// not kept alive in registers (widening again costs one instruction each).
+__device__ inline void refresh(uint4 (&v)[8]) {
 #pragma unroll
-    for (int i = 0; i < GS; i++) x[i] = in_to_f32(src(t, GS * j + i), g.bf16);
-    uint16_t s, z;
-    uint8_t codes[GS];
-    quantize_group(x, 3, s, z, codes);
+  for (int i = 0; i < 8; i++)
+    asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+}
+
+// Compiler barrier for LDS traffic between lanes of one wave (the hardware
+// runs a wave's LDS instructions in order).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bit j set when pair j has rank < n_hi (salient), rank >= 64 - n_lo1 (one bit).
+struct PairMasks {
+  uint64_t hi, one;
+};
+__device__ inline PairMasks pair_masks(const Geo& g, const int32_t* pr) {
+  uint64_t hi = 0, one = 0;
+  for (int r = 0; r < g.n_hi; r++) hi |= 1ull << (pr[r] & (NPAIR - 1));
+  for (int r = NPAIR - g.n_lo1; r < NPAIR; r++) one |= 1ull << (pr[r] & (NPAIR - 1));
+  return {hi, one};
+}
+
+// ------------------------------------------------------------- key group
+
+struct KeyLds {  // one wave's staging of a key-group record
+  uint32_t lo[GROUP_WORDS];
+  uint32_t hi[256];  // 4-bit: 32 words; raw 16-bit: 32 tokens x up to 16 halves
+};
+
+// rows: token 0 of the group, row stride D (prefill input or ring_k slots).
+__device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
+                               uint32_t* lo_out, uint8_t* hi_out, uint16_t* meta_out,
+                               KeyLds& L) {
+  const int lane = threadIdx.x & 63, cb = lane >> 2, tq = lane & 3;
+  uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < GS; i++) lds.codes[t][GS * j + i] = codes[i];
-    meta_out[j * GS + t] = s;
-    meta_out[D + j * GS + t] = z;
+  for (int i = 0; i < 8; i++) v[i] = *(const uint4*)(rows + (size_t)(8 * tq + i) * D + 8 * cb);
+
+  const bool bits4 = g.nh > 0 && g.bits_hi == 4, raw16 = g.nh > 0 && g.bits_hi == 16;
+  // bit allocation of the lane's channels 8cb + k
+  float lv[8];
+  bool raw[8];
+  int hish[8], dix[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const int c = 8 * cb + k, j = c & (NPAIR - 1);
+    const bool sal = (pm.hi >> j) & 1, one = (pm.one >> j) & 1;
+    dix[k] = __popcll(pm.hi & ((1ull << j) - 1)) + (c >= NPAIR ? g.n_hi : 0);
+    raw[k] = sal && g.bits_hi == 16;
+    lv[k] = sal ? 15.0f : (one ? 1.0f : 3.0f);
+    hish[k] = sal ? 2 * pos_swap(dix[k]) : 0;
   }
-  __syncthreads();
-  {
-    const int wi = tid, c = wi & 15, kq = (wi >> 4) & 3, j = wi >> 6;
-    uint32_t word = 0;
+  // per-channel min / max over the 32 tokens
+  float mn[8], mx[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    float a = in_to_f32(half_of(v[0], k), g.bf16), b = a;
+#pragma unroll
+    for (int i = 1; i < 8; i++) {
+      const float x = in_to_f32(half_of(v[i], k), g.bf16);
+      a = x < a ? x : a;
+      b = x > b ? x : b;
+    }
+    mn[k] = quad_min(a);
+    mx[k] = quad_max(b);
+  }
+  bool zmin = false;
+#pragma unroll
+  for (int k = 0; k < 8; k++) zmin |= mn[k] == 0.0f;
+  if (__any(zmin)) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      uint32_t f = 2;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float x = in_to_f32(half_of(v[i], k), g.bf16);
+        if (f == 2 && x == 0.0f) f = __float_as_uint(x) >> 31;
+      }
+      const uint32_t sgn = sign_of_first_zero(f);
+      if (mn[k] == 0.0f) mn[k] = __uint_as_float(sgn);
+    }
+  }
+  // lane tq computes channels 2tq and 2tq+1 of the quad's eight
+  auto pick = [&](const float (&a)[8], int o) {
+    return tq == 0 ? a[o] : tq == 1 ? a[2 + o] : tq == 2 ? a[4 + o] : a[6 + o];
+  };
+  auto pickb = [&](const bool (&a)[8], int o) {
+    return tq == 0 ? a[o] : tq == 1 ? a[2 + o] : tq == 2 ? a[4 + o] : a[6 + o];
+  };
+  const QParam p0 = qparam(pick(mn, 0), pick(mx, 0), pick(lv, 0), pickb(raw, 0));
+  const QParam p1 = qparam(pick(mn, 1), pick(mx, 1), pick(lv, 1), pickb(raw, 1));
+  uint32_t sz[8];
+  float rr[8];
+#define KVQ_BCAST(K)                                                              \
+  sz[2 * K] = quad_bcast<K>(p0.sz);                                              \
+  sz[2 * K + 1] = quad_bcast<K>(p1.sz);                                          \
+  rr[2 * K] = __uint_as_float(quad_bcast<K>(__float_as_uint(p0.r)));             \
+  rr[2 * K + 1] = __uint_as_float(quad_bcast<K>(__float_as_uint(p1.r)));
+  KVQ_BCAST(0) KVQ_BCAST(1) KVQ_BCAST(2) KVQ_BCAST(3)
+#undef KVQ_BCAST
+
+  // codes: low digits into half-words, high digits of 4-bit channels
+  refresh(v);
+  uint32_t hw[8], hh[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) hw[i] = hh[i] = 0;
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const float z = half_bits_to_f32((uint16_t)(sz[k] >> 16));
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const int t = 8 * kq + i, p = 2 * pos_swap(i);
-      word |= (uint32_t)lds.codes[t][GS * j + c] << p;
-      word |= (uint32_t)lds.codes[t][GS * j + 16 + c] << (16 + p);
+      const uint32_t code = qcode(in_to_f32(half_of(v[i], k), g.bf16), z, rr[k], lv[k]);
+      hw[i] |= (code & 3u) << (2 * pos_swap(k));
+      if (bits4) hh[i] |= (code >> 2) << hish[k];
     }
-    vc_out[wi] = word;
   }
-  __syncthreads();
+  // stage the record in LDS: token i of this lane is tile index
+  // e = 16 T + r with T = i / 4, r = 4 tq + i % 4
+  if (lane < 8) ((uint4*)L.hi)[lane] = make_uint4(0, 0, 0, 0);
+  wave_lds_sync();
+  const int w = cb >> 1, kq = w >> 1, u = w & 1, half = cb & 1;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int T = i >> 2, r = 4 * tq + (i & 3);
+    ((uint16_t*)L.lo)[(((T * 4 + kq) * 16 + r) * 2 + u) * 2 + half] = (uint16_t)hw[i];
+    if (bits4 && hh[i]) atomicOr(&L.hi[16 * T + r], hh[i]);
+  }
+  if (raw16) {
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+      if (raw[k]) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const int e = 16 * (i >> 2) + 4 * tq + (i & 3);
+          ((uint16_t*)L.hi)[e * g.nh + dix[k]] = half_of(v[i], k);
+        }
+      }
+  }
+  wave_lds_sync();
+  ((uint4*)lo_out)[lane] = ((const uint4*)L.lo)[lane];
+  if (lane < g.khi_bytes / 16) ((uint4*)hi_out)[lane] = ((const uint4*)L.hi)[lane];
+  if (tq < 2) {
+    uint32_t m[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++)
+      m[p] = tq == 0 ? (sz[2 * p] & 0xFFFFu) | (sz[2 * p + 1] << 16)
+                     : (sz[2 * p] >> 16) | (sz[2 * p + 1] & 0xFFFF0000u);
+    *(uint4*)(meta_out + tq * D + 8 * cb) = make_uint4(m[0], m[1], m[2], m[3]);
+  }
+}
+
+// ----------------------------------------------------------- value group
+
+// CHMAJOR false: src = token 0 of the group, row stride D (prefill input).
+// CHMAJOR true:  src = a ring_v slot block [128][32] (channel, slot).
+template <bool CHMAJOR>
+__device__ void value_group_wave(const Geo& g, const uint16_t* src, uint32_t* vc_out,
+                                 uint16_t* meta_out) {
+  const int lane = threadIdx.x & 63, cb = lane & 15, tq = lane >> 4, m = cb & 3, j = cb >> 2;
+  // x(i, k): token 8tq + i, channel 8cb + k
+  uint4 v[8];
+#pragma unroll
+  for (int n = 0; n < 8; n++)
+    v[n] = CHMAJOR ? *(const uint4*)(src + (size_t)(8 * cb + n) * GS + 8 * tq)
+                   : *(const uint4*)(src + (size_t)(8 * tq + n) * D + 8 * cb);
+  auto x = [&](int i, int k) {
+    return in_to_f32(CHMAJOR ? half_of(v[k], i) : half_of(v[i], k), g.bf16);
+  };
+  float mn[8], mx[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    float a = x(i, 0), b = a;
+#pragma unroll
+    for (int k = 1; k < 8; k++) {
+      const float e = x(i, k);
+      a = e < a ? e : a;
+      b = e > b ? e : b;
+    }
+    mn[i] = quad_min(a);
+    mx[i] = quad_max(b);
+  }
+  bool zmin = false;
+#pragma unroll
+  for (int i = 0; i < 8; i++) zmin |= mn[i] == 0.0f;
+  if (__any(zmin)) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      uint32_t f = 2;
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const float e = x(i, k);
+        if (f == 2 && e == 0.0f) f = __float_as_uint(e) >> 31;
+      }
+      const uint32_t sgn = sign_of_first_zero(f);
+      if (mn[i] == 0.0f) mn[i] = __uint_as_float(sgn);
+    }
+  }
+  auto pick = [&](const float (&a)[8], int o) {
+    return m == 0 ? a[o] : m == 1 ? a[2 + o] : m == 2 ? a[4 + o] : a[6 + o];
+  };
+  const QParam p0 = qparam(pick(mn, 0), pick(mx, 0), 3.0f, false);
+  const QParam p1 = qparam(pick(mn, 1), pick(mx, 1), 3.0f, false);
+  uint32_t sz[8];
+  float rr[8];
+#define KVQ_BCAST(K)                                                              \
+  sz[2 * K] = quad_bcast<K>(p0.sz);                                              \
+  sz[2 * K + 1] = quad_bcast<K>(p1.sz);                                          \
+  rr[2 * K] = __uint_as_float(quad_bcast<K>(__float_as_uint(p0.r)));             \
+  rr[2 * K + 1] = __uint_as_float(quad_bcast<K>(__float_as_uint(p1.r)));
+  KVQ_BCAST(0) KVQ_BCAST(1) KVQ_BCAST(2) KVQ_BCAST(3)
+#undef KVQ_BCAST
+  // half-word of channel k: its 8 tokens at positions pi(i)
+  uint32_t h[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) h[k] = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float z = half_bits_to_f32((uint16_t)(sz[i] >> 16));
+#pragma unroll
+    for (int k = 0; k < 8; k++) h[k] |= qcode(x(i, k), z, rr[i], 3.0f) << (2 * pos_swap(i));
+  }
+  // Word (j*4 + tq)*16 + c holds channel 32j + c (bits 0..15) and 32j+16+c
+  // (bits 16..31).  Lane m holds channels 32j + 8m + k: m = 0, 1 are low
+  // halves, m = 2, 3 the high halves of the same words (quad partner m ^ 2).
+  // The low lane keeps words k = 0..3 of its eight, the high lane k = 4..7.
+  const bool low = m < 2;
+  const uint32_t s0 = low ? (h[4] | (h[5] << 16)) : (h[0] | (h[1] << 16));
+  const uint32_t s1 = low ? (h[6] | (h[7] << 16)) : (h[2] | (h[3] << 16));
+  const uint32_t r0 = dpp<QUAD_XOR2>(s0), r1 = dpp<QUAD_XOR2>(s1);
+  const uint32_t o[4] = {r0 & 0xFFFFu, r0 >> 16, r1 & 0xFFFFu, r1 >> 16};
+  uint32_t wd[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+    wd[q] = low ? (h[q] | (o[q] << 16)) : (o[q] | (h[4 + q] << 16));
+  const int c0 = 8 * (m & 1) + 4 * (m >> 1);
+  *(uint4*)(vc_out + (j * 4 + tq) * 16 + c0) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  if (m < 2) {
+    uint32_t mm[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++)
+      mm[p] = m == 0 ? (sz[2 * p] & 0xFFFFu) | (sz[2 * p + 1] << 16)
+                     : (sz[2 * p] >> 16) | (sz[2 * p + 1] & 0xFFFF0000u);
+    *(uint4*)(meta_out + m * D + j * GS + 8 * tq) = make_uint4(mm[0], mm[1], mm[2], mm[3]);
+  }
 }
 
 // ------------------------------------------------------------------ prefill
 
+// Positions [n_q(T), T) of one (b, kv head) into the ring, 16 rows per
+// workgroup, 16 bytes per thread; the first ring workgroup sets len = T.
+__device__ void ring_fill(const Geo& g, const uint16_t* __restrict__ x, int T, int ry, bool is_v,
+                          kvq_cache& c) {
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int p = n_quant(T, g.R) + RING_ROWS * ry + (tid >> 4), ch = 8 * (tid & 15);
+  if (p < T) {
+    const uint4 val = *(const uint4*)(x + ((size_t)bh * T + p) * D + ch);
+    const int slot = p % g.RS;
+    if (!is_v) {
+      *(uint4*)((uint16_t*)c.ring_k + ((size_t)bh * g.RS + slot) * D + ch) = val;
+    } else {
+      uint16_t* blk = (uint16_t*)c.ring_v + ((size_t)bh * g.RS + (slot / GS) * GS) * D;
+#pragma unroll
+      for (int k = 0; k < 8; k++) blk[(size_t)(ch + k) * GS + slot % GS] = half_of(val, k);
+    }
+  }
+  if (ry == 0 && tid == 0) c.len[bh] = T;
+}
+
+// grid (B * Hkv, qblocks + ring blocks): blocks below qblocks quantize
+// QWAVES groups, one per wave; the rest fill the ring.
 __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint16_t* __restrict__ k,
-                                                              int T, kvq_cache c) {
-  __shared__ GroupLds lds;
-  const int bh = blockIdx.x, grp = blockIdx.y;
+                                                              int T, int qblocks, kvq_cache c) {
+  if ((int)blockIdx.y >= qblocks) {
+    ring_fill(g, k, T, blockIdx.y - qblocks, false, c);
+    return;
+  }
+  __shared__ KeyLds lds[QWAVES];
+  const int bh = blockIdx.x, wave = threadIdx.x >> 6;
+  const int grp = blockIdx.y * QWAVES + wave;
+  if (grp >= n_quant(T, g.R) / GS) return;
   const size_t rec = (size_t)bh * g.NG + grp;
-  DenseSrc src{k + ((size_t)bh * T + (size_t)grp * GS) * D};
-  quant_key_group(g, src, c.pairs + (size_t)bh * NPAIR, (uint32_t*)c.k_lo + rec * GROUP_WORDS,
-                  (uint8_t*)c.k_hi + rec * g.khi_bytes, (uint16_t*)c.k_meta + rec * 2 * D, lds);
+  key_group_wave(g, k + ((size_t)bh * T + (size_t)grp * GS) * D,
+                 pair_masks(g, c.pairs + (size_t)bh * NPAIR),
+                 (uint32_t*)c.k_lo + rec * GROUP_WORDS, (uint8_t*)c.k_hi + rec * g.khi_bytes,
+                 (uint16_t*)c.k_meta + rec * 2 * D, lds[wave]);
 }
 
 __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uint16_t* __restrict__ v,
-                                                                int T, kvq_cache c) {
-  __shared__ GroupLds lds;
-  const int bh = blockIdx.x, grp = blockIdx.y;
-  const size_t rec = (size_t)bh * g.NG + grp;
-  DenseSrc src{v + ((size_t)bh * T + (size_t)grp * GS) * D};
-  quant_value_group(g, src, (uint32_t*)c.v_codes + rec * GROUP_WORDS,
-                    (uint16_t*)c.v_meta + rec * 2 * D, lds);
-}
-
-// Copies positions [n_q(T), T) of one (b, kv head) into the ring and sets
-// len = T.  is_v selects the value ring's slot-block/channel/slot order.
-__global__ __launch_bounds__(QTHREADS) void ring_fill_kernel(Geo g, const uint16_t* __restrict__ x,
-                                                             int T, int is_v, kvq_cache c) {
-  const int bh = blockIdx.x;
-  const int p0 = n_quant(T, g.R);
-  const int n = (T - p0) * D;
-  const uint16_t* src = x + ((size_t)bh * T + p0) * D;
-  uint16_t* ring = (uint16_t*)(is_v ? c.ring_v : c.ring_k) + (size_t)bh * g.RS * D;
-  for (int i = threadIdx.x; i < n; i += QTHREADS) {
-    const int p = p0 + i / D, ch = i % D, slot = p % g.RS;
-    const size_t dst = is_v ? ((size_t)(slot / GS) * D + ch) * GS + slot % GS
-                            : (size_t)slot * D + ch;
-    ring[dst] = src[i];
+                                                                int T, int qblocks, kvq_cache c) {
+  if ((int)blockIdx.y >= qblocks) {
+    ring_fill(g, v, T, blockIdx.y - qblocks, true, c);
+    return;
   }
-  if (threadIdx.x == 0) c.len[bh] = T;
+  const int bh = blockIdx.x, wave = threadIdx.x >> 6;
+  const int grp = blockIdx.y * QWAVES + wave;
+  if (grp >= n_quant(T, g.R) / GS) return;
+  const size_t rec = (size_t)bh * g.NG + grp;
+  value_group_wave<false>(g, v + ((size_t)bh * T + (size_t)grp * GS) * D,
+                          (uint32_t*)c.v_codes + rec * GROUP_WORDS,
+                          (uint16_t*)c.v_meta + rec * 2 * D);
 }
 
 // ------------------------------------------------------------------- append
 
-__global__ __launch_bounds__(QTHREADS) void append_kernel(Geo g, const uint16_t* __restrict__ k_new,
-                                                          const uint16_t* __restrict__ v_new,
-                                                          kvq_cache c) {
-  __shared__ GroupLds lds;
+// One 128-thread workgroup per (b, kv head): the new token goes to ring slot
+// T mod RS; when n_q grows, wave 0 packs the oldest ring group's keys and
+// wave 1 its values (the new token is not in that group).
+__global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __restrict__ k_new,
+                                                     const uint16_t* __restrict__ v_new,
+                                                     kvq_cache c) {
+  __shared__ KeyLds lds;
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int T = c.len[bh];
   if (T >= g.max_tokens) {
@@ -190,43 +424,41 @@ __global__ __launch_bounds__(QTHREADS) void append_kernel(Geo g, const uint16_t*
   uint16_t* rk = (uint16_t*)c.ring_k + (size_t)bh * g.RS * D;
   uint16_t* rv = (uint16_t*)c.ring_v + (size_t)bh * g.RS * D;
   const int slot = T % g.RS;
-  if (tid < D) {
-    rk[(size_t)slot * D + tid] = k_new[(size_t)bh * D + tid];
-    rv[((size_t)(slot / GS) * D + tid) * GS + slot % GS] = v_new[(size_t)bh * D + tid];
-  }
+  rk[(size_t)slot * D + tid] = k_new[(size_t)bh * D + tid];
+  rv[((size_t)(slot / GS) * D + tid) * GS + slot % GS] = v_new[(size_t)bh * D + tid];
   const int nq0 = n_quant(T, g.R);
   if (n_quant(T + 1, g.R) > nq0) {
     // the group [nq0, nq0 + 32) ends at T + 1 - R <= T: the new token is not in it
     const int grp = nq0 / GS, s0 = nq0 % g.RS;
     const size_t rec = (size_t)bh * g.NG + grp;
-    quant_key_group(g, RingKSrc{rk, s0}, c.pairs + (size_t)bh * NPAIR,
-                    (uint32_t*)c.k_lo + rec * GROUP_WORDS, (uint8_t*)c.k_hi + rec * g.khi_bytes,
-                    (uint16_t*)c.k_meta + rec * 2 * D, lds);
-    quant_value_group(g, RingVSrc{rv + (size_t)(s0 / GS) * D * GS},
-                      (uint32_t*)c.v_codes + rec * GROUP_WORDS, (uint16_t*)c.v_meta + rec * 2 * D,
-                      lds);
+    if (tid < 64)
+      key_group_wave(g, rk + (size_t)s0 * D, pair_masks(g, c.pairs + (size_t)bh * NPAIR),
+                     (uint32_t*)c.k_lo + rec * GROUP_WORDS, (uint8_t*)c.k_hi + rec * g.khi_bytes,
+                     (uint16_t*)c.k_meta + rec * 2 * D, lds);
+    else
+      value_group_wave<true>(g, rv + (size_t)(s0 / GS) * D * GS,
+                             (uint32_t*)c.v_codes + rec * GROUP_WORDS,
+                             (uint16_t*)c.v_meta + rec * 2 * D);
   }
   __syncthreads();
   if (tid == 0) c.len[bh] = T + 1;
 }
 
+static int ring_blocks(const Geo& g, int T) {
+  return (T - n_quant(T, g.R) + RING_ROWS - 1) / RING_ROWS;
+}
+
 hipError_t launch_quant_keys(const Geo& g, const void* k, int T, kvq_cache* c, hipStream_t st) {
-  const int ng = n_quant(T, g.R) / GS;
-  if (ng > 0)
-    hipLaunchKernelGGL(quant_keys_kernel, dim3(g.B * g.Hkv, ng), dim3(QTHREADS), 0, st, g,
-                       (const uint16_t*)k, T, *c);
-  hipLaunchKernelGGL(ring_fill_kernel, dim3(g.B * g.Hkv), dim3(QTHREADS), 0, st, g,
-                     (const uint16_t*)k, T, 0, *c);
+  const int qb = (n_quant(T, g.R) / GS + QWAVES - 1) / QWAVES;
+  hipLaunchKernelGGL(quant_keys_kernel, dim3(g.B * g.Hkv, qb + ring_blocks(g, T)),
+                     dim3(QTHREADS), 0, st, g, (const uint16_t*)k, T, qb, *c);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_values(const Geo& g, const void* v, int T, kvq_cache* c, hipStream_t st) {
-  const int ng = n_quant(T, g.R) / GS;
-  if (ng > 0)
-    hipLaunchKernelGGL(quant_values_kernel, dim3(g.B * g.Hkv, ng), dim3(QTHREADS), 0, st, g,
-                       (const uint16_t*)v, T, *c);
-  hipLaunchKernelGGL(ring_fill_kernel, dim3(g.B * g.Hkv), dim3(QTHREADS), 0, st, g,
-                     (const uint16_t*)v, T, 1, *c);
+  const int qb = (n_quant(T, g.R) / GS + QWAVES - 1) / QWAVES;
+  hipLaunchKernelGGL(quant_values_kernel, dim3(g.B * g.Hkv, qb + ring_blocks(g, T)),
+                     dim3(QTHREADS), 0, st, g, (const uint16_t*)v, T, qb, *c);
   return hipGetLastError();
 }
 
@@ -284,7 +516,7 @@ hipError_t launch_shrink(const Geo& g, kvq_cache* c, int g0, int g1, hipStream_t
 
 hipError_t launch_append(const Geo& g, const void* k_new, const void* v_new, kvq_cache* c,
                          hipStream_t st) {
-  hipLaunchKernelGGL(append_kernel, dim3(g.B * g.Hkv), dim3(QTHREADS), 0, st, g,
+  hipLaunchKernelGGL(append_kernel, dim3(g.B * g.Hkv), dim3(128), 0, st, g,
                      (const uint16_t*)k_new, (const uint16_t*)v_new, *c);
   return hipGetLastError();
 }

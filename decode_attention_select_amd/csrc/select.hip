@@ -14,8 +14,9 @@
 
 namespace kvq {
 
-constexpr int SEL_THREADS = 256;          // 4 rows of 64 pairs in flight
-constexpr int SEL_ROWS_PER_BLOCK = 256;   // rows (tokens or queries) per block
+constexpr int SEL_THREADS = 256;
+constexpr int SEL_SLOTS = SEL_THREADS / 8;  // row slots: 8 threads (16-byte chunks) per row
+constexpr int SEL_ROWS_PER_BLOCK = 8 * SEL_SLOTS;  // 8 rows per thread, all loads up front
 
 __global__ void zero_u64_kernel(uint64_t* p, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -44,41 +45,55 @@ __device__ inline uint64_t norm_fixed(uint16_t a_bits, uint16_t b_bits, int bf16
   return (uint64_t)((double)n * 16777216.0);
 }
 
-// grid.x = B * Hkv; grid.y = key blocks + query blocks.  Thread t handles
-// pair t % 64 of rows t / 64, t / 64 + 4, ... of its block's row range.
+// 16-bit element e (0..7) of a 16-byte row chunk.
+__device__ inline uint16_t sel_half(const uint4& v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xFFFF);
+}
+
+// grid.x = B * Hkv; grid.y = key blocks + query blocks.  Thread t covers
+// pairs 8 cb .. 8 cb + 7 (cb = t % 8: channels 8cb.. and 64 + 8cb.., two
+// 16-byte loads per row) of rows t / 8 + 32 i, i = 0..7, of its block.
+// A (b, kv head)'s selection queries are G * n_qry consecutive rows.
 __global__ __launch_bounds__(SEL_THREADS) void pair_sums_kernel(
     Geo g, const uint16_t* __restrict__ q_sel, int n_qry,
     const uint16_t* __restrict__ k, int T, int key_blocks,
     uint64_t* __restrict__ sums) {
   const int bh = blockIdx.x;  // b * Hkv + kv head
   const int b = bh / g.Hkv, kh = bh % g.Hkv;
-  const int j = threadIdx.x & 63, sub = threadIdx.x >> 6;
-  uint64_t acc = 0;
-  int side;
-  if ((int)blockIdx.y < key_blocks) {
-    side = 1;
-    const int r0 = blockIdx.y * SEL_ROWS_PER_BLOCK;
-    const int r1 = min(T, r0 + SEL_ROWS_PER_BLOCK);
-    const uint16_t* base = k + (size_t)bh * T * D;
-    for (int r = r0 + sub; r < r1; r += 4)
-      acc += norm_fixed(base[(size_t)r * D + j], base[(size_t)r * D + j + NPAIR], g.bf16);
-  } else {
-    side = 0;
-    const int nrows = g.G * n_qry;
-    const int r0 = (blockIdx.y - key_blocks) * SEL_ROWS_PER_BLOCK;
-    const int r1 = min(nrows, r0 + SEL_ROWS_PER_BLOCK);
-    for (int r = r0 + sub; r < r1; r += 4) {
-      const int h = kh * g.G + r / n_qry, t = r % n_qry;
-      const uint16_t* row = q_sel + (((size_t)b * g.Hq + h) * n_qry + t) * D;
-      acc += norm_fixed(row[j], row[j + NPAIR], g.bf16);
+  const int cb = threadIdx.x & 7, slot = threadIdx.x >> 3;
+  const bool key = (int)blockIdx.y < key_blocks;
+  const uint16_t* base = key ? k + (size_t)bh * T * D
+                             : q_sel + ((size_t)b * g.Hq + (size_t)kh * g.G) * n_qry * D;
+  const int nrows = key ? T : g.G * n_qry;
+  const int r0 = (key ? blockIdx.y : blockIdx.y - key_blocks) * SEL_ROWS_PER_BLOCK;
+  uint4 va[8], vb[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int r = r0 + slot + SEL_SLOTS * i;
+    va[i] = vb[i] = make_uint4(0, 0, 0, 0);  // a zero row adds u(0) = 0
+    if (r < nrows) {
+      const uint16_t* row = base + (size_t)r * D;
+      va[i] = *(const uint4*)(row + 8 * cb);
+      vb[i] = *(const uint4*)(row + NPAIR + 8 * cb);
     }
   }
-  __shared__ uint64_t part[SEL_THREADS];
-  part[threadIdx.x] = acc;
+  uint64_t acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    acc[e] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[e] += norm_fixed(sel_half(va[i], e), sel_half(vb[i], e), g.bf16);
+  }
+  __shared__ uint64_t part[SEL_SLOTS][NPAIR];
+#pragma unroll
+  for (int e = 0; e < 8; e++) part[slot][8 * cb + e] = acc[e];
   __syncthreads();
-  if (threadIdx.x < 64) {
-    const uint64_t s = part[j] + part[j + 64] + part[j + 128] + part[j + 192];
-    if (s) atomicAdd((unsigned long long*)&sums[((size_t)bh * 2 + side) * NPAIR + j],
+  if (threadIdx.x < NPAIR) {
+    uint64_t s = 0;
+    for (int i = 0; i < SEL_SLOTS; i++) s += part[i][threadIdx.x];
+    if (s) atomicAdd((unsigned long long*)&sums[((size_t)bh * 2 + (key ? 1 : 0)) * NPAIR +
+                                                threadIdx.x],
                      (unsigned long long)s);
   }
 }
@@ -123,45 +138,111 @@ hipError_t launch_select(const Geo& g, const void* q_sel, int n_qry, const void*
 // product and the sum rounded once (no contraction).  Ranked descending,
 // ties to the lower pair id.  sums is scratch for R, then holds [0][j] = the
 // bits of S_j and [1][j] = 0.
-constexpr int QA_GROUPS_PER_BLOCK = 16;
+constexpr int QA_GROUPS_PER_WAVE = 4;
+constexpr int QA_GROUPS_PER_BLOCK = 4 * QA_GROUPS_PER_WAVE;
 
-// grid (B * Hkv, ceil(groups / 16)); thread c sums channel c's ranges over
-// the block's groups (rows of 128 channels are read coalesced)
-__global__ __launch_bounds__(D) void qa_ranges_kernel(Geo g, const uint16_t* __restrict__ k,
-                                                      int T, uint64_t* __restrict__ sums) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  const int ng = T / GS;
-  const int g0 = blockIdx.y * QA_GROUPS_PER_BLOCK, g1 = min(ng, g0 + QA_GROUPS_PER_BLOCK);
-  const uint16_t* base = k + (size_t)bh * T * D;
-  uint64_t acc = 0;
-  for (int gi = g0; gi < g1; gi++) {
-    float mn = INFINITY, mx = -INFINITY;
-    for (int i = 0; i < GS; i++) {
-      const float x = in_to_f32(base[(size_t)(gi * GS + i) * D + c], g.bf16);
-      mn = fminf(mn, x);
-      mx = fmaxf(mx, x);
-    }
-    acc += (uint64_t)((double)__fsub_rn(mx, mn) * 65536.0);  // non-negative: truncation = floor
-  }
-  if (acc) atomicAdd((unsigned long long*)&sums[(size_t)bh * D + c], (unsigned long long)acc);
+// min / max over the four lanes of a DPP quad
+__device__ inline float qa_quad(float v, bool want_max) {
+  float p = __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
+      (int)__float_as_uint(v), (int)__float_as_uint(v), 0xB1, 0xF, 0xF, false));
+  v = want_max ? fmaxf(v, p) : fminf(v, p);
+  p = __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
+      (int)__float_as_uint(v), (int)__float_as_uint(v), 0x4E, 0xF, 0xF, false));
+  return want_max ? fmaxf(v, p) : fminf(v, p);
 }
 
-// one workgroup of 128 threads per (b, kv head)
-__global__ __launch_bounds__(D) void qa_rank_kernel(Geo g, const uint16_t* __restrict__ q_sel,
-                                                    int n_qry, uint64_t* __restrict__ sums,
-                                                    int32_t* __restrict__ pairs) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  const int b = bh / g.Hkv, kh = bh % g.Hkv;
-  uint64_t A = 0;
-  for (int h = kh * g.G; h < (kh + 1) * g.G; h++)
-    for (int t = 0; t < n_qry; t++) {
-      const float x = fabsf(in_to_f32(q_sel[(((size_t)b * g.Hq + h) * n_qry + t) * D + c], g.bf16));
-      A += (uint64_t)((double)x * 16777216.0);
+// grid (B * Hkv, ceil(groups / 16)), 4 waves of 4 groups each.  Lane
+// 4 cb + tq holds channels 8cb .. 8cb+7 of tokens 8tq .. 8tq+7 of a group
+// (one 16-byte load per token), so a channel's 32 tokens lie in one quad.
+__global__ __launch_bounds__(256) void qa_ranges_kernel(Geo g, const uint16_t* __restrict__ k,
+                                                        int T, uint64_t* __restrict__ sums) {
+  const int bh = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cb = lane >> 2, tq = lane & 3;
+  const int ng = T / GS;
+  const uint16_t* base = k + (size_t)bh * T * D;
+  uint64_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int gw = blockIdx.y * QA_GROUPS_PER_BLOCK + wave * QA_GROUPS_PER_WAVE;
+  for (int h = 0; h < QA_GROUPS_PER_WAVE; h += 2) {
+    uint4 v[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int gi = min(gw + h + u, ng - 1);  // clamped: in bounds, counted below only if valid
+        v[u][i] = *(const uint4*)(base + ((size_t)gi * GS + 8 * tq + i) * D + 8 * cb);
+      }
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      if (gw + h + u >= ng) continue;  // wave-uniform
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        float mn = in_to_f32(sel_half(v[u][0], e), g.bf16), mx = mn;
+#pragma unroll
+        for (int i = 1; i < 8; i++) {
+          const float x = in_to_f32(sel_half(v[u][i], e), g.bf16);
+          mn = fminf(mn, x);
+          mx = fmaxf(mx, x);
+        }
+        mn = qa_quad(mn, false);
+        mx = qa_quad(mx, true);
+        acc[e] += (uint64_t)((double)__fsub_rn(mx, mn) * 65536.0);  // >= 0: truncation = floor
+      }
     }
+  }
+  __shared__ uint64_t part[4][D];
+  if (tq == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) part[wave][8 * cb + e] = acc[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const uint64_t s = part[0][threadIdx.x] + part[1][threadIdx.x] + part[2][threadIdx.x] +
+                       part[3][threadIdx.x];
+    if (s) atomicAdd((unsigned long long*)&sums[(size_t)bh * D + threadIdx.x],
+                     (unsigned long long)s);
+  }
+}
+
+// One 256-thread workgroup per (b, kv head).  Thread t sums |q| of channels
+// 8cb .. 8cb+7 (cb = t % 16) over rows t / 16 + 16 i of the head group's
+// G * n_qry selection queries, then the pair scores and ranks follow.
+__global__ __launch_bounds__(256) void qa_rank_kernel(Geo g, const uint16_t* __restrict__ q_sel,
+                                                      int n_qry, uint64_t* __restrict__ sums,
+                                                      int32_t* __restrict__ pairs) {
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int b = bh / g.Hkv, kh = bh % g.Hkv;
+  const int cb = tid & 15, slot = tid >> 4;
+  const uint16_t* base = q_sel + ((size_t)b * g.Hq + (size_t)kh * g.G) * n_qry * D;
+  const int nrows = g.G * n_qry;
+  uint64_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r0 = 0; r0 < nrows; r0 += 64) {
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = r0 + slot + 16 * i;
+      v[i] = r < nrows ? *(const uint4*)(base + (size_t)r * D + 8 * cb) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float x = fabsf(in_to_f32(sel_half(v[i], e), g.bf16));
+        acc[e] += (uint64_t)((double)x * 16777216.0);
+      }
+  }
+  __shared__ uint64_t Ap[16][D];
   __shared__ uint64_t As[D], Rs[D];
   __shared__ double S[NPAIR];
-  As[c] = A;
-  Rs[c] = sums[(size_t)bh * D + c];
+#pragma unroll
+  for (int e = 0; e < 8; e++) Ap[slot][8 * cb + e] = acc[e];
+  __syncthreads();
+  const int c = tid;
+  if (c < D) {
+    uint64_t A = 0;
+    for (int i = 0; i < 16; i++) A += Ap[i][c];
+    As[c] = A;
+    Rs[c] = sums[(size_t)bh * D + c];
+  }
   __syncthreads();
   if (c < NPAIR)
     S[c] = __dadd_rn(__dmul_rn((double)Rs[c], (double)As[c]),
@@ -173,7 +254,7 @@ __global__ __launch_bounds__(D) void qa_rank_kernel(Geo g, const uint16_t* __res
     for (int i = 0; i < NPAIR; i++) rank += (S[i] > mine) || (S[i] == mine && i < c);
     pairs[(size_t)bh * NPAIR + rank] = c;
     sums[(size_t)bh * D + c] = __double_as_longlong(mine);
-  } else {
+  } else if (c < D) {
     sums[(size_t)bh * D + c] = 0;
   }
 }
@@ -186,8 +267,8 @@ hipError_t launch_select_qa(const Geo& g, const void* q_sel, int n_qry, const vo
   if (ng > 0)
     hipLaunchKernelGGL(qa_ranges_kernel,
                        dim3(g.B * g.Hkv, (ng + QA_GROUPS_PER_BLOCK - 1) / QA_GROUPS_PER_BLOCK),
-                       dim3(D), 0, st, g, (const uint16_t*)k, T, c->sums);
-  hipLaunchKernelGGL(qa_rank_kernel, dim3(g.B * g.Hkv), dim3(D), 0, st, g,
+                       dim3(256), 0, st, g, (const uint16_t*)k, T, c->sums);
+  hipLaunchKernelGGL(qa_rank_kernel, dim3(g.B * g.Hkv), dim3(256), 0, st, g,
                      (const uint16_t*)q_sel, n_qry, c->sums, c->pairs);
   return hipGetLastError();
 }
