@@ -43,20 +43,17 @@ struct QuadBcast {  // quad_perm [K, K, K, K]
 template <int K>
 __device__ inline uint32_t quad_bcast(uint32_t x) { return dpp<QuadBcast<K>::ctrl>(x); }
 
-// min and max over the quad.  The result is the quad's min/max value;
-// only the sign of a zero minimum depends on the combining order, and the
-// caller settles that separately (sign_of_first_zero).
+// min and max over the quad (inputs are finite).  The result is the quad's
+// min/max value; only the sign of a zero minimum depends on the combining
+// order and on how the min instruction orders -0 and +0, and the caller
+// settles that separately (sign_of_first_zero).
 __device__ inline float quad_min(float v) {
-  float p = __uint_as_float(dpp<QUAD_XOR1>(__float_as_uint(v)));
-  v = p < v ? p : v;
-  p = __uint_as_float(dpp<QUAD_XOR2>(__float_as_uint(v)));
-  return p < v ? p : v;
+  v = fminf(v, __uint_as_float(dpp<QUAD_XOR1>(__float_as_uint(v))));
+  return fminf(v, __uint_as_float(dpp<QUAD_XOR2>(__float_as_uint(v))));
 }
 __device__ inline float quad_max(float v) {
-  float p = __uint_as_float(dpp<QUAD_XOR1>(__float_as_uint(v)));
-  v = p > v ? p : v;
-  p = __uint_as_float(dpp<QUAD_XOR2>(__float_as_uint(v)));
-  return p > v ? p : v;
+  v = fmaxf(v, __uint_as_float(dpp<QUAD_XOR1>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(dpp<QUAD_XOR2>(__float_as_uint(v))));
 }
 
 // A sequential scan keeps the first of equal minima, so a minimum of zero
@@ -91,12 +88,12 @@ __device__ inline QParam qparam(float mn, float mx, float L, bool raw) {
   return {(uint32_t)sb | ((uint32_t)zb << 16), r};
 }
 
-// code = clamp(rint((x - z) * r), 0, L); 0 when r == 0 (s == 0).
-__device__ inline uint32_t qcode(float x, float z, float r, float L) {
-  float q = rintf(__fmul_rn(__fsub_rn(x, z), r));
-  q = q < 0.0f ? 0.0f : q;
-  q = q > L ? L : q;
-  return (uint32_t)q;
+// code = clamp(rint((x - z) * r), 0, L) as an integer-valued float; 0 when
+// r == 0 (s == 0).  Inputs are finite 16-bit values within the fp16 range of
+// the scale and zero, so the product is never NaN.
+__device__ inline float qcode(float x, float z, float r, float L) {
+  const float q = rintf(__fmul_rn(__fsub_rn(x, z), r));
+  return __builtin_amdgcn_fmed3f(q, 0.0f, L);
 }
 
 // Marks the loaded words as changed, so that widened copies made before are
@@ -134,6 +131,7 @@ struct KeyLds {  // one wave's staging of a key-group record
 };
 
 // rows: token 0 of the group, row stride D (prefill input or ring_k slots).
+template <bool BF>
 __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
                                uint32_t* lo_out, uint8_t* hi_out, uint16_t* meta_out,
                                KeyLds& L) {
@@ -160,12 +158,13 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
   float mn[8], mx[8];
 #pragma unroll
   for (int k = 0; k < 8; k++) {
-    float a = in_to_f32(half_of(v[0], k), g.bf16), b = a;
+    float a = in_to_f32(half_of(v[0], k), BF), b = a;
 #pragma unroll
-    for (int i = 1; i < 8; i++) {
-      const float x = in_to_f32(half_of(v[i], k), g.bf16);
-      a = x < a ? x : a;
-      b = x > b ? x : b;
+    for (int i = 1; i < 8; i += 2) {  // three-input min / max
+      const float x = in_to_f32(half_of(v[i], k), BF);
+      const float y = i + 1 < 8 ? in_to_f32(half_of(v[i + 1], k), BF) : x;
+      a = fminf(a, fminf(x, y));
+      b = fmaxf(b, fmaxf(x, y));
     }
     mn[k] = quad_min(a);
     mx[k] = quad_max(b);
@@ -179,7 +178,7 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
       uint32_t f = 2;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        const float x = in_to_f32(half_of(v[i], k), g.bf16);
+        const float x = in_to_f32(half_of(v[i], k), BF);
         if (f == 2 && x == 0.0f) f = __float_as_uint(x) >> 31;
       }
       const uint32_t sgn = sign_of_first_zero(f);
@@ -205,21 +204,37 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
   KVQ_BCAST(0) KVQ_BCAST(1) KVQ_BCAST(2) KVQ_BCAST(3)
 #undef KVQ_BCAST
 
-  // codes: low digits into half-words, high digits of 4-bit channels
+  // codes: low digits summed into half-words as exact float integers
+  // (digit * 4^position, below 2^16); the high digits of 4-bit channels as
+  // integers, only for channel slots k where some lane holds a 4-bit channel
   refresh(v);
+  float hwf[8];
   uint32_t hw[8], hh[8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) hw[i] = hh[i] = 0;
+  for (int i = 0; i < 8; i++) {
+    hwf[i] = 0.0f;
+    hh[i] = 0;
+  }
 #pragma unroll
   for (int k = 0; k < 8; k++) {
     const float z = half_bits_to_f32((uint16_t)(sz[k] >> 16));
+    const float mul = (float)(1u << (2 * pos_swap(k)));
+    if (bits4 && __any(lv[k] == 15.0f)) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const uint32_t code = qcode(in_to_f32(half_of(v[i], k), g.bf16), z, rr[k], lv[k]);
-      hw[i] |= (code & 3u) << (2 * pos_swap(k));
-      if (bits4) hh[i] |= (code >> 2) << hish[k];
+      for (int i = 0; i < 8; i++) {
+        const float q = qcode(in_to_f32(half_of(v[i], k), BF), z, rr[k], lv[k]);
+        const float hd = floorf(q * 0.25f), ld = fmaf(hd, -4.0f, q);
+        hwf[i] = fmaf(ld, mul, hwf[i]);
+        hh[i] |= (uint32_t)hd << hish[k];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        hwf[i] = fmaf(qcode(in_to_f32(half_of(v[i], k), BF), z, rr[k], lv[k]), mul, hwf[i]);
     }
   }
+#pragma unroll
+  for (int i = 0; i < 8; i++) hw[i] = (uint32_t)hwf[i];
   // stage the record in LDS: token i of this lane is tile index
   // e = 16 T + r with T = i / 4, r = 4 tq + i % 4
   if (lane < 8) ((uint4*)L.hi)[lane] = make_uint4(0, 0, 0, 0);
@@ -259,7 +274,7 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
 
 // CHMAJOR false: src = token 0 of the group, row stride D (prefill input).
 // CHMAJOR true:  src = a ring_v slot block [128][32] (channel, slot).
-template <bool CHMAJOR>
+template <bool BF, bool CHMAJOR>
 __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint32_t* vc_out,
                                  uint16_t* meta_out) {
   const int lane = threadIdx.x & 63, cb = lane & 15, tq = lane >> 4, m = cb & 3, j = cb >> 2;
@@ -270,17 +285,17 @@ __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint32_t* vc
     v[n] = CHMAJOR ? *(const uint4*)(src + (size_t)(8 * cb + n) * GS + 8 * tq)
                    : *(const uint4*)(src + (size_t)(8 * tq + n) * D + 8 * cb);
   auto x = [&](int i, int k) {
-    return in_to_f32(CHMAJOR ? half_of(v[k], i) : half_of(v[i], k), g.bf16);
+    return in_to_f32(CHMAJOR ? half_of(v[k], i) : half_of(v[i], k), BF);
   };
   float mn[8], mx[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     float a = x(i, 0), b = a;
 #pragma unroll
-    for (int k = 1; k < 8; k++) {
-      const float e = x(i, k);
-      a = e < a ? e : a;
-      b = e > b ? e : b;
+    for (int k = 1; k < 8; k += 2) {  // three-input min / max
+      const float e = x(i, k), f = k + 1 < 8 ? x(i, k + 1) : e;
+      a = fminf(a, fminf(e, f));
+      b = fmaxf(b, fmaxf(e, f));
     }
     mn[i] = quad_min(a);
     mx[i] = quad_max(b);
@@ -315,16 +330,21 @@ __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint32_t* vc
   rr[2 * K + 1] = __uint_as_float(quad_bcast<K>(__float_as_uint(p1.r)));
   KVQ_BCAST(0) KVQ_BCAST(1) KVQ_BCAST(2) KVQ_BCAST(3)
 #undef KVQ_BCAST
-  // half-word of channel k: its 8 tokens at positions pi(i)
+  // half-word of channel k: its 8 tokens' codes at positions pi(i), summed
+  // as exact float integers (code * 4^position, below 2^16)
+  float hf[8];
   uint32_t h[8];
 #pragma unroll
-  for (int k = 0; k < 8; k++) h[k] = 0;
+  for (int k = 0; k < 8; k++) hf[k] = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const float z = half_bits_to_f32((uint16_t)(sz[i] >> 16));
+    const float mul = (float)(1u << (2 * pos_swap(i)));
 #pragma unroll
-    for (int k = 0; k < 8; k++) h[k] |= qcode(x(i, k), z, rr[i], 3.0f) << (2 * pos_swap(i));
+    for (int k = 0; k < 8; k++) hf[k] = fmaf(qcode(x(i, k), z, rr[i], 3.0f), mul, hf[k]);
   }
+#pragma unroll
+  for (int k = 0; k < 8; k++) h[k] = (uint32_t)hf[k];
   // Word (j*4 + tq)*16 + c holds channel 32j + c (bits 0..15) and 32j+16+c
   // (bits 16..31).  Lane m holds channels 32j + 8m + k: m = 0, 1 are low
   // halves, m = 2, 3 the high halves of the same words (quad partner m ^ 2).
@@ -374,6 +394,7 @@ __device__ void ring_fill(const Geo& g, const uint16_t* __restrict__ x, int T, i
 
 // grid (B * Hkv, qblocks + ring blocks): blocks below qblocks quantize
 // QWAVES groups, one per wave; the rest fill the ring.
+template <bool BF>
 __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint16_t* __restrict__ k,
                                                               int T, int qblocks, kvq_cache c) {
   if ((int)blockIdx.y >= qblocks) {
@@ -385,12 +406,13 @@ __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint1
   const int grp = blockIdx.y * QWAVES + wave;
   if (grp >= n_quant(T, g.R) / GS) return;
   const size_t rec = (size_t)bh * g.NG + grp;
-  key_group_wave(g, k + ((size_t)bh * T + (size_t)grp * GS) * D,
+  key_group_wave<BF>(g, k + ((size_t)bh * T + (size_t)grp * GS) * D,
                  pair_masks(g, c.pairs + (size_t)bh * NPAIR),
                  (uint32_t*)c.k_lo + rec * GROUP_WORDS, (uint8_t*)c.k_hi + rec * g.khi_bytes,
                  (uint16_t*)c.k_meta + rec * 2 * D, lds[wave]);
 }
 
+template <bool BF>
 __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uint16_t* __restrict__ v,
                                                                 int T, int qblocks, kvq_cache c) {
   if ((int)blockIdx.y >= qblocks) {
@@ -401,7 +423,7 @@ __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uin
   const int grp = blockIdx.y * QWAVES + wave;
   if (grp >= n_quant(T, g.R) / GS) return;
   const size_t rec = (size_t)bh * g.NG + grp;
-  value_group_wave<false>(g, v + ((size_t)bh * T + (size_t)grp * GS) * D,
+  value_group_wave<BF, false>(g, v + ((size_t)bh * T + (size_t)grp * GS) * D,
                           (uint32_t*)c.v_codes + rec * GROUP_WORDS,
                           (uint16_t*)c.v_meta + rec * 2 * D);
 }
@@ -411,6 +433,7 @@ __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uin
 // One 128-thread workgroup per (b, kv head): the new token goes to ring slot
 // T mod RS; when n_q grows, wave 0 packs the oldest ring group's keys and
 // wave 1 its values (the new token is not in that group).
+template <bool BF>
 __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new,
                                                      kvq_cache c) {
@@ -432,11 +455,11 @@ __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __re
     const int grp = nq0 / GS, s0 = nq0 % g.RS;
     const size_t rec = (size_t)bh * g.NG + grp;
     if (tid < 64)
-      key_group_wave(g, rk + (size_t)s0 * D, pair_masks(g, c.pairs + (size_t)bh * NPAIR),
+      key_group_wave<BF>(g, rk + (size_t)s0 * D, pair_masks(g, c.pairs + (size_t)bh * NPAIR),
                      (uint32_t*)c.k_lo + rec * GROUP_WORDS, (uint8_t*)c.k_hi + rec * g.khi_bytes,
                      (uint16_t*)c.k_meta + rec * 2 * D, lds);
     else
-      value_group_wave<true>(g, rv + (size_t)(s0 / GS) * D * GS,
+      value_group_wave<BF, true>(g, rv + (size_t)(s0 / GS) * D * GS,
                              (uint32_t*)c.v_codes + rec * GROUP_WORDS,
                              (uint16_t*)c.v_meta + rec * 2 * D);
   }
@@ -450,15 +473,25 @@ static int ring_blocks(const Geo& g, int T) {
 
 hipError_t launch_quant_keys(const Geo& g, const void* k, int T, kvq_cache* c, hipStream_t st) {
   const int qb = (n_quant(T, g.R) / GS + QWAVES - 1) / QWAVES;
-  hipLaunchKernelGGL(quant_keys_kernel, dim3(g.B * g.Hkv, qb + ring_blocks(g, T)),
-                     dim3(QTHREADS), 0, st, g, (const uint16_t*)k, T, qb, *c);
+  const dim3 grid(g.B * g.Hkv, qb + ring_blocks(g, T));
+  if (g.bf16)
+    hipLaunchKernelGGL(quant_keys_kernel<true>, grid, dim3(QTHREADS), 0, st, g,
+                       (const uint16_t*)k, T, qb, *c);
+  else
+    hipLaunchKernelGGL(quant_keys_kernel<false>, grid, dim3(QTHREADS), 0, st, g,
+                       (const uint16_t*)k, T, qb, *c);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_values(const Geo& g, const void* v, int T, kvq_cache* c, hipStream_t st) {
   const int qb = (n_quant(T, g.R) / GS + QWAVES - 1) / QWAVES;
-  hipLaunchKernelGGL(quant_values_kernel, dim3(g.B * g.Hkv, qb + ring_blocks(g, T)),
-                     dim3(QTHREADS), 0, st, g, (const uint16_t*)v, T, qb, *c);
+  const dim3 grid(g.B * g.Hkv, qb + ring_blocks(g, T));
+  if (g.bf16)
+    hipLaunchKernelGGL(quant_values_kernel<true>, grid, dim3(QTHREADS), 0, st, g,
+                       (const uint16_t*)v, T, qb, *c);
+  else
+    hipLaunchKernelGGL(quant_values_kernel<false>, grid, dim3(QTHREADS), 0, st, g,
+                       (const uint16_t*)v, T, qb, *c);
   return hipGetLastError();
 }
 
@@ -516,8 +549,12 @@ hipError_t launch_shrink(const Geo& g, kvq_cache* c, int g0, int g1, hipStream_t
 
 hipError_t launch_append(const Geo& g, const void* k_new, const void* v_new, kvq_cache* c,
                          hipStream_t st) {
-  hipLaunchKernelGGL(append_kernel, dim3(g.B * g.Hkv), dim3(128), 0, st, g,
-                     (const uint16_t*)k_new, (const uint16_t*)v_new, *c);
+  if (g.bf16)
+    hipLaunchKernelGGL(append_kernel<true>, dim3(g.B * g.Hkv), dim3(128), 0, st, g,
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, *c);
+  else
+    hipLaunchKernelGGL(append_kernel<false>, dim3(g.B * g.Hkv), dim3(128), 0, st, g,
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, *c);
   return hipGetLastError();
 }
 
