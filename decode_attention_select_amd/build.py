@@ -14,6 +14,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # fp32 division and sqrt correctly rounded (the quantizer and the pair
+    # norms are bit-exact IEEE computations)
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # keep MFMA accumulators in ordinary VGPRs (no AGPR copies around VALU use)

@@ -23,26 +23,27 @@ __global__ void zero_u64_kernel(uint64_t* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-// IEEE sqrt of a non-negative fp32, correctly rounded: the hardware estimate
-// is corrected by comparing x with the exact squares (in fp64: a 25-bit
-// midpoint squares exactly) of the midpoints to its neighbours.
-__device__ inline float sqrt_rn(float x) {
-  float y = sqrtf(x);
-  if (!(x > 0.0f) || isinf(x)) return y;
-  const double xd = x;
-  const float up = __uint_as_float(__float_as_uint(y) + 1u);
-  const double mu = 0.5 * ((double)y + (double)up);
-  if (mu * mu <= xd) return up;
-  const float dn = __uint_as_float(__float_as_uint(y) - 1u);
-  const double md = 0.5 * ((double)y + (double)dn);
-  return md * md > xd ? dn : y;
-}
-
-__device__ inline uint64_t norm_fixed(uint16_t a_bits, uint16_t b_bits, int bf16) {
-  const float a = in_to_f32(a_bits, bf16), b = in_to_f32(b_bits, bf16);
-  const float s = __fadd_rn(__fmul_rn(a, a), __fmul_rn(b, b));
-  const float n = sqrt_rn(s);
-  return (uint64_t)((double)n * 16777216.0);
+// u(n) = floor(n * 2^24) of the fp32 norm n = RN(sqrt(RN(a*a + b*b))), as an
+// integer-valued double.  a*a and b*b are exact for 16-bit inputs, so
+// fma(a, a, b*b) is the rounded sum.  The square root is correctly rounded:
+// the hardware estimate y (within one ulp) or a neighbour y-, y+, chosen by
+// the exact signs of s - y- y and s - y y+ (fma residuals); no float s lies
+// between y- y (y y+) and the squared midpoint, so these signs decide the
+// rounding.  Below s = 2^-48 every candidate is under 2^-24 and u = 0, so
+// subnormal estimates cannot matter.  n * 2^24 and its floor are exact in
+// double; a thread's sum of eight such terms stays exact for norms below
+// 2^25.
+template <bool BF>
+__device__ inline double norm_fixed(uint16_t a_bits, uint16_t b_bits) {
+  const float a = in_to_f32(a_bits, BF), b = in_to_f32(b_bits, BF);
+  const float s = fmaf(a, a, __fmul_rn(b, b));
+  const float y0 = __builtin_amdgcn_sqrtf(s);
+  const float ym = __uint_as_float(__float_as_uint(y0) - 1u);
+  const float yp = __uint_as_float(__float_as_uint(y0) + 1u);
+  const float rm = fmaf(-ym, y0, s), rp = fmaf(-yp, y0, s);
+  float y = rm <= 0.0f ? ym : y0;
+  y = rp > 0.0f ? yp : y;
+  return floor((double)y * 16777216.0);
 }
 
 // 16-bit element e (0..7) of a 16-byte row chunk.
@@ -55,6 +56,7 @@ __device__ inline uint16_t sel_half(const uint4& v, int e) {
 // pairs 8 cb .. 8 cb + 7 (cb = t % 8: channels 8cb.. and 64 + 8cb.., two
 // 16-byte loads per row) of rows t / 8 + 32 i, i = 0..7, of its block.
 // A (b, kv head)'s selection queries are G * n_qry consecutive rows.
+template <bool BF>
 __global__ __launch_bounds__(SEL_THREADS) void pair_sums_kernel(
     Geo g, const uint16_t* __restrict__ q_sel, int n_qry,
     const uint16_t* __restrict__ k, int T, int key_blocks,
@@ -81,9 +83,10 @@ __global__ __launch_bounds__(SEL_THREADS) void pair_sums_kernel(
   uint64_t acc[8];
 #pragma unroll
   for (int e = 0; e < 8; e++) {
-    acc[e] = 0;
+    double t = 0.0;
 #pragma unroll
-    for (int i = 0; i < 8; i++) acc[e] += norm_fixed(sel_half(va[i], e), sel_half(vb[i], e), g.bf16);
+    for (int i = 0; i < 8; i++) t += norm_fixed<BF>(sel_half(va[i], e), sel_half(vb[i], e));
+    acc[e] = (uint64_t)t;
   }
   __shared__ uint64_t part[SEL_SLOTS][NPAIR];
 #pragma unroll
@@ -118,9 +121,13 @@ hipError_t launch_select(const Geo& g, const void* q_sel, int n_qry, const void*
   hipLaunchKernelGGL(zero_u64_kernel, dim3((nsum + 255) / 256), dim3(256), 0, st, c->sums, nsum);
   const int key_blocks = (T + SEL_ROWS_PER_BLOCK - 1) / SEL_ROWS_PER_BLOCK;
   const int q_blocks = (g.G * n_qry + SEL_ROWS_PER_BLOCK - 1) / SEL_ROWS_PER_BLOCK;
-  hipLaunchKernelGGL(pair_sums_kernel, dim3(g.B * g.Hkv, key_blocks + q_blocks),
-                     dim3(SEL_THREADS), 0, st, g, (const uint16_t*)q_sel, n_qry,
-                     (const uint16_t*)k, T, key_blocks, c->sums);
+  const dim3 grid(g.B * g.Hkv, key_blocks + q_blocks);
+  if (g.bf16)
+    hipLaunchKernelGGL(pair_sums_kernel<true>, grid, dim3(SEL_THREADS), 0, st, g,
+                       (const uint16_t*)q_sel, n_qry, (const uint16_t*)k, T, key_blocks, c->sums);
+  else
+    hipLaunchKernelGGL(pair_sums_kernel<false>, grid, dim3(SEL_THREADS), 0, st, g,
+                       (const uint16_t*)q_sel, n_qry, (const uint16_t*)k, T, key_blocks, c->sums);
   hipLaunchKernelGGL(rank_pairs_kernel, dim3(g.B * g.Hkv), dim3(64), 0, st,
                      (const uint64_t*)c->sums, c->pairs);
   return hipGetLastError();
@@ -154,6 +161,7 @@ __device__ inline float qa_quad(float v, bool want_max) {
 // grid (B * Hkv, ceil(groups / 16)), 4 waves of 4 groups each.  Lane
 // 4 cb + tq holds channels 8cb .. 8cb+7 of tokens 8tq .. 8tq+7 of a group
 // (one 16-byte load per token), so a channel's 32 tokens lie in one quad.
+template <bool BF>
 __global__ __launch_bounds__(256) void qa_ranges_kernel(Geo g, const uint16_t* __restrict__ k,
                                                         int T, uint64_t* __restrict__ sums) {
   const int bh = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -176,12 +184,13 @@ __global__ __launch_bounds__(256) void qa_ranges_kernel(Geo g, const uint16_t* _
       if (gw + h + u >= ng) continue;  // wave-uniform
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        float mn = in_to_f32(sel_half(v[u][0], e), g.bf16), mx = mn;
+        float mn = in_to_f32(sel_half(v[u][0], e), BF), mx = mn;
 #pragma unroll
-        for (int i = 1; i < 8; i++) {
-          const float x = in_to_f32(sel_half(v[u][i], e), g.bf16);
-          mn = fminf(mn, x);
-          mx = fmaxf(mx, x);
+        for (int i = 1; i < 8; i += 2) {  // three-input min / max
+          const float x = in_to_f32(sel_half(v[u][i], e), BF);
+          const float y = i + 1 < 8 ? in_to_f32(sel_half(v[u][i + 1], e), BF) : x;
+          mn = fminf(mn, fminf(x, y));
+          mx = fmaxf(mx, fmaxf(x, y));
         }
         mn = qa_quad(mn, false);
         mx = qa_quad(mx, true);
@@ -265,7 +274,7 @@ hipError_t launch_select_qa(const Geo& g, const void* q_sel, int n_qry, const vo
   hipLaunchKernelGGL(zero_u64_kernel, dim3((nsum + 255) / 256), dim3(256), 0, st, c->sums, nsum);
   const int ng = T / GS;
   if (ng > 0)
-    hipLaunchKernelGGL(qa_ranges_kernel,
+    hipLaunchKernelGGL(g.bf16 ? qa_ranges_kernel<true> : qa_ranges_kernel<false>,
                        dim3(g.B * g.Hkv, (ng + QA_GROUPS_PER_BLOCK - 1) / QA_GROUPS_PER_BLOCK),
                        dim3(256), 0, st, g, (const uint16_t*)k, T, c->sums);
   hipLaunchKernelGGL(qa_rank_kernel, dim3(g.B * g.Hkv), dim3(256), 0, st, g,
