@@ -506,44 +506,60 @@ hipError_t launch_quant_values(const Geo& g, const void* v, int T, kvq_cache* c,
 // index e, so its key words are written by it alone.
 __device__ inline uint32_t shrink_4_to_2(uint32_t x) { return (13u * (x + 2u)) >> 6; }
 
-__global__ __launch_bounds__(64) void shrink_kernel(Geo g, kvq_cache c, int g0, int g1) {
-  const int bh = blockIdx.x, lane = threadIdx.x;
+constexpr int SHRINK_WAVES = 4;  // groups per workgroup, one per wave
+
+// Lane e < 32 owns the token of tile index e: its eight k_lo words (four
+// 8-byte pairs, u = 0 and 1 adjacent) and its k_hi word are loaded once,
+// rewritten in registers and stored once.  The salient channels are walked
+// in ascending order from the salient-pair mask (uniform loop).
+__global__ __launch_bounds__(64 * SHRINK_WAVES) void shrink_kernel(Geo g, kvq_cache c, int g0,
+                                                                   int g1) {
+  const int bh = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ngq = n_quant(c.len[bh], g.R) / GS;
-  const int grp = g0 + (int)blockIdx.y;
-  if (grp >= min(g1, ngq)) return;
+  const int grp = g0 + (int)blockIdx.y * SHRINK_WAVES + wave;
+  if (grp >= min(g1, ngq) || lane >= GS) return;
+  const uint64_t mhi = pair_masks(g, c.pairs + (size_t)bh * NPAIR).hi;
   const size_t rec = (size_t)bh * g.NG + grp;
-  // salient channels, ascending: pairs of rank < n_hi, then the same + 64
-  const int32_t* pr = c.pairs + (size_t)bh * NPAIR;
-  bool sal = false;
-  for (int r = 0; r < g.n_hi; r++) sal |= pr[r] == (lane & (NPAIR - 1));
-  const unsigned long long m = __ballot(sal);
-  __shared__ int hil[16];
-  if (sal && lane < NPAIR) {
-    const int idx = __popcll(m & ((1ull << lane) - 1));
-    hil[idx] = lane;
-    hil[g.n_hi + idx] = lane + NPAIR;
-  }
-  __syncthreads();
-  if (lane < GS) {
-    const int e = lane, T = e >> 4, r = e & 15;
-    uint32_t* hi = (uint32_t*)c.k_hi + rec * 32;
-    uint32_t* lo = (uint32_t*)c.k_lo + rec * GROUP_WORDS;
-    uint32_t hw = hi[e];
-    for (int d = 0; d < g.nh; d++) {
-      const int ch = hil[d], w = ch >> 4, kq = w >> 1, u = w & 1;
-      uint32_t& lw = lo[((T * 4 + kq) * 16 + r) * 2 + u];
+  const int e = lane, T = e >> 4, r = e & 15;
+  uint32_t* hi = (uint32_t*)c.k_hi + rec * 32;
+  uint2* lo = (uint2*)((uint32_t*)c.k_lo + rec * GROUP_WORDS);
+  uint2 lw[4];
+#pragma unroll
+  for (int kq = 0; kq < 4; kq++) lw[kq] = lo[(T * 4 + kq) * 16 + r];
+  uint32_t hw = hi[e];
+  int d = 0;
+  for (int side = 0; side < 2; side++) {  // channels j, then j + 64
+    for (uint64_t m = mhi; m; m &= m - 1, d++) {
+      const int ch = __ffsll((unsigned long long)m) - 1 + NPAIR * side, w = ch >> 4;
       const int pl = 2 * pos_swap(ch & 15), ph = 2 * pos_swap(d);
-      const uint32_t q = shrink_4_to_2((((hw >> ph) & 3u) << 2) | ((lw >> pl) & 3u));
-      lw = (lw & ~(3u << pl)) | (q << pl);
+      // the word holding channel ch: static register choice under a uniform test
+      uint32_t word = 0;
+#pragma unroll
+      for (int x = 0; x < 8; x++)
+        if (w == x) word = (x & 1) ? lw[x >> 1].y : lw[x >> 1].x;
+      const uint32_t q = shrink_4_to_2((((hw >> ph) & 3u) << 2) | ((word >> pl) & 3u));
+      word = (word & ~(3u << pl)) | (q << pl);
       hw = (hw & ~(3u << ph)) | (q << ph);
+#pragma unroll
+      for (int x = 0; x < 8; x++)
+        if (w == x) {
+          if (x & 1)
+            lw[x >> 1].y = word;
+          else
+            lw[x >> 1].x = word;
+        }
     }
-    hi[e] = hw;
   }
+#pragma unroll
+  for (int kq = 0; kq < 4; kq++) lo[(T * 4 + kq) * 16 + r] = lw[kq];
+  hi[e] = hw;
 }
 
 hipError_t launch_shrink(const Geo& g, kvq_cache* c, int g0, int g1, hipStream_t st) {
+  g1 = min(g1, g.NG);
   if (g1 <= g0 || g.nh == 0 || g.NG == 0) return hipSuccess;
-  hipLaunchKernelGGL(shrink_kernel, dim3(g.B * g.Hkv, g1 - g0), dim3(64), 0, st, g, *c, g0, g1);
+  hipLaunchKernelGGL(shrink_kernel, dim3(g.B * g.Hkv, (g1 - g0 + SHRINK_WAVES - 1) / SHRINK_WAVES),
+                     dim3(64 * SHRINK_WAVES), 0, st, g, *c, g0, g1);
   return hipGetLastError();
 }
 
