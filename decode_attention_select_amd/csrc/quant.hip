@@ -47,14 +47,22 @@ __device__ inline uint32_t quad_bcast(uint32_t x) { return dpp<QuadBcast<K>::ctr
 // min/max value; only the sign of a zero minimum depends on the combining
 // order and on how the min instruction orders -0 and +0, and the caller
 // settles that separately (sign_of_first_zero).
-__device__ inline float quad_min(float v) {
-  v = fminf(v, __uint_as_float(dpp<QUAD_XOR1>(__float_as_uint(v))));
-  return fminf(v, __uint_as_float(dpp<QUAD_XOR2>(__float_as_uint(v))));
-}
-__device__ inline float quad_max(float v) {
-  v = fmaxf(v, __uint_as_float(dpp<QUAD_XOR1>(__float_as_uint(v))));
-  return fmaxf(v, __uint_as_float(dpp<QUAD_XOR2>(__float_as_uint(v))));
-}
+// One VALU instruction per step: the min/max reads the partner lane through
+// its DPP source operand (written directly, since the compiler would add a
+// copy and a NaN-quieting max around a separate DPP move).  s_nop 1 covers
+// the wait states between a VALU write and a DPP read of the same register.
+#define KVQ_QUAD_OP(name, op)                                                      \
+  __device__ inline float name(float v) {                                          \
+    float t, r;                                                                    \
+    asm("s_nop 1\n\t" op "_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" \
+        : "=&v"(t) : "v"(v));                                                      \
+    asm("s_nop 1\n\t" op "_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" \
+        : "=&v"(r) : "v"(t));                                                      \
+    return r;                                                                      \
+  }
+KVQ_QUAD_OP(quad_min, "v_min_f32")
+KVQ_QUAD_OP(quad_max, "v_max_f32")
+#undef KVQ_QUAD_OP
 
 // A sequential scan keeps the first of equal minima, so a minimum of zero
 // carries the sign of the group's first zero element.  f = this lane's

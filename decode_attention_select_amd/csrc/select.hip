@@ -148,15 +148,21 @@ hipError_t launch_select(const Geo& g, const void* q_sel, int n_qry, const void*
 constexpr int QA_GROUPS_PER_WAVE = 4;
 constexpr int QA_GROUPS_PER_BLOCK = 4 * QA_GROUPS_PER_WAVE;
 
-// min / max over the four lanes of a DPP quad
-__device__ inline float qa_quad(float v, bool want_max) {
-  float p = __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
-      (int)__float_as_uint(v), (int)__float_as_uint(v), 0xB1, 0xF, 0xF, false));
-  v = want_max ? fmaxf(v, p) : fminf(v, p);
-  p = __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
-      (int)__float_as_uint(v), (int)__float_as_uint(v), 0x4E, 0xF, 0xF, false));
-  return want_max ? fmaxf(v, p) : fminf(v, p);
-}
+// min / max over the four lanes of a DPP quad, one VALU instruction per
+// step (the DPP source operand reads the partner lane; s_nop 1 covers the
+// wait states between a VALU write and a DPP read of the same register)
+#define KVQ_QA_QUAD(name, op)                                                      \
+  __device__ inline float name(float v) {                                          \
+    float t, r;                                                                    \
+    asm("s_nop 1\n\t" op "_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" \
+        : "=&v"(t) : "v"(v));                                                      \
+    asm("s_nop 1\n\t" op "_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" \
+        : "=&v"(r) : "v"(t));                                                      \
+    return r;                                                                      \
+  }
+KVQ_QA_QUAD(qa_quad_min, "v_min_f32")
+KVQ_QA_QUAD(qa_quad_max, "v_max_f32")
+#undef KVQ_QA_QUAD
 
 // grid (B * Hkv, ceil(groups / 16)), 4 waves of 4 groups each.  Lane
 // 4 cb + tq holds channels 8cb .. 8cb+7 of tokens 8tq .. 8tq+7 of a group
@@ -192,8 +198,8 @@ __global__ __launch_bounds__(256) void qa_ranges_kernel(Geo g, const uint16_t* _
           mn = fminf(mn, fminf(x, y));
           mx = fmaxf(mx, fmaxf(x, y));
         }
-        mn = qa_quad(mn, false);
-        mx = qa_quad(mx, true);
+        mn = qa_quad_min(mn);
+        mx = qa_quad_max(mx);
         acc[e] += (uint64_t)((double)__fsub_rn(mx, mn) * 65536.0);  // >= 0: truncation = floor
       }
     }
@@ -223,27 +229,29 @@ __global__ __launch_bounds__(256) void qa_rank_kernel(Geo g, const uint16_t* __r
   const int cb = tid & 15, slot = tid >> 4;
   const uint16_t* base = q_sel + ((size_t)b * g.Hq + (size_t)kh * g.G) * n_qry * D;
   const int nrows = g.G * n_qry;
-  uint64_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r0 = 0; r0 < nrows; r0 += 64) {
-    uint4 v[4];
+  // floor(|q| * 2^24) is an exact integer-valued double; a thread sums at most
+  // 1024 rows (G * n_qry <= 16 * 1024), exact for |q| below 2^19
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r0 = 0; r0 < nrows; r0 += 256) {  // 16 rows per thread in flight
+    uint4 v[16];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < 16; i++) {
       const int r = r0 + slot + 16 * i;
       v[i] = r < nrows ? *(const uint4*)(base + (size_t)r * D + 8 * cb) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 16; i++)
 #pragma unroll
       for (int e = 0; e < 8; e++) {
         const float x = fabsf(in_to_f32(sel_half(v[i], e), g.bf16));
-        acc[e] += (uint64_t)((double)x * 16777216.0);
+        acc[e] += floor((double)x * 16777216.0);
       }
   }
   __shared__ uint64_t Ap[16][D];
   __shared__ uint64_t As[D], Rs[D];
   __shared__ double S[NPAIR];
 #pragma unroll
-  for (int e = 0; e < 8; e++) Ap[slot][8 * cb + e] = acc[e];
+  for (int e = 0; e < 8; e++) Ap[slot][8 * cb + e] = (uint64_t)acc[e];
   __syncthreads();
   const int c = tid;
   if (c < D) {
