@@ -124,10 +124,24 @@ __device__ inline void wave_lds_sync() {
 struct PairMasks {
   uint64_t hi, one;
 };
+// The ranks are read in fixed-size blocks (wave-uniform scalar loads, all in
+// flight together) rather than one dependent load per rank.
 __device__ inline PairMasks pair_masks(const Geo& g, const int32_t* pr) {
   uint64_t hi = 0, one = 0;
-  for (int r = 0; r < g.n_hi; r++) hi |= 1ull << (pr[r] & (NPAIR - 1));
-  for (int r = NPAIR - g.n_lo1; r < NPAIR; r++) one |= 1ull << (pr[r] & (NPAIR - 1));
+  int p[8];
+#pragma unroll
+  for (int r = 0; r < 8; r++) p[r] = pr[r];  // n_hi <= 8
+#pragma unroll
+  for (int r = 0; r < 8; r++)
+    if (r < g.n_hi) hi |= 1ull << (p[r] & (NPAIR - 1));
+  if (g.n_lo1) {
+    int t[NPAIR];
+#pragma unroll
+    for (int r = 0; r < NPAIR; r++) t[r] = pr[r];
+#pragma unroll
+    for (int r = 0; r < NPAIR; r++)
+      if (r >= NPAIR - g.n_lo1) one |= 1ull << (t[r] & (NPAIR - 1));
+  }
   return {hi, one};
 }
 
