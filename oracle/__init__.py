@@ -255,3 +255,33 @@ def select_qa(q_sel, k, T: int, n_kv_heads: int, io_dtype: str):
                                int(T), _p(bits), _p(pairs))
     assert rc == 0
     return bits.view(np.float64), pairs
+
+
+def prune_chunks(q, n_kv_heads: int, io_dtype: str, n_keep: int) -> np.ndarray:
+    """Query-channel pruning (the Dual-QK reading): bool [B][Hkv][4], True
+    for the n_keep 32-channel key chunks of largest summed fixed-point |q|
+    over the group's heads (ties to the lower chunk)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    B, Hq, _ = q.shape
+    keep = np.zeros((B, n_kv_heads, 4), np.uint8)
+    rc = _load().orc_prune_chunks(B, Hq, n_kv_heads, _bf(io_dtype), _p(q), int(n_keep), _p(keep))
+    assert rc == 0
+    return keep.astype(bool)
+
+
+def attention_pruned(qz: Quantized, q, sm_scale: float, n_keep: int, with_lse: bool = False):
+    """Decode attention with pruned query channels: every logit sums q_c k^_c
+    over the kept chunks' channels only (quantized and ring tokens alike),
+    written as attention over the query with the pruned channels set to 0."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    B, Hq, _ = q.shape
+    Hkv = qz.kcodes.shape[1]
+    keep = prune_chunks(q, Hkv, qz.io_dtype, n_keep)
+    qm = q.copy()
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            for m in range(4):
+                if not keep[b, h // G, m]:
+                    qm[b, h, 32 * m:32 * m + 32] = 0
+    return attention(qz, qm, sm_scale, with_lse=with_lse)

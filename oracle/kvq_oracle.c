@@ -197,6 +197,38 @@ int orc_select_qa(int B, int Hq, int Hkv, int bf16, const uint16_t *q_sel,
   return 0;
 }
 
+/* Dynamic query-channel pruning at decode (Dual-QK, abstract: a decode
+ * query keeps its few large channels and drops the many small ones, so the
+ * key cache is read only for the kept channels; the page gives no rule, so
+ * this is a reading).  The unit is the cache's 32-channel key chunk
+ * (channels 32m .. 32m+31, m = 0..3), the smallest run of key codes that is
+ * contiguous in the packed layout, and the decision is per (b, kv head),
+ * since the G query heads share one key cache:
+ *   E_m = sum over the group's query heads h and channels c of chunk m of
+ *         floor(|q_{h,c}| * 2^24)
+ * The n_keep chunks of largest E_m are kept (ties to the lower m).
+ * keep[(b*Hkv + kh)*4 + m] = 1 for a kept chunk, else 0. */
+int orc_prune_chunks(int B, int Hq, int Hkv, int bf16, const uint16_t *q, int n_keep,
+                     uint8_t *keep) {
+  if (Hq % Hkv || n_keep < 1 || n_keep > 4) return -1;
+  int G = Hq / Hkv;
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++) {
+      uint64_t E[4] = {0, 0, 0, 0};
+      for (int h = kh * G; h < kh * G + G; h++)
+        for (int c = 0; c < D; c++) {
+          double x = fabs(to_f64(q[((size_t)b * Hq + h) * D + c], bf16));
+          E[c / 32] += (uint64_t)floor(x * 16777216.0);
+        }
+      for (int m = 0; m < 4; m++) {
+        int rank = 0;
+        for (int i = 0; i < 4; i++) rank += (E[i] > E[m]) || (E[i] == E[m] && i < m);
+        keep[((size_t)b * Hkv + kh) * 4 + m] = rank < n_keep;
+      }
+    }
+  return 0;
+}
+
 /* Bits of channel c given the rank table of its (b, kv head): the pairs of
  * the n_hi highest ranks at bits_hi, those of the n_lo1 lowest ranks at one
  * bit, all others at bits_lo (PN-Mix, abstract: more bits for the salient
