@@ -34,12 +34,22 @@ PEAK_GBS = 8000.0
 TRAFFIC = 27523686
 
 
-def algorithmic_bytes(w, T: int) -> int:
+def algorithmic_bytes(w, T: int, n_keep: int = 4) -> int:
+    """Bytes a decode step must move.  With n_keep < 4 (query-channel
+    pruning, 2-bit / 4-bit-salient layouts) only the kept chunks' low key
+    digits, key scale/zero and ring keys count; the salient high digits are
+    one word per token and are read whole."""
     R = w.residual
     nq = 32 * (max(0, T - R) // 32)
     nr = T - nq
     n_hi_ch, n_one_ch = 2 * w.n_pairs_hi, 2 * w.n_pairs_lo1
     n_two_ch = 128 - n_hi_ch - n_one_ch
+    bh = w.batch * w.n_kv_heads
+    qo = 2 * w.batch * w.n_q_heads * 128 * 2
+    if n_keep < 4:
+        assert w.bits_hi == 4 and w.n_pairs_lo1 == 0
+        per_tok = (2 * 32 * n_keep + 2 * n_hi_ch) / 8 + 4 * n_keep + 32 + 16
+        return int(round(bh * (nq * per_tok + nr * (64 * n_keep + 256)) + qo))
     if w.bits_hi == 16:
         k_code_bits = n_hi_ch * 16 + n_two_ch * 2 + n_one_ch
         k_meta = (128 - n_hi_ch) * 4 / 32
@@ -47,8 +57,7 @@ def algorithmic_bytes(w, T: int) -> int:
         k_code_bits = n_hi_ch * w.bits_hi + n_two_ch * 2 + n_one_ch
         k_meta = 128 * 4 / 32
     per_tok = k_code_bits / 8 + k_meta + 32 + 16
-    bh = w.batch * w.n_kv_heads
-    return int(round(bh * (nq * per_tok + nr * 512) + 2 * w.batch * w.n_q_heads * 128 * 2))
+    return int(round(bh * (nq * per_tok + nr * 512) + qo))
 
 
 def layout_bytes(cache, w, T: int) -> int:
@@ -458,6 +467,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--replica-mib", type=int, default=512)
+    ap.add_argument("--prune", type=int, default=4,
+                    help="kvq_decode_attn_pruned with this many of the four 32-channel key "
+                         "chunks kept (4: kvq_decode_attn)")
     ap.add_argument("--build", action="store_true",
                     help="time the cache-building calls on the workload instead of decode")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -514,8 +526,13 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(i):
-        kvq.kvq_decode_attn(layout, q, replicas[i % n_rep].struct, float(np.float32(SM_SCALE)),
-                            S, ws, out, stream=stream)
+        if args.prune < 4:
+            kvq.kvq_decode_attn_pruned(layout, q, replicas[i % n_rep].struct,
+                                       float(np.float32(SM_SCALE)), S, args.prune, ws, out,
+                                       stream=stream)
+        else:
+            kvq.kvq_decode_attn(layout, q, replicas[i % n_rep].struct,
+                                float(np.float32(SM_SCALE)), S, ws, out, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -534,7 +551,7 @@ def main():
     # One step is one launch of the decode kernel, back to back on one stream:
     # the event-timed average over the timed region is its average launch
     # duration (it also holds the short gap between launches).
-    alg = algorithmic_bytes(w, T)
+    alg = algorithmic_bytes(w, T, args.prune)
     gbs = alg / (ev_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -555,14 +572,19 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "context": T, "io_dtype": w.io_dtype,
                    "salient_pairs": w.n_pairs_hi, "salient_bits": w.bits_hi,
-                   "residual": w.residual, "n_splits": S, "cache_replicas": n_rep},
+                   "residual": w.residual, "n_splits": S, "cache_replicas": n_rep,
+                   **({"kept_key_chunks": args.prune} if args.prune < 4 else {})},
         "algorithmic_bytes_per_step": alg,
         "layout_bytes_per_step": layout_bytes(base, w, T),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4),
-                     "traffic": TRAFFIC},
+                     "traffic": TRAFFIC if (args.prune == 4 and
+                                            w.name == "llama3-8b-32k") else None},
     }
-    if not args.no_cpu_baseline:
+    if args.prune < 4:
+        res["note"] = ("query-channel pruning: %d of 4 key chunks kept per KV head; bytes are "
+                       "those of the kept chunks" % args.prune)
+    if not args.no_cpu_baseline and args.prune == 4:
         res["cpu_baseline"] = cpu_baseline(w, data)
     print(json.dumps(res), flush=True)
 

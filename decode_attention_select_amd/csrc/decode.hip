@@ -131,12 +131,17 @@ struct Pref {
   u4 meta;          // 16 B of the group's k_meta (lanes 0-31) or v_meta (lanes 32-63)
 };
 
+// kqa: the key chunk whose low digits this lane reads (its own, kq, unless
+// that chunk is pruned; then a kept chunk that other lanes read in the same
+// instruction, so no extra line is fetched); mla: the same for the lane's
+// 16-byte piece of the key scale/zero record.  A redirected lane's values
+// only ever meet a zero query.
 template <int HIMODE>
 __device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int col, int kq,
-                                  int nh, Pref& p) {
+                                  int kqa, int mla, int nh, Pref& p) {
   const u2* klo = (const u2*)((const uint32_t*)c.k_lo + rec * GROUP_WORDS);
-  p.klo[0] = klo[(0 * 4 + kq) * 16 + col];
-  p.klo[1] = klo[(1 * 4 + kq) * 16 + col];
+  p.klo[0] = klo[(0 * 4 + kqa) * 16 + col];
+  p.klo[1] = klo[(1 * 4 + kqa) * 16 + col];
   if constexpr (HIMODE == 4) {
     const uint32_t* kh = (const uint32_t*)c.k_hi + rec * 32;
     p.khi[0] = kh[col];
@@ -157,7 +162,7 @@ __device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int 
   for (int j = 0; j < 4; j++) p.vc[j] = vc[(j * 4 + kq) * 16 + col];
   const u4* meta = lane < 32 ? (const u4*)((const uint16_t*)c.k_meta + rec * 2 * D)
                              : (const u4*)((const uint16_t*)c.v_meta + rec * 2 * D);
-  p.meta = meta[lane & 31];
+  p.meta = meta[mla];
 }
 
 // Workspace of one call (zero-filled once by the caller; counters return to
@@ -218,10 +223,19 @@ struct Lds {
 // LO1: some pairs are at 1 bit.  Their scale is the whole group range, three
 // times a 2-bit channel's, so q*s is carried as an exact fp16 pair (rounded
 // value + rounding residual) through a second MFMA pass over the same codes.
-template <bool BF16, int HIMODE, bool HASQ, bool LO1>
+// PRUNE: query-channel pruning (Dual-QK, abstract: a decode query keeps its
+// few large channels and the key cache is read only for them).  Per
+// (sequence, KV head) the `keep` 32-channel key chunks of largest
+// sum over the group's heads of floor(|q_c| * 2^24) are kept (ties to the
+// lower chunk); the query is zero on the others, whose key codes and
+// scale/zero are not read (past the first PF prefetched groups, which are
+// issued before the query arrives): their lanes load a kept chunk's words
+// instead, which the same instruction fetches anyway.
+template <bool BF16, int HIMODE, bool HASQ, bool LO1, bool PRUNE>
 __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             kvq_cache c, float scale_log2, int S,
-                                                            Ws ws, uint16_t* __restrict__ out) {
+                                                            int keep, Ws ws,
+                                                            uint16_t* __restrict__ out) {
   __shared__ Lds lds;
   // the wave index is wave-uniform: keeping it in a scalar register makes every
   // group address scalar (one 64-bit base per load, no per-lane address math)
@@ -274,8 +288,51 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   Pref pf[PF];
   if constexpr (HASQ) {
 #pragma unroll
-    for (int k = 0; k < PF; k++) load_group<HIMODE>(c, group_at(k), lane, col, kq, g.nh, pf[k]);
+    for (int k = 0; k < PF; k++)
+      load_group<HIMODE>(c, group_at(k), lane, col, kq, kq, lane & 31, g.nh, pf[k]);
   }
+
+  // kept key chunks (all four unless PRUNE); every lane computes the same mask
+  uint32_t kmask = 0xFu;
+  if constexpr (PRUNE) {
+    double e = 0.0;  // exact: 32 terms, each an integer below 2^24 * |q|
+    if (hvalid) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+          const uint32_t x = qv[i][w];
+          e += floor((double)fabsf(in_to_f32((uint16_t)(x & 0xFFFF), BF16)) * 16777216.0);
+          e += floor((double)fabsf(in_to_f32((uint16_t)(x >> 16), BF16)) * 16777216.0);
+        }
+    }
+    uint64_t E = (uint64_t)e;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {  // the 16 lanes of chunk kq (heads col)
+      const uint32_t lo = __shfl_xor((uint32_t)E, o), hi = __shfl_xor((uint32_t)(E >> 32), o);
+      E += (uint64_t)lo | ((uint64_t)hi << 32);
+    }
+    int rank = 0;
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const uint32_t lo = __shfl((uint32_t)E, 16 * m), hi = __shfl((uint32_t)(E >> 32), 16 * m);
+      const uint64_t Em = (uint64_t)lo | ((uint64_t)hi << 32);
+      rank += (Em > E) || (Em == E && m < kq);
+    }
+    const uint64_t bal = __ballot(rank < keep);
+    kmask = __builtin_amdgcn_readfirstlane(
+        (uint32_t)((bal & 1u) | ((bal >> 15) & 2u) | ((bal >> 30) & 4u) | ((bal >> 45) & 8u)));
+    if (!((kmask >> kq) & 1u)) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) qv[i] = u4{0, 0, 0, 0};
+    }
+  }
+  // lanes 0..31 read the key scales (lanes 0..15) and zeros (16..31) of
+  // channels 8 (lane % 16) .. +7, i.e. of chunk (lane % 16) / 4
+  const int kept0 = __builtin_ctz(kmask);
+  const int kqa = ((kmask >> kq) & 1u) ? kq : kept0;
+  const int mla = (lane >= 32 || ((kmask >> ((lane & 15) >> 2)) & 1u))
+                      ? (lane & 31) : ((lane & 16) | (kept0 << 2) | (lane & 3));
 
   // query as fp16 pairs (zero past the G heads)
   uint32_t q16[16];
@@ -480,7 +537,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     u4 kt[2][4], vt[8];
 #pragma unroll
     for (int TT = 0; TT < 2; TT++) {
-      const u4* kr = (const u4*)(rk + (size_t)tile_token(16 * TT + col) * D + 32 * kq);
+      const u4* kr = (const u4*)(rk + (size_t)tile_token(16 * TT + col) * D + 32 * kqa);
 #pragma unroll
       for (int k = 0; k < 4; k++) kt[TT][k] = kr[k];
     }
@@ -534,7 +591,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
       for (int k = 0; k < PF; k++) {
         if (i + k < nmine) process_group(pf[k], group_at(i + k));
-        load_group<HIMODE>(c, group_at(i + k + PF), lane, col, kq, g.nh, pf[k]);
+        load_group<HIMODE>(c, group_at(i + k + PF), lane, col, kq, kqa, mla, g.nh, pf[k]);
       }
     }
   }
@@ -679,24 +736,29 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool BF16, int HIMODE, bool LO1>
+template <bool BF16, int HIMODE, bool LO1, bool PRUNE>
 static void launch_one(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
-                       const Ws& ws, void* out, hipStream_t st) {
+                       int keep, const Ws& ws, void* out, hipStream_t st) {
   if (g.NG > 0)
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, LO1>), dim3(g.B * g.Hkv * S),
-                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, ws,
-                       (uint16_t*)out);
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, LO1, PRUNE>), dim3(g.B * g.Hkv * S),
+                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, keep,
+                       ws, (uint16_t*)out);
   else
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, LO1>), dim3(g.B * g.Hkv * S),
-                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, ws,
-                       (uint16_t*)out);
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, LO1, PRUNE>), dim3(g.B * g.Hkv * S),
+                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, keep,
+                       ws, (uint16_t*)out);
 }
 
 template <bool BF16, int HIMODE>
 static void launch_lo1(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
-                       const Ws& ws, void* out, hipStream_t st) {
-  if (g.n_lo1 > 0) launch_one<BF16, HIMODE, true>(g, q, c, scale_log2, S, ws, out, st);
-  else launch_one<BF16, HIMODE, false>(g, q, c, scale_log2, S, ws, out, st);
+                       int keep, const Ws& ws, void* out, hipStream_t st) {
+  if (keep < 4) {
+    if (g.n_lo1 > 0) launch_one<BF16, HIMODE, true, true>(g, q, c, scale_log2, S, keep, ws, out, st);
+    else launch_one<BF16, HIMODE, false, true>(g, q, c, scale_log2, S, keep, ws, out, st);
+  } else {
+    if (g.n_lo1 > 0) launch_one<BF16, HIMODE, true, false>(g, q, c, scale_log2, S, 4, ws, out, st);
+    else launch_one<BF16, HIMODE, false, false>(g, q, c, scale_log2, S, 4, ws, out, st);
+  }
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {
@@ -704,18 +766,18 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {
 }
 
 hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float sm_scale,
-                         int S, void* workspace, void* out, hipStream_t st) {
+                         int S, int keep, void* workspace, void* out, hipStream_t st) {
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   const int hm = g.n_hi == 0 ? 0 : g.bits_hi;
   const Ws ws = ws_layout(workspace, g.B, g.Hq, S);
   if (g.bf16) {
-    if (hm == 0) launch_lo1<true, 0>(g, q, c, scale_log2, S, ws, out, st);
-    else if (hm == 4) launch_lo1<true, 4>(g, q, c, scale_log2, S, ws, out, st);
-    else launch_lo1<true, 16>(g, q, c, scale_log2, S, ws, out, st);
+    if (hm == 0) launch_lo1<true, 0>(g, q, c, scale_log2, S, keep, ws, out, st);
+    else if (hm == 4) launch_lo1<true, 4>(g, q, c, scale_log2, S, keep, ws, out, st);
+    else launch_lo1<true, 16>(g, q, c, scale_log2, S, keep, ws, out, st);
   } else {
-    if (hm == 0) launch_lo1<false, 0>(g, q, c, scale_log2, S, ws, out, st);
-    else if (hm == 4) launch_lo1<false, 4>(g, q, c, scale_log2, S, ws, out, st);
-    else launch_lo1<false, 16>(g, q, c, scale_log2, S, ws, out, st);
+    if (hm == 0) launch_lo1<false, 0>(g, q, c, scale_log2, S, keep, ws, out, st);
+    else if (hm == 4) launch_lo1<false, 4>(g, q, c, scale_log2, S, keep, ws, out, st);
+    else launch_lo1<false, 16>(g, q, c, scale_log2, S, keep, ws, out, st);
   }
   return hipGetLastError();
 }

@@ -15,7 +15,8 @@ hipError_t launch_shrink(const Geo& g, kvq_cache* c, int g0, int g1, hipStream_t
 hipError_t launch_append(const Geo& g, const void* k_new, const void* v_new, kvq_cache* c,
                          hipStream_t st);
 hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float sm_scale,
-                         int n_splits, void* workspace, void* out, hipStream_t st);
+                         int n_splits, int keep_chunks, void* workspace, void* out,
+                         hipStream_t st);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_splits);
 
 }  // namespace kvq

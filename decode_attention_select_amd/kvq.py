@@ -140,6 +140,15 @@ def kvq_decode_attn(layout, q, cache: kvq_cache, sm_scale, n_splits, workspace, 
           ctypes.c_size_t(ws_bytes), _ptr(out), _stream(stream))
 
 
+def kvq_decode_attn_pruned(layout, q, cache: kvq_cache, sm_scale, n_splits, n_keep, workspace,
+                           out, stream=None, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _call("kvq_decode_attn_pruned", ctypes.byref(layout), _ptr(q), ctypes.byref(cache),
+          ctypes.c_float(sm_scale), ctypes.c_int32(n_splits), ctypes.c_int32(n_keep),
+          _ptr(workspace), ctypes.c_size_t(ws_bytes), _ptr(out), _stream(stream))
+
+
 def kvq_check(cache: kvq_cache, stream=None) -> int:
     err = ctypes.c_int32(0)
     _call("kvq_check", ctypes.byref(cache), ctypes.byref(err), _stream(stream))

@@ -254,6 +254,26 @@ kvq_status kvq_decode_attn(const kvq_layout *L, const void *q,
                            int32_t n_splits, void *workspace, size_t ws_bytes,
                            void *out, void *stream);
 
+/* Decode attention with dynamic query-channel pruning ([Dual-QK] abstract:
+ * a decode query keeps its few large channels and drops the many small
+ * ones, so the key cache is read only for the kept channels; the page gives
+ * no rule, so this is a reading).  Per (b, kv head) the n_keep (1..4) of the
+ * four 32-channel key chunks (channels 32m .. 32m+31: the contiguous runs of
+ * k_lo, k_meta and ring_k) with the largest
+ *   E_m = sum over the group's query heads h and channels c of chunk m of
+ *         floor(|q[h][c]| * 2^24)
+ * are kept (ties to the lower m), and every logit sums q[h][c] * k^[t][c]
+ * over the kept channels only, for quantized and ring tokens alike (the
+ * query is zero on the pruned channels).  Past a split's first prefetched
+ * groups the pruned chunks' key codes and key scale/zero are not read.
+ * n_keep = 4 is kvq_decode_attn; n_keep outside 1..4 returns KVQ_EINVAL.
+ * All other arguments, limits and errors as for kvq_decode_attn. */
+kvq_status kvq_decode_attn_pruned(const kvq_layout *L, const void *q,
+                                  const kvq_cache *cache, float sm_scale,
+                                  int32_t n_splits, int32_t n_keep,
+                                  void *workspace, size_t ws_bytes, void *out,
+                                  void *stream);
+
 /* Synchronizes `stream`, then copies cache->err to *host_err (tests and
  * debugging only). */
 kvq_status kvq_check(const kvq_cache *cache, int32_t *host_err /*host*/,

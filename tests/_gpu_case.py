@@ -84,6 +84,16 @@ class Case:
         }
         return out
 
+    def decode_pruned(self, q_bits: np.ndarray, n_splits: int, n_keep: int):
+        """kvq_decode_attn_pruned -> GPU output widened to fp64."""
+        ws = torch.zeros(kvq.kvq_workspace_bytes(self.layout, n_splits), dtype=torch.uint8,
+                         device="cuda")
+        out = torch.empty((self.w.batch, self.w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+        kvq.kvq_decode_attn_pruned(self.layout, dev(q_bits), self.cache.struct, SM_SCALE,
+                                   n_splits, n_keep, ws, out)
+        torch.cuda.synchronize()
+        return kvq_synth.bits_to_f64(host(out, np.uint16), self.w.io_dtype)
+
     def decode(self, q_bits: np.ndarray, n_splits: int, partials: bool = False):
         """q_bits [B][Hq][128] -> GPU output widened to fp64; with `partials`
         also the per-split records read back from the workspace: fp32 (m, l)

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(names) >= {"kvq_select_pairs", "kvq_quant_keys", "kvq_quant_values",
                           "kvq_append", "kvq_decode_attn", "kvq_cache_sizes",
                           "kvq_workspace_bytes", "kvq_check", "kvq_status_str", "kvq_shrink",
-                          "kvq_select_pairs_qa"}
+                          "kvq_select_pairs_qa", "kvq_decode_attn_pruned"}
     lib = kvq.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -128,6 +128,14 @@ def test_decode_validation():
     bad = fake_cache()
     bad.len = 0
     assert call(cache=bad) == EINVAL
+    # the pruned variant: n_keep outside 1..4
+    for n_keep, want in ((0, EINVAL), (5, EINVAL), (-1, EINVAL)):
+        assert status_of("kvq_decode_attn_pruned", ctypes.byref(L), P(FAKE), ctypes.byref(c),
+                         ctypes.c_float(0.088), 8, n_keep, P(FAKE), ctypes.c_size_t(ws), P(FAKE),
+                         P(0)) == want
+    assert status_of("kvq_decode_attn_pruned", ctypes.byref(L), P(FAKE), ctypes.byref(c),
+                     ctypes.c_float(0.088), 8, 2, P(FAKE), ctypes.c_size_t(ws - 1), P(FAKE),
+                     P(0)) == ECAPACITY
 
 
 @no_gpu

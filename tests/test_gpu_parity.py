@@ -226,3 +226,38 @@ def test_select_qa_bit_exact(w):
     assert np.array_equal(g["sums"][:, :, 0], S.view(np.uint64))
     assert np.all(g["sums"][:, :, 1] == 0)
     assert np.array_equal(g["pairs"], pairs)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=_ids)
+@pytest.mark.parametrize("n_keep", [1, 2, 3])
+def test_pruned_decode_matches_oracle(w, n_keep):
+    # query-channel pruning: logits over the kept 32-channel key chunks only
+    case = Case(w)
+    qz = case.oracle_quant()
+    q = case.d["q_dec"][:, :, 0]
+    ref = oracle.attention_pruned(qz, q, SM_SCALE, n_keep)
+    for S in (1, 7):
+        err = check_output(case.decode_pruned(q, S, n_keep), ref, w.io_dtype, ATOL)
+        print("%s keep=%d S=%d max|err| %.3g" % (w.name, n_keep, S, err))
+
+
+def test_pruned_keep_all_equals_unpruned():
+    w = SMALL[1]
+    case = Case(w)
+    q = case.d["q_dec"][:, :, 0]
+    a = case.decode(q, 5)
+    b = case.decode_pruned(q, 5, 4)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("T", [1, 33, 161])
+def test_pruned_decode_edge_lengths(T):
+    # ring-only and ragged lengths: ring keys are pruned as well
+    w = kvq_synth.Workload("edge", 1, 4, 1, 200, n_qry=8, io_dtype="bf16", n_pairs_hi=6,
+                           residual=128, seed=30)
+    case = Case(w, T=T)
+    qz = case.oracle_quant()
+    q = case.d["q_dec"][:, :, 0]
+    for n_keep in (1, 3):
+        ref = oracle.attention_pruned(qz, q, SM_SCALE, n_keep)
+        check_output(case.decode_pruned(q, 3, n_keep), ref, w.io_dtype, ATOL)
