@@ -125,6 +125,7 @@ __device__ inline void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) 
 // Per-lane loads of one quantized group, issued one block ahead.
 struct Pref {
   u2 klo[2];        // k_lo words of tile 0 and 1 (token col of the tile, channels 32kq..)
+  uint32_t klc[2][4];  // pruned decode: k_lo word kq/2 of a key chunk per slot, tiles 0, 1
   uint32_t khi[2];  // k_hi word of tile 0 and 1
   u4 hraw[2];       // raw salient keys (HIMODE 16): 8 values of the lane's token, tile 0 and 1
   uint32_t vc[4];   // v_codes word of channel group j = 0..3
@@ -136,12 +137,26 @@ struct Pref {
 // instruction, so no extra line is fetched); mla: the same for the lane's
 // 16-byte piece of the key scale/zero record.  A redirected lane's values
 // only ever meet a zero query.
-template <int HIMODE>
+// CHUNKED (pruned decode): slot i (< NCH) holds, for key chunk
+// (cmap >> 2i) & 3, the lane token's k_lo word kq/2 of that chunk.  Pruned
+// chunks are never named in cmap, so they are never fetched.
+template <int HIMODE, bool CHUNKED, int NCH>
 __device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int col, int kq,
-                                  int kqa, int mla, int nh, Pref& p) {
-  const u2* klo = (const u2*)((const uint32_t*)c.k_lo + rec * GROUP_WORDS);
-  p.klo[0] = klo[(0 * 4 + kqa) * 16 + col];
-  p.klo[1] = klo[(1 * 4 + kqa) * 16 + col];
+                                  int kqa, int mla, uint32_t cmap, int nh, Pref& p) {
+  if constexpr (CHUNKED) {
+    const uint32_t* w = (const uint32_t*)c.k_lo + rec * GROUP_WORDS;
+#pragma unroll
+    for (int TT = 0; TT < 2; TT++)
+#pragma unroll
+      for (int i = 0; i < NCH; i++) {
+        const int mm = (cmap >> (2 * i)) & 3u;
+        p.klc[TT][i] = w[((TT * 4 + mm) * 16 + col) * 2 + (kq >> 1)];
+      }
+  } else {
+    const u2* klo = (const u2*)((const uint32_t*)c.k_lo + rec * GROUP_WORDS);
+    p.klo[0] = klo[(0 * 4 + kqa) * 16 + col];
+    p.klo[1] = klo[(1 * 4 + kqa) * 16 + col];
+  }
   if constexpr (HIMODE == 4) {
     const uint32_t* kh = (const uint32_t*)c.k_hi + rec * 32;
     p.khi[0] = kh[col];
@@ -223,19 +238,19 @@ struct Lds {
 // LO1: some pairs are at 1 bit.  Their scale is the whole group range, three
 // times a 2-bit channel's, so q*s is carried as an exact fp16 pair (rounded
 // value + rounding residual) through a second MFMA pass over the same codes.
-// PRUNE: query-channel pruning (Dual-QK, abstract: a decode query keeps its
-// few large channels and the key cache is read only for them).  Per
-// (sequence, KV head) the `keep` 32-channel key chunks of largest
+// KEEP < 4: query-channel pruning (Dual-QK, abstract: a decode query keeps
+// its few large channels and the key cache is read only for them).  Per
+// (sequence, KV head) the KEEP 32-channel key chunks of largest
 // sum over the group's heads of floor(|q_c| * 2^24) are kept (ties to the
 // lower chunk); the query is zero on the others, whose key codes and
 // scale/zero are not read (past the first PF prefetched groups, which are
 // issued before the query arrives): their lanes load a kept chunk's words
 // instead, which the same instruction fetches anyway.
-template <bool BF16, int HIMODE, bool HASQ, bool LO1, bool PRUNE>
+template <bool BF16, int HIMODE, bool HASQ, bool LO1, int KEEP>
 __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             kvq_cache c, float scale_log2, int S,
-                                                            int keep, Ws ws,
-                                                            uint16_t* __restrict__ out) {
+                                                            Ws ws, uint16_t* __restrict__ out) {
+  constexpr bool PRUNE = KEEP < 4;
   __shared__ Lds lds;
   // the wave index is wave-uniform: keeping it in a scalar register makes every
   // group address scalar (one 64-bit base per load, no per-lane address math)
@@ -289,7 +304,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   if constexpr (HASQ) {
 #pragma unroll
     for (int k = 0; k < PF; k++)
-      load_group<HIMODE>(c, group_at(k), lane, col, kq, kq, lane & 31, g.nh, pf[k]);
+      load_group<HIMODE, PRUNE, 4>(c, group_at(k), lane, col, kq, kq, lane & 31, 0xE4u, g.nh,
+                                   pf[k]);
   }
 
   // kept key chunks (all four unless PRUNE); every lane computes the same mask
@@ -319,7 +335,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       const uint64_t Em = (uint64_t)lo | ((uint64_t)hi << 32);
       rank += (Em > E) || (Em == E && m < kq);
     }
-    const uint64_t bal = __ballot(rank < keep);
+    const uint64_t bal = __ballot(rank < KEEP);
     kmask = __builtin_amdgcn_readfirstlane(
         (uint32_t)((bal & 1u) | ((bal >> 15) & 2u) | ((bal >> 30) & 4u) | ((bal >> 45) & 8u)));
     if (!((kmask >> kq) & 1u)) {
@@ -331,6 +347,18 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // channels 8 (lane % 16) .. +7, i.e. of chunk (lane % 16) / 4
   const int kept0 = __builtin_ctz(kmask);
   const int kqa = ((kmask >> kq) & 1u) ? kq : kept0;
+  // kept chunks in ascending order, two bits each (uniform)
+  uint32_t cmap = 0;
+  {
+    int n = 0;
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+      if ((kmask >> m) & 1u) {
+        cmap |= (uint32_t)m << (2 * n);
+        n++;
+      }
+  }
+
   const int mla = (lane >= 32 || ((kmask >> ((lane & 15) >> 2)) & 1u))
                       ? (lane & 31) : ((lane & 16) | (kept0 << 2) | (lane & 3));
 
@@ -386,6 +414,34 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     sal_ch = hil[lane & 15] & (D - 1);
   }
 
+  // PRUNE: each MFMA's 32-long contraction covers one key chunk m.  Lane
+  // (col, kq) feeds the pairs 16m + 8(kq/2) + 2b + (kq%2), b = 0..3, of
+  // chunk m: the codes of one nibble plane (kq%2) of k_lo word kq/2, in
+  // byte order.  qk[i] holds head col's fp16 query at those pairs of the
+  // i-th kept chunk.
+  const int pb = 8 * (kq >> 1) + (kq & 1);
+  uint32_t qk[4][4];
+  if constexpr (PRUNE) {
+    uint16_t(*wq)[D + 8] = lds.u.loop.q16[wave];
+    if constexpr (HIMODE == 0) {
+      if (hvalid) {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          *(u4*)&wq[col][32 * kq + 8 * i] =
+              u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
+      }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int i = 0; i < KEEP; i++) {
+      const int mm = (cmap >> (2 * i)) & 3u;
+#pragma unroll
+      for (int b = 0; b < 4; b++)
+        qk[i][b] = hvalid ? *(const uint32_t*)&wq[col][2 * (16 * mm + pb + 2 * b)] : 0u;
+    }
+  }
+
   float m_run = -INFINITY, l_raw = 0.0f;
   f4 O[8], Cvb = {0, 0, 0, 0};
 #pragma unroll
@@ -430,6 +486,27 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     // each tile's accumulator starts from the bias, so no VALU adds follow
     uint32_t qs[16], qsl[16];
     f4 cb = {0, 0, 0, 0};
+    if constexpr (PRUNE) {
+      // kept chunk i's q*s pairs into qs[4i..4i+3]; pruned chunks take no work
+#pragma unroll
+      for (int i = 0; i < KEEP; i++) {
+        const int mm = (cmap >> (2 * i)) & 3u;
+        uint32_t zp[4];
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const uint32_t sp = sm[16 * mm + pb + 2 * b];
+          zp[b] = sm[64 + 16 * mm + pb + 2 * b];
+          qs[4 * i + b] = pk_mul(qk[i][b], sp);
+          if constexpr (LO1) {
+            const h2 a = u2h(qk[i][b]), bb = u2h(sp), h = u2h(qs[4 * i + b]);
+            qsl[4 * i + b] = pk_rne(fmaf((float)a[0], (float)bb[0], -(float)h[0]),
+                                    fmaf((float)a[1], (float)bb[1], -(float)h[1]));
+          }
+        }
+        cb = mma_f16(u4{zp[0], zp[1], zp[2], zp[3]}, u4{qk[i][0], qk[i][1], qk[i][2], qk[i][3]},
+                     cb);
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const u4 sv = ((const u4*)(sm + 16 * kq))[i];
@@ -446,6 +523,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       }
       const u4 qb = u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
       cb = mma_f16(zv, qb, cb);
+    }
     }
     uint32_t qshi[4];
     if constexpr (HIMODE == 4) {
@@ -471,8 +549,19 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     f4 C[2];
 #pragma unroll
     for (int TT = 0; TT < 2; TT++) {
-      const u2 w = cur.klo[TT];
       f4 acc = cb;
+      if constexpr (PRUNE) {
+        const int sh = 2 * (kq & 1);
+#pragma unroll
+        for (int i = 0; i < KEEP; i++) {
+          const uint32_t x = (cur.klc[TT][i] >> sh) & 0x33333333u;
+          const u4 cd = u4{cvt2<0>(x), cvt2<1>(x), cvt2<2>(x), cvt2<3>(x)};
+          acc = mma_f16(cd, u4{qs[4 * i], qs[4 * i + 1], qs[4 * i + 2], qs[4 * i + 3]}, acc);
+          if constexpr (LO1)
+            acc = mma_f16(cd, u4{qsl[4 * i], qsl[4 * i + 1], qsl[4 * i + 2], qsl[4 * i + 3]}, acc);
+        }
+      } else {
+      const u2 w = cur.klo[TT];
 #pragma unroll
       for (int u = 0; u < 2; u++) {
         const uint32_t A = w[u] & 0x33333333u, Bn = (w[u] >> 2) & 0x33333333u;
@@ -485,6 +574,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
           acc = mma_f16(c0, u4{qsl[k0], qsl[k0 + 1], qsl[k0 + 2], qsl[k0 + 3]}, acc);
           acc = mma_f16(c1, u4{qsl[k0 + 4], qsl[k0 + 5], qsl[k0 + 6], qsl[k0 + 7]}, acc);
         }
+      }
       }
       if constexpr (HIMODE == 4) {
         const uint32_t wsel = (kq & 1) ? cur.khi[TT] >> 16 : cur.khi[TT];
@@ -587,11 +677,28 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   }
 
   if constexpr (HASQ) {
+    if constexpr (PRUNE) {
+      // the first prefetched groups hold all four chunks in chunk order:
+      // move the kept ones to slots 0 .. KEEP-1 (slot i reads chunk >= i).
+      // Done here, after the ring blocks, so that waiting for these loads
+      // does not hold up the set-up work above.
+#pragma unroll
+      for (int k = 0; k < PF; k++)
+#pragma unroll
+        for (int TT = 0; TT < 2; TT++)
+#pragma unroll
+          for (int i = 0; i < KEEP; i++) {
+            const uint32_t mm = (cmap >> (2 * i)) & 3u;
+            const uint32_t* a = pf[k].klc[TT];
+            pf[k].klc[TT][i] = mm == 0 ? a[0] : mm == 1 ? a[1] : mm == 2 ? a[2] : a[3];
+          }
+    }
     for (int i = 0; i < nmine; i += PF) {
 #pragma unroll
       for (int k = 0; k < PF; k++) {
         if (i + k < nmine) process_group(pf[k], group_at(i + k));
-        load_group<HIMODE>(c, group_at(i + k + PF), lane, col, kq, kqa, mla, g.nh, pf[k]);
+        load_group<HIMODE, PRUNE, KEEP>(c, group_at(i + k + PF), lane, col, kq, kqa, mla, cmap,
+                                        g.nh, pf[k]);
       }
     }
   }
@@ -736,29 +843,35 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool BF16, int HIMODE, bool LO1, bool PRUNE>
+template <bool BF16, int HIMODE, bool LO1, int KEEP>
 static void launch_one(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
-                       int keep, const Ws& ws, void* out, hipStream_t st) {
+                       const Ws& ws, void* out, hipStream_t st) {
   if (g.NG > 0)
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, LO1, PRUNE>), dim3(g.B * g.Hkv * S),
-                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, keep,
-                       ws, (uint16_t*)out);
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, LO1, KEEP>), dim3(g.B * g.Hkv * S),
+                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, ws,
+                       (uint16_t*)out);
   else
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, LO1, PRUNE>), dim3(g.B * g.Hkv * S),
-                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, keep,
-                       ws, (uint16_t*)out);
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, LO1, KEEP>), dim3(g.B * g.Hkv * S),
+                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, ws,
+                       (uint16_t*)out);
+}
+
+template <bool BF16, int HIMODE, bool LO1>
+static void launch_keep(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
+                        int keep, const Ws& ws, void* out, hipStream_t st) {
+  switch (keep) {
+    case 1: launch_one<BF16, HIMODE, LO1, 1>(g, q, c, scale_log2, S, ws, out, st); break;
+    case 2: launch_one<BF16, HIMODE, LO1, 2>(g, q, c, scale_log2, S, ws, out, st); break;
+    case 3: launch_one<BF16, HIMODE, LO1, 3>(g, q, c, scale_log2, S, ws, out, st); break;
+    default: launch_one<BF16, HIMODE, LO1, 4>(g, q, c, scale_log2, S, ws, out, st); break;
+  }
 }
 
 template <bool BF16, int HIMODE>
 static void launch_lo1(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
                        int keep, const Ws& ws, void* out, hipStream_t st) {
-  if (keep < 4) {
-    if (g.n_lo1 > 0) launch_one<BF16, HIMODE, true, true>(g, q, c, scale_log2, S, keep, ws, out, st);
-    else launch_one<BF16, HIMODE, false, true>(g, q, c, scale_log2, S, keep, ws, out, st);
-  } else {
-    if (g.n_lo1 > 0) launch_one<BF16, HIMODE, true, false>(g, q, c, scale_log2, S, 4, ws, out, st);
-    else launch_one<BF16, HIMODE, false, false>(g, q, c, scale_log2, S, 4, ws, out, st);
-  }
+  if (g.n_lo1 > 0) launch_keep<BF16, HIMODE, true>(g, q, c, scale_log2, S, keep, ws, out, st);
+  else launch_keep<BF16, HIMODE, false>(g, q, c, scale_log2, S, keep, ws, out, st);
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {
