@@ -97,18 +97,36 @@ def unpack_keys(k_lo, k_hi, k_meta, salient: list[int], bits_hi: int):
     return codes, raw, meta[:D].copy(), meta[D:].copy()
 
 
-def unpack_values(v_codes, v_meta):
-    """One group record -> (codes [32 tokens][128], s_bits [32][4],
-    z_bits [32][4])."""
-    codes = np.zeros((GS, D), np.int64)
+def _v_digits(words, base: int, nslot: int, slot: int):
+    """Digits [8 tokens][128] of one 8-token block stored in the v_codes word
+    format: word base + (j * nslot + slot) * 16 + c."""
+    d = np.zeros((8, D), np.int64)
     for j in range(4):
+        for c in range(16):
+            word = int(words[base + (j * nslot + slot) * 16 + c])
+            for i in range(8):
+                d[i, 32 * j + c] = _code(word & 0xFFFF, _pos(i))
+                d[i, 32 * j + 16 + c] = _code(word >> 16, _pos(i))
+    return d
+
+
+def unpack_values(v_codes, v_meta, v_hi=None):
+    """One group record -> (codes [32 tokens][128], s_bits [32][4],
+    z_bits [32][4]).  With a v_hi record (header word 0 = mask of the kept
+    8-token blocks, then their high digits block by block), a kept block's
+    code is low digit + 4 * high digit."""
+    codes = np.zeros((GS, D), np.int64)
+    for kq in range(4):
+        codes[8 * kq:8 * kq + 8] = _v_digits(v_codes, 0, 4, kq)
+    if v_hi is not None and len(v_hi) > 4:
+        nslot = (len(v_hi) - 4) // 64
+        mask = int(v_hi[0])
+        slot = 0
         for kq in range(4):
-            for c in range(16):
-                word = int(v_codes[(j * 4 + kq) * 16 + c])
-                for i in range(8):
-                    t = 8 * kq + i
-                    codes[t, 32 * j + c] = _code(word & 0xFFFF, _pos(i))
-                    codes[t, 32 * j + 16 + c] = _code(word >> 16, _pos(i))
+            if (mask >> kq) & 1:
+                codes[8 * kq:8 * kq + 8] += 4 * _v_digits(v_hi, 4, nslot, slot)
+                slot += 1
+        assert slot == nslot
     meta = np.asarray(v_meta, np.uint16).reshape(2, 4, GS)
     return codes, meta[0].T.copy(), meta[1].T.copy()
 

@@ -368,23 +368,57 @@ int orc_quant_keys(int B, int Hkv, int bf16, const uint16_t *k, int Tstride,
 
 /* Values.  v [B][Hkv][Tstride][128].  codes [B][Hkv][NG][32][128] (token,
  * channel), s/z [B][Hkv][NG][32][4] fp16 bits (token, channel group). */
+/* Two value precisions by token (SemKV, abstract: tokens are ranked by a
+ * model-internal score and given one of two adjacent precisions; the page
+ * names no indicator and finds the indicators interchangeable above the
+ * quality cliff, so this is a reading).  The unit is the 8-token block (a
+ * quarter of a 32-token group).  A block's score is
+ *   E = sum over its 8 tokens and 128 channels of min(floor(4096 |v|), 2^20)
+ * (integer, so order-free); the n_vblk_hi blocks of largest E in each group
+ * (ties to the lower block) are quantized at bits_vhi bits (L = 2^bits_vhi -
+ * 1), the others at bits_v bits.  blkmask[group] gets bit b for a kept
+ * block b (may be NULL when n_vblk_hi == 0). */
+static uint64_t orc_vblock_score(const uint16_t *rows, int bf16) {
+  uint64_t e = 0;
+  for (int t = 0; t < 8; t++)
+    for (int c = 0; c < D; c++) {
+      double u = floor(4096.0 * fabs(to_f64(rows[(size_t)t * D + c], bf16)));
+      e += (uint64_t)(u < 1048576.0 ? u : 1048576.0);
+    }
+  return e;
+}
+
 int orc_quant_values(int B, int Hkv, int bf16, const uint16_t *v, int Tstride,
-                     int T, int R, int bits_v, int NG, uint8_t *codes,
-                     uint16_t *s, uint16_t *z) {
+                     int T, int R, int bits_v, int NG, int n_vblk_hi, int bits_vhi,
+                     uint8_t *codes, uint16_t *s, uint16_t *z, uint8_t *blkmask) {
   int ng = orc_n_quant(T, R) / GS;
-  if (ng > NG) return -1;
+  if (ng > NG || n_vblk_hi < 0 || n_vblk_hi > 4) return -1;
   float x[GS];
   for (int b = 0; b < B; b++)
     for (int kh = 0; kh < Hkv; kh++)
-      for (int g = 0; g < ng; g++)
+      for (int g = 0; g < ng; g++) {
+        const uint16_t *grow = v + (((size_t)b * Hkv + kh) * Tstride + g * GS) * D;
+        uint64_t E[4];
+        for (int k = 0; k < 4; k++) E[k] = orc_vblock_score(grow + (size_t)8 * k * D, bf16);
+        int kept[4];
+        uint8_t mask = 0;
+        for (int k = 0; k < 4; k++) {
+          int rank = 0;
+          for (int i = 0; i < 4; i++) rank += (E[i] > E[k]) || (E[i] == E[k] && i < k);
+          kept[k] = rank < n_vblk_hi;
+          if (kept[k]) mask |= (uint8_t)(1u << k);
+        }
+        if (blkmask) blkmask[(size_t)(b * Hkv + kh) * NG + g] = mask;
         for (int t = 0; t < GS; t++)
           for (int j = 0; j < D / GS; j++) {
             size_t tok = ((size_t)(b * Hkv + kh) * NG + g) * GS + t;
-            const uint16_t *row = v + (((size_t)b * Hkv + kh) * Tstride + g * GS + t) * D;
+            const uint16_t *row = grow + (size_t)t * D;
+            int bits = kept[t / 8] ? bits_vhi : bits_v;
             for (int i = 0; i < GS; i++) x[i] = (float)to_f64(row[j * GS + i], bf16);
-            orc_quant_group(x, (1 << bits_v) - 1, s + tok * 4 + j, z + tok * 4 + j,
+            orc_quant_group(x, (1 << bits) - 1, s + tok * 4 + j, z + tok * 4 + j,
                             codes + tok * D + j * GS);
           }
+      }
   return 0;
 }
 
@@ -527,9 +561,15 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
 
 /* Packs the logical value codes: v_codes [..][NG][256] u32,
  * v_meta [..][NG][2][4][32] u16. */
+/* v_codes holds the low two bits of every value code.  With n_vblk_hi > 0,
+ * v_hi holds per group 4 + 64 n_vblk_hi words: word 0 the kept-block mask,
+ * words 1..3 zero, then for the s-th kept block (ascending) and channel
+ * group j the words 4 + (j n_vblk_hi + s) 16 + c, in the v_codes word format,
+ * of the codes' high two bits (NULL when n_vblk_hi == 0). */
 int orc_pack_values(int B, int Hkv, int T, int R, int NG, const uint8_t *codes,
-                    const uint16_t *s, const uint16_t *z, uint32_t *v_codes,
-                    uint16_t *v_meta) {
+                    const uint16_t *s, const uint16_t *z, int n_vblk_hi,
+                    const uint8_t *blkmask, uint32_t *v_codes, uint16_t *v_meta,
+                    uint32_t *v_hi) {
   int ng = orc_n_quant(T, R) / GS;
   for (int b = 0; b < B; b++)
     for (int kh = 0; kh < Hkv; kh++)
@@ -544,11 +584,33 @@ int orc_pack_values(int B, int Hkv, int T, int R, int NG, const uint8_t *codes,
               uint32_t w = 0;
               for (int i = 0; i < 8; i++) {
                 int t = 8 * kq + i;
-                w |= (uint32_t)cg[t * D + 32 * j + c] << (2 * pos_swap(i));
-                w |= (uint32_t)cg[t * D + 32 * j + 16 + c] << (16 + 2 * pos_swap(i));
+                w |= (uint32_t)(cg[t * D + 32 * j + c] & 3) << (2 * pos_swap(i));
+                w |= (uint32_t)(cg[t * D + 32 * j + 16 + c] & 3) << (16 + 2 * pos_swap(i));
               }
               vc[(j * 4 + kq) * 16 + c] = w;
             }
+        if (n_vblk_hi > 0) {
+          size_t rw = 4 + 64 * (size_t)n_vblk_hi;
+          uint32_t *vh = v_hi + grp * rw;
+          memset(vh, 0, rw * 4);
+          uint8_t mask = blkmask[grp];
+          vh[0] = mask;
+          int slot = 0;
+          for (int kq = 0; kq < 4; kq++) {
+            if (!((mask >> kq) & 1)) continue;
+            for (int j = 0; j < 4; j++)
+              for (int c = 0; c < 16; c++) {
+                uint32_t w = 0;
+                for (int i = 0; i < 8; i++) {
+                  int t = 8 * kq + i;
+                  w |= (uint32_t)(cg[t * D + 32 * j + c] >> 2) << (2 * pos_swap(i));
+                  w |= (uint32_t)(cg[t * D + 32 * j + 16 + c] >> 2) << (16 + 2 * pos_swap(i));
+                }
+                vh[4 + (j * n_vblk_hi + slot) * 16 + c] = w;
+              }
+            slot++;
+          }
+        }
         uint16_t *meta = v_meta + grp * 256;
         for (int j = 0; j < 4; j++)
           for (int t = 0; t < GS; t++) {
