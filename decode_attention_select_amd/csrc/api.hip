@@ -23,6 +23,8 @@ kvq_status check_layout(const kvq_layout* L) {
   if (L->residual < GS || L->residual % GS) return KVQ_EINVAL;
   if (L->max_tokens < 1 || L->max_tokens > (1 << 20)) return KVQ_EINVAL;
   if (L->io_dtype != KVQ_FP16 && L->io_dtype != KVQ_BF16) return KVQ_EINVAL;
+  if (L->n_vblk_hi < 0 || L->n_vblk_hi > 4) return KVQ_EINVAL;
+  if (L->n_vblk_hi > 0 && L->bits_vhi != 3 && L->bits_vhi != 4) return KVQ_ENOTSUP;
   return KVQ_OK;
 }
 
@@ -42,6 +44,9 @@ Geo make_geo(const kvq_layout* L) {
   g.bf16 = L->io_dtype == KVQ_BF16;
   g.max_tokens = L->max_tokens;
   g.khi_bytes = g.n_hi == 0 ? 0 : (g.bits_hi == 4 ? 32 * 4 : GS * g.nh * 2);
+  g.n_vhi = L->n_vblk_hi;
+  g.bits_vhi = g.n_vhi ? L->bits_vhi : 2;
+  g.vhi_words = g.n_vhi ? 4 + 64 * g.n_vhi : 0;
   return g;
 }
 
@@ -63,6 +68,8 @@ kvq_status check_cache(const Geo& g, const kvq_cache* c, bool need_groups) {
       if (kvq_status s = check_ptr(p)) return s;
     if (g.khi_bytes)
       if (kvq_status s = check_ptr(c->k_hi)) return s;
+    if (g.vhi_words)
+      if (kvq_status s = check_ptr(c->v_hi)) return s;
   }
   return KVQ_OK;
 }
@@ -93,6 +100,7 @@ kvq_status kvq_cache_sizes(const kvq_layout* L, size_t sizes[KVQ_NBUF]) {
   sizes[8] = bh * 4;                 // len
   sizes[9] = bh * 2 * NPAIR * 8;     // sums
   sizes[10] = 4;                     // err
+  sizes[11] = grp * g.vhi_words * 4; // v_hi
   return KVQ_OK;
 }
 
@@ -181,6 +189,7 @@ static kvq_status decode_common(const kvq_layout* L, const void* q, const kvq_ca
   if (ws_bytes < need) return KVQ_ECAPACITY;
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_EINVAL;
   if (keep < 1 || keep > 4) return KVQ_EINVAL;
+  if (keep < 4 && g.n_vhi > 0) return KVQ_ENOTSUP;  // pruning with two value precisions
   if (kvq_status s = check_ptr(q)) return s;
   if (kvq_status s = check_ptr(out)) return s;
   if (kvq_status s = check_ptr(workspace)) return s;

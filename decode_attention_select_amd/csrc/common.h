@@ -27,6 +27,8 @@ struct Geo {
   int bf16;            // io dtype is bfloat16
   int max_tokens;
   int khi_bytes;       // bytes of the salient section per group
+  int n_vhi, bits_vhi; // value blocks at the higher precision, their bits
+  int vhi_words;       // u32 words of a group's v_hi record (0 when n_vhi == 0)
 };
 
 // Quantized tokens for T held tokens: 32 * floor(max(0, T - R) / 32).

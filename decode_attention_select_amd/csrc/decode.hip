@@ -79,6 +79,12 @@ __device__ inline uint32_t cvt2(uint32_t w) {
   return h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, BYTE));
 }
 
+// ... and with the digit times 4 (scale 8): high value digits
+template <int BYTE>
+__device__ inline uint32_t cvt2x4(uint32_t w) {
+  return h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 8.0f, BYTE));
+}
+
 __device__ inline f4 mma_f16(u4 a, u4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a),
                                                 __builtin_bit_cast(h8, b), c, 0, 0, 0);
@@ -130,6 +136,8 @@ struct Pref {
   u4 hraw[2];       // raw salient keys (HIMODE 16): 8 values of the lane's token, tile 0 and 1
   uint32_t vc[4];   // v_codes word of channel group j = 0..3
   u4 meta;          // 16 B of the group's k_meta (lanes 0-31) or v_meta (lanes 32-63)
+  uint32_t vh[4][2];  // two value precisions: high-digit words of block kq's two candidate slots
+  uint32_t vmask;     // two value precisions: the group's kept-block mask
 };
 
 // kqa: the key chunk whose low digits this lane reads (its own, kq, unless
@@ -140,9 +148,24 @@ struct Pref {
 // CHUNKED (pruned decode): slot i (< NCH) holds, for key chunk
 // (cmap >> 2i) & 3, the lane token's k_lo word kq/2 of that chunk.  Pruned
 // chunks are never named in cmap, so they are never fetched.
-template <int HIMODE, bool CHUNKED, int NCH>
+// VHI (two value precisions, g.n_vhi kept blocks per group): block kq's
+// compact slot is the number of kept blocks below it, so it lies in
+// [max(0, kq - (4 - n)), min(kq, n - 1)], at most two values; both words are
+// read with the rest of the group (no wait on the mask) and the right one is
+// picked when the group is processed.
+template <int HIMODE, bool CHUNKED, int NCH, bool VHI>
 __device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int col, int kq,
-                                  int kqa, int mla, uint32_t cmap, int nh, Pref& p) {
+                                  int kqa, int mla, uint32_t cmap, int nh, int nvhi, Pref& p) {
+  if constexpr (VHI) {
+    const uint32_t* vh = c.v_hi + rec * (4 + 64 * nvhi);
+    p.vmask = vh[0];
+    const int s0 = max(0, kq - (4 - nvhi)), s1 = min(kq, nvhi - 1);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      p.vh[j][0] = vh[4 + (j * nvhi + s0) * 16 + col];
+      p.vh[j][1] = vh[4 + (j * nvhi + s1) * 16 + col];
+    }
+  }
   if constexpr (CHUNKED) {
     const uint32_t* w = (const uint32_t*)c.k_lo + rec * GROUP_WORDS;
 #pragma unroll
@@ -246,7 +269,9 @@ struct Lds {
 // scale/zero are not read (past the first PF prefetched groups, which are
 // issued before the query arrives): their lanes load a kept chunk's words
 // instead, which the same instruction fetches anyway.
-template <bool BF16, int HIMODE, bool HASQ, bool LO1, int KEEP>
+// VHI: the cache has two value precisions (g.n_vhi > 0): kept 8-token blocks
+// add their high value digits (4 * digit) through one more MFMA per tile.
+template <bool BF16, int HIMODE, bool HASQ, bool LO1, int KEEP, bool VHI>
 __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             kvq_cache c, float scale_log2, int S,
                                                             Ws ws, uint16_t* __restrict__ out) {
@@ -304,8 +329,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   if constexpr (HASQ) {
 #pragma unroll
     for (int k = 0; k < PF; k++)
-      load_group<HIMODE, PRUNE, 4>(c, group_at(k), lane, col, kq, kq, lane & 31, 0xE4u, g.nh,
-                                   pf[k]);
+      load_group<HIMODE, PRUNE, 4, VHI>(c, group_at(k), lane, col, kq, kq, lane & 31, 0xE4u,
+                                        g.nh, g.n_vhi, pf[k]);
   }
 
   // kept key chunks (all four unless PRUNE); every lane computes the same mask
@@ -472,6 +497,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   };
 
   uint32_t* sm = lds.u.loop.stage[wave];
+  const int vs0 = max(0, kq - (4 - g.n_vhi));  // VHI: the first candidate slot of block kq
   auto process_group = [&](const Pref& cur, size_t rec) {
     // stage the metadata record: [0,64) k scale pairs, [64,128) k zero
     // pairs, [128,192) v scale pairs (j-major), [192,256) v zero pairs.
@@ -600,6 +626,12 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     softmax_step(cr, scale_log2, p);
     const u4 P = u4{pk_rne(p[0], p[1]), pk_rne(p[2], p[3]), pk_rne(p[4], p[5]), pk_rne(p[6], p[7])};
     // values
+    bool vkept = false;
+    int vslot = 0;
+    if constexpr (VHI) {
+      vkept = (cur.vmask >> kq) & 1u;
+      vslot = __popc(cur.vmask & ((1u << kq) - 1u));
+    }
     const u4 za = col < 4 ? ((const u4*)(sm + 192 + 16 * col))[kq]
                           : (col == 4 ? u4{ONES, ONES, ONES, ONES} : u4{0, 0, 0, 0});
     Cvb = mma_f16(za, P, Cvb);
@@ -612,6 +644,15 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       const uint32_t A = wv & 0x33333333u, Bn = (wv >> 2) & 0x33333333u;
       O[2 * j] = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)}, pj, O[2 * j]);
       O[2 * j + 1] = mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)}, pj, O[2 * j + 1]);
+      if constexpr (VHI) {
+        // block kq's high digits (0 unless kept), weighted 4 by the convert
+        const uint32_t wh = vkept ? (vslot == vs0 ? cur.vh[j][0] : cur.vh[j][1]) : 0u;
+        const uint32_t Ah = wh & 0x33333333u, Bh = (wh >> 2) & 0x33333333u;
+        O[2 * j] = mma_f16(u4{cvt2x4<0>(Ah), cvt2x4<0>(Bh), cvt2x4<1>(Ah), cvt2x4<1>(Bh)}, pj,
+                           O[2 * j]);
+        O[2 * j + 1] = mma_f16(u4{cvt2x4<2>(Ah), cvt2x4<2>(Bh), cvt2x4<3>(Ah), cvt2x4<3>(Bh)}, pj,
+                               O[2 * j + 1]);
+      }
     }
   };
 
@@ -697,8 +738,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
       for (int k = 0; k < PF; k++) {
         if (i + k < nmine) process_group(pf[k], group_at(i + k));
-        load_group<HIMODE, PRUNE, KEEP>(c, group_at(i + k + PF), lane, col, kq, kqa, mla, cmap,
-                                        g.nh, pf[k]);
+        load_group<HIMODE, PRUNE, KEEP, VHI>(c, group_at(i + k + PF), lane, col, kq, kqa, mla,
+                                             cmap, g.nh, g.n_vhi, pf[k]);
       }
     }
   }
@@ -843,22 +884,26 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool BF16, int HIMODE, bool LO1, int KEEP>
+template <bool BF16, int HIMODE, bool LO1, int KEEP, bool VHI = false>
 static void launch_one(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
                        const Ws& ws, void* out, hipStream_t st) {
   if (g.NG > 0)
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, LO1, KEEP>), dim3(g.B * g.Hkv * S),
-                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, ws,
-                       (uint16_t*)out);
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, LO1, KEEP, VHI>),
+                       dim3(g.B * g.Hkv * S), dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c,
+                       scale_log2, S, ws, (uint16_t*)out);
   else
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, LO1, KEEP>), dim3(g.B * g.Hkv * S),
-                       dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c, scale_log2, S, ws,
-                       (uint16_t*)out);
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, LO1, KEEP, false>),
+                       dim3(g.B * g.Hkv * S), dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c,
+                       scale_log2, S, ws, (uint16_t*)out);
 }
 
 template <bool BF16, int HIMODE, bool LO1>
 static void launch_keep(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
                         int keep, const Ws& ws, void* out, hipStream_t st) {
+  if (g.n_vhi > 0) {  // two value precisions: unpruned only (checked by the caller)
+    launch_one<BF16, HIMODE, LO1, 4, true>(g, q, c, scale_log2, S, ws, out, st);
+    return;
+  }
   switch (keep) {
     case 1: launch_one<BF16, HIMODE, LO1, 1>(g, q, c, scale_log2, S, ws, out, st); break;
     case 2: launch_one<BF16, HIMODE, LO1, 2>(g, q, c, scale_log2, S, ws, out, st); break;

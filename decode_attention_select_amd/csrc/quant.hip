@@ -296,9 +296,19 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
 
 // CHMAJOR false: src = token 0 of the group, row stride D (prefill input).
 // CHMAJOR true:  src = a ring_v slot block [128][32] (channel, slot).
-template <bool BF, bool CHMAJOR>
+// VHI (g.n_vhi > 0: two value precisions, the SemKV reading documented in
+// include/kvq.h at v_hi): lane (cb, tq) holds 8-token block tq, whose score
+// is summed over the lane's 64 values and the 16 lanes of its DPP row; the
+// n_vhi best blocks quantize at L = 2^bits_vhi - 1, and the high digits of
+// their codes go to vhi_out (the group's v_hi record).
+template <int CTRL>
+__device__ inline uint32_t dpp_row(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+template <bool BF, bool CHMAJOR, bool VHI>
 __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint32_t* vc_out,
-                                 uint16_t* meta_out) {
+                                 uint16_t* meta_out, uint32_t* vhi_out) {
   const int lane = threadIdx.x & 63, cb = lane & 15, tq = lane >> 4, m = cb & 3, j = cb >> 2;
   // x(i, k): token 8tq + i, channel 8cb + k
   uint4 v[8];
@@ -338,11 +348,37 @@ __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint32_t* vc
       if (mn[i] == 0.0f) mn[i] = __uint_as_float(sgn);
     }
   }
+  // block scores and the kept-block mask (uniform)
+  uint32_t kept = 0;
+  if constexpr (VHI) {
+    uint32_t e = 0;  // at most 64 * 2^20 per lane, 2^30 per row
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int k = 0; k < 8; k++)
+        e += (uint32_t)fminf(4096.0f * fabsf(x(i, k)), 1048576.0f);
+    e += dpp_row<0x128>(e);  // row_ror:8
+    e += dpp_row<0x124>(e);  // row_ror:4
+    e += dpp_row<0x122>(e);  // row_ror:2
+    e += dpp_row<0x121>(e);  // row_ror:1
+    uint32_t E[4];
+#pragma unroll
+    for (int b = 0; b < 4; b++) E[b] = __builtin_amdgcn_readlane(e, 16 * b);
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      int rank = 0;
+#pragma unroll
+      for (int a = 0; a < 4; a++) rank += (E[a] > E[b]) || (E[a] == E[b] && a < b);
+      if (rank < g.n_vhi) kept |= 1u << b;
+    }
+  }
+  const bool hiblk = (kept >> tq) & 1u;
+  const float Lv = hiblk ? (float)((1 << g.bits_vhi) - 1) : 3.0f;
   auto pick = [&](const float (&a)[8], int o) {
     return m == 0 ? a[o] : m == 1 ? a[2 + o] : m == 2 ? a[4 + o] : a[6 + o];
   };
-  const QParam p0 = qparam(pick(mn, 0), pick(mx, 0), 3.0f, false);
-  const QParam p1 = qparam(pick(mn, 1), pick(mx, 1), 3.0f, false);
+  const QParam p0 = qparam(pick(mn, 0), pick(mx, 0), Lv, false);
+  const QParam p1 = qparam(pick(mn, 1), pick(mx, 1), Lv, false);
   uint32_t sz[8];
   float rr[8];
 #define KVQ_BCAST(K)                                                              \
@@ -353,35 +389,60 @@ __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint32_t* vc
   KVQ_BCAST(0) KVQ_BCAST(1) KVQ_BCAST(2) KVQ_BCAST(3)
 #undef KVQ_BCAST
   // half-word of channel k: its 8 tokens' codes at positions pi(i), summed
-  // as exact float integers (code * 4^position, below 2^16)
-  float hf[8];
-  uint32_t h[8];
+  // as exact float integers (digit * 4^position, below 2^16); codes above 3
+  // (kept blocks) split into a low digit here and a high digit in hh
+  float hf[8], hhf[8];
+  uint32_t h[8], hh[8];
 #pragma unroll
-  for (int k = 0; k < 8; k++) hf[k] = 0.0f;
+  for (int k = 0; k < 8; k++) hf[k] = hhf[k] = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const float z = half_bits_to_f32((uint16_t)(sz[i] >> 16));
     const float mul = (float)(1u << (2 * pos_swap(i)));
 #pragma unroll
-    for (int k = 0; k < 8; k++) hf[k] = fmaf(qcode(x(i, k), z, rr[i], 3.0f), mul, hf[k]);
+    for (int k = 0; k < 8; k++) {
+      const float q = qcode(x(i, k), z, rr[i], Lv);
+      if constexpr (VHI) {
+        const float hd = floorf(q * 0.25f);
+        hf[k] = fmaf(fmaf(hd, -4.0f, q), mul, hf[k]);
+        hhf[k] = fmaf(hd, mul, hhf[k]);
+      } else {
+        hf[k] = fmaf(q, mul, hf[k]);
+      }
+    }
   }
 #pragma unroll
-  for (int k = 0; k < 8; k++) h[k] = (uint32_t)hf[k];
+  for (int k = 0; k < 8; k++) {
+    h[k] = (uint32_t)hf[k];
+    hh[k] = (uint32_t)hhf[k];
+  }
   // Word (j*4 + tq)*16 + c holds channel 32j + c (bits 0..15) and 32j+16+c
   // (bits 16..31).  Lane m holds channels 32j + 8m + k: m = 0, 1 are low
   // halves, m = 2, 3 the high halves of the same words (quad partner m ^ 2).
   // The low lane keeps words k = 0..3 of its eight, the high lane k = 4..7.
   const bool low = m < 2;
-  const uint32_t s0 = low ? (h[4] | (h[5] << 16)) : (h[0] | (h[1] << 16));
-  const uint32_t s1 = low ? (h[6] | (h[7] << 16)) : (h[2] | (h[3] << 16));
-  const uint32_t r0 = dpp<QUAD_XOR2>(s0), r1 = dpp<QUAD_XOR2>(s1);
-  const uint32_t o[4] = {r0 & 0xFFFFu, r0 >> 16, r1 & 0xFFFFu, r1 >> 16};
-  uint32_t wd[4];
+  auto words = [&](const uint32_t (&hv)[8], uint32_t (&wd)[4]) {
+    const uint32_t s0 = low ? (hv[4] | (hv[5] << 16)) : (hv[0] | (hv[1] << 16));
+    const uint32_t s1 = low ? (hv[6] | (hv[7] << 16)) : (hv[2] | (hv[3] << 16));
+    const uint32_t r0 = dpp<QUAD_XOR2>(s0), r1 = dpp<QUAD_XOR2>(s1);
+    const uint32_t o[4] = {r0 & 0xFFFFu, r0 >> 16, r1 & 0xFFFFu, r1 >> 16};
 #pragma unroll
-  for (int q = 0; q < 4; q++)
-    wd[q] = low ? (h[q] | (o[q] << 16)) : (o[q] | (h[4 + q] << 16));
+    for (int q = 0; q < 4; q++)
+      wd[q] = low ? (hv[q] | (o[q] << 16)) : (o[q] | (hv[4 + q] << 16));
+  };
+  uint32_t wd[4];
+  words(h, wd);
   const int c0 = 8 * (m & 1) + 4 * (m >> 1);
   *(uint4*)(vc_out + (j * 4 + tq) * 16 + c0) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  if constexpr (VHI) {
+    uint32_t wh[4];
+    words(hh, wh);
+    if (lane == 0) *(uint4*)vhi_out = make_uint4(kept, 0, 0, 0);
+    if (hiblk) {
+      const int slot = __popc(kept & ((1u << tq) - 1));
+      *(uint4*)(vhi_out + 4 + (j * g.n_vhi + slot) * 16 + c0) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    }
+  }
   if (m < 2) {
     uint32_t mm[4];
 #pragma unroll
@@ -434,7 +495,7 @@ __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint1
                  (uint16_t*)c.k_meta + rec * 2 * D, lds[wave]);
 }
 
-template <bool BF>
+template <bool BF, bool VHI>
 __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uint16_t* __restrict__ v,
                                                                 int T, int qblocks, kvq_cache c) {
   if ((int)blockIdx.y >= qblocks) {
@@ -445,9 +506,9 @@ __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uin
   const int grp = blockIdx.y * QWAVES + wave;
   if (grp >= n_quant(T, g.R) / GS) return;
   const size_t rec = (size_t)bh * g.NG + grp;
-  value_group_wave<BF, false>(g, v + ((size_t)bh * T + (size_t)grp * GS) * D,
+  value_group_wave<BF, false, VHI>(g, v + ((size_t)bh * T + (size_t)grp * GS) * D,
                           (uint32_t*)c.v_codes + rec * GROUP_WORDS,
-                          (uint16_t*)c.v_meta + rec * 2 * D);
+                          (uint16_t*)c.v_meta + rec * 2 * D, c.v_hi + rec * g.vhi_words);
 }
 
 // ------------------------------------------------------------------- append
@@ -455,7 +516,7 @@ __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uin
 // One 128-thread workgroup per (b, kv head): the new token goes to ring slot
 // T mod RS; when n_q grows, wave 0 packs the oldest ring group's keys and
 // wave 1 its values (the new token is not in that group).
-template <bool BF>
+template <bool BF, bool VHI>
 __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new,
                                                      kvq_cache c) {
@@ -481,9 +542,9 @@ __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __re
                      (uint32_t*)c.k_lo + rec * GROUP_WORDS, (uint8_t*)c.k_hi + rec * g.khi_bytes,
                      (uint16_t*)c.k_meta + rec * 2 * D, lds);
     else
-      value_group_wave<BF, true>(g, rv + (size_t)(s0 / GS) * D * GS,
-                             (uint32_t*)c.v_codes + rec * GROUP_WORDS,
-                             (uint16_t*)c.v_meta + rec * 2 * D);
+      value_group_wave<BF, true, VHI>(g, rv + (size_t)(s0 / GS) * D * GS,
+                                 (uint32_t*)c.v_codes + rec * GROUP_WORDS,
+                                 (uint16_t*)c.v_meta + rec * 2 * D, c.v_hi + rec * g.vhi_words);
   }
   __syncthreads();
   if (tid == 0) c.len[bh] = T + 1;
@@ -508,12 +569,11 @@ hipError_t launch_quant_keys(const Geo& g, const void* k, int T, kvq_cache* c, h
 hipError_t launch_quant_values(const Geo& g, const void* v, int T, kvq_cache* c, hipStream_t st) {
   const int qb = (n_quant(T, g.R) / GS + QWAVES - 1) / QWAVES;
   const dim3 grid(g.B * g.Hkv, qb + ring_blocks(g, T));
-  if (g.bf16)
-    hipLaunchKernelGGL(quant_values_kernel<true>, grid, dim3(QTHREADS), 0, st, g,
-                       (const uint16_t*)v, T, qb, *c);
-  else
-    hipLaunchKernelGGL(quant_values_kernel<false>, grid, dim3(QTHREADS), 0, st, g,
-                       (const uint16_t*)v, T, qb, *c);
+  const auto kern = g.bf16 ? (g.n_vhi ? quant_values_kernel<true, true>
+                                       : quant_values_kernel<true, false>)
+                           : (g.n_vhi ? quant_values_kernel<false, true>
+                                       : quant_values_kernel<false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(QTHREADS), 0, st, g, (const uint16_t*)v, T, qb, *c);
   return hipGetLastError();
 }
 
@@ -587,12 +647,10 @@ hipError_t launch_shrink(const Geo& g, kvq_cache* c, int g0, int g1, hipStream_t
 
 hipError_t launch_append(const Geo& g, const void* k_new, const void* v_new, kvq_cache* c,
                          hipStream_t st) {
-  if (g.bf16)
-    hipLaunchKernelGGL(append_kernel<true>, dim3(g.B * g.Hkv), dim3(128), 0, st, g,
-                       (const uint16_t*)k_new, (const uint16_t*)v_new, *c);
-  else
-    hipLaunchKernelGGL(append_kernel<false>, dim3(g.B * g.Hkv), dim3(128), 0, st, g,
-                       (const uint16_t*)k_new, (const uint16_t*)v_new, *c);
+  const auto kern = g.bf16 ? (g.n_vhi ? append_kernel<true, true> : append_kernel<true, false>)
+                           : (g.n_vhi ? append_kernel<false, true> : append_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3(g.B * g.Hkv), dim3(128), 0, st, g, (const uint16_t*)k_new,
+                     (const uint16_t*)v_new, *c);
   return hipGetLastError();
 }
 

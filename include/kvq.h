@@ -79,6 +79,10 @@ typedef struct {
                           32 <= R */
   int32_t max_tokens;  /* capacity per sequence, 1 <= max_tokens <= 2^20 */
   int32_t io_dtype;    /* KVQ_FP16 | KVQ_BF16 */
+  int32_t n_vblk_hi;   /* 0..4: 8-token blocks per 32-token group whose values
+                          take bits_vhi bits ([SemKV] abstract: two
+                          precisions chosen per token; see v_hi) */
+  int32_t bits_vhi;    /* 3 or 4 when n_vblk_hi > 0 (ignored otherwise) */
 } kvq_layout;
 
 /* Device buffers of one cache, all caller-allocated with the sizes returned
@@ -123,6 +127,21 @@ typedef struct {
  *          [0] query side, [1] key side (see kvq_select_pairs).
  *  err     [1] int32: sticky error word, 0 = none; bit 0 = an append found
  *          the cache full.
+ *  v_hi    n_vblk_hi > 0: [B][Hkv][NG][4 + 64 n_vblk_hi] u32.  Value
+ *          precision by token ([SemKV] abstract: tokens ranked by a
+ *          model-internal score get one of two adjacent precisions; the page
+ *          names no indicator, so this is a reading): a group's four 8-token
+ *          blocks (tokens 8m .. 8m+7) are ranked by
+ *            E_m = sum over the block's 8 tokens and 128 channels of
+ *                  min(floor(4096 |v|), 2^20)
+ *          (ties to the lower block); the n_vblk_hi blocks of largest E_m
+ *          quantize their values at L = 2^bits_vhi - 1 levels, the others at
+ *          L = 3.  v_codes always holds the low two bits of a value code.
+ *          Word 0 of a group record is the mask of the kept blocks (bit m),
+ *          words 1..3 are 0, and words 4 + (j n_vblk_hi + s) 16 + c hold,
+ *          in the v_codes word format, the high two bits of the codes of the
+ *          s-th kept block (ascending) for channel group j.  Zero bytes when
+ *          n_vblk_hi == 0.
  */
 typedef struct {
   void *k_lo, *k_hi, *k_meta, *v_codes, *v_meta, *ring_k, *ring_v;
@@ -130,9 +149,10 @@ typedef struct {
   int32_t *len;
   uint64_t *sums;
   int32_t *err;
+  uint32_t *v_hi;
 } kvq_cache;
 
-#define KVQ_NBUF 11
+#define KVQ_NBUF 12
 
 /* Bytes of each cache buffer, in kvq_cache field order (host only, no GPU).
  * Returns KVQ_EINVAL / KVQ_ENOTSUP for a layout the library rejects. */

@@ -52,6 +52,8 @@ class Workload:
     residual: int = 128
     n_splits: int = 0        # 0 = library default
     seed: int = 0
+    n_vblk_hi: int = 0       # 8-token value blocks per group at bits_vhi bits
+    bits_vhi: int = 4
 
     @property
     def group_size(self) -> int:

@@ -36,7 +36,8 @@ class Case:
                                       n_pairs_hi=w.n_pairs_hi, bits_hi=w.bits_hi,
                                       n_pairs_lo1=w.n_pairs_lo1,
                                       residual=w.residual, max_tokens=self.max_tokens,
-                                      io_dtype=w.io_dtype)
+                                      io_dtype=w.io_dtype, n_vblk_hi=w.n_vblk_hi,
+                                      bits_vhi=w.bits_vhi)
         self.cache = kvq.Cache(self.layout)
         self.NG = max(self.max_tokens - w.residual, 0) // 32
         # selection always looks at the workload's prefill (once, at prefill)
@@ -61,7 +62,8 @@ class Case:
         return oracle.quantize(self.d["k"], self.d["v"], self.T if T is None else T, pairs,
                                residual=self.w.residual, n_pairs_hi=self.w.n_pairs_hi,
                                bits_hi=self.w.bits_hi, io_dtype=self.w.io_dtype,
-                               ng=max(self.NG, 1), n_pairs_lo1=self.w.n_pairs_lo1)
+                               ng=max(self.NG, 1), n_pairs_lo1=self.w.n_pairs_lo1,
+                               n_vblk_hi=self.w.n_vblk_hi, bits_vhi=self.w.bits_vhi)
 
     # -------------------------------------------------------------- GPU side
     def gpu_bytes(self) -> dict:
@@ -82,6 +84,9 @@ class Case:
             "len": host(c["len"], np.int32).reshape(B, H),
             "sums": host(c["sums"], np.uint64).reshape(B, H, 2, 64),
         }
+        vw = 4 + 64 * self.w.n_vblk_hi if self.w.n_vblk_hi else 0
+        out["v_hi"] = (host(c["v_hi"], np.uint32)[:B * H * NG * vw].reshape(B, H, NG, vw)
+                       if vw and NG else np.zeros((B, H, NG, 0), np.uint32))
         return out
 
     def decode_pruned(self, q_bits: np.ndarray, n_splits: int, n_keep: int):
@@ -167,6 +172,9 @@ def compare_cache(case: Case, qz, ng: int):
     if o["k_hi"].shape[-1]:
         a, b = g["k_hi"][:, :, :ng], o["k_hi"][:, :, :ng]
         assert np.array_equal(a, b), "k_hi differs at %s" % np.argwhere(a != b)[:5]
+    if case.w.n_vblk_hi:
+        a, b = g["v_hi"][:, :, :ng], o["v_hi"][:, :, :ng]
+        assert np.array_equal(a, b), "v_hi differs at %s" % np.argwhere(a != b)[:5]
     slots = oracle.live_ring_slots(qz.T, qz.R)
     assert np.array_equal(g["ring_k"][:, :, slots], o["ring_k"][:, :, slots])
     rv_g = g["ring_v"].reshape(*g["ring_v"].shape[:2], -1, 128, 32)

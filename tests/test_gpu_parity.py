@@ -261,3 +261,60 @@ def test_pruned_decode_edge_lengths(T):
     for n_keep in (1, 3):
         ref = oracle.attention_pruned(qz, q, SM_SCALE, n_keep)
         check_output(case.decode_pruned(q, 3, n_keep), ref, w.io_dtype, ATOL)
+
+
+VMIX = [
+    kvq_synth.Workload("vmix-1x4", 2, 8, 2, 700, n_qry=8, io_dtype="bf16", outliers="pct2x10",
+                       n_pairs_hi=6, residual=64, seed=81, n_vblk_hi=1, bits_vhi=4),
+    kvq_synth.Workload("vmix-2x3-fp16", 1, 4, 1, 420, n_qry=8, io_dtype="fp16",
+                       n_pairs_hi=8, residual=32, seed=82, n_vblk_hi=2, bits_vhi=3),
+    kvq_synth.Workload("vmix-3x4-raw16", 1, 8, 2, 333, n_qry=8, io_dtype="bf16",
+                       n_pairs_hi=6, bits_hi=16, residual=32, seed=83, n_vblk_hi=3, bits_vhi=4),
+    kvq_synth.Workload("vmix-4x4-lo1", 1, 8, 2, 300, n_qry=8, io_dtype="bf16",
+                       n_pairs_hi=0, n_pairs_lo1=32, residual=64, seed=84, n_vblk_hi=4,
+                       bits_vhi=4),
+]
+
+
+@pytest.mark.parametrize("w", VMIX, ids=_ids)
+def test_two_value_precisions_bit_exact_and_decode(w):
+    # SemKV reading: kept 8-token blocks at 3 or 4 bits; bytes (with the
+    # high-digit records) equal the oracle's, decoding matches its attention
+    case = Case(w)
+    qz = case.oracle_quant()
+    compare_cache(case, qz, qz.nq // 32)
+    q = case.d["q_dec"][:, :, 0]
+    ref = oracle.attention(qz, q, SM_SCALE)
+    for S in (1, 9):
+        got, part = case.decode(q, S, partials=True)
+        err = check_output(got, ref, w.io_dtype, ATOL)
+        if S == 1:
+            check_single_split(part, ref, ATOL)
+        print("%s S=%d max|err| %.3g" % (w.name, S, err))
+
+
+def test_two_value_precisions_append_equals_prefill():
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    w = VMIX[0]
+    T0 = 100
+    case = Case(w, T=T0, max_tokens=w.tokens)
+    for t in range(T0, w.tokens):
+        kvq.kvq_append(case.layout, dev(np.ascontiguousarray(case.d["k"][:, :, t])),
+                       dev(np.ascontiguousarray(case.d["v"][:, :, t])), case.cache.struct)
+    torch.cuda.synchronize()
+    case.T = w.tokens
+    qz = case.oracle_quant()
+    compare_cache(case, qz, qz.nq // 32)
+
+
+def test_two_value_precisions_reject_pruning():
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    case = Case(VMIX[0])
+    ws = torch.zeros(kvq.kvq_workspace_bytes(case.layout, 4), dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, 8, 128), dtype=torch.int16, device="cuda")
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_attn_pruned(case.layout, dev(case.d["q_dec"][:, :, 0]), case.cache.struct,
+                                   SM_SCALE, 4, 2, ws, out)
+    assert e.value.status == -2
