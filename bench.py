@@ -57,6 +57,8 @@ def algorithmic_bytes(w, T: int, n_keep: int = 4) -> int:
         k_code_bits = n_hi_ch * w.bits_hi + n_two_ch * 2 + n_one_ch
         k_meta = 128 * 4 / 32
     per_tok = k_code_bits / 8 + k_meta + 32 + 16
+    if w.n_vblk_hi:  # the kept value blocks' extra bits and a 4-bit block mask per group
+        per_tok += w.n_vblk_hi / 4 * (w.bits_vhi - 2) * 128 / 8 + 0.5 / 32
     return int(round(bh * (nq * per_tok + nr * 512) + qo))
 
 
@@ -68,7 +70,8 @@ def layout_bytes(cache, w, T: int) -> int:
     ng = nq // 32
     bh = w.batch * w.n_kv_heads
     khi = cache.sizes[1] // max(1, bh * cache_ng(cache, w))
-    per_grp = 1024 + khi + 512 + 1024 + 512
+    vhi = cache.sizes[11] // max(1, bh * cache_ng(cache, w))
+    per_grp = 1024 + khi + 512 + 1024 + 512 + vhi
     return bh * (ng * per_grp + nr * 512) + 2 * w.batch * w.n_q_heads * 128 * 2
 
 
@@ -244,7 +247,8 @@ def streaming_leg(args, w):
 
 def pareto_leg(args, w):
     """Bit-allocation sweep on one workload: for every point of
-    kvq_synth.PARETO_POINTS, the decode time and effective GB/s (cache
+    kvq_synth.PARETO_POINTS (key bits) and kvq_synth.VALUE_POINTS (two value
+    precisions on the 2.26-bit keys), the decode time and effective GB/s (cache
     replicas beyond the Infinity Cache, as in the main leg) and the attention
     error of the GPU output against plain softmax attention over the
     unquantized 16-bit keys and values (fp64 on the host)."""
@@ -272,11 +276,16 @@ def pareto_leg(args, w):
             ref[b, kh * G:(kh + 1) * G] = (p / p.sum(axis=1, keepdims=True)) @ V
     points = []
     S = args.splits or w.n_splits or default_splits(w)
-    for label, n_hi, bits_hi, n_lo1 in kvq_synth.PARETO_POINTS:
-        wp = dataclasses.replace(w, n_pairs_hi=n_hi, bits_hi=bits_hi, n_pairs_lo1=n_lo1)
+    pts = [(label, n_hi, bits_hi, n_lo1, 0, 4)
+           for label, n_hi, bits_hi, n_lo1 in kvq_synth.PARETO_POINTS]
+    pts += [(label, 6, 4, 0, nvb, bvh) for label, nvb, bvh in kvq_synth.VALUE_POINTS]
+    for label, n_hi, bits_hi, n_lo1, nvb, bvh in pts:
+        wp = dataclasses.replace(w, n_pairs_hi=n_hi, bits_hi=bits_hi, n_pairs_lo1=n_lo1,
+                                 n_vblk_hi=nvb, bits_vhi=bvh)
         layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads, n_pairs_hi=n_hi,
                                  bits_hi=bits_hi, n_pairs_lo1=n_lo1, residual=w.residual,
-                                 max_tokens=T, io_dtype=w.io_dtype)
+                                 max_tokens=T, io_dtype=w.io_dtype, n_vblk_hi=nvb,
+                                 bits_vhi=bvh)
         base = kvq.Cache(layout)
         kvq.kvq_select_pairs(layout, dev(data["q_sel"]), w.n_qry, dev(data["k"][:, :, :T]), T,
                              base.struct)
@@ -310,7 +319,8 @@ def pareto_leg(args, w):
         err = np.abs(got - ref)
         alg = algorithmic_bytes(wp, T)
         points.append({"bits": label, "salient_pairs": n_hi, "salient_bits": bits_hi,
-                       "one_bit_pairs": n_lo1, "us_per_step": round(us, 3),
+                       "one_bit_pairs": n_lo1, "value_blocks_hi": nvb,
+                       "value_bits_hi": bvh if nvb else None, "us_per_step": round(us, 3),
                        "GBs": round(alg / (us * 1e-6) / 1e9, 1),
                        "algorithmic_bytes": alg, "layout_bytes": layout_bytes(base, wp, T),
                        "max_abs_err_vs_unquantized": float(err.max()),

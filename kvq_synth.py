@@ -86,6 +86,9 @@ WORKLOADS = [
 # Bit points of the precision sweep: (label, salient pairs, their bits,
 # pairs at 1 bit).  "1.5": 32 pairs at 2 bits and the 32 lowest-ranked at 1.
 PARETO_POINTS = [("1.5", 0, 4, 32), ("2.0", 0, 4, 0), ("2.26", 6, 4, 0), ("3.0", 6, 16, 0)]
+# Value-precision points on the 2.26-bit keys: (label, kept 8-token value
+# blocks per 32-token group, their bits).
+VALUE_POINTS = [("2.26 v1@3", 1, 3), ("2.26 v1@4", 1, 4), ("2.26 v2@4", 2, 4)]
 
 
 def workload(name: str) -> Workload:
