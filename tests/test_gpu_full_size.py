@@ -109,3 +109,50 @@ def test_streaming_b16_appends():
     e32 = check_single_split(part, ref, ATOL)
     print("%s T=%d S=%d max|err| %.3g max|o| %.3g split-record max|err| %.3g"
           % (w.name, T, S, err, np.abs(ref).max(), e32))
+
+
+@pytest.mark.timeout(400)
+def test_llama3_8b_32k_pruned_and_query_aware_and_shrink():
+    # the later calls at the 32K layer's full size: query-aware selection
+    # (bit-exact), pruned decode at the benchmark's split count (every output),
+    # and the shrink of every quantized group (every byte, then decode)
+    from decode_attention_select_amd import kvq
+    import torch
+    w = kvq_synth.workload("llama3-8b-32k")
+    print("case", w.name, "pruned / query-aware / shrink", flush=True)
+    case = Case(w)
+    pairs = check_selection(case)
+    qz = case.oracle_quant(pairs=pairs)
+    q = case.d["q_dec"][:, :, 0]
+    S = bench.default_splits(w)
+    for n_keep in (2, 3):
+        ref = oracle.attention_pruned(qz, q, SM_SCALE, n_keep)
+        err = check_output(case.decode_pruned(q, S, n_keep), ref, w.io_dtype, ATOL)
+        print("%s keep=%d S=%d max|err| %.3g" % (w.name, n_keep, S, err), flush=True)
+    kvq.kvq_shrink(case.layout, case.cache.struct, 0, qz.nq // 32)
+    torch.cuda.synchronize()
+    sh = oracle.shrink(qz, 0, qz.nq // 32)
+    compare_cache(case, sh, sh.nq // 32)
+    err = check_output(case.decode(q, S), oracle.attention(sh, q, SM_SCALE), w.io_dtype, ATOL)
+    print("%s shrunk S=%d max|err| %.3g" % (w.name, S, err), flush=True)
+    kvq.kvq_select_pairs_qa(case.layout, case.q_sel, w.n_qry, case.k_sel, w.tokens,
+                            case.cache.struct)
+    torch.cuda.synchronize()
+    Sq, pq = oracle.select_qa(case.d["q_sel"], case.d["k"], w.tokens, w.n_kv_heads, w.io_dtype)
+    g = case.gpu_bytes()
+    assert np.array_equal(g["sums"][:, :, 0], Sq.view(np.uint64))
+    assert np.array_equal(g["pairs"], pq)
+
+
+@pytest.mark.timeout(400)
+def test_llama3_8b_32k_two_value_precisions():
+    w = kvq_synth.workload("llama3-8b-32k").replace(n_vblk_hi=2, bits_vhi=4)
+    print("case", w.name, "two value precisions", flush=True)
+    case = Case(w)
+    qz = case.oracle_quant()
+    compare_cache(case, qz, qz.nq // 32)
+    q = case.d["q_dec"][:, :, 0]
+    ref = oracle.attention(qz, q, SM_SCALE)
+    S = bench.default_splits(w)
+    err = check_output(case.decode(q, S), ref, w.io_dtype, ATOL)
+    print("%s v2@4 S=%d max|err| %.3g" % (w.name, S, err))
