@@ -318,3 +318,21 @@ def test_two_value_precisions_reject_pruning():
         kvq.kvq_decode_attn_pruned(case.layout, dev(case.d["q_dec"][:, :, 0]), case.cache.struct,
                                    SM_SCALE, 4, 2, ws, out)
     assert e.value.status == -2
+
+
+@pytest.mark.parametrize("T", [1, 33, 95, 161])
+def test_two_value_precisions_edge_lengths(T):
+    # ring-only, one group and ragged lengths with kept value blocks
+    w = kvq_synth.Workload("edge-vmix", 1, 4, 1, 200, n_qry=8, io_dtype="bf16", n_pairs_hi=6,
+                           residual=32, seed=33, n_vblk_hi=1, bits_vhi=3)
+    case = Case(w, T=T)
+    qz = case.oracle_quant()
+    if qz.nq:
+        compare_cache(case, qz, qz.nq // 32)
+    q = case.d["q_dec"][:, :, 0]
+    ref = oracle.attention(qz, q, SM_SCALE)
+    for S in (1, 5):
+        got, part = case.decode(q, S, partials=True)
+        check_output(got, ref, w.io_dtype, ATOL)
+        if S == 1:
+            check_single_split(part, ref, ATOL)
