@@ -305,26 +305,28 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   }
 
   // The 32-token blocks of this (sequence, KV head): the nrb ring blocks
-  // first, then the quantized groups (block n >= nrb is group n - nrb).  A
-  // ring block has the longest latency chain, so it goes to the first split
-  // and is worked on while the group stream warms up.  Split s takes blocks
-  // [n0, n1); its waves take them round-robin.
+  // first, then the quantized groups (block n >= nrb is group n - nrb).
+  // Blocks are dealt out interleaved: wave w of split s takes blocks
+  // s + S*w + S*NW*i, so at every step the workgroups of a KV head read one
+  // contiguous band of groups, and the ring blocks (the longest latency
+  // chains) go to the first waves of different splits, worked on while the
+  // group stream warms up.
   const int nq = n_quant(T, g.R), ngq = nq / GS;
   const int nrb = (T - nq + GS - 1) / GS;
   const int NB = ngq + nrb;
-  const int n0 = (int)((long long)s * NB / S), n1 = (int)((long long)(s + 1) * NB / S);
+  const int STR = S * NW;         // block stride of one wave
   const size_t rec0 = (size_t)bh * g.NG;
-  const int first = n0 + wave;  // this wave's blocks: first + i*NW < n1
-  const int i0 = first >= nrb ? 0 : (nrb - first + NW - 1) / NW;  // its first group block
+  const int first = s + S * wave;  // this wave's blocks: first + i*STR < NB
+  const int i0 = first >= nrb ? 0 : (nrb - first + STR - 1) / STR;  // its first group block
 
-  // This wave's quantized groups are gfirst + i*NW, i < nmine.  Exactly PF
+  // This wave's quantized groups are gfirst + i*STR, i < nmine.  Exactly PF
   // group loads are kept in flight (past the end the index is clamped to the
   // wave's last group, or to group 0: cache hits, never used), so the
   // compiler can count outstanding loads and never drains the prefetches.
-  const int gfirst = first + i0 * NW - nrb;  // >= 0
-  const int nmine = first + i0 * NW < n1 ? (n1 - (first + i0 * NW) + NW - 1) / NW : 0;
-  const int nlast = nmine > 0 ? gfirst + (nmine - 1) * NW : 0;
-  auto group_at = [&](int i) { return rec0 + (size_t)min(gfirst + i * NW, nlast); };
+  const int gfirst = first + i0 * STR - nrb;  // >= 0
+  const int nmine = first + i0 * STR < NB ? (NB - (first + i0 * STR) + STR - 1) / STR : 0;
+  const int nlast = nmine > 0 ? gfirst + (nmine - 1) * STR : 0;
+  auto group_at = [&](int i) { return rec0 + (size_t)min(gfirst + i * STR, nlast); };
   Pref pf[PF];
   if constexpr (HASQ) {
 #pragma unroll
@@ -659,7 +661,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // ring blocks (16-bit keys and values) of this wave: blocks n < nrb.  Key
   // and value tiles are requested together (one round trip); the query is
   // the raw one already in registers.
-  for (int n = first; n < min(n1, nrb); n += NW) {
+  for (int n = first; n < nrb; n += STR) {
     const int pbase = nq + GS * n;
     const int nvalid = min(GS, T - pbase);
     const int sb = (pbase / GS) % (g.RS / GS);
