@@ -295,6 +295,22 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
     for (int i = 0; i < 4; i++) qv[i] = qg[i];
   }
+  // Quantized group g goes to wave w of split s with s + S*w = g mod S*NW,
+  // so a wave's groups are first + i*STR: their addresses do not depend on
+  // the length, and the first PF are requested before it arrives (clamped
+  // to the capacity; loads past the wave's last group are never used).  At
+  // every step the workgroups of a KV head read one contiguous band.
+  const int STR = S * NW;          // group stride of one wave
+  const size_t rec0 = (size_t)bh * g.NG;
+  const int first = s + S * wave;  // this wave's groups: first + i*STR < ngq
+  Pref pf[PF];
+  if constexpr (HASQ) {
+#pragma unroll
+    for (int k = 0; k < PF; k++)
+      load_group<HIMODE, PRUNE, 4, VHI>(c, rec0 + (size_t)min(first + k * STR, g.NG - 1), lane,
+                                        col, kq, kq, lane & 31, 0xE4u, g.nh, g.n_vhi, pf[k]);
+  }
+
   // scalar loads: the length and the 8 leading ranks
   const int T = c.len[bh];
   int top[8];
@@ -303,37 +319,19 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
     for (int r = 0; r < 8; r++) top[r] = pr[r];
   }
-
-  // The 32-token blocks of this (sequence, KV head): the nrb ring blocks
-  // first, then the quantized groups (block n >= nrb is group n - nrb).
-  // Blocks are dealt out interleaved: wave w of split s takes blocks
-  // s + S*w + S*NW*i, so at every step the workgroups of a KV head read one
-  // contiguous band of groups, and the ring blocks (the longest latency
-  // chains) go to the first waves of different splits, worked on while the
-  // group stream warms up.
   const int nq = n_quant(T, g.R), ngq = nq / GS;
   const int nrb = (T - nq + GS - 1) / GS;
-  const int NB = ngq + nrb;
-  const int STR = S * NW;         // block stride of one wave
-  const size_t rec0 = (size_t)bh * g.NG;
-  const int first = s + S * wave;  // this wave's blocks: first + i*STR < NB
-  const int i0 = first >= nrb ? 0 : (nrb - first + STR - 1) / STR;  // its first group block
-
-  // This wave's quantized groups are gfirst + i*STR, i < nmine.  Exactly PF
+  // This wave's quantized groups are first + i*STR, i < nmine.  Exactly PF
   // group loads are kept in flight (past the end the index is clamped to the
   // wave's last group, or to group 0: cache hits, never used), so the
   // compiler can count outstanding loads and never drains the prefetches.
-  const int gfirst = first + i0 * STR - nrb;  // >= 0
-  const int nmine = first + i0 * STR < NB ? (NB - (first + i0 * STR) + STR - 1) / STR : 0;
-  const int nlast = nmine > 0 ? gfirst + (nmine - 1) * STR : 0;
-  auto group_at = [&](int i) { return rec0 + (size_t)min(gfirst + i * STR, nlast); };
-  Pref pf[PF];
-  if constexpr (HASQ) {
-#pragma unroll
-    for (int k = 0; k < PF; k++)
-      load_group<HIMODE, PRUNE, 4, VHI>(c, group_at(k), lane, col, kq, kq, lane & 31, 0xE4u,
-                                        g.nh, g.n_vhi, pf[k]);
-  }
+  const int nmine = first < ngq ? (ngq - first + STR - 1) / STR : 0;
+  const int nlast = nmine > 0 ? first + (nmine - 1) * STR : 0;
+  auto group_at = [&](int i) { return rec0 + (size_t)min(first + i * STR, nlast); };
+  // The nrb ring blocks continue the same order after the groups (block
+  // ngq + r), so they fall to waves holding one group fewer than the most;
+  // a ring block is worked on first, while the group stream warms up.
+  const int ring0 = ((first - ngq) % STR + STR) % STR;
 
   // kept key chunks (all four unless PRUNE); every lane computes the same mask
   uint32_t kmask = 0xFu;
@@ -661,7 +659,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // ring blocks (16-bit keys and values) of this wave: blocks n < nrb.  Key
   // and value tiles are requested together (one round trip); the query is
   // the raw one already in registers.
-  for (int n = first; n < nrb; n += STR) {
+  for (int n = ring0; n < nrb; n += STR) {
     const int pbase = nq + GS * n;
     const int nvalid = min(GS, T - pbase);
     const int sb = (pbase / GS) % (g.RS / GS);
