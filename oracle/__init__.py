@@ -130,9 +130,12 @@ def quantize(k, v, T: int, pairs, *, residual: int, n_pairs_hi: int,
              bits_hi: int, io_dtype: str, ng: int | None = None,
              n_pairs_lo1: int = 0, n_vblk_hi: int = 0, bits_vhi: int = 4) -> Quantized:
     """Quantize keys and values of the first T tokens (k, v
-    [B][Hkv][Tstride][128] bits) with the given rank table.  n_vblk_hi of the
-    four 8-token blocks of each group (those of largest fixed-point value
-    magnitude) get bits_vhi-bit values, the rest 2-bit (the SemKV reading)."""
+    [B][Hkv][Tstride][128] bits) with the given rank table.  With n_vblk_hi >
+    0 each group's tokens are ordered by descending key magnitude (``order``
+    [B][Hkv][NG][32]: slot -> position; identity otherwise) and the values of
+    the first 8 n_vblk_hi tokens in that order get bits_vhi bits, the rest 2
+    bits (the SemKV reading).  Codes, scales and zeros stay in position
+    order."""
     lib = _load()
     k = np.ascontiguousarray(k, dtype=np.uint16)
     v = np.ascontiguousarray(v, dtype=np.uint16)
@@ -150,16 +153,19 @@ def quantize(k, v, T: int, pairs, *, residual: int, n_pairs_hi: int,
                             int(residual), int(n_pairs_hi), int(bits_hi),
                             int(n_pairs_lo1), _p(pairs), NG, _p(kc), _p(ks), _p(kz))
     assert rc == 0
-    vblk = np.zeros((B, Hkv, NG), np.uint8)
+    order = np.zeros((B, Hkv, NG, GS), np.uint8)
+    rc = lib.orc_token_order(B, Hkv, _bf(io_dtype), _p(k), Tstride, int(T), int(residual),
+                             NG, int(n_vblk_hi), _p(order))
+    assert rc == 0
     rc = lib.orc_quant_values(B, Hkv, _bf(io_dtype), _p(v), Tstride, int(T),
                               int(residual), 2, NG, int(n_vblk_hi), int(bits_vhi),
-                              _p(vc), _p(vs), _p(vz), _p(vblk))
+                              _p(order), _p(vc), _p(vs), _p(vz))
     assert rc == 0
     return Quantized(k=k, v=v, T=int(T), R=int(residual), n_hi=int(n_pairs_hi),
                      bits_hi=int(bits_hi), n_lo1=int(n_pairs_lo1), io_dtype=io_dtype,
                      pairs=pairs,
                      NG=NG, nq=nq, kcodes=kc, ks=ks, kz=kz, vcodes=vc, vs=vs,
-                     vz=vz, n_vblk_hi=int(n_vblk_hi), bits_vhi=int(bits_vhi), vblk=vblk)
+                     vz=vz, n_vblk_hi=int(n_vblk_hi), bits_vhi=int(bits_vhi), order=order)
 
 
 def attention(qz: Quantized, q, sm_scale: float, with_lse: bool = False):
@@ -201,12 +207,12 @@ def pack(qz: Quantized) -> dict:
     ring_k = np.zeros((B, Hkv, RS, D), np.uint16)
     ring_v = np.zeros((B, Hkv, RS // GS, D, GS), np.uint16)
     lib.orc_pack_keys(B, Hkv, _p(qz.k), Tstride, qz.T, qz.R, qz.n_hi,
-                      qz.bits_hi, qz.n_lo1, _p(qz.pairs), NG, _p(qz.kcodes), _p(qz.ks),
-                      _p(qz.kz), _p(k_lo), _p(k_hi), _p(k_meta))
-    nvb = getattr(qz, "n_vblk_hi", 0)
-    v_hi = np.zeros((B, Hkv, NG, 4 + 64 * nvb), np.uint32)
+                      qz.bits_hi, qz.n_lo1, _p(qz.pairs), NG, _p(qz.order), _p(qz.kcodes),
+                      _p(qz.ks), _p(qz.kz), _p(k_lo), _p(k_hi), _p(k_meta))
+    nvb = qz.n_vblk_hi
+    v_hi = np.zeros((B, Hkv, NG, 8 + 64 * nvb if nvb else 0), np.uint32)
     lib.orc_pack_values(B, Hkv, qz.T, qz.R, NG, _p(qz.vcodes), _p(qz.vs),
-                        _p(qz.vz), int(nvb), _p(qz.vblk) if nvb else None, _p(v_codes),
+                        _p(qz.vz), int(nvb), _p(qz.order), _p(v_codes),
                         _p(v_meta), _p(v_hi) if nvb else None)
     lib.orc_ring(B, Hkv, _p(qz.k), _p(qz.v), Tstride, qz.T, qz.R, _p(ring_k),
                  _p(ring_v))

@@ -111,24 +111,23 @@ def _v_digits(words, base: int, nslot: int, slot: int):
 
 
 def unpack_values(v_codes, v_meta, v_hi=None):
-    """One group record -> (codes [32 tokens][128], s_bits [32][4],
-    z_bits [32][4]).  With a v_hi record (header word 0 = mask of the kept
-    8-token blocks, then their high digits block by block), a kept block's
-    code is low digit + 4 * high digit."""
+    """One group record -> (codes [32 slots][128], s_bits [32][4],
+    z_bits [32][4], order [32]).  Without a v_hi record slot = position and
+    every code is its two-bit digit.  With one (8 header words holding the
+    32 order bytes slot -> position, then the high digits of the first
+    n 8-slot blocks), the codes of those blocks are low digit + 4 * high
+    digit."""
     codes = np.zeros((GS, D), np.int64)
     for kq in range(4):
         codes[8 * kq:8 * kq + 8] = _v_digits(v_codes, 0, 4, kq)
-    if v_hi is not None and len(v_hi) > 4:
-        nslot = (len(v_hi) - 4) // 64
-        mask = int(v_hi[0])
-        slot = 0
-        for kq in range(4):
-            if (mask >> kq) & 1:
-                codes[8 * kq:8 * kq + 8] += 4 * _v_digits(v_hi, 4, nslot, slot)
-                slot += 1
-        assert slot == nslot
+    order = np.arange(GS)
+    if v_hi is not None and len(v_hi) > 0:
+        nslot = (len(v_hi) - 8) // 64
+        order = np.frombuffer(np.asarray(v_hi[:8], np.uint32).tobytes(), np.uint8).astype(np.int64)
+        for kq in range(nslot):
+            codes[8 * kq:8 * kq + 8] += 4 * _v_digits(v_hi, 8, nslot, kq)
     meta = np.asarray(v_meta, np.uint16).reshape(2, 4, GS)
-    return codes, meta[0].T.copy(), meta[1].T.copy()
+    return codes, meta[0].T.copy(), meta[1].T.copy(), order
 
 
 def attention_textbook(q: np.ndarray, K: np.ndarray, V: np.ndarray,

@@ -371,53 +371,64 @@ int orc_quant_keys(int B, int Hkv, int bf16, const uint16_t *k, int Tstride,
 /* Two value precisions by token (SemKV, abstract: tokens are ranked by a
  * model-internal score and given one of two adjacent precisions; the page
  * names no indicator and finds the indicators interchangeable above the
- * quality cliff, so this is a reading).  The unit is the 8-token block (a
- * quarter of a 32-token group).  A block's score is
- *   E = sum over its 8 tokens and 128 channels of min(floor(4096 |v|), 2^20)
- * (integer, so order-free); the n_vblk_hi blocks of largest E in each group
- * (ties to the lower block) are quantized at bits_vhi bits (L = 2^bits_vhi -
- * 1), the others at bits_v bits.  blkmask[group] gets bit b for a kept
- * block b (may be NULL when n_vblk_hi == 0). */
-static uint64_t orc_vblock_score(const uint16_t *rows, int bf16) {
-  uint64_t e = 0;
-  for (int t = 0; t < 8; t++)
-    for (int c = 0; c < D; c++) {
-      double u = floor(4096.0 * fabs(to_f64(rows[(size_t)t * D + c], bf16)));
-      e += (uint64_t)(u < 1048576.0 ? u : 1048576.0);
-    }
-  return e;
+ * quality cliff, so this is a reading).  The indicator is the token's key
+ * magnitude,
+ *   E_t = sum over the 128 channels of min(floor(4096 |k_t,c|), 2^20)
+ * (integer, so order-free).  Within each 32-token group the tokens are
+ * stored in descending E order (ties to the lower position): order[slot] =
+ * position; attention does not depend on the order.  The 8 n_vblk_hi
+ * tokens in the first slots quantize their values at bits_vhi bits, the
+ * others at bits_v bits.  With n_vblk_hi == 0 the order is the identity. */
+int orc_token_order(int B, int Hkv, int bf16, const uint16_t *k, int Tstride, int T, int R,
+                    int NG, int n_vblk_hi, uint8_t *order) {
+  int ng = orc_n_quant(T, R) / GS;
+  if (ng > NG) return -1;
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++)
+      for (int g = 0; g < ng; g++) {
+        uint8_t *ord = order + ((size_t)(b * Hkv + kh) * NG + g) * GS;
+        uint64_t E[GS];
+        for (int t = 0; t < GS; t++) {
+          const uint16_t *row = k + (((size_t)b * Hkv + kh) * Tstride + g * GS + t) * D;
+          E[t] = 0;
+          for (int c = 0; c < D; c++) {
+            double u = floor(4096.0 * fabs(to_f64(row[c], bf16)));
+            E[t] += (uint64_t)(u < 1048576.0 ? u : 1048576.0);
+          }
+        }
+        for (int t = 0; t < GS; t++) {
+          int rank = 0;
+          if (n_vblk_hi > 0)
+            for (int i = 0; i < GS; i++) rank += (E[i] > E[t]) || (E[i] == E[t] && i < t);
+          else
+            rank = t;
+          ord[rank] = (uint8_t)t;
+        }
+      }
+  return 0;
 }
 
 int orc_quant_values(int B, int Hkv, int bf16, const uint16_t *v, int Tstride,
                      int T, int R, int bits_v, int NG, int n_vblk_hi, int bits_vhi,
-                     uint8_t *codes, uint16_t *s, uint16_t *z, uint8_t *blkmask) {
+                     const uint8_t *order, uint8_t *codes, uint16_t *s, uint16_t *z) {
   int ng = orc_n_quant(T, R) / GS;
   if (ng > NG || n_vblk_hi < 0 || n_vblk_hi > 4) return -1;
   float x[GS];
   for (int b = 0; b < B; b++)
     for (int kh = 0; kh < Hkv; kh++)
       for (int g = 0; g < ng; g++) {
-        const uint16_t *grow = v + (((size_t)b * Hkv + kh) * Tstride + g * GS) * D;
-        uint64_t E[4];
-        for (int k = 0; k < 4; k++) E[k] = orc_vblock_score(grow + (size_t)8 * k * D, bf16);
-        int kept[4];
-        uint8_t mask = 0;
-        for (int k = 0; k < 4; k++) {
-          int rank = 0;
-          for (int i = 0; i < 4; i++) rank += (E[i] > E[k]) || (E[i] == E[k] && i < k);
-          kept[k] = rank < n_vblk_hi;
-          if (kept[k]) mask |= (uint8_t)(1u << k);
-        }
-        if (blkmask) blkmask[(size_t)(b * Hkv + kh) * NG + g] = mask;
-        for (int t = 0; t < GS; t++)
+        const uint8_t *ord = order + ((size_t)(b * Hkv + kh) * NG + g) * GS;
+        for (int slot = 0; slot < GS; slot++) {
+          int t = ord[slot];
+          int bits = slot < 8 * n_vblk_hi ? bits_vhi : bits_v;
+          size_t tok = ((size_t)(b * Hkv + kh) * NG + g) * GS + t;
+          const uint16_t *row = v + (((size_t)b * Hkv + kh) * Tstride + g * GS + t) * D;
           for (int j = 0; j < D / GS; j++) {
-            size_t tok = ((size_t)(b * Hkv + kh) * NG + g) * GS + t;
-            const uint16_t *row = grow + (size_t)t * D;
-            int bits = kept[t / 8] ? bits_vhi : bits_v;
             for (int i = 0; i < GS; i++) x[i] = (float)to_f64(row[j * GS + i], bf16);
             orc_quant_group(x, (1 << bits) - 1, s + tok * 4 + j, z + tok * 4 + j,
                             codes + tok * D + j * GS);
           }
+        }
       }
   return 0;
 }
@@ -507,10 +518,12 @@ static int pos_swap(int c) { return (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1); 
 /* Packs the logical key codes of groups [0, ng) into the byte records.
  * k_lo [..][NG][256] u32, k_hi (4-bit: [..][NG][32] u32; 16-bit:
  * [..][NG][32][2*n_hi] u16 raw), k_meta [..][NG][2][128] u16. */
+/* Key records in the group's token order: tile index e holds the token at
+ * slot tile_token(e), i.e. position order[tile_token(e)]. */
 int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
                   int n_hi, int bits_hi, int n_lo1, const int32_t *pairs, int NG,
-                  const uint8_t *codes, const uint16_t *s, const uint16_t *z,
-                  uint32_t *k_lo, void *k_hi, uint16_t *k_meta) {
+                  const uint8_t *order, const uint8_t *codes, const uint16_t *s,
+                  const uint16_t *z, uint32_t *k_lo, void *k_hi, uint16_t *k_meta) {
   int ng = orc_n_quant(T, R) / GS;
   for (int b = 0; b < B; b++)
     for (int kh = 0; kh < Hkv; kh++) {
@@ -521,10 +534,11 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
       for (int g = 0; g < ng; g++) {
         size_t grp = (size_t)(b * Hkv + kh) * NG + g;
         const uint8_t *cg = codes + grp * D * GS;
+        const uint8_t *ord = order + grp * GS;
         uint32_t *lo = k_lo + grp * 256;
         memset(lo, 0, 256 * 4);
         for (int e = 0; e < 32; e++) {
-          int t = tile_token(e), Tt = e / 16, r = e % 16;
+          int t = ord[tile_token(e)], Tt = e / 16, r = e % 16;
           for (int c = 0; c < D; c++) {
             int w = c / 16, kq = w / 2, u = w % 2;
             int bits = orc_channel_bits(pr, n_hi, bits_hi, n_lo1, 2, c);
@@ -537,14 +551,14 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
           uint32_t *hi = (uint32_t *)k_hi + grp * 32;
           memset(hi, 0, 32 * 4);
           for (int e = 0; e < 32; e++) {
-            int t = tile_token(e);
+            int t = ord[tile_token(e)];
             for (int d = 0; d < nh; d++)
               hi[e] |= (uint32_t)(cg[hil[d] * GS + t] >> 2) << (2 * pos_swap(d));
           }
         } else if (nh && bits_hi == 16) {
           uint16_t *hi = (uint16_t *)k_hi + grp * 32 * nh;
           for (int e = 0; e < 32; e++) {
-            int t = tile_token(e);
+            int t = ord[tile_token(e)];
             for (int d = 0; d < nh; d++)
               hi[e * nh + d] = k[(((size_t)b * Hkv + kh) * Tstride + g * GS + t) * D + hil[d]];
           }
@@ -561,14 +575,16 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
 
 /* Packs the logical value codes: v_codes [..][NG][256] u32,
  * v_meta [..][NG][2][4][32] u16. */
-/* v_codes holds the low two bits of every value code.  With n_vblk_hi > 0,
- * v_hi holds per group 4 + 64 n_vblk_hi words: word 0 the kept-block mask,
- * words 1..3 zero, then for the s-th kept block (ascending) and channel
- * group j the words 4 + (j n_vblk_hi + s) 16 + c, in the v_codes word format,
- * of the codes' high two bits (NULL when n_vblk_hi == 0). */
+/* Value records in the group's token order: slot 8 kq + i of the v_codes
+ * word format holds position order[8 kq + i].  v_codes holds the low two
+ * bits of every value code.  With n_vblk_hi > 0, v_hi holds per group
+ * 8 + 64 n_vblk_hi words: the 32 order bytes (slot -> position), then for
+ * slot block kq < n_vblk_hi and channel group j the words
+ * 8 + (j n_vblk_hi + kq) 16 + c, in the v_codes word format, of the codes'
+ * high two bits (NULL when n_vblk_hi == 0). */
 int orc_pack_values(int B, int Hkv, int T, int R, int NG, const uint8_t *codes,
                     const uint16_t *s, const uint16_t *z, int n_vblk_hi,
-                    const uint8_t *blkmask, uint32_t *v_codes, uint16_t *v_meta,
+                    const uint8_t *order, uint32_t *v_codes, uint16_t *v_meta,
                     uint32_t *v_hi) {
   int ng = orc_n_quant(T, R) / GS;
   for (int b = 0; b < B; b++)
@@ -576,6 +592,7 @@ int orc_pack_values(int B, int Hkv, int T, int R, int NG, const uint8_t *codes,
       for (int g = 0; g < ng; g++) {
         size_t grp = (size_t)(b * Hkv + kh) * NG + g;
         const uint8_t *cg = codes + grp * GS * D; /* [token][channel] */
+        const uint8_t *ord = order + grp * GS;
         uint32_t *vc = v_codes + grp * 256;
         memset(vc, 0, 256 * 4);
         for (int j = 0; j < 4; j++)
@@ -583,39 +600,34 @@ int orc_pack_values(int B, int Hkv, int T, int R, int NG, const uint8_t *codes,
             for (int c = 0; c < 16; c++) {
               uint32_t w = 0;
               for (int i = 0; i < 8; i++) {
-                int t = 8 * kq + i;
+                int t = ord[8 * kq + i];
                 w |= (uint32_t)(cg[t * D + 32 * j + c] & 3) << (2 * pos_swap(i));
                 w |= (uint32_t)(cg[t * D + 32 * j + 16 + c] & 3) << (16 + 2 * pos_swap(i));
               }
               vc[(j * 4 + kq) * 16 + c] = w;
             }
         if (n_vblk_hi > 0) {
-          size_t rw = 4 + 64 * (size_t)n_vblk_hi;
+          size_t rw = 8 + 64 * (size_t)n_vblk_hi;
           uint32_t *vh = v_hi + grp * rw;
           memset(vh, 0, rw * 4);
-          uint8_t mask = blkmask[grp];
-          vh[0] = mask;
-          int slot = 0;
-          for (int kq = 0; kq < 4; kq++) {
-            if (!((mask >> kq) & 1)) continue;
+          memcpy(vh, ord, GS);
+          for (int kq = 0; kq < n_vblk_hi; kq++)
             for (int j = 0; j < 4; j++)
               for (int c = 0; c < 16; c++) {
                 uint32_t w = 0;
                 for (int i = 0; i < 8; i++) {
-                  int t = 8 * kq + i;
+                  int t = ord[8 * kq + i];
                   w |= (uint32_t)(cg[t * D + 32 * j + c] >> 2) << (2 * pos_swap(i));
                   w |= (uint32_t)(cg[t * D + 32 * j + 16 + c] >> 2) << (16 + 2 * pos_swap(i));
                 }
-                vh[4 + (j * n_vblk_hi + slot) * 16 + c] = w;
+                vh[8 + (j * n_vblk_hi + kq) * 16 + c] = w;
               }
-            slot++;
-          }
         }
         uint16_t *meta = v_meta + grp * 256;
         for (int j = 0; j < 4; j++)
-          for (int t = 0; t < GS; t++) {
-            meta[j * 32 + t] = s[(grp * GS + t) * 4 + j];
-            meta[128 + j * 32 + t] = z[(grp * GS + t) * 4 + j];
+          for (int sl = 0; sl < GS; sl++) {
+            meta[j * 32 + sl] = s[(grp * GS + ord[sl]) * 4 + j];
+            meta[128 + j * 32 + sl] = z[(grp * GS + ord[sl]) * 4 + j];
           }
       }
   return 0;

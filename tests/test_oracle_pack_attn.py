@@ -59,7 +59,7 @@ def test_pack_roundtrip(w):
                 if raw is not None:
                     ref = d["k"][b, kh, 32 * g:32 * g + 32][:, sal].T
                     assert np.array_equal(raw, ref)
-                vc, vs, vz = brute.unpack_values(pk["v_codes"][b, kh, g], pk["v_meta"][b, kh, g])
+                vc, vs, vz, _ = brute.unpack_values(pk["v_codes"][b, kh, g], pk["v_meta"][b, kh, g])
                 assert np.array_equal(vc, qz.vcodes[b, kh, g])
                 assert np.array_equal(vs, qz.vs[b, kh, g]) and np.array_equal(vz, qz.vz[b, kh, g])
             # 4-bit channels hold codes up to 15, 2-bit ones up to 3
@@ -84,7 +84,7 @@ def _dequant_from_bytes(w, d, pairs, pk, b, kh, T):
             if w.bits_hi == 16 and c in sal:
                 continue
             K[32 * g:32 * g + 32, c] = f16(z[c]) + f16(s[c]) * codes[c]
-        vc, vs, vz = brute.unpack_values(pk["v_codes"][b, kh, g], pk["v_meta"][b, kh, g])
+        vc, vs, vz, _ = brute.unpack_values(pk["v_codes"][b, kh, g], pk["v_meta"][b, kh, g])
         for t in range(32):
             for j in range(4):
                 V[32 * g + t, 32 * j:32 * j + 32] = f16(vz[t, j]) + f16(vs[t, j]) * vc[t, 32 * j:32 * j + 32]

@@ -127,7 +127,7 @@ def test_pruned_attention_matches_textbook_on_kept_columns(data, n_keep):
                                                    pk["k_meta"][b, kh, g], sal, W.bits_hi)
                 for c in range(128):
                     K[32 * g:32 * g + 32, c] = f16(z[c]) + f16(s[c]) * codes[c]
-                vc, vs, vz = brute.unpack_values(pk["v_codes"][b, kh, g], pk["v_meta"][b, kh, g])
+                vc, vs, vz, _ = brute.unpack_values(pk["v_codes"][b, kh, g], pk["v_meta"][b, kh, g])
                 for t in range(32):
                     for j in range(4):
                         V[32 * g + t, 32 * j:32 * j + 32] = (f16(vz[t, j]) + f16(vs[t, j]) *

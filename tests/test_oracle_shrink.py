@@ -114,7 +114,7 @@ def test_attention_over_shrunk_bytes_matches_textbook():
                 assert set(np.unique(codes[sal])) <= {0, 5, 10, 15}
                 for c in range(128):
                     K[32 * g:32 * g + 32, c] = _f16(z[c]) + _f16(s[c]) * codes[c]
-                vc, vs, vz = brute.unpack_values(pk["v_codes"][b, kh, g], pk["v_meta"][b, kh, g])
+                vc, vs, vz, _ = brute.unpack_values(pk["v_codes"][b, kh, g], pk["v_meta"][b, kh, g])
                 for t in range(32):
                     for j in range(4):
                         V[32 * g + t, 32 * j:32 * j + 32] = (_f16(vz[t, j]) + _f16(vs[t, j]) *
