@@ -57,8 +57,8 @@ def algorithmic_bytes(w, T: int, n_keep: int = 4) -> int:
         k_code_bits = n_hi_ch * w.bits_hi + n_two_ch * 2 + n_one_ch
         k_meta = 128 * 4 / 32
     per_tok = k_code_bits / 8 + k_meta + 32 + 16
-    if w.n_vblk_hi:  # the kept value blocks' extra bits and a 4-bit block mask per group
-        per_tok += w.n_vblk_hi / 4 * (w.bits_vhi - 2) * 128 / 8 + 0.5 / 32
+    if w.n_vblk_hi:  # the high-precision tokens' extra value bits (decode skips the order bytes)
+        per_tok += w.n_vblk_hi / 4 * (w.bits_vhi - 2) * 128 / 8
     return int(round(bh * (nq * per_tok + nr * 512) + qo))
 
 
@@ -374,7 +374,7 @@ def prefill_leg(args, w):
     data = kvq_synth.generate(w)
     layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads, n_pairs_hi=w.n_pairs_hi,
                              bits_hi=w.bits_hi, residual=w.residual, max_tokens=T,
-                             io_dtype=w.io_dtype)
+                             io_dtype=w.io_dtype, n_vblk_hi=w.n_vblk_hi, bits_vhi=w.bits_vhi)
     cache = kvq.Cache(layout)
     k0, v0, q0 = dev(data["k"][:, :, :T]), dev(data["v"][:, :, :T]), dev(data["q_sel"])
     n_rep = max(1, math.ceil(args.replica_mib * 2 ** 20 / (k0.numel() * 2)))
@@ -393,6 +393,10 @@ def prefill_leg(args, w):
         k_tok = (n_hi_ch * 16 + (128 - n_hi_ch) * 2) / 8 + (128 - n_hi_ch) * 4 / 32
     else:
         k_tok = (n_hi_ch * w.bits_hi + (128 - n_hi_ch) * 2) / 8 + 16
+    # two value precisions: the key side writes each group's 32 order bytes,
+    # the value side reads them and writes 256 bytes per 8 high-precision tokens
+    vhi_k = bh * (nq // 32) * 32 if w.n_vblk_hi else 0
+    vhi_v = bh * (nq // 32) * (32 + 256 * w.n_vblk_hi) if w.n_vblk_hi else 0
     calls = [
         ("kvq_select_pairs", q_in + kv_in + sel_out,
          st(lambda i: kvq.kvq_select_pairs(layout, qs[i], w.n_qry, ks[i], T, cache.struct,
@@ -400,9 +404,9 @@ def prefill_leg(args, w):
         ("kvq_select_pairs_qa", q_in + kv_in + sel_out,
          st(lambda i: kvq.kvq_select_pairs_qa(layout, qs[i], w.n_qry, ks[i], T, cache.struct,
                                               stream=stream))),
-        ("kvq_quant_keys", kv_in + int(bh * (nq * k_tok + nr * 256)),
+        ("kvq_quant_keys", kv_in + int(bh * (nq * k_tok + nr * 256)) + vhi_k,
          st(lambda i: kvq.kvq_quant_keys(layout, ks[i], T, cache.struct, stream=stream))),
-        ("kvq_quant_values", kv_in + bh * (nq * 48 + nr * 256),
+        ("kvq_quant_values", kv_in + bh * (nq * 48 + nr * 256) + vhi_v,
          st(lambda i: kvq.kvq_quant_values(layout, vs[i], T, cache.struct, stream=stream))),
     ]
     res_calls = []
@@ -463,7 +467,9 @@ def prefill_leg(args, w):
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "context": T,
                    "selection_queries": w.n_qry, "io_dtype": w.io_dtype,
                    "salient_pairs": w.n_pairs_hi, "salient_bits": w.bits_hi,
-                   "residual": w.residual, "input_replicas": n_rep},
+                   "residual": w.residual, "input_replicas": n_rep,
+                   "value_hi_tokens": 8 * w.n_vblk_hi,
+                   "value_hi_bits": w.bits_vhi if w.n_vblk_hi else None},
         "calls": res_calls,
     }
 
@@ -482,6 +488,9 @@ def main():
                          "chunks kept (4: kvq_decode_attn)")
     ap.add_argument("--build", action="store_true",
                     help="time the cache-building calls on the workload instead of decode")
+    ap.add_argument("--value-hi", default="",
+                    help="with --build: N:B, the N*8 tokens of largest key magnitude per group "
+                         "get B-bit values (two value precisions)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run the copy-kernel calibration of this size")
     args = ap.parse_args()
@@ -500,6 +509,9 @@ def main():
     from decode_attention_select_amd import kvq
 
     w = kvq_synth.workload(args.workload)
+    if args.value_hi:
+        nvb, bvh = (int(x) for x in args.value_hi.split(":"))
+        w = w.replace(n_vblk_hi=nvb, bits_vhi=bvh)
     if args.build:
         print(json.dumps(prefill_leg(args, w)), flush=True)
         return

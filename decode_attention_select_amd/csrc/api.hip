@@ -46,7 +46,7 @@ Geo make_geo(const kvq_layout* L) {
   g.khi_bytes = g.n_hi == 0 ? 0 : (g.bits_hi == 4 ? 32 * 4 : GS * g.nh * 2);
   g.n_vhi = L->n_vblk_hi;
   g.bits_vhi = g.n_vhi ? L->bits_vhi : 2;
-  g.vhi_words = g.n_vhi ? 4 + 64 * g.n_vhi : 0;
+  g.vhi_words = g.n_vhi ? 8 + 64 * g.n_vhi : 0;
   return g;
 }
 

@@ -136,8 +136,7 @@ struct Pref {
   u4 hraw[2];       // raw salient keys (HIMODE 16): 8 values of the lane's token, tile 0 and 1
   uint32_t vc[4];   // v_codes word of channel group j = 0..3
   u4 meta;          // 16 B of the group's k_meta (lanes 0-31) or v_meta (lanes 32-63)
-  uint32_t vh[4][2];  // two value precisions: high-digit words of block kq's two candidate slots
-  uint32_t vmask;     // two value precisions: the group's kept-block mask
+  uint32_t vh[4];   // two value precisions: high-digit word of block kq, channel group j
 };
 
 // kqa: the key chunk whose low digits this lane reads (its own, kq, unless
@@ -148,23 +147,17 @@ struct Pref {
 // CHUNKED (pruned decode): slot i (< NCH) holds, for key chunk
 // (cmap >> 2i) & 3, the lane token's k_lo word kq/2 of that chunk.  Pruned
 // chunks are never named in cmap, so they are never fetched.
-// VHI (two value precisions, g.n_vhi kept blocks per group): block kq's
-// compact slot is the number of kept blocks below it, so it lies in
-// [max(0, kq - (4 - n)), min(kq, n - 1)], at most two values; both words are
-// read with the rest of the group (no wait on the mask) and the right one is
-// picked when the group is processed.
+// VHI (two value precisions by token, g.n_vhi high-precision 8-slot blocks
+// per group, the group's slots in key-magnitude order): blocks kq < n have
+// high-digit words; lanes of the other blocks read block n - 1's (fetched
+// anyway) and drop them when the group is processed.
 template <int HIMODE, bool CHUNKED, int NCH, bool VHI>
 __device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int col, int kq,
                                   int kqa, int mla, uint32_t cmap, int nh, int nvhi, Pref& p) {
   if constexpr (VHI) {
-    const uint32_t* vh = c.v_hi + rec * (4 + 64 * nvhi);
-    p.vmask = vh[0];
-    const int s0 = max(0, kq - (4 - nvhi)), s1 = min(kq, nvhi - 1);
+    const uint32_t* vh = c.v_hi + rec * (8 + 64 * nvhi) + 8 + min(kq, nvhi - 1) * 16 + col;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      p.vh[j][0] = vh[4 + (j * nvhi + s0) * 16 + col];
-      p.vh[j][1] = vh[4 + (j * nvhi + s1) * 16 + col];
-    }
+    for (int j = 0; j < 4; j++) p.vh[j] = vh[j * nvhi * 16];
   }
   if constexpr (CHUNKED) {
     const uint32_t* w = (const uint32_t*)c.k_lo + rec * GROUP_WORDS;
@@ -269,8 +262,9 @@ struct Lds {
 // scale/zero are not read (past the first PF prefetched groups, which are
 // issued before the query arrives): their lanes load a kept chunk's words
 // instead, which the same instruction fetches anyway.
-// VHI: the cache has two value precisions (g.n_vhi > 0): kept 8-token blocks
-// add their high value digits (4 * digit) through one more MFMA per tile.
+// VHI: the cache has two value precisions (g.n_vhi > 0): the first n_vhi
+// 8-slot blocks of each group (its tokens of largest key magnitude) add their
+// high value digits (4 * digit) through one more MFMA per tile.
 template <bool BF16, int HIMODE, bool HASQ, bool LO1, int KEEP, bool VHI>
 __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             kvq_cache c, float scale_log2, int S,
@@ -497,7 +491,6 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   };
 
   uint32_t* sm = lds.u.loop.stage[wave];
-  const int vs0 = max(0, kq - (4 - g.n_vhi));  // VHI: the first candidate slot of block kq
   auto process_group = [&](const Pref& cur, size_t rec) {
     // stage the metadata record: [0,64) k scale pairs, [64,128) k zero
     // pairs, [128,192) v scale pairs (j-major), [192,256) v zero pairs.
@@ -626,12 +619,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     softmax_step(cr, scale_log2, p);
     const u4 P = u4{pk_rne(p[0], p[1]), pk_rne(p[2], p[3]), pk_rne(p[4], p[5]), pk_rne(p[6], p[7])};
     // values
-    bool vkept = false;
-    int vslot = 0;
-    if constexpr (VHI) {
-      vkept = (cur.vmask >> kq) & 1u;
-      vslot = __popc(cur.vmask & ((1u << kq) - 1u));
-    }
+    const bool vkept = VHI && kq < g.n_vhi;
     const u4 za = col < 4 ? ((const u4*)(sm + 192 + 16 * col))[kq]
                           : (col == 4 ? u4{ONES, ONES, ONES, ONES} : u4{0, 0, 0, 0});
     Cvb = mma_f16(za, P, Cvb);
@@ -645,8 +633,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       O[2 * j] = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)}, pj, O[2 * j]);
       O[2 * j + 1] = mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)}, pj, O[2 * j + 1]);
       if constexpr (VHI) {
-        // block kq's high digits (0 unless kept), weighted 4 by the convert
-        const uint32_t wh = vkept ? (vslot == vs0 ? cur.vh[j][0] : cur.vh[j][1]) : 0u;
+        // block kq's high digits (0 past the high-precision blocks), weighted
+        // 4 by the convert
+        const uint32_t wh = vkept ? cur.vh[j] : 0u;
         const uint32_t Ah = wh & 0x33333333u, Bh = (wh >> 2) & 0x33333333u;
         O[2 * j] = mma_f16(u4{cvt2x4<0>(Ah), cvt2x4<0>(Bh), cvt2x4<1>(Ah), cvt2x4<1>(Bh)}, pj,
                            O[2 * j]);

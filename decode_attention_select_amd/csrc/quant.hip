@@ -150,17 +150,57 @@ __device__ inline PairMasks pair_masks(const Geo& g, const int32_t* pr) {
 struct KeyLds {  // one wave's staging of a key-group record
   uint32_t lo[GROUP_WORDS];
   uint32_t hi[256];  // 4-bit: 32 words; raw 16-bit: 32 tokens x up to 16 halves
+  uint32_t ord[8];   // two value precisions: the group's order bytes (slot -> position)
 };
 
-// rows: token 0 of the group, row stride D (prefill input or ring_k slots).
+// Token order of one group for two value precisions by token (the SemKV
+// reading documented in include/kvq.h at v_hi): token t's key magnitude
+// E_t = sum over the 128 channels of min(floor(4096 |k|), 2^20) (integer, at
+// most 2^27), and slot rank(t) = the number of tokens with larger E or equal
+// E and lower position.  rows: token 0 of the group, row stride D.  Lanes
+// 2t and 2t+1 sum the two channel halves of token t; every lane then ranks
+// its token against the 32 sums read back from lanes 2a.  Writes order
+// bytes (ord[rank(t)] = t) to LDS; the caller syncs before reading them.
 template <bool BF>
+__device__ void token_order_wave(const uint16_t* rows, uint32_t* ord) {
+  const int lane = threadIdx.x & 63, t = lane >> 1, h = lane & 1;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) v[i] = *(const uint4*)(rows + (size_t)t * D + 64 * h + 8 * i);
+  uint32_t e = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int k = 0; k < 8; k++)  // 4096 |x| is exact; the conversion truncates
+      e += (uint32_t)fminf(4096.0f * fabsf(in_to_f32(half_of(v[i], k), BF)), 1048576.0f);
+  e += dpp<QUAD_XOR1>(e);
+  uint32_t rank = 0;
+#pragma unroll
+  for (int a = 0; a < GS; a++) {
+    const uint32_t ea = __builtin_amdgcn_readlane(e, 2 * a);
+    rank += (ea > e) || (ea == e && a < t);
+  }
+  if (h == 0) ((uint8_t*)ord)[rank] = (uint8_t)t;
+}
+
+// rows: token 0 of the group, row stride D (prefill input or ring_k slots).
+// VHI: the tokens are taken in the order held in L.ord (slot i = position
+// L.ord[i]), so the record's token index is the slot.
+template <bool BF, bool VHI>
 __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
                                uint32_t* lo_out, uint8_t* hi_out, uint16_t* meta_out,
                                KeyLds& L) {
   const int lane = threadIdx.x & 63, cb = lane >> 2, tq = lane & 3;
+  // positions of the lane's slots 8tq .. 8tq+7, one byte each
+  uint2 pos = make_uint2(0, 0);
+  if constexpr (VHI) pos = ((const uint2*)L.ord)[tq];
+  auto pos_of = [&](int i) -> uint32_t {
+    if constexpr (VHI) return ((i < 4 ? pos.x : pos.y) >> (8 * (i & 3))) & 0xFFu;
+    return 8 * tq + i;
+  };
   uint4 v[8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) v[i] = *(const uint4*)(rows + (size_t)(8 * tq + i) * D + 8 * cb);
+  for (int i = 0; i < 8; i++) v[i] = *(const uint4*)(rows + (size_t)pos_of(i) * D + 8 * cb);
 
   const bool bits4 = g.nh > 0 && g.bits_hi == 4, raw16 = g.nh > 0 && g.bits_hi == 16;
   // bit allocation of the lane's channels 8cb + k
@@ -197,14 +237,27 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
   if (__any(zmin)) {
 #pragma unroll
     for (int k = 0; k < 8; k++) {
-      uint32_t f = 2;
+      if constexpr (VHI) {
+        // the first zero by position: smallest 2 * position + sign bit
+        uint32_t f = 0xFFFFu;
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const float x = in_to_f32(half_of(v[i], k), BF);
-        if (f == 2 && x == 0.0f) f = __float_as_uint(x) >> 31;
+        for (int i = 0; i < 8; i++) {
+          const float x = in_to_f32(half_of(v[i], k), BF);
+          if (x == 0.0f) f = min(f, 2 * pos_of(i) + (__float_as_uint(x) >> 31));
+        }
+        f = min(f, dpp<QUAD_XOR1>(f));
+        f = min(f, dpp<QUAD_XOR2>(f));
+        if (mn[k] == 0.0f) mn[k] = __uint_as_float((f & 1u) << 31);
+      } else {
+        uint32_t f = 2;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const float x = in_to_f32(half_of(v[i], k), BF);
+          if (f == 2 && x == 0.0f) f = __float_as_uint(x) >> 31;
+        }
+        const uint32_t sgn = sign_of_first_zero(f);
+        if (mn[k] == 0.0f) mn[k] = __uint_as_float(sgn);
       }
-      const uint32_t sgn = sign_of_first_zero(f);
-      if (mn[k] == 0.0f) mn[k] = __uint_as_float(sgn);
     }
   }
   // lane tq computes channels 2tq and 2tq+1 of the quad's eight
@@ -296,26 +349,38 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
 
 // CHMAJOR false: src = token 0 of the group, row stride D (prefill input).
 // CHMAJOR true:  src = a ring_v slot block [128][32] (channel, slot).
-// VHI (g.n_vhi > 0: two value precisions, the SemKV reading documented in
-// include/kvq.h at v_hi): lane (cb, tq) holds 8-token block tq, whose score
-// is summed over the lane's 64 values and the 16 lanes of its DPP row; the
-// n_vhi best blocks quantize at L = 2^bits_vhi - 1, and the high digits of
-// their codes go to vhi_out (the group's v_hi record).
-template <int CTRL>
-__device__ inline uint32_t dpp_row(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
-}
-
+// VHI (g.n_vhi > 0: two value precisions by token, the SemKV reading
+// documented in include/kvq.h at v_hi): pos holds the positions of the
+// lane's slots 8tq .. 8tq+7 (one byte each, from the group's token order);
+// slots below 8 n_vhi quantize at L = 2^bits_vhi - 1, and the high digits
+// of their codes go to vhi_out (the group's v_hi record) after its 8-word
+// order header, which the key side writes.
 template <bool BF, bool CHMAJOR, bool VHI>
-__device__ void value_group_wave(const Geo& g, const uint16_t* src, uint32_t* vc_out,
+__device__ void value_group_wave(const Geo& g, const uint16_t* src, uint2 pos, uint32_t* vc_out,
                                  uint16_t* meta_out, uint32_t* vhi_out) {
   const int lane = threadIdx.x & 63, cb = lane & 15, tq = lane >> 4, m = cb & 3, j = cb >> 2;
-  // x(i, k): token 8tq + i, channel 8cb + k
+  auto pos_of = [&](int i) -> uint32_t {
+    return ((i < 4 ? pos.x : pos.y) >> (8 * (i & 3))) & 0xFFu;
+  };
+  // x(i, k): slot 8tq + i, channel 8cb + k
   uint4 v[8];
+  if constexpr (VHI && CHMAJOR) {
+    // the slot's token is scattered in the channel-major ring block: gather
+    // 16-bit values, channel row n of the lane from the eight positions
 #pragma unroll
-  for (int n = 0; n < 8; n++)
-    v[n] = CHMAJOR ? *(const uint4*)(src + (size_t)(8 * cb + n) * GS + 8 * tq)
-                   : *(const uint4*)(src + (size_t)(8 * tq + n) * D + 8 * cb);
+    for (int n = 0; n < 8; n++) {
+      const uint16_t* r = src + (size_t)(8 * cb + n) * GS;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) w[i] = r[pos_of(2 * i)] | ((uint32_t)r[pos_of(2 * i + 1)] << 16);
+      v[n] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < 8; n++)
+      v[n] = CHMAJOR ? *(const uint4*)(src + (size_t)(8 * cb + n) * GS + 8 * tq)
+                     : *(const uint4*)(src + (size_t)(VHI ? pos_of(n) : 8 * tq + n) * D + 8 * cb);
+  }
   auto x = [&](int i, int k) {
     return in_to_f32(CHMAJOR ? half_of(v[k], i) : half_of(v[i], k), BF);
   };
@@ -348,31 +413,7 @@ __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint32_t* vc
       if (mn[i] == 0.0f) mn[i] = __uint_as_float(sgn);
     }
   }
-  // block scores and the kept-block mask (uniform)
-  uint32_t kept = 0;
-  if constexpr (VHI) {
-    uint32_t e = 0;  // at most 64 * 2^20 per lane, 2^30 per row
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-#pragma unroll
-      for (int k = 0; k < 8; k++)
-        e += (uint32_t)fminf(4096.0f * fabsf(x(i, k)), 1048576.0f);
-    e += dpp_row<0x128>(e);  // row_ror:8
-    e += dpp_row<0x124>(e);  // row_ror:4
-    e += dpp_row<0x122>(e);  // row_ror:2
-    e += dpp_row<0x121>(e);  // row_ror:1
-    uint32_t E[4];
-#pragma unroll
-    for (int b = 0; b < 4; b++) E[b] = __builtin_amdgcn_readlane(e, 16 * b);
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-      int rank = 0;
-#pragma unroll
-      for (int a = 0; a < 4; a++) rank += (E[a] > E[b]) || (E[a] == E[b] && a < b);
-      if (rank < g.n_vhi) kept |= 1u << b;
-    }
-  }
-  const bool hiblk = (kept >> tq) & 1u;
+  const bool hiblk = VHI && tq < g.n_vhi;
   const float Lv = hiblk ? (float)((1 << g.bits_vhi) - 1) : 3.0f;
   auto pick = [&](const float (&a)[8], int o) {
     return m == 0 ? a[o] : m == 1 ? a[2 + o] : m == 2 ? a[4 + o] : a[6 + o];
@@ -390,7 +431,7 @@ __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint32_t* vc
 #undef KVQ_BCAST
   // half-word of channel k: its 8 tokens' codes at positions pi(i), summed
   // as exact float integers (digit * 4^position, below 2^16); codes above 3
-  // (kept blocks) split into a low digit here and a high digit in hh
+  // (high-precision slots) split into a low digit here and a high digit in hh
   float hf[8], hhf[8];
   uint32_t h[8], hh[8];
 #pragma unroll
@@ -437,11 +478,8 @@ __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint32_t* vc
   if constexpr (VHI) {
     uint32_t wh[4];
     words(hh, wh);
-    if (lane == 0) *(uint4*)vhi_out = make_uint4(kept, 0, 0, 0);
-    if (hiblk) {
-      const int slot = __popc(kept & ((1u << tq) - 1));
-      *(uint4*)(vhi_out + 4 + (j * g.n_vhi + slot) * 16 + c0) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-    }
+    if (hiblk)
+      *(uint4*)(vhi_out + 8 + (j * g.n_vhi + tq) * 16 + c0) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
   }
   if (m < 2) {
     uint32_t mm[4];
@@ -477,7 +515,9 @@ __device__ void ring_fill(const Geo& g, const uint16_t* __restrict__ x, int T, i
 
 // grid (B * Hkv, qblocks + ring blocks): blocks below qblocks quantize
 // QWAVES groups, one per wave; the rest fill the ring.
-template <bool BF>
+// VHI: each wave first ranks its group's tokens, writes the order to the
+// group's v_hi header and packs the keys in that order.
+template <bool BF, bool VHI>
 __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint16_t* __restrict__ k,
                                                               int T, int qblocks, kvq_cache c) {
   if ((int)blockIdx.y >= qblocks) {
@@ -485,16 +525,24 @@ __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint1
     return;
   }
   __shared__ KeyLds lds[QWAVES];
-  const int bh = blockIdx.x, wave = threadIdx.x >> 6;
+  const int bh = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = blockIdx.y * QWAVES + wave;
   if (grp >= n_quant(T, g.R) / GS) return;
   const size_t rec = (size_t)bh * g.NG + grp;
-  key_group_wave<BF>(g, k + ((size_t)bh * T + (size_t)grp * GS) * D,
-                 pair_masks(g, c.pairs + (size_t)bh * NPAIR),
-                 (uint32_t*)c.k_lo + rec * GROUP_WORDS, (uint8_t*)c.k_hi + rec * g.khi_bytes,
-                 (uint16_t*)c.k_meta + rec * 2 * D, lds[wave]);
+  const uint16_t* rows = k + ((size_t)bh * T + (size_t)grp * GS) * D;
+  if constexpr (VHI) {
+    token_order_wave<BF>(rows, lds[wave].ord);
+    wave_lds_sync();
+    if (lane < 2) ((uint4*)(c.v_hi + rec * g.vhi_words))[lane] = ((const uint4*)lds[wave].ord)[lane];
+  }
+  key_group_wave<BF, VHI>(g, rows, pair_masks(g, c.pairs + (size_t)bh * NPAIR),
+                          (uint32_t*)c.k_lo + rec * GROUP_WORDS,
+                          (uint8_t*)c.k_hi + rec * g.khi_bytes, (uint16_t*)c.k_meta + rec * 2 * D,
+                          lds[wave]);
 }
 
+// VHI: the group's token order comes from the v_hi header that the key
+// kernel wrote (an earlier launch on the same stream).
 template <bool BF, bool VHI>
 __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uint16_t* __restrict__ v,
                                                                 int T, int qblocks, kvq_cache c) {
@@ -502,25 +550,31 @@ __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uin
     ring_fill(g, v, T, blockIdx.y - qblocks, true, c);
     return;
   }
-  const int bh = blockIdx.x, wave = threadIdx.x >> 6;
+  const int bh = blockIdx.x, wave = threadIdx.x >> 6, tq = (threadIdx.x & 63) >> 4;
   const int grp = blockIdx.y * QWAVES + wave;
   if (grp >= n_quant(T, g.R) / GS) return;
   const size_t rec = (size_t)bh * g.NG + grp;
-  value_group_wave<BF, false, VHI>(g, v + ((size_t)bh * T + (size_t)grp * GS) * D,
-                          (uint32_t*)c.v_codes + rec * GROUP_WORDS,
-                          (uint16_t*)c.v_meta + rec * 2 * D, c.v_hi + rec * g.vhi_words);
+  uint32_t* vhi = c.v_hi + rec * g.vhi_words;
+  uint2 pos = make_uint2(0, 0);
+  if constexpr (VHI) pos = ((const uint2*)vhi)[tq];
+  value_group_wave<BF, false, VHI>(g, v + ((size_t)bh * T + (size_t)grp * GS) * D, pos,
+                                   (uint32_t*)c.v_codes + rec * GROUP_WORDS,
+                                   (uint16_t*)c.v_meta + rec * 2 * D, vhi);
 }
 
 // ------------------------------------------------------------------- append
 
 // One 128-thread workgroup per (b, kv head): the new token goes to ring slot
 // T mod RS; when n_q grows, wave 0 packs the oldest ring group's keys and
-// wave 1 its values (the new token is not in that group).
+// wave 1 its values (the new token is not in that group).  VHI: both waves
+// rank the group's tokens from the ring keys (the same integer sums, so the
+// same order); wave 0 also writes it to the v_hi header.
 template <bool BF, bool VHI>
 __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new,
                                                      kvq_cache c) {
   __shared__ KeyLds lds;
+  __shared__ __align__(16) uint32_t vord[8];
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int T = c.len[bh];
   if (T >= g.max_tokens) {
@@ -537,14 +591,28 @@ __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __re
     // the group [nq0, nq0 + 32) ends at T + 1 - R <= T: the new token is not in it
     const int grp = nq0 / GS, s0 = nq0 % g.RS;
     const size_t rec = (size_t)bh * g.NG + grp;
-    if (tid < 64)
-      key_group_wave<BF>(g, rk + (size_t)s0 * D, pair_masks(g, c.pairs + (size_t)bh * NPAIR),
-                     (uint32_t*)c.k_lo + rec * GROUP_WORDS, (uint8_t*)c.k_hi + rec * g.khi_bytes,
-                     (uint16_t*)c.k_meta + rec * 2 * D, lds);
-    else
-      value_group_wave<BF, true, VHI>(g, rv + (size_t)(s0 / GS) * D * GS,
-                                 (uint32_t*)c.v_codes + rec * GROUP_WORDS,
-                                 (uint16_t*)c.v_meta + rec * 2 * D, c.v_hi + rec * g.vhi_words);
+    uint32_t* vhi = c.v_hi + rec * g.vhi_words;
+    if (tid < 64) {
+      if constexpr (VHI) {
+        token_order_wave<BF>(rk + (size_t)s0 * D, lds.ord);
+        wave_lds_sync();
+        if (tid < 2) ((uint4*)vhi)[tid] = ((const uint4*)lds.ord)[tid];
+      }
+      key_group_wave<BF, VHI>(g, rk + (size_t)s0 * D, pair_masks(g, c.pairs + (size_t)bh * NPAIR),
+                              (uint32_t*)c.k_lo + rec * GROUP_WORDS,
+                              (uint8_t*)c.k_hi + rec * g.khi_bytes,
+                              (uint16_t*)c.k_meta + rec * 2 * D, lds);
+    } else {
+      uint2 pos = make_uint2(0, 0);
+      if constexpr (VHI) {
+        token_order_wave<BF>(rk + (size_t)s0 * D, vord);
+        wave_lds_sync();
+        pos = ((const uint2*)vord)[((tid & 63) >> 4)];
+      }
+      value_group_wave<BF, true, VHI>(g, rv + (size_t)(s0 / GS) * D * GS, pos,
+                                      (uint32_t*)c.v_codes + rec * GROUP_WORDS,
+                                      (uint16_t*)c.v_meta + rec * 2 * D, vhi);
+    }
   }
   __syncthreads();
   if (tid == 0) c.len[bh] = T + 1;
@@ -557,12 +625,11 @@ static int ring_blocks(const Geo& g, int T) {
 hipError_t launch_quant_keys(const Geo& g, const void* k, int T, kvq_cache* c, hipStream_t st) {
   const int qb = (n_quant(T, g.R) / GS + QWAVES - 1) / QWAVES;
   const dim3 grid(g.B * g.Hkv, qb + ring_blocks(g, T));
-  if (g.bf16)
-    hipLaunchKernelGGL(quant_keys_kernel<true>, grid, dim3(QTHREADS), 0, st, g,
-                       (const uint16_t*)k, T, qb, *c);
-  else
-    hipLaunchKernelGGL(quant_keys_kernel<false>, grid, dim3(QTHREADS), 0, st, g,
-                       (const uint16_t*)k, T, qb, *c);
+  const auto kern = g.bf16 ? (g.n_vhi ? quant_keys_kernel<true, true>
+                                       : quant_keys_kernel<true, false>)
+                           : (g.n_vhi ? quant_keys_kernel<false, true>
+                                       : quant_keys_kernel<false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(QTHREADS), 0, st, g, (const uint16_t*)k, T, qb, *c);
   return hipGetLastError();
 }
 

@@ -79,9 +79,10 @@ typedef struct {
                           32 <= R */
   int32_t max_tokens;  /* capacity per sequence, 1 <= max_tokens <= 2^20 */
   int32_t io_dtype;    /* KVQ_FP16 | KVQ_BF16 */
-  int32_t n_vblk_hi;   /* 0..4: 8-token blocks per 32-token group whose values
-                          take bits_vhi bits ([SemKV] abstract: two
-                          precisions chosen per token; see v_hi) */
+  int32_t n_vblk_hi;   /* 0..4: a group's 8 n_vblk_hi tokens of largest key
+                          magnitude take bits_vhi-bit values ([SemKV]
+                          abstract: two precisions chosen per token; see
+                          v_hi) */
   int32_t bits_vhi;    /* 3 or 4 when n_vblk_hi > 0 (ignored otherwise) */
 } kvq_layout;
 
@@ -127,21 +128,24 @@ typedef struct {
  *          [0] query side, [1] key side (see kvq_select_pairs).
  *  err     [1] int32: sticky error word, 0 = none; bit 0 = an append found
  *          the cache full.
- *  v_hi    n_vblk_hi > 0: [B][Hkv][NG][4 + 64 n_vblk_hi] u32.  Value
+ *  v_hi    n_vblk_hi > 0: [B][Hkv][NG][8 + 64 n_vblk_hi] u32.  Value
  *          precision by token ([SemKV] abstract: tokens ranked by a
  *          model-internal score get one of two adjacent precisions; the page
- *          names no indicator, so this is a reading): a group's four 8-token
- *          blocks (tokens 8m .. 8m+7) are ranked by
- *            E_m = sum over the block's 8 tokens and 128 channels of
- *                  min(floor(4096 |v|), 2^20)
- *          (ties to the lower block); the n_vblk_hi blocks of largest E_m
- *          quantize their values at L = 2^bits_vhi - 1 levels, the others at
- *          L = 3.  v_codes always holds the low two bits of a value code.
- *          Word 0 of a group record is the mask of the kept blocks (bit m),
- *          words 1..3 are 0, and words 4 + (j n_vblk_hi + s) 16 + c hold,
- *          in the v_codes word format, the high two bits of the codes of the
- *          s-th kept block (ascending) for channel group j.  Zero bytes when
- *          n_vblk_hi == 0.
+ *          names no indicator, so this is a reading).  A group's tokens are
+ *          ranked by their key magnitude
+ *            E_t = sum over the 128 channels of min(floor(4096 |k_t,c|), 2^20)
+ *          (descending, ties to the lower position) and stored in that order:
+ *          slot i of every key and value record of the group (the token
+ *          index of the k_lo / k_hi / v_codes / v_meta formats) holds the
+ *          token at position 32g + order[i]; attention does not depend on
+ *          the order.  Slots 0 .. 8 n_vblk_hi - 1 quantize their values at
+ *          L = 2^bits_vhi - 1 levels, the others at L = 3; v_codes always
+ *          holds the low two bits of a value code.  Words 0..7 of a group
+ *          record are the 32 order bytes (byte i = order[i]), and words
+ *          8 + (j n_vblk_hi + kq) 16 + c hold, in the v_codes word format,
+ *          the high two bits of the codes of slots 8kq .. 8kq+7
+ *          (kq < n_vblk_hi) for channel group j.  Ring tokens stay in
+ *          position order.  Zero bytes when n_vblk_hi == 0 (order = identity).
  */
 typedef struct {
   void *k_lo, *k_hi, *k_meta, *v_codes, *v_meta, *ring_k, *ring_v;
@@ -218,14 +222,19 @@ kvq_status kvq_select_pairs_qa(const kvq_layout *L, const void *q_sel,
  * Channels of the n_pairs_hi top-ranked pairs use bits_hi, those of the
  * n_pairs_lo1 lowest-ranked pairs 1 bit (L = 1), all others bits_lo.
  * Fills groups [0, n_q(T)/32), copies positions [n_q(T), T) into ring_k and
- * sets len[b][h] = T.   k: [B][Hkv][T][128], 1 <= T <= max_tokens. */
+ * sets len[b][h] = T.   k: [B][Hkv][T][128], 1 <= T <= max_tokens.  With
+ * n_vblk_hi > 0 it also ranks each group's tokens, stores the keys in that
+ * order and writes the order to v_hi (see there). */
 kvq_status kvq_quant_keys(const kvq_layout *L, const void *k, int32_t T,
                           kvq_cache *cache, void *stream);
 
 /* Value quantization at prefill ([MixKVQ] abstract, [PM-KVQ]
  * supporting_citations: per-token values).  Same quantizer as the keys over
  * each token's channel groups [32j, 32j+32) at bits_v bits.  Fills groups
- * [0, n_q(T)/32), copies positions [n_q(T), T) into ring_v, sets len = T. */
+ * [0, n_q(T)/32), copies positions [n_q(T), T) into ring_v, sets len = T.
+ * With n_vblk_hi > 0 it reads each group's token order from v_hi, which
+ * kvq_quant_keys writes: call kvq_quant_keys for the same T first (same
+ * stream, or synchronized). */
 kvq_status kvq_quant_values(const kvq_layout *L, const void *v, int32_t T,
                             kvq_cache *cache, void *stream);
 

@@ -84,7 +84,7 @@ class Case:
             "len": host(c["len"], np.int32).reshape(B, H),
             "sums": host(c["sums"], np.uint64).reshape(B, H, 2, 64),
         }
-        vw = 4 + 64 * self.w.n_vblk_hi if self.w.n_vblk_hi else 0
+        vw = 8 + 64 * self.w.n_vblk_hi if self.w.n_vblk_hi else 0
         out["v_hi"] = (host(c["v_hi"], np.uint32)[:B * H * NG * vw].reshape(B, H, NG, vw)
                        if vw and NG else np.zeros((B, H, NG, 0), np.uint32))
         return out

@@ -56,9 +56,9 @@ def test_cache_sizes_closed_form():
     ng, bh = (32768 - 128) // 32, 8
     assert s == [bh * ng * 1024, bh * ng * 128, bh * ng * 512, bh * ng * 1024, bh * ng * 512,
                  bh * 160 * 256, bh * 160 * 256, bh * 64 * 4, bh * 4, bh * 2 * 64 * 8, 4, 0]
-    # two value precisions: a 16-byte header + 256 bytes per kept 8-token block
+    # two value precisions: 32 order bytes + 256 bytes per 8 high-precision tokens
     for n in (1, 2, 4):
-        assert kvq.kvq_cache_sizes(L32k(n_vblk_hi=n, bits_vhi=3))[11] == bh * ng * (16 + 256 * n)
+        assert kvq.kvq_cache_sizes(L32k(n_vblk_hi=n, bits_vhi=3))[11] == bh * ng * (32 + 256 * n)
     # raw 16-bit salient channels: 32 tokens x 12 channels x 2 B per group
     s16 = kvq.kvq_cache_sizes(L32k(bits_hi=16))
     assert s16[1] == bh * ng * 32 * 12 * 2 + 32  # + tail slack of the 16-byte row reads

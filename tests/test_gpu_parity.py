@@ -336,3 +336,74 @@ def test_two_value_precisions_edge_lengths(T):
         check_output(got, ref, w.io_dtype, ATOL)
         if S == 1:
             check_single_split(part, ref, ATOL)
+
+
+def _plant_zeros_and_ties(d, T, seed):
+    """Keys and values with zero minima of both signs and with equal key
+    magnitudes: in every group, some key channels and value channel groups
+    are made non-negative with a -0 and a +0 planted in either order (the
+    quantizer's zero point takes the sign of the first zero by position),
+    and some tokens repeat another token's key row (equal ranking scores,
+    decided by position) or have an all-zero key row."""
+    rng = np.random.default_rng(seed)
+    k, v = d["k"].copy(), d["v"].copy()
+    B, H = k.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            for g in range(T // 32):
+                base = 32 * g
+                for c in rng.choice(128, 12, replace=False):
+                    k[b, h, base:base + 32, c] &= 0x7FFF
+                    p1, p2 = sorted(rng.choice(32, 2, replace=False))
+                    s = rng.integers(2)
+                    k[b, h, base + p1, c] = 0x8000 if s else 0x0000
+                    k[b, h, base + p2, c] = 0x0000 if s else 0x8000
+                for t in rng.choice(32, 6, replace=False):
+                    j = rng.integers(4)
+                    v[b, h, base + t, 32 * j:32 * j + 32] &= 0x7FFF
+                    p1, p2 = sorted(rng.choice(32, 2, replace=False))
+                    s = rng.integers(2)
+                    v[b, h, base + t, 32 * j + p1] = 0x8000 if s else 0x0000
+                    v[b, h, base + t, 32 * j + p2] = 0x0000 if s else 0x8000
+                a, c2, z1, z2 = rng.choice(32, 4, replace=False)
+                k[b, h, base + max(a, c2)] = k[b, h, base + min(a, c2)]
+                k[b, h, base + z1] = 0
+                k[b, h, base + z2] = 0x8000
+    out = dict(d)
+    out["k"], out["v"] = k, v
+    return out
+
+
+ZT = [
+    kvq_synth.Workload("zeros-ties-vmix", 1, 8, 2, 420, n_qry=8, io_dtype="bf16",
+                       n_pairs_hi=6, residual=32, seed=91, n_vblk_hi=2, bits_vhi=4),
+    kvq_synth.Workload("zeros-ties-fp16", 1, 8, 2, 420, n_qry=8, io_dtype="fp16",
+                       n_pairs_hi=6, residual=32, seed=92),
+]
+
+
+@pytest.mark.parametrize("w", ZT, ids=_ids)
+@pytest.mark.parametrize("path", ["prefill", "append"])
+def test_signed_zero_minima_and_tied_scores(w, path):
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    data = _plant_zeros_and_ties(kvq_synth.generate(w), w.tokens, w.seed)
+    if path == "prefill":
+        case = Case(w, data=data)
+    else:
+        T0 = 40
+        case = Case(w, T=T0, max_tokens=w.tokens, data=data)
+        for t in range(T0, w.tokens):
+            kvq.kvq_append(case.layout, dev(np.ascontiguousarray(data["k"][:, :, t])),
+                           dev(np.ascontiguousarray(data["v"][:, :, t])), case.cache.struct)
+        torch.cuda.synchronize()
+        case.T = w.tokens
+    qz = case.oracle_quant()
+    # the planted zero minima reach the oracle's zero points with both signs
+    nq = qz.nq // 32
+    assert np.any(qz.kz[:, :, :nq] == 0x8000) and np.any(qz.kz[:, :, :nq] == 0)
+    assert np.any(qz.vz[:, :, :nq] == 0x8000) and np.any(qz.vz[:, :, :nq] == 0)
+    compare_cache(case, qz, nq)
+    q = case.d["q_dec"][:, :, 0]
+    got = case.decode(q, 4)
+    check_output(got, oracle.attention(qz, q, SM_SCALE), w.io_dtype, ATOL)
