@@ -205,8 +205,10 @@ int orc_select_qa(int B, int Hq, int Hkv, int bf16, const uint16_t *q_sel,
  * contiguous in the packed layout, and the decision is per (b, kv head),
  * since the G query heads share one key cache:
  *   E_m = sum over the group's query heads h and channels c of chunk m of
- *         floor(|q_{h,c}| * 2^24)
- * The n_keep chunks of largest E_m are kept (ties to the lower m).
+ *         min(floor(4096 |q_{h,c}|), 2^20)
+ * (the fixed-point magnitude also used to rank tokens; an integer sum, exact
+ * for every 16-bit input).  The n_keep chunks of largest E_m are kept (ties
+ * to the lower m).
  * keep[(b*Hkv + kh)*4 + m] = 1 for a kept chunk, else 0. */
 int orc_prune_chunks(int B, int Hq, int Hkv, int bf16, const uint16_t *q, int n_keep,
                      uint8_t *keep) {
@@ -217,8 +219,8 @@ int orc_prune_chunks(int B, int Hq, int Hkv, int bf16, const uint16_t *q, int n_
       uint64_t E[4] = {0, 0, 0, 0};
       for (int h = kh * G; h < kh * G + G; h++)
         for (int c = 0; c < D; c++) {
-          double x = fabs(to_f64(q[((size_t)b * Hq + h) * D + c], bf16));
-          E[c / 32] += (uint64_t)floor(x * 16777216.0);
+          double u = floor(4096.0 * fabs(to_f64(q[((size_t)b * Hq + h) * D + c], bf16)));
+          E[c / 32] += (uint64_t)(u < 1048576.0 ? u : 1048576.0);
         }
       for (int m = 0; m < 4; m++) {
         int rank = 0;

@@ -2,14 +2,16 @@
 keep a decode query's few large channels, drop the many small ones, and read
 the key cache only for the kept ones).  The page gives no rule; the reading
 keeps, per (b, kv head), the n_keep of the four 32-channel key chunks with
-the largest summed |q| over the group's heads (fixed point, ties to the lower
-chunk), and every logit sums q_c k^_c over the kept channels only.
+the largest summed |q| over the group's heads (fixed point: min(floor(4096
+|q|), 2^20) per value; ties to the lower chunk), and every logit sums
+q_c k^_c over the kept channels only.
 
 * Selection: the kept set is the top n_keep by a plain float64 sum of |q|
-  wherever that sum separates the chunks; it does not change when q is
-  doubled, when heads are permuted inside a group or channels inside a
-  chunk; a planted chunk is kept first; an all-zero query keeps chunks
-  0 .. n_keep-1; the kept sets are nested in n_keep.
+  wherever that sum separates the chunks; it does not change when heads are
+  permuted inside a group or channels inside a chunk, nor when q is doubled
+  for values whose fixed-point form is exact (multiples of 1/4096); a planted
+  chunk is kept first; an all-zero query keeps chunks 0 .. n_keep-1; a
+  query far beyond the cap still ranks; the kept sets are nested in n_keep.
 * Attention: n_keep = 4 is unpruned attention, bit for bit; otherwise it
   equals textbook softmax attention whose logits use only the kept channels'
   columns of the key matrix, rebuilt from the packed bytes by the brute-force
@@ -47,7 +49,8 @@ def test_selection_matches_float_sums_where_separated(data):
                 e = qf[b, kh * G:(kh + 1) * G].reshape(G, 4, 32).sum(axis=(0, 2))
                 order = np.argsort(-e, kind="stable")
                 srt = e[order]
-                if srt[n_keep - 1] - srt[n_keep] < 1e-6 * srt[0]:
+                # the fixed point drops under 1/4096 per value: 1/32 per chunk and head
+                if srt[n_keep - 1] - srt[n_keep] < G / 16:
                     continue  # too close for a float sum to decide
                 want = np.zeros(4, bool)
                 want[order[:n_keep]] = True
@@ -65,7 +68,13 @@ def test_selection_invariances(data):
     hp = np.concatenate([kh * G + rng.permutation(G) for kh in range(W.n_kv_heads)])
     cp = np.concatenate([32 * m + rng.permutation(32) for m in range(4)])
     q2 = q[:, hp][:, :, cp]
-    q3 = kvq_synth.to_bits(2 * qf, W.io_dtype)  # exact for bf16 values of this data
+    # doubling: values rounded to multiples of 1/4096 (and below the cap)
+    qr = np.clip(np.round(qf * 4096) / 4096, -100, 100)
+    q = kvq_synth.to_bits(qr, W.io_dtype)
+    assert np.array_equal(kvq_synth.bits_to_f64(q, W.io_dtype) * 4096,
+                          np.round(kvq_synth.bits_to_f64(q, W.io_dtype) * 4096))
+    q2 = q[:, hp][:, :, cp]
+    q3 = kvq_synth.to_bits(2 * kvq_synth.bits_to_f64(q, W.io_dtype), W.io_dtype)
     for n_keep in (1, 2, 3, 4):
         k0 = oracle.prune_chunks(q, W.n_kv_heads, W.io_dtype, n_keep)
         assert np.array_equal(k0, oracle.prune_chunks(q2, W.n_kv_heads, W.io_dtype, n_keep))
@@ -90,6 +99,14 @@ def test_planted_chunk_and_zero_query(data):
     for n_keep in (1, 2, 3):
         keep = oracle.prune_chunks(zero, W.n_kv_heads, W.io_dtype, n_keep)
         assert np.all(keep == (np.arange(4) < n_keep))
+    # huge values: every one capped at 2^20 / 4096 = 256; the chunk with the
+    # most of them wins, whatever their size beyond the cap
+    big = np.zeros((1, W.group_size, 128))
+    big[0, :, 32 * 2:32 * 2 + 3] = 1e30
+    big[0, :, 32 * 1:32 * 1 + 2] = 3e38
+    big[0, :, 32 * 3] = 1000.0
+    keep = oracle.prune_chunks(kvq_synth.to_bits(big, "bf16"), 1, "bf16", 1)
+    assert np.array_equal(keep[0, 0], [False, False, True, False])
 
 
 def _quantized(data):
