@@ -257,7 +257,7 @@ struct Lds {
 // KEEP < 4: query-channel pruning (Dual-QK, abstract: a decode query keeps
 // its few large channels and the key cache is read only for them).  Per
 // (sequence, KV head) the KEEP 32-channel key chunks of largest
-// sum over the group's heads of floor(|q_c| * 2^24) are kept (ties to the
+// sum over the group's heads of min(floor(4096 |q_c|), 2^20) are kept (ties to the
 // lower chunk); the query is zero on the others, whose key codes and
 // scale/zero are not read (past the first PF prefetched groups, which are
 // issued before the query arrives): their lanes load a kept chunk's words
@@ -327,36 +327,38 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // a ring block is worked on first, while the group stream warms up.
   const int ring0 = ((first - ngq) % STR + STR) % STR;
 
-  // kept key chunks (all four unless PRUNE); every lane computes the same mask
+  // kept key chunks (all four unless PRUNE), a wave-uniform mask: E_m sums
+  // min(floor(4096 |q|), 2^20) over chunk m's 32 channels and the G heads
+  // (at most 2^29, exact in 32 bits); the 16 lanes of chunk kq are DPP row kq
   uint32_t kmask = 0xFu;
   if constexpr (PRUNE) {
-    double e = 0.0;  // exact: 32 terms, each an integer below 2^24 * |q|
+    uint32_t e = 0;
     if (hvalid) {
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int w = 0; w < 4; w++) {
-          const uint32_t x = qv[i][w];
-          e += floor((double)fabsf(in_to_f32((uint16_t)(x & 0xFFFF), BF16)) * 16777216.0);
-          e += floor((double)fabsf(in_to_f32((uint16_t)(x >> 16), BF16)) * 16777216.0);
+          const uint32_t x = qv[i][w];  // 4096 |q| is exact; the conversion truncates
+          e += (uint32_t)fminf(4096.0f * fabsf(in_to_f32((uint16_t)(x & 0xFFFF), BF16)),
+                               1048576.0f);
+          e += (uint32_t)fminf(4096.0f * fabsf(in_to_f32((uint16_t)(x >> 16), BF16)), 1048576.0f);
         }
     }
-    uint64_t E = (uint64_t)e;
+    e += (uint32_t)__builtin_amdgcn_update_dpp((int)e, (int)e, 0x128, 0xF, 0xF, false);  // row_ror:8
+    e += (uint32_t)__builtin_amdgcn_update_dpp((int)e, (int)e, 0x124, 0xF, 0xF, false);  // row_ror:4
+    e += (uint32_t)__builtin_amdgcn_update_dpp((int)e, (int)e, 0x122, 0xF, 0xF, false);  // row_ror:2
+    e += (uint32_t)__builtin_amdgcn_update_dpp((int)e, (int)e, 0x121, 0xF, 0xF, false);  // row_ror:1
+    uint32_t E[4];
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {  // the 16 lanes of chunk kq (heads col)
-      const uint32_t lo = __shfl_xor((uint32_t)E, o), hi = __shfl_xor((uint32_t)(E >> 32), o);
-      E += (uint64_t)lo | ((uint64_t)hi << 32);
-    }
-    int rank = 0;
+    for (int m = 0; m < 4; m++) E[m] = (uint32_t)__builtin_amdgcn_readlane((int)e, 16 * m);
+    kmask = 0;
 #pragma unroll
     for (int m = 0; m < 4; m++) {
-      const uint32_t lo = __shfl((uint32_t)E, 16 * m), hi = __shfl((uint32_t)(E >> 32), 16 * m);
-      const uint64_t Em = (uint64_t)lo | ((uint64_t)hi << 32);
-      rank += (Em > E) || (Em == E && m < kq);
+      int rank = 0;
+#pragma unroll
+      for (int i = 0; i < 4; i++) rank += (E[i] > E[m]) || (E[i] == E[m] && i < m);
+      if (rank < KEEP) kmask |= 1u << m;
     }
-    const uint64_t bal = __ballot(rank < KEEP);
-    kmask = __builtin_amdgcn_readfirstlane(
-        (uint32_t)((bal & 1u) | ((bal >> 15) & 2u) | ((bal >> 30) & 4u) | ((bal >> 45) & 8u)));
     if (!((kmask >> kq) & 1u)) {
 #pragma unroll
       for (int i = 0; i < 4; i++) qv[i] = u4{0, 0, 0, 0};

@@ -34,6 +34,10 @@ template <int CTRL>
 __device__ inline uint32_t dpp(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
 }
+template <int CTRL>  // row_* controls (rotations within a 16-lane row)
+__device__ inline uint32_t dpp_row(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
 constexpr int QUAD_XOR1 = 0xB1;  // quad_perm [1, 0, 3, 2]
 constexpr int QUAD_XOR2 = 0x4E;  // quad_perm [2, 3, 0, 1]
 template <int K>
@@ -148,9 +152,16 @@ __device__ inline PairMasks pair_masks(const Geo& g, const int32_t* pr) {
 // ------------------------------------------------------------- key group
 
 struct KeyLds {  // one wave's staging of a key-group record
-  uint32_t lo[GROUP_WORDS];
-  uint32_t hi[256];  // 4-bit: 32 words; raw 16-bit: 32 tokens x up to 16 halves
-  uint32_t ord[8];   // two value precisions: the group's order bytes (slot -> position)
+  union {
+    struct {
+      uint32_t lo[GROUP_WORDS];
+      uint32_t hi[256];  // 4-bit: 32 words; raw 16-bit: 32 tokens x up to 16 halves
+    };
+    // two value precisions, before the record is staged: the group's 32 key
+    // rows (16-byte pieces [row][cb]), then the partial scores [4][32]
+    uint32_t tile[GS * 16 * 4 + 4 * GS];
+  };
+  uint32_t ord[8];  // two value precisions: the group's order bytes (slot -> position)
 };
 
 // Token order of one group for two value precisions by token (the SemKV
@@ -162,6 +173,27 @@ struct KeyLds {  // one wave's staging of a key-group record
 // its token against the 32 sums read back from lanes 2a.  Writes order
 // bytes (ord[rank(t)] = t) to LDS; the caller syncs before reading them.
 template <bool BF>
+__device__ inline uint32_t key_score(const uint4& v) {  // 8 channels of one token
+  uint32_t e = 0;
+#pragma unroll
+  for (int k = 0; k < 8; k++)  // 4096 |x| is exact; the conversion truncates
+    e += (uint32_t)fminf(4096.0f * fabsf(in_to_f32(half_of(v, k), BF)), 1048576.0f);
+  return e;
+}
+
+// Writes ord[rank(t)] = t for the token whose score e lanes t < 32 hold.
+__device__ inline void order_from_scores(uint32_t e, uint32_t* ord) {
+  const int lane = threadIdx.x & 63;
+  uint32_t rank = 0;
+#pragma unroll
+  for (int a = 0; a < GS; a++) {
+    const uint32_t ea = __builtin_amdgcn_readlane(e, a);
+    rank += (ea > e) || (ea == e && a < lane);
+  }
+  if (lane < GS) ((uint8_t*)ord)[rank] = (uint8_t)lane;
+}
+
+template <bool BF>
 __device__ void token_order_wave(const uint16_t* rows, uint32_t* ord) {
   const int lane = threadIdx.x & 63, t = lane >> 1, h = lane & 1;
   uint4 v[8];
@@ -169,38 +201,56 @@ __device__ void token_order_wave(const uint16_t* rows, uint32_t* ord) {
   for (int i = 0; i < 8; i++) v[i] = *(const uint4*)(rows + (size_t)t * D + 64 * h + 8 * i);
   uint32_t e = 0;
 #pragma unroll
-  for (int i = 0; i < 8; i++)
-#pragma unroll
-    for (int k = 0; k < 8; k++)  // 4096 |x| is exact; the conversion truncates
-      e += (uint32_t)fminf(4096.0f * fabsf(in_to_f32(half_of(v[i], k), BF)), 1048576.0f);
+  for (int i = 0; i < 8; i++) e += key_score<BF>(v[i]);
   e += dpp<QUAD_XOR1>(e);
-  uint32_t rank = 0;
-#pragma unroll
-  for (int a = 0; a < GS; a++) {
-    const uint32_t ea = __builtin_amdgcn_readlane(e, 2 * a);
-    rank += (ea > e) || (ea == e && a < t);
-  }
-  if (h == 0) ((uint8_t*)ord)[rank] = (uint8_t)t;
+  // token t's score to lane t
+  e = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((2 * lane) & 63), (int)e);
+  order_from_scores(e, ord);
 }
 
 // rows: token 0 of the group, row stride D (prefill input or ring_k slots).
-// VHI: the tokens are taken in the order held in L.ord (slot i = position
-// L.ord[i]), so the record's token index is the slot.
+// VHI: the wave first ranks the group's tokens (token_order_wave's scores,
+// summed from the rows it holds), writes the order bytes to L.ord and takes
+// the rows in that order through the LDS tile, so the record's token index
+// is the slot (slot i = position L.ord[i]).
 template <bool BF, bool VHI>
 __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
                                uint32_t* lo_out, uint8_t* hi_out, uint16_t* meta_out,
                                KeyLds& L) {
   const int lane = threadIdx.x & 63, cb = lane >> 2, tq = lane & 3;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) v[i] = *(const uint4*)(rows + (size_t)(8 * tq + i) * D + 8 * cb);
   // positions of the lane's slots 8tq .. 8tq+7, one byte each
   uint2 pos = make_uint2(0, 0);
-  if constexpr (VHI) pos = ((const uint2*)L.ord)[tq];
+  if constexpr (VHI) {
+    uint4* tile = (uint4*)L.tile;
+    uint32_t* rs = L.tile + GS * 16 * 4;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      // the lane's 8 channels, then the 4 channel blocks of its DPP row
+      uint32_t e = key_score<BF>(v[i]);
+      e += dpp_row<0x124>(e);  // row_ror:4 (same tq, next cb)
+      e += dpp_row<0x128>(e);  // row_ror:8
+      if ((cb & 3) == 0) rs[(cb >> 2) * GS + 8 * tq + i] = e;
+      tile[(8 * tq + i) * 16 + cb] = v[i];
+    }
+    wave_lds_sync();
+    const int t = lane & (GS - 1);
+    order_from_scores(rs[t] + rs[GS + t] + rs[2 * GS + t] + rs[3 * GS + t], L.ord);
+    wave_lds_sync();
+    pos = ((const uint2*)L.ord)[tq];
+  }
   auto pos_of = [&](int i) -> uint32_t {
     if constexpr (VHI) return ((i < 4 ? pos.x : pos.y) >> (8 * (i & 3))) & 0xFFu;
     return 8 * tq + i;
   };
-  uint4 v[8];
+  if constexpr (VHI) {
+    const uint4* tile = (const uint4*)L.tile;
 #pragma unroll
-  for (int i = 0; i < 8; i++) v[i] = *(const uint4*)(rows + (size_t)pos_of(i) * D + 8 * cb);
+    for (int i = 0; i < 8; i++) v[i] = tile[pos_of(i) * 16 + cb];
+    wave_lds_sync();  // the tile's space is reused for the record below
+  }
 
   const bool bits4 = g.nh > 0 && g.bits_hi == 4, raw16 = g.nh > 0 && g.bits_hi == 16;
   // bit allocation of the lane's channels 8cb + k
@@ -515,8 +565,8 @@ __device__ void ring_fill(const Geo& g, const uint16_t* __restrict__ x, int T, i
 
 // grid (B * Hkv, qblocks + ring blocks): blocks below qblocks quantize
 // QWAVES groups, one per wave; the rest fill the ring.
-// VHI: each wave first ranks its group's tokens, writes the order to the
-// group's v_hi header and packs the keys in that order.
+// VHI: each wave ranks its group's tokens, packs the keys in that order and
+// writes the order to the group's v_hi header.
 template <bool BF, bool VHI>
 __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint16_t* __restrict__ k,
                                                               int T, int qblocks, kvq_cache c) {
@@ -529,16 +579,13 @@ __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint1
   const int grp = blockIdx.y * QWAVES + wave;
   if (grp >= n_quant(T, g.R) / GS) return;
   const size_t rec = (size_t)bh * g.NG + grp;
-  const uint16_t* rows = k + ((size_t)bh * T + (size_t)grp * GS) * D;
-  if constexpr (VHI) {
-    token_order_wave<BF>(rows, lds[wave].ord);
-    wave_lds_sync();
-    if (lane < 2) ((uint4*)(c.v_hi + rec * g.vhi_words))[lane] = ((const uint4*)lds[wave].ord)[lane];
-  }
-  key_group_wave<BF, VHI>(g, rows, pair_masks(g, c.pairs + (size_t)bh * NPAIR),
+  key_group_wave<BF, VHI>(g, k + ((size_t)bh * T + (size_t)grp * GS) * D,
+                          pair_masks(g, c.pairs + (size_t)bh * NPAIR),
                           (uint32_t*)c.k_lo + rec * GROUP_WORDS,
                           (uint8_t*)c.k_hi + rec * g.khi_bytes, (uint16_t*)c.k_meta + rec * 2 * D,
                           lds[wave]);
+  if constexpr (VHI)
+    if (lane < 2) ((uint4*)(c.v_hi + rec * g.vhi_words))[lane] = ((const uint4*)lds[wave].ord)[lane];
 }
 
 // VHI: the group's token order comes from the v_hi header that the key
@@ -593,15 +640,12 @@ __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __re
     const size_t rec = (size_t)bh * g.NG + grp;
     uint32_t* vhi = c.v_hi + rec * g.vhi_words;
     if (tid < 64) {
-      if constexpr (VHI) {
-        token_order_wave<BF>(rk + (size_t)s0 * D, lds.ord);
-        wave_lds_sync();
-        if (tid < 2) ((uint4*)vhi)[tid] = ((const uint4*)lds.ord)[tid];
-      }
       key_group_wave<BF, VHI>(g, rk + (size_t)s0 * D, pair_masks(g, c.pairs + (size_t)bh * NPAIR),
                               (uint32_t*)c.k_lo + rec * GROUP_WORDS,
                               (uint8_t*)c.k_hi + rec * g.khi_bytes,
                               (uint16_t*)c.k_meta + rec * 2 * D, lds);
+      if constexpr (VHI)
+        if (tid < 2) ((uint4*)vhi)[tid] = ((const uint4*)lds.ord)[tid];
     } else {
       uint2 pos = make_uint2(0, 0);
       if constexpr (VHI) {

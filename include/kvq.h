@@ -290,8 +290,9 @@ kvq_status kvq_decode_attn(const kvq_layout *L, const void *q,
  * four 32-channel key chunks (channels 32m .. 32m+31: the contiguous runs of
  * k_lo, k_meta and ring_k) with the largest
  *   E_m = sum over the group's query heads h and channels c of chunk m of
- *         floor(|q[h][c]| * 2^24)
- * are kept (ties to the lower m), and every logit sums q[h][c] * k^[t][c]
+ *         min(floor(4096 |q[h][c]|), 2^20)
+ * (exact in 32 bits for every 16-bit query) are kept (ties to the lower m),
+ * and every logit sums q[h][c] * k^[t][c]
  * over the kept channels only, for quantized and ring tokens alike (the
  * query is zero on the pruned channels).  Past a split's first prefetched
  * groups the pruned chunks' key codes and key scale/zero are not read.

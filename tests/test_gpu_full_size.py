@@ -156,3 +156,40 @@ def test_llama3_8b_32k_two_value_precisions():
     S = bench.default_splits(w)
     err = check_output(case.decode(q, S), ref, w.io_dtype, ATOL)
     print("%s v2@4 S=%d max|err| %.3g" % (w.name, S, err))
+
+
+@pytest.mark.timeout(600)
+def test_maximum_context_append_to_capacity():
+    # the largest capacity a layout accepts (2^20 tokens per sequence): prefill
+    # one token short, append the last one (it completes a group, which is
+    # packed from the ring), then one more append must report a full cache
+    from decode_attention_select_amd import kvq
+    T = 1 << 20
+    w = kvq_synth.Workload("max-context-1m", 1, 4, 1, T, n_qry=8, io_dtype="bf16",
+                           outliers="pct2x10", n_pairs_hi=6, residual=128, seed=95)
+    print("case", w.name, flush=True)
+    case = Case(w, T=T - 1, max_tokens=T)
+    pairs = check_selection(case)
+    assert oracle.n_quant(T, w.residual) > oracle.n_quant(T - 1, w.residual)
+    kvq.kvq_append(case.layout, dev(np.ascontiguousarray(case.d["k"][:, :, T - 1])),
+                   dev(np.ascontiguousarray(case.d["v"][:, :, T - 1])), case.cache.struct)
+    assert kvq.kvq_check(case.cache.struct) == 0
+    case.T = T
+    qz = case.oracle_quant(pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
+    q = case.d["q_dec"][:, :, 0]
+    ref = oracle.attention(qz, q, SM_SCALE)
+    S = bench.default_splits(w)
+    got = case.decode(q, S)
+    err = check_output(got, ref, w.io_dtype, ATOL)
+    # the averaged outputs are small here, so also bound the relative error:
+    # bf16 output rounding is at most 2^-9 relative, fp16 weights 2^-11
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    assert rel < 5e-3, rel
+    print("%s S=%d max|err| %.3g max|o| %.3g rel-L2 %.3g" % (w.name, S, err, np.abs(ref).max(),
+                                                           rel), flush=True)
+    # a full cache: the next append sets the error bit and leaves len alone
+    kvq.kvq_append(case.layout, dev(np.ascontiguousarray(case.d["k"][:, :, T - 1])),
+                   dev(np.ascontiguousarray(case.d["v"][:, :, T - 1])), case.cache.struct)
+    assert kvq.kvq_check(case.cache.struct) != 0
+    assert np.all(case.gpu_bytes()["len"] == T)
