@@ -306,7 +306,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   }
 
   // scalar loads: the length and the 8 leading ranks
-  const int T = c.len[bh];
+  const int T = min(max(c.len[bh], 0), g.max_tokens);  // reads stay inside the cache
   int top[8];
   if constexpr (HIMODE != 0) {
     const int32_t* pr = c.pairs + (size_t)bh * NPAIR;

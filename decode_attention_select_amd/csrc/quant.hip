@@ -589,7 +589,9 @@ __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint1
 }
 
 // VHI: the group's token order comes from the v_hi header that the key
-// kernel wrote (an earlier launch on the same stream).
+// kernel wrote (an earlier launch on the same stream).  Its bytes are masked
+// to 0..31, so a header the key kernel never wrote cannot move a load out
+// of the group.
 template <bool BF, bool VHI>
 __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uint16_t* __restrict__ v,
                                                                 int T, int qblocks, kvq_cache c) {
@@ -603,7 +605,11 @@ __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uin
   const size_t rec = (size_t)bh * g.NG + grp;
   uint32_t* vhi = c.v_hi + rec * g.vhi_words;
   uint2 pos = make_uint2(0, 0);
-  if constexpr (VHI) pos = ((const uint2*)vhi)[tq];
+  if constexpr (VHI) {
+    pos = ((const uint2*)vhi)[tq];
+    pos.x &= 0x1F1F1F1Fu;
+    pos.y &= 0x1F1F1F1Fu;
+  }
   value_group_wave<BF, false, VHI>(g, v + ((size_t)bh * T + (size_t)grp * GS) * D, pos,
                                    (uint32_t*)c.v_codes + rec * GROUP_WORDS,
                                    (uint16_t*)c.v_meta + rec * 2 * D, vhi);
@@ -624,8 +630,8 @@ __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __re
   __shared__ __align__(16) uint32_t vord[8];
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int T = c.len[bh];
-  if (T >= g.max_tokens) {
-    if (tid == 0) atomicOr(c.err, 1);
+  if (T < 0 || T >= g.max_tokens) {  // full, or a length no call of this library wrote
+    if (tid == 0) atomicOr(c.err, T < 0 ? 2 : 1);
     return;
   }
   uint16_t* rk = (uint16_t*)c.ring_k + (size_t)bh * g.RS * D;

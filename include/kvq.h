@@ -127,7 +127,8 @@ typedef struct {
  *  sums    [B][Hkv][2][64] uint64: fixed-point saliency sums per pair id,
  *          [0] query side, [1] key side (see kvq_select_pairs).
  *  err     [1] int32: sticky error word, 0 = none; bit 0 = an append found
- *          the cache full.
+ *          the cache full; bit 1 = an append found a negative len (a cache
+ *          no prefill or zero-fill initialized).
  *  v_hi    n_vblk_hi > 0: [B][Hkv][NG][8 + 64 n_vblk_hi] u32.  Value
  *          precision by token ([SemKV] abstract: tokens ranked by a
  *          model-internal score get one of two adjacent precisions; the page
@@ -234,7 +235,8 @@ kvq_status kvq_quant_keys(const kvq_layout *L, const void *k, int32_t T,
  * [0, n_q(T)/32), copies positions [n_q(T), T) into ring_v, sets len = T.
  * With n_vblk_hi > 0 it reads each group's token order from v_hi, which
  * kvq_quant_keys writes: call kvq_quant_keys for the same T first (same
- * stream, or synchronized). */
+ * stream, or synchronized).  Otherwise the value records are unspecified
+ * (every read still stays inside the group's input rows). */
 kvq_status kvq_quant_values(const kvq_layout *L, const void *v, int32_t T,
                             kvq_cache *cache, void *stream);
 
@@ -274,7 +276,9 @@ kvq_status kvq_shrink(const kvq_layout *L, kvq_cache *cache, int32_t g0,
  * (b, kv head) (limits as for kvq_workspace_bytes), each reduced with an
  * online softmax; a log-sum-exp combine merges them inside the same launch.
  * Computation is fp32 with fp16 matrix operands; the result is rounded to
- * the io dtype (nearest even).  Requires T >= 1 (T = 0 writes zeros).
+ * the io dtype (nearest even).  Requires T >= 1 (T = 0 writes zeros); a
+ * len outside [0, max_tokens] is clamped into it (the result is then
+ * unspecified, but every read stays inside the cache).
  *   q   [B][Hq][128] io dtype;  out [B][Hq][128] io dtype
  *   workspace: >= kvq_workspace_bytes(L, n_splits) bytes (else
  *   KVQ_ECAPACITY), zero-filled before its first use. */

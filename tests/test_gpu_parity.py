@@ -407,3 +407,36 @@ def test_signed_zero_minima_and_tied_scores(w, path):
     q = case.d["q_dec"][:, :, 0]
     got = case.decode(q, 4)
     check_output(got, oracle.attention(qz, q, SM_SCALE), w.io_dtype, ATOL)
+
+
+def test_state_no_call_wrote_stays_in_bounds():
+    # a length beyond the capacity decodes as the capacity; a negative one is
+    # reported by append and decodes as an empty cache
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    w = kvq_synth.Workload("cap", 1, 4, 1, 96, n_qry=4, io_dtype="bf16", residual=32, seed=33)
+    case = Case(w, T=96, max_tokens=96)
+    q = case.d["q_dec"][:, :, 0]
+    want = case.decode(q, 3)
+    lens = case.cache["len"].view(torch.int32)
+    lens.fill_(96 + 1000)
+    assert np.array_equal(case.decode(q, 3), want)
+    lens.fill_(-5)
+    z = dev(np.zeros((1, 1, 128), np.uint16))
+    kvq.kvq_append(case.layout, z, z, case.cache.struct)
+    assert kvq.kvq_check(case.cache.struct) == 2
+    assert np.all(case.gpu_bytes()["len"] == -5)
+    assert np.all(case.decode(q, 3) == 0)
+    # two value precisions: values quantized over order bytes no key pass
+    # wrote (0xFF) read inside their group; the usual order then gives the
+    # oracle's bytes
+    wv = VMIX[0]
+    cv = Case(wv)
+    cv.cache["v_hi"].fill_(0xFF)
+    kvq.kvq_quant_values(cv.layout, dev(cv.d["v"][:, :, :cv.T]), cv.T, cv.cache.struct)
+    torch.cuda.synchronize()
+    kvq.kvq_quant_keys(cv.layout, dev(cv.d["k"][:, :, :cv.T]), cv.T, cv.cache.struct)
+    kvq.kvq_quant_values(cv.layout, dev(cv.d["v"][:, :, :cv.T]), cv.T, cv.cache.struct)
+    torch.cuda.synchronize()
+    qz = cv.oracle_quant()
+    compare_cache(cv, qz, qz.nq // 32)
