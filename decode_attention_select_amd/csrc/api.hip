@@ -189,7 +189,6 @@ static kvq_status decode_common(const kvq_layout* L, const void* q, const kvq_ca
   if (ws_bytes < need) return KVQ_ECAPACITY;
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_EINVAL;
   if (keep < 1 || keep > 4) return KVQ_EINVAL;
-  if (keep < 4 && g.n_vhi > 0) return KVQ_ENOTSUP;  // pruning with two value precisions
   if (kvq_status s = check_ptr(q)) return s;
   if (kvq_status s = check_ptr(out)) return s;
   if (kvq_status s = check_ptr(workspace)) return s;

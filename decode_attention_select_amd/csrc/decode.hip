@@ -888,26 +888,29 @@ static void launch_one(const Geo& g, const void* q, const kvq_cache* c, float sc
                        scale_log2, S, ws, (uint16_t*)out);
 }
 
-template <bool BF16, int HIMODE, bool LO1>
+template <bool BF16, int HIMODE, bool LO1, bool VHI>
 static void launch_keep(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
                         int keep, const Ws& ws, void* out, hipStream_t st) {
-  if (g.n_vhi > 0) {  // two value precisions: unpruned only (checked by the caller)
-    launch_one<BF16, HIMODE, LO1, 4, true>(g, q, c, scale_log2, S, ws, out, st);
-    return;
-  }
   switch (keep) {
-    case 1: launch_one<BF16, HIMODE, LO1, 1>(g, q, c, scale_log2, S, ws, out, st); break;
-    case 2: launch_one<BF16, HIMODE, LO1, 2>(g, q, c, scale_log2, S, ws, out, st); break;
-    case 3: launch_one<BF16, HIMODE, LO1, 3>(g, q, c, scale_log2, S, ws, out, st); break;
-    default: launch_one<BF16, HIMODE, LO1, 4>(g, q, c, scale_log2, S, ws, out, st); break;
+    case 1: launch_one<BF16, HIMODE, LO1, 1, VHI>(g, q, c, scale_log2, S, ws, out, st); break;
+    case 2: launch_one<BF16, HIMODE, LO1, 2, VHI>(g, q, c, scale_log2, S, ws, out, st); break;
+    case 3: launch_one<BF16, HIMODE, LO1, 3, VHI>(g, q, c, scale_log2, S, ws, out, st); break;
+    default: launch_one<BF16, HIMODE, LO1, 4, VHI>(g, q, c, scale_log2, S, ws, out, st); break;
   }
 }
 
+// Two value precisions touch only the value side and pruning only the key
+// side, so every combination has its own kernel.
 template <bool BF16, int HIMODE>
 static void launch_lo1(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
                        int keep, const Ws& ws, void* out, hipStream_t st) {
-  if (g.n_lo1 > 0) launch_keep<BF16, HIMODE, true>(g, q, c, scale_log2, S, keep, ws, out, st);
-  else launch_keep<BF16, HIMODE, false>(g, q, c, scale_log2, S, keep, ws, out, st);
+  if (g.n_lo1 > 0) {
+    if (g.n_vhi > 0) launch_keep<BF16, HIMODE, true, true>(g, q, c, scale_log2, S, keep, ws, out, st);
+    else launch_keep<BF16, HIMODE, true, false>(g, q, c, scale_log2, S, keep, ws, out, st);
+  } else {
+    if (g.n_vhi > 0) launch_keep<BF16, HIMODE, false, true>(g, q, c, scale_log2, S, keep, ws, out, st);
+    else launch_keep<BF16, HIMODE, false, false>(g, q, c, scale_log2, S, keep, ws, out, st);
+  }
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {

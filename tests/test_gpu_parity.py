@@ -308,16 +308,17 @@ def test_two_value_precisions_append_equals_prefill():
     compare_cache(case, qz, qz.nq // 32)
 
 
-def test_two_value_precisions_reject_pruning():
-    from decode_attention_select_amd import kvq
-    from tests._gpu_case import dev
-    case = Case(VMIX[0])
-    ws = torch.zeros(kvq.kvq_workspace_bytes(case.layout, 4), dtype=torch.uint8, device="cuda")
-    out = torch.empty((1, 8, 128), dtype=torch.int16, device="cuda")
-    with pytest.raises(kvq.KvqError) as e:
-        kvq.kvq_decode_attn_pruned(case.layout, dev(case.d["q_dec"][:, :, 0]), case.cache.struct,
-                                   SM_SCALE, 4, 2, ws, out)
-    assert e.value.status == -2
+@pytest.mark.parametrize("w", VMIX, ids=_ids)
+def test_two_value_precisions_with_pruned_decode(w):
+    # pruning touches only the key side, the high value digits only the value
+    # side: the pruned oracle over the two-precision cache
+    case = Case(w)
+    qz = case.oracle_quant()
+    q = case.d["q_dec"][:, :, 0]
+    for n_keep in (1, 2, 3):
+        ref = oracle.attention_pruned(qz, q, SM_SCALE, n_keep)
+        for S in (1, 6):
+            check_output(case.decode_pruned(q, S, n_keep), ref, w.io_dtype, ATOL)
 
 
 @pytest.mark.parametrize("T", [1, 33, 95, 161])
