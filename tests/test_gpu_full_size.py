@@ -193,3 +193,19 @@ def test_maximum_context_append_to_capacity():
                    dev(np.ascontiguousarray(case.d["v"][:, :, T - 1])), case.cache.struct)
     assert kvq.kvq_check(case.cache.struct) != 0
     assert np.all(case.gpu_bytes()["len"] == T)
+
+
+@pytest.mark.timeout(400)
+def test_llama3_8b_32k_fp16():
+    # the same layer with fp16 inputs and outputs: every byte, every output
+    w = kvq_synth.workload("llama3-8b-32k").replace(io_dtype="fp16", seed=1096)
+    print("case", w.name, "fp16", flush=True)
+    case = Case(w)
+    pairs = check_selection(case)
+    qz = case.oracle_quant(pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
+    q = case.d["q_dec"][:, :, 0]
+    ref = oracle.attention(qz, q, SM_SCALE)
+    S = bench.default_splits(w)
+    err = check_output(case.decode(q, S), ref, w.io_dtype, ATOL)
+    print("%s fp16 S=%d max|err| %.3g max|o| %.3g" % (w.name, S, err, np.abs(ref).max()))
