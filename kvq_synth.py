@@ -52,7 +52,7 @@ class Workload:
     residual: int = 128
     n_splits: int = 0        # 0 = library default
     seed: int = 0
-    n_vblk_hi: int = 0       # 8-token value blocks per group at bits_vhi bits
+    n_vblk_hi: int = 0       # per group, 8 * n_vblk_hi tokens (largest keys) get bits_vhi-bit values
     bits_vhi: int = 4
 
     @property

@@ -278,8 +278,9 @@ VMIX = [
 
 @pytest.mark.parametrize("w", VMIX, ids=_ids)
 def test_two_value_precisions_bit_exact_and_decode(w):
-    # SemKV reading: kept 8-token blocks at 3 or 4 bits; bytes (with the
-    # high-digit records) equal the oracle's, decoding matches its attention
+    # SemKV reading: each group's 8 n tokens of largest key magnitude, stored
+    # first, at 3 or 4 bits; bytes (order headers and high digits included)
+    # equal the oracle's, decoding matches its attention
     case = Case(w)
     qz = case.oracle_quant()
     compare_cache(case, qz, qz.nq // 32)
