@@ -209,3 +209,76 @@ def test_llama3_8b_32k_fp16():
     S = bench.default_splits(w)
     err = check_output(case.decode(q, S), ref, w.io_dtype, ATOL)
     print("%s fp16 S=%d max|err| %.3g max|o| %.3g" % (w.name, S, err, np.abs(ref).max()))
+
+
+@pytest.mark.timeout(600)
+def test_batch_with_offsets_beyond_4gib():
+    # 32 sequences x 8 KV heads x 128K tokens: the key and value inputs are
+    # 8.6 GB each and the cache 3.4 GB, so byte offsets pass 2^32.  Inputs
+    # are seeded N(0,1) drawn on the GPU; the oracle checks the first and the
+    # last (sequence, KV head) on their own slices (every quantity is per
+    # (sequence, KV head)): ranks and sums, every cache byte, the outputs.
+    import torch
+    from decode_attention_select_amd import kvq
+    B, Hq, Hkv, T, NQ, R = 32, 32, 8, 1 << 17, 8, 128
+    G, NG, RS = Hq // Hkv, (T - R) // 32, R + 32
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+
+    def rnd(shape):
+        t = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        for i in range(shape[0]):
+            t[i] = torch.randn(shape[1:], generator=gen, device="cuda").to(torch.bfloat16)
+        return t.view(torch.int16)
+
+    k, v = rnd((B, Hkv, T, 128)), rnd((B, Hkv, T, 128))
+    q_sel, q = rnd((B, Hq, NQ, 128)), rnd((B, Hq, 128))
+    layout = kvq.make_layout(B, Hq, Hkv, n_pairs_hi=6, bits_hi=4, residual=R, max_tokens=T,
+                             io_dtype="bf16")
+    cache = kvq.Cache(layout)
+    kvq.kvq_select_pairs(layout, q_sel, NQ, k, T, cache.struct)
+    kvq.kvq_quant_keys(layout, k, T, cache.struct)
+    kvq.kvq_quant_values(layout, v, T, cache.struct)
+    S = bench.default_splits(kvq_synth.Workload("b32", B, Hq, Hkv, T))
+    ws = torch.zeros(kvq.kvq_workspace_bytes(layout, S), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, 128), dtype=torch.int16, device="cuda")
+    kvq.kvq_decode_attn(layout, q, cache.struct, SM_SCALE, S, ws, out)
+    torch.cuda.synchronize()
+    print("case b32-128k S=%d" % S, flush=True)
+
+    def host(t, dt):
+        return t.contiguous().cpu().numpy().view(dt)
+
+    def buf(name, dt, tdt, *shape):
+        n = int(np.prod(shape)) * np.dtype(dt).itemsize
+        return cache[name][:n].view(tdt).reshape(*shape)
+
+    for b, kh in ((0, 0), (B - 1, Hkv - 1)):
+        ks, vs = host(k[b, kh], np.uint16)[None, None], host(v[b, kh], np.uint16)[None, None]
+        qs = host(q_sel[b, kh * G:(kh + 1) * G], np.uint16)[None]
+        qd = host(q[b, kh * G:(kh + 1) * G], np.uint16)[None]
+        sums, pairs = oracle.select(qs, ks, T, 1, "bf16")
+        assert np.array_equal(host(buf("sums", np.uint64, torch.int64, B, Hkv, 2, 64)[b, kh],
+                                   np.uint64), sums[0, 0])
+        assert np.array_equal(host(buf("pairs", np.int32, torch.int32, B, Hkv, 64)[b, kh],
+                                   np.int32), pairs[0, 0])
+        qz = oracle.quantize(ks, vs, T, pairs, residual=R, n_pairs_hi=6, bits_hi=4,
+                             io_dtype="bf16", ng=NG)
+        pk = oracle.pack(qz)
+        for name, dt, tdt, w in (("k_lo", np.uint32, torch.int32, 256),
+                                 ("k_hi", np.uint8, torch.uint8, 128),
+                                 ("k_meta", np.uint16, torch.int16, 256),
+                                 ("v_codes", np.uint32, torch.int32, 256),
+                                 ("v_meta", np.uint16, torch.int16, 256)):
+            got = host(buf(name, dt, tdt, B, Hkv, NG, w)[b, kh], dt)
+            assert np.array_equal(got, pk[name][0, 0]), "%s differs at (%d, %d)" % (name, b, kh)
+        slots = oracle.live_ring_slots(T, R)
+        rk = host(buf("ring_k", np.uint16, torch.int16, B, Hkv, RS, 128)[b, kh], np.uint16)
+        rv = host(buf("ring_v", np.uint16, torch.int16, B, Hkv, RS // 32, 128, 32)[b, kh],
+                  np.uint16)
+        assert np.array_equal(rk[slots], pk["ring_k"][0, 0][slots])
+        for s_ in slots:
+            assert np.array_equal(rv[s_ // 32, :, s_ % 32], pk["ring_v"][0, 0][s_ // 32, :, s_ % 32])
+        ref = oracle.attention(qz, qd, SM_SCALE)
+        got = kvq_synth.bits_to_f64(host(out[b, kh * G:(kh + 1) * G], np.uint16)[None], "bf16")
+        err = check_output(got, ref, "bf16", ATOL)
+        print("b%d kh%d max|err| %.3g" % (b, kh, err), flush=True)
