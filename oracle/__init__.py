@@ -185,6 +185,20 @@ def attention(qz: Quantized, q, sm_scale: float, with_lse: bool = False):
     return (out, lse) if with_lse else out
 
 
+def attention_after_append(qz: Quantized, q, sm_scale: float, with_lse: bool = False):
+    """Decode attention of a call that appends token T-1 and decodes in one
+    step (qz holds the cache after the append, T tokens): every token is
+    attended, but the quantized prefix is the one from before the append,
+    n_q(T-1).  A group that the append packs is attended at 16 bits in that
+    call (it is still in the ring), and quantized from the next call on
+    (PM-KVQ, key_machinery: new tokens are held at 16 bits first and
+    quantized later).  Since n_q(T, R+1) = n_q(T-1, R) for every T, this is
+    the attention above with the residual window one token longer."""
+    kw = dict(qz.__dict__)
+    kw["R"] = qz.R + 1
+    return attention(Quantized(**kw), q, sm_scale, with_lse=with_lse)
+
+
 def k_hi_words(n_pairs_hi: int, bits_hi: int) -> int:
     """Bytes of the salient-key section of one group record."""
     if n_pairs_hi == 0:

@@ -1,0 +1,76 @@
+"""Pins of the oracle's attention for a call that appends a token and decodes
+in one step (PM-KVQ, key_machinery: new tokens are held at 16 bits first and
+quantized later).  The reading: all T tokens after the append are attended,
+with the quantized prefix of before the append, n_q(T-1), so a group that the
+append packs is attended at 16 bits in that call.
+
+* The identity the oracle uses, n_q(T, R+1) = n_q(T-1, R), holds for every T
+  and R tried (closed form of n_q).
+* Where the append packs no group the result is plain attention, bit for bit.
+* Where it packs one, the result is textbook softmax attention over the
+  first n_q(T-1) tokens rebuilt from the packed bytes by the brute-force
+  unpackers and the remaining tokens at 16 bits, and it differs from the
+  attention that reads the new group quantized.
+"""
+import numpy as np
+import pytest
+
+import kvq_synth
+import oracle
+from oracle import brute
+
+SM = float(np.float32(1.0 / np.sqrt(128.0)))
+
+
+def test_quantized_prefix_identity():
+    for R in (32, 64, 96, 128):
+        for T in range(1, 700):
+            want = 32 * (max(0, T - 1 - R) // 32)
+            assert oracle.n_quant(T - 1, R) == want
+            assert oracle.n_quant(T, R + 1) == want
+
+
+def _case(T, seed):
+    w = kvq_synth.Workload("fused", 1, 4, 1, T, n_qry=8, io_dtype="bf16", outliers="pct2x10",
+                           n_pairs_hi=6, residual=64, seed=seed)
+    d = kvq_synth.generate(w)
+    _, pairs = oracle.select(d["q_sel"], d["k"], T, 1, "bf16")
+    qz = oracle.quantize(d["k"], d["v"], T, pairs, residual=64, n_pairs_hi=6, bits_hi=4,
+                         io_dtype="bf16")
+    return w, d, qz
+
+
+@pytest.mark.parametrize("T", [40, 64 + 33, 64 + 32 * 4 + 17])
+def test_no_group_packed_is_plain_attention(T):
+    assert oracle.n_quant(T, 64) == oracle.n_quant(T - 1, 64)
+    w, d, qz = _case(T, 5)
+    q = d["q_dec"][:, :, 0]
+    assert np.array_equal(oracle.attention_after_append(qz, q, SM), oracle.attention(qz, q, SM))
+
+
+@pytest.mark.parametrize("T", [64 + 32, 64 + 32 * 5])
+def test_packed_group_attended_at_sixteen_bits(T):
+    R = 64
+    assert oracle.n_quant(T, R) == oracle.n_quant(T - 1, R) + 32
+    w, d, qz = _case(T, 6)
+    pk = oracle.pack(qz)
+    q = d["q_dec"][:, :, 0]
+    got = oracle.attention_after_append(qz, q, SM)
+    nq = oracle.n_quant(T - 1, R)
+    f16 = lambda x: float(np.uint16(x).view(np.float16))
+    sal = sorted([int(p) for p in qz.pairs[0, 0, :6]] + [int(p) + 64 for p in qz.pairs[0, 0, :6]])
+    K = kvq_synth.bits_to_f64(d["k"][0, 0, :T], "bf16").copy()
+    V = kvq_synth.bits_to_f64(d["v"][0, 0, :T], "bf16").copy()
+    for g in range(nq // 32):
+        codes, _, s, z = brute.unpack_keys(pk["k_lo"][0, 0, g], pk["k_hi"][0, 0, g],
+                                           pk["k_meta"][0, 0, g], sal, 4)
+        for c in range(128):
+            K[32 * g:32 * g + 32, c] = f16(z[c]) + f16(s[c]) * codes[c]
+        vc, vs, vz, _ = brute.unpack_values(pk["v_codes"][0, 0, g], pk["v_meta"][0, 0, g])
+        for t in range(32):
+            for j in range(4):
+                V[32 * g + t, 32 * j:32 * j + 32] = f16(vz[t, j]) + f16(vs[t, j]) * vc[t, 32 * j:32 * j + 32]
+    for h in range(4):
+        ref = brute.attention_textbook(kvq_synth.bits_to_f64(q[0, h], "bf16"), K, V, SM)
+        assert np.max(np.abs(got[0, h] - ref)) < 1e-12
+    assert not np.array_equal(got, oracle.attention(qz, q, SM))
