@@ -9,7 +9,6 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["api.hip", "select.hip", "quant.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -26,13 +25,38 @@ FLAGS = [
 ]
 
 
+# (source, extra flags): decode.hip is compiled twice, one half of its kernel
+# variants each, so that the two halves build in parallel
+UNITS = [("api.hip", []), ("select.hip", []), ("quant.hip", []),
+         ("decode.hip", ["-DKVQ_DECODE_PART=0"]), ("decode.hip", ["-DKVQ_DECODE_PART=1"])]
+
+
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    """Compiles every unit to an object (in parallel), then links libkvq.so."""
+    tag = "%d" % os.getpid()
+    objs, procs = [], []
+    for i, (src, extra) in enumerate(UNITS):
+        obj = os.path.join(PKG, "_unit%d.%s.o" % (i, tag))
+        cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + extra + \
+              ["-c", "-o", obj, os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        objs.append(obj)
+        procs.append(subprocess.Popen(cmd))
+    try:
+        failed = [p.wait() for p in procs]
+        if any(failed):
+            raise subprocess.CalledProcessError(max(failed), "hipcc")
+        tmp = LIB + ".tmp" + tag
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

@@ -179,22 +179,28 @@ kvq_status kvq_shrink(const kvq_layout* L, kvq_cache* cache, int32_t g0, int32_t
   return hip_status(launch_shrink(g, cache, g0, g1, (hipStream_t)stream));
 }
 
+// keep 1..4: kept key chunks; 0: append k_new / v_new and decode in one launch
 static kvq_status decode_common(const kvq_layout* L, const void* q, const kvq_cache* cache,
                                 float sm_scale, int32_t n_splits, int32_t keep, void* workspace,
-                                size_t ws_bytes, void* out, void* stream) {
+                                size_t ws_bytes, void* out, void* stream,
+                                const void* k_new = nullptr, const void* v_new = nullptr) {
   if (kvq_status s = check_layout(L)) return s;
   const Geo g = make_geo(L);
   size_t need = 0;
   if (kvq_status s = kvq_workspace_bytes(L, n_splits, &need)) return s;
   if (ws_bytes < need) return KVQ_ECAPACITY;
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_EINVAL;
-  if (keep < 1 || keep > 4) return KVQ_EINVAL;
+  if (keep < 0 || keep > 4) return KVQ_EINVAL;
   if (kvq_status s = check_ptr(q)) return s;
   if (kvq_status s = check_ptr(out)) return s;
   if (kvq_status s = check_ptr(workspace)) return s;
+  if (keep == 0) {
+    if (kvq_status s = check_ptr(k_new)) return s;
+    if (kvq_status s = check_ptr(v_new)) return s;
+  }
   if (kvq_status s = check_cache(g, cache, true)) return s;
   return hip_status(launch_decode(g, q, cache, sm_scale, n_splits, keep, workspace, out,
-                                  (hipStream_t)stream));
+                                  (hipStream_t)stream, k_new, v_new));
 }
 
 kvq_status kvq_decode_attn(const kvq_layout* L, const void* q, const kvq_cache* cache,
@@ -206,7 +212,16 @@ kvq_status kvq_decode_attn(const kvq_layout* L, const void* q, const kvq_cache* 
 kvq_status kvq_decode_attn_pruned(const kvq_layout* L, const void* q, const kvq_cache* cache,
                                   float sm_scale, int32_t n_splits, int32_t n_keep,
                                   void* workspace, size_t ws_bytes, void* out, void* stream) {
+  if (n_keep < 1) return KVQ_EINVAL;
   return decode_common(L, q, cache, sm_scale, n_splits, n_keep, workspace, ws_bytes, out, stream);
+}
+
+kvq_status kvq_append_decode_attn(const kvq_layout* L, const void* k_new, const void* v_new,
+                                  const void* q, kvq_cache* cache, float sm_scale,
+                                  int32_t n_splits, void* workspace, size_t ws_bytes, void* out,
+                                  void* stream) {
+  return decode_common(L, q, cache, sm_scale, n_splits, 0, workspace, ws_bytes, out, stream,
+                       k_new, v_new);
 }
 
 kvq_status kvq_check(const kvq_cache* cache, int32_t* host_err, void* stream) {

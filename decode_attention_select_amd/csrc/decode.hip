@@ -35,6 +35,11 @@
 // with the log-sum-exp rule and writes the output.
 #include "common.h"
 #include "internal.h"
+#include "quant_group.h"
+
+#ifndef KVQ_DECODE_PART
+#define KVQ_DECODE_PART 1
+#endif
 
 namespace kvq {
 
@@ -245,8 +250,10 @@ struct Lds {
   union {
     LdsLoop loop;
     LdsMerge merge;
+    PackLds pack;  // FUSED: the append step of the last workgroup, after the merge
   } u;
   int last;
+  int first;  // FUSED: the first workgroup of its (sequence, KV head) to finish
 };
 
 // HASQ: the cache has quantized-group storage (capacity NG >= 1); without it
@@ -265,10 +272,21 @@ struct Lds {
 // VHI: the cache has two value precisions (g.n_vhi > 0): the first n_vhi
 // 8-slot blocks of each group (its tokens of largest key magnitude) add their
 // high value digits (4 * digit) through one more MFMA per tile.
-template <bool BF16, int HIMODE, bool HASQ, bool LO1, int KEEP, bool VHI>
+// FUSED: the call also appends one token per (sequence, KV head) (knew,
+// vnew) and attends it (PM-KVQ, key_machinery: 16-bit first, quantized
+// later).  Every wave reads the length before the append and attends the
+// quantized prefix of that length plus the ring and the new token, which
+// it takes from knew/vnew; a group that the append completes is attended
+// from the ring at 16 bits in this call.  The last workgroup of the
+// (sequence, KV head), after the merge (so after every workgroup has read
+// the length and the ring), writes the token to its ring slot, packs the
+// completed group and stores the new length.
+template <bool BF16, int HIMODE, bool HASQ, bool LO1, int KEEP, bool VHI, bool FUSED>
 __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             kvq_cache c, float scale_log2, int S,
-                                                            Ws ws, uint16_t* __restrict__ out) {
+                                                            Ws ws, uint16_t* __restrict__ out,
+                                                            const uint16_t* __restrict__ knew,
+                                                            const uint16_t* __restrict__ vnew) {
   constexpr bool PRUNE = KEEP < 4;
   __shared__ Lds lds;
   // the wave index is wave-uniform: keeping it in a scalar register makes every
@@ -297,6 +315,14 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int STR = S * NW;          // group stride of one wave
   const size_t rec0 = (size_t)bh * g.NG;
   const int first = s + S * wave;  // this wave's groups: first + i*STR < ngq
+  // FUSED: the new token's key and value channel tid (for the ring write of
+  // the last workgroup), requested now so that the end does not wait for them
+  uint16_t knv = 0, vnv = 0;
+  if constexpr (FUSED)
+    if (tid < D) {
+      knv = knew[(size_t)bh * D + tid];
+      vnv = vnew[(size_t)bh * D + tid];
+    }
   Pref pf[PF];
   if constexpr (HASQ) {
 #pragma unroll
@@ -306,14 +332,19 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   }
 
   // scalar loads: the length and the 8 leading ranks
-  const int T = min(max(c.len[bh], 0), g.max_tokens);  // reads stay inside the cache
+  const int len = c.len[bh];
+  const int T_old = min(max(len, 0), g.max_tokens);  // reads stay inside the cache
+  // FUSED: whether this call appends (a full cache or a negative length is
+  // reported and decoded as it stands)
+  const bool app = FUSED && len >= 0 && len < g.max_tokens;
+  const int T = T_old + (app ? 1 : 0);
   int top[8];
   if constexpr (HIMODE != 0) {
     const int32_t* pr = c.pairs + (size_t)bh * NPAIR;
 #pragma unroll
     for (int r = 0; r < 8; r++) top[r] = pr[r];
   }
-  const int nq = n_quant(T, g.R), ngq = nq / GS;
+  const int nq = n_quant(T_old, g.R), ngq = nq / GS;  // FUSED: the prefix before the append
   const int nrb = (T - nq + GS - 1) / GS;
   // This wave's quantized groups are first + i*STR, i < nmine.  Exactly PF
   // group loads are kept in flight (past the end the index is clamped to the
@@ -656,15 +687,35 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     const int sb = (pbase / GS) % (g.RS / GS);
     const uint16_t* rk = (const uint16_t*)c.ring_k + ((size_t)bh * g.RS + sb * GS) * D;
     const uint16_t* rv = (const uint16_t*)c.ring_v + (((size_t)bh * (g.RS / GS) + sb) * D) * GS;
+    // FUSED: the appended token's index in this block (-1 if not here); its
+    // key row and value column come from knew / vnew, not from the ring
+    const int tnew = app ? T_old - pbase : -1;
     u4 kt[2][4], vt[8];
 #pragma unroll
     for (int TT = 0; TT < 2; TT++) {
-      const u4* kr = (const u4*)(rk + (size_t)tile_token(16 * TT + col) * D + 32 * kqa);
+      const int tok = tile_token(16 * TT + col);
+      const u4* kr = (const u4*)(rk + (size_t)tok * D + 32 * kqa);
+      if constexpr (FUSED)
+        if (tok == tnew) kr = (const u4*)(knew + (size_t)bh * D + 32 * kqa);
 #pragma unroll
       for (int k = 0; k < 4; k++) kt[TT][k] = kr[k];
     }
 #pragma unroll
     for (int tt = 0; tt < 8; tt++) vt[tt] = *(const u4*)(rv + (size_t)(16 * tt + col) * GS + 8 * kq);
+    if constexpr (FUSED) {
+      const int dt = tnew - 8 * kq;  // the new token among this lane's 8 slots
+      if (dt >= 0 && dt < 8) {
+#pragma unroll
+        for (int tt = 0; tt < 8; tt++) {
+          const uint32_t x = vnew[(size_t)bh * D + 16 * tt + col];
+          const int e = dt >> 1, sh = 16 * (dt & 1);
+          const uint32_t m = 0xFFFFu << sh;
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+            if (i == e) vt[tt][i] = (vt[tt][i] & ~m) | (x << sh);
+        }
+      }
+    }
     uint32_t qraw[16];
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -794,8 +845,29 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         __hip_atomic_fetch_add(&ws.tick[(size_t)bh * TICK_STRIDE], 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     lds.last = prev == (uint32_t)(S - 1);
+    if constexpr (FUSED) lds.first = prev == 0u;
   }
   __syncthreads();
+  if constexpr (FUSED) {
+    // the first workgroup to finish does the append's ring write and packing
+    // while the others still run: nothing in this call reads the packed
+    // records, and the token's ring slot held a quantized position (T_old -
+    // RS < nq), which no wave reads from the ring (the new token itself
+    // comes from knew / vnew).  The length is stored by the last workgroup,
+    // after every workgroup has read it.
+    if (lds.first && app) {
+      const int slot = T_old % g.RS;
+      if (tid < D) {
+        uint16_t* rk = (uint16_t*)c.ring_k + (size_t)bh * g.RS * D;
+        uint16_t* rv = (uint16_t*)c.ring_v + (size_t)bh * g.RS * D;
+        rk[(size_t)slot * D + tid] = knv;
+        rv[((size_t)(slot / GS) * D + tid) * GS + slot % GS] = vnv;
+      }
+      // the group [nq, nq + 32) ends at T - R <= T_old: the new token is not in it
+      if (n_quant(T, g.R) > nq && tid < 128)
+        pack_ring_group<BF16, VHI>(g, c, bh, nq, tid, lds.u.pack);
+    }
+  }
   if (!lds.last) return;
   // item = (head, 8 channels); nsub lanes (a power of two, within one wave)
   // share an item's splits, each loading up to 8 records at once, and
@@ -873,65 +945,95 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   if (tid == 0)  // ready for the next call
     __hip_atomic_store(&ws.tick[(size_t)bh * TICK_STRIDE], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (FUSED) {
+    // the append's length (or its error): every workgroup of this (sequence,
+    // KV head) has read the length before it took its ticket
+    if (tid == 0) {
+      if (app) c.len[bh] = T;
+      else atomicOr(c.err, len < 0 ? 2 : 1);
+    }
+  }
 }
 
-template <bool BF16, int HIMODE, bool LO1, int KEEP, bool VHI = false>
-static void launch_one(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
-                       const Ws& ws, void* out, hipStream_t st) {
+// The launch arguments shared by every kernel variant.
+struct Launch {
+  const void* q;
+  const kvq_cache* c;
+  float scale_log2;
+  int S;
+  Ws ws;
+  void* out;
+  const void* knew;  // FUSED only
+  const void* vnew;
+  hipStream_t st;
+};
+
+template <bool BF16, int HIMODE, bool LO1, int KEEP, bool VHI, bool FUSED>
+static void launch_one(const Geo& g, const Launch& a) {
+  const dim3 grid(g.B * g.Hkv * a.S), block(WG_THREADS);
   if (g.NG > 0)
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, LO1, KEEP, VHI>),
-                       dim3(g.B * g.Hkv * S), dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c,
-                       scale_log2, S, ws, (uint16_t*)out);
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, LO1, KEEP, VHI, FUSED>), grid, block, 0,
+                       a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,
+                       (uint16_t*)a.out, (const uint16_t*)a.knew, (const uint16_t*)a.vnew);
   else
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, LO1, KEEP, false>),
-                       dim3(g.B * g.Hkv * S), dim3(WG_THREADS), 0, st, g, (const uint16_t*)q, *c,
-                       scale_log2, S, ws, (uint16_t*)out);
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, LO1, KEEP, false, FUSED>), grid, block,
+                       0, a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,
+                       (uint16_t*)a.out, (const uint16_t*)a.knew, (const uint16_t*)a.vnew);
 }
 
+// keep 0: the fused append-and-decode call (all four key chunks)
 template <bool BF16, int HIMODE, bool LO1, bool VHI>
-static void launch_keep(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
-                        int keep, const Ws& ws, void* out, hipStream_t st) {
+static void launch_keep(const Geo& g, int keep, const Launch& a) {
   switch (keep) {
-    case 1: launch_one<BF16, HIMODE, LO1, 1, VHI>(g, q, c, scale_log2, S, ws, out, st); break;
-    case 2: launch_one<BF16, HIMODE, LO1, 2, VHI>(g, q, c, scale_log2, S, ws, out, st); break;
-    case 3: launch_one<BF16, HIMODE, LO1, 3, VHI>(g, q, c, scale_log2, S, ws, out, st); break;
-    default: launch_one<BF16, HIMODE, LO1, 4, VHI>(g, q, c, scale_log2, S, ws, out, st); break;
+    case 0: launch_one<BF16, HIMODE, LO1, 4, VHI, true>(g, a); break;
+    case 1: launch_one<BF16, HIMODE, LO1, 1, VHI, false>(g, a); break;
+    case 2: launch_one<BF16, HIMODE, LO1, 2, VHI, false>(g, a); break;
+    case 3: launch_one<BF16, HIMODE, LO1, 3, VHI, false>(g, a); break;
+    default: launch_one<BF16, HIMODE, LO1, 4, VHI, false>(g, a); break;
   }
 }
 
 // Two value precisions touch only the value side and pruning only the key
 // side, so every combination has its own kernel.
 template <bool BF16, int HIMODE>
-static void launch_lo1(const Geo& g, const void* q, const kvq_cache* c, float scale_log2, int S,
-                       int keep, const Ws& ws, void* out, hipStream_t st) {
+static void launch_lo1(const Geo& g, int keep, const Launch& a) {
   if (g.n_lo1 > 0) {
-    if (g.n_vhi > 0) launch_keep<BF16, HIMODE, true, true>(g, q, c, scale_log2, S, keep, ws, out, st);
-    else launch_keep<BF16, HIMODE, true, false>(g, q, c, scale_log2, S, keep, ws, out, st);
+    if (g.n_vhi > 0) launch_keep<BF16, HIMODE, true, true>(g, keep, a);
+    else launch_keep<BF16, HIMODE, true, false>(g, keep, a);
   } else {
-    if (g.n_vhi > 0) launch_keep<BF16, HIMODE, false, true>(g, q, c, scale_log2, S, keep, ws, out, st);
-    else launch_keep<BF16, HIMODE, false, false>(g, q, c, scale_log2, S, keep, ws, out, st);
+    if (g.n_vhi > 0) launch_keep<BF16, HIMODE, false, true>(g, keep, a);
+    else launch_keep<BF16, HIMODE, false, false>(g, keep, a);
   }
 }
+
+template <bool BF16>
+hipError_t launch_decode_io(const Geo& g, int keep, const Launch& a) {
+  const int hm = g.n_hi == 0 ? 0 : g.bits_hi;
+  if (hm == 0) launch_lo1<BF16, 0>(g, keep, a);
+  else if (hm == 4) launch_lo1<BF16, 4>(g, keep, a);
+  else launch_lo1<BF16, 16>(g, keep, a);
+  return hipGetLastError();
+}
+
+// The file is compiled twice so that the two halves of the kernel variants
+// build in parallel: KVQ_DECODE_PART 0 holds the fp16 kernels, 1 the bf16
+// kernels and the entry points.
+#if KVQ_DECODE_PART == 0
+template hipError_t launch_decode_io<false>(const Geo&, int, const Launch&);
+#else
+extern template hipError_t launch_decode_io<false>(const Geo&, int, const Launch&);
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {
   return ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S) + (size_t)B * Hkv * TICK_STRIDE * 4;
 }
 
 hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float sm_scale,
-                         int S, int keep, void* workspace, void* out, hipStream_t st) {
-  const float scale_log2 = sm_scale * 1.4426950408889634f;
-  const int hm = g.n_hi == 0 ? 0 : g.bits_hi;
-  const Ws ws = ws_layout(workspace, g.B, g.Hq, S);
-  if (g.bf16) {
-    if (hm == 0) launch_lo1<true, 0>(g, q, c, scale_log2, S, keep, ws, out, st);
-    else if (hm == 4) launch_lo1<true, 4>(g, q, c, scale_log2, S, keep, ws, out, st);
-    else launch_lo1<true, 16>(g, q, c, scale_log2, S, keep, ws, out, st);
-  } else {
-    if (hm == 0) launch_lo1<false, 0>(g, q, c, scale_log2, S, keep, ws, out, st);
-    else if (hm == 4) launch_lo1<false, 4>(g, q, c, scale_log2, S, keep, ws, out, st);
-    else launch_lo1<false, 16>(g, q, c, scale_log2, S, keep, ws, out, st);
-  }
-  return hipGetLastError();
+                         int S, int keep, void* workspace, void* out, hipStream_t st,
+                         const void* k_new, const void* v_new) {
+  const Launch a{q, c, sm_scale * 1.4426950408889634f, S, ws_layout(workspace, g.B, g.Hq, S),
+                 out, k_new, v_new, st};
+  return g.bf16 ? launch_decode_io<true>(g, keep, a) : launch_decode_io<false>(g, keep, a);
 }
+#endif
 
 }  // namespace kvq

@@ -14,9 +14,12 @@ hipError_t launch_quant_values(const Geo& g, const void* v, int T, kvq_cache* c,
 hipError_t launch_shrink(const Geo& g, kvq_cache* c, int g0, int g1, hipStream_t st);
 hipError_t launch_append(const Geo& g, const void* k_new, const void* v_new, kvq_cache* c,
                          hipStream_t st);
+// keep_chunks 1..4: kept key chunks (4: unpruned); 0: the fused append and
+// decode, which appends k_new / v_new (null otherwise)
 hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float sm_scale,
                          int n_splits, int keep_chunks, void* workspace, void* out,
-                         hipStream_t st);
+                         hipStream_t st, const void* k_new = nullptr,
+                         const void* v_new = nullptr);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_splits);
 
 }  // namespace kvq

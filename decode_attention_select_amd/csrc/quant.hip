@@ -21,6 +21,7 @@
 // broadcast, so each division runs once per quad.
 #include "common.h"
 #include "internal.h"
+#include "quant_group.h"
 
 namespace kvq {
 
@@ -28,518 +29,9 @@ constexpr int QWAVES = 4;                 // groups per prefill workgroup, one p
 constexpr int QTHREADS = 64 * QWAVES;
 constexpr int RING_ROWS = QTHREADS / 16;  // ring-fill rows per workgroup (16 B per thread)
 
-// ------------------------------------------------------------ lane exchange
-
-template <int CTRL>
-__device__ inline uint32_t dpp(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>  // row_* controls (rotations within a 16-lane row)
-__device__ inline uint32_t dpp_row(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
-}
-constexpr int QUAD_XOR1 = 0xB1;  // quad_perm [1, 0, 3, 2]
-constexpr int QUAD_XOR2 = 0x4E;  // quad_perm [2, 3, 0, 1]
-template <int K>
-struct QuadBcast {  // quad_perm [K, K, K, K]
-  static constexpr int ctrl = K | (K << 2) | (K << 4) | (K << 6);
-};
-template <int K>
-__device__ inline uint32_t quad_bcast(uint32_t x) { return dpp<QuadBcast<K>::ctrl>(x); }
-
-// min and max over the quad (inputs are finite).  The result is the quad's
-// min/max value; only the sign of a zero minimum depends on the combining
-// order and on how the min instruction orders -0 and +0, and the caller
-// settles that separately (sign_of_first_zero).
-// One VALU instruction per step: the min/max reads the partner lane through
-// its DPP source operand (written directly, since the compiler would add a
-// copy and a NaN-quieting max around a separate DPP move).  s_nop 1 covers
-// the wait states between a VALU write and a DPP read of the same register.
-#define KVQ_QUAD_OP(name, op)                                                      \
-  __device__ inline float name(float v) {                                          \
-    float t, r;                                                                    \
-    asm("s_nop 1\n\t" op "_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" \
-        : "=&v"(t) : "v"(v));                                                      \
-    asm("s_nop 1\n\t" op "_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" \
-        : "=&v"(r) : "v"(t));                                                      \
-    return r;                                                                      \
-  }
-KVQ_QUAD_OP(quad_min, "v_min_f32")
-KVQ_QUAD_OP(quad_max, "v_max_f32")
-#undef KVQ_QUAD_OP
-
-// A sequential scan keeps the first of equal minima, so a minimum of zero
-// carries the sign of the group's first zero element.  f = this lane's
-// first zero in its eight elements (0: +0, 1: -0, 2: none), lanes of the
-// quad in element order; returns the sign bit of the quad's first zero.
-__device__ inline uint32_t sign_of_first_zero(uint32_t f) {
-  const uint32_t f0 = quad_bcast<0>(f), f1 = quad_bcast<1>(f), f2 = quad_bcast<2>(f),
-                 f3 = quad_bcast<3>(f);
-  const uint32_t s = f0 != 2 ? f0 : f1 != 2 ? f1 : f2 != 2 ? f2 : f3;
-  return s == 1 ? 0x80000000u : 0u;
-}
-
-// 16-bit element e (0..7) of a 16-byte row chunk, widened to fp32.
-__device__ inline uint16_t half_of(const uint4& v, int e) {
-  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
-  return (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xFFFF);
-}
-
-// Affine parameters of one group at L levels (the quantizer of common.h):
-// z = fp16(min), s = fp16((max - z) / L) or 0, r = 1 / s (0 when s == 0).
-struct QParam {
-  uint32_t sz;  // s bits | z bits << 16
-  float r;
-};
-__device__ inline QParam qparam(float mn, float mx, float L, bool raw) {
-  if (raw) return {0u, 0.0f};
-  const uint16_t zb = f32_to_half_bits(mn);
-  const float diff = __fsub_rn(mx, half_bits_to_f32(zb));
-  const uint16_t sb = diff > 0.0f ? f32_to_half_bits(__fdiv_rn(diff, L)) : (uint16_t)0;
-  const float r = sb ? __fdiv_rn(1.0f, half_bits_to_f32(sb)) : 0.0f;
-  return {(uint32_t)sb | ((uint32_t)zb << 16), r};
-}
-
-// code = clamp(rint((x - z) * r), 0, L) as an integer-valued float; 0 when
-// r == 0 (s == 0).  Inputs are finite 16-bit values within the fp16 range of
-// the scale and zero, so the product is never NaN.
-__device__ inline float qcode(float x, float z, float r, float L) {
-  const float q = rintf(__fmul_rn(__fsub_rn(x, z), r));
-  return __builtin_amdgcn_fmed3f(q, 0.0f, L);
-}
-
-// Marks the loaded words as changed, so that widened copies made before are
-// not kept alive in registers (widening again costs one instruction each).
-__device__ inline void refresh(uint4 (&v)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; i++)
-    asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
-}
-
-// Compiler barrier for LDS traffic between lanes of one wave (the hardware
-// runs a wave's LDS instructions in order).
-__device__ inline void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Bit j set when pair j has rank < n_hi (salient), rank >= 64 - n_lo1 (one bit).
-struct PairMasks {
-  uint64_t hi, one;
-};
-// The ranks are read in fixed-size blocks (wave-uniform scalar loads, all in
-// flight together) rather than one dependent load per rank.
-__device__ inline PairMasks pair_masks(const Geo& g, const int32_t* pr) {
-  uint64_t hi = 0, one = 0;
-  int p[8];
-#pragma unroll
-  for (int r = 0; r < 8; r++) p[r] = pr[r];  // n_hi <= 8
-#pragma unroll
-  for (int r = 0; r < 8; r++)
-    if (r < g.n_hi) hi |= 1ull << (p[r] & (NPAIR - 1));
-  if (g.n_lo1) {
-    int t[NPAIR];
-#pragma unroll
-    for (int r = 0; r < NPAIR; r++) t[r] = pr[r];
-#pragma unroll
-    for (int r = 0; r < NPAIR; r++)
-      if (r >= NPAIR - g.n_lo1) one |= 1ull << (t[r] & (NPAIR - 1));
-  }
-  return {hi, one};
-}
-
-// ------------------------------------------------------------- key group
-
-struct KeyLds {  // one wave's staging of a key-group record
-  union {
-    struct {
-      uint32_t lo[GROUP_WORDS];
-      uint32_t hi[256];  // 4-bit: 32 words; raw 16-bit: 32 tokens x up to 16 halves
-    };
-    // two value precisions, before the record is staged: the group's 32 key
-    // rows (16-byte pieces [row][cb]), then the partial scores [4][32]
-    uint32_t tile[GS * 16 * 4 + 4 * GS];
-  };
-  uint32_t ord[8];  // two value precisions: the group's order bytes (slot -> position)
-};
-
-// Token order of one group for two value precisions by token (the SemKV
-// reading documented in include/kvq.h at v_hi): token t's key magnitude
-// E_t = sum over the 128 channels of min(floor(4096 |k|), 2^20) (integer, at
-// most 2^27), and slot rank(t) = the number of tokens with larger E or equal
-// E and lower position.  rows: token 0 of the group, row stride D.  Lanes
-// 2t and 2t+1 sum the two channel halves of token t; every lane then ranks
-// its token against the 32 sums read back from lanes 2a.  Writes order
-// bytes (ord[rank(t)] = t) to LDS; the caller syncs before reading them.
-template <bool BF>
-__device__ inline uint32_t key_score(const uint4& v) {  // 8 channels of one token
-  uint32_t e = 0;
-#pragma unroll
-  for (int k = 0; k < 8; k++)  // 4096 |x| is exact; the conversion truncates
-    e += (uint32_t)fminf(4096.0f * fabsf(in_to_f32(half_of(v, k), BF)), 1048576.0f);
-  return e;
-}
-
-// Writes ord[rank(t)] = t for the token whose score e lanes t < 32 hold.
-__device__ inline void order_from_scores(uint32_t e, uint32_t* ord) {
-  const int lane = threadIdx.x & 63;
-  uint32_t rank = 0;
-#pragma unroll
-  for (int a = 0; a < GS; a++) {
-    const uint32_t ea = __builtin_amdgcn_readlane(e, a);
-    rank += (ea > e) || (ea == e && a < lane);
-  }
-  if (lane < GS) ((uint8_t*)ord)[rank] = (uint8_t)lane;
-}
-
-template <bool BF>
-__device__ void token_order_wave(const uint16_t* rows, uint32_t* ord) {
-  const int lane = threadIdx.x & 63, t = lane >> 1, h = lane & 1;
-  uint4 v[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) v[i] = *(const uint4*)(rows + (size_t)t * D + 64 * h + 8 * i);
-  uint32_t e = 0;
-#pragma unroll
-  for (int i = 0; i < 8; i++) e += key_score<BF>(v[i]);
-  e += dpp<QUAD_XOR1>(e);
-  // token t's score to lane t
-  e = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((2 * lane) & 63), (int)e);
-  order_from_scores(e, ord);
-}
-
-// rows: token 0 of the group, row stride D (prefill input or ring_k slots).
-// VHI: the wave first ranks the group's tokens (token_order_wave's scores,
-// summed from the rows it holds), writes the order bytes to L.ord and takes
-// the rows in that order through the LDS tile, so the record's token index
-// is the slot (slot i = position L.ord[i]).
-template <bool BF, bool VHI>
-__device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
-                               uint32_t* lo_out, uint8_t* hi_out, uint16_t* meta_out,
-                               KeyLds& L) {
-  const int lane = threadIdx.x & 63, cb = lane >> 2, tq = lane & 3;
-  uint4 v[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) v[i] = *(const uint4*)(rows + (size_t)(8 * tq + i) * D + 8 * cb);
-  // positions of the lane's slots 8tq .. 8tq+7, one byte each
-  uint2 pos = make_uint2(0, 0);
-  if constexpr (VHI) {
-    uint4* tile = (uint4*)L.tile;
-    uint32_t* rs = L.tile + GS * 16 * 4;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      // the lane's 8 channels, then the 4 channel blocks of its DPP row
-      uint32_t e = key_score<BF>(v[i]);
-      e += dpp_row<0x124>(e);  // row_ror:4 (same tq, next cb)
-      e += dpp_row<0x128>(e);  // row_ror:8
-      if ((cb & 3) == 0) rs[(cb >> 2) * GS + 8 * tq + i] = e;
-      tile[(8 * tq + i) * 16 + cb] = v[i];
-    }
-    wave_lds_sync();
-    const int t = lane & (GS - 1);
-    order_from_scores(rs[t] + rs[GS + t] + rs[2 * GS + t] + rs[3 * GS + t], L.ord);
-    wave_lds_sync();
-    pos = ((const uint2*)L.ord)[tq];
-  }
-  auto pos_of = [&](int i) -> uint32_t {
-    if constexpr (VHI) return ((i < 4 ? pos.x : pos.y) >> (8 * (i & 3))) & 0xFFu;
-    return 8 * tq + i;
-  };
-  if constexpr (VHI) {
-    const uint4* tile = (const uint4*)L.tile;
-#pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = tile[pos_of(i) * 16 + cb];
-    wave_lds_sync();  // the tile's space is reused for the record below
-  }
-
-  const bool bits4 = g.nh > 0 && g.bits_hi == 4, raw16 = g.nh > 0 && g.bits_hi == 16;
-  // bit allocation of the lane's channels 8cb + k
-  float lv[8];
-  bool raw[8];
-  int hish[8], dix[8];
-#pragma unroll
-  for (int k = 0; k < 8; k++) {
-    const int c = 8 * cb + k, j = c & (NPAIR - 1);
-    const bool sal = (pm.hi >> j) & 1, one = (pm.one >> j) & 1;
-    dix[k] = __popcll(pm.hi & ((1ull << j) - 1)) + (c >= NPAIR ? g.n_hi : 0);
-    raw[k] = sal && g.bits_hi == 16;
-    lv[k] = sal ? 15.0f : (one ? 1.0f : 3.0f);
-    hish[k] = sal ? 2 * pos_swap(dix[k]) : 0;
-  }
-  // per-channel min / max over the 32 tokens
-  float mn[8], mx[8];
-#pragma unroll
-  for (int k = 0; k < 8; k++) {
-    float a = in_to_f32(half_of(v[0], k), BF), b = a;
-#pragma unroll
-    for (int i = 1; i < 8; i += 2) {  // three-input min / max
-      const float x = in_to_f32(half_of(v[i], k), BF);
-      const float y = i + 1 < 8 ? in_to_f32(half_of(v[i + 1], k), BF) : x;
-      a = fminf(a, fminf(x, y));
-      b = fmaxf(b, fmaxf(x, y));
-    }
-    mn[k] = quad_min(a);
-    mx[k] = quad_max(b);
-  }
-  bool zmin = false;
-#pragma unroll
-  for (int k = 0; k < 8; k++) zmin |= mn[k] == 0.0f;
-  if (__any(zmin)) {
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      if constexpr (VHI) {
-        // the first zero by position: smallest 2 * position + sign bit
-        uint32_t f = 0xFFFFu;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-          const float x = in_to_f32(half_of(v[i], k), BF);
-          if (x == 0.0f) f = min(f, 2 * pos_of(i) + (__float_as_uint(x) >> 31));
-        }
-        f = min(f, dpp<QUAD_XOR1>(f));
-        f = min(f, dpp<QUAD_XOR2>(f));
-        if (mn[k] == 0.0f) mn[k] = __uint_as_float((f & 1u) << 31);
-      } else {
-        uint32_t f = 2;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-          const float x = in_to_f32(half_of(v[i], k), BF);
-          if (f == 2 && x == 0.0f) f = __float_as_uint(x) >> 31;
-        }
-        const uint32_t sgn = sign_of_first_zero(f);
-        if (mn[k] == 0.0f) mn[k] = __uint_as_float(sgn);
-      }
-    }
-  }
-  // lane tq computes channels 2tq and 2tq+1 of the quad's eight
-  auto pick = [&](const float (&a)[8], int o) {
-    return tq == 0 ? a[o] : tq == 1 ? a[2 + o] : tq == 2 ? a[4 + o] : a[6 + o];
-  };
-  auto pickb = [&](const bool (&a)[8], int o) {
-    return tq == 0 ? a[o] : tq == 1 ? a[2 + o] : tq == 2 ? a[4 + o] : a[6 + o];
-  };
-  const QParam p0 = qparam(pick(mn, 0), pick(mx, 0), pick(lv, 0), pickb(raw, 0));
-  const QParam p1 = qparam(pick(mn, 1), pick(mx, 1), pick(lv, 1), pickb(raw, 1));
-  uint32_t sz[8];
-  float rr[8];
-#define KVQ_BCAST(K)                                                              \
-  sz[2 * K] = quad_bcast<K>(p0.sz);                                              \
-  sz[2 * K + 1] = quad_bcast<K>(p1.sz);                                          \
-  rr[2 * K] = __uint_as_float(quad_bcast<K>(__float_as_uint(p0.r)));             \
-  rr[2 * K + 1] = __uint_as_float(quad_bcast<K>(__float_as_uint(p1.r)));
-  KVQ_BCAST(0) KVQ_BCAST(1) KVQ_BCAST(2) KVQ_BCAST(3)
-#undef KVQ_BCAST
-
-  // codes: low digits summed into half-words as exact float integers
-  // (digit * 4^position, below 2^16); the high digits of 4-bit channels as
-  // integers, only for channel slots k where some lane holds a 4-bit channel
-  refresh(v);
-  float hwf[8];
-  uint32_t hw[8], hh[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    hwf[i] = 0.0f;
-    hh[i] = 0;
-  }
-#pragma unroll
-  for (int k = 0; k < 8; k++) {
-    const float z = half_bits_to_f32((uint16_t)(sz[k] >> 16));
-    const float mul = (float)(1u << (2 * pos_swap(k)));
-    if (bits4 && __any(lv[k] == 15.0f)) {
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const float q = qcode(in_to_f32(half_of(v[i], k), BF), z, rr[k], lv[k]);
-        const float hd = floorf(q * 0.25f), ld = fmaf(hd, -4.0f, q);
-        hwf[i] = fmaf(ld, mul, hwf[i]);
-        hh[i] |= (uint32_t)hd << hish[k];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; i++)
-        hwf[i] = fmaf(qcode(in_to_f32(half_of(v[i], k), BF), z, rr[k], lv[k]), mul, hwf[i]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; i++) hw[i] = (uint32_t)hwf[i];
-  // stage the record in LDS: token i of this lane is tile index
-  // e = 16 T + r with T = i / 4, r = 4 tq + i % 4
-  if (lane < 8) ((uint4*)L.hi)[lane] = make_uint4(0, 0, 0, 0);
-  wave_lds_sync();
-  const int w = cb >> 1, kq = w >> 1, u = w & 1, half = cb & 1;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int T = i >> 2, r = 4 * tq + (i & 3);
-    ((uint16_t*)L.lo)[(((T * 4 + kq) * 16 + r) * 2 + u) * 2 + half] = (uint16_t)hw[i];
-    if (bits4 && hh[i]) atomicOr(&L.hi[16 * T + r], hh[i]);
-  }
-  if (raw16) {
-#pragma unroll
-    for (int k = 0; k < 8; k++)
-      if (raw[k]) {
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-          const int e = 16 * (i >> 2) + 4 * tq + (i & 3);
-          ((uint16_t*)L.hi)[e * g.nh + dix[k]] = half_of(v[i], k);
-        }
-      }
-  }
-  wave_lds_sync();
-  ((uint4*)lo_out)[lane] = ((const uint4*)L.lo)[lane];
-  if (lane < g.khi_bytes / 16) ((uint4*)hi_out)[lane] = ((const uint4*)L.hi)[lane];
-  if (tq < 2) {
-    uint32_t m[4];
-#pragma unroll
-    for (int p = 0; p < 4; p++)
-      m[p] = tq == 0 ? (sz[2 * p] & 0xFFFFu) | (sz[2 * p + 1] << 16)
-                     : (sz[2 * p] >> 16) | (sz[2 * p + 1] & 0xFFFF0000u);
-    *(uint4*)(meta_out + tq * D + 8 * cb) = make_uint4(m[0], m[1], m[2], m[3]);
-  }
-}
-
-// ----------------------------------------------------------- value group
-
-// CHMAJOR false: src = token 0 of the group, row stride D (prefill input).
-// CHMAJOR true:  src = a ring_v slot block [128][32] (channel, slot).
-// VHI (g.n_vhi > 0: two value precisions by token, the SemKV reading
-// documented in include/kvq.h at v_hi): pos holds the positions of the
-// lane's slots 8tq .. 8tq+7 (one byte each, from the group's token order);
-// slots below 8 n_vhi quantize at L = 2^bits_vhi - 1, and the high digits
-// of their codes go to vhi_out (the group's v_hi record) after its 8-word
-// order header, which the key side writes.
-template <bool BF, bool CHMAJOR, bool VHI>
-__device__ void value_group_wave(const Geo& g, const uint16_t* src, uint2 pos, uint32_t* vc_out,
-                                 uint16_t* meta_out, uint32_t* vhi_out) {
-  const int lane = threadIdx.x & 63, cb = lane & 15, tq = lane >> 4, m = cb & 3, j = cb >> 2;
-  auto pos_of = [&](int i) -> uint32_t {
-    return ((i < 4 ? pos.x : pos.y) >> (8 * (i & 3))) & 0xFFu;
-  };
-  // x(i, k): slot 8tq + i, channel 8cb + k
-  uint4 v[8];
-  if constexpr (VHI && CHMAJOR) {
-    // the slot's token is scattered in the channel-major ring block: gather
-    // 16-bit values, channel row n of the lane from the eight positions
-#pragma unroll
-    for (int n = 0; n < 8; n++) {
-      const uint16_t* r = src + (size_t)(8 * cb + n) * GS;
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) w[i] = r[pos_of(2 * i)] | ((uint32_t)r[pos_of(2 * i + 1)] << 16);
-      v[n] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  } else {
-#pragma unroll
-    for (int n = 0; n < 8; n++)
-      v[n] = CHMAJOR ? *(const uint4*)(src + (size_t)(8 * cb + n) * GS + 8 * tq)
-                     : *(const uint4*)(src + (size_t)(VHI ? pos_of(n) : 8 * tq + n) * D + 8 * cb);
-  }
-  auto x = [&](int i, int k) {
-    return in_to_f32(CHMAJOR ? half_of(v[k], i) : half_of(v[i], k), BF);
-  };
-  float mn[8], mx[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    float a = x(i, 0), b = a;
-#pragma unroll
-    for (int k = 1; k < 8; k += 2) {  // three-input min / max
-      const float e = x(i, k), f = k + 1 < 8 ? x(i, k + 1) : e;
-      a = fminf(a, fminf(e, f));
-      b = fmaxf(b, fmaxf(e, f));
-    }
-    mn[i] = quad_min(a);
-    mx[i] = quad_max(b);
-  }
-  bool zmin = false;
-#pragma unroll
-  for (int i = 0; i < 8; i++) zmin |= mn[i] == 0.0f;
-  if (__any(zmin)) {
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      uint32_t f = 2;
-#pragma unroll
-      for (int k = 0; k < 8; k++) {
-        const float e = x(i, k);
-        if (f == 2 && e == 0.0f) f = __float_as_uint(e) >> 31;
-      }
-      const uint32_t sgn = sign_of_first_zero(f);
-      if (mn[i] == 0.0f) mn[i] = __uint_as_float(sgn);
-    }
-  }
-  const bool hiblk = VHI && tq < g.n_vhi;
-  const float Lv = hiblk ? (float)((1 << g.bits_vhi) - 1) : 3.0f;
-  auto pick = [&](const float (&a)[8], int o) {
-    return m == 0 ? a[o] : m == 1 ? a[2 + o] : m == 2 ? a[4 + o] : a[6 + o];
-  };
-  const QParam p0 = qparam(pick(mn, 0), pick(mx, 0), Lv, false);
-  const QParam p1 = qparam(pick(mn, 1), pick(mx, 1), Lv, false);
-  uint32_t sz[8];
-  float rr[8];
-#define KVQ_BCAST(K)                                                              \
-  sz[2 * K] = quad_bcast<K>(p0.sz);                                              \
-  sz[2 * K + 1] = quad_bcast<K>(p1.sz);                                          \
-  rr[2 * K] = __uint_as_float(quad_bcast<K>(__float_as_uint(p0.r)));             \
-  rr[2 * K + 1] = __uint_as_float(quad_bcast<K>(__float_as_uint(p1.r)));
-  KVQ_BCAST(0) KVQ_BCAST(1) KVQ_BCAST(2) KVQ_BCAST(3)
-#undef KVQ_BCAST
-  // half-word of channel k: its 8 tokens' codes at positions pi(i), summed
-  // as exact float integers (digit * 4^position, below 2^16); codes above 3
-  // (high-precision slots) split into a low digit here and a high digit in hh
-  float hf[8], hhf[8];
-  uint32_t h[8], hh[8];
-#pragma unroll
-  for (int k = 0; k < 8; k++) hf[k] = hhf[k] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const float z = half_bits_to_f32((uint16_t)(sz[i] >> 16));
-    const float mul = (float)(1u << (2 * pos_swap(i)));
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const float q = qcode(x(i, k), z, rr[i], Lv);
-      if constexpr (VHI) {
-        const float hd = floorf(q * 0.25f);
-        hf[k] = fmaf(fmaf(hd, -4.0f, q), mul, hf[k]);
-        hhf[k] = fmaf(hd, mul, hhf[k]);
-      } else {
-        hf[k] = fmaf(q, mul, hf[k]);
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 8; k++) {
-    h[k] = (uint32_t)hf[k];
-    hh[k] = (uint32_t)hhf[k];
-  }
-  // Word (j*4 + tq)*16 + c holds channel 32j + c (bits 0..15) and 32j+16+c
-  // (bits 16..31).  Lane m holds channels 32j + 8m + k: m = 0, 1 are low
-  // halves, m = 2, 3 the high halves of the same words (quad partner m ^ 2).
-  // The low lane keeps words k = 0..3 of its eight, the high lane k = 4..7.
-  const bool low = m < 2;
-  auto words = [&](const uint32_t (&hv)[8], uint32_t (&wd)[4]) {
-    const uint32_t s0 = low ? (hv[4] | (hv[5] << 16)) : (hv[0] | (hv[1] << 16));
-    const uint32_t s1 = low ? (hv[6] | (hv[7] << 16)) : (hv[2] | (hv[3] << 16));
-    const uint32_t r0 = dpp<QUAD_XOR2>(s0), r1 = dpp<QUAD_XOR2>(s1);
-    const uint32_t o[4] = {r0 & 0xFFFFu, r0 >> 16, r1 & 0xFFFFu, r1 >> 16};
-#pragma unroll
-    for (int q = 0; q < 4; q++)
-      wd[q] = low ? (hv[q] | (o[q] << 16)) : (o[q] | (hv[4 + q] << 16));
-  };
-  uint32_t wd[4];
-  words(h, wd);
-  const int c0 = 8 * (m & 1) + 4 * (m >> 1);
-  *(uint4*)(vc_out + (j * 4 + tq) * 16 + c0) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-  if constexpr (VHI) {
-    uint32_t wh[4];
-    words(hh, wh);
-    if (hiblk)
-      *(uint4*)(vhi_out + 8 + (j * g.n_vhi + tq) * 16 + c0) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-  }
-  if (m < 2) {
-    uint32_t mm[4];
-#pragma unroll
-    for (int p = 0; p < 4; p++)
-      mm[p] = m == 0 ? (sz[2 * p] & 0xFFFFu) | (sz[2 * p + 1] << 16)
-                     : (sz[2 * p] >> 16) | (sz[2 * p + 1] & 0xFFFF0000u);
-    *(uint4*)(meta_out + m * D + j * GS + 8 * tq) = make_uint4(mm[0], mm[1], mm[2], mm[3]);
-  }
-}
+// The device code that packs one 32-token group (one wave for its keys, one
+// for its values) is in quant_group.h, shared with the decode kernel's
+// append step.
 
 // ------------------------------------------------------------------ prefill
 
@@ -626,8 +118,7 @@ template <bool BF, bool VHI>
 __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new,
                                                      kvq_cache c) {
-  __shared__ KeyLds lds;
-  __shared__ __align__(16) uint32_t vord[8];
+  __shared__ PackLds lds;
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int T = c.len[bh];
   if (T < 0 || T >= g.max_tokens) {  // full, or a length no call of this library wrote
@@ -640,30 +131,7 @@ __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __re
   rk[(size_t)slot * D + tid] = k_new[(size_t)bh * D + tid];
   rv[((size_t)(slot / GS) * D + tid) * GS + slot % GS] = v_new[(size_t)bh * D + tid];
   const int nq0 = n_quant(T, g.R);
-  if (n_quant(T + 1, g.R) > nq0) {
-    // the group [nq0, nq0 + 32) ends at T + 1 - R <= T: the new token is not in it
-    const int grp = nq0 / GS, s0 = nq0 % g.RS;
-    const size_t rec = (size_t)bh * g.NG + grp;
-    uint32_t* vhi = c.v_hi + rec * g.vhi_words;
-    if (tid < 64) {
-      key_group_wave<BF, VHI>(g, rk + (size_t)s0 * D, pair_masks(g, c.pairs + (size_t)bh * NPAIR),
-                              (uint32_t*)c.k_lo + rec * GROUP_WORDS,
-                              (uint8_t*)c.k_hi + rec * g.khi_bytes,
-                              (uint16_t*)c.k_meta + rec * 2 * D, lds);
-      if constexpr (VHI)
-        if (tid < 2) ((uint4*)vhi)[tid] = ((const uint4*)lds.ord)[tid];
-    } else {
-      uint2 pos = make_uint2(0, 0);
-      if constexpr (VHI) {
-        token_order_wave<BF>(rk + (size_t)s0 * D, vord);
-        wave_lds_sync();
-        pos = ((const uint2*)vord)[((tid & 63) >> 4)];
-      }
-      value_group_wave<BF, true, VHI>(g, rv + (size_t)(s0 / GS) * D * GS, pos,
-                                      (uint32_t*)c.v_codes + rec * GROUP_WORDS,
-                                      (uint16_t*)c.v_meta + rec * 2 * D, vhi);
-    }
-  }
+  if (n_quant(T + 1, g.R) > nq0) pack_ring_group<BF, VHI>(g, c, bh, nq0, tid, lds);
   __syncthreads();
   if (tid == 0) c.len[bh] = T + 1;
 }

@@ -149,6 +149,15 @@ def kvq_decode_attn_pruned(layout, q, cache: kvq_cache, sm_scale, n_splits, n_ke
           _ptr(workspace), ctypes.c_size_t(ws_bytes), _ptr(out), _stream(stream))
 
 
+def kvq_append_decode_attn(layout, k_new, v_new, q, cache: kvq_cache, sm_scale, n_splits,
+                           workspace, out, stream=None, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _call("kvq_append_decode_attn", ctypes.byref(layout), _ptr(k_new), _ptr(v_new), _ptr(q),
+          ctypes.byref(cache), ctypes.c_float(sm_scale), ctypes.c_int32(n_splits),
+          _ptr(workspace), ctypes.c_size_t(ws_bytes), _ptr(out), _stream(stream))
+
+
 def kvq_check(cache: kvq_cache, stream=None) -> int:
     err = ctypes.c_int32(0)
     _call("kvq_check", ctypes.byref(cache), ctypes.byref(err), _stream(stream))

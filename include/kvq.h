@@ -308,6 +308,30 @@ kvq_status kvq_decode_attn_pruned(const kvq_layout *L, const void *q,
                                   void *workspace, size_t ws_bytes, void *out,
                                   void *stream);
 
+/* One decode step in one launch: kvq_append of (k_new, v_new), then
+ * single-token decode attention of q over the cache including the new token
+ * ([PM-KVQ] key_machinery: new tokens are held at 16 bits first and
+ * quantized later; [PN-Mix] abstract: decode reads the low-bit cache).
+ * Per (b, kv head), with T = len before the call:
+ *  - if 0 <= T < max_tokens: the token is appended exactly as kvq_append
+ *    does it (ring slot T mod RS, len = T + 1, and the group of positions
+ *    [n_q(T), n_q(T) + 32) is packed when n_q(T + 1) > n_q(T)); attention
+ *    runs over all T + 1 tokens, with the quantized prefix of before the
+ *    append, n_q(T): a group that this call packs is attended at 16 bits in
+ *    this call (it is still in the ring) and quantized from the next call on.
+ *    Where no group is packed the output equals kvq_append followed by
+ *    kvq_decode_attn.
+ *  - if T == max_tokens (T < 0): sets err bit 0 (bit 1), changes nothing,
+ *    and decodes over the cache as it stands.
+ * Saves the append's launch.  Pruned key chunks are not offered here.
+ *   k_new, v_new: [B][Hkv][128] io dtype;  q, out: as for kvq_decode_attn.
+ * Other arguments, limits and errors as for kvq_decode_attn. */
+kvq_status kvq_append_decode_attn(const kvq_layout *L, const void *k_new,
+                                  const void *v_new, const void *q,
+                                  kvq_cache *cache, float sm_scale,
+                                  int32_t n_splits, void *workspace,
+                                  size_t ws_bytes, void *out, void *stream);
+
 /* Synchronizes `stream`, then copies cache->err to *host_err (tests and
  * debugging only). */
 kvq_status kvq_check(const kvq_cache *cache, int32_t *host_err /*host*/,

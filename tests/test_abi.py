@@ -32,7 +32,8 @@ def test_library_exports_every_declared_entry_point():
     assert set(names) >= {"kvq_select_pairs", "kvq_quant_keys", "kvq_quant_values",
                           "kvq_append", "kvq_decode_attn", "kvq_cache_sizes",
                           "kvq_workspace_bytes", "kvq_check", "kvq_status_str", "kvq_shrink",
-                          "kvq_select_pairs_qa", "kvq_decode_attn_pruned"}
+                          "kvq_select_pairs_qa", "kvq_decode_attn_pruned",
+                          "kvq_append_decode_attn"}
     lib = kvq.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -140,6 +141,16 @@ def test_decode_validation():
     assert status_of("kvq_decode_attn_pruned", ctypes.byref(L), P(FAKE), ctypes.byref(c),
                      ctypes.c_float(0.088), 8, 2, P(FAKE), ctypes.c_size_t(ws - 1), P(FAKE),
                      P(0)) == ECAPACITY
+    # the append-and-decode call: its token pointers, then the decode checks
+
+    def fused(k=FAKE, v=FAKE, sm=0.088, wsb=ws):
+        return status_of("kvq_append_decode_attn", ctypes.byref(L), P(k), P(v), P(FAKE),
+                         ctypes.byref(c), ctypes.c_float(sm), 8, P(FAKE), ctypes.c_size_t(wsb),
+                         P(FAKE), P(0))
+    assert fused(k=0) == EINVAL and fused(v=0) == EINVAL
+    assert fused(v=FAKE + 4) == EALIGN
+    assert fused(sm=0.0) == EINVAL
+    assert fused(wsb=ws - 1) == ECAPACITY
 
 
 @no_gpu

@@ -442,3 +442,67 @@ def test_state_no_call_wrote_stays_in_bounds():
     torch.cuda.synchronize()
     qz = cv.oracle_quant()
     compare_cache(cv, qz, qz.nq // 32)
+
+
+FUSED = [
+    kvq_synth.Workload("fused-gqa4", 2, 8, 2, 330, n_qry=8, io_dtype="bf16", outliers="pct2x10",
+                       n_pairs_hi=6, residual=64, seed=101),
+    kvq_synth.Workload("fused-fp16-g1", 1, 3, 3, 200, n_qry=8, io_dtype="fp16", n_pairs_hi=8,
+                       residual=32, seed=102),
+    kvq_synth.Workload("fused-raw16", 1, 8, 2, 230, n_qry=8, io_dtype="bf16", n_pairs_hi=6,
+                       bits_hi=16, residual=32, seed=103),
+    kvq_synth.Workload("fused-lo1-vmix", 1, 8, 2, 230, n_qry=8, io_dtype="bf16", n_pairs_hi=0,
+                       n_pairs_lo1=32, residual=32, seed=104, n_vblk_hi=2, bits_vhi=4),
+]
+
+
+@pytest.mark.parametrize("w", FUSED, ids=_ids)
+def test_append_and_decode_in_one_launch(w):
+    # every step's output against the oracle of the fused call (the group
+    # packed by a step is attended at 16 bits in that step), then every byte
+    # against the prefill of the same tokens
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    T0 = w.tokens - 100
+    case = Case(w, T=T0, max_tokens=w.tokens)
+    pairs = case.oracle_select()[1]
+    S = 3
+    ws = torch.zeros(kvq.kvq_workspace_bytes(case.layout, S), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    q_bits = case.d["q_dec"][:, :, 0]
+    q = dev(q_bits)
+    packed = 0
+    for t in range(T0, w.tokens):
+        kvq.kvq_append_decode_attn(case.layout, dev(np.ascontiguousarray(case.d["k"][:, :, t])),
+                                   dev(np.ascontiguousarray(case.d["v"][:, :, t])), q,
+                                   case.cache.struct, SM_SCALE, S, ws, out)
+        qz = case.oracle_quant(T=t + 1, pairs=pairs)
+        packed += oracle.n_quant(t + 1, w.residual) > oracle.n_quant(t, w.residual)
+        got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype)
+        check_output(got, oracle.attention_after_append(qz, q_bits, SM_SCALE), w.io_dtype, ATOL)
+    assert packed >= 2
+    assert kvq.kvq_check(case.cache.struct) == 0
+    case.T = w.tokens
+    qz = case.oracle_quant(pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
+
+
+def test_append_and_decode_at_capacity():
+    # a full cache: error bit 0, nothing changes, the output is the plain decode
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    w = kvq_synth.Workload("cap", 1, 4, 1, 96, n_qry=4, io_dtype="bf16", residual=32, seed=33)
+    case = Case(w, T=96, max_tokens=96)
+    q_bits = case.d["q_dec"][:, :, 0]
+    want = case.decode(q_bits, 3)
+    before = case.gpu_bytes()
+    ws = torch.zeros(kvq.kvq_workspace_bytes(case.layout, 3), dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, 4, 128), dtype=torch.int16, device="cuda")
+    z = dev(np.zeros((1, 1, 128), np.uint16))
+    kvq.kvq_append_decode_attn(case.layout, z, z, dev(q_bits), case.cache.struct, SM_SCALE, 3,
+                               ws, out)
+    assert kvq.kvq_check(case.cache.struct) == 1
+    assert np.array_equal(kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), "bf16"), want)
+    after = case.gpu_bytes()
+    for k in before:
+        assert np.array_equal(before[k], after[k])
