@@ -506,3 +506,33 @@ def test_append_and_decode_at_capacity():
     after = case.gpu_bytes()
     for k in before:
         assert np.array_equal(before[k], after[k])
+
+
+@pytest.mark.parametrize("w", [
+    kvq_synth.Workload("fused-from-one", 1, 8, 2, 100, n_qry=8, io_dtype="bf16", n_pairs_hi=6,
+                       residual=32, seed=105),
+    kvq_synth.Workload("fused-from-one-vmix", 1, 4, 1, 100, n_qry=8, io_dtype="fp16",
+                       n_pairs_hi=6, residual=32, seed=106, n_vblk_hi=1, bits_vhi=3),
+], ids=_ids)
+def test_append_and_decode_from_one_token(w):
+    # ring-only steps, then the first two packed groups (R = 32: at T = 64, 96)
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    case = Case(w, T=1, max_tokens=w.tokens)
+    pairs = case.oracle_select()[1]
+    ws = torch.zeros(kvq.kvq_workspace_bytes(case.layout, 2), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    q_bits = case.d["q_dec"][:, :, 0]
+    q = dev(q_bits)
+    for t in range(1, w.tokens):
+        kvq.kvq_append_decode_attn(case.layout, dev(np.ascontiguousarray(case.d["k"][:, :, t])),
+                                   dev(np.ascontiguousarray(case.d["v"][:, :, t])), q,
+                                   case.cache.struct, SM_SCALE, 2, ws, out)
+        qz = case.oracle_quant(T=t + 1, pairs=pairs)
+        got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype)
+        check_output(got, oracle.attention_after_append(qz, q_bits, SM_SCALE), w.io_dtype, ATOL)
+    assert kvq.kvq_check(case.cache.struct) == 0
+    case.T = w.tokens
+    qz = case.oracle_quant(pairs=pairs)
+    assert qz.nq == 64
+    compare_cache(case, qz, qz.nq // 32)
