@@ -177,3 +177,14 @@ def test_prefill_and_append_validation():
     assert status_of("kvq_shrink", ctypes.byref(L), ctypes.byref(c), 5, 4, P(0)) == EINVAL
     L16 = L32k(bits_hi=16)
     assert status_of("kvq_shrink", ctypes.byref(L16), ctypes.byref(c), 0, 4, P(0)) == ENOTSUP
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the benchmark measures one GPU; asked for more it says so and exits 2
+    # before touching a device
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
