@@ -23,16 +23,19 @@
 // K-lanes 16..31 of that MFMA.
 //
 // Work split: an 8-wave workgroup per (sequence, KV head, token split), one
-// workgroup per CU by default.  The waves take the split's 32-token blocks
-// round-robin, each with its own online softmax (base 2, scale folded into
-// the exponent; the running max is raised only when a block exceeds it by
-// more than 2^8, so most blocks skip the rescale).  Four blocks' codes and
-// scale/zero records are in flight per wave in registers; the record of the
-// block in work is staged through a per-wave LDS buffer so that the 16 lanes
-// sharing a channel slice read it as a broadcast.  The waves merge in LDS
-// into one record per head (m, l, o/l in fp16); the last workgroup of a
-// (sequence, KV head) to finish (atomic counter) merges the split records
-// with the log-sum-exp rule and writes the output.
+// workgroup per CU by default.  The 32-token blocks of a (sequence, KV head)
+// are dealt to its waves interleaved across splits (block b to the wave w of
+// split s with s + S w = b mod S * 8), each wave with its own online softmax
+// (base 2, scale folded into the exponent; the running max is raised only
+// when a block exceeds it by more than 2^8, so most blocks skip the
+// rescale).  The codes and scale/zero records of the next PF blocks are in
+// flight per wave in registers; the record of the block in work is staged
+// through a per-wave LDS buffer so that the 16 lanes sharing a channel slice
+// read it as a broadcast.  The waves merge in LDS into one record per head
+// (m, l, o/l in fp16); the last workgroup of a (sequence, KV head) to finish
+// (atomic counter) merges the split records with the log-sum-exp rule and
+// writes the output.  The fused variant also carries the step's append (see
+// FUSED at the kernel).
 #include "common.h"
 #include "internal.h"
 #include "quant_group.h"
