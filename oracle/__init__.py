@@ -18,6 +18,12 @@ outliers, RoPE invariance and token-order invariance; packing against an
 independent bit-level unpacker; attention against textbook softmax attention
 (all-16-bit cache), T = 1, q = 0 and a brute-force pass over the dequantized
 cache.
+
+Parity unpinned: the query-aware pair score (select_qa), the kept key chunks
+of pruned decode (prune_chunks) and the token order of two value precisions
+(order in quantize) follow rules the pages describe without a formula; their
+tests pin each to its own rule (float sums, invariances, planted cases), not
+to values the pages fix.
 """
 from __future__ import annotations
 

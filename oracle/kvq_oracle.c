@@ -26,7 +26,14 @@
  *   saliency sums in fixed point u(n) = floor(n * 2^24) of fp32 norms;
  *   z = fp16(min), s = fp16((max - z) / L), codes rint((x - z) * (1/s));
  *   K groups = 32 tokens of one channel; V groups = 32 channels of one token;
- *   n_q(T) = 32 * floor(max(0, T - R) / 32) quantized tokens, the rest raw.
+ *   n_q(T) = 32 * floor(max(0, T - R) / 32) quantized tokens, the rest raw;
+ *   the rules of orc_select_qa, orc_prune_chunks and orc_token_order, which
+ *   the pages describe without a formula.
+ *
+ * Parity unpinned: orc_select_qa, orc_prune_chunks and orc_token_order have
+ * no value the pages fix.  Their tests pin each to its own stated rule
+ * (float sums where they separate, invariances, planted cases), not to the
+ * pages.
  */
 #include <math.h>
 #include <stdint.h>
