@@ -27,8 +27,8 @@
 // are dealt to its waves interleaved across splits (block b to the wave w of
 // split s with s + S w = b mod S * 8), each wave with its own online softmax
 // (base 2, scale folded into the exponent; the running max is raised only
-// when a block exceeds it by more than 2^8, so most blocks skip the
-// rescale).  The codes and scale/zero records of the next PF blocks are in
+// when a block's weights would exceed 2, so most blocks skip the rescale and
+// the fp16 products of weights and value scales stay finite).  The codes and scale/zero records of the next PF blocks are in
 // flight per wave in registers; the record of the block in work is staged
 // through a per-wave LDS buffer so that the 16 lanes sharing a channel slice
 // read it as a broadcast.  The waves merge in LDS into one record per head
@@ -59,7 +59,10 @@ constexpr int NW = 8;                  // waves per workgroup (one workgroup per
 constexpr int WG_THREADS = 64 * NW;
 constexpr int PF = 2;                  // quantized groups in flight per wave
 constexpr int MAXG = 16;
-constexpr float RESCALE_SLACK = 8.0f;  // log2 headroom before the running max moves
+// log2 headroom before the running max moves.  It bounds the softmax
+// weights p by 2^1, so that the fp16 products p * s of the value path stay
+// finite for every value scale (s <= 65504 / 3).
+constexpr float RESCALE_SLACK = 1.0f;
 
 __device__ inline uint32_t h2u(h2 x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ inline h2 u2h(uint32_t x) { return __builtin_bit_cast(h2, x); }
@@ -78,6 +81,30 @@ template <bool BF16>
 __device__ inline uint32_t to_f16_pair(uint32_t w) {
   if constexpr (!BF16) return w;
   return pk_rne(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
+// An io-dtype pair as two floats (exact).
+template <bool BF16>
+__device__ inline void io_pair_f32(uint32_t w, float& a, float& b) {
+  if constexpr (BF16) {
+    a = __uint_as_float(w << 16);
+    b = __uint_as_float(w & 0xffff0000u);
+  } else {
+    a = half_bits_to_f32((uint16_t)(w & 0xFFFF));
+    b = half_bits_to_f32((uint16_t)(w >> 16));
+  }
+}
+
+// An io-dtype pair times a power of two, in the io dtype (exact for bf16;
+// fp16 rounds only where the product is subnormal).
+template <bool BF16>
+__device__ inline uint32_t scaled_io_pair(uint32_t w, float pow2) {
+  float a, b;
+  io_pair_f32<BF16>(w, a, b);
+  a *= pow2;
+  b *= pow2;
+  if constexpr (BF16) return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+  return pk_rne(a, b);
 }
 
 // Two codes of nibble pair `byte` of w (each nibble 0..3, value = code / 2 in
@@ -417,12 +444,35 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int mla = (lane >= 32 || ((kmask >> ((lane & 15) >> 2)) & 1u))
                       ? (lane & 31) : ((lane & 16) | (kept0 << 2) | (lane & 3));
 
-  // query as fp16 pairs (zero past the G heads)
+  // The quantized path multiplies q by key scales in fp16 (q*s, 4*q*s), so
+  // each head's query is first scaled by a power of two 2^-qe that puts its
+  // largest magnitude in [1/8, 1/4): then 4 |q| s < s <= 65504 for every
+  // channel.  The scaling is exact (barring fp16 subnormals); the head's
+  // logits take the factor back through sc_q.  Ring tokens use the raw query.
+  float qmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      float a, b;
+      io_pair_f32<BF16>(qv[i][e], a, b);
+      qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(b)));
+    }
+  qmax = wave_max_kq(qmax);  // over the head's 128 channels (the 4 lanes of column col)
+  const int qbexp = (int)((__float_as_uint(qmax) >> 23) & 0xFFu);
+  const int qe = qbexp ? min(max(qbexp - 124, -100), 100) : 0;  // largest |q| < 2^(qe - 2)
+  const float qsc = __uint_as_float((uint32_t)(127 - qe) << 23);  // 2^-qe
+  const float sc_q = scale_log2 * __uint_as_float((uint32_t)(127 + qe) << 23);
+  // query as fp16 pairs, scaled (zero past the G heads)
   uint32_t q16[16];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int e = 0; e < 4; e++) q16[4 * i + e] = hvalid ? to_f16_pair<BF16>(qv[i][e]) : 0u;
+    for (int e = 0; e < 4; e++) {
+      float a, b;
+      io_pair_f32<BF16>(qv[i][e], a, b);
+      q16[4 * i + e] = hvalid ? pk_rne(a * qsc, b * qsc) : 0u;
+    }
 
   uint32_t qhi[4] = {0, 0, 0, 0};  // HIMODE 4: 4*q (fp16); HIMODE 16: raw q
   float q4f[8];                    // HIMODE 4: 4*q in fp32
@@ -437,7 +487,12 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         *(u4*)&wq[col][32 * kq + 8 * i] = u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
-        if constexpr (HIMODE == 16) *(u4*)&wr[col][32 * kq + 8 * i] = qv[i];
+        if constexpr (HIMODE == 16) {  // raw salient keys meet the scaled query in its io dtype
+          u4 r;
+#pragma unroll
+          for (int e = 0; e < 4; e++) r[e] = scaled_io_pair<BF16>(qv[i][e], qsc);
+          *(u4*)&wr[col][32 * kq + 8 * i] = r;
+        }
       }
     }
     bool sal = false;
@@ -652,7 +707,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     float cr[8], p[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) cr[i] = C[i >> 2][i & 3];
-    softmax_step(cr, scale_log2, p);
+    softmax_step(cr, sc_q, p);
     const u4 P = u4{pk_rne(p[0], p[1]), pk_rne(p[2], p[3]), pk_rne(p[4], p[5]), pk_rne(p[6], p[7])};
     // values
     const bool vkept = VHI && kq < g.n_vhi;

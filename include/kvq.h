@@ -36,7 +36,8 @@
  *     its loaded code objects; calls on different caches may run concurrently.
  *   - 16-bit inputs (KVQ_FP16 or KVQ_BF16, `io_dtype`) are contiguous,
  *     row-major, last dimension = channel.  Inputs must be finite with
- *     |x| <= 32752 (so that every scale below stays finite).
+ *     |x| <= 32752, so that every scale below stays finite; for such inputs
+ *     every intermediate of decoding stays finite too.
  *
  * Shapes: B = batch, Hq = query heads, Hkv = KV heads, G = Hq / Hkv (query
  * heads sharing one KV head; 1 <= G <= 16), D = head_dim = 128, 64 RoPE pairs.
@@ -276,7 +277,11 @@ kvq_status kvq_shrink(const kvq_layout *L, kvq_cache *cache, int32_t g0,
  * (b, kv head) (limits as for kvq_workspace_bytes), each reduced with an
  * online softmax; a log-sum-exp combine merges them inside the same launch.
  * Computation is fp32 with fp16 matrix operands; the result is rounded to
- * the io dtype (nearest even).  Requires T >= 1 (T = 0 writes zeros); a
+ * the io dtype (nearest even).  The fp16 operands (each head's query scaled
+ * by a power of two so that q * s stays in range, the softmax weights, at
+ * most 2) carry a relative 2^-11 per term, so the error grows with the size
+ * of the logits: with |q| |k| in the thousands the softmax can move beyond
+ * the 2e-3 of ordinary data.  Requires T >= 1 (T = 0 writes zeros); a
  * len outside [0, max_tokens] is clamped into it (the result is then
  * unspecified, but every read stays inside the cache).
  *   q   [B][Hq][128] io dtype;  out [B][Hq][128] io dtype

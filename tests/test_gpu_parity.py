@@ -536,3 +536,88 @@ def test_append_and_decode_from_one_token(w):
     qz = case.oracle_quant(pairs=pairs)
     assert qz.nq == 64
     compare_cache(case, qz, qz.nq // 32)
+
+
+DEGEN = [
+    kvq_synth.Workload("degenerate-bf16", 2, 8, 2, 300, n_qry=8, io_dtype="bf16",
+                       n_pairs_hi=6, residual=64, seed=111),
+    kvq_synth.Workload("degenerate-fp16", 2, 8, 2, 300, n_qry=8, io_dtype="fp16",
+                       n_pairs_hi=6, bits_hi=16, residual=64, seed=112),
+]
+
+
+@pytest.mark.parametrize("w", DEGEN, ids=_ids)
+def test_degenerate_groups(w):
+    # zero steps (s = 0): constant key channels, a group of identical key
+    # rows, constant value groups; an all-zero query for one sequence
+    # (uniform weights)
+    rng = np.random.default_rng(w.seed)
+    d = kvq_synth.generate(w)
+    kf = kvq_synth.bits_to_f64(d["k"], w.io_dtype)
+    vf = kvq_synth.bits_to_f64(d["v"], w.io_dtype)
+    for c in rng.choice(128, 10, replace=False):
+        kf[:, :, 0:32, c] = 0.75
+    kf[:, :, 32:64, :] = kf[:, :, 32:33, :]
+    for t in rng.choice(np.arange(64, 192), 12, replace=False):
+        vf[:, :, t, 32:64] = -1.5
+    d["k"] = kvq_synth.to_bits(kf, w.io_dtype)
+    d["v"] = kvq_synth.to_bits(vf, w.io_dtype)
+    q = d["q_dec"][:, :, 0].copy()
+    q[1] = 0
+    case = Case(w, data=d)
+    qz = case.oracle_quant()
+    assert np.any(qz.ks[:, :, :qz.nq // 32] == 0) and np.any(qz.vs[:, :, :qz.nq // 32] == 0)
+    compare_cache(case, qz, qz.nq // 32)
+    ref = oracle.attention(qz, q, SM_SCALE)
+    for S in (1, 4):
+        check_output(case.decode(q, S), ref, w.io_dtype, ATOL)
+
+
+@pytest.mark.parametrize("w", DEGEN, ids=_ids)
+def test_values_at_the_input_limit(w):
+    # values up to the documented limit |x| <= 32752: every byte bit-exact
+    # (scales near the top of fp16), outputs finite and within 2^-8 of each
+    # output row's largest magnitude (the fp16 weights p*s carry 2^-11)
+    from tests._gpu_case import half_ulp
+    rng = np.random.default_rng(w.seed + 1)
+    d = kvq_synth.generate(w)
+    vf = kvq_synth.bits_to_f64(d["v"], w.io_dtype)
+    big = 32752.0 if w.io_dtype == "fp16" else 32512.0  # largest value <= 32752 in the format
+    for t in rng.choice(w.tokens, 20, replace=False):
+        vf[:, :, t, rng.integers(128)] = big * (1 if rng.integers(2) else -1)
+    d["v"] = kvq_synth.to_bits(vf, w.io_dtype)
+    case = Case(w, data=d)
+    qz = case.oracle_quant()
+    compare_cache(case, qz, qz.nq // 32)
+    q = d["q_dec"][:, :, 0]
+    ref = oracle.attention(qz, q, SM_SCALE)
+    for S in (1, 4):
+        got = case.decode(q, S)
+        assert np.all(np.isfinite(got))
+        bound = (ATOL + half_ulp(ref, "fp16") + half_ulp(ref, w.io_dtype) +
+                 2.0 ** -8 * np.abs(ref).max(axis=-1, keepdims=True))
+        assert np.all(np.abs(got - ref) <= bound), np.abs(got - ref).max()
+
+
+@pytest.mark.parametrize("w", DEGEN, ids=_ids)
+def test_keys_and_queries_at_the_input_limit(w):
+    # keys up to the input limit and queries in the hundreds: every byte
+    # bit-exact and every output finite (the products q*s, formed in fp16, are
+    # kept in range by a power-of-two scaling of each head's query).  With
+    # logits this large the softmax is nearly one-hot and its conditioning,
+    # not the kernel, sets the error, so only finiteness and the bytes are
+    # checked here.
+    rng = np.random.default_rng(w.seed + 2)
+    d = kvq_synth.generate(w)
+    kf = kvq_synth.bits_to_f64(d["k"], w.io_dtype)
+    big = 32752.0 if w.io_dtype == "fp16" else 32512.0
+    for t in rng.choice(w.tokens, 20, replace=False):
+        kf[:, :, t, rng.integers(128)] = big * (1 if rng.integers(2) else -1)
+    d["k"] = kvq_synth.to_bits(kf, w.io_dtype)
+    qf = kvq_synth.bits_to_f64(d["q_dec"][:, :, 0], w.io_dtype) * 256
+    q = kvq_synth.to_bits(qf, w.io_dtype)
+    case = Case(w, data=d)
+    qz = case.oracle_quant()
+    compare_cache(case, qz, qz.nq // 32)
+    for S in (1, 4):
+        assert np.all(np.isfinite(case.decode(q, S)))
