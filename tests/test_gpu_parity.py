@@ -119,7 +119,8 @@ def test_split_counts_agree():
     w = SMALL[1]
     case = Case(w)
     q = case.d["q_dec"][:, :, 0]
-    outs = [case.decode(q, S) for S in (1, 7, 32, 256)]
+    outs = [case.decode(q, S) for S in (1, 7, 32, 256, 1024)]  # 1024: the largest accepted
+    check_output(outs[-1], oracle.attention(case.oracle_quant(), q, SM_SCALE), w.io_dtype, ATOL)
     for o in outs[1:]:
         # the fp32 results differ only by rounding order; stored in bf16 they
         # may land one output ulp apart
@@ -621,3 +622,37 @@ def test_keys_and_queries_at_the_input_limit(w):
     compare_cache(case, qz, qz.nq // 32)
     for S in (1, 4):
         assert np.all(np.isfinite(case.decode(q, S)))
+
+
+def test_capacity_within_the_residual_window():
+    # max_tokens <= R + 31: the cache has no quantized-group storage at all
+    # (its own kernel variant) and every token lives in the ring: prefill,
+    # decode, one-launch steps up to the capacity, then the capacity error
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    w = kvq_synth.Workload("ring-only-cap", 1, 8, 2, 60, n_qry=8, io_dtype="bf16", n_pairs_hi=6,
+                           residual=32, seed=121)
+    case = Case(w, T=40, max_tokens=60)
+    assert case.NG == 0
+    pairs = case.oracle_select()[1]
+    q_bits = case.d["q_dec"][:, :, 0]
+    qz = case.oracle_quant(pairs=pairs)
+    for S in (1, 3):
+        check_output(case.decode(q_bits, S), oracle.attention(qz, q_bits, SM_SCALE), w.io_dtype,
+                     ATOL)
+    ws = torch.zeros(kvq.kvq_workspace_bytes(case.layout, 3), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    q = dev(q_bits)
+    for t in range(40, 60):
+        kvq.kvq_append_decode_attn(case.layout, dev(np.ascontiguousarray(case.d["k"][:, :, t])),
+                                   dev(np.ascontiguousarray(case.d["v"][:, :, t])), q,
+                                   case.cache.struct, SM_SCALE, 3, ws, out)
+        qz = case.oracle_quant(T=t + 1, pairs=pairs)
+        got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype)
+        check_output(got, oracle.attention_after_append(qz, q_bits, SM_SCALE), w.io_dtype, ATOL)
+    assert kvq.kvq_check(case.cache.struct) == 0
+    case.T = 60
+    compare_cache(case, case.oracle_quant(pairs=pairs), 0)
+    z = dev(np.zeros((1, 2, 128), np.uint16))
+    kvq.kvq_append(case.layout, z, z, case.cache.struct)
+    assert kvq.kvq_check(case.cache.struct) == 1
