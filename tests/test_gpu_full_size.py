@@ -282,3 +282,40 @@ def test_batch_with_offsets_beyond_4gib():
         got = kvq_synth.bits_to_f64(host(out[b, kh * G:(kh + 1) * G], np.uint16)[None], "bf16")
         err = check_output(got, ref, "bf16", ATOL)
         print("b%d kh%d max|err| %.3g" % (b, kh, err), flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_streaming_b16_one_launch_steps():
+    # the streaming layer stepped with kvq_append_decode_attn, at the bench's
+    # split count: outputs at the step that packs a group and at the last
+    # step against the oracle, then every byte against the prefill
+    import torch
+    from decode_attention_select_amd import kvq
+    w = kvq_synth.workload("streaming-b16")
+    print("case", w.name, "one launch", flush=True)
+    n_app = 40
+    case = Case(w, T=w.tokens, max_tokens=w.max_tokens)
+    pairs = check_selection(case)
+    S = bench.default_splits(w)
+    ws = torch.zeros(kvq.kvq_workspace_bytes(case.layout, S), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    kn = dev(np.ascontiguousarray(case.d["k"][:, :, w.tokens:w.tokens + n_app]))
+    vn = dev(np.ascontiguousarray(case.d["v"][:, :, w.tokens:w.tokens + n_app]))
+    packs = [i for i in range(n_app) if oracle.n_quant(w.tokens + i + 1, w.residual) >
+             oracle.n_quant(w.tokens + i, w.residual)]
+    assert packs
+    for i in range(n_app):
+        q_bits = np.ascontiguousarray(case.d["q_dec"][:, :, i])
+        kvq.kvq_append_decode_attn(case.layout, kn[:, :, i].contiguous(), vn[:, :, i].contiguous(),
+                                   dev(q_bits), case.cache.struct, SM_SCALE, S, ws, out)
+        if i in (packs[0], n_app - 1):
+            qz = case.oracle_quant(T=w.tokens + i + 1, pairs=pairs)
+            got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype)
+            err = check_output(got, oracle.attention_after_append(qz, q_bits, SM_SCALE),
+                               w.io_dtype, ATOL)
+            print("step %d max|err| %.3g" % (i, err), flush=True)
+    assert kvq.kvq_check(case.cache.struct) == 0
+    T = w.tokens + n_app
+    case.T = T
+    qz = case.oracle_quant(T=T, pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
