@@ -27,8 +27,9 @@
 // are dealt to its waves interleaved across splits (block b to the wave w of
 // split s with s + S w = b mod S * 8), each wave with its own online softmax
 // (base 2, scale folded into the exponent; the running max is raised only
-// when a block's weights would exceed 2, so most blocks skip the rescale and
-// the fp16 products of weights and value scales stay finite).  The codes and scale/zero records of the next PF blocks are in
+// when a block's weights would exceed 2^8, or 2 in a group with very wide
+// value scales, so most blocks skip the rescale and the fp16 products of
+// weights and value scales stay finite).  The codes and scale/zero records of the next PF blocks are in
 // flight per wave in registers; the record of the block in work is staged
 // through a per-wave LDS buffer so that the 16 lanes sharing a channel slice
 // read it as a broadcast.  The waves merge in LDS into one record per head
@@ -59,10 +60,14 @@ constexpr int NW = 8;                  // waves per workgroup (one workgroup per
 constexpr int WG_THREADS = 64 * NW;
 constexpr int PF = 2;                  // quantized groups in flight per wave
 constexpr int MAXG = 16;
-// log2 headroom before the running max moves.  It bounds the softmax
-// weights p by 2^1, so that the fp16 products p * s of the value path stay
-// finite for every value scale (s <= 65504 / 3).
-constexpr float RESCALE_SLACK = 1.0f;
+// log2 headroom before the running max moves: the softmax weights p stay
+// below 2^slack.  The value path forms p * s in fp16, so a group holding a
+// value scale above 65504 / 2^8 (fp16 bits 0x5BFF) takes the slack 1 (p <= 2,
+// finite for every scale up to 65504 / 3); all other groups take 8, so that
+// most blocks skip the rescale.
+constexpr float RESCALE_SLACK = 8.0f;
+constexpr float RESCALE_SLACK_WIDE = 1.0f;
+constexpr uint32_t VSCALE_WIDE = 0x5BFFu;
 
 __device__ inline uint32_t h2u(h2 x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ inline h2 u2h(uint32_t x) { return __builtin_bit_cast(h2, x); }
@@ -81,6 +86,13 @@ template <bool BF16>
 __device__ inline uint32_t to_f16_pair(uint32_t w) {
   if constexpr (!BF16) return w;
   return pk_rne(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
+// Elementwise max of two u16 pairs.
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, a),
+                                                                __builtin_bit_cast(us2, b)));
 }
 
 // An io-dtype pair as two floats (exact).
@@ -563,12 +575,12 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // The running max moves only when some logit exceeds it by more than the
   // slack: a per-lane test and a ballot decide that; the cross-lane max is
   // taken only then.
-  auto softmax_step = [&](const float (&c)[8], float sc, float (&p)[8]) {
+  auto softmax_step = [&](const float (&c)[8], float sc, float slack, float (&p)[8]) {
     const float mc = fmaxf(fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])),
                            fmaxf(fmaxf(c[4], c[5]), fmaxf(c[6], c[7])));
-    if (__builtin_amdgcn_ballot_w64(mc * sc > m_run + RESCALE_SLACK)) {
+    if (__builtin_amdgcn_ballot_w64(mc * sc > m_run + slack)) {
       const float mx = wave_max_kq(mc) * sc;
-      const bool need = mx > m_run + RESCALE_SLACK;
+      const bool need = mx > m_run + slack;
       const float m_new = need ? mx : m_run;
       const float alpha = ex2(m_run - m_new);
 #pragma unroll
@@ -707,7 +719,13 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     float cr[8], p[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) cr[i] = C[i >> 2][i & 3];
-    softmax_step(cr, sc_q, p);
+    // lanes 32..47 staged the group's value scales (non-negative fp16, so
+    // their bits order as integers)
+    const uint32_t vs2 = pk_max_u16(pk_max_u16(cur.meta[0], cur.meta[1]),
+                                    pk_max_u16(cur.meta[2], cur.meta[3]));
+    const bool wide = lane >= 32 && lane < 48 && max(vs2 & 0xFFFFu, vs2 >> 16) > VSCALE_WIDE;
+    softmax_step(cr, sc_q, __builtin_amdgcn_ballot_w64(wide) ? RESCALE_SLACK_WIDE : RESCALE_SLACK,
+                 p);
     const u4 P = u4{pk_rne(p[0], p[1]), pk_rne(p[2], p[3]), pk_rne(p[4], p[5]), pk_rne(p[6], p[7])};
     // values
     const bool vkept = VHI && kq < g.n_vhi;
@@ -795,7 +813,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       const int t = 8 * kq + 4 * (i >> 2) + (i & 3);
       cr[i] = t < nvalid ? C[i >> 2][i & 3] : -INFINITY;
     }
-    softmax_step(cr, scale_log2, p);
+    softmax_step(cr, scale_log2, RESCALE_SLACK, p);  // raw values: the products stay in fp32
 #pragma unroll
     for (int i = 0; i < 8; i++) l_raw += p[i];
     uint32_t Ph[4], Pl[4];
