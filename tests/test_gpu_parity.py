@@ -656,3 +656,59 @@ def test_capacity_within_the_residual_window():
     z = dev(np.zeros((1, 2, 128), np.uint16))
     kvq.kvq_append(case.layout, z, z, case.cache.struct)
     assert kvq.kvq_check(case.cache.struct) == 1
+
+
+def _random_layouts(n, seed):
+    """Seeded draws over the layout space the ABI accepts (small sizes)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2, 3]))
+        R = int(rng.choice([32, 64, 96, 128]))
+        n_hi = int(rng.integers(0, 9))
+        bits_hi = int(rng.choice([4, 16]))
+        n_lo1 = int(rng.choice([0, 0, 8, 32]))
+        nvb = int(rng.choice([0, 0, 1, 2, 3, 4]))
+        T = int(rng.integers(1, 720))
+        out.append(kvq_synth.Workload(
+            "rand%d" % i, int(rng.integers(1, 3)), G * Hkv, Hkv, T + 1, n_qry=8,
+            io_dtype=str(rng.choice(["fp16", "bf16"])),
+            outliers=str(rng.choice(["none", "pairs4x8", "pct2x10"])), n_pairs_hi=n_hi,
+            bits_hi=bits_hi, n_pairs_lo1=n_lo1, residual=R, seed=200 + i, n_vblk_hi=nvb,
+            bits_vhi=int(rng.choice([3, 4]))))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_layouts(12, 7), ids=_ids)
+def test_random_layouts(w):
+    # prefill w.tokens - 1 tokens: every byte; plain and pruned decode at a
+    # drawn split count; one one-launch step (the last token)
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    rng = np.random.default_rng(w.seed)
+    T0 = w.tokens - 1
+    case = Case(w, T=T0, max_tokens=w.tokens)
+    pairs = case.oracle_select()[1]
+    if T0 >= 1:
+        qz = case.oracle_quant(pairs=pairs)
+        compare_cache(case, qz, qz.nq // 32)
+        q = case.d["q_dec"][:, :, 0]
+        S = int(rng.integers(1, 10))
+        check_output(case.decode(q, S), oracle.attention(qz, q, SM_SCALE), w.io_dtype, ATOL)
+        keep = int(rng.integers(1, 4))
+        check_output(case.decode_pruned(q, S, keep), oracle.attention_pruned(qz, q, SM_SCALE, keep),
+                     w.io_dtype, ATOL)
+    S = int(rng.integers(1, 10))
+    ws = torch.zeros(kvq.kvq_workspace_bytes(case.layout, S), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    q_bits = case.d["q_dec"][:, :, 0]
+    kvq.kvq_append_decode_attn(case.layout, dev(np.ascontiguousarray(case.d["k"][:, :, T0])),
+                               dev(np.ascontiguousarray(case.d["v"][:, :, T0])), dev(q_bits),
+                               case.cache.struct, SM_SCALE, S, ws, out)
+    assert kvq.kvq_check(case.cache.struct) == 0
+    case.T = w.tokens
+    qz = case.oracle_quant(pairs=pairs)
+    got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype)
+    check_output(got, oracle.attention_after_append(qz, q_bits, SM_SCALE), w.io_dtype, ATOL)
+    compare_cache(case, qz, qz.nq // 32)
