@@ -712,3 +712,40 @@ def test_random_layouts(w):
     got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype)
     check_output(got, oracle.attention_after_append(qz, q_bits, SM_SCALE), w.io_dtype, ATOL)
     compare_cache(case, qz, qz.nq // 32)
+
+
+@pytest.mark.parametrize("w", _random_layouts(12, 7), ids=_ids)
+def test_random_layouts_query_aware_and_shrink(w):
+    # the query-aware scorer (scores and ranks), then, on the prefilled cache,
+    # the shrink of a drawn group range (4-bit salient layouts): bytes and decode
+    from decode_attention_select_amd import kvq
+    from tests._gpu_case import dev
+    rng = np.random.default_rng(w.seed + 7)
+    case = Case(w, T=w.tokens)
+    kvq.kvq_select_pairs_qa(case.layout, case.q_sel, w.n_qry, case.k_sel, w.tokens,
+                            case.cache.struct)
+    torch.cuda.synchronize()
+    S, pairs_qa = oracle.select_qa(case.d["q_sel"], case.d["k"], w.tokens, w.n_kv_heads,
+                                   w.io_dtype)
+    g = case.gpu_bytes()
+    assert np.array_equal(g["sums"][:, :, 0], S.view(np.uint64))
+    assert np.array_equal(g["pairs"], pairs_qa)
+    if w.bits_hi != 4 or w.n_pairs_hi == 0:
+        return
+    # re-prefill with the query-aware ranking in place, then shrink
+    case2 = Case(w, T=w.tokens)
+    kvq.kvq_select_pairs_qa(case2.layout, case2.q_sel, w.n_qry, case2.k_sel, w.tokens,
+                            case2.cache.struct)
+    kvq.kvq_quant_keys(case2.layout, dev(case2.d["k"][:, :, :w.tokens]), w.tokens,
+                       case2.cache.struct)
+    kvq.kvq_quant_values(case2.layout, dev(case2.d["v"][:, :, :w.tokens]), w.tokens,
+                         case2.cache.struct)
+    ng = oracle.n_quant(w.tokens, w.residual) // 32
+    g0 = int(rng.integers(0, ng + 1))
+    g1 = int(rng.integers(g0, ng + 2))
+    kvq.kvq_shrink(case2.layout, case2.cache.struct, g0, g1)
+    torch.cuda.synchronize()
+    qz = oracle.shrink(case2.oracle_quant(pairs=pairs_qa), g0, min(g1, case2.NG))
+    compare_cache(case2, qz, qz.nq // 32)
+    q = case2.d["q_dec"][:, :, 0]
+    check_output(case2.decode(q, 3), oracle.attention(qz, q, SM_SCALE), w.io_dtype, ATOL)
