@@ -31,7 +31,8 @@ __global__ void zero_u64_kernel(uint64_t* p, int n) {
 // between y- y (y y+) and the squared midpoint, so these signs decide the
 // rounding.  Below s = 2^-48 every candidate is under 2^-24 and u = 0, so
 // subnormal estimates cannot matter.  n * 2^24 and its floor are exact in
-// double; a thread's sum of eight such terms stays exact for norms below
+// fp32 (a power-of-two scaling, then an fp32 floor), and so in double; a
+// thread's sum of eight such terms in double stays exact for norms below
 // 2^25.
 template <bool BF>
 __device__ inline double norm_fixed(uint16_t a_bits, uint16_t b_bits) {
@@ -43,7 +44,8 @@ __device__ inline double norm_fixed(uint16_t a_bits, uint16_t b_bits) {
   const float rm = fmaf(-ym, y0, s), rp = fmaf(-yp, y0, s);
   float y = rm <= 0.0f ? ym : y0;
   y = rp > 0.0f ? yp : y;
-  return floor((double)y * 16777216.0);
+  // y * 2^24 is exact in fp32 (a power-of-two scaling), so is its floor
+  return (double)floorf(y * 16777216.0f);
 }
 
 // 16-bit element e (0..7) of a 16-byte row chunk.
@@ -200,7 +202,8 @@ __global__ __launch_bounds__(256) void qa_ranges_kernel(Geo g, const uint16_t* _
         }
         mn = qa_quad_min(mn);
         mx = qa_quad_max(mx);
-        acc[e] += (uint64_t)((double)__fsub_rn(mx, mn) * 65536.0);  // >= 0: truncation = floor
+        // range * 2^16 is exact and below 2^32 (range <= 65504): truncation = floor
+        acc[e] += (uint32_t)(__fsub_rn(mx, mn) * 65536.0f);
       }
     }
   }
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(256) void qa_rank_kernel(Geo g, const uint16_t* __r
 #pragma unroll
       for (int e = 0; e < 8; e++) {
         const float x = fabsf(in_to_f32(sel_half(v[i], e), g.bf16));
-        acc[e] += floor((double)x * 16777216.0);
+        acc[e] += (double)floorf(x * 16777216.0f);  // x * 2^24 is exact in fp32
       }
   }
   __shared__ uint64_t Ap[16][D];
