@@ -236,11 +236,14 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
   float lv[8];
   bool raw[8];
   int hish[8], dix[8];
+  // the lane's 8 channels are the consecutive pair ids j0 .. j0+7
+  const int j0 = (8 * cb) & (NPAIR - 1);
+  const uint32_t hib = (uint32_t)(pm.hi >> j0) & 0xFFu, oneb = (uint32_t)(pm.one >> j0) & 0xFFu;
+  const int dbase = __popcll(pm.hi & ((1ull << j0) - 1)) + (8 * cb >= NPAIR ? g.n_hi : 0);
 #pragma unroll
   for (int k = 0; k < 8; k++) {
-    const int c = 8 * cb + k, j = c & (NPAIR - 1);
-    const bool sal = (pm.hi >> j) & 1, one = (pm.one >> j) & 1;
-    dix[k] = __popcll(pm.hi & ((1ull << j) - 1)) + (c >= NPAIR ? g.n_hi : 0);
+    const bool sal = (hib >> k) & 1u, one = (oneb >> k) & 1u;
+    dix[k] = dbase + __popc(hib & ((1u << k) - 1u));
     raw[k] = sal && g.bits_hi == 16;
     lv[k] = sal ? 15.0f : (one ? 1.0f : 3.0f);
     hish[k] = sal ? 2 * pos_swap(dix[k]) : 0;
