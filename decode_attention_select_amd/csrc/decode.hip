@@ -340,14 +340,24 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int G = g.G;
   const bool hvalid = col < G;
 
-  // ---- every wave starts on its own.  Its first request is its query
-  // slice (head col, channels 32kq..32kq+31): memory counters retire in
-  // order, so anything requested behind the cache stream would wait for it.
+  // ---- every wave starts on its own.  Its first requests are the length,
+  // its query slice (head col, channels 32kq..32kq+31) and the 8 leading
+  // ranks: anything requested behind the cache stream would wait for it.
+  // The ranks are a buffer load, so that they stay in that order (memory
+  // counters retire in order) rather than being issued where they are used.
+  int len = c.len[bh];
   u4 qv[4];
   {
     const u4* qg = (const u4*)(q + ((size_t)b * g.Hq + kh * G + min(col, G - 1)) * D + 32 * kq);
 #pragma unroll
     for (int i = 0; i < 4; i++) qv[i] = qg[i];
+  }
+  u4 topv[2];
+  if constexpr (HIMODE != 0) {
+    const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(c.pairs + (size_t)bh * NPAIR), 0, 32, BUF_RSRC_WORD3);
+    topv[0] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, 0, 0, 0);
+    topv[1] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, 16, 0, 0);
   }
   // Quantized group g goes to wave w of split s with s + S*w = g mod S*NW,
   // so a wave's groups are first + i*STR: their addresses do not depend on
@@ -373,32 +383,6 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
                                         col, kq, kq, lane & 31, 0xE4u, g.nh, g.n_vhi, pf[k]);
   }
 
-  // scalar loads: the length and the 8 leading ranks
-  const int len = c.len[bh];
-  const int T_old = min(max(len, 0), g.max_tokens);  // reads stay inside the cache
-  // FUSED: whether this call appends (a full cache or a negative length is
-  // reported and decoded as it stands)
-  const bool app = FUSED && len >= 0 && len < g.max_tokens;
-  const int T = T_old + (app ? 1 : 0);
-  int top[8];
-  if constexpr (HIMODE != 0) {
-    const int32_t* pr = c.pairs + (size_t)bh * NPAIR;
-#pragma unroll
-    for (int r = 0; r < 8; r++) top[r] = pr[r];
-  }
-  const int nq = n_quant(T_old, g.R), ngq = nq / GS;  // FUSED: the prefix before the append
-  const int nrb = (T - nq + GS - 1) / GS;
-  // This wave's quantized groups are first + i*STR, i < nmine.  Exactly PF
-  // group loads are kept in flight (past the end the index is clamped to the
-  // wave's last group, or to group 0: cache hits, never used), so the
-  // compiler can count outstanding loads and never drains the prefetches.
-  const int nmine = first < ngq ? (ngq - first + STR - 1) / STR : 0;
-  const int nlast = nmine > 0 ? first + (nmine - 1) * STR : 0;
-  auto group_at = [&](int i) { return rec0 + (size_t)min(first + i * STR, nlast); };
-  // The nrb ring blocks continue the same order after the groups (block
-  // ngq + r), so they fall to waves holding one group fewer than the most;
-  // a ring block is worked on first, while the group stream warms up.
-  const int ring0 = ((first - ngq) % STR + STR) % STR;
 
   // kept key chunks (all four unless PRUNE), a wave-uniform mask: E_m sums
   // min(floor(4096 |q|), 2^20) over chunk m's 32 channels and the G heads
@@ -486,6 +470,25 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       q16[4 * i + e] = hvalid ? pk_rne(a * qsc, b * qsc) : 0u;
     }
 
+  const int T_old = min(max(len, 0), g.max_tokens);  // reads stay inside the cache
+  // FUSED: whether this call appends (a full cache or a negative length is
+  // reported and decoded as it stands)
+  const bool app = FUSED && len >= 0 && len < g.max_tokens;
+  const int T = T_old + (app ? 1 : 0);
+  const int nq = n_quant(T_old, g.R), ngq = nq / GS;  // FUSED: the prefix before the append
+  const int nrb = (T - nq + GS - 1) / GS;
+  // This wave's quantized groups are first + i*STR, i < nmine.  Exactly PF
+  // group loads are kept in flight (past the end the index is clamped to the
+  // wave's last group, or to group 0: cache hits, never used), so the
+  // compiler can count outstanding loads and never drains the prefetches.
+  const int nmine = first < ngq ? (ngq - first + STR - 1) / STR : 0;
+  const int nlast = nmine > 0 ? first + (nmine - 1) * STR : 0;
+  auto group_at = [&](int i) { return rec0 + (size_t)min(first + i * STR, nlast); };
+  // The nrb ring blocks continue the same order after the groups (block
+  // ngq + r), so they fall to waves holding one group fewer than the most;
+  // a ring block is worked on first, while the group stream warms up.
+  const int ring0 = ((first - ngq) % STR + STR) % STR;
+
   uint32_t qhi[4] = {0, 0, 0, 0};  // HIMODE 4: 4*q (fp16); HIMODE 16: raw q
   float q4f[8];                    // HIMODE 4: 4*q in fp32
   int sal_ch = 0;                  // HIMODE 4: salient channel whose scale lane%16 copies
@@ -509,7 +512,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     }
     bool sal = false;
 #pragma unroll
-    for (int r = 0; r < 8; r++) sal |= r < g.n_hi && (top[r] & 63) == lane;
+    for (int r = 0; r < 8; r++)
+      sal |= r < g.n_hi && (__builtin_amdgcn_readfirstlane((int)topv[r >> 2][r & 3]) & 63) == lane;
     const unsigned long long m = __ballot(sal);
     if (lane < 16) hil[lane] = 0;  // stays in range even for a malformed rank table
     if (sal) {
