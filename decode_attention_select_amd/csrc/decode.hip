@@ -962,18 +962,22 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     const bool act = item < items;
     const int h = act ? item / (D / 8) : 0, c8 = act ? 8 * (item % (D / 8)) : 0;
     float M = -INFINITY, L = 0.0f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i0 = sub; act && i0 < S; i0 += 8 * nsub) {
-      uint64_t mlw[8];
-      u4 ov[8];
+    // a batch: KB records per lane requested at once, then merged in order
+    // (each as it arrives); indices past S repeat the last record and are
+    // skipped
+    auto batch = [&](auto kb, int i0) {
+      constexpr int KB = decltype(kb)::value;
+      uint64_t mlw[KB];
+      u4 ov[KB];
 #pragma unroll
-      for (int k = 0; k < 8; k++) {
+      for (int k = 0; k < KB; k++) {
         const int i = min(i0 + k * nsub, S - 1);
         mlw[k] = __hip_atomic_load(mlb + (size_t)i * G + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ov[k] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, (int)(((i * G + h) * D + c8) * 2), 0,
                                                       CPOL_SC1);
       }
 #pragma unroll
-      for (int k = 0; k < 8; k++) {
+      for (int k = 0; k < KB; k++) {
         const float m = __uint_as_float((uint32_t)mlw[k]);
         const float l = __uint_as_float((uint32_t)(mlw[k] >> 32));
         if (i0 + k * nsub >= S || m == -INFINITY) continue;
@@ -993,6 +997,11 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
           acc[2 * e + 1] += wgt * (float)v[1];
         }
       }
+    };
+    if (S <= 4 * nsub) {  // one batch of 4 covers every split
+      if (act) batch(std::integral_constant<int, 4>{}, sub);
+    } else {
+      for (int i0 = sub; act && i0 < S; i0 += 8 * nsub) batch(std::integral_constant<int, 8>{}, i0);
     }
     for (int o = 1; o < nsub; o <<= 1) {
       const float M2 = __shfl_xor(M, o), L2 = __shfl_xor(L, o);
