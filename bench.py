@@ -31,7 +31,7 @@ PEAK_GBS = 8000.0
 # HBM bytes per launch of the decode kernel on the default workload, from the
 # FETCH_SIZE and WRITE_SIZE counters scaled by a plain copy; None when the
 # kernel has changed since they were read.
-TRAFFIC = None
+TRAFFIC = 27513237
 
 
 def algorithmic_bytes(w, T: int, n_keep: int = 4) -> int:
