@@ -42,23 +42,40 @@ GS = 32
 D = 128
 
 
-def build(force: bool = True) -> str:
-    """Compile liboracle.so with gcc (IEEE arithmetic, no FMA contraction)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+# set (to any value) in a process started with the sanitizer runtime
+# preloaded: the oracle is then loaded from its address- and
+# undefined-behaviour-checked build
+SANITIZED_ENV = "KVQ_ORACLE_SANITIZED"
+
+
+def build(force: bool = True, sanitized: bool = False) -> str:
+    """Compile liboracle.so with gcc (IEEE arithmetic, no FMA contraction).
+    sanitized: the same source into liboracle_san.so under AddressSanitizer
+    and UndefinedBehaviorSanitizer (any finding aborts)."""
+    lib = _LIB_SAN if sanitized else _LIB
+    if force or not os.path.exists(lib):
+        tmp = lib + ".tmp%d" % os.getpid()
+        opt = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                "-fno-sanitize-recover=all"] if sanitized else ["-O2"])
+        subprocess.check_call(["gcc"] + opt + ["-std=c11", "-fPIC", "-shared",
                                "-ffp-contract=off", "-fno-fast-math",
                                "-Wall", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=True)
-        _lib = ctypes.CDLL(_LIB)
+        if os.environ.get(SANITIZED_ENV):
+            if not os.path.exists(_LIB_SAN):
+                build(force=True, sanitized=True)
+            _lib = ctypes.CDLL(_LIB_SAN)
+        else:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            _lib = ctypes.CDLL(_LIB)
     return _lib
 
 
