@@ -33,7 +33,7 @@
 // flight per wave in registers; the record of the block in work is staged
 // through a per-wave LDS buffer so that the 16 lanes sharing a channel slice
 // read it as a broadcast.  The waves merge in LDS into one record per head
-// (m, l, o/l in fp16); the last workgroup of a (sequence, KV head) to finish
+// (m, l, o/l, all fp32); the last workgroup of a (sequence, KV head) to finish
 // (atomic counter) merges the split records with the log-sum-exp rule and
 // writes the output.  The fused variant also carries the step's append (see
 // FUSED at the kernel).
@@ -245,32 +245,57 @@ __device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int 
 
 // Workspace of one call (zero-filled once by the caller; counters return to
 // zero at the end of every call):
-//   ml   float2 [B*Hkv][S][G]        per split and head: running max m (log2
-//                                     units) and softmax denominator l
-//   o    fp16   [B*Hkv][S][G][128]   per split and head: o / l
 //   tick u32    [B*Hkv][64]          splits finished (word 0; each counter
 //                                     on a 256-byte line of its own, so the
 //                                     splits of different KV heads never
-//                                     contend for one line)
+//                                     contend for one line).  First, so that
+//                                     its place does not depend on the split
+//                                     count: a workspace may serve calls with
+//                                     different split counts in turn.
+//   ml   float2 [B*Hkv][S][G]        per split and head: running max m (log2
+//                                     units) and softmax denominator l
+//   o    float  [B*Hkv][S][G][128]   per split and head: o / l
 struct Ws {
-  float2* ml;
-  uint16_t* o;
   uint32_t* tick;
+  float2* ml;
+  float* o;
+#ifdef KVQ_STAMPS
+  unsigned long long* st;  // phase timestamps, STAMP_SLOTS per workgroup
+#endif
 };
 
+// Phase timestamps (the KVQ_STAMPS build only; the product build compiles
+// them out): s_memrealtime (a 100 MHz clock shared by the whole device) at
+// fixed points of each workgroup, stored after the workspace proper.
+constexpr int STAMP_SLOTS = 32;
+#ifdef KVQ_STAMPS
+#define KVQ_STAMP(cond, slot)                                                          \
+  do {                                                                                 \
+    if (cond)                                                                          \
+      ws.st[(size_t)blockIdx.x * STAMP_SLOTS + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define KVQ_STAMP(cond, slot) \
+  do {                        \
+  } while (0)
+#endif
+
+constexpr int TICK_STRIDE = 64;  // u32 words between counters (256 bytes)
+__host__ __device__ inline size_t ws_tick_bytes(int B, int Hkv) {
+  return (size_t)B * Hkv * TICK_STRIDE * 4;
+}
 __host__ __device__ inline size_t ws_ml_bytes(int B, int Hq, int S) {
   return ((size_t)B * Hq * S * 8 + 255) & ~(size_t)255;
 }
-constexpr int TICK_STRIDE = 64;  // u32 words between counters (256 bytes)
 __host__ __device__ inline size_t ws_o_bytes(int B, int Hq, int S) {
-  return ((size_t)B * Hq * S * D * 2 + 255) & ~(size_t)255;
+  return (size_t)B * Hq * S * D * 4;
 }
 
-inline Ws ws_layout(void* base, int B, int Hq, int S) {
+inline Ws ws_layout(void* base, int B, int Hq, int Hkv, int S) {
   Ws w;
-  w.ml = (float2*)base;
-  w.o = (uint16_t*)((char*)base + ws_ml_bytes(B, Hq, S));
-  w.tick = (uint32_t*)((char*)base + ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S));
+  w.tick = (uint32_t*)base;
+  w.ml = (float2*)((char*)base + ws_tick_bytes(B, Hkv));
+  w.o = (float*)((char*)base + ws_tick_bytes(B, Hkv) + ws_ml_bytes(B, Hq, S));
   return w;
 }
 
@@ -345,6 +370,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // ranks: anything requested behind the cache stream would wait for it.
   // The ranks are a buffer load, so that they stay in that order (memory
   // counters retire in order) rather than being issued where they are used.
+  KVQ_STAMP(tid == 0, 0);
   int len = c.len[bh];
   u4 qv[4];
   {
@@ -455,6 +481,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(b)));
     }
   qmax = wave_max_kq(qmax);  // over the head's 128 channels (the 4 lanes of column col)
+  KVQ_STAMP(tid == 0 && qmax >= 0.0f, 1);
   const int qbexp = (int)((__float_as_uint(qmax) >> 23) & 0xFFu);
   const int qe = qbexp ? min(max(qbexp - 124, -100), 100) : 0;  // largest |q| < 2^(qe - 2)
   const float qsc = __uint_as_float((uint32_t)(127 - qe) << 23);  // 2^-qe
@@ -839,6 +866,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     }
   }
 
+  KVQ_STAMP(tid == 0, 2);
   if constexpr (HASQ) {
     if constexpr (PRUNE) {
       // the first prefetched groups hold all four chunks in chunk order:
@@ -860,6 +888,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
       for (int k = 0; k < PF; k++) {
         if (i + k < nmine) process_group(pf[k], group_at(i + k));
+#ifdef KVQ_STAMPS
+        if (i + k == 0) KVQ_STAMP(tid == 0 && O[0][0] != 12345.0f, 11);
+#endif
         load_group<HIMODE, PRUNE, KEEP, VHI>(c, group_at(i + k + PF), lane, col, kq, kqa, mla,
                                              cmap, g.nh, g.n_vhi, pf[k]);
       }
@@ -867,6 +898,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   }
 
   // ---- merge the waves: per head m, l and unnormalized o
+  KVQ_STAMP(lane == 0 && O[0][0] != 12345.0f, 3 + wave);
   __syncthreads();  // every wave is done with the loop-phase LDS
   {
     const float l_q = __shfl(Cvb[0], 16 + col);  // all-ones row 4 -> lane 16 + col
@@ -885,12 +917,12 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     }
   }
   __syncthreads();
-  // split record: (m, l) and o / l in fp16; thread -> (head, 8 channels).
+  // split record: (m, l) and o / l, fp32; thread -> (head, 8 channels).
   // Records cross workgroups (and L2 slices): every access to them is
   // device-coherent (sc1), so no cache-wide writeback or invalidate is needed.
   const size_t rbh = (size_t)bh * S * G;  // first record of this (sequence, KV head)
   const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
-      ws.o + rbh * D, 0, (int)(S * G * D * 2), BUF_RSRC_WORD3);
+      ws.o + rbh * D, 0, (int)(S * G * D * 4), BUF_RSRC_WORD3);
   for (int i = tid; i < G * (D / 8); i += WG_THREADS) {
     const int h = i / (D / 8), c8 = 8 * (i % (D / 8));
     float M = lds.u.merge.m[0][h];
@@ -907,9 +939,10 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       l += a * lds.u.merge.l[w][h];
     }
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const u4 ov = u4{pk_rne(oa[0] * inv, oa[1] * inv), pk_rne(oa[2] * inv, oa[3] * inv),
-                     pk_rne(ob[0] * inv, ob[1] * inv), pk_rne(ob[2] * inv, ob[3] * inv)};
-    __builtin_amdgcn_raw_buffer_store_b128(ov, rs_o, (int)(((s * G + h) * D + c8) * 2), 0, CPOL_SC1);
+    const int ooff = ((s * G + h) * D + c8) * 4;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, oa * inv), rs_o, ooff, 0, CPOL_SC1);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, ob * inv), rs_o, ooff + 16, 0,
+                                           CPOL_SC1);
     if (c8 == 0)
       __hip_atomic_store((uint64_t*)&ws.ml[rbh + (size_t)s * G + h],
                          (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(l) << 32),
@@ -918,13 +951,23 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 
   // ---- the last workgroup of this (sequence, KV head) merges all splits.
   // Every record store has completed (s_waitcnt) before the counter moves.
+  KVQ_STAMP(tid == 0, 12);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  KVQ_STAMP(tid == 0, 13);
   if (tid == 0) {
     const uint32_t prev =
         __hip_atomic_fetch_add(&ws.tick[(size_t)bh * TICK_STRIDE], 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     lds.last = prev == (uint32_t)(S - 1);
+#ifdef KVQ_STAMPS
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    ws.st[(size_t)blockIdx.x * STAMP_SLOTS + 14] = __builtin_amdgcn_s_memrealtime() + 0 * prev;
+    ws.st[(size_t)blockIdx.x * STAMP_SLOTS + 17] =
+        (unsigned long long)bh | ((unsigned long long)s << 16) | ((unsigned long long)xcc << 32) |
+        ((unsigned long long)prev << 40);
+#endif
     if constexpr (FUSED) lds.first = prev == 0u;
   }
   __syncthreads();
@@ -968,13 +1011,14 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     auto batch = [&](auto kb, int i0) {
       constexpr int KB = decltype(kb)::value;
       uint64_t mlw[KB];
-      u4 ov[KB];
+      u4 ov[KB][2];
 #pragma unroll
       for (int k = 0; k < KB; k++) {
         const int i = min(i0 + k * nsub, S - 1);
         mlw[k] = __hip_atomic_load(mlb + (size_t)i * G + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ov[k] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, (int)(((i * G + h) * D + c8) * 2), 0,
-                                                      CPOL_SC1);
+        const int ooff = ((i * G + h) * D + c8) * 4;
+        ov[k][0] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, ooff, 0, CPOL_SC1);
+        ov[k][1] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, ooff + 16, 0, CPOL_SC1);
       }
 #pragma unroll
       for (int k = 0; k < KB; k++) {
@@ -991,11 +1035,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         const float wgt = ex2(m - M) * l;
         L += wgt;
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const h2 v = u2h(ov[k][e]);
-          acc[2 * e] += wgt * (float)v[0];
-          acc[2 * e + 1] += wgt * (float)v[1];
-        }
+        for (int e = 0; e < 8; e++) acc[e] += wgt * __uint_as_float(ov[k][e >> 2][e & 3]);
       }
     };
     if (S <= 4 * nsub) {  // one batch of 4 covers every split
@@ -1031,6 +1071,11 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
                     bits[4] | ((uint32_t)bits[5] << 16), bits[6] | ((uint32_t)bits[7] << 16)};
     }
   }
+  KVQ_STAMP(tid == 0, 15);
+#ifdef KVQ_STAMPS
+  __builtin_amdgcn_s_waitcnt(0);
+  KVQ_STAMP(tid == 0, 16);
+#endif
   if (tid == 0)  // ready for the next call
     __hip_atomic_store(&ws.tick[(size_t)bh * TICK_STRIDE], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -1113,14 +1158,22 @@ template hipError_t launch_decode_io<false>(const Geo&, int, const Launch&);
 extern template hipError_t launch_decode_io<false>(const Geo&, int, const Launch&);
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {
-  return ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S) + (size_t)B * Hkv * TICK_STRIDE * 4;
+  size_t n = ws_tick_bytes(B, Hkv) + ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S);
+#ifdef KVQ_STAMPS
+  n += (size_t)B * Hkv * S * STAMP_SLOTS * 8;  // the timestamps of every workgroup
+#endif
+  return n;
 }
 
 hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float sm_scale,
                          int S, int keep, void* workspace, void* out, hipStream_t st,
                          const void* k_new, const void* v_new) {
-  const Launch a{q, c, sm_scale * 1.4426950408889634f, S, ws_layout(workspace, g.B, g.Hq, S),
-                 out, k_new, v_new, st};
+  Ws w = ws_layout(workspace, g.B, g.Hq, g.Hkv, S);
+#ifdef KVQ_STAMPS
+  w.st = (unsigned long long*)((char*)workspace + ws_tick_bytes(g.B, g.Hkv) +
+                               ws_ml_bytes(g.B, g.Hq, S) + ws_o_bytes(g.B, g.Hq, S));
+#endif
+  const Launch a{q, c, sm_scale * 1.4426950408889634f, S, w, out, k_new, v_new, st};
   return g.bf16 ? launch_decode_io<true>(g, keep, a) : launch_decode_io<false>(g, keep, a);
 }
 #endif

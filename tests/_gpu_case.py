@@ -102,9 +102,10 @@ class Case:
     def decode(self, q_bits: np.ndarray, n_splits: int, partials: bool = False):
         """q_bits [B][Hq][128] -> GPU output widened to fp64; with `partials`
         also the per-split records read back from the workspace: fp32 (m, l)
-        [B][Hq][S][2] and the fp16 normalized o/l [B][Hq][S][128] (fp64).
-        The workspace holds them as [B*Hkv][S][G] (m, l), 256-byte aligned,
-        then [B*Hkv][S][G][128] fp16."""
+        [B][Hq][S][2] and the fp32 normalized o/l [B][Hq][S][128] (fp64).
+        The workspace holds the split counters first ([B*Hkv] lines of 256
+        bytes), then the (m, l) records [B*Hkv][S][G], 256-byte aligned,
+        then [B*Hkv][S][G][128] fp32."""
         ws = torch.zeros(kvq.kvq_workspace_bytes(self.layout, n_splits), dtype=torch.uint8,
                          device="cuda")
         out = torch.empty((self.w.batch, self.w.n_q_heads, 128), dtype=torch.int16, device="cuda")
@@ -114,15 +115,32 @@ class Case:
         o = kvq_synth.bits_to_f64(host(out, np.uint16), self.w.io_dtype)
         if not partials:
             return o
-        B, Hkv, G, S = self.w.batch, self.w.n_kv_heads, self.w.group_size, n_splits
-        nrec = B * Hkv * S * G
-        raw = host(ws, np.uint8)
-        ml_bytes = (nrec * 8 + 255) // 256 * 256
-        ml = raw[:nrec * 8].view(np.float32).reshape(B, Hkv, S, G, 2)
-        o16 = raw[ml_bytes:ml_bytes + nrec * 256].view(np.float16).reshape(B, Hkv, S, G, 128)
-        ml = ml.transpose(0, 1, 3, 2, 4).reshape(B, Hkv * G, S, 2).astype(np.float64)
-        o16 = o16.transpose(0, 1, 3, 2, 4).reshape(B, Hkv * G, S, 128).astype(np.float64)
-        return o, (ml, o16)
+        return o, read_partials(host(ws, np.uint8), self.w.batch, self.w.n_kv_heads,
+                                self.w.group_size, n_splits)
+
+
+def read_partials(raw: np.ndarray, B: int, Hkv: int, G: int, S: int):
+    """Split records of a decode workspace (layout in include/kvq.h) as fp64:
+    (m, l) [B][Hq][S][2] and o/l [B][Hq][S][128]."""
+    nrec = B * Hkv * S * G
+    t_bytes = B * Hkv * 256
+    ml_bytes = (nrec * 8 + 255) // 256 * 256
+    ml = raw[t_bytes:t_bytes + nrec * 8].view(np.float32).reshape(B, Hkv, S, G, 2)
+    o32 = raw[t_bytes + ml_bytes:t_bytes + ml_bytes + nrec * 512].view(np.float32)
+    o32 = o32.reshape(B, Hkv, S, G, 128)
+    ml = ml.transpose(0, 1, 3, 2, 4).reshape(B, Hkv * G, S, 2).astype(np.float64)
+    o32 = o32.transpose(0, 1, 3, 2, 4).reshape(B, Hkv * G, S, 128).astype(np.float64)
+    return ml, o32
+
+
+def lse_merge(part) -> np.ndarray:
+    """The log-sum-exp combine of a call's split records, in fp64 on the
+    host: o = sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s."""
+    ml, o = part
+    m, l = ml[..., 0], ml[..., 1]
+    M = np.max(np.where(l > 0, m, -np.inf), axis=-1, keepdims=True)
+    w = np.where(l > 0, np.exp2(np.where(l > 0, m, 0.0) - M) * l, 0.0)
+    return np.einsum("bhs,bhsc->bhc", w, o) / w.sum(axis=-1)[..., None]
 
 
 def half_ulp(x: np.ndarray, io_dtype: str) -> np.ndarray:
@@ -135,10 +153,18 @@ def half_ulp(x: np.ndarray, io_dtype: str) -> np.ndarray:
 
 
 def check_output(got, ref, io_dtype, atol):
-    """|got - ref| <= atol + half an fp16 ulp (the split records hold o/l in
-    fp16) + half an output ulp, elementwise; returns the largest error."""
+    """|got - ref| <= atol elementwise: the budget holds the output's own
+    rounding to the 16-bit dtype.  Only where that rounding alone can take
+    more than half the budget (half an output ulp above 1e-3: |o| >= 0.5 in
+    bf16) is the half ulp added on top; the number of such elements and the
+    largest |o| are printed.  Returns the largest error."""
     err = np.abs(got - ref)
-    bound = atol + half_ulp(ref, "fp16") + half_ulp(ref, io_dtype)
+    hu = half_ulp(ref, io_dtype)
+    wide = hu > 1e-3
+    bound = atol + np.where(wide, hu, 0.0)
+    if np.any(wide):
+        print("check_output: %d of %d elements with |o| where half an %s ulp exceeds 1e-3 "
+              "(max |o| %.3g)" % (int(wide.sum()), wide.size, io_dtype, float(np.abs(ref).max())))
     assert np.all(err <= bound), "max err %.3g (bound there %.3g)" % (
         err.max(), bound.flat[np.argmax(err - bound)])
     return float(err.max())
@@ -146,18 +172,18 @@ def check_output(got, ref, io_dtype, atol):
 
 def single_split(part) -> np.ndarray:
     """Attention result of a one-split call before the 16-bit output
-    rounding: the split record's o/l, computed in fp32 and stored as fp16."""
-    ml, o16 = part
-    assert o16.shape[2] == 1
-    return o16[:, :, 0]
+    rounding: the split record's o/l, computed and stored in fp32."""
+    ml, o32 = part
+    assert o32.shape[2] == 1
+    return o32[:, :, 0]
 
 
 def check_single_split(part, ref, atol):
-    """The fp32 result, seen through its fp16 record: within `atol` plus
-    half an fp16 ulp of the oracle."""
+    """The fp32 result of a one-split call, read from its record: within
+    `atol` of the oracle (no rounding allowance)."""
     got = single_split(part)
     err = np.abs(got - ref)
-    assert np.all(err <= atol + half_ulp(ref, "fp16")), "max err %.3g" % err.max()
+    assert np.all(err <= atol), "max err %.3g" % err.max()
     return float(err.max())
 
 

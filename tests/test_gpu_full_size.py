@@ -11,8 +11,10 @@ configuration the benchmark times:
   per sequence and head, then every cache byte and every output element.
 
 Bars as in the small-case tests: bit-exact indices, sums, codes, scales,
-zero points and ring bytes; attention within 2e-3 (+ the rounding of the
-fp16 split record and of the 16-bit output)."""
+zero points and ring bytes; attention within 2e-3, the 16-bit output's own
+rounding included (half an output ulp is added only where it exceeds 1e-3,
+|o| >= 0.5 in bf16); the fp32 split record of a one-split call within 2e-3
+with no allowance."""
 import numpy as np
 import pytest
 
@@ -60,6 +62,35 @@ def test_llama3_8b_32k_full():
     e32 = check_single_split(part, ref, ATOL)
     print("%s S=%d max|err| %.3g max|o| %.3g split-record max|err| %.3g"
           % (w.name, S, err, np.abs(ref).max(), e32))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.xfail(strict=True, reason="single fp16 roundings of q*s and p*s exceed 2e-3 at these "
+                                      "logits (measured 0.0125 and 0.028); exact split pending")
+@pytest.mark.parametrize("qscale", [8, 16])
+def test_llama3_8b_32k_large_logits(qscale):
+    # PN-Mix (abstract): the error of pairs with large pair-norm products
+    # dominates the logits.  Outlier-heavy keys (2 % of pairs x10) met by
+    # queries scaled x8 and x16: logits far beyond those of N(0,1) data, every
+    # output against the oracle at 2e-3.
+    w = kvq_synth.workload("llama3-8b-32k")
+    print("case", w.name, "queries x%d" % qscale, flush=True)
+    case = Case(w)
+    qz = case.oracle_quant()
+    qf = kvq_synth.bits_to_f64(case.d["q_dec"][:, :, 0], w.io_dtype) * qscale
+    q = kvq_synth.to_bits(qf, w.io_dtype)
+    qf = kvq_synth.bits_to_f64(q, w.io_dtype)
+    G = w.group_size
+    kf = kvq_synth.bits_to_f64(case.d["k"][:, :, :w.tokens], w.io_dtype)
+    max_logit = max(float(np.abs(kf[0, h // G] @ qf[0, h]).max()) * SM_SCALE
+                    for h in range(w.n_q_heads))
+    ref = oracle.attention(qz, q, SM_SCALE)
+    S = bench.default_splits(w)
+    err = check_output(case.decode(q, S), ref, w.io_dtype, ATOL)
+    _, part = case.decode(q, 1, partials=True)
+    e32 = check_single_split(part, ref, ATOL)
+    print("%s queries x%d: max|logit| %.1f max|err| %.3g max|o| %.3g split-record max|err| %.3g"
+          % (w.name, qscale, max_logit, err, np.abs(ref).max(), e32))
 
 
 @pytest.mark.timeout(600)
