@@ -494,6 +494,89 @@ def prefill_leg(args, w):
     }
 
 
+STAMP_NAMES = [(0, "entry"), (1, "query in"), (2, "ring blocks done"),
+               (11, "first group done"), ("loop", "waves' loop end (last wave)"),
+               (12, "waves merged in LDS"), (13, "records stored"), (14, "ticket back"),
+               (15, "last workgroup: merge done"), (16, "last workgroup: output stored")]
+
+
+def stamps_leg(args, w):
+    """Phase timestamps of the decode kernel (libkvq_stamps.so: the same
+    kernel with s_memrealtime stamps at fixed points, 100 MHz): per timed
+    call, every workgroup's stamps relative to the earliest workgroup entry;
+    reported as the median over calls of each phase's median and maximum
+    over workgroups, in microseconds."""
+    import numpy as np
+    import torch
+
+    import kvq_synth
+    from decode_attention_select_amd import kvq
+    kvq.use_stamps_library()
+    S = args.splits or w.n_splits or default_splits(w)
+    T = w.tokens
+    data = kvq_synth.generate(w)
+    layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads, n_pairs_hi=w.n_pairs_hi,
+                             bits_hi=w.bits_hi, residual=w.residual, max_tokens=T,
+                             io_dtype=w.io_dtype)
+    base = kvq.Cache(layout)
+    kvq.kvq_select_pairs(layout, dev(data["q_sel"]), w.n_qry, dev(data["k"][:, :, :T]), T,
+                         base.struct)
+    kvq.kvq_quant_keys(layout, dev(data["k"][:, :, :T]), T, base.struct)
+    kvq.kvq_quant_values(layout, dev(data["v"][:, :, :T]), T, base.struct)
+    torch.cuda.synchronize()
+    n_rep = max(1, math.ceil(args.replica_mib * 2 ** 20 / base.nbytes()))
+    reps = [base]
+    for _ in range(n_rep - 1):
+        r = kvq.Cache.__new__(kvq.Cache)
+        r.layout, r.sizes = base.layout, base.sizes
+        r.bufs = {k: v.clone() for k, v in base.bufs.items()}
+        r.struct = kvq.kvq_cache(*[r.bufs[n].data_ptr() for n in kvq.BUF_NAMES])
+        reps.append(r)
+    q = dev(data["q_dec"][:, :, 0])
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    wsb = kvq.kvq_workspace_bytes(layout, S)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    nwg = w.batch * w.n_kv_heads * S
+    st_off = wsb - nwg * 32 * 8
+    stream = torch.cuda.current_stream()
+    sc = float(np.float32(SM_SCALE))
+    for i in range(args.warmup):
+        kvq.kvq_decode_attn(layout, q, reps[i % n_rep].struct, sc, S, ws, out, stream=stream)
+    torch.cuda.synchronize()
+    per_call = []
+    for i in range(args.steps):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        kvq.kvq_decode_attn(layout, q, reps[i % n_rep].struct, sc, S, ws, out, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        st = ws[st_off:].cpu().numpy().view(np.uint64).reshape(nwg, 32).astype(np.int64)
+        t0 = st[:, 0].min()
+        rel = (st - t0) * 0.01  # 100 MHz ticks -> microseconds
+        last = ((st[:, 17] >> 40) & 0xFFFF) == S - 1
+        row = {"event_us": ev0.elapsed_time(ev1) * 1e3}
+        for slot, name in STAMP_NAMES:
+            if slot == "loop":
+                v = rel[:, 3:3 + 8].max(axis=1)
+            elif slot in (15, 16):
+                v = rel[last, slot]
+            else:
+                v = rel[:, slot]
+            row[name] = (float(np.median(v)), float(v.max()))
+        per_call.append(row)
+    phases = []
+    for slot, name in STAMP_NAMES:
+        phases.append({"phase": name,
+                       "p50_us": round(float(np.median([r[name][0] for r in per_call])), 3),
+                       "max_us": round(float(np.median([r[name][1] for r in per_call])), 3)})
+    return {"stamps": w.name, "n_splits": S, "workgroups": nwg, "calls": args.steps,
+            "event_us_median": round(float(np.median([r["event_us"] for r in per_call])), 3),
+            "phases": phases,
+            "note": "medians over calls of each phase's median and maximum over workgroups, "
+                    "from the earliest workgroup entry; one call at a time (events around "
+                    "each), so the event time holds the launch"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -511,6 +594,8 @@ def main():
     ap.add_argument("--value-hi", default="",
                     help="with --build: N:B, the N*8 tokens of largest key magnitude per group "
                          "get B-bit values (two value precisions)")
+    ap.add_argument("--stamps", action="store_true",
+                    help="phase timestamps of the decode kernel (libkvq_stamps.so)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run the copy-kernel calibration of this size")
     args = ap.parse_args()
@@ -534,6 +619,9 @@ def main():
         w = w.replace(n_vblk_hi=nvb, bits_vhi=bvh)
     if args.build:
         print(json.dumps(prefill_leg(args, w)), flush=True)
+        return
+    if args.stamps:
+        print(json.dumps(stamps_leg(args, w)), flush=True)
         return
     if w.n_app:
         print(json.dumps(streaming_leg(args, w)), flush=True)

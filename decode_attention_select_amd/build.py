@@ -31,32 +31,42 @@ UNITS = [("api.hip", []), ("select.hip", []), ("quant.hip", []),
          ("decode.hip", ["-DKVQ_DECODE_PART=0"]), ("decode.hip", ["-DKVQ_DECODE_PART=1"])]
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every unit to an object (in parallel), then links libkvq.so."""
+STAMPS_LIB = os.path.join(PKG, "libkvq_stamps.so")
+
+
+def build(verbose: bool = False, stamps: bool = True) -> str:
+    """Compiles every unit to an object (in parallel), then links libkvq.so.
+    With `stamps`, also libkvq_stamps.so: the same sources with the decode
+    kernel's phase timestamps compiled in (-DKVQ_STAMPS; measurement only)."""
     tag = "%d" % os.getpid()
-    objs, procs = [], []
-    for i, (src, extra) in enumerate(UNITS):
-        obj = os.path.join(PKG, "_unit%d.%s.o" % (i, tag))
-        cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + extra + \
-              ["-c", "-o", obj, os.path.join(CSRC, src)]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        objs.append(obj)
-        procs.append(subprocess.Popen(cmd))
+    variants = [(LIB, [])] + ([(STAMPS_LIB, ["-DKVQ_STAMPS"])] if stamps else [])
+    objs, procs = {}, []
+    for lib, vflags in variants:
+        objs[lib] = []
+        for i, (src, extra) in enumerate(UNITS):
+            obj = os.path.join(PKG, "_unit%d%s.%s.o" % (i, "s" if vflags else "", tag))
+            cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + vflags + extra + \
+                  ["-c", "-o", obj, os.path.join(CSRC, src)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            objs[lib].append(obj)
+            procs.append(subprocess.Popen(cmd))
     try:
         failed = [p.wait() for p in procs]
         if any(failed):
             raise subprocess.CalledProcessError(max(failed), "hipcc")
-        tmp = LIB + ".tmp" + tag
-        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
-        os.replace(tmp, LIB)
+        for lib, _ in variants:
+            tmp = lib + ".tmp" + tag
+            cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs[lib]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.check_call(cmd)
+            os.replace(tmp, lib)
     finally:
-        for o in objs:
-            if os.path.exists(o):
-                os.remove(o)
+        for ol in objs.values():
+            for o in ol:
+                if os.path.exists(o):
+                    os.remove(o)
     return LIB
 
 

@@ -40,6 +40,12 @@ class kvq_cache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in BUF_NAMES]
 
 
+# The same library with the decode kernel's phase timestamps compiled in
+# (measurement builds only: its workspace holds the timestamps after the
+# records, so kvq_workspace_bytes reports more).
+STAMPS_LIB_PATH = os.path.join(_PKG, "libkvq_stamps.so")
+
+
 def lib():
     """The loaded libkvq.so; raises if it has not been built."""
     global _lib
@@ -49,6 +55,15 @@ def lib():
         _lib = ctypes.CDLL(LIB_PATH)
         _lib.kvq_status_str.restype = ctypes.c_char_p
     return _lib
+
+
+def use_stamps_library():
+    """Binds every call of this module to libkvq_stamps.so instead of
+    libkvq.so (before any call has loaded the library)."""
+    global _lib, LIB_PATH
+    if _lib is not None and LIB_PATH != STAMPS_LIB_PATH:
+        raise RuntimeError("kvq: libkvq.so is already loaded")
+    LIB_PATH = STAMPS_LIB_PATH
 
 
 def make_layout(batch, n_q_heads, n_kv_heads, *, n_pairs_hi=6, bits_hi=4,
