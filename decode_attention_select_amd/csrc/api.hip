@@ -3,12 +3,51 @@
 // synchronizes (except kvq_check).
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
 using namespace kvq;
 
+// Decode workspace of kvq_decode_attn_noalloc: one copy per GPU, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, never
+// the device array: every host use goes through the per-device address that
+// hipGetSymbolAddress returns (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_WORKSPACE_BYTES];
+
 namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Zero fill of n 32-bit words (a kernel, not a memset, so that a caller's
+// graph capture records a plain kernel node).
+__global__ void zero_words(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// The current device's scratch address.  The first call on a device resolves
+// it and enqueues one zero fill on `st` (the split counters must start at
+// zero; every completed decode leaves them at zero again).
+kvq_status scratch_ptr(void** out, hipStream_t st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return KVQ_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_EHIP;
+    hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, st, (uint32_t*)p,
+                       (size_t)KVQ_NOALLOC_WORKSPACE_BYTES / 4);
+    if (hipGetLastError() != hipSuccess) return KVQ_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
 
 kvq_status check_layout(const kvq_layout* L) {
   if (!L) return KVQ_EINVAL;
@@ -222,6 +261,18 @@ kvq_status kvq_append_decode_attn(const kvq_layout* L, const void* k_new, const 
                                   void* stream) {
   return decode_common(L, q, cache, sm_scale, n_splits, 0, workspace, ws_bytes, out, stream,
                        k_new, v_new);
+}
+
+kvq_status kvq_decode_attn_noalloc(const kvq_layout* L, const void* q, const kvq_cache* cache,
+                                   float sm_scale, int32_t n_splits, void* out, void* stream) {
+  if (kvq_status s = check_layout(L)) return s;
+  size_t need = 0;
+  if (kvq_status s = kvq_workspace_bytes(L, n_splits, &need)) return s;
+  if (need > (size_t)KVQ_NOALLOC_WORKSPACE_BYTES) return KVQ_ECAPACITY;
+  void* ws = nullptr;
+  if (kvq_status s = scratch_ptr(&ws, (hipStream_t)stream)) return s;
+  return decode_common(L, q, cache, sm_scale, n_splits, 4, ws,
+                       (size_t)KVQ_NOALLOC_WORKSPACE_BYTES, out, stream);
 }
 
 kvq_status kvq_check(const kvq_cache* cache, int32_t* host_err, void* stream) {

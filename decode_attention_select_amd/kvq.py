@@ -173,6 +173,14 @@ def kvq_append_decode_attn(layout, k_new, v_new, q, cache: kvq_cache, sm_scale, 
           _ptr(workspace), ctypes.c_size_t(ws_bytes), _ptr(out), _stream(stream))
 
 
+NOALLOC_WORKSPACE_BYTES = 4 << 20
+
+
+def kvq_decode_attn_noalloc(layout, q, cache: kvq_cache, sm_scale, n_splits, out, stream=None):
+    _call("kvq_decode_attn_noalloc", ctypes.byref(layout), _ptr(q), ctypes.byref(cache),
+          ctypes.c_float(sm_scale), ctypes.c_int32(n_splits), _ptr(out), _stream(stream))
+
+
 def kvq_check(cache: kvq_cache, stream=None) -> int:
     err = ctypes.c_int32(0)
     _call("kvq_check", ctypes.byref(cache), ctypes.byref(err), _stream(stream))

@@ -339,6 +339,23 @@ kvq_status kvq_append_decode_attn(const kvq_layout *L, const void *k_new,
                                   int32_t n_splits, void *workspace,
                                   size_t ws_bytes, void *out, void *stream);
 
+/* kvq_decode_attn with no workspace argument and no allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The workspace is a
+ * static device array of KVQ_NOALLOC_WORKSPACE_BYTES inside the library, one
+ * per GPU, held until the process ends.  The first call on a GPU resolves its
+ * address and enqueues one zero-fill kernel on `stream`; every completed call
+ * leaves its split counters at zero again.  All calls on one GPU share that
+ * array: calls that overlap on one GPU (different streams, or host threads
+ * without ordering) race and give wrong results.  Returns KVQ_ECAPACITY when
+ * kvq_workspace_bytes(L, n_splits) exceeds KVQ_NOALLOC_WORKSPACE_BYTES; all
+ * other arguments, results and errors as for kvq_decode_attn.  Calls no
+ * hipMalloc, hipFree or allocating library routine. */
+#define KVQ_NOALLOC_WORKSPACE_BYTES (4u << 20)
+kvq_status kvq_decode_attn_noalloc(const kvq_layout *L, const void *q,
+                                   const kvq_cache *cache, float sm_scale,
+                                   int32_t n_splits, void *out, void *stream);
+
 /* Synchronizes `stream`, then copies cache->err to *host_err (tests and
  * debugging only). */
 kvq_status kvq_check(const kvq_cache *cache, int32_t *host_err /*host*/,
