@@ -13,30 +13,40 @@
 // Both right-hand sums are dense contractions with small integer operands,
 // done on the matrix cores (v_mfma_f32_16x16x32_f16): codes become exact fp16
 // integers with one scaled fp4 convert per two codes (a 2-bit code in a
-// nibble is the e2m1 value code/2), the pre-scaled operands (q*s, p*s) are
-// fp16, accumulation is fp32.  The z terms are one more MFMA each; an extra
-// all-ones row in the value-zero MFMA yields the softmax denominator from the
-// same rounded p.  Query heads of one KV head fill the 16 MFMA columns
-// (G <= 16).  Ring (16-bit) tokens use the same MFMA shapes on raw values.
-// The salient keys' high digits weigh 4*q*s, which is split exactly into an
-// fp16 value and its fp16 rounding residual carried by the otherwise unused
-// K-lanes 16..31 of that MFMA.
+// nibble is the e2m1 value code/2), accumulation is fp32.  The products q*s
+// and p*s enter as an exact pair of fp16 operands, hi = fp16(x*y) and
+// lo = fp16(x*y - hi) (one fused multiply-add; the residual of a product of
+// two fp16 values is itself an fp16 value), each through its own MFMA into
+// the same accumulator, so no product is rounded: the only roundings left
+// are the fp16 softmax weights (the same rounded weights feed the numerator
+// and the denominator) and fp32 accumulation.  The z terms are one more MFMA
+// each (fp16 x fp16 products are exact in fp32); an extra all-ones row in the
+// value-zero MFMA yields the softmax denominator from the same rounded p.
+// Query heads of one KV head fill the 16 MFMA columns (G <= 16).  Ring
+// (16-bit) tokens use the same MFMA shapes on raw values.  The salient keys'
+// high digits weigh 4*q*s, split the same way and carried by the otherwise
+// unused K-lanes 16..31 of that MFMA.
 //
 // Work split: an 8-wave workgroup per (sequence, KV head, token split), one
-// workgroup per CU by default.  The 32-token blocks of a (sequence, KV head)
-// are dealt to its waves interleaved across splits (block b to the wave w of
-// split s with s + S w = b mod S * 8), each wave with its own online softmax
-// (base 2, scale folded into the exponent; the running max is raised only
-// when a block's weights would exceed 2^8, or 2 in a group with very wide
-// value scales, so most blocks skip the rescale and the fp16 products of
-// weights and value scales stay finite).  The codes and scale/zero records of the next PF blocks are in
-// flight per wave in registers; the record of the block in work is staged
-// through a per-wave LDS buffer so that the 16 lanes sharing a channel slice
-// read it as a broadcast.  The waves merge in LDS into one record per head
-// (m, l, o/l, all fp32); the last workgroup of a (sequence, KV head) to finish
-// (atomic counter) merges the split records with the log-sum-exp rule and
-// writes the output.  The fused variant also carries the step's append (see
-// FUSED at the kernel).
+// workgroup per CU by default.  Wave w of split s owns the flat index
+// f = s + S w of its (sequence, KV head); f < RS/32 also owns physical ring
+// block f (32 ring slots), and the 32-token groups g = f - RS/32 + i S NW
+// (i >= 0, g >= 0) are its quantized groups.  Every address a wave reads is
+// fixed before the length arrives, so each wave issues all its first loads at
+// entry: the query, its ring block (to registers) and its first quantized
+// groups, copied straight from HBM into per-wave LDS slots by direct
+// global->LDS loads (each slot one group's records; a consumed slot is
+// refilled with the wave's next group).  The record in work is read from its
+// slot, the 16 lanes sharing a channel slice reading the metadata as a
+// broadcast.  Each wave keeps its own online softmax (base 2, scale folded
+// into the exponent; the running max is raised only when a block's weights
+// would exceed 2^8, or 2 in a group with very wide value scales, so most
+// blocks skip the rescale and the fp16 products of weights and value scales
+// stay finite).  The waves merge in LDS into one record per head (m, l, o/l,
+// fp32); the last workgroups of a (sequence, KV head) to finish (atomic
+// counter) merge the split records with the log-sum-exp rule, each a share of
+// the heads' channels, and write the output.  The fused variant also carries
+// the step's append (see FUSED at the kernel).
 #include "common.h"
 #include "internal.h"
 #include "quant_group.h"
@@ -56,9 +66,11 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 // 16 bytes at a 4-byte-aligned address (raw salient rows are 2*nh bytes long)
 typedef uint32_t u4a __attribute__((ext_vector_type(4), aligned(4)));
 
-constexpr int NW = 8;                  // waves per workgroup (one workgroup per CU)
+#ifndef KVQ_DECODE_WAVES
+#define KVQ_DECODE_WAVES 8
+#endif
+constexpr int NW = KVQ_DECODE_WAVES;   // waves per workgroup (one workgroup per CU)
 constexpr int WG_THREADS = 64 * NW;
-constexpr int PF = 2;                  // quantized groups in flight per wave
 constexpr int MAXG = 16;
 // log2 headroom before the running max moves: the softmax weights p stay
 // below 2^slack.  The value path forms p * s in fp16, so a group holding a
@@ -80,6 +92,7 @@ __device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 // the cache-policy bit that makes a buffer access device-coherent (sc1).
 constexpr int BUF_RSRC_WORD3 = 0x00020000;
 constexpr int CPOL_SC1 = 16;
+constexpr int CPOL_SC0 = 1;  // bypasses the CU's L1 only: reads what the XCD's L2 holds
 
 // 16-bit input pair -> fp16 pair (bf16 widened exactly, then RNE to fp16)
 template <bool BF16>
@@ -158,6 +171,28 @@ __device__ inline float wave_sum_kq(float x) {
   return x + __shfl_xor(x, 32);
 }
 
+// A lane's value moved by a DPP pattern (all rows and banks enabled).
+#define KVQ_DPP(x, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), (ctrl), 0xF, 0xF, false))
+// max / sum over all 64 lanes: within each row of 16 (quad xor 1, quad xor
+// 2, half-row mirror, row mirror), then across the four rows
+__device__ inline float wave_max64(float x) {
+  x = fmaxf(x, KVQ_DPP(x, 0xB1));
+  x = fmaxf(x, KVQ_DPP(x, 0x4E));
+  x = fmaxf(x, KVQ_DPP(x, 0x141));
+  x = fmaxf(x, KVQ_DPP(x, 0x140));
+  return wave_max_kq(x);
+}
+__device__ inline float wave_sum64(float x) {
+  x += KVQ_DPP(x, 0xB1);
+  x += KVQ_DPP(x, 0x4E);
+  x += KVQ_DPP(x, 0x141);
+  x += KVQ_DPP(x, 0x140);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Splits fp32 p into two 16-bit parts of the raw dtype with p ~= hi + lo to
 // ~2^-16 relative, so that the ring's raw 16-bit values multiply p at fp32-
 // like precision.
@@ -175,72 +210,113 @@ __device__ inline void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) 
   }
 }
 
-// Per-lane loads of one quantized group, issued one block ahead.
-struct Pref {
-  u2 klo[2];        // k_lo words of tile 0 and 1 (token col of the tile, channels 32kq..)
-  uint32_t klc[2][4];  // pruned decode: k_lo word kq/2 of a key chunk per slot, tiles 0, 1
-  uint32_t khi[2];  // k_hi word of tile 0 and 1
-  u4 hraw[2];       // raw salient keys (HIMODE 16): 8 values of the lane's token, tile 0 and 1
-  uint32_t vc[4];   // v_codes word of channel group j = 0..3
-  u4 meta;          // 16 B of the group's k_meta (lanes 0-31) or v_meta (lanes 32-63)
-  uint32_t vh[4];   // two value precisions: high-digit word of block kq, channel group j
+
+// The value of lane 15 - (l % 16) of the same 16-lane row (DPP row_mirror).
+__device__ inline float mirror16(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+}
+
+// Exact residual of an fp16 pair product: fp16(a*b - hi) in one fused
+// multiply-add (v_pk_fma_f16); with hi = fp16(a*b) it is the exact
+// remainder, so hi + lo = a*b (barring fp16 underflow of the remainder).
+__device__ inline uint32_t pk_fma_lo(uint32_t a, uint32_t b, uint32_t hi) {
+  return h2u(__builtin_elementwise_fma(u2h(a), u2h(b), -u2h(hi)));
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt lgkmcnt(0) (LDS and scalar memory), vmcnt and expcnt left alone.
+__device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+// Keeps the compiler from moving memory accesses across this point (the
+// direct global->LDS copies are invisible to its LDS dependence tracking).
+__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+// One direct global->LDS copy: every active lane moves the 16 bytes at `src`
+// to LDS address `dst` + 16 * lane (dst uniform).
+__device__ inline void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
+}
+
+// One LDS slot holds the records of one quantized group, copied from HBM by
+// direct loads (16 bytes per lane and instruction):
+//   KLO  [0, 1024)     k_lo
+//   META [1024, 2048)  k_meta (512) then v_meta (512): [0,64) key scale
+//                      pairs, [64,128) key zero pairs, [128,192) value scale
+//                      pairs (j-major), [192,256) value zero pairs (words)
+//   VC   [2048, 3072)  v_codes
+//   KHI  1024 bytes: k_hi (HIMODE 4 its 128 bytes, HIMODE 16 its 64 nh bytes)
+//   VH   1024 bytes: v_hi words 8 .. 8 + 64 n_vhi (VHI only)
+// Every copy is a whole-wave instruction (NLD per group), so that the
+// compiler counts each one in its own waits: lanes past a short record copy
+// 16 bytes of it again into the slack after it, which nothing reads.  NSLOT
+// slots per wave within the LDS budget.
+constexpr int SLOT_LDS_BUDGET = 147456;
+template <int HIMODE, bool VHI>
+struct SlotCfg {
+  static constexpr int KLO = 0, META = 1024, VC = 2048, KHI = 3072;
+  static constexpr int VH = KHI + (HIMODE != 0 ? 1024 : 0);
+  static constexpr int BYTES = VH + (VHI ? 1024 : 0);
+  static constexpr int NLD = 3 + (HIMODE != 0 ? 1 : 0) + (VHI ? 1 : 0);
+  static constexpr int FIT = SLOT_LDS_BUDGET / (NW * BYTES);
+  static constexpr int NSLOT = FIT < 5 ? FIT : 5;
+  static_assert(NSLOT >= 2, "LDS slots");
+  static_assert((NSLOT - 1) * NLD < 64, "vmcnt range");
 };
 
-// kqa: the key chunk whose low digits this lane reads (its own, kq, unless
-// that chunk is pruned; then a kept chunk that other lanes read in the same
-// instruction, so no extra line is fetched); mla: the same for the lane's
-// 16-byte piece of the key scale/zero record.  A redirected lane's values
-// only ever meet a zero query.
-// CHUNKED (pruned decode): slot i (< NCH) holds, for key chunk
-// (cmap >> 2i) & 3, the lane token's k_lo word kq/2 of that chunk.  Pruned
-// chunks are never named in cmap, so they are never fetched.
-// VHI (two value precisions by token, g.n_vhi high-precision 8-slot blocks
-// per group, the group's slots in key-magnitude order): blocks kq < n have
-// high-digit words; lanes of the other blocks read block n - 1's (fetched
-// anyway) and drop them when the group is processed.
-template <int HIMODE, bool CHUNKED, int NCH, bool VHI>
-__device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int col, int kq,
-                                  int kqa, int mla, uint32_t cmap, int nh, int nvhi, Pref& p) {
-  if constexpr (VHI) {
-    const uint32_t* vh = c.v_hi + rec * (8 + 64 * nvhi) + 8 + min(kq, nvhi - 1) * 16 + col;
-#pragma unroll
-    for (int j = 0; j < 4; j++) p.vh[j] = vh[j * nvhi * 16];
+// Issues the copies of quantized group `rec` into `slot`.  PRUNE: the lanes
+// of pruned key chunks (k_lo words, key scale/zero) read the kept chunk
+// kept0 instead, lines the same instruction fetches anyway, so the pruned
+// chunks' bytes are not read; what those lanes write is never read.
+template <int HIMODE, bool VHI, bool PRUNE>
+__device__ inline void issue_group(const kvq_cache& c, size_t rec, uint8_t* slot, int lane,
+                                   uint32_t kmask, int kept0, int nh, int nvhi) {
+  using C = SlotCfg<HIMODE, VHI>;
+  // k_lo: lane l holds words 4l .. 4l+3, of key chunk (l / 8) % 4
+  int lk = lane;
+  if (PRUNE && !((kmask >> ((lane >> 3) & 3)) & 1u)) lk = (lane & ~24) | (kept0 << 3);
+  dma16((const uint8_t*)c.k_lo + rec * 1024 + lk * 16, slot + C::KLO);
+  // metadata: lanes 0..31 k_meta (0..15 scales, 16..31 zeros of channels
+  // 8 (l % 16) .. +7, chunk (l % 16) / 4), lanes 32..63 v_meta
+  {
+    int lm = lane;
+    if (PRUNE && lane < 32 && !((kmask >> ((lane & 15) >> 2)) & 1u))
+      lm = (lane & 16) | (kept0 << 2) | (lane & 3);
+    const uint8_t* src = lane < 32 ? (const uint8_t*)c.k_meta + rec * 512 + lm * 16
+                                   : (const uint8_t*)c.v_meta + rec * 512 + (lane - 32) * 16;
+    dma16(src, slot + C::META);
   }
-  if constexpr (CHUNKED) {
-    const uint32_t* w = (const uint32_t*)c.k_lo + rec * GROUP_WORDS;
-#pragma unroll
-    for (int TT = 0; TT < 2; TT++)
-#pragma unroll
-      for (int i = 0; i < NCH; i++) {
-        const int mm = (cmap >> (2 * i)) & 3u;
-        p.klc[TT][i] = w[((TT * 4 + mm) * 16 + col) * 2 + (kq >> 1)];
-      }
-  } else {
-    const u2* klo = (const u2*)((const uint32_t*)c.k_lo + rec * GROUP_WORDS);
-    p.klo[0] = klo[(0 * 4 + kqa) * 16 + col];
-    p.klo[1] = klo[(1 * 4 + kqa) * 16 + col];
+  dma16((const uint8_t*)c.v_codes + rec * 1024 + lane * 16, slot + C::VC);
+  if constexpr (HIMODE == 4)  // 128 bytes
+    dma16((const uint8_t*)c.k_hi + rec * 128 + (lane & 7) * 16, slot + C::KHI);
+  if constexpr (HIMODE == 16)  // 32 rows of nh raw salient values: 64 nh bytes (nh >= 2)
+    dma16((const uint8_t*)c.k_hi + rec * 64 * nh + (lane < 4 * nh ? lane : lane & 3) * 16,
+          slot + C::KHI);
+  if constexpr (VHI)  // the high-digit words (after the 8 order words): 256 n_vhi bytes
+    dma16((const uint8_t*)(c.v_hi + rec * (8 + 64 * nvhi) + 8) +
+              (lane < 16 * nvhi ? lane : lane & 15) * 16,
+          slot + C::VH);
+}
+
+// Waits until the copies of the group issued `after` groups before the last
+// one issued have landed (vmcnt counts this wave's vector memory operations
+// in issue order; only the slot copies are outstanding in the group loop).
+template <int NLD, int NSLOT>
+__device__ inline void wait_slot(int after) {
+  static_assert(NSLOT <= 5, "cases");
+  switch (after) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<NLD>(); break;
+    case 2: wait_vmcnt<2 * NLD>(); break;
+    case 3: wait_vmcnt<3 * NLD < 64 ? 3 * NLD : 63>(); break;
+    default: wait_vmcnt<4 * NLD < 64 ? 4 * NLD : 63>(); break;
   }
-  if constexpr (HIMODE == 4) {
-    const uint32_t* kh = (const uint32_t*)c.k_hi + rec * 32;
-    p.khi[0] = kh[col];
-    p.khi[1] = kh[16 + col];
-  }
-  if constexpr (HIMODE == 16) {
-    // salient channels 8*(kq&1) .. +7 of the lane's token (entries past nh
-    // are masked later; the buffer carries 32 bytes of tail slack)
-    const uint16_t* kh = (const uint16_t*)c.k_hi + rec * GS * nh;
-#pragma unroll
-    for (int TT = 0; TT < 2; TT++) {
-      const u4a v = *(const u4a*)(kh + (16 * TT + col) * nh + 8 * (kq & 1));
-      p.hraw[TT] = u4{v[0], v[1], v[2], v[3]};
-    }
-  }
-  const uint32_t* vc = (const uint32_t*)c.v_codes + rec * GROUP_WORDS;
-#pragma unroll
-  for (int j = 0; j < 4; j++) p.vc[j] = vc[(j * 4 + kq) * 16 + col];
-  const u4* meta = lane < 32 ? (const u4*)((const uint16_t*)c.k_meta + rec * 2 * D)
-                             : (const u4*)((const uint16_t*)c.v_meta + rec * 2 * D);
-  p.meta = meta[mla];
+  compiler_fence();
 }
 
 // Workspace of one call (zero-filled once by the caller; counters return to
@@ -257,8 +333,10 @@ __device__ inline void load_group(const kvq_cache& c, size_t rec, int lane, int 
 //   o    float  [B*Hkv][S][G][128]   per split and head: o / l
 struct Ws {
   uint32_t* tick;
-  float2* ml;
+  float2* ml;    // device-coherent copy of the split records
   float* o;
+  float2* mlL;   // the same records, stored for the L2 of the storing CU
+  float* oL;
 #ifdef KVQ_STAMPS
   unsigned long long* st;  // phase timestamps, STAMP_SLOTS per workgroup
 #endif
@@ -267,16 +345,25 @@ struct Ws {
 // Phase timestamps (the KVQ_STAMPS build only; the product build compiles
 // them out): s_memrealtime (a 100 MHz clock shared by the whole device) at
 // fixed points of each workgroup, stored after the workspace proper.
-constexpr int STAMP_SLOTS = 32;
+[[maybe_unused]] constexpr int STAMP_SLOTS = 32;
+// They are kept in LDS and stored once at exit, so that no store of theirs
+// changes how the compiler orders the kernel's own memory accesses.
 #ifdef KVQ_STAMPS
-#define KVQ_STAMP(cond, slot)                                                          \
-  do {                                                                                 \
-    if (cond)                                                                          \
-      ws.st[(size_t)blockIdx.x * STAMP_SLOTS + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+#define KVQ_STAMP(cond, slot)                                        \
+  do {                                                               \
+    if (cond) lds.stamp[(slot)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define KVQ_STAMP_FLUSH()                                                                 \
+  do {                                                                                    \
+    __syncthreads();                                                                      \
+    if (tid < STAMP_SLOTS) ws.st[(size_t)blockIdx.x * STAMP_SLOTS + tid] = lds.stamp[tid]; \
   } while (0)
 #else
 #define KVQ_STAMP(cond, slot) \
   do {                        \
+  } while (0)
+#define KVQ_STAMP_FLUSH() \
+  do {                    \
   } while (0)
 #endif
 
@@ -293,122 +380,182 @@ __host__ __device__ inline size_t ws_o_bytes(int B, int Hq, int S) {
 
 inline Ws ws_layout(void* base, int B, int Hq, int Hkv, int S) {
   Ws w;
+  const size_t t = ws_tick_bytes(B, Hkv), m = ws_ml_bytes(B, Hq, S), o = ws_o_bytes(B, Hq, S);
   w.tick = (uint32_t*)base;
-  w.ml = (float2*)((char*)base + ws_tick_bytes(B, Hkv));
-  w.o = (float*)((char*)base + ws_tick_bytes(B, Hkv) + ws_ml_bytes(B, Hq, S));
+  w.ml = (float2*)((char*)base + t);
+  w.o = (float*)((char*)base + t + m);
+  w.mlL = (float2*)((char*)base + t + m + o);
+  w.oL = (float*)((char*)base + t + 2 * m + o);
   return w;
 }
 
-// LDS, one layout per phase.  The loop phase is private to each wave (no
-// workgroup barrier before the stream); a barrier separates it from the
-// merge phase.
-struct LdsLoop {
-  uint16_t q16[NW][MAXG][D + 8];   // per wave: query as fp16 (padded rows)
-  uint16_t qraw[NW][MAXG][D + 8];  // per wave: query in the io dtype (16-bit salient keys)
-  uint32_t stage[NW][256];         // per wave: metadata record of the group in work
-  int hil[NW][16];                 // per wave: salient channels, ascending
-  uint16_t sal_s[NW][16];          // per wave: scales of the salient channels, group in work
-};
+// LDS.  Loop phase: the per-wave group slots and the query tables (every wave
+// writes the same values into the tables and reads only after its own writes,
+// so no workgroup barrier is needed before the stream).  Merge phase (after a
+// barrier, every slot copy consumed or drained): the wave records, or the
+// fused variant's packing step.
 struct LdsMerge {
-  float o[NW][MAXG][D + 4];        // wave results before the workgroup merge (padded rows)
+  float o[NW][MAXG][D + 4];  // wave results before the workgroup merge (padded rows)
   float m[NW][MAXG], l[NW][MAXG];
+  float a[NW][MAXG];         // each wave's weight 2^(m_w - M) per head
+  float M[MAXG], inv[MAXG], L[MAXG];
 };
+// The final merge: each split's weight per head, 2^(m_s - M) l_s / L.
+struct LdsFinal {
+  float wn[1024 * MAXG];
+};
+template <int SLOTB, int NSLOT>
 struct Lds {
   union {
-    LdsLoop loop;
+    __align__(16) uint8_t slots[NW][NSLOT][SLOTB];
     LdsMerge merge;
-    PackLds pack;  // FUSED: the append step of the last workgroup, after the merge
+    LdsFinal fin;
+    PackLds pack;  // FUSED: the append step of the first workgroup, after its ticket
   } u;
-  int last;
-  int first;  // FUSED: the first workgroup of its (sequence, KV head) to finish
+  __align__(16) uint16_t qin[MAXG][D];       // the query as copied in (io dtype), every head
+  __align__(16) uint16_t q16[MAXG][D + 8];   // query as fp16 (scaled), every head
+  __align__(16) uint16_t qraw[MAXG][D + 8];  // query in the io dtype, scaled (HIMODE 16)
+  int hil[16];                               // salient channels, ascending
+  uint16_t sal_s[NW][16];                    // per wave: salient scales of the group in work
+  int mrank;                                 // -1: not the last split; 0/1: merge (1: all splits on this XCD)
+#ifdef KVQ_STAMPS
+  unsigned long long stamp[STAMP_SLOTS];
+#endif
+  int first;                                 // FUSED: the first workgroup of its (sequence, KV head) to finish
 };
 
 // HASQ: the cache has quantized-group storage (capacity NG >= 1); without it
 // no group address exists and the group stream is compiled out.
-// LO1: some pairs are at 1 bit.  Their scale is the whole group range, three
-// times a 2-bit channel's, so q*s is carried as an exact fp16 pair (rounded
-// value + rounding residual) through a second MFMA pass over the same codes.
 // KEEP < 4: query-channel pruning (Dual-QK, abstract: a decode query keeps
 // its few large channels and the key cache is read only for them).  Per
 // (sequence, KV head) the KEEP 32-channel key chunks of largest
 // sum over the group's heads of min(floor(4096 |q_c|), 2^20) are kept (ties to the
 // lower chunk); the query is zero on the others, whose key codes and
-// scale/zero are not read (past the first PF prefetched groups, which are
-// issued before the query arrives): their lanes load a kept chunk's words
-// instead, which the same instruction fetches anyway.
+// scale/zero are not copied (past the first slots, which are issued before
+// the query arrives).
 // VHI: the cache has two value precisions (g.n_vhi > 0): the first n_vhi
 // 8-slot blocks of each group (its tokens of largest key magnitude) add their
-// high value digits (4 * digit) through one more MFMA per tile.
+// high value digits (4 * digit) through more MFMAs per tile.
 // FUSED: the call also appends one token per (sequence, KV head) (knew,
 // vnew) and attends it (PM-KVQ, key_machinery: 16-bit first, quantized
 // later).  Every wave reads the length before the append and attends the
 // quantized prefix of that length plus the ring and the new token, which
 // it takes from knew/vnew; a group that the append completes is attended
-// from the ring at 16 bits in this call.  The last workgroup of the
-// (sequence, KV head), after the merge (so after every workgroup has read
-// the length and the ring), writes the token to its ring slot, packs the
-// completed group and stores the new length.
-template <bool BF16, int HIMODE, bool HASQ, bool LO1, int KEEP, bool VHI, bool FUSED>
+// from the ring at 16 bits in this call.  The first workgroup of the
+// (sequence, KV head) to take its ticket writes the token to its ring slot
+// and packs the completed group; the last merging workgroup, after every
+// workgroup has read the length, stores the new length.
+// LOCOL (G <= 8): the exact pair (hi, lo) of every product q*s and p*s
+// enters one MFMA, hi in column h of head h and lo in the spare column
+// 15 - h; lane (col, kq) serves head col (col < G) or 15 - col (col >= 16 -
+// G).  Logits and outputs add the two columns (a row_mirror DPP).  Without
+// it (G > 8, every column taken) hi and lo take an MFMA each.
+template <bool BF16, int HIMODE, bool HASQ, int KEEP, bool VHI, bool FUSED, bool LOCOL>
 __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             kvq_cache c, float scale_log2, int S,
                                                             Ws ws, uint16_t* __restrict__ out,
                                                             const uint16_t* __restrict__ knew,
                                                             const uint16_t* __restrict__ vnew) {
   constexpr bool PRUNE = KEEP < 4;
-  __shared__ Lds lds;
+  using SC = SlotCfg<HIMODE, VHI>;
+  constexpr int NSLOT = SC::NSLOT, NLD = SC::NLD, SLOTB = SC::BYTES;
+  __shared__ Lds<SLOTB, NSLOT> lds;
   // the wave index is wave-uniform: keeping it in a scalar register makes every
-  // group address scalar (one 64-bit base per load, no per-lane address math)
+  // group address scalar (one 64-bit base per copy, no per-lane address math)
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
-  const int bh = blockIdx.x / S, s = blockIdx.x % S;
+  // Workgroups are dealt to the 8 XCDs round robin (workgroup i to XCD
+  // i mod 8): when the (sequence, KV head) count is a multiple of 8, the
+  // splits of one (sequence, KV head) take workgroups of one residue, so
+  // that they share an L2 (the final merge then reads their records there;
+  // the ticket checks where every split actually ran).
+  const bool xmap = (g.B * g.Hkv) % 8 == 0;
+  const int bh = xmap ? (int)(blockIdx.x % 8) + 8 * (int)((blockIdx.x / 8) / S)
+                      : (int)(blockIdx.x / S);
+  const int s = xmap ? (int)((blockIdx.x / 8) % S) : (int)(blockIdx.x % S);
   const int b = bh / g.Hkv, kh = bh % g.Hkv;
   const int G = g.G;
-  const bool hvalid = col < G;
-
-  // ---- every wave starts on its own.  Its first requests are the length,
-  // its query slice (head col, channels 32kq..32kq+31) and the 8 leading
-  // ranks: anything requested behind the cache stream would wait for it.
-  // The ranks are a buffer load, so that they stay in that order (memory
-  // counters retire in order) rather than being issued where they are used.
+  const bool hvalid = col < G;                    // lane of head col's hi column
+  const bool lo_lane = LOCOL && col >= 16 - G;    // lane of head 15 - col's lo column
+  const bool qvalid = hvalid || lo_lane;          // the lane carries a query
+  const int hq = hvalid ? col : (lo_lane ? 15 - col : 0);
   KVQ_STAMP(tid == 0, 0);
-  int len = c.len[bh];
-  u4 qv[4];
-  {
-    const u4* qg = (const u4*)(q + ((size_t)b * g.Hq + kh * G + min(col, G - 1)) * D + 32 * kq);
-#pragma unroll
-    for (int i = 0; i < 4; i++) qv[i] = qg[i];
-  }
-  u4 topv[2];
-  if constexpr (HIMODE != 0) {
-    const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(c.pairs + (size_t)bh * NPAIR), 0, 32, BUF_RSRC_WORD3);
-    topv[0] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, 0, 0, 0);
-    topv[1] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, 16, 0, 0);
-  }
-  // Quantized group g goes to wave w of split s with s + S*w = g mod S*NW,
-  // so a wave's groups are first + i*STR: their addresses do not depend on
-  // the length, and the first PF are requested before it arrives (clamped
-  // to the capacity; loads past the wave's last group are never used).  At
-  // every step the workgroups of a KV head read one contiguous band.
-  const int STR = S * NW;          // group stride of one wave
-  const size_t rec0 = (size_t)bh * g.NG;
-  const int first = s + S * wave;  // this wave's groups: first + i*STR < ngq
-  // FUSED: the new token's key and value channel tid (for the ring write of
-  // the last workgroup), requested now so that the end does not wait for them
-  uint16_t knv = 0, vnv = 0;
-  if constexpr (FUSED)
-    if (tid < D) {
-      knv = knew[(size_t)bh * D + tid];
-      vnv = vnew[(size_t)bh * D + tid];
-    }
-  Pref pf[PF];
-  if constexpr (HASQ) {
-#pragma unroll
-    for (int k = 0; k < PF; k++)
-      load_group<HIMODE, PRUNE, 4, VHI>(c, rec0 + (size_t)min(first + k * STR, g.NG - 1), lane,
-                                        col, kq, kq, lane & 31, 0xE4u, g.nh, g.n_vhi, pf[k]);
-  }
 
+  // ---- entry.  The length and the leading ranks are scalar loads; the
+  // query (every head of the group: G rows of 256 bytes) is copied straight
+  // into LDS like the group records, so that no vector-register load is
+  // waited for while copies are in flight (the compiler cannot count the two
+  // kinds together and would wait for all of them).
+  const int len = c.len[bh];
+  int top[8];
+#pragma unroll
+  for (int r = 0; r < 8; r++) top[r] = c.pairs[(size_t)bh * NPAIR + r];
+  {
+    const uint8_t* qsrc = (const uint8_t*)(q + ((size_t)b * g.Hq + kh * G) * D);
+    for (int i = 0; i < (G + 3) / 4; i++) {
+      // 1 KB = 4 rows per copy; rows past G re-read row G - 1 (never read back)
+      const int row = min(4 * i + (lane >> 4), G - 1);
+      dma16(qsrc + (size_t)row * (D * 2) + (lane & 15) * 16, &lds.qin[4 * i][0]);
+    }
+  }
+  const int RSB = g.RS / GS;        // physical ring blocks
+  const int STR = S * NW;           // flat indices of one (sequence, KV head)
+  const int f = s + S * wave;       // this wave's flat index
+  const bool ring_owner = f < RSB;  // owns physical ring blocks f, f + STR, ... < RSB
+  // quantized groups of this wave: g_i = gfirst + i STR (the first such index
+  // >= 0), copied into slot i % NSLOT.  The first NSLOT copies go out at
+  // once, a fixed number (past the capacity the index is clamped into it;
+  // such copies are never consumed and are drained before the LDS is
+  // reused).  A ring-owning wave first loads and attends its ring blocks (in
+  // vector registers) and issues its copies after that.
+  const size_t rec0 = (size_t)bh * g.NG;
+  const int gfirst = f - RSB + (ring_owner ? (RSB - f + STR - 1) / STR * STR : 0);
+  uint8_t* slots = &lds.u.slots[wave][0][0];
+  int issued = 0;
+  auto issue_first = [&]() {
+    if constexpr (HASQ) {
+#pragma unroll
+      for (int i = 0; i < NSLOT; i++)
+        issue_group<HIMODE, VHI, false>(c, rec0 + (size_t)min(gfirst + i * STR, g.NG - 1),
+                                        slots + i * SLOTB, lane, 0xFu, 0, g.nh, g.n_vhi);
+      issued = NSLOT;
+    }
+  };
+  u4 kt[2][4], vt[8];
+  u4 knk[4];
+  uint16_t vnk[8];
+  // ring block rb (32 slots): key rows in tile order, value columns
+  auto load_ring = [&](int rb) {
+    const uint16_t* rk = (const uint16_t*)c.ring_k + ((size_t)bh * g.RS + rb * GS) * D;
+    const uint16_t* rv = (const uint16_t*)c.ring_v + (((size_t)bh * RSB + rb) * D) * GS;
+#pragma unroll
+    for (int TT = 0; TT < 2; TT++) {
+      const u4* kr = (const u4*)(rk + (size_t)tile_token(16 * TT + col) * D + 32 * kq);
+#pragma unroll
+      for (int k = 0; k < 4; k++) kt[TT][k] = kr[k];
+    }
+#pragma unroll
+    for (int tt = 0; tt < 8; tt++) vt[tt] = *(const u4*)(rv + (size_t)(16 * tt + col) * GS + 8 * kq);
+  };
+  if (ring_owner) {
+    load_ring(f);
+    if constexpr (FUSED) {
+      const u4* kn = (const u4*)(knew + (size_t)bh * D + 32 * kq);
+#pragma unroll
+      for (int k = 0; k < 4; k++) knk[k] = kn[k];
+#pragma unroll
+      for (int tt = 0; tt < 8; tt++) vnk[tt] = vnew[(size_t)bh * D + 16 * tt + col];
+    }
+    wait_vmcnt<0>();
+  } else {
+    issue_first();
+    wait_vmcnt<HASQ ? NSLOT * NLD : 0>();  // the query copies (issued before the group copies)
+  }
+  compiler_fence();
+  // the query slice of lane (col, kq): head col, channels 32kq .. 32kq+31
+  u4 qv[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) qv[i] = *(const u4*)&lds.qin[hq][32 * kq + 8 * i];
 
   // kept key chunks (all four unless PRUNE), a wave-uniform mask: E_m sums
   // min(floor(4096 |q|), 2^20) over chunk m's 32 channels and the G heads
@@ -447,8 +594,6 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       for (int i = 0; i < 4; i++) qv[i] = u4{0, 0, 0, 0};
     }
   }
-  // lanes 0..31 read the key scales (lanes 0..15) and zeros (16..31) of
-  // channels 8 (lane % 16) .. +7, i.e. of chunk (lane % 16) / 4
   const int kept0 = __builtin_ctz(kmask);
   const int kqa = ((kmask >> kq) & 1u) ? kq : kept0;
   // kept chunks in ascending order, two bits each (uniform)
@@ -463,9 +608,6 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       }
   }
 
-  const int mla = (lane >= 32 || ((kmask >> ((lane & 15) >> 2)) & 1u))
-                      ? (lane & 31) : ((lane & 16) | (kept0 << 2) | (lane & 3));
-
   // The quantized path multiplies q by key scales in fp16 (q*s, 4*q*s), so
   // each head's query is first scaled by a power of two 2^-qe that puts its
   // largest magnitude in [1/8, 1/4): then 4 |q| s < s <= 65504 for every
@@ -476,9 +618,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   for (int i = 0; i < 4; i++)
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-      float a, b;
-      io_pair_f32<BF16>(qv[i][e], a, b);
-      qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(b)));
+      float a, bb;
+      io_pair_f32<BF16>(qv[i][e], a, bb);
+      qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(bb)));
     }
   qmax = wave_max_kq(qmax);  // over the head's 128 channels (the 4 lanes of column col)
   KVQ_STAMP(tid == 0 && qmax >= 0.0f, 1);
@@ -486,15 +628,18 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int qe = qbexp ? min(max(qbexp - 124, -100), 100) : 0;  // largest |q| < 2^(qe - 2)
   const float qsc = __uint_as_float((uint32_t)(127 - qe) << 23);  // 2^-qe
   const float sc_q = scale_log2 * __uint_as_float((uint32_t)(127 + qe) << 23);
-  // query as fp16 pairs, scaled (zero past the G heads)
-  uint32_t q16[16];
+  // query as fp16 pairs, scaled (zero on lanes of no head); LOCOL: qm is the
+  // same on lo lanes and zero elsewhere, so that pk_fma(q, s, -q_m s) gives
+  // the rounding hi of q*s on hi lanes and its residual lo on lo lanes
+  uint32_t q16[16], qm[16];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-      float a, b;
-      io_pair_f32<BF16>(qv[i][e], a, b);
-      q16[4 * i + e] = hvalid ? pk_rne(a * qsc, b * qsc) : 0u;
+      float a, bb;
+      io_pair_f32<BF16>(qv[i][e], a, bb);
+      q16[4 * i + e] = qvalid ? pk_rne(a * qsc, bb * qsc) : 0u;
+      qm[4 * i + e] = lo_lane ? q16[4 * i + e] : 0u;
     }
 
   const int T_old = min(max(len, 0), g.max_tokens);  // reads stay inside the cache
@@ -503,68 +648,74 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const bool app = FUSED && len >= 0 && len < g.max_tokens;
   const int T = T_old + (app ? 1 : 0);
   const int nq = n_quant(T_old, g.R), ngq = nq / GS;  // FUSED: the prefix before the append
-  const int nrb = (T - nq + GS - 1) / GS;
-  // This wave's quantized groups are first + i*STR, i < nmine.  Exactly PF
-  // group loads are kept in flight (past the end the index is clamped to the
-  // wave's last group, or to group 0: cache hits, never used), so the
-  // compiler can count outstanding loads and never drains the prefetches.
-  const int nmine = first < ngq ? (ngq - first + STR - 1) / STR : 0;
-  const int nlast = nmine > 0 ? first + (nmine - 1) * STR : 0;
-  auto group_at = [&](int i) { return rec0 + (size_t)min(first + i * STR, nlast); };
-  // The nrb ring blocks continue the same order after the groups (block
-  // ngq + r), so they fall to waves holding one group fewer than the most;
-  // a ring block is worked on first, while the group stream warms up.
-  const int ring0 = ((first - ngq) % STR + STR) % STR;
+  const int nr = T - nq;                               // raw (ring) tokens, <= RS
+  // this wave's live groups: g_i < ngq
+  const int nmine = (HASQ && gfirst < ngq) ? (ngq - 1 - gfirst) / STR + 1 : 0;
 
   uint32_t qhi[4] = {0, 0, 0, 0};  // HIMODE 4: 4*q (fp16); HIMODE 16: raw q
-  float q4f[8];                    // HIMODE 4: 4*q in fp32
   int sal_ch = 0;                  // HIMODE 4: salient channel whose scale lane%16 copies
-  if constexpr (HIMODE != 0) {
-    // per-wave tables: this wave's query rows and the salient channels
-    // (pairs of rank < n_hi ascending, then the same + 64)
-    uint16_t(*wq)[D + 8] = lds.u.loop.q16[wave];
-    uint16_t(*wr)[D + 8] = lds.u.loop.qraw[wave];
-    int* hil = lds.u.loop.hil[wave];
+  if constexpr (HIMODE != 0 || PRUNE) {
+    // tables: every head's query rows (each wave writes the same values and
+    // reads only after its own writes) and the salient channels (pairs of
+    // rank < n_hi ascending, then the same + 64)
     if (hvalid) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        *(u4*)&wq[col][32 * kq + 8 * i] = u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
+        *(u4*)&lds.q16[col][32 * kq + 8 * i] =
+            u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
         if constexpr (HIMODE == 16) {  // raw salient keys meet the scaled query in its io dtype
           u4 r;
 #pragma unroll
           for (int e = 0; e < 4; e++) r[e] = scaled_io_pair<BF16>(qv[i][e], qsc);
-          *(u4*)&wr[col][32 * kq + 8 * i] = r;
+          *(u4*)&lds.qraw[col][32 * kq + 8 * i] = r;
         }
       }
     }
+  }
+  if constexpr (HIMODE != 0) {
     bool sal = false;
 #pragma unroll
     for (int r = 0; r < 8; r++)
-      sal |= r < g.n_hi && (__builtin_amdgcn_readfirstlane((int)topv[r >> 2][r & 3]) & 63) == lane;
+      sal |= r < g.n_hi && (top[r] & 63) == lane;
     const unsigned long long m = __ballot(sal);
-    if (lane < 16) hil[lane] = 0;  // stays in range even for a malformed rank table
-    if (sal) {
-      const int idx = __popcll(m & ((1ull << lane) - 1));
-      hil[idx] = lane;
-      hil[g.n_hi + idx] = lane + NPAIR;
+    // the salient channel list in ascending order: entry d < n_hi is the
+    // d-th set bit of m, entry n_hi + d the same + 64; entries past 2 n_hi
+    // are 0 (in range even for a malformed rank table).  Lane d < 16 forms
+    // entry d.
+    if (lane < 16) {
+      const int want = lane < g.n_hi ? lane : lane - g.n_hi;
+      unsigned long long mm = m;
+      int v = 0;
+#pragma unroll
+      for (int d = 0; d < 8; d++) {
+        const int p = mm ? __builtin_ctzll(mm) : 0;
+        v = d == want ? p : v;
+        mm &= mm - 1;
+      }
+      v += lane >= g.n_hi ? NPAIR : 0;
+      lds.hil[lane] = lane < 2 * g.n_hi ? v : 0;
     }
     // LDS accesses of one wave execute in order: a compiler barrier suffices
     __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
+    compiler_fence();
+    // (every read unconditional, in range, so that the eight go out together)
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const int d = 8 * (kq & 1) + e;
       // HIMODE 4: K-lanes 16..31 (kq 2, 3) repeat the digits of lanes 0..15
-      // and carry the rounding residual of 4*q*s; HIMODE 16 uses lanes 0..15
+      // and carry the rounding residual of 4*q*s; HIMODE 16 uses lanes 0..15.
+      // Only the hi columns take the salient terms.
       const bool ok = hvalid && d < g.nh && (HIMODE == 4 || kq < 2);
-      const int ch = ok ? (hil[d] & (D - 1)) : 0;
-      const float v = ok ? half_bits_to_f32(wq[col][ch]) : 0.0f;
-      q4f[e] = 4.0f * v;
-      const uint32_t bits = HIMODE == 4 ? (uint32_t)f32_to_half_bits(4.0f * v)
-                                        : (ok ? (uint32_t)wr[col][ch] : 0u);
-      qhi[e >> 1] |= bits << (16 * (e & 1));
+      const int ch = lds.hil[d] & (D - 1);
+      const uint32_t v = HIMODE == 4 ? (uint32_t)lds.q16[col][ch] : (uint32_t)lds.qraw[col][ch];
+      qhi[e >> 1] |= (ok ? v : 0u) << (16 * (e & 1));
     }
-    sal_ch = hil[lane & 15] & (D - 1);
+    if constexpr (HIMODE == 4) {
+      // 4 q (exact in fp16)
+#pragma unroll
+      for (int e = 0; e < 4; e++) qhi[e] = h2u(u2h(qhi[e]) * u2h(0x44004400u));
+    }
+    sal_ch = lds.hil[lane & 15] & (D - 1);
   }
 
   // PRUNE: each MFMA's 32-long contraction covers one key chunk m.  Lane
@@ -575,23 +726,16 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int pb = 8 * (kq >> 1) + (kq & 1);
   uint32_t qk[4][4];
   if constexpr (PRUNE) {
-    uint16_t(*wq)[D + 8] = lds.u.loop.q16[wave];
     if constexpr (HIMODE == 0) {
-      if (hvalid) {
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-          *(u4*)&wq[col][32 * kq + 8 * i] =
-              u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
-      }
       __builtin_amdgcn_wave_barrier();
-      asm volatile("" ::: "memory");
+      compiler_fence();
     }
 #pragma unroll
     for (int i = 0; i < KEEP; i++) {
       const int mm = (cmap >> (2 * i)) & 3u;
 #pragma unroll
-      for (int b = 0; b < 4; b++)
-        qk[i][b] = hvalid ? *(const uint32_t*)&wq[col][2 * (16 * mm + pb + 2 * b)] : 0u;
+      for (int bb = 0; bb < 4; bb++)
+        qk[i][bb] = qvalid ? *(const uint32_t*)&lds.q16[hq][2 * (16 * mm + pb + 2 * bb)] : 0u;
     }
   }
 
@@ -606,9 +750,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // The running max moves only when some logit exceeds it by more than the
   // slack: a per-lane test and a ballot decide that; the cross-lane max is
   // taken only then.
-  auto softmax_step = [&](const float (&c)[8], float sc, float slack, float (&p)[8]) {
-    const float mc = fmaxf(fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])),
-                           fmaxf(fmaxf(c[4], c[5]), fmaxf(c[6], c[7])));
+  auto softmax_step = [&](const float (&cc)[8], float sc, float slack, float (&p)[8]) {
+    const float mc = fmaxf(fmaxf(fmaxf(cc[0], cc[1]), fmaxf(cc[2], cc[3])),
+                           fmaxf(fmaxf(cc[4], cc[5]), fmaxf(cc[6], cc[7])));
     if (__builtin_amdgcn_ballot_w64(mc * sc > m_run + slack)) {
       const float mx = wave_max_kq(mc) * sc;
       const bool need = mx > m_run + slack;
@@ -621,22 +765,15 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       m_run = m_new;
     }
 #pragma unroll
-    for (int i = 0; i < 8; i++) p[i] = ex2(fmaf(c[i], sc, -m_run));
+    for (int i = 0; i < 8; i++) p[i] = ex2(fmaf(cc[i], sc, -m_run));
   };
 
-  uint32_t* sm = lds.u.loop.stage[wave];
-  auto process_group = [&](const Pref& cur, size_t rec) {
-    // stage the metadata record: [0,64) k scale pairs, [64,128) k zero
-    // pairs, [128,192) v scale pairs (j-major), [192,256) v zero pairs.
-    // LDS accesses of one wave execute in order, so only the compiler must
-    // not move the reads below above this write (a memory fence here would
-    // also wait for the prefetches in flight).
-    ((u4*)sm)[lane] = cur.meta;
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
-
-    // keys: q' = q * s (fp16), bias = q . z (the same for every token row);
-    // each tile's accumulator starts from the bias, so no VALU adds follow
+  // One quantized group, its records in `slot` (copies landed).
+  auto process_group = [&](const uint8_t* slot) {
+    const uint32_t* sm = (const uint32_t*)(slot + SC::META);
+    // keys: q' = q * s as an exact fp16 pair (qs + qsl), bias = q . z (the
+    // same for every token row); each tile's accumulator starts from the
+    // bias, so no VALU adds follow
     uint32_t qs[16], qsl[16];
     f4 cb = {0, 0, 0, 0};
     if constexpr (PRUNE) {
@@ -646,14 +783,14 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         const int mm = (cmap >> (2 * i)) & 3u;
         uint32_t zp[4];
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
-          const uint32_t sp = sm[16 * mm + pb + 2 * b];
-          zp[b] = sm[64 + 16 * mm + pb + 2 * b];
-          qs[4 * i + b] = pk_mul(qk[i][b], sp);
-          if constexpr (LO1) {
-            const h2 a = u2h(qk[i][b]), bb = u2h(sp), h = u2h(qs[4 * i + b]);
-            qsl[4 * i + b] = pk_rne(fmaf((float)a[0], (float)bb[0], -(float)h[0]),
-                                    fmaf((float)a[1], (float)bb[1], -(float)h[1]));
+        for (int bb = 0; bb < 4; bb++) {
+          const uint32_t sp = sm[16 * mm + pb + 2 * bb];
+          zp[bb] = sm[64 + 16 * mm + pb + 2 * bb];
+          if constexpr (LOCOL) {
+            qs[4 * i + bb] = pk_fma_lo(qk[i][bb], sp, pk_mul(lo_lane ? qk[i][bb] : 0u, sp));
+          } else {
+            qs[4 * i + bb] = pk_mul(qk[i][bb], sp);
+            qsl[4 * i + bb] = pk_fma_lo(qk[i][bb], sp, qs[4 * i + bb]);
           }
         }
         cb = mma_f16(u4{zp[0], zp[1], zp[2], zp[3]}, u4{qk[i][0], qk[i][1], qk[i][2], qk[i][3]},
@@ -661,42 +798,42 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       }
     } else {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const u4 sv = ((const u4*)(sm + 16 * kq))[i];
-      const u4 zv = ((const u4*)(sm + 64 + 16 * kq))[i];
+      for (int i = 0; i < 4; i++) {
+        const u4 sv = ((const u4*)(sm + 16 * kq))[i];
+        const u4 zv = ((const u4*)(sm + 64 + 16 * kq))[i];
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        qs[4 * i + e] = pk_mul(q16[4 * i + e], sv[e]);
-        if constexpr (LO1) {
-          // q*s is exact in fp32: its residual after the fp16 rounding
-          const h2 a = u2h(q16[4 * i + e]), b = u2h(sv[e]), h = u2h(qs[4 * i + e]);
-          qsl[4 * i + e] = pk_rne(fmaf((float)a[0], (float)b[0], -(float)h[0]),
-                                  fmaf((float)a[1], (float)b[1], -(float)h[1]));
+        for (int e = 0; e < 4; e++) {
+          if constexpr (LOCOL) {
+            qs[4 * i + e] = pk_fma_lo(q16[4 * i + e], sv[e], pk_mul(qm[4 * i + e], sv[e]));
+          } else {
+            qs[4 * i + e] = pk_mul(q16[4 * i + e], sv[e]);
+            qsl[4 * i + e] = pk_fma_lo(q16[4 * i + e], sv[e], qs[4 * i + e]);
+          }
         }
+        const u4 qb = u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
+        cb = mma_f16(zv, qb, cb);
       }
-      const u4 qb = u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
-      cb = mma_f16(zv, qb, cb);
     }
+    if constexpr (LOCOL) {
+      // the bias enters the hi columns only
+#pragma unroll
+      for (int r = 0; r < 4; r++) cb[r] = lo_lane ? 0.0f : cb[r];
     }
     uint32_t qshi[4];
     if constexpr (HIMODE == 4) {
       // the salient channels' scales, gathered once into a contiguous row
       // (lane l copies digit l%16), then read 8 at a time
-      uint16_t* ss = lds.u.loop.sal_s[wave];
+      uint16_t* ss = lds.sal_s[wave];
       ss[lane & 15] = ((const uint16_t*)sm)[sal_ch];
       __builtin_amdgcn_wave_barrier();
-      asm volatile("" ::: "memory");
+      compiler_fence();
       const u4 spv = *(const u4*)(ss + 8 * (kq & 1));
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        // 4*q*s is exact in fp32; split it into its fp16 rounding hi and the
-        // fp16 residual lo
-        const uint32_t sp = spv[e];
-        const uint32_t hi = pk_mul(qhi[e], sp);
-        const h2 sh = u2h(sp), hh = u2h(hi);
-        const uint32_t lo = pk_rne(fmaf(q4f[2 * e], (float)sh[0], -(float)hh[0]),
-                                   fmaf(q4f[2 * e + 1], (float)sh[1], -(float)hh[1]));
-        qshi[e] = kq < 2 ? hi : lo;
+        // 4*q*s as an exact fp16 pair: K-lanes 0..15 its rounding hi,
+        // K-lanes 16..31 the residual lo
+        const uint32_t hi = pk_mul(qhi[e], spv[e]);
+        qshi[e] = kq < 2 ? hi : pk_fma_lo(qhi[e], spv[e], hi);
       }
     }
     f4 C[2];
@@ -707,36 +844,44 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         const int sh = 2 * (kq & 1);
 #pragma unroll
         for (int i = 0; i < KEEP; i++) {
-          const uint32_t x = (cur.klc[TT][i] >> sh) & 0x33333333u;
+          const int mm = (cmap >> (2 * i)) & 3u;
+          const uint32_t w =
+              ((const uint32_t*)(slot + SC::KLO))[((TT * 4 + mm) * 16 + col) * 2 + (kq >> 1)];
+          const uint32_t x = (w >> sh) & 0x33333333u;
           const u4 cd = u4{cvt2<0>(x), cvt2<1>(x), cvt2<2>(x), cvt2<3>(x)};
           acc = mma_f16(cd, u4{qs[4 * i], qs[4 * i + 1], qs[4 * i + 2], qs[4 * i + 3]}, acc);
-          if constexpr (LO1)
+          if constexpr (!LOCOL)
             acc = mma_f16(cd, u4{qsl[4 * i], qsl[4 * i + 1], qsl[4 * i + 2], qsl[4 * i + 3]}, acc);
         }
       } else {
-      const u2 w = cur.klo[TT];
+        const u2 w = ((const u2*)(slot + SC::KLO))[(TT * 4 + kqa) * 16 + col];
 #pragma unroll
-      for (int u = 0; u < 2; u++) {
-        const uint32_t A = w[u] & 0x33333333u, Bn = (w[u] >> 2) & 0x33333333u;
-        const int k0 = 8 * u;
-        const u4 c0 = u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)};
-        const u4 c1 = u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)};
-        acc = mma_f16(c0, u4{qs[k0], qs[k0 + 1], qs[k0 + 2], qs[k0 + 3]}, acc);
-        acc = mma_f16(c1, u4{qs[k0 + 4], qs[k0 + 5], qs[k0 + 6], qs[k0 + 7]}, acc);
-        if constexpr (LO1) {
-          acc = mma_f16(c0, u4{qsl[k0], qsl[k0 + 1], qsl[k0 + 2], qsl[k0 + 3]}, acc);
-          acc = mma_f16(c1, u4{qsl[k0 + 4], qsl[k0 + 5], qsl[k0 + 6], qsl[k0 + 7]}, acc);
+        for (int u = 0; u < 2; u++) {
+          const uint32_t A = w[u] & 0x33333333u, Bn = (w[u] >> 2) & 0x33333333u;
+          const int k0 = 8 * u;
+          const u4 c0 = u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)};
+          const u4 c1 = u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)};
+          acc = mma_f16(c0, u4{qs[k0], qs[k0 + 1], qs[k0 + 2], qs[k0 + 3]}, acc);
+          acc = mma_f16(c1, u4{qs[k0 + 4], qs[k0 + 5], qs[k0 + 6], qs[k0 + 7]}, acc);
+          if constexpr (!LOCOL) {
+            acc = mma_f16(c0, u4{qsl[k0], qsl[k0 + 1], qsl[k0 + 2], qsl[k0 + 3]}, acc);
+            acc = mma_f16(c1, u4{qsl[k0 + 4], qsl[k0 + 5], qsl[k0 + 6], qsl[k0 + 7]}, acc);
+          }
         }
       }
-      }
       if constexpr (HIMODE == 4) {
-        const uint32_t wsel = (kq & 1) ? cur.khi[TT] >> 16 : cur.khi[TT];
+        const uint32_t kw = ((const uint32_t*)(slot + SC::KHI))[16 * TT + col];
+        const uint32_t wsel = (kq & 1) ? kw >> 16 : kw;
         const uint32_t A = wsel & 0x33333333u, Bn = (wsel >> 2) & 0x33333333u;
         acc = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)},
                       u4{qshi[0], qshi[1], qshi[2], qshi[3]}, acc);
       }
       if constexpr (HIMODE == 16) {
-        u4 a = cur.hraw[TT];
+        // salient channels 8*(kq&1) .. +7 of the lane's token (entries past nh
+        // are masked; the read may run past the record, inside the LDS)
+        const uint16_t* kr = (const uint16_t*)(slot + SC::KHI) + (16 * TT + col) * g.nh + 8 * (kq & 1);
+        const u4a v = *(const u4a*)kr;
+        u4 a = u4{v[0], v[1], v[2], v[3]};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int d = 8 * (kq & 1) + 2 * e;
@@ -749,16 +894,21 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     }
     float cr[8], p[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) cr[i] = C[i >> 2][i & 3];
-    // lanes 32..47 staged the group's value scales (non-negative fp16, so
-    // their bits order as integers)
-    const uint32_t vs2 = pk_max_u16(pk_max_u16(cur.meta[0], cur.meta[1]),
-                                    pk_max_u16(cur.meta[2], cur.meta[3]));
+    for (int i = 0; i < 8; i++)
+      cr[i] = LOCOL ? C[i >> 2][i & 3] + mirror16(C[i >> 2][i & 3]) : C[i >> 2][i & 3];
+    // lanes 32..47 hold the group's value scales in their 16 staged bytes
+    // (non-negative fp16, so their bits order as integers)
+    const u4 meta = ((const u4*)sm)[lane];
+    const uint32_t vs2 = pk_max_u16(pk_max_u16(meta[0], meta[1]), pk_max_u16(meta[2], meta[3]));
     const bool wide = lane >= 32 && lane < 48 && max(vs2 & 0xFFFFu, vs2 >> 16) > VSCALE_WIDE;
     softmax_step(cr, sc_q, __builtin_amdgcn_ballot_w64(wide) ? RESCALE_SLACK_WIDE : RESCALE_SLACK,
                  p);
     const u4 P = u4{pk_rne(p[0], p[1]), pk_rne(p[2], p[3]), pk_rne(p[4], p[5]), pk_rne(p[6], p[7])};
-    // values
+    // LOCOL: the weights on lo lanes (zero elsewhere), as qm for the query
+    u4 Pm;
+#pragma unroll
+    for (int e = 0; e < 4; e++) Pm[e] = lo_lane ? P[e] : 0u;
+    // values: p*s as an exact fp16 pair (pj + pjl) per channel group j
     const bool vkept = VHI && kq < g.n_vhi;
     const u4 za = col < 4 ? ((const u4*)(sm + 192 + 16 * col))[kq]
                           : (col == 4 ? u4{ONES, ONES, ONES, ONES} : u4{0, 0, 0, 0});
@@ -766,60 +916,79 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const u4 sv = ((const u4*)(sm + 128 + 16 * j))[kq];
-      const u4 pj = u4{pk_mul(P[0], sv[0]), pk_mul(P[1], sv[1]), pk_mul(P[2], sv[2]),
-                       pk_mul(P[3], sv[3])};
-      const uint32_t wv = cur.vc[j];
+      u4 pj, pjl;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        if constexpr (LOCOL) {
+          pj[e] = pk_fma_lo(P[e], sv[e], pk_mul(Pm[e], sv[e]));
+        } else {
+          pj[e] = pk_mul(P[e], sv[e]);
+          pjl[e] = pk_fma_lo(P[e], sv[e], pj[e]);
+        }
+      }
+      const uint32_t wv = ((const uint32_t*)(slot + SC::VC))[(j * 4 + kq) * 16 + col];
       const uint32_t A = wv & 0x33333333u, Bn = (wv >> 2) & 0x33333333u;
-      O[2 * j] = mma_f16(u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)}, pj, O[2 * j]);
-      O[2 * j + 1] = mma_f16(u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)}, pj, O[2 * j + 1]);
+      const u4 v0 = u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)};
+      const u4 v1 = u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)};
+      O[2 * j] = mma_f16(v0, pj, O[2 * j]);
+      O[2 * j + 1] = mma_f16(v1, pj, O[2 * j + 1]);
+      if constexpr (!LOCOL) {
+        O[2 * j] = mma_f16(v0, pjl, O[2 * j]);
+        O[2 * j + 1] = mma_f16(v1, pjl, O[2 * j + 1]);
+      }
       if constexpr (VHI) {
         // block kq's high digits (0 past the high-precision blocks), weighted
         // 4 by the convert
-        const uint32_t wh = vkept ? cur.vh[j] : 0u;
+        const uint32_t wh =
+            vkept ? ((const uint32_t*)(slot + SC::VH))[(j * g.n_vhi + kq) * 16 + col] : 0u;
         const uint32_t Ah = wh & 0x33333333u, Bh = (wh >> 2) & 0x33333333u;
-        O[2 * j] = mma_f16(u4{cvt2x4<0>(Ah), cvt2x4<0>(Bh), cvt2x4<1>(Ah), cvt2x4<1>(Bh)}, pj,
-                           O[2 * j]);
-        O[2 * j + 1] = mma_f16(u4{cvt2x4<2>(Ah), cvt2x4<2>(Bh), cvt2x4<3>(Ah), cvt2x4<3>(Bh)}, pj,
-                               O[2 * j + 1]);
+        const u4 h0 = u4{cvt2x4<0>(Ah), cvt2x4<0>(Bh), cvt2x4<1>(Ah), cvt2x4<1>(Bh)};
+        const u4 h1 = u4{cvt2x4<2>(Ah), cvt2x4<2>(Bh), cvt2x4<3>(Ah), cvt2x4<3>(Bh)};
+        O[2 * j] = mma_f16(h0, pj, O[2 * j]);
+        O[2 * j + 1] = mma_f16(h1, pj, O[2 * j + 1]);
+        if constexpr (!LOCOL) {
+          O[2 * j] = mma_f16(h0, pjl, O[2 * j]);
+          O[2 * j + 1] = mma_f16(h1, pjl, O[2 * j + 1]);
+        }
       }
     }
   };
 
-  // ring blocks (16-bit keys and values) of this wave: blocks n < nrb.  Key
-  // and value tiles are requested together (one round trip); the query is
-  // the raw one already in registers.
-  for (int n = ring0; n < nrb; n += STR) {
-    const int pbase = nq + GS * n;
-    const int nvalid = min(GS, T - pbase);
-    const int sb = (pbase / GS) % (g.RS / GS);
-    const uint16_t* rk = (const uint16_t*)c.ring_k + ((size_t)bh * g.RS + sb * GS) * D;
-    const uint16_t* rv = (const uint16_t*)c.ring_v + (((size_t)bh * (g.RS / GS) + sb) * D) * GS;
+  // ---- the ring blocks (16-bit keys and values) of a ring-owning wave:
+  // physical slots 32 rb .. 32 rb + 31; slot sigma holds the position
+  // nq + ((sigma - nq) mod RS), live when that is below T.
+  for (int rb = f; ring_owner && rb < RSB; rb += STR) {
+    if (rb != f) load_ring(rb);
+    if (nr <= 0) continue;
     // FUSED: the appended token's index in this block (-1 if not here); its
     // key row and value column come from knew / vnew, not from the ring
-    const int tnew = app ? T_old - pbase : -1;
-    u4 kt[2][4], vt[8];
-#pragma unroll
-    for (int TT = 0; TT < 2; TT++) {
-      const int tok = tile_token(16 * TT + col);
-      const u4* kr = (const u4*)(rk + (size_t)tok * D + 32 * kqa);
-      if constexpr (FUSED)
-        if (tok == tnew) kr = (const u4*)(knew + (size_t)bh * D + 32 * kqa);
-#pragma unroll
-      for (int k = 0; k < 4; k++) kt[TT][k] = kr[k];
-    }
-#pragma unroll
-    for (int tt = 0; tt < 8; tt++) vt[tt] = *(const u4*)(rv + (size_t)(16 * tt + col) * GS + 8 * kq);
+    const int snew = app ? T_old % g.RS : -1;
+    const int tnew = (snew >= rb * GS && snew < rb * GS + GS) ? snew - rb * GS : -1;
+    auto live = [&](int t) {
+      const int sigma = rb * GS + t;
+      const int d = ((sigma - nq) % g.RS + g.RS) % g.RS;
+      return d < nr;
+    };
+    // a block with no live slot adds nothing (and its logits, all -inf,
+    // must not meet a running max that is still -inf)
+    if (!__builtin_amdgcn_ballot_w64(lane < GS && live(lane))) continue;
     if constexpr (FUSED) {
+#pragma unroll
+      for (int TT = 0; TT < 2; TT++)
+        if (tile_token(16 * TT + col) == tnew) {
+#pragma unroll
+          for (int k = 0; k < 4; k++) kt[TT][k] = knk[k];
+        }
       const int dt = tnew - 8 * kq;  // the new token among this lane's 8 slots
-      if (dt >= 0 && dt < 8) {
+      if (tnew >= 0 && dt >= 0 && dt < 8) {
 #pragma unroll
         for (int tt = 0; tt < 8; tt++) {
-          const uint32_t x = vnew[(size_t)bh * D + 16 * tt + col];
+          const uint32_t x = vnk[tt];
           const int e = dt >> 1, sh = 16 * (dt & 1);
-          const uint32_t m = 0xFFFFu << sh;
+          const uint32_t mk = 0xFFFFu << sh;
 #pragma unroll
           for (int i = 0; i < 4; i++)
-            if (i == e) vt[tt][i] = (vt[tt][i] & ~m) | (x << sh);
+            if (i == e) vt[tt][i] = (vt[tt][i] & ~mk) | (x << sh);
         }
       }
     }
@@ -828,7 +997,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     for (int i = 0; i < 4; i++)
 #pragma unroll
       for (int e = 0; e < 4; e++) qraw[4 * i + e] = hvalid ? qv[i][e] : 0u;
-    f4 C[2];
+    f4 Cr[2];
 #pragma unroll
     for (int TT = 0; TT < 2; TT++) {
       f4 acc = {0, 0, 0, 0};
@@ -836,65 +1005,85 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       for (int k = 0; k < 4; k++)
         acc = mma_raw<BF16>(kt[TT][k],
                             u4{qraw[4 * k], qraw[4 * k + 1], qraw[4 * k + 2], qraw[4 * k + 3]}, acc);
-      C[TT] = acc;
+      Cr[TT] = acc;
     }
     float cr[8], p[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const int t = 8 * kq + 4 * (i >> 2) + (i & 3);
-      cr[i] = t < nvalid ? C[i >> 2][i & 3] : -INFINITY;
+      const float x = LOCOL ? Cr[i >> 2][i & 3] + mirror16(Cr[i >> 2][i & 3]) : Cr[i >> 2][i & 3];
+      cr[i] = live(t) ? x : -INFINITY;
     }
     softmax_step(cr, scale_log2, RESCALE_SLACK, p);  // raw values: the products stay in fp32
 #pragma unroll
     for (int i = 0; i < 8; i++) l_raw += p[i];
     uint32_t Ph[4], Pl[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) split_pair<BF16>(p[2 * i], p[2 * i + 1], Ph[i], Pl[i]);
+    for (int i = 0; i < 4; i++) {
+      split_pair<BF16>(p[2 * i], p[2 * i + 1], Ph[i], Pl[i]);
+      if (lo_lane) Ph[i] = Pl[i] = 0u;  // the raw values enter the hi columns only
+    }
+    uint32_t vkeep[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int t0 = 8 * kq + 2 * e;
+      vkeep[e] = (live(t0) ? 0x0000ffffu : 0u) | (live(t0 + 1) ? 0xffff0000u : 0u);
+    }
 #pragma unroll
     for (int tt = 0; tt < 8; tt++) {
       u4 a = vt[tt];
-      // zero slots past the last token (they may hold stale data)
+      // zero dead slots (they may hold stale data)
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int t0 = 8 * kq + 2 * e;
-        const uint32_t keep =
-            (t0 < nvalid ? 0x0000ffffu : 0u) | (t0 + 1 < nvalid ? 0xffff0000u : 0u);
-        a[e] &= keep;
-      }
+      for (int e = 0; e < 4; e++) a[e] &= vkeep[e];
       O[tt] = mma_raw<BF16>(a, u4{Ph[0], Ph[1], Ph[2], Ph[3]}, O[tt]);
       O[tt] = mma_raw<BF16>(a, u4{Pl[0], Pl[1], Pl[2], Pl[3]}, O[tt]);
     }
   }
-
+  if (ring_owner) issue_first();
   KVQ_STAMP(tid == 0, 2);
+
+  // ---- the quantized groups: slot i % NSLOT holds group i; a consumed slot
+  // is refilled with group i + NSLOT
   if constexpr (HASQ) {
-    if constexpr (PRUNE) {
-      // the first prefetched groups hold all four chunks in chunk order:
-      // move the kept ones to slots 0 .. KEEP-1 (slot i reads chunk >= i).
-      // Done here, after the ring blocks, so that waiting for these loads
-      // does not hold up the set-up work above.
-#pragma unroll
-      for (int k = 0; k < PF; k++)
-#pragma unroll
-        for (int TT = 0; TT < 2; TT++)
-#pragma unroll
-          for (int i = 0; i < KEEP; i++) {
-            const uint32_t mm = (cmap >> (2 * i)) & 3u;
-            const uint32_t* a = pf[k].klc[TT];
-            pf[k].klc[TT][i] = mm == 0 ? a[0] : mm == 1 ? a[1] : mm == 2 ? a[2] : a[3];
-          }
-    }
-    for (int i = 0; i < nmine; i += PF) {
-#pragma unroll
-      for (int k = 0; k < PF; k++) {
-        if (i + k < nmine) process_group(pf[k], group_at(i + k));
+    for (int i = 0; i < nmine; i++) {
+      wait_slot<NLD, NSLOT>(issued - 1 - i);
+      uint8_t* slot = slots + (i % NSLOT) * SLOTB;
+      process_group(slot);
 #ifdef KVQ_STAMPS
-        if (i + k == 0) KVQ_STAMP(tid == 0 && O[0][0] != 12345.0f, 11);
+      if (i == 0) KVQ_STAMP(tid == 0 && O[0][0] != 12345.0f, 11);
 #endif
-        load_group<HIMODE, PRUNE, KEEP, VHI>(c, group_at(i + k + PF), lane, col, kq, kqa, mla,
-                                             cmap, g.nh, g.n_vhi, pf[k]);
+      if (issued < nmine) {
+        // every read of this slot has returned before the copy overwrites it
+        wait_lgkmcnt0();
+        compiler_fence();
+        issue_group<HIMODE, VHI, PRUNE>(c, rec0 + gfirst + (size_t)issued * STR, slot, lane,
+                                        kmask, kept0, g.nh, g.n_vhi);
+        issued++;
       }
     }
+    // copies issued before the length was known, past the live groups: they
+    // must land before the LDS is reused
+    if (issued > nmine) {
+      wait_vmcnt<0>();
+      compiler_fence();
+    }
+  }
+
+  // FUSED: the new token's key and value channel tid, for the ring write of
+  // the first workgroup (loaded after the stream: only copies are in flight
+  // during it)
+  uint16_t knv = 0, vnv = 0;
+  if constexpr (FUSED)
+    if (tid < D) {
+      knv = knew[(size_t)bh * D + tid];
+      vnv = vnew[(size_t)bh * D + tid];
+    }
+
+  if constexpr (LOCOL) {
+#pragma unroll
+    for (int t = 0; t < 8; t++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) O[t][r] += mirror16(O[t][r]);
   }
 
   // ---- merge the waves: per head m, l and unnormalized o
@@ -917,67 +1106,91 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     }
   }
   __syncthreads();
-  // split record: (m, l) and o / l, fp32; thread -> (head, 8 channels).
-  // Records cross workgroups (and L2 slices): every access to them is
-  // device-coherent (sc1), so no cache-wide writeback or invalidate is needed.
+  // per head: the waves' weights relative to the head's largest running max
+  if (tid < G) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; w++) M = fmaxf(M, lds.u.merge.m[w][tid]);
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+      const float mw = lds.u.merge.m[w][tid];
+      const float a = mw == -INFINITY ? 0.0f : ex2(mw - M);
+      lds.u.merge.a[w][tid] = a;
+      L += a * lds.u.merge.l[w][tid];
+    }
+    lds.u.merge.M[tid] = M;
+    lds.u.merge.L[tid] = L;
+    lds.u.merge.inv[tid] = L > 0.0f ? 1.0f / L : 0.0f;
+  }
+  __syncthreads();
+  // split record: (m, l) and o / l, fp32, one element per thread.  Stored
+  // twice: once device-coherent (sc1 stores, seen by a merging workgroup on
+  // any XCD) and once as plain stores, which stay in the L2 of this CU's XCD
+  // (read by the merging workgroup when every split of the (sequence, KV
+  // head) ran on its XCD, which the ticket tells).
   const size_t rbh = (size_t)bh * S * G;  // first record of this (sequence, KV head)
   const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
       ws.o + rbh * D, 0, (int)(S * G * D * 4), BUF_RSRC_WORD3);
-  for (int i = tid; i < G * (D / 8); i += WG_THREADS) {
-    const int h = i / (D / 8), c8 = 8 * (i % (D / 8));
-    float M = lds.u.merge.m[0][h];
+  const __amdgpu_buffer_rsrc_t rs_oL = __builtin_amdgcn_make_buffer_rsrc(
+      ws.oL + rbh * D, 0, (int)(S * G * D * 4), BUF_RSRC_WORD3);
+  for (int e = tid; e < G * D; e += WG_THREADS) {
+    const int h = e / D, cc = e % D;
+    float o = 0.0f;
 #pragma unroll
-    for (int w = 1; w < NW; w++) M = fmaxf(M, lds.u.merge.m[w][h]);
-    f4 oa = {0, 0, 0, 0}, ob = {0, 0, 0, 0};
-    float l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; w++) {
-      const float mw = lds.u.merge.m[w][h];
-      const float a = mw == -INFINITY ? 0.0f : ex2(mw - M);
-      oa += a * *(const f4*)&lds.u.merge.o[w][h][c8];
-      ob += a * *(const f4*)&lds.u.merge.o[w][h][c8 + 4];
-      l += a * lds.u.merge.l[w][h];
-    }
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const int ooff = ((s * G + h) * D + c8) * 4;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, oa * inv), rs_o, ooff, 0, CPOL_SC1);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, ob * inv), rs_o, ooff + 16, 0,
-                                           CPOL_SC1);
-    if (c8 == 0)
-      __hip_atomic_store((uint64_t*)&ws.ml[rbh + (size_t)s * G + h],
-                         (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(l) << 32),
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int w = 0; w < NW; w++) o += lds.u.merge.a[w][h] * lds.u.merge.o[w][h][cc];
+    const float v = o * lds.u.merge.inv[h];
+    const int ooff = ((s * G + h) * D + cc) * 4;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs_o, ooff, 0, CPOL_SC1);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs_oL, ooff, 0, 0);
+  }
+  if (tid < G) {
+    const uint64_t mlv = (uint64_t)__float_as_uint(lds.u.merge.M[tid]) |
+                         ((uint64_t)__float_as_uint(lds.u.merge.L[tid]) << 32);
+    __hip_atomic_store((uint64_t*)&ws.ml[rbh + (size_t)s * G + tid], mlv, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    *(uint64_t*)&ws.mlL[rbh + (size_t)s * G + tid] = mlv;
   }
 
-  // ---- the last workgroup of this (sequence, KV head) merges all splits.
-  // Every record store has completed (s_waitcnt) before the counter moves.
+  // ---- ticket.  Every record store has completed (s_waitcnt) before the
+  // counter moves: the workgroup that takes the last ticket sees every
+  // coherent record, and every plain one in its own L2 if all splits ran on
+  // its XCD.  The 64-bit counter holds one byte per XCD (splits of this
+  // (sequence, KV head) that ran there; S <= 255), or a plain count.
   KVQ_STAMP(tid == 0, 12);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   KVQ_STAMP(tid == 0, 13);
+  uint64_t* tick = (uint64_t*)(ws.tick + (size_t)bh * TICK_STRIDE);
   if (tid == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(&ws.tick[(size_t)bh * TICK_STRIDE], 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    lds.last = prev == (uint32_t)(S - 1);
-#ifdef KVQ_STAMPS
     uint32_t xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-    ws.st[(size_t)blockIdx.x * STAMP_SLOTS + 14] = __builtin_amdgcn_s_memrealtime() + 0 * prev;
-    ws.st[(size_t)blockIdx.x * STAMP_SLOTS + 17] =
+    xcc &= 7u;
+    const bool bytes = S <= 255;
+    const uint64_t mine = bytes ? 1ull << (8 * xcc) : 1ull;
+    const uint64_t prev = __hip_atomic_fetch_add(tick, mine, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t now = prev + mine;
+    // byte sums fit in a byte (S <= 255)
+    const uint32_t arrived = bytes ? (uint32_t)((now * 0x0101010101010101ull) >> 56) : (uint32_t)now;
+    const uint32_t before = arrived - 1;
+    lds.mrank = arrived == (uint32_t)S ? (bytes && now == ((uint64_t)S << (8 * xcc)) ? 1 : 0) : -1;
+    if constexpr (FUSED) lds.first = before == 0u;
+#ifdef KVQ_STAMPS
+    lds.stamp[14] = __builtin_amdgcn_s_memrealtime() + 0 * prev;
+    lds.stamp[17] =
         (unsigned long long)bh | ((unsigned long long)s << 16) | ((unsigned long long)xcc << 32) |
-        ((unsigned long long)prev << 40);
+        ((unsigned long long)before << 40);
 #endif
-    if constexpr (FUSED) lds.first = prev == 0u;
   }
   __syncthreads();
   if constexpr (FUSED) {
     // the first workgroup to finish does the append's ring write and packing
     // while the others still run: nothing in this call reads the packed
-    // records, and the token's ring slot held a quantized position (T_old -
-    // RS < nq), which no wave reads from the ring (the new token itself
-    // comes from knew / vnew).  The length is stored by the last workgroup,
-    // after every workgroup has read it.
+    // records, the ring slot it writes is read by this call's ring block only
+    // as a dead slot or replaced by knew / vnew, and the group [nq, nq + 32)
+    // ends at T - R <= T_old (the new token is not in it).  The length is
+    // stored by the last workgroup, after every workgroup has read it.
     if (lds.first && app) {
       const int slot = T_old % g.RS;
       if (tid < D) {
@@ -986,102 +1199,122 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         rk[(size_t)slot * D + tid] = knv;
         rv[((size_t)(slot / GS) * D + tid) * GS + slot % GS] = vnv;
       }
-      // the group [nq, nq + 32) ends at T - R <= T_old: the new token is not in it
       if (n_quant(T, g.R) > nq && tid < 128)
         pack_ring_group<BF16, VHI>(g, c, bh, nq, tid, lds.u.pack);
     }
+    __syncthreads();  // the packing's LDS is free again before the merge uses it
   }
-  if (!lds.last) return;
-  // item = (head, 8 channels); nsub lanes (a power of two, within one wave)
-  // share an item's splits, each loading up to 8 records at once, and
-  // reduce with shuffles
-  const int items = G * (D / 8);
-  int nsub = 1;
-  while (nsub < 64 && items * nsub * 2 <= WG_THREADS) nsub *= 2;
-  const uint64_t* mlb = (const uint64_t*)(ws.ml + rbh);
+  const int mr = lds.mrank;
+  if (mr < 0) {
+    KVQ_STAMP_FLUSH();
+    return;
+  }
+  const bool local = mr == 1;  // every split ran on this XCD: read the L2 copy
+  if (tid == 0) __hip_atomic_store(tick, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // The last workgroup merges all splits.  Thread (chunk q, subset r): the
+  // 4 channels 4 (q % 32) .. of head q / 32, over splits r, r + NR, ...; the
+  // NR threads of a chunk are adjacent lanes and add up with shuffles.  The
+  // records of the first batch are requested first; the weights
+  // wn[s][h] = 2^(m_s - M_h) l_s / L_h (one wave per head, lanes over splits)
+  // are formed while they arrive.
+  const int NQ = G * (D / 4);
+  int NR = 1;
+  while (NR * 2 * NQ <= WG_THREADS) NR *= 2;
+  const int qc = tid / NR, r = tid % NR;
+  const bool act = qc < NQ;
+  const int h = act ? qc / (D / 4) : 0, c4 = act ? 4 * (qc % (D / 4)) : 0;
+  constexpr int KB = 8;
+  u4 ov[KB];
+  auto load_batch = [&](int k0) {
+#pragma unroll
+    for (int k = 0; k < KB; k++) {
+      const int i = min(r + (k0 + k) * NR, S - 1);  // past S: repeats, never used
+      const int ooff = ((i * G + h) * D + c4) * 4;
+      ov[k] = local ? __builtin_amdgcn_raw_buffer_load_b128(rs_oL, ooff, 0, CPOL_SC0)
+                    : __builtin_amdgcn_raw_buffer_load_b128(rs_o, ooff, 0, CPOL_SC1);
+    }
+  };
+  load_batch(0);
   {
-    const int t = tid;
-    const int item = t / nsub, sub = t % nsub;
-    const bool act = item < items;
-    const int h = act ? item / (D / 8) : 0, c8 = act ? 8 * (item % (D / 8)) : 0;
-    float M = -INFINITY, L = 0.0f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    // a batch: KB records per lane requested at once, then merged in order
-    // (each as it arrives); indices past S repeat the last record and are
-    // skipped
-    auto batch = [&](auto kb, int i0) {
-      constexpr int KB = decltype(kb)::value;
-      uint64_t mlw[KB];
-      u4 ov[KB][2];
+    const uint64_t* mlb = (const uint64_t*)(ws.ml + rbh);
+    const __amdgpu_buffer_rsrc_t rs_mlL = __builtin_amdgcn_make_buffer_rsrc(
+        ws.mlL + rbh, 0, (int)(S * G * 8), BUF_RSRC_WORD3);
+    for (int hh = wave; hh < G; hh += NW) {
+      float mk[16], lk[16];  // split lane + 64 k (S <= 1024)
+      float M = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < KB; k++) {
-        const int i = min(i0 + k * nsub, S - 1);
-        mlw[k] = __hip_atomic_load(mlb + (size_t)i * G + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int ooff = ((i * G + h) * D + c8) * 4;
-        ov[k][0] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, ooff, 0, CPOL_SC1);
-        ov[k][1] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, ooff + 16, 0, CPOL_SC1);
-      }
-#pragma unroll
-      for (int k = 0; k < KB; k++) {
-        const float m = __uint_as_float((uint32_t)mlw[k]);
-        const float l = __uint_as_float((uint32_t)(mlw[k] >> 32));
-        if (i0 + k * nsub >= S || m == -INFINITY) continue;
-        if (m > M) {
-          const float a = ex2(M - m);
-          L *= a;
-#pragma unroll
-          for (int e = 0; e < 8; e++) acc[e] *= a;
-          M = m;
+      for (int k = 0; k < 16; k++) {
+        const int i = lane + 64 * k;
+        mk[k] = -INFINITY;
+        lk[k] = 0.0f;
+        if (i < S) {
+          uint64_t mv;
+          if (local) {
+            const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs_mlL, (i * G + hh) * 8, 0, CPOL_SC0);
+            mv = (uint64_t)x[0] | ((uint64_t)x[1] << 32);
+          } else {
+            mv = __hip_atomic_load(mlb + (size_t)i * G + hh, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+          }
+          mk[k] = __uint_as_float((uint32_t)mv);
+          lk[k] = __uint_as_float((uint32_t)(mv >> 32));
+          M = fmaxf(M, mk[k]);
         }
-        const float wgt = ex2(m - M) * l;
-        L += wgt;
-#pragma unroll
-        for (int e = 0; e < 8; e++) acc[e] += wgt * __uint_as_float(ov[k][e >> 2][e & 3]);
       }
-    };
-    if (S <= 4 * nsub) {  // one batch of 4 covers every split
-      if (act) batch(std::integral_constant<int, 4>{}, sub);
-    } else {
-      for (int i0 = sub; act && i0 < S; i0 += 8 * nsub) batch(std::integral_constant<int, 8>{}, i0);
-    }
-    for (int o = 1; o < nsub; o <<= 1) {
-      const float M2 = __shfl_xor(M, o), L2 = __shfl_xor(L, o);
-      const float Mn = fmaxf(M, M2);
-      const float a1 = M == -INFINITY ? 0.0f : ex2(M - Mn);
-      const float a2 = M2 == -INFINITY ? 0.0f : ex2(M2 - Mn);
-      L = L * a1 + L2 * a2;
+      M = wave_max64(M);
+      float L = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; e++) acc[e] = acc[e] * a1 + __shfl_xor(acc[e], o) * a2;
-      M = Mn;
-    }
-    if (act && sub == 0) {
+      for (int k = 0; k < 16; k++) {
+        const float w = mk[k] == -INFINITY ? 0.0f : ex2(mk[k] - M) * lk[k];
+        mk[k] = w;
+        L += w;
+      }
+      L = wave_sum64(L);
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      uint16_t* op = out + ((size_t)b * g.Hq + kh * G + h) * D + c8;
-      uint16_t bits[8];
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const float v = acc[e] * inv;
-        if constexpr (BF16) {
-          const uint32_t u = __float_as_uint(v);
-          bits[e] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-        } else {
-          bits[e] = f32_to_half_bits(v);
-        }
-      }
-      *(u4*)op = u4{bits[0] | ((uint32_t)bits[1] << 16), bits[2] | ((uint32_t)bits[3] << 16),
-                    bits[4] | ((uint32_t)bits[5] << 16), bits[6] | ((uint32_t)bits[7] << 16)};
+      for (int k = 0; k < 16; k++)
+        if (lane + 64 * k < S) lds.u.fin.wn[(lane + 64 * k) * MAXG + hh] = mk[k] * inv;
     }
+  }
+  __syncthreads();
+  f4 acc = {0, 0, 0, 0};
+  const int nk = (S - r + NR - 1) / NR;  // this thread's splits
+  for (int k0 = 0; k0 < nk; k0 += KB) {
+    if (k0 > 0) load_batch(k0);
+#pragma unroll
+    for (int k = 0; k < KB; k++) {
+      if (k0 + k >= nk) break;
+      const float w = lds.u.fin.wn[(r + (k0 + k) * NR) * MAXG + h];
+      acc += w * __builtin_bit_cast(f4, ov[k]);
+    }
+  }
+  for (int o = 1; o < NR; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; e++) acc[e] += __shfl_xor(acc[e], o);
+  if (act && r == 0) {
+    uint16_t* op = out + ((size_t)b * g.Hq + kh * G + h) * D + c4;
+    uint16_t bits[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const float v = acc[e];
+      if constexpr (BF16) {
+        const uint32_t u = __float_as_uint(v);
+        bits[e] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+      } else {
+        bits[e] = f32_to_half_bits(v);
+      }
+    }
+    *(u2*)op = u2{bits[0] | ((uint32_t)bits[1] << 16), bits[2] | ((uint32_t)bits[3] << 16)};
   }
   KVQ_STAMP(tid == 0, 15);
 #ifdef KVQ_STAMPS
   __builtin_amdgcn_s_waitcnt(0);
   KVQ_STAMP(tid == 0, 16);
 #endif
-  if (tid == 0)  // ready for the next call
-    __hip_atomic_store(&ws.tick[(size_t)bh * TICK_STRIDE], 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  KVQ_STAMP_FLUSH();
   if constexpr (FUSED) {
     // the append's length (or its error): every workgroup of this (sequence,
-    // KV head) has read the length before it took its ticket
+    // KV head) read the length before it took its ticket
     if (tid == 0) {
       if (app) c.len[bh] = T;
       else atomicOr(c.err, len < 0 ? 2 : 1);
@@ -1102,50 +1335,51 @@ struct Launch {
   hipStream_t st;
 };
 
-template <bool BF16, int HIMODE, bool LO1, int KEEP, bool VHI, bool FUSED>
-static void launch_one(const Geo& g, const Launch& a) {
+template <bool BF16, int HIMODE, int KEEP, bool VHI, bool FUSED, bool LOCOL>
+static void launch_cols(const Geo& g, const Launch& a) {
   const dim3 grid(g.B * g.Hkv * a.S), block(WG_THREADS);
   if (g.NG > 0)
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, LO1, KEEP, VHI, FUSED>), grid, block, 0,
-                       a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, KEEP, VHI, FUSED, LOCOL>), grid, block,
+                       0, a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,
                        (uint16_t*)a.out, (const uint16_t*)a.knew, (const uint16_t*)a.vnew);
   else
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, LO1, KEEP, false, FUSED>), grid, block,
-                       0, a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, KEEP, false, FUSED, LOCOL>), grid,
+                       block, 0, a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,
                        (uint16_t*)a.out, (const uint16_t*)a.knew, (const uint16_t*)a.vnew);
 }
 
+template <bool BF16, int HIMODE, int KEEP, bool VHI, bool FUSED>
+static void launch_one(const Geo& g, const Launch& a) {
+  if (g.G <= 8) launch_cols<BF16, HIMODE, KEEP, VHI, FUSED, true>(g, a);
+  else launch_cols<BF16, HIMODE, KEEP, VHI, FUSED, false>(g, a);
+}
+
 // keep 0: the fused append-and-decode call (all four key chunks)
-template <bool BF16, int HIMODE, bool LO1, bool VHI>
+template <bool BF16, int HIMODE, bool VHI>
 static void launch_keep(const Geo& g, int keep, const Launch& a) {
   switch (keep) {
-    case 0: launch_one<BF16, HIMODE, LO1, 4, VHI, true>(g, a); break;
-    case 1: launch_one<BF16, HIMODE, LO1, 1, VHI, false>(g, a); break;
-    case 2: launch_one<BF16, HIMODE, LO1, 2, VHI, false>(g, a); break;
-    case 3: launch_one<BF16, HIMODE, LO1, 3, VHI, false>(g, a); break;
-    default: launch_one<BF16, HIMODE, LO1, 4, VHI, false>(g, a); break;
+    case 0: launch_one<BF16, HIMODE, 4, VHI, true>(g, a); break;
+    case 1: launch_one<BF16, HIMODE, 1, VHI, false>(g, a); break;
+    case 2: launch_one<BF16, HIMODE, 2, VHI, false>(g, a); break;
+    case 3: launch_one<BF16, HIMODE, 3, VHI, false>(g, a); break;
+    default: launch_one<BF16, HIMODE, 4, VHI, false>(g, a); break;
   }
 }
 
 // Two value precisions touch only the value side and pruning only the key
 // side, so every combination has its own kernel.
 template <bool BF16, int HIMODE>
-static void launch_lo1(const Geo& g, int keep, const Launch& a) {
-  if (g.n_lo1 > 0) {
-    if (g.n_vhi > 0) launch_keep<BF16, HIMODE, true, true>(g, keep, a);
-    else launch_keep<BF16, HIMODE, true, false>(g, keep, a);
-  } else {
-    if (g.n_vhi > 0) launch_keep<BF16, HIMODE, false, true>(g, keep, a);
-    else launch_keep<BF16, HIMODE, false, false>(g, keep, a);
-  }
+static void launch_vhi(const Geo& g, int keep, const Launch& a) {
+  if (g.n_vhi > 0) launch_keep<BF16, HIMODE, true>(g, keep, a);
+  else launch_keep<BF16, HIMODE, false>(g, keep, a);
 }
 
 template <bool BF16>
 hipError_t launch_decode_io(const Geo& g, int keep, const Launch& a) {
   const int hm = g.n_hi == 0 ? 0 : g.bits_hi;
-  if (hm == 0) launch_lo1<BF16, 0>(g, keep, a);
-  else if (hm == 4) launch_lo1<BF16, 4>(g, keep, a);
-  else launch_lo1<BF16, 16>(g, keep, a);
+  if (hm == 0) launch_vhi<BF16, 0>(g, keep, a);
+  else if (hm == 4) launch_vhi<BF16, 4>(g, keep, a);
+  else launch_vhi<BF16, 16>(g, keep, a);
   return hipGetLastError();
 }
 
@@ -1158,7 +1392,7 @@ template hipError_t launch_decode_io<false>(const Geo&, int, const Launch&);
 extern template hipError_t launch_decode_io<false>(const Geo&, int, const Launch&);
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {
-  size_t n = ws_tick_bytes(B, Hkv) + ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S);
+  size_t n = ws_tick_bytes(B, Hkv) + 2 * (ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S));
 #ifdef KVQ_STAMPS
   n += (size_t)B * Hkv * S * STAMP_SLOTS * 8;  // the timestamps of every workgroup
 #endif
@@ -1171,7 +1405,7 @@ hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float 
   Ws w = ws_layout(workspace, g.B, g.Hq, g.Hkv, S);
 #ifdef KVQ_STAMPS
   w.st = (unsigned long long*)((char*)workspace + ws_tick_bytes(g.B, g.Hkv) +
-                               ws_ml_bytes(g.B, g.Hq, S) + ws_o_bytes(g.B, g.Hq, S));
+                               2 * (ws_ml_bytes(g.B, g.Hq, S) + ws_o_bytes(g.B, g.Hq, S)));
 #endif
   const Launch a{q, c, sm_scale * 1.4426950408889634f, S, w, out, k_new, v_new, st};
   return g.bf16 ? launch_decode_io<true>(g, keep, a) : launch_decode_io<false>(g, keep, a);

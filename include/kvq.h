@@ -165,15 +165,17 @@ typedef struct {
 kvq_status kvq_cache_sizes(const kvq_layout *L, size_t sizes[KVQ_NBUF] /*host*/);
 
 /* Workspace bytes kvq_decode_attn needs for `n_splits` token splits per
- * (sequence, KV head), 1 <= n_splits <= 1024: first one 32-bit counter per
+ * (sequence, KV head), 1 <= n_splits <= 1024: first one 64-bit counter per
  * (sequence, KV head), each on a 256-byte line of its own (at offset 0
  * whatever the split count), then per query head and split one fp32
- * (running max, sum) record, then one fp32 [128] normalized partial output;
- * each part starts on a 256-byte boundary.  The caller zero-fills a
- * workspace once before its first use; every completed call leaves the
- * counters at zero again, so one workspace may serve calls with different
- * split counts and layouts in turn (each needing no more than its size).
- * One workspace serves one call at a time. */
+ * (running max, sum) record, then one fp32 [128] normalized partial output,
+ * then a second copy of both record arrays (the first is stored
+ * device-coherent, the second stays in the L2 of the storing XCD); each part
+ * starts on a 256-byte boundary.  The caller zero-fills a workspace once
+ * before its first use; every completed call leaves its counters at zero
+ * again, so one workspace may serve calls with different split counts and
+ * layouts in turn (each needing no more than its size).  One workspace
+ * serves one call at a time. */
 kvq_status kvq_workspace_bytes(const kvq_layout *L, int32_t n_splits,
                                size_t *bytes /*host*/);
 

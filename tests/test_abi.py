@@ -95,8 +95,9 @@ def test_workspace_bytes():
     L = L32k()
     assert kvq.kvq_workspace_bytes(L, 1) < kvq.kvq_workspace_bytes(L, 32)
     rec = 32 * 32  # query heads x splits
-    # counters (one 256-byte line per KV head), fp32 (m, l), fp32 o/l [128]
-    want = 8 * 256 + (rec * 8 + 255) // 256 * 256 + rec * 512
+    # counters (one 256-byte line per KV head), then twice (a device-coherent
+    # copy and an L2-local copy) fp32 (m, l) and fp32 o/l [128]
+    want = 8 * 256 + 2 * ((rec * 8 + 255) // 256 * 256 + rec * 512)
     assert kvq.kvq_workspace_bytes(L, 32) == want
     n = ctypes.c_size_t(0)
     for S in (0, 1025, -1):

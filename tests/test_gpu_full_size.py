@@ -65,8 +65,6 @@ def test_llama3_8b_32k_full():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.xfail(strict=True, reason="single fp16 roundings of q*s and p*s exceed 2e-3 at these "
-                                      "logits (measured 0.0125 and 0.028); exact split pending")
 @pytest.mark.parametrize("qscale", [8, 16])
 def test_llama3_8b_32k_large_logits(qscale):
     # PN-Mix (abstract): the error of pairs with large pair-norm products
