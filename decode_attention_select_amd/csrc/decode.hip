@@ -60,6 +60,7 @@ namespace kvq {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
@@ -93,6 +94,10 @@ __device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int BUF_RSRC_WORD3 = 0x00020000;
 constexpr int CPOL_SC1 = 16;
 constexpr int CPOL_SC0 = 1;  // bypasses the CU's L1 only: reads what the XCD's L2 holds
+// non-temporal: the streamed group records go through the L2 with the
+// streaming policy, so that they do not push out what is reused there (the
+// kernel's code, the split records)
+constexpr int CPOL_NT = 2;
 
 // 16-bit input pair -> fp16 pair (bf16 widened exactly, then RNE to fp16)
 template <bool BF16>
@@ -239,8 +244,9 @@ __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // One direct global->LDS copy: every active lane moves the 16 bytes at `src`
 // to LDS address `dst` + 16 * lane (dst uniform).
+template <int CPOL = 0>
 __device__ inline void dma16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, CPOL);
 }
 
 // One LDS slot holds the records of one quantized group, copied from HBM by
@@ -280,7 +286,7 @@ __device__ inline void issue_group(const kvq_cache& c, size_t rec, uint8_t* slot
   // k_lo: lane l holds words 4l .. 4l+3, of key chunk (l / 8) % 4
   int lk = lane;
   if (PRUNE && !((kmask >> ((lane >> 3) & 3)) & 1u)) lk = (lane & ~24) | (kept0 << 3);
-  dma16((const uint8_t*)c.k_lo + rec * 1024 + lk * 16, slot + C::KLO);
+  dma16<CPOL_NT>((const uint8_t*)c.k_lo + rec * 1024 + lk * 16, slot + C::KLO);
   // metadata: lanes 0..31 k_meta (0..15 scales, 16..31 zeros of channels
   // 8 (l % 16) .. +7, chunk (l % 16) / 4), lanes 32..63 v_meta
   {
@@ -289,16 +295,16 @@ __device__ inline void issue_group(const kvq_cache& c, size_t rec, uint8_t* slot
       lm = (lane & 16) | (kept0 << 2) | (lane & 3);
     const uint8_t* src = lane < 32 ? (const uint8_t*)c.k_meta + rec * 512 + lm * 16
                                    : (const uint8_t*)c.v_meta + rec * 512 + (lane - 32) * 16;
-    dma16(src, slot + C::META);
+    dma16<CPOL_NT>(src, slot + C::META);
   }
-  dma16((const uint8_t*)c.v_codes + rec * 1024 + lane * 16, slot + C::VC);
+  dma16<CPOL_NT>((const uint8_t*)c.v_codes + rec * 1024 + lane * 16, slot + C::VC);
   if constexpr (HIMODE == 4)  // 128 bytes
-    dma16((const uint8_t*)c.k_hi + rec * 128 + (lane & 7) * 16, slot + C::KHI);
+    dma16<CPOL_NT>((const uint8_t*)c.k_hi + rec * 128 + (lane & 7) * 16, slot + C::KHI);
   if constexpr (HIMODE == 16)  // 32 rows of nh raw salient values: 64 nh bytes (nh >= 2)
-    dma16((const uint8_t*)c.k_hi + rec * 64 * nh + (lane < 4 * nh ? lane : lane & 3) * 16,
+    dma16<CPOL_NT>((const uint8_t*)c.k_hi + rec * 64 * nh + (lane < 4 * nh ? lane : lane & 3) * 16,
           slot + C::KHI);
   if constexpr (VHI)  // the high-digit words (after the 8 order words): 256 n_vhi bytes
-    dma16((const uint8_t*)(c.v_hi + rec * (8 + 64 * nvhi) + 8) +
+    dma16<CPOL_NT>((const uint8_t*)(c.v_hi + rec * (8 + 64 * nvhi) + 8) +
               (lane < 16 * nvhi ? lane : lane & 15) * 16,
           slot + C::VH);
 }
@@ -397,12 +403,12 @@ inline Ws ws_layout(void* base, int B, int Hq, int Hkv, int S) {
 struct LdsMerge {
   float o[NW][MAXG][D + 4];  // wave results before the workgroup merge (padded rows)
   float m[NW][MAXG], l[NW][MAXG];
-  float a[NW][MAXG];         // each wave's weight 2^(m_w - M) per head
-  float M[MAXG], inv[MAXG], L[MAXG];
 };
-// The final merge: each split's weight per head, 2^(m_s - M) l_s / L.
+// The final merge: every split's (m, l) per head, then its weight, and per
+// head 1 / L.
 struct LdsFinal {
-  float wn[1024 * MAXG];
+  f2 ml[1024 * MAXG];  // (m, l), then (w, l) with w = 2^(m - M) l
+  float inv[MAXG];
 };
 template <int SLOTB, int NSLOT>
 struct Lds {
@@ -1089,6 +1095,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // ---- merge the waves: per head m, l and unnormalized o
   KVQ_STAMP(lane == 0 && O[0][0] != 12345.0f, 3 + wave);
   __syncthreads();  // every wave is done with the loop-phase LDS
+  KVQ_STAMP(tid == 0, 23);
   {
     const float l_q = __shfl(Cvb[0], 16 + col);  // all-ones row 4 -> lane 16 + col
     const float l = l_q + wave_sum_kq(l_raw);
@@ -1106,29 +1113,13 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     }
   }
   __syncthreads();
-  // per head: the waves' weights relative to the head's largest running max
-  if (tid < G) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; w++) M = fmaxf(M, lds.u.merge.m[w][tid]);
-    float L = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; w++) {
-      const float mw = lds.u.merge.m[w][tid];
-      const float a = mw == -INFINITY ? 0.0f : ex2(mw - M);
-      lds.u.merge.a[w][tid] = a;
-      L += a * lds.u.merge.l[w][tid];
-    }
-    lds.u.merge.M[tid] = M;
-    lds.u.merge.L[tid] = L;
-    lds.u.merge.inv[tid] = L > 0.0f ? 1.0f / L : 0.0f;
-  }
-  __syncthreads();
-  // split record: (m, l) and o / l, fp32, one element per thread.  Stored
-  // twice: once device-coherent (sc1 stores, seen by a merging workgroup on
-  // any XCD) and once as plain stores, which stay in the L2 of this CU's XCD
-  // (read by the merging workgroup when every split of the (sequence, KV
-  // head) ran on its XCD, which the ticket tells).
+  KVQ_STAMP(tid == 0, 24);
+  // split record: (m, l) and o / l per head, fp32, one element per thread
+  // (each thread forms its head's wave weights 2^(m_w - M) itself from
+  // broadcast reads).  Stored twice: once device-coherent (sc1 stores, seen
+  // by a merging workgroup on any XCD) and once as plain stores, which stay
+  // in the L2 of this CU's XCD (read by the merging workgroup when every
+  // split of the (sequence, KV head) ran on its XCD, which the ticket tells).
   const size_t rbh = (size_t)bh * S * G;  // first record of this (sequence, KV head)
   const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
       ws.o + rbh * D, 0, (int)(S * G * D * 4), BUF_RSRC_WORD3);
@@ -1136,20 +1127,27 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       ws.oL + rbh * D, 0, (int)(S * G * D * 4), BUF_RSRC_WORD3);
   for (int e = tid; e < G * D; e += WG_THREADS) {
     const int h = e / D, cc = e % D;
-    float o = 0.0f;
+    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; w++) o += lds.u.merge.a[w][h] * lds.u.merge.o[w][h][cc];
-    const float v = o * lds.u.merge.inv[h];
+    for (int w = 0; w < NW; w++) M = fmaxf(M, lds.u.merge.m[w][h]);
+    float L = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+      const float mw = lds.u.merge.m[w][h];
+      const float aw = mw == -INFINITY ? 0.0f : ex2(mw - M);
+      L += aw * lds.u.merge.l[w][h];
+      o += aw * lds.u.merge.o[w][h][cc];
+    }
+    const float v = L > 0.0f ? o / L : 0.0f;
     const int ooff = ((s * G + h) * D + cc) * 4;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs_o, ooff, 0, CPOL_SC1);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs_oL, ooff, 0, 0);
-  }
-  if (tid < G) {
-    const uint64_t mlv = (uint64_t)__float_as_uint(lds.u.merge.M[tid]) |
-                         ((uint64_t)__float_as_uint(lds.u.merge.L[tid]) << 32);
-    __hip_atomic_store((uint64_t*)&ws.ml[rbh + (size_t)s * G + tid], mlv, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    *(uint64_t*)&ws.mlL[rbh + (size_t)s * G + tid] = mlv;
+    if (cc == 0) {
+      const uint64_t mlv = (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(L) << 32);
+      __hip_atomic_store((uint64_t*)&ws.ml[rbh + (size_t)s * G + h], mlv, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      *(uint64_t*)&ws.mlL[rbh + (size_t)s * G + h] = mlv;
+    }
   }
 
   // ---- ticket.  Every record store has completed (s_waitcnt) before the
@@ -1214,9 +1212,10 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // The last workgroup merges all splits.  Thread (chunk q, subset r): the
   // 4 channels 4 (q % 32) .. of head q / 32, over splits r, r + NR, ...; the
   // NR threads of a chunk are adjacent lanes and add up with shuffles.  The
-  // records of the first batch are requested first; the weights
-  // wn[s][h] = 2^(m_s - M_h) l_s / L_h (one wave per head, lanes over splits)
-  // are formed while they arrive.
+  // (m, l) of the first 64 splits and the records of up to 2 KB splits per
+  // thread are requested at once, in that order; meanwhile each head's
+  // weights w_i = 2^(m_i - M) l_i (M the largest running max) and 1 / L,
+  // L = sum w_i, are formed (one wave per head, lanes over splits).
   const int NQ = G * (D / 4);
   int NR = 1;
   while (NR * 2 * NQ <= WG_THREADS) NR *= 2;
@@ -1224,79 +1223,76 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const bool act = qc < NQ;
   const int h = act ? qc / (D / 4) : 0, c4 = act ? 4 * (qc % (D / 4)) : 0;
   constexpr int KB = 8;
-  u4 ov[KB];
-  auto load_batch = [&](int k0) {
+  const int nk = (S - r + NR - 1) / NR;  // this thread's splits
+  const int nkmax = (S + NR - 1) / NR;   // the most any thread has
+  const __amdgpu_buffer_rsrc_t rs_mlL =
+      __builtin_amdgcn_make_buffer_rsrc(ws.mlL + rbh, 0, (int)(S * G * 8), BUF_RSRC_WORD3);
+  auto load_ml = [&](int i, int hh) -> uint64_t {
+    if (local) {
+      const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs_mlL, (i * G + hh) * 8, 0, CPOL_SC0);
+      return (uint64_t)x[0] | ((uint64_t)x[1] << 32);
+    }
+    return __hip_atomic_load((const uint64_t*)&ws.ml[rbh + (size_t)i * G + hh], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto load_batch = [&](u4 (&ov)[KB], int k0) {
 #pragma unroll
     for (int k = 0; k < KB; k++) {
-      const int i = min(r + (k0 + k) * NR, S - 1);  // past S: repeats, never used
-      const int ooff = ((i * G + h) * D + c4) * 4;
+      const int ooff = ((min(r + (k0 + k) * NR, S - 1) * G + h) * D + c4) * 4;  // past S: unused
       ov[k] = local ? __builtin_amdgcn_raw_buffer_load_b128(rs_oL, ooff, 0, CPOL_SC0)
                     : __builtin_amdgcn_raw_buffer_load_b128(rs_o, ooff, 0, CPOL_SC1);
     }
   };
-  load_batch(0);
-  {
-    const uint64_t* mlb = (const uint64_t*)(ws.ml + rbh);
-    const __amdgpu_buffer_rsrc_t rs_mlL = __builtin_amdgcn_make_buffer_rsrc(
-        ws.mlL + rbh, 0, (int)(S * G * 8), BUF_RSRC_WORD3);
-    for (int hh = wave; hh < G; hh += NW) {
-      float mk[16], lk[16];  // split lane + 64 k (S <= 1024)
-      float M = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 16; k++) {
-        const int i = lane + 64 * k;
-        mk[k] = -INFINITY;
-        lk[k] = 0.0f;
-        if (i < S) {
-          uint64_t mv;
-          if (local) {
-            const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs_mlL, (i * G + hh) * 8, 0, CPOL_SC0);
-            mv = (uint64_t)x[0] | ((uint64_t)x[1] << 32);
-          } else {
-            mv = __hip_atomic_load(mlb + (size_t)i * G + hh, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-          }
-          mk[k] = __uint_as_float((uint32_t)mv);
-          lk[k] = __uint_as_float((uint32_t)(mv >> 32));
-          M = fmaxf(M, mk[k]);
-        }
-      }
-      M = wave_max64(M);
-      float L = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 16; k++) {
-        const float w = mk[k] == -INFINITY ? 0.0f : ex2(mk[k] - M) * lk[k];
-        mk[k] = w;
-        L += w;
-      }
-      L = wave_sum64(L);
-      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-#pragma unroll
-      for (int k = 0; k < 16; k++)
-        if (lane + 64 * k < S) lds.u.fin.wn[(lane + 64 * k) * MAXG + hh] = mk[k] * inv;
+  const uint64_t ml0 = wave < G ? load_ml(min(lane, S - 1), wave) : 0ull;
+  u4 ova[KB], ovb[KB];
+  load_batch(ova, 0);
+  if (nkmax > KB) load_batch(ovb, KB);
+  KVQ_STAMP(tid == 0, 18);
+  for (int hh = wave; hh < G; hh += NW) {
+    float M = -INFINITY;
+    for (int i = lane; i < S; i += 64) {
+      const uint64_t mv = (hh == wave && i == lane) ? ml0 : load_ml(i, hh);
+      const float mi = __uint_as_float((uint32_t)mv);
+      lds.u.fin.ml[i * MAXG + hh] = f2{mi, __uint_as_float((uint32_t)(mv >> 32))};
+      M = fmaxf(M, mi);
     }
+    M = wave_max64(M);
+    float L = 0.0f;
+    for (int i = lane; i < S; i += 64) {
+      const f2 x = lds.u.fin.ml[i * MAXG + hh];
+      const float w = x[0] == -INFINITY ? 0.0f : ex2(x[0] - M) * x[1];
+      lds.u.fin.ml[i * MAXG + hh][0] = w;
+      L += w;
+    }
+    L = wave_sum64(L);
+    if (lane == 0) lds.u.fin.inv[hh] = L > 0.0f ? 1.0f / L : 0.0f;
   }
   __syncthreads();
+  KVQ_STAMP(tid == 0, 19);
   f4 acc = {0, 0, 0, 0};
-  const int nk = (S - r + NR - 1) / NR;  // this thread's splits
-  for (int k0 = 0; k0 < nk; k0 += KB) {
-    if (k0 > 0) load_batch(k0);
+  auto accum = [&](const u4 (&ov)[KB], int k0) {
 #pragma unroll
-    for (int k = 0; k < KB; k++) {
-      if (k0 + k >= nk) break;
-      const float w = lds.u.fin.wn[(r + (k0 + k) * NR) * MAXG + h];
-      acc += w * __builtin_bit_cast(f4, ov[k]);
-    }
+    for (int k = 0; k < KB; k++)
+      if (k0 + k < nk)
+        acc += lds.u.fin.ml[(r + (k0 + k) * NR) * MAXG + h][0] * __builtin_bit_cast(f4, ov[k]);
+  };
+  accum(ova, 0);
+  if (nkmax > KB) accum(ovb, KB);
+  for (int k0 = 2 * KB; k0 < nkmax; k0 += KB) {
+    load_batch(ova, k0);
+    accum(ova, k0);
   }
   for (int o = 1; o < NR; o <<= 1)
 #pragma unroll
     for (int e = 0; e < 4; e++) acc[e] += __shfl_xor(acc[e], o);
+  KVQ_STAMP(tid == 0, 20);
   if (act && r == 0) {
+    const float inv = lds.u.fin.inv[h];
     uint16_t* op = out + ((size_t)b * g.Hq + kh * G + h) * D + c4;
     uint16_t bits[4];
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-      const float v = acc[e];
+      const float v = acc[e] * inv;
       if constexpr (BF16) {
         const uint32_t u = __float_as_uint(v);
         bits[e] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
