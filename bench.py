@@ -28,10 +28,75 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
-# HBM bytes per launch of the decode kernel on the default workload, from the
-# FETCH_SIZE and WRITE_SIZE counters scaled by a plain copy; None when the
-# kernel has changed since they were read.
-TRAFFIC = 27513237
+# HBM bytes per launch of the decode kernel on the default workload: a
+# committed record of the FETCH_SIZE and WRITE_SIZE counters scaled by a plain
+# copy (written by --traffic-from), valid only for the sources it was
+# measured on (their hash is in the record); null once they have changed.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_traffic_llama3-8b-32k.md")
+DECODE_SOURCES = ["decode_attention_select_amd/csrc/decode.hip",
+                  "decode_attention_select_amd/csrc/stream.h",
+                  "decode_attention_select_amd/csrc/common.h",
+                  "decode_attention_select_amd/csrc/quant_group.h", "include/kvq.h"]
+
+
+def decode_sources_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """Bytes per launch from the committed counter record, or None when there
+    is no record for this workload or the decode sources have changed."""
+    try:
+        lines = open(TRAFFIC_RECORD).read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        if line.startswith("record: "):
+            rec = json.loads(line[len("record: "):])
+            if rec.get("workload") == workload and rec.get("sources") == decode_sources_hash():
+                return int(rec["bytes_per_launch"])
+    return None
+
+
+def counter_means(db_dir: str, kernel_substring: str) -> dict:
+    """Per-dispatch means of every counter of the dispatches whose kernel name
+    holds `kernel_substring`, from a rocprofv3 --pmc output directory."""
+    import glob
+    import sqlite3
+    out = {}
+    for db in glob.glob(os.path.join(db_dir, "**", "*.db"), recursive=True):
+        con = sqlite3.connect(db)
+        q = ("select s.kernel_name, d.id, p.name, e.value from rocpd_kernel_dispatch d "
+             "join rocpd_info_kernel_symbol s on d.kernel_id = s.id "
+             "join rocpd_pmc_event e on e.event_id = d.event_id "
+             "join rocpd_info_pmc p on e.pmc_id = p.id")
+        for name, did, pmc, val in con.execute(q):
+            if kernel_substring in name:
+                out.setdefault(pmc, {}).setdefault(did, 0.0)
+                out[pmc][did] += val
+    return {k: sum(v.values()) / len(v) for k, v in out.items()}
+
+
+def traffic_record(dec_fetch, dec_write, copy_fetch, copy_write, copy_mib=256):
+    """The traffic record line from four rocprofv3 --pmc directories: the
+    decode kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
+    by what the same counter reads for a copy of copy_mib MiB."""
+    f = counter_means(dec_fetch, "decode_kernel")["FETCH_SIZE"]
+    wr = counter_means(dec_write, "decode_kernel")["WRITE_SIZE"]
+    cf = counter_means(copy_fetch, "copyBuffer")["FETCH_SIZE"]
+    cw = counter_means(copy_write, "copyBuffer")["WRITE_SIZE"]
+    kib = copy_mib * 1024.0
+    sf, sw = kib / cf, kib / cw
+    return {"workload": "llama3-8b-32k", "sources": decode_sources_hash(),
+            "fetch_kib": round(f, 2), "write_kib": round(wr, 2),
+            "copy_fetch_kib": round(cf, 2), "copy_write_kib": round(cw, 2),
+            "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
+            "bytes_per_launch": int(round((f * sf + wr * sw) * 1024))}
 
 
 def algorithmic_bytes(w, T: int, n_keep: int = 4) -> int:
@@ -108,9 +173,33 @@ def copy_calibration(mib: int, reps: int = 5):
     print(json.dumps({"copy_calibration_mib": mib, "reps": reps}), flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores() -> int:
+    """Threads for the all-core leg: the CPUs this process may run on, at most
+    16 (one GPU's share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(w, data, min_s: float = 10.0):
-    """The oracle's decode step (all query heads, unsplit fp64) timed on this
-    host, single thread, repeated until about `min_s` seconds have passed."""
+    """The oracle's decode step (all query heads, unsplit fp64) on this host:
+    once on one thread, then on every host core (one thread per core, each
+    running whole steps; the oracle is one C call that releases the GIL), each
+    leg repeated until about `min_s` seconds have passed."""
+    import threading
+
     import numpy as np
     import oracle
     T = w.tokens
@@ -118,19 +207,39 @@ def cpu_baseline(w, data, min_s: float = 10.0):
     qz = oracle.quantize(data["k"], data["v"], T, pairs, residual=w.residual,
                          n_pairs_hi=w.n_pairs_hi, bits_hi=w.bits_hi, io_dtype=w.io_dtype)
     q = data["q_dec"][:, :, 0]
-    n, t0 = 0, time.perf_counter()
-    while True:
-        oracle.attention(qz, q, float(np.float32(SM_SCALE)))
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= min_s:
-            break
-    per_step_s = el / n
-    return {"value": round(algorithmic_bytes(w, T) / per_step_s / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": "%d full decode steps of the same workload (all %d query heads, %d "
-                      "tokens), fp64, 1 thread" % (n, w.batch * w.n_q_heads, T),
-            "us_per_step": round(per_step_s * 1e6, 1)}
+    sc = float(np.float32(SM_SCALE))
+
+    def leg(n_threads):
+        counts = [0] * n_threads
+        stop = time.perf_counter() + min_s
+
+        def worker(i):
+            while True:
+                oracle.attention(qz, q, sc)
+                counts[i] += 1
+                if time.perf_counter() >= stop:
+                    break
+        ts = [threading.Thread(target=worker, args=(i,)) for i in range(n_threads)]
+        t0 = time.perf_counter()
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        return sum(counts), time.perf_counter() - t0
+
+    alg = algorithmic_bytes(w, T)
+    n1, el1 = leg(1)
+    cores = host_cores()
+    nc, elc = leg(cores)
+    return {"value": round(alg * nc / elc / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "whole decode steps of the same workload (all %d query heads, %d tokens), "
+                      "fp64: %d steps on %d threads in %.1f s; single thread: %d steps in %.1f s"
+                      % (w.batch * w.n_q_heads, T, nc, cores, elc, n1, el1),
+            "us_per_step": round(elc / nc * 1e6, 1),
+            "single_thread": {"value": round(alg * n1 / el1 / 1e9, 4), "unit": "GB/s",
+                              "us_per_step": round(el1 / n1 * 1e6, 1)},
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def streaming_leg(args, w):
@@ -496,8 +605,13 @@ def prefill_leg(args, w):
 
 STAMP_NAMES = [(0, "entry"), (1, "query in"), (2, "ring blocks done"),
                (11, "first group done"), ("loop", "waves' loop end (last wave)"),
-               (12, "waves merged in LDS"), (13, "records stored"), (14, "ticket back"),
-               (15, "last workgroup: merge done"), (16, "last workgroup: output stored")]
+               (23, "every wave done"), (24, "wave results in LDS"),
+               (12, "waves merged, records issued"), (13, "records stored"),
+               (14, "ticket back"), (18, "last workgroup: records requested"),
+               (19, "last workgroup: split weights formed"),
+               (20, "last workgroup: weighted sum done"),
+               (15, "last workgroup: output issued"), (16, "last workgroup: output stored")]
+LAST_WG_SLOTS = (15, 16, 18, 19, 20)
 
 
 def stamps_leg(args, w):
@@ -558,7 +672,7 @@ def stamps_leg(args, w):
         for slot, name in STAMP_NAMES:
             if slot == "loop":
                 v = rel[:, 3:3 + 8].max(axis=1)
-            elif slot in (15, 16):
+            elif slot in LAST_WG_SLOTS:
                 v = rel[last, slot]
             else:
                 v = rel[:, slot]
@@ -598,7 +712,16 @@ def main():
                     help="phase timestamps of the decode kernel (libkvq_stamps.so)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run the copy-kernel calibration of this size")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="time only kvq_read_ceiling (the decode's reads, no arithmetic)")
+    ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
+                    help="print the traffic record from four rocprofv3 --pmc output "
+                         "directories: decode FETCH_SIZE, decode WRITE_SIZE, copy FETCH_SIZE, "
+                         "copy WRITE_SIZE (the copy of --copy-mib 256)")
     args = ap.parse_args()
+    if args.traffic_from:
+        print("record: " + json.dumps(traffic_record(*args.traffic_from)), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -655,6 +778,29 @@ def main():
     ws = torch.zeros(kvq.kvq_workspace_bytes(layout, S), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+
+    def ceiling_us():
+        """kvq_read_ceiling over the same replicas, steps and splits."""
+        for i in range(args.warmup):
+            kvq.kvq_read_ceiling(layout, replicas[i % n_rep].struct, S, sink, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            kvq.kvq_read_ceiling(layout, replicas[i % n_rep].struct, S, sink, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    if args.ceiling:
+        cus = ceiling_us()
+        cg = algorithmic_bytes(w, T) / (cus * 1e-6) / 1e9
+        print(json.dumps({"ceiling": w.name, "us_per_step": round(cus, 3), "GBs": round(cg, 1),
+                          "frac": round(cg / PEAK_GBS, 4), "n_splits": S, "steps": args.steps,
+                          "cache_replicas": n_rep}), flush=True)
+        return
+
     def step(i):
         if args.prune < 4:
             kvq.kvq_decode_attn_pruned(layout, q, replicas[i % n_rep].struct,
@@ -708,9 +854,16 @@ def main():
         "layout_bytes_per_step": layout_bytes(base, w, T),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4),
-                     "traffic": TRAFFIC if (args.prune == 4 and
-                                            w.name == "llama3-8b-32k") else None},
+                     "traffic": measured_traffic(w.name) if args.prune == 4 else None},
     }
+    if args.prune == 4:
+        cus = ceiling_us()
+        cg = alg / (cus * 1e-6) / 1e9
+        res["ceiling"] = {"us_per_step": round(cus, 3), "GBs": round(cg, 1),
+                          "frac": round(cg / PEAK_GBS, 4),
+                          "decode_over_ceiling": round(ev_ms * 1e3 / cus, 3),
+                          "note": "kvq_read_ceiling: the decode kernel's grid, XCD mapping and "
+                                  "group copies over the same cache replicas, reads only"}
     if args.prune < 4:
         res["note"] = ("query-channel pruning: %d of 4 key chunks kept per KV head; bytes are "
                        "those of the kept chunks" % args.prune)

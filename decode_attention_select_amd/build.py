@@ -27,7 +27,7 @@ FLAGS = [
 
 # (source, extra flags): decode.hip is compiled twice, one half of its kernel
 # variants each, so that the two halves build in parallel
-UNITS = [("api.hip", []), ("select.hip", []), ("quant.hip", []),
+UNITS = [("api.hip", []), ("select.hip", []), ("quant.hip", []), ("ceiling.hip", []),
          ("decode.hip", ["-DKVQ_DECODE_PART=0"]), ("decode.hip", ["-DKVQ_DECODE_PART=1"])]
 
 

@@ -21,6 +21,12 @@ namespace {
 constexpr int MAX_DEVICES = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[MAX_DEVICES] = {};
+// Leading bytes of each device's scratch known to be zero once the work
+// enqueued so far has run: a decode call leaves its split counters (the
+// first 256 B * B * Hkv bytes) at zero and writes its split records right
+// after them, so a later call with more (sequence, KV head) pairs finds
+// records where its extra counters go.
+size_t g_scratch_clean[MAX_DEVICES] = {};
 
 // Zero fill of n 32-bit words (a kernel, not a memset, so that a caller's
 // graph capture records a plain kernel node).
@@ -30,10 +36,12 @@ __global__ void zero_words(uint32_t* p, size_t n) {
     p[i] = 0u;
 }
 
-// The current device's scratch address.  The first call on a device resolves
-// it and enqueues one zero fill on `st` (the split counters must start at
-// zero; every completed decode leaves them at zero again).
-kvq_status scratch_ptr(void** out, hipStream_t st) {
+// The current device's scratch address, for a call whose split counters take
+// the first `tick_bytes` bytes.  The first call on a device resolves it and
+// enqueues one zero fill of the whole array on `st`; a later call whose
+// counters reach past the bytes known to be zero first zero-fills the
+// difference on `st` (the counters must start at zero).
+kvq_status scratch_ptr(void** out, size_t tick_bytes, hipStream_t st) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return KVQ_EHIP;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
@@ -44,8 +52,17 @@ kvq_status scratch_ptr(void** out, hipStream_t st) {
                        (size_t)KVQ_NOALLOC_WORKSPACE_BYTES / 4);
     if (hipGetLastError() != hipSuccess) return KVQ_EHIP;
     g_scratch_ptr[dev] = p;
+    g_scratch_clean[dev] = KVQ_NOALLOC_WORKSPACE_BYTES;
   }
-  *out = g_scratch_ptr[dev];
+  unsigned char* p = (unsigned char*)g_scratch_ptr[dev];
+  if (tick_bytes > g_scratch_clean[dev]) {
+    const size_t c = g_scratch_clean[dev];
+    hipLaunchKernelGGL(zero_words, dim3(64), dim3(256), 0, st, (uint32_t*)(p + c),
+                       (tick_bytes - c) / 4);
+    if (hipGetLastError() != hipSuccess) return KVQ_EHIP;
+  }
+  g_scratch_clean[dev] = tick_bytes;  // records follow the counters from here on
+  *out = p;
   return KVQ_OK;
 }
 
@@ -270,9 +287,22 @@ kvq_status kvq_decode_attn_noalloc(const kvq_layout* L, const void* q, const kvq
   if (kvq_status s = kvq_workspace_bytes(L, n_splits, &need)) return s;
   if (need > (size_t)KVQ_NOALLOC_WORKSPACE_BYTES) return KVQ_ECAPACITY;
   void* ws = nullptr;
-  if (kvq_status s = scratch_ptr(&ws, (hipStream_t)stream)) return s;
+  if (kvq_status s = scratch_ptr(&ws, decode_tick_bytes(L->batch, L->n_kv_heads),
+                                 (hipStream_t)stream))
+    return s;
   return decode_common(L, q, cache, sm_scale, n_splits, 4, ws,
                        (size_t)KVQ_NOALLOC_WORKSPACE_BYTES, out, stream);
+}
+
+kvq_status kvq_read_ceiling(const kvq_layout* L, const kvq_cache* cache, int32_t n_splits,
+                            void* sink, void* stream) {
+  if (kvq_status s = check_layout(L)) return s;
+  const Geo g = make_geo(L);
+  size_t need = 0;
+  if (kvq_status s = kvq_workspace_bytes(L, n_splits, &need)) return s;  // n_splits limits
+  if (kvq_status s = check_ptr(sink)) return s;
+  if (kvq_status s = check_cache(g, cache, true)) return s;
+  return hip_status(launch_ceiling(g, cache, n_splits, sink, (hipStream_t)stream));
 }
 
 kvq_status kvq_check(const kvq_cache* cache, int32_t* host_err, void* stream) {

@@ -50,6 +50,7 @@
 #include "common.h"
 #include "internal.h"
 #include "quant_group.h"
+#include "stream.h"
 
 #ifndef KVQ_DECODE_PART
 #define KVQ_DECODE_PART 1
@@ -67,11 +68,6 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 // 16 bytes at a 4-byte-aligned address (raw salient rows are 2*nh bytes long)
 typedef uint32_t u4a __attribute__((ext_vector_type(4), aligned(4)));
 
-#ifndef KVQ_DECODE_WAVES
-#define KVQ_DECODE_WAVES 8
-#endif
-constexpr int NW = KVQ_DECODE_WAVES;   // waves per workgroup (one workgroup per CU)
-constexpr int WG_THREADS = 64 * NW;
 constexpr int MAXG = 16;
 // log2 headroom before the running max moves: the softmax weights p stay
 // below 2^slack.  The value path forms p * s in fp16, so a group holding a
@@ -89,15 +85,6 @@ __device__ inline uint32_t pk_mul(uint32_t a, uint32_t b) { return h2u(u2h(a) * 
 __device__ inline uint32_t pk_rne(float a, float b) { return h2u(h2{(_Float16)a, (_Float16)b}); }
 __device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Buffer descriptor word 3 for raw byte-addressed buffers (gfx9 family), and
-// the cache-policy bit that makes a buffer access device-coherent (sc1).
-constexpr int BUF_RSRC_WORD3 = 0x00020000;
-constexpr int CPOL_SC1 = 16;
-constexpr int CPOL_SC0 = 1;  // bypasses the CU's L1 only: reads what the XCD's L2 holds
-// non-temporal: the streamed group records go through the L2 with the
-// streaming policy, so that they do not push out what is reused there (the
-// kernel's code, the split records)
-constexpr int CPOL_NT = 2;
 
 // 16-bit input pair -> fp16 pair (bf16 widened exactly, then RNE to fp16)
 template <bool BF16>
@@ -226,103 +213,6 @@ __device__ inline float mirror16(float x) {
 // remainder, so hi + lo = a*b (barring fp16 underflow of the remainder).
 __device__ inline uint32_t pk_fma_lo(uint32_t a, uint32_t b, uint32_t hi) {
   return h2u(__builtin_elementwise_fma(u2h(a), u2h(b), -u2h(hi)));
-}
-
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// s_waitcnt lgkmcnt(0) (LDS and scalar memory), vmcnt and expcnt left alone.
-__device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
-// Keeps the compiler from moving memory accesses across this point (the
-// direct global->LDS copies are invisible to its LDS dependence tracking).
-__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
-
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-// One direct global->LDS copy: every active lane moves the 16 bytes at `src`
-// to LDS address `dst` + 16 * lane (dst uniform).
-template <int CPOL = 0>
-__device__ inline void dma16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, CPOL);
-}
-
-// One LDS slot holds the records of one quantized group, copied from HBM by
-// direct loads (16 bytes per lane and instruction):
-//   KLO  [0, 1024)     k_lo
-//   META [1024, 2048)  k_meta (512) then v_meta (512): [0,64) key scale
-//                      pairs, [64,128) key zero pairs, [128,192) value scale
-//                      pairs (j-major), [192,256) value zero pairs (words)
-//   VC   [2048, 3072)  v_codes
-//   KHI  1024 bytes: k_hi (HIMODE 4 its 128 bytes, HIMODE 16 its 64 nh bytes)
-//   VH   1024 bytes: v_hi words 8 .. 8 + 64 n_vhi (VHI only)
-// Every copy is a whole-wave instruction (NLD per group), so that the
-// compiler counts each one in its own waits: lanes past a short record copy
-// 16 bytes of it again into the slack after it, which nothing reads.  NSLOT
-// slots per wave within the LDS budget.
-constexpr int SLOT_LDS_BUDGET = 147456;
-template <int HIMODE, bool VHI>
-struct SlotCfg {
-  static constexpr int KLO = 0, META = 1024, VC = 2048, KHI = 3072;
-  static constexpr int VH = KHI + (HIMODE != 0 ? 1024 : 0);
-  static constexpr int BYTES = VH + (VHI ? 1024 : 0);
-  static constexpr int NLD = 3 + (HIMODE != 0 ? 1 : 0) + (VHI ? 1 : 0);
-  static constexpr int FIT = SLOT_LDS_BUDGET / (NW * BYTES);
-  static constexpr int NSLOT = FIT < 5 ? FIT : 5;
-  static_assert(NSLOT >= 2, "LDS slots");
-  static_assert((NSLOT - 1) * NLD < 64, "vmcnt range");
-};
-
-// Issues the copies of quantized group `rec` into `slot`.  PRUNE: the lanes
-// of pruned key chunks (k_lo words, key scale/zero) read the kept chunk
-// kept0 instead, lines the same instruction fetches anyway, so the pruned
-// chunks' bytes are not read; what those lanes write is never read.
-template <int HIMODE, bool VHI, bool PRUNE>
-__device__ inline void issue_group(const kvq_cache& c, size_t rec, uint8_t* slot, int lane,
-                                   uint32_t kmask, int kept0, int nh, int nvhi) {
-  using C = SlotCfg<HIMODE, VHI>;
-  // k_lo: lane l holds words 4l .. 4l+3, of key chunk (l / 8) % 4
-  int lk = lane;
-  if (PRUNE && !((kmask >> ((lane >> 3) & 3)) & 1u)) lk = (lane & ~24) | (kept0 << 3);
-  dma16<CPOL_NT>((const uint8_t*)c.k_lo + rec * 1024 + lk * 16, slot + C::KLO);
-  // metadata: lanes 0..31 k_meta (0..15 scales, 16..31 zeros of channels
-  // 8 (l % 16) .. +7, chunk (l % 16) / 4), lanes 32..63 v_meta
-  {
-    int lm = lane;
-    if (PRUNE && lane < 32 && !((kmask >> ((lane & 15) >> 2)) & 1u))
-      lm = (lane & 16) | (kept0 << 2) | (lane & 3);
-    const uint8_t* src = lane < 32 ? (const uint8_t*)c.k_meta + rec * 512 + lm * 16
-                                   : (const uint8_t*)c.v_meta + rec * 512 + (lane - 32) * 16;
-    dma16<CPOL_NT>(src, slot + C::META);
-  }
-  dma16<CPOL_NT>((const uint8_t*)c.v_codes + rec * 1024 + lane * 16, slot + C::VC);
-  if constexpr (HIMODE == 4)  // 128 bytes
-    dma16<CPOL_NT>((const uint8_t*)c.k_hi + rec * 128 + (lane & 7) * 16, slot + C::KHI);
-  if constexpr (HIMODE == 16)  // 32 rows of nh raw salient values: 64 nh bytes (nh >= 2)
-    dma16<CPOL_NT>((const uint8_t*)c.k_hi + rec * 64 * nh + (lane < 4 * nh ? lane : lane & 3) * 16,
-          slot + C::KHI);
-  if constexpr (VHI)  // the high-digit words (after the 8 order words): 256 n_vhi bytes
-    dma16<CPOL_NT>((const uint8_t*)(c.v_hi + rec * (8 + 64 * nvhi) + 8) +
-              (lane < 16 * nvhi ? lane : lane & 15) * 16,
-          slot + C::VH);
-}
-
-// Waits until the copies of the group issued `after` groups before the last
-// one issued have landed (vmcnt counts this wave's vector memory operations
-// in issue order; only the slot copies are outstanding in the group loop).
-template <int NLD, int NSLOT>
-__device__ inline void wait_slot(int after) {
-  static_assert(NSLOT <= 5, "cases");
-  switch (after) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<NLD>(); break;
-    case 2: wait_vmcnt<2 * NLD>(); break;
-    case 3: wait_vmcnt<3 * NLD < 64 ? 3 * NLD : 63>(); break;
-    default: wait_vmcnt<4 * NLD < 64 ? 4 * NLD : 63>(); break;
-  }
-  compiler_fence();
 }
 
 // Workspace of one call (zero-filled once by the caller; counters return to
@@ -1386,6 +1276,8 @@ hipError_t launch_decode_io(const Geo& g, int keep, const Launch& a) {
 template hipError_t launch_decode_io<false>(const Geo&, int, const Launch&);
 #else
 extern template hipError_t launch_decode_io<false>(const Geo&, int, const Launch&);
+
+size_t decode_tick_bytes(int B, int Hkv) { return ws_tick_bytes(B, Hkv); }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int S) {
   size_t n = ws_tick_bytes(B, Hkv) + 2 * (ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S));

@@ -21,5 +21,10 @@ hipError_t launch_decode(const Geo& g, const void* q, const kvq_cache* c, float 
                          hipStream_t st, const void* k_new = nullptr,
                          const void* v_new = nullptr);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_splits);
+// bytes of the split counters at the start of a decode workspace
+size_t decode_tick_bytes(int B, int Hkv);
+// the decode kernel's grid and group stream, reading only (ceiling.hip)
+hipError_t launch_ceiling(const Geo& g, const kvq_cache* c, int n_splits, void* sink,
+                          hipStream_t st);
 
 }  // namespace kvq

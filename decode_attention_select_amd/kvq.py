@@ -181,6 +181,11 @@ def kvq_decode_attn_noalloc(layout, q, cache: kvq_cache, sm_scale, n_splits, out
           ctypes.c_float(sm_scale), ctypes.c_int32(n_splits), _ptr(out), _stream(stream))
 
 
+def kvq_read_ceiling(layout, cache: kvq_cache, n_splits, sink, stream=None):
+    _call("kvq_read_ceiling", ctypes.byref(layout), ctypes.byref(cache),
+          ctypes.c_int32(n_splits), _ptr(sink), _stream(stream))
+
+
 def kvq_check(cache: kvq_cache, stream=None) -> int:
     err = ctypes.c_int32(0)
     _call("kvq_check", ctypes.byref(cache), ctypes.byref(err), _stream(stream))

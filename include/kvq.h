@@ -173,8 +173,11 @@ kvq_status kvq_cache_sizes(const kvq_layout *L, size_t sizes[KVQ_NBUF] /*host*/)
  * device-coherent, the second stays in the L2 of the storing XCD); each part
  * starts on a 256-byte boundary.  The caller zero-fills a workspace once
  * before its first use; every completed call leaves its counters at zero
- * again, so one workspace may serve calls with different split counts and
- * layouts in turn (each needing no more than its size).  One workspace
+ * again and its records right after them, so one workspace may serve calls
+ * with different split counts and layouts in turn (each needing no more
+ * than its size) as long as no call has more (sequence, KV head) pairs than
+ * the call before it on that workspace: more pairs put counters where the
+ * earlier call left records, so zero-fill again first.  One workspace
  * serves one call at a time. */
 kvq_status kvq_workspace_bytes(const kvq_layout *L, int32_t n_splits,
                                size_t *bytes /*host*/);
@@ -281,11 +284,13 @@ kvq_status kvq_shrink(const kvq_layout *L, kvq_cache *cache, int32_t g0,
  * (b, kv head) (limits as for kvq_workspace_bytes), each reduced with an
  * online softmax; a log-sum-exp combine merges them inside the same launch.
  * Computation is fp32 with fp16 matrix operands; the result is rounded to
- * the io dtype (nearest even).  The fp16 operands (each head's query scaled
- * by a power of two so that q * s stays in range, the softmax weights, at
- * most 2) carry a relative 2^-11 per term, so the error grows with the size
- * of the logits: with |q| |k| in the thousands the softmax can move beyond
- * the 2e-3 of ordinary data.  Requires T >= 1 (T = 0 writes zeros); a
+ * the io dtype (nearest even).  Every product of a query channel and a key
+ * scale, and of a softmax weight and a value scale, enters as an exact pair
+ * of fp16 values (the rounded product and its remainder), so no product is
+ * rounded (barring fp16 underflow of a remainder): the roundings left are
+ * the softmax weights' (to fp16; numerator and denominator take the same
+ * rounded weights) and fp32 accumulation, whatever the size of the logits.
+ * Requires T >= 1 (T = 0 writes zeros); a
  * len outside [0, max_tokens] is clamped into it (the result is then
  * unspecified, but every read stays inside the cache).
  *   q   [B][Hq][128] io dtype;  out [B][Hq][128] io dtype
@@ -347,7 +352,9 @@ kvq_status kvq_append_decode_attn(const kvq_layout *L, const void *k_new,
  * static device array of KVQ_NOALLOC_WORKSPACE_BYTES inside the library, one
  * per GPU, held until the process ends.  The first call on a GPU resolves its
  * address and enqueues one zero-fill kernel on `stream`; every completed call
- * leaves its split counters at zero again.  All calls on one GPU share that
+ * leaves its split counters at zero again, and a call with more (sequence,
+ * KV head) pairs than the one before it on that GPU first enqueues a
+ * zero-fill kernel over its extra counters.  All calls on one GPU share that
  * array: calls that overlap on one GPU (different streams, or host threads
  * without ordering) race and give wrong results.  Returns KVQ_ECAPACITY when
  * kvq_workspace_bytes(L, n_splits) exceeds KVQ_NOALLOC_WORKSPACE_BYTES; all
@@ -357,6 +364,20 @@ kvq_status kvq_append_decode_attn(const kvq_layout *L, const void *k_new,
 kvq_status kvq_decode_attn_noalloc(const kvq_layout *L, const void *q,
                                    const kvq_cache *cache, float sm_scale,
                                    int32_t n_splits, void *out, void *stream);
+
+/* Measurement only: the read ceiling of kvq_decode_attn.  One launch of a
+ * kernel with the decode kernel's grid (n_splits workgroups per (b, kv
+ * head)), workgroup-to-XCD mapping, wave work split and group copies that
+ * reads every cache byte a decode step over the same cache reads, in the
+ * same 16-byte-per-lane direct-to-LDS copies, and does no arithmetic on them
+ * (decode cost is the read of the cache: [PN-Mix] and [Dual-QK], abstracts).
+ * Its time bounds from below what any decode with these loads can reach.
+ * Reads cache as kvq_decode_attn does (len, ring, every quantized group of
+ * each (b, kv head)); writes nothing but, for almost no data, one word of
+ * `sink` (>= 4 bytes of device memory, 16-byte aligned).  n_splits limits
+ * and errors as for kvq_decode_attn. */
+kvq_status kvq_read_ceiling(const kvq_layout *L, const kvq_cache *cache,
+                            int32_t n_splits, void *sink, void *stream);
 
 /* Synchronizes `stream`, then copies cache->err to *host_err (tests and
  * debugging only). */

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_entry_point():
                           "kvq_append", "kvq_decode_attn", "kvq_cache_sizes",
                           "kvq_workspace_bytes", "kvq_check", "kvq_status_str", "kvq_shrink",
                           "kvq_select_pairs_qa", "kvq_decode_attn_pruned",
-                          "kvq_append_decode_attn"}
+                          "kvq_append_decode_attn", "kvq_read_ceiling"}
     lib = kvq.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -153,6 +153,11 @@ def test_decode_validation():
     assert fused(v=FAKE + 4) == EALIGN
     assert fused(sm=0.0) == EINVAL
     assert fused(wsb=ws - 1) == ECAPACITY
+    # the read ceiling: its sink and split count
+    ceil = lambda sink=FAKE, S=8: status_of("kvq_read_ceiling", ctypes.byref(L), ctypes.byref(c),
+                                            S, P(sink), P(0))
+    assert ceil(sink=0) == EINVAL and ceil(sink=FAKE + 4) == EALIGN
+    assert ceil(S=0) == EINVAL and ceil(S=1025) == EINVAL
 
 
 @no_gpu

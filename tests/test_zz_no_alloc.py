@@ -1,6 +1,7 @@
 """kvq_decode_attn_noalloc: the decode entry point whose workspace is the
-library's static per-GPU scratch array.  Through the C ABI, on two calls in
-a row (the second with a smaller layout, fewer splits and tokens), its
+library's static per-GPU scratch array.  Through the C ABI, on calls in a
+row (the second with a smaller layout, fewer splits and tokens, the third
+with the first layout again), its
 outputs equal kvq_decode_attn's on a fresh workspace bit for bit (the same
 kernels) and meet the oracle's 2e-3; a layout whose workspace exceeds the
 array is rejected before any launch."""
@@ -33,7 +34,9 @@ def test_noalloc_matches_decode_attn_on_two_calls():
                              outliers="pct2x10", n_pairs_hi=6, residual=128, seed=301)
     small = kvq_synth.Workload("noalloc-small", 1, 4, 1, 230, n_qry=8, io_dtype="fp16",
                                n_pairs_hi=8, residual=32, seed=302)
-    for w, S in ((big, 48), (small, 3)):
+    # big, then smaller, then big again: the third call's extra split
+    # counters sit where the second call left its records
+    for w, S in ((big, 48), (small, 3), (big, 48)):
         print("case", w.name, "S", S, flush=True)
         case = Case(w)
         q = case.d["q_dec"][:, :, 0]
