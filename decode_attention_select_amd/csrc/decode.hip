@@ -742,7 +742,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         for (int i = 0; i < KEEP; i++) {
           const int mm = (cmap >> (2 * i)) & 3u;
           const uint32_t w =
-              ((const uint32_t*)(slot + SC::KLO))[((TT * 4 + mm) * 16 + col) * 2 + (kq >> 1)];
+              ((const uint32_t*)(slot + SC::KLO))[((TT * 4 + mm) * 2 + (kq >> 1)) * 16 + col];
           const uint32_t x = (w >> sh) & 0x33333333u;
           const u4 cd = u4{cvt2<0>(x), cvt2<1>(x), cvt2<2>(x), cvt2<3>(x)};
           acc = mma_f16(cd, u4{qs[4 * i], qs[4 * i + 1], qs[4 * i + 2], qs[4 * i + 3]}, acc);
@@ -750,7 +750,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
             acc = mma_f16(cd, u4{qsl[4 * i], qsl[4 * i + 1], qsl[4 * i + 2], qsl[4 * i + 3]}, acc);
         }
       } else {
-        const u2 w = ((const u2*)(slot + SC::KLO))[(TT * 4 + kqa) * 16 + col];
+        const uint32_t* kw0 = (const uint32_t*)(slot + SC::KLO) + (TT * 4 + kqa) * 32 + col;
+        const u2 w = u2{kw0[0], kw0[16]};  // the two 16-channel runs of chunk kqa
 #pragma unroll
         for (int u = 0; u < 2; u++) {
           const uint32_t A = w[u] & 0x33333333u, Bn = (w[u] >> 2) & 0x33333333u;

@@ -175,8 +175,8 @@ __device__ inline uint32_t shrink_4_to_2(uint32_t x) { return (13u * (x + 2u)) >
 
 constexpr int SHRINK_WAVES = 4;  // groups per workgroup, one per wave
 
-// Lane e < 32 owns the token of tile index e: its eight k_lo words (four
-// 8-byte pairs, u = 0 and 1 adjacent) and its k_hi word are loaded once,
+// Lane e < 32 owns the token of tile index e: its eight k_lo words (one per
+// 16-channel run, kept as four (u = 0, u = 1) pairs) and its k_hi word are loaded once,
 // rewritten in registers and stored once.  The salient channels are walked
 // in ascending order from the salient-pair mask (uniform loop).
 __global__ __launch_bounds__(64 * SHRINK_WAVES) void shrink_kernel(Geo g, kvq_cache c, int g0,
@@ -189,10 +189,11 @@ __global__ __launch_bounds__(64 * SHRINK_WAVES) void shrink_kernel(Geo g, kvq_ca
   const size_t rec = (size_t)bh * g.NG + grp;
   const int e = lane, T = e >> 4, r = e & 15;
   uint32_t* hi = (uint32_t*)c.k_hi + rec * 32;
-  uint2* lo = (uint2*)((uint32_t*)c.k_lo + rec * GROUP_WORDS);
+  uint32_t* lo = (uint32_t*)c.k_lo + rec * GROUP_WORDS;
   uint2 lw[4];
 #pragma unroll
-  for (int kq = 0; kq < 4; kq++) lw[kq] = lo[(T * 4 + kq) * 16 + r];
+  for (int kq = 0; kq < 4; kq++)
+    lw[kq] = make_uint2(lo[((T * 4 + kq) * 2) * 16 + r], lo[((T * 4 + kq) * 2 + 1) * 16 + r]);
   uint32_t hw = hi[e];
   int d = 0;
   for (int side = 0; side < 2; side++) {  // channels j, then j + 64
@@ -218,7 +219,10 @@ __global__ __launch_bounds__(64 * SHRINK_WAVES) void shrink_kernel(Geo g, kvq_ca
     }
   }
 #pragma unroll
-  for (int kq = 0; kq < 4; kq++) lo[(T * 4 + kq) * 16 + r] = lw[kq];
+  for (int kq = 0; kq < 4; kq++) {
+    lo[((T * 4 + kq) * 2) * 16 + r] = lw[kq].x;
+    lo[((T * 4 + kq) * 2 + 1) * 16 + r] = lw[kq].y;
+  }
   hi[e] = hw;
 }
 

@@ -350,7 +350,7 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const int T = i >> 2, r = 4 * tq + (i & 3);
-    ((uint16_t*)L.lo)[(((T * 4 + kq) * 16 + r) * 2 + u) * 2 + half] = (uint16_t)hw[i];
+    ((uint16_t*)L.lo)[(((T * 4 + kq) * 2 + u) * 16 + r) * 2 + half] = (uint16_t)hw[i];
     if (bits4 && hh[i]) atomicOr(&L.hi[16 * T + r], hh[i]);
   }
   if (raw16) {

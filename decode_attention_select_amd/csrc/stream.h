@@ -79,7 +79,8 @@ template <int HIMODE, bool VHI, bool PRUNE>
 __device__ inline void issue_group(const kvq_cache& c, size_t rec, uint8_t* slot, int lane,
                                    uint32_t kmask, int kept0, int nh, int nvhi) {
   using C = SlotCfg<HIMODE, VHI>;
-  // k_lo: lane l holds words 4l .. 4l+3, of key chunk (l / 8) % 4
+  // k_lo: lane l holds words 4l .. 4l+3: tokens 4 (l % 4) .. +3 of the 16-channel
+  // run u = (l / 4) % 2 of key chunk (l / 8) % 4, tile half l / 32
   int lk = lane;
   if (PRUNE && !((kmask >> ((lane >> 3) & 3)) & 1u)) lk = (lane & ~24) | (kept0 << 3);
   dma16<CPOL_NT>((const uint8_t*)c.k_lo + rec * 1024 + lk * 16, slot + C::KLO);

@@ -102,9 +102,10 @@ typedef struct {
  * A 2-bit code at position p occupies bits [2p, 2p+2) of a little-endian
  * 32-bit word (of a 16-bit half-word for v_codes).
  *
- *  k_lo    [B][Hkv][NG][256] u32: word ((T*4 + kq)*16 + r)*2 + u holds,
+ *  k_lo    [B][Hkv][NG][256] u32: word ((T*4 + kq)*2 + u)*16 + r holds,
  *          for the token at tile index 16T + r, channels 16w .. 16w+15 with
- *          w = 2kq + u, channel 16w + c at position pi(c).  The stored digit
+ *          w = 2kq + u, channel 16w + c at position pi(c) (so each 16-channel
+ *          run of 16 tokens is 64 contiguous bytes).  The stored digit
  *          is the 2-bit code of a 2-bit channel, the code (0 or 1) of a
  *          1-bit channel, the low two bits of the code of a 4-bit channel,
  *          and 0 for a 16-bit channel.

@@ -77,7 +77,7 @@ def unpack_keys(k_lo, k_hi, k_meta, salient: list[int], bits_hi: int):
         for c in range(D):
             w = c // 16
             kq, u = divmod(w, 2)
-            word = k_lo[((T * 4 + kq) * 16 + r) * 2 + u]
+            word = k_lo[((T * 4 + kq) * 2 + u) * 16 + r]
             codes[c, t] = _code(word, _pos(c % 16))
     raw = None
     if salient and bits_hi == 4:

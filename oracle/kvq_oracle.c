@@ -552,7 +552,7 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
             int w = c / 16, kq = w / 2, u = w % 2;
             int bits = orc_channel_bits(pr, n_hi, bits_hi, n_lo1, 2, c);
             uint32_t digit = bits == 16 ? 0u : (uint32_t)(cg[c * GS + t] & 3);
-            size_t word = ((size_t)(Tt * 4 + kq) * 16 + r) * 2 + u;
+            size_t word = ((size_t)(Tt * 4 + kq) * 2 + u) * 16 + r;
             lo[word] |= digit << (2 * pos_swap(c % 16));
           }
         }

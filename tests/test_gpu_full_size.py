@@ -8,7 +8,9 @@ configuration the benchmark times:
   cache byte; outputs of two sampled KV heads (16 query heads) against the
   oracle, which computes those heads alone;
 * the streaming layer (B16, prefill 4096): 40 appends, which pack one group
-  per sequence and head, then every cache byte and every output element.
+  per sequence and head, then every cache byte and every output element;
+* the bit-allocation sweep's layer (B4 x 16K) at each of its four key
+  precisions: every cache byte and every output element.
 
 Bars as in the small-case tests: bit-exact indices, sums, codes, scales,
 zero points and ring bytes; attention within 2e-3, the 16-bit output's own
@@ -89,6 +91,31 @@ def test_llama3_8b_32k_large_logits(qscale):
     e32 = check_single_split(part, ref, ATOL)
     print("%s queries x%d: max|logit| %.1f max|err| %.3g max|o| %.3g split-record max|err| %.3g"
           % (w.name, qscale, max_logit, err, np.abs(ref).max(), e32))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("point", kvq_synth.PARETO_POINTS, ids=[p[0] for p in kvq_synth.PARETO_POINTS])
+def test_pareto_b4_16k_every_bit_point(point):
+    # the bit-allocation sweep's layer (B4 x 16K, 32 q / 8 kv heads, bf16) at
+    # each key precision it sweeps: 1.5 (half the pairs at 1 bit), 2.0, 2.26
+    # (6 salient pairs at 4 bits), 3.0 (6 salient pairs at 16 bits); every
+    # cache byte and every output element, at the benchmark's split count
+    label, n_hi, bits_hi, n_lo1 = point
+    w = kvq_synth.workload("pareto-b4-16k").replace(n_pairs_hi=n_hi, bits_hi=bits_hi,
+                                                    n_pairs_lo1=n_lo1)
+    print("case", w.name, "bits", label, flush=True)
+    case = Case(w)
+    pairs = check_selection(case)
+    qz = case.oracle_quant(pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
+    q = case.d["q_dec"][:, :, 0]
+    ref = oracle.attention(qz, q, SM_SCALE)
+    S = bench.default_splits(w)
+    err = check_output(case.decode(q, S), ref, w.io_dtype, ATOL)
+    _, part = case.decode(q, 1, partials=True)
+    e32 = check_single_split(part, ref, ATOL)
+    print("%s %s bits S=%d max|err| %.3g split-record max|err| %.3g"
+          % (w.name, label, S, err, e32))
 
 
 @pytest.mark.timeout(600)
