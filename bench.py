@@ -99,11 +99,11 @@ def traffic_record(dec_fetch, dec_write, copy_fetch, copy_write, copy_mib=256):
             "bytes_per_launch": int(round((f * sf + wr * sw) * 1024))}
 
 
-def algorithmic_bytes(w, T: int, n_keep: int = 4) -> int:
-    """Bytes a decode step must move.  With n_keep < 4 (query-channel
-    pruning, 2-bit / 4-bit-salient layouts) only the kept chunks' low key
-    digits, key scale/zero and ring keys count; the salient high digits are
-    one word per token and are read whole."""
+def algorithmic_bytes(w, T: int, n_keep: int = 8) -> int:
+    """Bytes a decode step must move.  With n_keep < 8 (query-channel
+    pruning, 2-bit / 4-bit-salient layouts) only the kept 16-channel runs'
+    low key digits, key scale/zero and ring keys count; the salient high
+    digits are one word per token and are read whole."""
     R = w.residual
     nq = 32 * (max(0, T - R) // 32)
     nr = T - nq
@@ -111,10 +111,10 @@ def algorithmic_bytes(w, T: int, n_keep: int = 4) -> int:
     n_two_ch = 128 - n_hi_ch - n_one_ch
     bh = w.batch * w.n_kv_heads
     qo = 2 * w.batch * w.n_q_heads * 128 * 2
-    if n_keep < 4:
+    if n_keep < 8:
         assert w.bits_hi == 4 and w.n_pairs_lo1 == 0
-        per_tok = (2 * 32 * n_keep + 2 * n_hi_ch) / 8 + 4 * n_keep + 32 + 16
-        return int(round(bh * (nq * per_tok + nr * (64 * n_keep + 256)) + qo))
+        per_tok = (2 * 16 * n_keep + 2 * n_hi_ch) / 8 + 2 * n_keep + 32 + 16
+        return int(round(bh * (nq * per_tok + nr * (32 * n_keep + 256)) + qo))
     if w.bits_hi == 16:
         k_code_bits = n_hi_ch * 16 + n_two_ch * 2 + n_one_ch
         k_meta = (128 - n_hi_ch) * 4 / 32
@@ -700,9 +700,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--replica-mib", type=int, default=512)
-    ap.add_argument("--prune", type=int, default=4,
-                    help="kvq_decode_attn_pruned with this many of the four 32-channel key "
-                         "chunks kept (4: kvq_decode_attn)")
+    ap.add_argument("--prune", type=int, default=8,
+                    help="kvq_decode_attn_pruned with this many of the eight 16-channel key "
+                         "runs kept (8: kvq_decode_attn)")
     ap.add_argument("--build", action="store_true",
                     help="time the cache-building calls on the workload instead of decode")
     ap.add_argument("--value-hi", default="",
@@ -802,7 +802,7 @@ def main():
         return
 
     def step(i):
-        if args.prune < 4:
+        if args.prune < 8:
             kvq.kvq_decode_attn_pruned(layout, q, replicas[i % n_rep].struct,
                                        float(np.float32(SM_SCALE)), S, args.prune, ws, out,
                                        stream=stream)
@@ -849,14 +849,14 @@ def main():
                    "kv_heads": w.n_kv_heads, "context": T, "io_dtype": w.io_dtype,
                    "salient_pairs": w.n_pairs_hi, "salient_bits": w.bits_hi,
                    "residual": w.residual, "n_splits": S, "cache_replicas": n_rep,
-                   **({"kept_key_chunks": args.prune} if args.prune < 4 else {})},
+                   **({"kept_key_runs": args.prune} if args.prune < 8 else {})},
         "algorithmic_bytes_per_step": alg,
         "layout_bytes_per_step": layout_bytes(base, w, T),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name) if args.prune == 4 else None},
+                     "traffic": measured_traffic(w.name) if args.prune == 8 else None},
     }
-    if args.prune == 4:
+    if args.prune == 8:
         cus = ceiling_us()
         cg = alg / (cus * 1e-6) / 1e9
         res["ceiling"] = {"us_per_step": round(cus, 3), "GBs": round(cg, 1),
@@ -864,10 +864,10 @@ def main():
                           "decode_over_ceiling": round(ev_ms * 1e3 / cus, 3),
                           "note": "kvq_read_ceiling: the decode kernel's grid, XCD mapping and "
                                   "group copies over the same cache replicas, reads only"}
-    if args.prune < 4:
-        res["note"] = ("query-channel pruning: %d of 4 key chunks kept per KV head; bytes are "
-                       "those of the kept chunks" % args.prune)
-    if not args.no_cpu_baseline and args.prune == 4:
+    if args.prune < 8:
+        res["note"] = ("query-channel pruning: %d of 8 16-channel key runs kept per KV head; "
+                       "bytes are those of the kept runs" % args.prune)
+    if not args.no_cpu_baseline and args.prune == 8:
         res["cpu_baseline"] = cpu_baseline(w, data)
     print(json.dumps(res), flush=True)
 

@@ -235,7 +235,8 @@ kvq_status kvq_shrink(const kvq_layout* L, kvq_cache* cache, int32_t g0, int32_t
   return hip_status(launch_shrink(g, cache, g0, g1, (hipStream_t)stream));
 }
 
-// keep 1..4: kept key chunks; 0: append k_new / v_new and decode in one launch
+// keep 1..8: kept 16-channel key runs (8: all); 0: append k_new / v_new and
+// decode in one launch
 static kvq_status decode_common(const kvq_layout* L, const void* q, const kvq_cache* cache,
                                 float sm_scale, int32_t n_splits, int32_t keep, void* workspace,
                                 size_t ws_bytes, void* out, void* stream,
@@ -246,7 +247,7 @@ static kvq_status decode_common(const kvq_layout* L, const void* q, const kvq_ca
   if (kvq_status s = kvq_workspace_bytes(L, n_splits, &need)) return s;
   if (ws_bytes < need) return KVQ_ECAPACITY;
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_EINVAL;
-  if (keep < 0 || keep > 4) return KVQ_EINVAL;
+  if (keep < 0 || keep > 8) return KVQ_EINVAL;
   if (kvq_status s = check_ptr(q)) return s;
   if (kvq_status s = check_ptr(out)) return s;
   if (kvq_status s = check_ptr(workspace)) return s;
@@ -262,7 +263,7 @@ static kvq_status decode_common(const kvq_layout* L, const void* q, const kvq_ca
 kvq_status kvq_decode_attn(const kvq_layout* L, const void* q, const kvq_cache* cache,
                            float sm_scale, int32_t n_splits, void* workspace, size_t ws_bytes,
                            void* out, void* stream) {
-  return decode_common(L, q, cache, sm_scale, n_splits, 4, workspace, ws_bytes, out, stream);
+  return decode_common(L, q, cache, sm_scale, n_splits, 8, workspace, ws_bytes, out, stream);
 }
 
 kvq_status kvq_decode_attn_pruned(const kvq_layout* L, const void* q, const kvq_cache* cache,
@@ -290,7 +291,7 @@ kvq_status kvq_decode_attn_noalloc(const kvq_layout* L, const void* q, const kvq
   if (kvq_status s = scratch_ptr(&ws, decode_tick_bytes(L->batch, L->n_kv_heads),
                                  (hipStream_t)stream))
     return s;
-  return decode_common(L, q, cache, sm_scale, n_splits, 4, ws,
+  return decode_common(L, q, cache, sm_scale, n_splits, 8, ws,
                        (size_t)KVQ_NOALLOC_WORKSPACE_BYTES, out, stream);
 }
 

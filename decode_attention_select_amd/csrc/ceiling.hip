@@ -41,7 +41,7 @@ __global__ __launch_bounds__(WG_THREADS) void ceiling_kernel(Geo g, kvq_cache c,
 #pragma unroll
       for (int i = 0; i < NSLOT; i++)
         issue_group<HIMODE, VHI, false>(c, rec0 + (size_t)min(gfirst + i * STR, g.NG - 1),
-                                        sl + i * SLOTB, lane, 0xFu, 0, g.nh, g.n_vhi);
+                                        sl + i * SLOTB, lane, 0xFFu, 0, g.nh, g.n_vhi);
     }
   };
   if (!ring_owner) issue_first();
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(WG_THREADS) void ceiling_kernel(Geo g, kvq_cache c,
     if (issued < nmine) {
       wait_lgkmcnt0();  // the slot's read is done before its refill lands
       compiler_fence();
-      issue_group<HIMODE, VHI, false>(c, rec0 + gfirst + (size_t)issued * STR, slot, lane, 0xFu,
+      issue_group<HIMODE, VHI, false>(c, rec0 + gfirst + (size_t)issued * STR, slot, lane, 0xFFu,
                                       0, g.nh, g.n_vhi);
       issued++;
     }

@@ -322,13 +322,14 @@ struct Lds {
 
 // HASQ: the cache has quantized-group storage (capacity NG >= 1); without it
 // no group address exists and the group stream is compiled out.
-// KEEP < 4: query-channel pruning (Dual-QK, abstract: a decode query keeps
-// its few large channels and the key cache is read only for them).  Per
-// (sequence, KV head) the KEEP 32-channel key chunks of largest
-// sum over the group's heads of min(floor(4096 |q_c|), 2^20) are kept (ties to the
-// lower chunk); the query is zero on the others, whose key codes and
-// scale/zero are not copied (past the first slots, which are issued before
-// the query arrives).
+// KB > 0: query-channel pruning (Dual-QK, abstract: a decode query keeps its
+// few large channels and the key cache is read only for them).  Per
+// (sequence, KV head) the nkeep (1..7) 16-channel key runs of largest sum
+// over the group's heads of min(floor(4096 |q_c|), 2^20) are kept (ties to
+// the lower run); the query is zero on the others, whose key codes and
+// scale/zero are not copied: a pruning wave issues its first copies only
+// once the query has arrived and the runs are chosen.  The kept runs pair
+// up into the MFMAs' 32-long contractions, KB = ceil(nkeep / 2) per tile.
 // VHI: the cache has two value precisions (g.n_vhi > 0): the first n_vhi
 // 8-slot blocks of each group (its tokens of largest key magnitude) add their
 // high value digits (4 * digit) through more MFMAs per tile.
@@ -346,13 +347,14 @@ struct Lds {
 // 15 - h; lane (col, kq) serves head col (col < G) or 15 - col (col >= 16 -
 // G).  Logits and outputs add the two columns (a row_mirror DPP).  Without
 // it (G > 8, every column taken) hi and lo take an MFMA each.
-template <bool BF16, int HIMODE, bool HASQ, int KEEP, bool VHI, bool FUSED, bool LOCOL>
+template <bool BF16, int HIMODE, bool HASQ, int KB, bool VHI, bool FUSED, bool LOCOL>
 __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             kvq_cache c, float scale_log2, int S,
                                                             Ws ws, uint16_t* __restrict__ out,
                                                             const uint16_t* __restrict__ knew,
-                                                            const uint16_t* __restrict__ vnew) {
-  constexpr bool PRUNE = KEEP < 4;
+                                                            const uint16_t* __restrict__ vnew,
+                                                            int nkeep) {
+  constexpr bool PRUNE = KB > 0;
   using SC = SlotCfg<HIMODE, VHI>;
   constexpr int NSLOT = SC::NSLOT, NLD = SC::NLD, SLOTB = SC::BYTES;
   __shared__ Lds<SLOTB, NSLOT> lds;
@@ -408,12 +410,16 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int gfirst = f - RSB + (ring_owner ? (RSB - f + STR - 1) / STR * STR : 0);
   uint8_t* slots = &lds.u.slots[wave][0][0];
   int issued = 0;
+  // kept 16-channel key runs (bit s: run s; all eight unless PRUNE) and the
+  // first of them; PRUNE sets them once the query has arrived
+  uint32_t kmask = 0xFFu;
+  int kept0 = 0;
   auto issue_first = [&]() {
     if constexpr (HASQ) {
 #pragma unroll
       for (int i = 0; i < NSLOT; i++)
-        issue_group<HIMODE, VHI, false>(c, rec0 + (size_t)min(gfirst + i * STR, g.NG - 1),
-                                        slots + i * SLOTB, lane, 0xFu, 0, g.nh, g.n_vhi);
+        issue_group<HIMODE, VHI, PRUNE>(c, rec0 + (size_t)min(gfirst + i * STR, g.NG - 1),
+                                        slots + i * SLOTB, lane, kmask, kept0, g.nh, g.n_vhi);
       issued = NSLOT;
     }
   };
@@ -443,6 +449,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       for (int tt = 0; tt < 8; tt++) vnk[tt] = vnew[(size_t)bh * D + 16 * tt + col];
     }
     wait_vmcnt<0>();
+  } else if constexpr (PRUNE) {
+    wait_vmcnt<0>();  // the query; the group copies wait for the kept runs
   } else {
     issue_first();
     wait_vmcnt<HASQ ? NSLOT * NLD : 0>();  // the query copies (issued before the group copies)
@@ -453,56 +461,59 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
   for (int i = 0; i < 4; i++) qv[i] = *(const u4*)&lds.qin[hq][32 * kq + 8 * i];
 
-  // kept key chunks (all four unless PRUNE), a wave-uniform mask: E_m sums
-  // min(floor(4096 |q|), 2^20) over chunk m's 32 channels and the G heads
-  // (at most 2^29, exact in 32 bits); the 16 lanes of chunk kq are DPP row kq
-  uint32_t kmask = 0xFu;
+  // kept key runs (PRUNE), a wave-uniform mask: E_s sums min(floor(4096 |q|),
+  // 2^20) over run s's 16 channels and the G heads (at most 2^28, exact in 32
+  // bits); lane (col, kq) holds runs 2kq (qv[0..1]) and 2kq + 1 (qv[2..3]),
+  // and the 16 lanes of row kq are DPP row kq
+  uint32_t cmap = 0;  // kept runs in ascending order, three bits each
   if constexpr (PRUNE) {
-    uint32_t e = 0;
+    uint32_t e[2] = {0, 0};
     if (hvalid) {
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int w = 0; w < 4; w++) {
           const uint32_t x = qv[i][w];  // 4096 |q| is exact; the conversion truncates
-          e += (uint32_t)fminf(4096.0f * fabsf(in_to_f32((uint16_t)(x & 0xFFFF), BF16)),
-                               1048576.0f);
-          e += (uint32_t)fminf(4096.0f * fabsf(in_to_f32((uint16_t)(x >> 16), BF16)), 1048576.0f);
+          e[i >> 1] += (uint32_t)fminf(4096.0f * fabsf(in_to_f32((uint16_t)(x & 0xFFFF), BF16)),
+                                       1048576.0f);
+          e[i >> 1] += (uint32_t)fminf(4096.0f * fabsf(in_to_f32((uint16_t)(x >> 16), BF16)),
+                                       1048576.0f);
         }
     }
-    e += (uint32_t)__builtin_amdgcn_update_dpp((int)e, (int)e, 0x128, 0xF, 0xF, false);  // row_ror:8
-    e += (uint32_t)__builtin_amdgcn_update_dpp((int)e, (int)e, 0x124, 0xF, 0xF, false);  // row_ror:4
-    e += (uint32_t)__builtin_amdgcn_update_dpp((int)e, (int)e, 0x122, 0xF, 0xF, false);  // row_ror:2
-    e += (uint32_t)__builtin_amdgcn_update_dpp((int)e, (int)e, 0x121, 0xF, 0xF, false);  // row_ror:1
-    uint32_t E[4];
+    uint32_t E[8];
 #pragma unroll
-    for (int m = 0; m < 4; m++) E[m] = (uint32_t)__builtin_amdgcn_readlane((int)e, 16 * m);
+    for (int h = 0; h < 2; h++) {
+      uint32_t x = e[h];
+      x += (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
+      x += (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x124, 0xF, 0xF, false);  // row_ror:4
+      x += (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x122, 0xF, 0xF, false);  // row_ror:2
+      x += (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x121, 0xF, 0xF, false);  // row_ror:1
+#pragma unroll
+      for (int m = 0; m < 4; m++) E[2 * m + h] = (uint32_t)__builtin_amdgcn_readlane((int)x, 16 * m);
+    }
     kmask = 0;
 #pragma unroll
-    for (int m = 0; m < 4; m++) {
+    for (int r = 0; r < 8; r++) {
       int rank = 0;
 #pragma unroll
-      for (int i = 0; i < 4; i++) rank += (E[i] > E[m]) || (E[i] == E[m] && i < m);
-      if (rank < KEEP) kmask |= 1u << m;
+      for (int i = 0; i < 8; i++) rank += (E[i] > E[r]) || (E[i] == E[r] && i < r);
+      if (rank < nkeep) kmask |= 1u << r;
     }
-    if (!((kmask >> kq) & 1u)) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) qv[i] = u4{0, 0, 0, 0};
-    }
-  }
-  const int kept0 = __builtin_ctz(kmask);
-  const int kqa = ((kmask >> kq) & 1u) ? kq : kept0;
-  // kept chunks in ascending order, two bits each (uniform)
-  uint32_t cmap = 0;
-  {
+    kmask = __builtin_amdgcn_readfirstlane(kmask);
+    kept0 = __builtin_ctz(kmask);
     int n = 0;
 #pragma unroll
-    for (int m = 0; m < 4; m++)
-      if ((kmask >> m) & 1u) {
-        cmap |= (uint32_t)m << (2 * n);
+    for (int r = 0; r < 8; r++)
+      if ((kmask >> r) & 1u) {
+        cmap |= (uint32_t)r << (3 * n);
         n++;
       }
+    if (!ring_owner) issue_first();  // only the kept runs' codes and scale/zero
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+      if (!((kmask >> (2 * kq + h)) & 1u)) qv[2 * h] = qv[2 * h + 1] = u4{0, 0, 0, 0};
   }
+  const int kqa = kq;
 
   // The quantized path multiplies q by key scales in fp16 (q*s, 4*q*s), so
   // each head's query is first scaled by a power of two 2^-qe that puts its
@@ -614,24 +625,28 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     sal_ch = lds.hil[lane & 15] & (D - 1);
   }
 
-  // PRUNE: each MFMA's 32-long contraction covers one key chunk m.  Lane
-  // (col, kq) feeds the pairs 16m + 8(kq/2) + 2b + (kq%2), b = 0..3, of
-  // chunk m: the codes of one nibble plane (kq%2) of k_lo word kq/2, in
-  // byte order.  qk[i] holds head col's fp16 query at those pairs of the
-  // i-th kept chunk.
-  const int pb = 8 * (kq >> 1) + (kq & 1);
-  uint32_t qk[4][4];
+  // PRUNE: the i-th MFMA contraction of a tile (i < ceil(nkeep / 2)) covers
+  // the kept runs 2i (K-lanes of kq 0, 1) and 2i + 1 (kq 2, 3).  Lane (col,
+  // kq) feeds the pairs 8 r + 4 (kq%2) + b, b = 0..3, of its run r (channels
+  // 16 r ..): the low (kq%2 = 0) or high half of run r's k_lo word, as the
+  // unpruned path takes a word's halves.  qk[i] holds head col's fp16 query
+  // at those pairs; it is zero where the run is past the kept ones (odd
+  // nkeep).
+  const int khalf = kq & 1;
+  int krun[4];
+  u4 qk[4];
   if constexpr (PRUNE) {
     if constexpr (HIMODE == 0) {
       __builtin_amdgcn_wave_barrier();
       compiler_fence();
     }
 #pragma unroll
-    for (int i = 0; i < KEEP; i++) {
-      const int mm = (cmap >> (2 * i)) & 3u;
-#pragma unroll
-      for (int bb = 0; bb < 4; bb++)
-        qk[i][bb] = qvalid ? *(const uint32_t*)&lds.q16[hq][2 * (16 * mm + pb + 2 * bb)] : 0u;
+    for (int i = 0; i < 4; i++) {
+      if (i >= KB) break;
+      const int n = 2 * i + (kq >> 1);
+      krun[i] = (cmap >> (3 * n)) & 7u;
+      const bool live = qvalid && n < nkeep;
+      qk[i] = live ? *(const u4*)&lds.q16[hq][16 * krun[i] + 8 * khalf] : u4{0, 0, 0, 0};
     }
   }
 
@@ -673,15 +688,15 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     uint32_t qs[16], qsl[16];
     f4 cb = {0, 0, 0, 0};
     if constexpr (PRUNE) {
-      // kept chunk i's q*s pairs into qs[4i..4i+3]; pruned chunks take no work
+      // contraction i's q*s pairs into qs[4i..4i+3]; pruned runs take no work
 #pragma unroll
-      for (int i = 0; i < KEEP; i++) {
-        const int mm = (cmap >> (2 * i)) & 3u;
-        uint32_t zp[4];
+      for (int i = 0; i < 4; i++) {
+        if (i >= KB) break;
+        const int pb = 8 * krun[i] + 4 * khalf;
+        const u4 spv = *(const u4*)(sm + pb), zp = *(const u4*)(sm + 64 + pb);
 #pragma unroll
         for (int bb = 0; bb < 4; bb++) {
-          const uint32_t sp = sm[16 * mm + pb + 2 * bb];
-          zp[bb] = sm[64 + 16 * mm + pb + 2 * bb];
+          const uint32_t sp = spv[bb];
           if constexpr (LOCOL) {
             qs[4 * i + bb] = pk_fma_lo(qk[i][bb], sp, pk_mul(lo_lane ? qk[i][bb] : 0u, sp));
           } else {
@@ -737,14 +752,15 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     for (int TT = 0; TT < 2; TT++) {
       f4 acc = cb;
       if constexpr (PRUNE) {
-        const int sh = 2 * (kq & 1);
+        const int sh = 16 * khalf;
 #pragma unroll
-        for (int i = 0; i < KEEP; i++) {
-          const int mm = (cmap >> (2 * i)) & 3u;
+        for (int i = 0; i < 4; i++) {
+          if (i >= KB) break;
+          // the lane's half of run krun[i]'s word: pairs 4 khalf .. +3
           const uint32_t w =
-              ((const uint32_t*)(slot + SC::KLO))[((TT * 4 + mm) * 2 + (kq >> 1)) * 16 + col];
-          const uint32_t x = (w >> sh) & 0x33333333u;
-          const u4 cd = u4{cvt2<0>(x), cvt2<1>(x), cvt2<2>(x), cvt2<3>(x)};
+              ((const uint32_t*)(slot + SC::KLO))[(TT * 8 + krun[i]) * 16 + col] >> sh;
+          const uint32_t A = w & 0x33333333u, Bn = (w >> 2) & 0x33333333u;
+          const u4 cd = u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)};
           acc = mma_f16(cd, u4{qs[4 * i], qs[4 * i + 1], qs[4 * i + 2], qs[4 * i + 3]}, acc);
           if constexpr (!LOCOL)
             acc = mma_f16(cd, u4{qsl[4 * i], qsl[4 * i + 1], qsl[4 * i + 2], qsl[4 * i + 3]}, acc);
@@ -1103,7 +1119,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // The last workgroup merges all splits.  Thread (chunk q, subset r): the
   // 4 channels 4 (q % 32) .. of head q / 32, over splits r, r + NR, ...; the
   // NR threads of a chunk are adjacent lanes and add up with shuffles.  The
-  // (m, l) of the first 64 splits and the records of up to 2 KB splits per
+  // (m, l) of the first 64 splits and the records of up to 2 RB splits per
   // thread are requested at once, in that order; meanwhile each head's
   // weights w_i = 2^(m_i - M) l_i (M the largest running max) and 1 / L,
   // L = sum w_i, are formed (one wave per head, lanes over splits).
@@ -1113,7 +1129,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int qc = tid / NR, r = tid % NR;
   const bool act = qc < NQ;
   const int h = act ? qc / (D / 4) : 0, c4 = act ? 4 * (qc % (D / 4)) : 0;
-  constexpr int KB = 8;
+  constexpr int RB = 8;
   const int nk = (S - r + NR - 1) / NR;  // this thread's splits
   const int nkmax = (S + NR - 1) / NR;   // the most any thread has
   const __amdgpu_buffer_rsrc_t rs_mlL =
@@ -1126,18 +1142,18 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     return __hip_atomic_load((const uint64_t*)&ws.ml[rbh + (size_t)i * G + hh], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   };
-  auto load_batch = [&](u4 (&ov)[KB], int k0) {
+  auto load_batch = [&](u4 (&ov)[RB], int k0) {
 #pragma unroll
-    for (int k = 0; k < KB; k++) {
+    for (int k = 0; k < RB; k++) {
       const int ooff = ((min(r + (k0 + k) * NR, S - 1) * G + h) * D + c4) * 4;  // past S: unused
       ov[k] = local ? __builtin_amdgcn_raw_buffer_load_b128(rs_oL, ooff, 0, CPOL_SC0)
                     : __builtin_amdgcn_raw_buffer_load_b128(rs_o, ooff, 0, CPOL_SC1);
     }
   };
   const uint64_t ml0 = wave < G ? load_ml(min(lane, S - 1), wave) : 0ull;
-  u4 ova[KB], ovb[KB];
+  u4 ova[RB], ovb[RB];
   load_batch(ova, 0);
-  if (nkmax > KB) load_batch(ovb, KB);
+  if (nkmax > RB) load_batch(ovb, RB);
   KVQ_STAMP(tid == 0, 18);
   for (int hh = wave; hh < G; hh += NW) {
     float M = -INFINITY;
@@ -1161,15 +1177,15 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   __syncthreads();
   KVQ_STAMP(tid == 0, 19);
   f4 acc = {0, 0, 0, 0};
-  auto accum = [&](const u4 (&ov)[KB], int k0) {
+  auto accum = [&](const u4 (&ov)[RB], int k0) {
 #pragma unroll
-    for (int k = 0; k < KB; k++)
+    for (int k = 0; k < RB; k++)
       if (k0 + k < nk)
         acc += lds.u.fin.ml[(r + (k0 + k) * NR) * MAXG + h][0] * __builtin_bit_cast(f4, ov[k]);
   };
   accum(ova, 0);
-  if (nkmax > KB) accum(ovb, KB);
-  for (int k0 = 2 * KB; k0 < nkmax; k0 += KB) {
+  if (nkmax > RB) accum(ovb, RB);
+  for (int k0 = 2 * RB; k0 < nkmax; k0 += RB) {
     load_batch(ova, k0);
     accum(ova, k0);
   }
@@ -1222,34 +1238,36 @@ struct Launch {
   hipStream_t st;
 };
 
-template <bool BF16, int HIMODE, int KEEP, bool VHI, bool FUSED, bool LOCOL>
-static void launch_cols(const Geo& g, const Launch& a) {
+template <bool BF16, int HIMODE, int KB, bool VHI, bool FUSED, bool LOCOL>
+static void launch_cols(const Geo& g, int keep, const Launch& a) {
   const dim3 grid(g.B * g.Hkv * a.S), block(WG_THREADS);
   if (g.NG > 0)
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, KEEP, VHI, FUSED, LOCOL>), grid, block,
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, KB, VHI, FUSED, LOCOL>), grid, block,
                        0, a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,
-                       (uint16_t*)a.out, (const uint16_t*)a.knew, (const uint16_t*)a.vnew);
+                       (uint16_t*)a.out, (const uint16_t*)a.knew, (const uint16_t*)a.vnew, keep);
   else
-    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, KEEP, false, FUSED, LOCOL>), grid,
+    hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, false, KB, false, FUSED, LOCOL>), grid,
                        block, 0, a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,
-                       (uint16_t*)a.out, (const uint16_t*)a.knew, (const uint16_t*)a.vnew);
+                       (uint16_t*)a.out, (const uint16_t*)a.knew, (const uint16_t*)a.vnew, keep);
 }
 
-template <bool BF16, int HIMODE, int KEEP, bool VHI, bool FUSED>
-static void launch_one(const Geo& g, const Launch& a) {
-  if (g.G <= 8) launch_cols<BF16, HIMODE, KEEP, VHI, FUSED, true>(g, a);
-  else launch_cols<BF16, HIMODE, KEEP, VHI, FUSED, false>(g, a);
+template <bool BF16, int HIMODE, int KB, bool VHI, bool FUSED>
+static void launch_one(const Geo& g, int keep, const Launch& a) {
+  if (g.G <= 8) launch_cols<BF16, HIMODE, KB, VHI, FUSED, true>(g, keep, a);
+  else launch_cols<BF16, HIMODE, KB, VHI, FUSED, false>(g, keep, a);
 }
 
-// keep 0: the fused append-and-decode call (all four key chunks)
+// keep 0: the fused append-and-decode call (every key run); 1..7: kept
+// 16-channel key runs; 8: unpruned
 template <bool BF16, int HIMODE, bool VHI>
 static void launch_keep(const Geo& g, int keep, const Launch& a) {
   switch (keep) {
-    case 0: launch_one<BF16, HIMODE, 4, VHI, true>(g, a); break;
-    case 1: launch_one<BF16, HIMODE, 1, VHI, false>(g, a); break;
-    case 2: launch_one<BF16, HIMODE, 2, VHI, false>(g, a); break;
-    case 3: launch_one<BF16, HIMODE, 3, VHI, false>(g, a); break;
-    default: launch_one<BF16, HIMODE, 4, VHI, false>(g, a); break;
+    case 0: launch_one<BF16, HIMODE, 0, VHI, true>(g, 8, a); break;
+    case 1: case 2: launch_one<BF16, HIMODE, 1, VHI, false>(g, keep, a); break;
+    case 3: case 4: launch_one<BF16, HIMODE, 2, VHI, false>(g, keep, a); break;
+    case 5: case 6: launch_one<BF16, HIMODE, 3, VHI, false>(g, keep, a); break;
+    case 7: launch_one<BF16, HIMODE, 4, VHI, false>(g, keep, a); break;
+    default: launch_one<BF16, HIMODE, 0, VHI, false>(g, 8, a); break;
   }
 }
 

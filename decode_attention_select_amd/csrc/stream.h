@@ -71,10 +71,11 @@ struct SlotCfg {
   static_assert((NSLOT - 1) * NLD < 64, "vmcnt range");
 };
 
-// Issues the copies of quantized group `rec` into `slot`.  PRUNE: the lanes
-// of pruned key chunks (k_lo words, key scale/zero) read the kept chunk
-// kept0 instead, lines the same instruction fetches anyway, so the pruned
-// chunks' bytes are not read; what those lanes write is never read.
+// Issues the copies of quantized group `rec` into `slot`.  PRUNE (kmask bit
+// s: 16-channel key run s kept): the lanes of pruned runs (their k_lo words,
+// their key scale/zero) read the kept run kept0 instead, bytes the same
+// instruction fetches anyway, so the pruned runs' bytes are not read; what
+// those lanes write is never read.
 template <int HIMODE, bool VHI, bool PRUNE>
 __device__ inline void issue_group(const kvq_cache& c, size_t rec, uint8_t* slot, int lane,
                                    uint32_t kmask, int kept0, int nh, int nvhi) {
@@ -82,14 +83,14 @@ __device__ inline void issue_group(const kvq_cache& c, size_t rec, uint8_t* slot
   // k_lo: lane l holds words 4l .. 4l+3: tokens 4 (l % 4) .. +3 of the 16-channel
   // run u = (l / 4) % 2 of key chunk (l / 8) % 4, tile half l / 32
   int lk = lane;
-  if (PRUNE && !((kmask >> ((lane >> 3) & 3)) & 1u)) lk = (lane & ~24) | (kept0 << 3);
+  if (PRUNE && !((kmask >> ((lane >> 2) & 7)) & 1u)) lk = (lane & ~28) | (kept0 << 2);
   dma16<CPOL_NT>((const uint8_t*)c.k_lo + rec * 1024 + lk * 16, slot + C::KLO);
   // metadata: lanes 0..31 k_meta (0..15 scales, 16..31 zeros of channels
-  // 8 (l % 16) .. +7, chunk (l % 16) / 4), lanes 32..63 v_meta
+  // 8 (l % 16) .. +7, run (l % 16) / 2), lanes 32..63 v_meta
   {
     int lm = lane;
-    if (PRUNE && lane < 32 && !((kmask >> ((lane & 15) >> 2)) & 1u))
-      lm = (lane & 16) | (kept0 << 2) | (lane & 3);
+    if (PRUNE && lane < 32 && !((kmask >> ((lane & 15) >> 1)) & 1u))
+      lm = (lane & 16) | (kept0 << 1) | (lane & 1);
     const uint8_t* src = lane < 32 ? (const uint8_t*)c.k_meta + rec * 512 + lm * 16
                                    : (const uint8_t*)c.v_meta + rec * 512 + (lane - 32) * 16;
     dma16<CPOL_NT>(src, slot + C::META);

@@ -305,18 +305,19 @@ kvq_status kvq_decode_attn(const kvq_layout *L, const void *q,
 /* Decode attention with dynamic query-channel pruning ([Dual-QK] abstract:
  * a decode query keeps its few large channels and drops the many small
  * ones, so the key cache is read only for the kept channels; the page gives
- * no rule, so this is a reading).  Per (b, kv head) the n_keep (1..4) of the
- * four 32-channel key chunks (channels 32m .. 32m+31: the contiguous runs of
- * k_lo, k_meta and ring_k) with the largest
- *   E_m = sum over the group's query heads h and channels c of chunk m of
+ * no rule, so this is a reading).  Per (b, kv head) the n_keep (1..8) of the
+ * eight 16-channel key runs (channels 16s .. 16s+15: the contiguous runs of
+ * k_lo (64 bytes per 16 tokens), k_meta and ring_k) with the largest
+ *   E_s = sum over the group's query heads h and channels c of run s of
  *         min(floor(4096 |q[h][c]|), 2^20)
- * (exact in 32 bits for every 16-bit query) are kept (ties to the lower m),
+ * (exact in 32 bits for every 16-bit query) are kept (ties to the lower s),
  * and every logit sums q[h][c] * k^[t][c]
  * over the kept channels only, for quantized and ring tokens alike (the
- * query is zero on the pruned channels).  Past a split's first prefetched
- * groups the pruned chunks' key codes and key scale/zero are not read.
- * n_keep = 4 is kvq_decode_attn; n_keep outside 1..4 returns KVQ_EINVAL.
- * All other arguments, limits and errors as for kvq_decode_attn. */
+ * query is zero on the pruned channels).  The pruned runs' key codes and
+ * key scale/zero are not read (the group copies wait for the query and the
+ * choice); n_keep = 5 drops 37.5 % of the key channels.  n_keep = 8 is
+ * kvq_decode_attn; n_keep outside 1..8 returns KVQ_EINVAL.  All other
+ * arguments, limits and errors as for kvq_decode_attn. */
 kvq_status kvq_decode_attn_pruned(const kvq_layout *L, const void *q,
                                   const kvq_cache *cache, float sm_scale,
                                   int32_t n_splits, int32_t n_keep,

@@ -19,7 +19,7 @@ independent bit-level unpacker; attention against textbook softmax attention
 (all-16-bit cache), T = 1, q = 0 and a brute-force pass over the dequantized
 cache.
 
-Parity unpinned: the query-aware pair score (select_qa), the kept key chunks
+Parity unpinned: the query-aware pair score (select_qa), the kept key runs
 of pruned decode (prune_chunks) and the token order of two value precisions
 (order in quantize) follow rules the pages describe without a formula; their
 tests pin each to its own rule (float sums, invariances, planted cases), not
@@ -308,12 +308,12 @@ def select_qa(q_sel, k, T: int, n_kv_heads: int, io_dtype: str):
 
 
 def prune_chunks(q, n_kv_heads: int, io_dtype: str, n_keep: int) -> np.ndarray:
-    """Query-channel pruning (the Dual-QK reading): bool [B][Hkv][4], True
-    for the n_keep 32-channel key chunks of largest summed fixed-point |q|
-    over the group's heads (ties to the lower chunk)."""
+    """Query-channel pruning (the Dual-QK reading): bool [B][Hkv][8], True
+    for the n_keep 16-channel key runs of largest summed fixed-point |q|
+    over the group's heads (ties to the lower run)."""
     q = np.ascontiguousarray(q, dtype=np.uint16)
     B, Hq, _ = q.shape
-    keep = np.zeros((B, n_kv_heads, 4), np.uint8)
+    keep = np.zeros((B, n_kv_heads, 8), np.uint8)
     rc = _load().orc_prune_chunks(B, Hq, n_kv_heads, _bf(io_dtype), _p(q), int(n_keep), _p(keep))
     assert rc == 0
     return keep.astype(bool)
@@ -321,7 +321,7 @@ def prune_chunks(q, n_kv_heads: int, io_dtype: str, n_keep: int) -> np.ndarray:
 
 def attention_pruned(qz: Quantized, q, sm_scale: float, n_keep: int, with_lse: bool = False):
     """Decode attention with pruned query channels: every logit sums q_c k^_c
-    over the kept chunks' channels only (quantized and ring tokens alike),
+    over the kept runs' channels only (quantized and ring tokens alike),
     written as attention over the query with the pruned channels set to 0."""
     q = np.ascontiguousarray(q, dtype=np.uint16)
     B, Hq, _ = q.shape
@@ -331,7 +331,7 @@ def attention_pruned(qz: Quantized, q, sm_scale: float, n_keep: int, with_lse: b
     G = Hq // Hkv
     for b in range(B):
         for h in range(Hq):
-            for m in range(4):
-                if not keep[b, h // G, m]:
-                    qm[b, h, 32 * m:32 * m + 32] = 0
+            for s in range(8):
+                if not keep[b, h // G, s]:
+                    qm[b, h, 16 * s:16 * s + 16] = 0
     return attention(qz, qm, sm_scale, with_lse=with_lse)

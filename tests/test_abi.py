@@ -135,8 +135,8 @@ def test_decode_validation():
     bad = fake_cache()
     bad.len = 0
     assert call(cache=bad) == EINVAL
-    # the pruned variant: n_keep outside 1..4
-    for n_keep, want in ((0, EINVAL), (5, EINVAL), (-1, EINVAL)):
+    # the pruned variant: n_keep outside 1..8
+    for n_keep, want in ((0, EINVAL), (9, EINVAL), (-1, EINVAL)):
         assert status_of("kvq_decode_attn_pruned", ctypes.byref(L), P(FAKE), ctypes.byref(c),
                          ctypes.c_float(0.088), 8, n_keep, P(FAKE), ctypes.c_size_t(ws), P(FAKE),
                          P(0)) == want

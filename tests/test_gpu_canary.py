@@ -91,7 +91,7 @@ def test_guard_bands_survive_every_call(cfg):
         kvq.kvq_decode_attn(layout, q.ptr(), cache, SM_SCALE, S, ws.ptr(), out.ptr(),
                             ws_bytes=ws.n)
         kvq.kvq_read_ceiling(layout, cache, S, sink.ptr())
-    kvq.kvq_decode_attn_pruned(layout, q.ptr(), cache, SM_SCALE, 3, 2, ws.ptr(), out.ptr(),
+    kvq.kvq_decode_attn_pruned(layout, q.ptr(), cache, SM_SCALE, 3, 5, ws.ptr(), out.ptr(),
                                ws_bytes=ws.n)
     # appends across group boundaries, every other one fused with a decode
     for i in range(n_app):

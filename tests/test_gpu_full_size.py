@@ -181,7 +181,7 @@ def test_llama3_8b_32k_pruned_and_query_aware_and_shrink():
     qz = case.oracle_quant(pairs=pairs)
     q = case.d["q_dec"][:, :, 0]
     S = bench.default_splits(w)
-    for n_keep in (2, 3):
+    for n_keep in (5, 6):
         ref = oracle.attention_pruned(qz, q, SM_SCALE, n_keep)
         err = check_output(case.decode_pruned(q, S, n_keep), ref, w.io_dtype, ATOL)
         print("%s keep=%d S=%d max|err| %.3g" % (w.name, n_keep, S, err), flush=True)

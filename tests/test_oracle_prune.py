@@ -1,18 +1,18 @@
 """Pins of the oracle's query-channel pruning at decode (Dual-QK, abstract:
 keep a decode query's few large channels, drop the many small ones, and read
 the key cache only for the kept ones).  The page gives no rule; the reading
-keeps, per (b, kv head), the n_keep of the four 32-channel key chunks with
+keeps, per (b, kv head), the n_keep of the eight 16-channel key runs with
 the largest summed |q| over the group's heads (fixed point: min(floor(4096
-|q|), 2^20) per value; ties to the lower chunk), and every logit sums
+|q|), 2^20) per value; ties to the lower run), and every logit sums
 q_c k^_c over the kept channels only.
 
 * Selection: the kept set is the top n_keep by a plain float64 sum of |q|
-  wherever that sum separates the chunks; it does not change when heads are
-  permuted inside a group or channels inside a chunk, nor when q is doubled
+  wherever that sum separates the runs; it does not change when heads are
+  permuted inside a group or channels inside a run, nor when q is doubled
   for values whose fixed-point form is exact (multiples of 1/4096); a planted
-  chunk is kept first; an all-zero query keeps chunks 0 .. n_keep-1; a
+  run is kept first; an all-zero query keeps runs 0 .. n_keep-1; a
   query far beyond the cap still ranks; the kept sets are nested in n_keep.
-* Attention: n_keep = 4 is unpruned attention, bit for bit; otherwise it
+* Attention: n_keep = 8 is unpruned attention, bit for bit; otherwise it
   equals textbook softmax attention whose logits use only the kept channels'
   columns of the key matrix, rebuilt from the packed bytes by the brute-force
   unpacker (quantized groups) and from the 16-bit inputs (ring).
@@ -42,17 +42,17 @@ def test_selection_matches_float_sums_where_separated(data):
     G = W.group_size
     qf = np.abs(kvq_synth.bits_to_f64(q, W.io_dtype))
     checked = 0
-    for n_keep in (1, 2, 3):
+    for n_keep in range(1, 8):
         keep = oracle.prune_chunks(q, W.n_kv_heads, W.io_dtype, n_keep)
         for b in range(W.batch):
             for kh in range(W.n_kv_heads):
-                e = qf[b, kh * G:(kh + 1) * G].reshape(G, 4, 32).sum(axis=(0, 2))
+                e = qf[b, kh * G:(kh + 1) * G].reshape(G, 8, 16).sum(axis=(0, 2))
                 order = np.argsort(-e, kind="stable")
                 srt = e[order]
-                # the fixed point drops under 1/4096 per value: 1/32 per chunk and head
-                if srt[n_keep - 1] - srt[n_keep] < G / 16:
+                # the fixed point drops under 1/4096 per value: 1/256 per run and head
+                if srt[n_keep - 1] - srt[n_keep] < G / 128:
                     continue  # too close for a float sum to decide
-                want = np.zeros(4, bool)
+                want = np.zeros(8, bool)
                 want[order[:n_keep]] = True
                 assert np.array_equal(keep[b, kh], want)
                 checked += 1
@@ -64,9 +64,9 @@ def test_selection_invariances(data):
     G = W.group_size
     rng = np.random.default_rng(5)
     qf = kvq_synth.bits_to_f64(q, W.io_dtype)
-    # heads permuted inside each group, channels permuted inside each chunk
+    # heads permuted inside each group, channels permuted inside each run
     hp = np.concatenate([kh * G + rng.permutation(G) for kh in range(W.n_kv_heads)])
-    cp = np.concatenate([32 * m + rng.permutation(32) for m in range(4)])
+    cp = np.concatenate([16 * m + rng.permutation(16) for m in range(8)])
     q2 = q[:, hp][:, :, cp]
     # doubling: values rounded to multiples of 1/4096 (and below the cap)
     qr = np.clip(np.round(qf * 4096) / 4096, -100, 100)
@@ -75,38 +75,38 @@ def test_selection_invariances(data):
                           np.round(kvq_synth.bits_to_f64(q, W.io_dtype) * 4096))
     q2 = q[:, hp][:, :, cp]
     q3 = kvq_synth.to_bits(2 * kvq_synth.bits_to_f64(q, W.io_dtype), W.io_dtype)
-    for n_keep in (1, 2, 3, 4):
+    for n_keep in range(1, 9):
         k0 = oracle.prune_chunks(q, W.n_kv_heads, W.io_dtype, n_keep)
         assert np.array_equal(k0, oracle.prune_chunks(q2, W.n_kv_heads, W.io_dtype, n_keep))
         assert np.array_equal(k0, oracle.prune_chunks(q3, W.n_kv_heads, W.io_dtype, n_keep))
         assert np.all(k0.sum(axis=2) == n_keep)
-        if n_keep < 4:  # nested
+        if n_keep < 8:  # nested
             k1 = oracle.prune_chunks(q, W.n_kv_heads, W.io_dtype, n_keep + 1)
             assert np.all(k1[k0])
 
 
-def test_planted_chunk_and_zero_query(data):
+def test_planted_run_and_zero_query(data):
     q = _q(data)
     qf = kvq_synth.bits_to_f64(q, W.io_dtype)
-    for m in range(4):
+    for m in range(8):
         qp = qf.copy()
-        qp[:, :, 32 * m:32 * m + 32] *= 64
+        qp[:, :, 16 * m:16 * m + 16] *= 64
         keep = oracle.prune_chunks(kvq_synth.to_bits(qp, W.io_dtype), W.n_kv_heads, W.io_dtype, 1)
-        want = np.zeros(4, bool)
+        want = np.zeros(8, bool)
         want[m] = True
         assert np.all(keep == want)
     zero = np.zeros_like(q)
-    for n_keep in (1, 2, 3):
+    for n_keep in range(1, 8):
         keep = oracle.prune_chunks(zero, W.n_kv_heads, W.io_dtype, n_keep)
-        assert np.all(keep == (np.arange(4) < n_keep))
-    # huge values: every one capped at 2^20 / 4096 = 256; the chunk with the
+        assert np.all(keep == (np.arange(8) < n_keep))
+    # huge values: every one capped at 2^20 / 4096 = 256; the run with the
     # most of them wins, whatever their size beyond the cap
     big = np.zeros((1, W.group_size, 128))
-    big[0, :, 32 * 2:32 * 2 + 3] = 1e30
-    big[0, :, 32 * 1:32 * 1 + 2] = 3e38
-    big[0, :, 32 * 3] = 1000.0
+    big[0, :, 16 * 5:16 * 5 + 3] = 1e30
+    big[0, :, 16 * 2:16 * 2 + 2] = 3e38
+    big[0, :, 16 * 7] = 1000.0
     keep = oracle.prune_chunks(kvq_synth.to_bits(big, "bf16"), 1, "bf16", 1)
-    assert np.array_equal(keep[0, 0], [False, False, True, False])
+    assert np.array_equal(keep[0, 0], np.arange(8) == 5)
 
 
 def _quantized(data):
@@ -119,11 +119,11 @@ def test_keep_all_is_unpruned_attention(data):
     qz = _quantized(data)
     sm = float(np.float32(1.0 / np.sqrt(128.0)))
     a = oracle.attention(qz, _q(data), sm)
-    b = oracle.attention_pruned(qz, _q(data), sm, 4)
+    b = oracle.attention_pruned(qz, _q(data), sm, 8)
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("n_keep", [1, 2, 3])
+@pytest.mark.parametrize("n_keep", [1, 3, 5, 7])
 def test_pruned_attention_matches_textbook_on_kept_columns(data, n_keep):
     qz = _quantized(data)
     pk = oracle.pack(qz)
@@ -149,7 +149,7 @@ def test_pruned_attention_matches_textbook_on_kept_columns(data, n_keep):
                     for j in range(4):
                         V[32 * g + t, 32 * j:32 * j + 32] = (f16(vz[t, j]) + f16(vs[t, j]) *
                                                              vc[t, 32 * j:32 * j + 32])
-            cols = np.concatenate([np.arange(32 * m, 32 * m + 32) for m in range(4)
+            cols = np.concatenate([np.arange(16 * m, 16 * m + 16) for m in range(8)
                                    if keep[b, kh, m]])
             for h in range(kh * G, kh * G + G):
                 qf = kvq_synth.bits_to_f64(q[b, h], W.io_dtype)
