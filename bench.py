@@ -145,8 +145,12 @@ def cache_ng(cache, w):
 
 
 def default_splits(w) -> int:
-    # one 8-wave workgroup per CU: 256 CUs / (sequences * KV heads)
-    return max(1, min(1024, math.ceil(256 / (w.batch * w.n_kv_heads))))
+    """One 8-wave workgroup per CU (256 CUs / (sequences * KV heads)), but no
+    more splits than give every wave two quantized groups: a short context
+    spread over many splits only adds merge work."""
+    per_cu = math.ceil(256 / (w.batch * w.n_kv_heads))
+    groups = max(0, w.tokens - w.residual) // 32
+    return max(1, min(1024, per_cu, math.ceil(groups / 16)))
 
 
 SM_SCALE = 1.0 / math.sqrt(128.0)

@@ -67,7 +67,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads, seed = 1000 + index.
+# The five workloads, seed = 1000 + index, and one measurement variant.
 WORKLOADS = [
     Workload("tiny", 1, 1, 1, 512, io_dtype="fp16", outliers="pairs4x8",
              n_pairs_hi=8, residual=32, seed=1000),
@@ -80,6 +80,10 @@ WORKLOADS = [
     # 256 token partitions in all: 32 per KV head, one workgroup per CU
     Workload("long-128k", 1, 64, 8, 131072, outliers="pairs4x8",
              n_pairs_hi=6, residual=128, n_splits=32, seed=1004),
+    # the 32K layer's cache with one query head per KV head (G = 1): the same
+    # bytes, 1 of 16 MFMA head columns used
+    Workload("g1-32k", 1, 8, 8, 32768, outliers="pct2x10",
+             n_pairs_hi=6, residual=128, seed=1005),
 ]
 
 # Key bit points of the Pareto sweep: (label, n_pairs_hi, bits_hi).
