@@ -30,27 +30,64 @@ sys.path.insert(0, ROOT)
 PEAK_GBS = 8000.0
 # HBM bytes per launch of the decode kernel on the default workload: a
 # committed record of the FETCH_SIZE and WRITE_SIZE counters scaled by a plain
-# copy (written by --traffic-from), valid only for the sources it was
-# measured on (their hash is in the record); null once they have changed.
+# copy (written by --traffic-from), valid only for the machine code it was
+# measured on (a hash of the kernel's bytes in the built library is in the
+# record); null once the kernel has changed.
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_traffic_llama3-8b-32k.md")
-DECODE_SOURCES = ["decode_attention_select_amd/csrc/decode.hip",
-                  "decode_attention_select_amd/csrc/stream.h",
-                  "decode_attention_select_amd/csrc/common.h",
-                  "decode_attention_select_amd/csrc/quant_group.h", "include/kvq.h"]
+# the decode kernel instance of the default workload: bf16, 4-bit salient
+# digits, quantized groups, unpruned, one value precision, no append, G <= 8
+DECODE_KERNEL = "_ZN3kvq13decode_kernelILb1ELi4ELb1ELi0ELb0ELb0ELb1E"
 
 
-def decode_sources_hash() -> str:
+def kernel_code_hash(symbol_prefix: str = DECODE_KERNEL, lib_path: str = None):
+    """sha256 (16 hex digits) of a kernel's machine code in the gfx950 code
+    objects embedded in libkvq.so (this build's own library), or None."""
     import hashlib
-    h = hashlib.sha256()
-    for rel in DECODE_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    import struct
+    if lib_path is None:
+        lib_path = os.path.join(ROOT, "decode_attention_select_amd", "libkvq.so")
+    try:
+        data = open(lib_path, "rb").read()
+    except OSError:
+        return None
+
+    def sections(buf, base):
+        shoff = struct.unpack_from("<Q", buf, base + 40)[0]
+        shentsize, shnum, shstrndx = struct.unpack_from("<HHH", buf, base + 58)
+        secs = [struct.unpack_from("<IIQQQQIIQQ", buf, base + shoff + k * shentsize)
+                for k in range(shnum)]
+        return secs, secs[shstrndx]
+
+    def cstr(buf, at):
+        return buf[at:buf.index(b"\0", at)].decode()
+
+    secs, strtab = sections(data, 0)
+    fat = [sh for sh in secs if cstr(data, strtab[4] + sh[0]) == ".hip_fatbin"]
+    if not fat:
+        return None
+    blob = data[fat[0][4]:fat[0][4] + fat[0][5]]
+    i = 0
+    while True:
+        i = blob.find(b"\x7fELF", i)
+        if i < 0:
+            return None
+        if struct.unpack_from("<H", blob, i + 18)[0] == 224:  # EM_AMDGPU
+            csecs, _ = sections(blob, i)
+            for st in [sh for sh in csecs if sh[1] == 2]:  # SHT_SYMTAB
+                names = csecs[st[6]]
+                for k in range(st[5] // 24):
+                    nm, info, _, shndx, val, size = struct.unpack_from("<IBBHQQ", blob,
+                                                                       i + st[4] + k * 24)
+                    if (info & 15) == 2 and cstr(blob, i + names[4] + nm).startswith(symbol_prefix):
+                        sec = csecs[shndx]
+                        at = i + sec[4] + (val - sec[3])
+                        return hashlib.sha256(blob[at:at + size]).hexdigest()[:16]
+        i += 4
 
 
 def measured_traffic(workload: str):
     """Bytes per launch from the committed counter record, or None when there
-    is no record for this workload or the decode sources have changed."""
+    is no record for this workload or the kernel's machine code has changed."""
     try:
         lines = open(TRAFFIC_RECORD).read().splitlines()
     except OSError:
@@ -58,7 +95,7 @@ def measured_traffic(workload: str):
     for line in lines:
         if line.startswith("record: "):
             rec = json.loads(line[len("record: "):])
-            if rec.get("workload") == workload and rec.get("sources") == decode_sources_hash():
+            if rec.get("workload") == workload and rec.get("kernel") == kernel_code_hash():
                 return int(rec["bytes_per_launch"])
     return None
 
@@ -92,7 +129,7 @@ def traffic_record(dec_fetch, dec_write, copy_fetch, copy_write, copy_mib=256):
     cw = counter_means(copy_write, "copyBuffer")["WRITE_SIZE"]
     kib = copy_mib * 1024.0
     sf, sw = kib / cf, kib / cw
-    return {"workload": "llama3-8b-32k", "sources": decode_sources_hash(),
+    return {"workload": "llama3-8b-32k", "kernel": kernel_code_hash(),
             "fetch_kib": round(f, 2), "write_kib": round(wr, 2),
             "copy_fetch_kib": round(cf, 2), "copy_write_kib": round(cw, 2),
             "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),

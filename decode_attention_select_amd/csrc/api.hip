@@ -1,6 +1,8 @@
 // api.hip — the C ABI of libkvq (declared in include/kvq.h): argument
 // validation, buffer sizes and launch dispatch.  No call allocates or
 // synchronizes (except kvq_check).
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -64,6 +66,25 @@ kvq_status scratch_ptr(void** out, size_t tick_bytes, hipStream_t st) {
   g_scratch_clean[dev] = tick_bytes;  // records follow the counters from here on
   *out = p;
   return KVQ_OK;
+}
+
+// KVQ_LOG set (to anything but "0") in the environment: every launch prints
+// its call, shape and launch geometry on stderr (host side only).
+bool log_on() {
+  static const bool on = [] {
+    const char* e = getenv("KVQ_LOG");
+    return e && *e && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void log_launch(const char* call, const Geo& g, int T, int splits, int keep) {
+  if (!log_on()) return;
+  fprintf(stderr,
+          "kvq: %s B=%d Hq=%d Hkv=%d G=%d T=%d R=%d groups<=%d n_hi=%d bits_hi=%d n_lo1=%d "
+          "n_vhi=%d io=%s splits=%d keep=%d\n",
+          call, g.B, g.Hq, g.Hkv, g.G, T, g.R, g.NG, g.n_hi, g.bits_hi, g.n_lo1, g.n_vhi,
+          g.bf16 ? "bf16" : "fp16", splits, keep);
 }
 
 kvq_status check_layout(const kvq_layout* L) {
@@ -176,6 +197,7 @@ kvq_status kvq_select_pairs(const kvq_layout* L, const void* q_sel, int32_t n_qr
   if (kvq_status s = check_ptr(q_sel)) return s;
   if (kvq_status s = check_ptr(k)) return s;
   if (kvq_status s = check_cache(g, cache, false)) return s;
+  log_launch("kvq_select_pairs", g, T, 0, 0);
   return hip_status(launch_select(g, q_sel, n_qry, k, T, cache, (hipStream_t)stream));
 }
 
@@ -188,6 +210,7 @@ kvq_status kvq_select_pairs_qa(const kvq_layout* L, const void* q_sel, int32_t n
   if (kvq_status s = check_ptr(q_sel)) return s;
   if (kvq_status s = check_ptr(k)) return s;
   if (kvq_status s = check_cache(g, cache, false)) return s;
+  log_launch("kvq_select_pairs_qa", g, T, 0, 0);
   return hip_status(launch_select_qa(g, q_sel, n_qry, k, T, cache, (hipStream_t)stream));
 }
 
@@ -199,6 +222,7 @@ kvq_status kvq_quant_keys(const kvq_layout* L, const void* k, int32_t T, kvq_cac
   if (T > g.max_tokens) return KVQ_ECAPACITY;
   if (kvq_status s = check_ptr(k)) return s;
   if (kvq_status s = check_cache(g, cache, true)) return s;
+  log_launch("kvq_quant_keys", g, T, 0, 0);
   return hip_status(launch_quant_keys(g, k, T, cache, (hipStream_t)stream));
 }
 
@@ -210,6 +234,7 @@ kvq_status kvq_quant_values(const kvq_layout* L, const void* v, int32_t T, kvq_c
   if (T > g.max_tokens) return KVQ_ECAPACITY;
   if (kvq_status s = check_ptr(v)) return s;
   if (kvq_status s = check_cache(g, cache, true)) return s;
+  log_launch("kvq_quant_values", g, T, 0, 0);
   return hip_status(launch_quant_values(g, v, T, cache, (hipStream_t)stream));
 }
 
@@ -220,6 +245,7 @@ kvq_status kvq_append(const kvq_layout* L, const void* k_new, const void* v_new,
   if (kvq_status s = check_ptr(k_new)) return s;
   if (kvq_status s = check_ptr(v_new)) return s;
   if (kvq_status s = check_cache(g, cache, true)) return s;
+  log_launch("kvq_append", g, -1, 0, 0);
   return hip_status(launch_append(g, k_new, v_new, cache, (hipStream_t)stream));
 }
 
@@ -232,6 +258,7 @@ kvq_status kvq_shrink(const kvq_layout* L, kvq_cache* cache, int32_t g0, int32_t
   if (kvq_status s = check_cache(g, cache, true)) return s;
   if (g.NG > 0 && g1 > g.NG) g1 = g.NG;
   if (g0 > g1) g0 = g1;
+  log_launch("kvq_shrink", g, -1, g1 - g0, 0);
   return hip_status(launch_shrink(g, cache, g0, g1, (hipStream_t)stream));
 }
 
@@ -256,6 +283,9 @@ static kvq_status decode_common(const kvq_layout* L, const void* q, const kvq_ca
     if (kvq_status s = check_ptr(v_new)) return s;
   }
   if (kvq_status s = check_cache(g, cache, true)) return s;
+  log_launch(keep == 0 ? "kvq_append_decode_attn" : keep < 8 ? "kvq_decode_attn_pruned"
+                                                             : "kvq_decode_attn",
+             g, -1, n_splits, keep);
   return hip_status(launch_decode(g, q, cache, sm_scale, n_splits, keep, workspace, out,
                                   (hipStream_t)stream, k_new, v_new));
 }
@@ -303,6 +333,7 @@ kvq_status kvq_read_ceiling(const kvq_layout* L, const kvq_cache* cache, int32_t
   if (kvq_status s = kvq_workspace_bytes(L, n_splits, &need)) return s;  // n_splits limits
   if (kvq_status s = check_ptr(sink)) return s;
   if (kvq_status s = check_cache(g, cache, true)) return s;
+  log_launch("kvq_read_ceiling", g, -1, n_splits, 8);
   return hip_status(launch_ceiling(g, cache, n_splits, sink, (hipStream_t)stream));
 }
 

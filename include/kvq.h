@@ -33,7 +33,11 @@
  *     kvq_check.  No call allocates or frees memory.  A failed launch returns
  *     KVQ_EHIP.
  *   - All memory is owned by the caller.  The library keeps no state besides
- *     its loaded code objects; calls on different caches may run concurrently.
+ *     its loaded code objects and the static workspace of
+ *     kvq_decode_attn_noalloc; calls on different caches may run concurrently.
+ *   - With KVQ_LOG set in the environment (to anything but "0"), every
+ *     launch prints its call, shape, split count and kept key runs on stderr
+ *     (host side only).
  *   - 16-bit inputs (KVQ_FP16 or KVQ_BF16, `io_dtype`) are contiguous,
  *     row-major, last dimension = channel.  Inputs must be finite with
  *     |x| <= 32752, so that every scale below stays finite; for such inputs

@@ -195,3 +195,14 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_record_is_keyed_to_the_kernel_code():
+    # roofline.traffic comes from a committed counter record only while the
+    # decode kernel's machine code in the built library is the one measured
+    import bench
+    h = bench.kernel_code_hash()
+    assert h is not None and len(h) == 16 and int(h, 16) >= 0
+    assert bench.kernel_code_hash() == h
+    assert bench.kernel_code_hash("_ZN3kvq_no_such_kernel") is None
+    assert bench.measured_traffic("no-such-workload") is None
