@@ -692,8 +692,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         if (i >= KB) break;
-        const int pb = 8 * krun[i] + 4 * khalf;
-        const u4 spv = *(const u4*)(sm + pb), zp = *(const u4*)(sm + 64 + pb);
+        const int pb = 16 * krun[i] + 4 * khalf;  // the run's scale pairs, then its zero pairs
+        const u4 spv = *(const u4*)(sm + pb), zp = *(const u4*)(sm + pb + 8);
 #pragma unroll
         for (int bb = 0; bb < 4; bb++) {
           const uint32_t sp = spv[bb];
@@ -710,8 +710,10 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     } else {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const u4 sv = ((const u4*)(sm + 16 * kq))[i];
-        const u4 zv = ((const u4*)(sm + 64 + 16 * kq))[i];
+        // chunk kq's channel pairs 4i .. 4i+3: run 2kq + i/2, its pairs 4 (i%2) ..
+        const uint32_t* rm = sm + (2 * kq + (i >> 1)) * 16 + 4 * (i & 1);
+        const u4 sv = *(const u4*)rm;
+        const u4 zv = *(const u4*)(rm + 8);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           if constexpr (LOCOL) {
@@ -735,7 +737,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       // the salient channels' scales, gathered once into a contiguous row
       // (lane l copies digit l%16), then read 8 at a time
       uint16_t* ss = lds.sal_s[wave];
-      ss[lane & 15] = ((const uint16_t*)sm)[sal_ch];
+      ss[lane & 15] = ((const uint16_t*)sm)[(sal_ch >> 4) * 32 + (sal_ch & 15)];
       __builtin_amdgcn_wave_barrier();
       compiler_fence();
       const u4 spv = *(const u4*)(ss + 8 * (kq & 1));
@@ -758,7 +760,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
           if (i >= KB) break;
           // the lane's half of run krun[i]'s word: pairs 4 khalf .. +3
           const uint32_t w =
-              ((const uint32_t*)(slot + SC::KLO))[(TT * 8 + krun[i]) * 16 + col] >> sh;
+              ((const uint32_t*)(slot + SC::KLO))[(krun[i] * 2 + TT) * 16 + col] >> sh;
           const uint32_t A = w & 0x33333333u, Bn = (w >> 2) & 0x33333333u;
           const u4 cd = u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)};
           acc = mma_f16(cd, u4{qs[4 * i], qs[4 * i + 1], qs[4 * i + 2], qs[4 * i + 3]}, acc);
@@ -766,8 +768,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
             acc = mma_f16(cd, u4{qsl[4 * i], qsl[4 * i + 1], qsl[4 * i + 2], qsl[4 * i + 3]}, acc);
         }
       } else {
-        const uint32_t* kw0 = (const uint32_t*)(slot + SC::KLO) + (TT * 4 + kqa) * 32 + col;
-        const u2 w = u2{kw0[0], kw0[16]};  // the two 16-channel runs of chunk kqa
+        const uint32_t* kw0 = (const uint32_t*)(slot + SC::KLO) + (kqa * 4 + TT) * 16 + col;
+        const u2 w = u2{kw0[0], kw0[32]};  // the two 16-channel runs of chunk kqa
 #pragma unroll
         for (int u = 0; u < 2; u++) {
           const uint32_t A = w[u] & 0x33333333u, Bn = (w[u] >> 2) & 0x33333333u;

@@ -193,7 +193,7 @@ __global__ __launch_bounds__(64 * SHRINK_WAVES) void shrink_kernel(Geo g, kvq_ca
   uint2 lw[4];
 #pragma unroll
   for (int kq = 0; kq < 4; kq++)
-    lw[kq] = make_uint2(lo[((T * 4 + kq) * 2) * 16 + r], lo[((T * 4 + kq) * 2 + 1) * 16 + r]);
+    lw[kq] = make_uint2(lo[((kq * 2) * 2 + T) * 16 + r], lo[((kq * 2 + 1) * 2 + T) * 16 + r]);
   uint32_t hw = hi[e];
   int d = 0;
   for (int side = 0; side < 2; side++) {  // channels j, then j + 64
@@ -220,8 +220,8 @@ __global__ __launch_bounds__(64 * SHRINK_WAVES) void shrink_kernel(Geo g, kvq_ca
   }
 #pragma unroll
   for (int kq = 0; kq < 4; kq++) {
-    lo[((T * 4 + kq) * 2) * 16 + r] = lw[kq].x;
-    lo[((T * 4 + kq) * 2 + 1) * 16 + r] = lw[kq].y;
+    lo[((kq * 2) * 2 + T) * 16 + r] = lw[kq].x;
+    lo[((kq * 2 + 1) * 2 + T) * 16 + r] = lw[kq].y;
   }
   hi[e] = hw;
 }

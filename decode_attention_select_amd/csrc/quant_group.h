@@ -350,7 +350,7 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const int T = i >> 2, r = 4 * tq + (i & 3);
-    ((uint16_t*)L.lo)[(((T * 4 + kq) * 2 + u) * 16 + r) * 2 + half] = (uint16_t)hw[i];
+    ((uint16_t*)L.lo)[(((kq * 2 + u) * 2 + T) * 16 + r) * 2 + half] = (uint16_t)hw[i];
     if (bits4 && hh[i]) atomicOr(&L.hi[16 * T + r], hh[i]);
   }
   if (raw16) {
@@ -373,7 +373,9 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
     for (int p = 0; p < 4; p++)
       m[p] = tq == 0 ? (sz[2 * p] & 0xFFFFu) | (sz[2 * p + 1] << 16)
                      : (sz[2 * p] >> 16) | (sz[2 * p + 1] & 0xFFFF0000u);
-    *(uint4*)(meta_out + tq * D + 8 * cb) = make_uint4(m[0], m[1], m[2], m[3]);
+    // run cb / 2 of the record: its 16 scales, then its 16 zeros
+    *(uint4*)(meta_out + (cb >> 1) * 32 + tq * 16 + 8 * (cb & 1)) =
+        make_uint4(m[0], m[1], m[2], m[3]);
   }
 }
 

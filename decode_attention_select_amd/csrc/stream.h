@@ -48,9 +48,10 @@ __device__ inline void dma16(const void* src, void* dst) {
 // One LDS slot holds the records of one quantized group, copied from HBM by
 // direct loads (16 bytes per lane and instruction):
 //   KLO  [0, 1024)     k_lo
-//   META [1024, 2048)  k_meta (512) then v_meta (512): [0,64) key scale
-//                      pairs, [64,128) key zero pairs, [128,192) value scale
-//                      pairs (j-major), [192,256) value zero pairs (words)
+//   META [1024, 2048)  k_meta (512) then v_meta (512): words [16w, 16w+8)
+//                      the scale pairs and [16w+8, 16w+16) the zero pairs of
+//                      key run w (channels 16w ..), [128,192) value scale
+//                      pairs (j-major), [192,256) value zero pairs
 //   VC   [2048, 3072)  v_codes
 //   KHI  1024 bytes: k_hi (HIMODE 4 its 128 bytes, HIMODE 16 its 64 nh bytes)
 //   VH   1024 bytes: v_hi words 8 .. 8 + 64 n_vhi (VHI only)
@@ -80,17 +81,16 @@ template <int HIMODE, bool VHI, bool PRUNE>
 __device__ inline void issue_group(const kvq_cache& c, size_t rec, uint8_t* slot, int lane,
                                    uint32_t kmask, int kept0, int nh, int nvhi) {
   using C = SlotCfg<HIMODE, VHI>;
-  // k_lo: lane l holds words 4l .. 4l+3: tokens 4 (l % 4) .. +3 of the 16-channel
-  // run u = (l / 4) % 2 of key chunk (l / 8) % 4, tile half l / 32
+  // k_lo: lane l holds words 4l .. 4l+3: tokens 4 (l % 4) .. +3 of tile half
+  // (l / 4) % 2 of the 16-channel run l / 8 (128 bytes per run)
   int lk = lane;
-  if (PRUNE && !((kmask >> ((lane >> 2) & 7)) & 1u)) lk = (lane & ~28) | (kept0 << 2);
+  if (PRUNE && !((kmask >> (lane >> 3)) & 1u)) lk = (lane & 7) | (kept0 << 3);
   dma16<CPOL_NT>((const uint8_t*)c.k_lo + rec * 1024 + lk * 16, slot + C::KLO);
-  // metadata: lanes 0..31 k_meta (0..15 scales, 16..31 zeros of channels
-  // 8 (l % 16) .. +7, run (l % 16) / 2), lanes 32..63 v_meta
+  // metadata: lanes 0..31 k_meta (64 bytes per 16-channel run: lanes 4w,
+  // 4w+1 its scales, 4w+2, 4w+3 its zeros), lanes 32..63 v_meta
   {
     int lm = lane;
-    if (PRUNE && lane < 32 && !((kmask >> ((lane & 15) >> 1)) & 1u))
-      lm = (lane & 16) | (kept0 << 1) | (lane & 1);
+    if (PRUNE && lane < 32 && !((kmask >> (lane >> 2)) & 1u)) lm = (lane & 3) | (kept0 << 2);
     const uint8_t* src = lane < 32 ? (const uint8_t*)c.k_meta + rec * 512 + lm * 16
                                    : (const uint8_t*)c.v_meta + rec * 512 + (lane - 32) * 16;
     dma16<CPOL_NT>(src, slot + C::META);

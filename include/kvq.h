@@ -106,10 +106,10 @@ typedef struct {
  * A 2-bit code at position p occupies bits [2p, 2p+2) of a little-endian
  * 32-bit word (of a 16-bit half-word for v_codes).
  *
- *  k_lo    [B][Hkv][NG][256] u32: word ((T*4 + kq)*2 + u)*16 + r holds,
- *          for the token at tile index 16T + r, channels 16w .. 16w+15 with
- *          w = 2kq + u, channel 16w + c at position pi(c) (so each 16-channel
- *          run of 16 tokens is 64 contiguous bytes).  The stored digit
+ *  k_lo    [B][Hkv][NG][256] u32: word (w*2 + T)*16 + r holds, for the
+ *          token at tile index 16T + r, channels 16w .. 16w+15 (w = 0..7),
+ *          channel 16w + c at position pi(c): each 16-channel run of the
+ *          group is 128 contiguous bytes.  The stored digit
  *          is the 2-bit code of a 2-bit channel, the code (0 or 1) of a
  *          1-bit channel, the low two bits of the code of a 4-bit channel,
  *          and 0 for a 16-bit channel.
@@ -119,8 +119,9 @@ typedef struct {
  *          position pi(d).  bits_hi == 16: [B][Hkv][NG][32][2*n_pairs_hi]
  *          16-bit raw values, tile order, salient channels ascending.
  *          Zero bytes when n_pairs_hi == 0.
- *  k_meta  [B][Hkv][NG][2][128] fp16: scale s[c] then zero z[c] per channel,
- *          natural channel order; 0 for 16-bit channels.
+ *  k_meta  [B][Hkv][NG][8][2][16] fp16: per 16-channel run w, the scales
+ *          s[16w + c] (c = 0..15), then the zeros z[16w + c]; 0 for 16-bit
+ *          channels.
  *  v_codes [B][Hkv][NG][256] u32: word (j*4 + kq)*16 + c holds channel
  *          32j + c in bits 0..15 and channel 32j + 16 + c in bits 16..31;
  *          token 8*kq + i of the group at position pi(i) of that half.

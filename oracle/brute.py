@@ -77,7 +77,7 @@ def unpack_keys(k_lo, k_hi, k_meta, salient: list[int], bits_hi: int):
         for c in range(D):
             w = c // 16
             kq, u = divmod(w, 2)
-            word = k_lo[((T * 4 + kq) * 2 + u) * 16 + r]
+            word = k_lo[((kq * 2 + u) * 2 + T) * 16 + r]
             codes[c, t] = _code(word, _pos(c % 16))
     raw = None
     if salient and bits_hi == 4:
@@ -93,8 +93,8 @@ def unpack_keys(k_lo, k_hi, k_meta, salient: list[int], bits_hi: int):
         for t in range(GS):
             e = _tile_index(t)
             raw[:, t] = vals[e * n:(e + 1) * n]
-    meta = np.asarray(k_meta, np.uint16)
-    return codes, raw, meta[:D].copy(), meta[D:].copy()
+    meta = np.asarray(k_meta, np.uint16).reshape(8, 2, 16)  # run, (scale, zero), channel
+    return codes, raw, meta[:, 0].reshape(D).copy(), meta[:, 1].reshape(D).copy()
 
 
 def _v_digits(words, base: int, nslot: int, slot: int):

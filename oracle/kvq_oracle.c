@@ -527,7 +527,7 @@ static int pos_swap(int c) { return (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1); 
 
 /* Packs the logical key codes of groups [0, ng) into the byte records.
  * k_lo [..][NG][256] u32, k_hi (4-bit: [..][NG][32] u32; 16-bit:
- * [..][NG][32][2*n_hi] u16 raw), k_meta [..][NG][2][128] u16. */
+ * [..][NG][32][2*n_hi] u16 raw), k_meta [..][NG][8][2][16] u16. */
 /* Key records in the group's token order: tile index e holds the token at
  * slot tile_token(e), i.e. position order[tile_token(e)]. */
 int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
@@ -553,7 +553,7 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
             int w = c / 16, kq = w / 2, u = w % 2;
             int bits = orc_channel_bits(pr, n_hi, bits_hi, n_lo1, 2, c);
             uint32_t digit = bits == 16 ? 0u : (uint32_t)(cg[c * GS + t] & 3);
-            size_t word = ((size_t)(Tt * 4 + kq) * 2 + u) * 16 + r;
+            size_t word = ((size_t)(kq * 2 + u) * 2 + Tt) * 16 + r;
             lo[word] |= digit << (2 * pos_swap(c % 16));
           }
         }
@@ -575,8 +575,8 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
         }
         uint16_t *meta = k_meta + grp * 256;
         for (int c = 0; c < D; c++) {
-          meta[c] = s[grp * D + c];
-          meta[D + c] = z[grp * D + c];
+          meta[(c / 16) * 32 + c % 16] = s[grp * D + c];
+          meta[(c / 16) * 32 + 16 + c % 16] = z[grp * D + c];
         }
       }
     }
