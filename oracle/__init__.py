@@ -151,14 +151,18 @@ class Quantized:
 
 def quantize(k, v, T: int, pairs, *, residual: int, n_pairs_hi: int,
              bits_hi: int, io_dtype: str, ng: int | None = None,
-             n_pairs_lo1: int = 0, n_vblk_hi: int = 0, bits_vhi: int = 4) -> Quantized:
+             n_pairs_lo1: int = 0, n_vblk_hi: int = 0, bits_vhi: int = 4,
+             prog_w8: int = 0, prog_w4: int = 0) -> Quantized:
     """Quantize keys and values of the first T tokens (k, v
     [B][Hkv][Tstride][128] bits) with the given rank table.  With n_vblk_hi >
     0 each group's tokens are ordered by descending key magnitude (``order``
     [B][Hkv][NG][32]: slot -> position; identity otherwise) and the values of
     the first 8 n_vblk_hi tokens in that order get bits_vhi bits, the rest 2
     bits (the SemKV reading).  Codes, scales and zeros stay in position
-    order."""
+    order.  prog_w4 > 0: progressive precision (the PM-KVQ reading of
+    orc_prog_keys): every group quantized at 8 bits, then shrunk to 4 and 2
+    bits by its age, the newest prog_w8 groups held at 8 bits and the newest
+    prog_w4 at 4 bits or more (no 1-bit pairs, one value precision)."""
     lib = _load()
     k = np.ascontiguousarray(k, dtype=np.uint16)
     v = np.ascontiguousarray(v, dtype=np.uint16)
@@ -172,23 +176,35 @@ def quantize(k, v, T: int, pairs, *, residual: int, n_pairs_hi: int,
     vc = np.zeros((B, Hkv, NG, GS, D), np.uint8)
     vs = np.zeros((B, Hkv, NG, GS, 4), np.uint16)
     vz = np.zeros((B, Hkv, NG, GS, 4), np.uint16)
-    rc = lib.orc_quant_keys(B, Hkv, _bf(io_dtype), _p(k), Tstride, int(T),
-                            int(residual), int(n_pairs_hi), int(bits_hi),
-                            int(n_pairs_lo1), _p(pairs), NG, _p(kc), _p(ks), _p(kz))
+    prog = prog_w4 > 0
+    assert not prog or (n_pairs_lo1 == 0 and n_vblk_hi == 0 and 0 <= prog_w8 <= prog_w4)
+    if prog:
+        rc = lib.orc_prog_keys(B, Hkv, _bf(io_dtype), _p(k), Tstride, int(T), int(residual),
+                               int(n_pairs_hi), int(bits_hi), _p(pairs), NG, int(prog_w8),
+                               int(prog_w4), _p(kc), _p(ks), _p(kz))
+    else:
+        rc = lib.orc_quant_keys(B, Hkv, _bf(io_dtype), _p(k), Tstride, int(T),
+                                int(residual), int(n_pairs_hi), int(bits_hi),
+                                int(n_pairs_lo1), _p(pairs), NG, _p(kc), _p(ks), _p(kz))
     assert rc == 0
     order = np.zeros((B, Hkv, NG, GS), np.uint8)
     rc = lib.orc_token_order(B, Hkv, _bf(io_dtype), _p(k), Tstride, int(T), int(residual),
                              NG, int(n_vblk_hi), _p(order))
     assert rc == 0
-    rc = lib.orc_quant_values(B, Hkv, _bf(io_dtype), _p(v), Tstride, int(T),
-                              int(residual), 2, NG, int(n_vblk_hi), int(bits_vhi),
-                              _p(order), _p(vc), _p(vs), _p(vz))
+    if prog:
+        rc = lib.orc_prog_values(B, Hkv, _bf(io_dtype), _p(v), Tstride, int(T), int(residual),
+                                 NG, int(prog_w8), int(prog_w4), _p(vc), _p(vs), _p(vz))
+    else:
+        rc = lib.orc_quant_values(B, Hkv, _bf(io_dtype), _p(v), Tstride, int(T),
+                                  int(residual), 2, NG, int(n_vblk_hi), int(bits_vhi),
+                                  _p(order), _p(vc), _p(vs), _p(vz))
     assert rc == 0
     return Quantized(k=k, v=v, T=int(T), R=int(residual), n_hi=int(n_pairs_hi),
                      bits_hi=int(bits_hi), n_lo1=int(n_pairs_lo1), io_dtype=io_dtype,
                      pairs=pairs,
                      NG=NG, nq=nq, kcodes=kc, ks=ks, kz=kz, vcodes=vc, vs=vs,
-                     vz=vz, n_vblk_hi=int(n_vblk_hi), bits_vhi=int(bits_vhi), order=order)
+                     vz=vz, n_vblk_hi=int(n_vblk_hi), bits_vhi=int(bits_vhi), order=order,
+                     prog_w8=int(prog_w8), prog_w4=int(prog_w4))
 
 
 def attention(qz: Quantized, q, sm_scale: float, with_lse: bool = False):
@@ -255,8 +271,33 @@ def pack(qz: Quantized) -> dict:
                  _p(ring_v))
     if k_hi_words(qz.n_hi, qz.bits_hi) == 0:
         k_hi = k_hi[..., :0]
+    w8, w4 = getattr(qz, "prog_w8", 0), getattr(qz, "prog_w4", 0)
+    nslot = w4 + 2 * w8
+    k_pl = np.zeros((B, Hkv, nslot, 256), np.uint32)
+    v_pl = np.zeros((B, Hkv, nslot, 256), np.uint32)
+    if w4 > 0:
+        lib.orc_pack_planes(B, Hkv, qz.T, qz.R, NG, w8, w4, _p(qz.kcodes), _p(qz.vcodes),
+                            _p(k_pl), _p(v_pl))
     return dict(k_lo=k_lo, k_hi=k_hi, k_meta=k_meta, v_codes=v_codes,
-                v_meta=v_meta, ring_k=ring_k, ring_v=ring_v, v_hi=v_hi)
+                v_meta=v_meta, ring_k=ring_k, ring_v=ring_v, v_hi=v_hi, k_pl=k_pl, v_pl=v_pl)
+
+
+def prog_width(age: int, w8: int, w4: int) -> int:
+    """Bits of a progressive group of the given age (0 = newest)."""
+    return int(_load().orc_prog_width(int(age), int(w8), int(w4)))
+
+
+def live_plane_slots(T: int, R: int, w8: int, w4: int):
+    """(group, plane slot) of every digit plane a progressive cache holds
+    with T tokens: digit 1 of the groups younger than w4 at slot g % w4,
+    digits 2 and 3 of those younger than w8 at w4 + 2 (g % w8) and the next."""
+    ng = n_quant(T, R) // GS
+    out = []
+    for g in range(max(ng - w4, 0), ng):
+        out.append((g, g % w4))
+        if ng - 1 - g < w8:
+            out += [(g, w4 + 2 * (g % w8)), (g, w4 + 2 * (g % w8) + 1)]
+    return out
 
 
 def live_ring_slots(T: int, R: int) -> np.ndarray:

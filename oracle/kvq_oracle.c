@@ -16,6 +16,9 @@
  *     values, recent tokens at 16 bits);
  *   - affine quantizer with scale and zero point (SemKV, abstract);
  *   - per-token 2-bit values (MixKVQ, abstract);
+ *   - progressive precision (PM-KVQ review, lead and key_machinery): codes
+ *     held at 8 bits first and shrunk in place to 4 and 2 bits as their group
+ *     ages, by the equivalent right shift (orc_prog_keys / orc_prog_values);
  *   - decode attention: the textbook softmax(scale * q.k) . v over the
  *     dequantized cache, unsplit, in fp64.
  * Floating point follows IEEE binary32 / binary64 exactly (build with
@@ -28,7 +31,8 @@
  *   K groups = 32 tokens of one channel; V groups = 32 channels of one token;
  *   n_q(T) = 32 * floor(max(0, T - R) / 32) quantized tokens, the rest raw;
  *   the rules of orc_select_qa, orc_prune_chunks and orc_token_order, which
- *   the pages describe without a formula.
+ *   the pages describe without a formula;
+ *   the age rule of progressive precision and the fp16 step after a shrink.
  *
  * Parity unpinned: orc_select_qa, orc_prune_chunks and orc_token_order have
  * no value the pages fix.  Their tests pin each to its own stated rule
@@ -563,7 +567,7 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
           for (int e = 0; e < 32; e++) {
             int t = ord[tile_token(e)];
             for (int d = 0; d < nh; d++)
-              hi[e] |= (uint32_t)(cg[hil[d] * GS + t] >> 2) << (2 * pos_swap(d));
+              hi[e] |= (uint32_t)((cg[hil[d] * GS + t] >> 2) & 3) << (2 * pos_swap(d));
           }
         } else if (nh && bits_hi == 16) {
           uint16_t *hi = (uint16_t *)k_hi + grp * 32 * nh;
@@ -639,6 +643,135 @@ int orc_pack_values(int B, int Hkv, int T, int R, int NG, const uint8_t *codes,
             meta[j * 32 + sl] = s[(grp * GS + ord[sl]) * 4 + j];
             meta[128 + j * 32 + sl] = z[(grp * GS + ord[sl]) * 4 + j];
           }
+      }
+  return 0;
+}
+
+/* ------------------------------------------------- progressive precision */
+
+/* PM-KVQ review (lead, key_machinery, referee report summary): the cache is
+ * held at 16 bits first and then at ever fewer bits as it ages, 8, 4, 2, each
+ * step shrinking a 2b-bit code to b bits in place (orc_shrink_code: zero point
+ * kept, step times 2^b + 1).  Readings:
+ *   - a quantized group's width follows its age a = ng - 1 - g among the ng
+ *     quantized groups of its (sequence, KV head): 8 bits while a < W8, 4 bits
+ *     while a < W4, then the layout's final width (2 bits; salient 4-bit
+ *     channels stop at 4; 16-bit channels stay raw);
+ *   - every group is quantized at 8 bits first (the 16 -> 8 step is the
+ *     quantizer itself, L = 255), then shrunk through the chain;
+ *   - the step after a shrink is stored as fp16(s (2^b + 1)), the product
+ *     exact in fp32 and rounded once to nearest even. */
+int orc_prog_width(int age, int W8, int W4) { return age < W8 ? 8 : (age < W4 ? 4 : 2); }
+
+/* One shrink of n codes sharing the scale *s, from 2b to b bits. */
+static void orc_prog_step(uint8_t *codes, int n, uint16_t *s, int b) {
+  for (int i = 0; i < n; i++) codes[i] = (uint8_t)orc_shrink_code(codes[i], b);
+  *s = orc_f32_to_half((float)orc_half_to_f64(*s) * (float)((1 << b) + 1));
+}
+
+/* Keys of a progressive cache: as orc_quant_keys (no 1-bit pairs), but every
+ * quantized channel at 8 bits first, then shrunk by the group's age. */
+int orc_prog_keys(int B, int Hkv, int bf16, const uint16_t *k, int Tstride, int T, int R,
+                  int n_hi, int bits_hi, const int32_t *pairs, int NG, int W8, int W4,
+                  uint8_t *codes, uint16_t *s, uint16_t *z) {
+  int ng = orc_n_quant(T, R) / GS;
+  if (ng > NG || W8 < 0 || W4 < W8) return -1;
+  float x[GS];
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++) {
+      const int32_t *pr = pairs + (size_t)(b * Hkv + kh) * NPAIR;
+      for (int g = 0; g < ng; g++) {
+        int w = orc_prog_width(ng - 1 - g, W8, W4);
+        for (int c = 0; c < D; c++) {
+          size_t slot = ((size_t)(b * Hkv + kh) * NG + g) * D + c;
+          int bits = orc_channel_bits(pr, n_hi, bits_hi, 0, 2, c);
+          if (bits == 16) {
+            memset(codes + slot * GS, 0, GS);
+            s[slot] = z[slot] = 0;
+            continue;
+          }
+          for (int i = 0; i < GS; i++)
+            x[i] = (float)to_f64(k[(((size_t)b * Hkv + kh) * Tstride + g * GS + i) * D + c], bf16);
+          orc_quant_group(x, 255, s + slot, z + slot, codes + slot * GS);
+          if (w <= 4) orc_prog_step(codes + slot * GS, GS, s + slot, 4);
+          if (w == 2 && bits == 2) orc_prog_step(codes + slot * GS, GS, s + slot, 2);
+        }
+      }
+    }
+  return 0;
+}
+
+/* Values of a progressive cache: each token's 32-channel groups at 8 bits
+ * first, then shrunk by the group's age down to 2 bits. */
+int orc_prog_values(int B, int Hkv, int bf16, const uint16_t *v, int Tstride, int T, int R,
+                    int NG, int W8, int W4, uint8_t *codes, uint16_t *s, uint16_t *z) {
+  int ng = orc_n_quant(T, R) / GS;
+  if (ng > NG || W8 < 0 || W4 < W8) return -1;
+  float x[GS];
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++)
+      for (int g = 0; g < ng; g++) {
+        int w = orc_prog_width(ng - 1 - g, W8, W4);
+        for (int t = 0; t < GS; t++) {
+          size_t tok = ((size_t)(b * Hkv + kh) * NG + g) * GS + t;
+          const uint16_t *row = v + (((size_t)b * Hkv + kh) * Tstride + g * GS + t) * D;
+          for (int j = 0; j < D / GS; j++) {
+            uint8_t *cj = codes + tok * D + j * GS;
+            for (int i = 0; i < GS; i++) x[i] = (float)to_f64(row[j * GS + i], bf16);
+            orc_quant_group(x, 255, s + tok * 4 + j, z + tok * 4 + j, cj);
+            if (w <= 4) orc_prog_step(cj, GS, s + tok * 4 + j, 4);
+            if (w == 2) orc_prog_step(cj, GS, s + tok * 4 + j, 2);
+          }
+        }
+      }
+  return 0;
+}
+
+/* Digit planes of the groups held above 2 bits.  Digit d of a code X is
+ * (X >> 2d) & 3; k_lo / v_codes hold digit 0 of every group.  k_pl
+ * [B][Hkv][W4 + 2 W8][256] u32: digit 1 of group g (age < W4) at plane slot
+ * g mod W4, digits 2 and 3 of group g (age < W8) at slots W4 + 2 (g mod W8)
+ * and the one after, each in the k_lo word format; v_pl the same in the
+ * v_codes word format.  Slots of no live wide group are left as they are. */
+int orc_pack_planes(int B, int Hkv, int T, int R, int NG, int W8, int W4,
+                    const uint8_t *kcodes, const uint8_t *vcodes, uint32_t *k_pl,
+                    uint32_t *v_pl) {
+  int ng = orc_n_quant(T, R) / GS;
+  size_t nslot = (size_t)W4 + 2 * (size_t)W8;
+  for (int b = 0; b < B; b++)
+    for (int kh = 0; kh < Hkv; kh++)
+      for (int g = 0; g < ng; g++) {
+        int age = ng - 1 - g;
+        if (age >= W4) continue;
+        size_t grp = (size_t)(b * Hkv + kh) * NG + g;
+        const uint8_t *kc = kcodes + grp * D * GS; /* [channel][token] */
+        const uint8_t *vc = vcodes + grp * GS * D; /* [token][channel] */
+        for (int d = 1; d <= (age < W8 ? 3 : 1); d++) {
+          size_t ps = d == 1 ? (size_t)(g % W4) : (size_t)W4 + 2 * (size_t)(g % W8) + (d - 2);
+          uint32_t *kp = k_pl + ((size_t)(b * Hkv + kh) * nslot + ps) * 256;
+          uint32_t *vp = v_pl + ((size_t)(b * Hkv + kh) * nslot + ps) * 256;
+          memset(kp, 0, 256 * 4);
+          memset(vp, 0, 256 * 4);
+          for (int e = 0; e < 32; e++) {
+            int t = tile_token(e), Tt = e / 16, r = e % 16;
+            for (int c = 0; c < D; c++) {
+              uint32_t digit = (uint32_t)(kc[c * GS + t] >> (2 * d)) & 3u;
+              kp[((size_t)(c / 16) * 2 + Tt) * 16 + r] |= digit << (2 * pos_swap(c % 16));
+            }
+          }
+          for (int j = 0; j < 4; j++)
+            for (int kq = 0; kq < 4; kq++)
+              for (int c = 0; c < 16; c++) {
+                uint32_t w = 0;
+                for (int i = 0; i < 8; i++) {
+                  int t = 8 * kq + i;
+                  w |= ((uint32_t)(vc[t * D + 32 * j + c] >> (2 * d)) & 3u) << (2 * pos_swap(i));
+                  w |= ((uint32_t)(vc[t * D + 32 * j + 16 + c] >> (2 * d)) & 3u)
+                       << (16 + 2 * pos_swap(i));
+                }
+                vp[(j * 4 + kq) * 16 + c] = w;
+              }
+        }
       }
   return 0;
 }
