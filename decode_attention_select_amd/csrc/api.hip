@@ -82,9 +82,9 @@ void log_launch(const char* call, const Geo& g, int T, int splits, int keep) {
   if (!log_on()) return;
   fprintf(stderr,
           "kvq: %s B=%d Hq=%d Hkv=%d G=%d T=%d R=%d groups<=%d n_hi=%d bits_hi=%d n_lo1=%d "
-          "n_vhi=%d io=%s splits=%d keep=%d\n",
+          "n_vhi=%d w8=%d w4=%d io=%s splits=%d keep=%d\n",
           call, g.B, g.Hq, g.Hkv, g.G, T, g.R, g.NG, g.n_hi, g.bits_hi, g.n_lo1, g.n_vhi,
-          g.bf16 ? "bf16" : "fp16", splits, keep);
+          g.w8, g.w4, g.bf16 ? "bf16" : "fp16", splits, keep);
 }
 
 kvq_status check_layout(const kvq_layout* L) {
@@ -102,6 +102,8 @@ kvq_status check_layout(const kvq_layout* L) {
   if (L->io_dtype != KVQ_FP16 && L->io_dtype != KVQ_BF16) return KVQ_EINVAL;
   if (L->n_vblk_hi < 0 || L->n_vblk_hi > 4) return KVQ_EINVAL;
   if (L->n_vblk_hi > 0 && L->bits_vhi != 3 && L->bits_vhi != 4) return KVQ_ENOTSUP;
+  if (L->prog_w8 < 0 || L->prog_w4 < L->prog_w8 || L->prog_w4 > 256) return KVQ_EINVAL;
+  if (L->prog_w4 > 0 && (L->n_pairs_lo1 > 0 || L->n_vblk_hi > 0)) return KVQ_ENOTSUP;
   return KVQ_OK;
 }
 
@@ -124,6 +126,9 @@ Geo make_geo(const kvq_layout* L) {
   g.n_vhi = L->n_vblk_hi;
   g.bits_vhi = g.n_vhi ? L->bits_vhi : 2;
   g.vhi_words = g.n_vhi ? 8 + 64 * g.n_vhi : 0;
+  g.w4 = L->prog_w4;
+  g.w8 = g.w4 > 0 ? L->prog_w8 : 0;
+  g.npl = g.w4 + 2 * g.w8;
   return g;
 }
 
@@ -147,6 +152,10 @@ kvq_status check_cache(const Geo& g, const kvq_cache* c, bool need_groups) {
       if (kvq_status s = check_ptr(c->k_hi)) return s;
     if (g.vhi_words)
       if (kvq_status s = check_ptr(c->v_hi)) return s;
+    if (g.npl) {
+      if (kvq_status s = check_ptr(c->k_pl)) return s;
+      if (kvq_status s = check_ptr(c->v_pl)) return s;
+    }
   }
   return KVQ_OK;
 }
@@ -178,6 +187,8 @@ kvq_status kvq_cache_sizes(const kvq_layout* L, size_t sizes[KVQ_NBUF]) {
   sizes[9] = bh * 2 * NPAIR * 8;     // sums
   sizes[10] = 4;                     // err
   sizes[11] = grp * g.vhi_words * 4; // v_hi
+  sizes[12] = g.NG > 0 ? bh * g.npl * GROUP_WORDS * 4 : 0;  // k_pl
+  sizes[13] = sizes[12];             // v_pl
   return KVQ_OK;
 }
 
@@ -254,6 +265,7 @@ kvq_status kvq_shrink(const kvq_layout* L, kvq_cache* cache, int32_t g0, int32_t
   if (kvq_status s = check_layout(L)) return s;
   const Geo g = make_geo(L);
   if (g.n_hi > 0 && g.bits_hi != 4) return KVQ_ENOTSUP;
+  if (g.w4 > 0) return KVQ_ENOTSUP;
   if (g0 < 0 || g1 < g0) return KVQ_EINVAL;
   if (kvq_status s = check_cache(g, cache, true)) return s;
   if (g.NG > 0 && g1 > g.NG) g1 = g.NG;
@@ -275,6 +287,7 @@ static kvq_status decode_common(const kvq_layout* L, const void* q, const kvq_ca
   if (ws_bytes < need) return KVQ_ECAPACITY;
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_EINVAL;
   if (keep < 0 || keep > 8) return KVQ_EINVAL;
+  if (g.w4 > 0 && keep != 8) return KVQ_ENOTSUP;
   if (kvq_status s = check_ptr(q)) return s;
   if (kvq_status s = check_ptr(out)) return s;
   if (kvq_status s = check_ptr(workspace)) return s;
@@ -331,6 +344,7 @@ kvq_status kvq_read_ceiling(const kvq_layout* L, const kvq_cache* cache, int32_t
   const Geo g = make_geo(L);
   size_t need = 0;
   if (kvq_status s = kvq_workspace_bytes(L, n_splits, &need)) return s;  // n_splits limits
+  if (g.w4 > 0) return KVQ_ENOTSUP;
   if (kvq_status s = check_ptr(sink)) return s;
   if (kvq_status s = check_cache(g, cache, true)) return s;
   log_launch("kvq_read_ceiling", g, -1, n_splits, 8);

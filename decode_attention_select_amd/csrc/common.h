@@ -29,7 +29,20 @@ struct Geo {
   int khi_bytes;       // bytes of the salient section per group
   int n_vhi, bits_vhi; // value blocks at the higher precision, their bits
   int vhi_words;       // u32 words of a group's v_hi record (0 when n_vhi == 0)
+  int w8, w4;          // progressive precision: groups younger than w8 at 8 bits,
+                       // younger than w4 at 4 or more (w4 == 0: off)
+  int npl;             // digit-plane slots per (b, kv head): w4 + 2 w8
 };
+
+// Bits of a progressive group of age a (0 = the newest quantized group).
+__host__ __device__ inline int prog_width(int a, int w8, int w4) {
+  return a < w8 ? 8 : (a < w4 ? 4 : 2);
+}
+
+// The equivalent right shift: a 2b-bit code X on the b-bit grid of step
+// s (2^b + 1), round(X / (2^b + 1)) = ((2^2b - 2^b + 1)(X + 2^(b-1))) >> 3b.
+__host__ __device__ inline uint32_t ers4(uint32_t x) { return (241u * (x + 8u)) >> 12; }
+__host__ __device__ inline uint32_t ers2(uint32_t x) { return (13u * (x + 2u)) >> 6; }
 
 // Quantized tokens for T held tokens: 32 * floor(max(0, T - R) / 32).
 __host__ __device__ inline int n_quant(int T, int R) {

@@ -137,6 +137,13 @@ __device__ inline uint32_t cvt2x4(uint32_t w) {
   return h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 8.0f, BYTE));
 }
 
+// ... and with the digit times sc / 2 (sc a power of two: digit d of a
+// progressive code takes sc = 2 * 4^d)
+template <int BYTE>
+__device__ inline uint32_t cvt2s(uint32_t w, float sc) {
+  return h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, BYTE));
+}
+
 __device__ inline f4 mma_f16(u4 a, u4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a),
                                                 __builtin_bit_cast(h8, b), c, 0, 0, 0);
@@ -347,7 +354,19 @@ struct Lds {
 // 15 - h; lane (col, kq) serves head col (col < G) or 15 - col (col >= 16 -
 // G).  Logits and outputs add the two columns (a row_mirror DPP).  Without
 // it (G > 8, every column taken) hi and lo take an MFMA each.
-template <bool BF16, int HIMODE, bool HASQ, int KB, bool VHI, bool FUSED, bool LOCOL>
+// PROG: progressive precision (PM-KVQ review, lead and key_machinery: codes
+// held at more bits while young and shrunk as they age).  The g.w4 newest
+// groups (8 or 4 bits) are "window" items: after the ring blocks, in the
+// same round robin over the waves, each is copied with its digit planes
+// (digit d of a code (X >> 2d) & 3; plane d enters the MFMA with the weight
+// 4^d through the convert's scale) into the wave's free slots and attended
+// there; the stream takes the older (2-bit) groups only.
+template <bool B>
+struct Wide {
+  static constexpr bool value = B;
+};
+template <bool BF16, int HIMODE, bool HASQ, int KB, bool VHI, bool FUSED, bool LOCOL,
+          bool PROG = false>
 __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             kvq_cache c, float scale_log2, int S,
                                                             Ws ws, uint16_t* __restrict__ out,
@@ -357,6 +376,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   constexpr bool PRUNE = KB > 0;
   using SC = SlotCfg<HIMODE, VHI>;
   constexpr int NSLOT = SC::NSLOT, NLD = SC::NLD, SLOTB = SC::BYTES;
+  static_assert(!PROG || (NSLOT >= 3 && SLOTB >= 3072 && !PRUNE && !VHI && !FUSED),
+                "a window group takes three slots: its record and three planes per side");
   __shared__ Lds<SLOTB, NSLOT> lds;
   // the wave index is wave-uniform: keeping it in a scalar register makes every
   // group address scalar (one 64-bit base per copy, no per-lane address math)
@@ -400,6 +421,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int STR = S * NW;           // flat indices of one (sequence, KV head)
   const int f = s + S * wave;       // this wave's flat index
   const bool ring_owner = f < RSB;  // owns physical ring blocks f, f + STR, ... < RSB
+  // PROG: flat items RSB .. NBLK - 1 are the window groups (age f - RSB)
+  const int NBLK = RSB + (PROG ? g.w4 : 0);
+  const bool blk_owner = f < NBLK;
   // quantized groups of this wave: g_i = gfirst + i STR (the first such index
   // >= 0), copied into slot i % NSLOT.  The first NSLOT copies go out at
   // once, a fixed number (past the capacity the index is clamped into it;
@@ -407,7 +431,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // reused).  A ring-owning wave first loads and attends its ring blocks (in
   // vector registers) and issues its copies after that.
   const size_t rec0 = (size_t)bh * g.NG;
-  const int gfirst = f - RSB + (ring_owner ? (RSB - f + STR - 1) / STR * STR : 0);
+  const int gfirst = f - NBLK + (blk_owner ? (NBLK - f + STR - 1) / STR * STR : 0);
   uint8_t* slots = &lds.u.slots[wave][0][0];
   int issued = 0;
   // kept 16-channel key runs (bit s: run s; all eight unless PRUNE) and the
@@ -449,8 +473,10 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       for (int tt = 0; tt < 8; tt++) vnk[tt] = vnew[(size_t)bh * D + 16 * tt + col];
     }
     wait_vmcnt<0>();
-  } else if constexpr (PRUNE) {
-    wait_vmcnt<0>();  // the query; the group copies wait for the kept runs
+  } else if (PRUNE || blk_owner) {
+    // the query; PRUNE: the group copies wait for the kept runs; a window
+    // owner first takes its window groups into its slots
+    wait_vmcnt<0>();
   } else {
     issue_first();
     wait_vmcnt<HASQ ? NSLOT * NLD : 0>();  // the query copies (issued before the group copies)
@@ -557,7 +583,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int nq = n_quant(T_old, g.R), ngq = nq / GS;  // FUSED: the prefix before the append
   const int nr = T - nq;                               // raw (ring) tokens, <= RS
   // this wave's live groups: g_i < ngq
-  const int nmine = (HASQ && gfirst < ngq) ? (ngq - 1 - gfirst) / STR + 1 : 0;
+  // PROG: the stream takes groups [0, n2), the window the rest
+  const int nwin = PROG ? min(g.w4, ngq) : 0, n2 = ngq - nwin;
+  const int nmine = (HASQ && gfirst < n2) ? (n2 - 1 - gfirst) / STR + 1 : 0;
 
   uint32_t qhi[4] = {0, 0, 0, 0};  // HIMODE 4: 4*q (fp16); HIMODE 16: raw q
   int sal_ch = 0;                  // HIMODE 4: salient channel whose scale lane%16 copies
@@ -679,8 +707,13 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     for (int i = 0; i < 8; i++) p[i] = ex2(fmaf(cc[i], sc, -m_run));
   };
 
-  // One quantized group, its records in `slot` (copies landed).
-  auto process_group = [&](const uint8_t* slot) {
+  // One quantized group, its records in `slot` (copies landed).  WIDE (a
+  // window group of `width` 4 or 8 bits): digit planes 1.. of its keys at
+  // kpl + 1024 (d - 1), of its values at vpl + 1024 (d - 1); plane 1 holds
+  // the salient channels' digit 1 too, so the k_hi term is left out.
+  auto process_group = [&](const uint8_t* slot, auto wide_tag, int width, const uint8_t* kpl,
+                           const uint8_t* vpl) {
+    constexpr bool WIDE = decltype(wide_tag)::value;
     const uint32_t* sm = (const uint32_t*)(slot + SC::META);
     // keys: q' = q * s as an exact fp16 pair (qs + qsl), bias = q . z (the
     // same for every token row); each tile's accumulator starts from the
@@ -733,7 +766,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       for (int r = 0; r < 4; r++) cb[r] = lo_lane ? 0.0f : cb[r];
     }
     uint32_t qshi[4];
-    if constexpr (HIMODE == 4) {
+    if constexpr (HIMODE == 4 && !WIDE) {
       // the salient channels' scales, gathered once into a contiguous row
       // (lane l copies digit l%16), then read 8 at a time
       uint16_t* ss = lds.sal_s[wave];
@@ -783,8 +816,31 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
             acc = mma_f16(c1, u4{qsl[k0 + 4], qsl[k0 + 5], qsl[k0 + 6], qsl[k0 + 7]}, acc);
           }
         }
+        if constexpr (WIDE) {
+          // digits 1 (and 2, 3) of every channel, weighted 4^d by the convert
+#pragma unroll
+          for (int d = 1; d <= 3; d++) {
+            if (d > 1 && width < 8) break;
+            const float sc = (float)(2 << (2 * d));
+            const uint32_t* pw0 = (const uint32_t*)(kpl + (d - 1) * 1024) + (kqa * 4 + TT) * 16 + col;
+            const u2 wp = u2{pw0[0], pw0[32]};
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+              const uint32_t A = wp[u] & 0x33333333u, Bn = (wp[u] >> 2) & 0x33333333u;
+              const int k0 = 8 * u;
+              const u4 c0 = u4{cvt2s<0>(A, sc), cvt2s<0>(Bn, sc), cvt2s<1>(A, sc), cvt2s<1>(Bn, sc)};
+              const u4 c1 = u4{cvt2s<2>(A, sc), cvt2s<2>(Bn, sc), cvt2s<3>(A, sc), cvt2s<3>(Bn, sc)};
+              acc = mma_f16(c0, u4{qs[k0], qs[k0 + 1], qs[k0 + 2], qs[k0 + 3]}, acc);
+              acc = mma_f16(c1, u4{qs[k0 + 4], qs[k0 + 5], qs[k0 + 6], qs[k0 + 7]}, acc);
+              if constexpr (!LOCOL) {
+                acc = mma_f16(c0, u4{qsl[k0], qsl[k0 + 1], qsl[k0 + 2], qsl[k0 + 3]}, acc);
+                acc = mma_f16(c1, u4{qsl[k0 + 4], qsl[k0 + 5], qsl[k0 + 6], qsl[k0 + 7]}, acc);
+              }
+            }
+          }
+        }
       }
-      if constexpr (HIMODE == 4) {
+      if constexpr (HIMODE == 4 && !WIDE) {
         const uint32_t kw = ((const uint32_t*)(slot + SC::KHI))[16 * TT + col];
         const uint32_t wsel = (kq & 1) ? kw >> 16 : kw;
         const uint32_t A = wsel & 0x33333333u, Bn = (wsel >> 2) & 0x33333333u;
@@ -850,6 +906,23 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       if constexpr (!LOCOL) {
         O[2 * j] = mma_f16(v0, pjl, O[2 * j]);
         O[2 * j + 1] = mma_f16(v1, pjl, O[2 * j + 1]);
+      }
+      if constexpr (WIDE) {
+#pragma unroll
+        for (int d = 1; d <= 3; d++) {
+          if (d > 1 && width < 8) break;
+          const float sc = (float)(2 << (2 * d));
+          const uint32_t wq = ((const uint32_t*)(vpl + (d - 1) * 1024))[(j * 4 + kq) * 16 + col];
+          const uint32_t Aq = wq & 0x33333333u, Bq = (wq >> 2) & 0x33333333u;
+          const u4 h0 = u4{cvt2s<0>(Aq, sc), cvt2s<0>(Bq, sc), cvt2s<1>(Aq, sc), cvt2s<1>(Bq, sc)};
+          const u4 h1 = u4{cvt2s<2>(Aq, sc), cvt2s<2>(Bq, sc), cvt2s<3>(Aq, sc), cvt2s<3>(Bq, sc)};
+          O[2 * j] = mma_f16(h0, pj, O[2 * j]);
+          O[2 * j + 1] = mma_f16(h1, pj, O[2 * j + 1]);
+          if constexpr (!LOCOL) {
+            O[2 * j] = mma_f16(h0, pjl, O[2 * j]);
+            O[2 * j + 1] = mma_f16(h1, pjl, O[2 * j + 1]);
+          }
+        }
       }
       if constexpr (VHI) {
         // block kq's high digits (0 past the high-precision blocks), weighted
@@ -954,7 +1027,36 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       O[tt] = mma_raw<BF16>(a, u4{Pl[0], Pl[1], Pl[2], Pl[3]}, O[tt]);
     }
   }
-  if (ring_owner) issue_first();
+  // ---- PROG: the window groups of this wave (flat items RSB .. NBLK - 1,
+  // age = item - RSB), each copied with its planes into the wave's slots 0
+  // (record), 1 (key planes) and 2 (value planes), attended, and drained
+  // before the slots take the stream's copies
+  if constexpr (PROG && HASQ) {
+    uint8_t* s1 = slots + SLOTB;
+    uint8_t* s2 = slots + 2 * SLOTB;
+    for (int it = ring_owner ? f + (RSB - f + STR - 1) / STR * STR : f; it < RSB + nwin;
+         it += STR) {
+      const int age = it - RSB, gw = ngq - 1 - age;
+      const int width = prog_width(age, g.w8, g.w4);
+      issue_group<HIMODE, VHI, false>(c, rec0 + gw, slots, lane, 0xFFu, 0, g.nh, g.n_vhi);
+      const size_t p1 = ((size_t)bh * g.npl + gw % g.w4) * 1024 + lane * 16;
+      dma16<CPOL_NT>((const uint8_t*)c.k_pl + p1, s1);
+      dma16<CPOL_NT>((const uint8_t*)c.v_pl + p1, s2);
+      if (width == 8) {
+        const size_t p23 = ((size_t)bh * g.npl + g.w4 + 2 * (gw % g.w8)) * 1024 + lane * 16;
+        dma16<CPOL_NT>((const uint8_t*)c.k_pl + p23, s1 + 1024);
+        dma16<CPOL_NT>((const uint8_t*)c.k_pl + p23 + 1024, s1 + 2048);
+        dma16<CPOL_NT>((const uint8_t*)c.v_pl + p23, s2 + 1024);
+        dma16<CPOL_NT>((const uint8_t*)c.v_pl + p23 + 1024, s2 + 2048);
+      }
+      wait_vmcnt<0>();
+      compiler_fence();
+      process_group(slots, Wide<true>{}, width, s1, s2);
+      wait_lgkmcnt0();  // every read of the slots has returned before they are refilled
+      compiler_fence();
+    }
+  }
+  if (blk_owner) issue_first();
   KVQ_STAMP(tid == 0, 2);
 
   // ---- the quantized groups: slot i % NSLOT holds group i; a consumed slot
@@ -963,7 +1065,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     for (int i = 0; i < nmine; i++) {
       wait_slot<NLD, NSLOT>(issued - 1 - i);
       uint8_t* slot = slots + (i % NSLOT) * SLOTB;
-      process_group(slot);
+      process_group(slot, Wide<false>{}, 2, nullptr, nullptr);
 #ifdef KVQ_STAMPS
       if (i == 0) KVQ_STAMP(tid == 0 && O[0][0] != 12345.0f, 11);
 #endif
@@ -1243,6 +1345,14 @@ struct Launch {
 template <bool BF16, int HIMODE, int KB, bool VHI, bool FUSED, bool LOCOL>
 static void launch_cols(const Geo& g, int keep, const Launch& a) {
   const dim3 grid(g.B * g.Hkv * a.S), block(WG_THREADS);
+  if constexpr (KB == 0 && !VHI && !FUSED) {
+    if (g.NG > 0 && g.w4 > 0) {
+      hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, 0, false, false, LOCOL, true>), grid,
+                         block, 0, a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,
+                         (uint16_t*)a.out, (const uint16_t*)a.knew, (const uint16_t*)a.vnew, keep);
+      return;
+    }
+  }
   if (g.NG > 0)
     hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, KB, VHI, FUSED, LOCOL>), grid, block,
                        0, a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,

@@ -71,11 +71,14 @@ __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint1
   const int grp = blockIdx.y * QWAVES + wave;
   if (grp >= n_quant(T, g.R) / GS) return;
   const size_t rec = (size_t)bh * g.NG + grp;
+  // progressive precision: the width of the group's age among n_q / 32
+  const int width = g.w4 > 0 ? prog_width(n_quant(T, g.R) / GS - 1 - grp, g.w8, g.w4) : 0;
   key_group_wave<BF, VHI>(g, k + ((size_t)bh * T + (size_t)grp * GS) * D,
                           pair_masks(g, c.pairs + (size_t)bh * NPAIR),
                           (uint32_t*)c.k_lo + rec * GROUP_WORDS,
                           (uint8_t*)c.k_hi + rec * g.khi_bytes, (uint16_t*)c.k_meta + rec * 2 * D,
-                          lds[wave]);
+                          lds[wave], width, width >= 4 ? plane1(g, c.k_pl, bh, grp) : nullptr,
+                          width == 8 ? plane23(g, c.k_pl, bh, grp) : nullptr);
   if constexpr (VHI)
     if (lane < 2) ((uint4*)(c.v_hi + rec * g.vhi_words))[lane] = ((const uint4*)lds[wave].ord)[lane];
 }
@@ -102,9 +105,12 @@ __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uin
     pos.x &= 0x1F1F1F1Fu;
     pos.y &= 0x1F1F1F1Fu;
   }
+  const int width = g.w4 > 0 ? prog_width(n_quant(T, g.R) / GS - 1 - grp, g.w8, g.w4) : 0;
   value_group_wave<BF, false, VHI>(g, v + ((size_t)bh * T + (size_t)grp * GS) * D, pos,
                                    (uint32_t*)c.v_codes + rec * GROUP_WORDS,
-                                   (uint16_t*)c.v_meta + rec * 2 * D, vhi);
+                                   (uint16_t*)c.v_meta + rec * 2 * D, vhi, width,
+                                   width >= 4 ? plane1(g, c.v_pl, bh, grp) : nullptr,
+                                   width == 8 ? plane23(g, c.v_pl, bh, grp) : nullptr);
 }
 
 // ------------------------------------------------------------------- append

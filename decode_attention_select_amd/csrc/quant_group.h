@@ -135,6 +135,7 @@ struct KeyLds {  // one wave's staging of a key-group record
     struct {
       uint32_t lo[GROUP_WORDS];
       uint32_t hi[256];  // 4-bit: 32 words; raw 16-bit: 32 tokens x up to 16 halves
+      uint32_t pl[3][GROUP_WORDS];  // progressive: digit planes 1..3
     };
     // two value precisions, before the record is staged: the group's 32 key
     // rows (16-byte pieces [row][cb]), then the partial scores [4][32]
@@ -192,10 +193,17 @@ __device__ void token_order_wave(const uint16_t* rows, uint32_t* ord) {
 // summed from the rows it holds), writes the order bytes to L.ord and takes
 // the rows in that order through the LDS tile, so the record's token index
 // is the slot (slot i = position L.ord[i]).
+// width > 0 (progressive precision, not with VHI): every quantized channel
+// is quantized at 8 bits, then shrunk to `width` bits (8, 4 or 2; salient
+// 4-bit channels stop at 4) by the equivalent right shift, its step
+// multiplied by 17, then 5, each product rounded to fp16; digit 0 goes to
+// lo_out, digit 1 of salient channels to hi_out, digit 1 of every channel to
+// pl1 (width >= 4) and digits 2, 3 to pl23 and pl23 + 256 (width 8).
 template <bool BF, bool VHI>
 __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
                                uint32_t* lo_out, uint8_t* hi_out, uint16_t* meta_out,
-                               KeyLds& L) {
+                               KeyLds& L, int width = 0, uint32_t* pl1 = nullptr,
+                               uint32_t* pl23 = nullptr) {
   const int lane = threadIdx.x & 63, cb = lane >> 2, tq = lane & 3;
   uint4 v[8];
 #pragma unroll
@@ -245,7 +253,7 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
     const bool sal = (hib >> k) & 1u, one = (oneb >> k) & 1u;
     dix[k] = dbase + __popc(hib & ((1u << k) - 1u));
     raw[k] = sal && g.bits_hi == 16;
-    lv[k] = sal ? 15.0f : (one ? 1.0f : 3.0f);
+    lv[k] = width > 0 ? 255.0f : (sal ? 15.0f : (one ? 1.0f : 3.0f));
     hish[k] = sal ? 2 * pos_swap(dix[k]) : 0;
   }
   // per-channel min / max over the 32 tokens
@@ -317,13 +325,40 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
   refresh(v);
   float hwf[8];
   uint32_t hw[8], hh[8];
+  uint32_t pw[3][8];  // progressive: digits 1..3 (half-words like hw)
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     hwf[i] = 0.0f;
     hh[i] = 0;
+    pw[0][i] = pw[1][i] = pw[2][i] = 0;
+  }
+  if (width > 0) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const float z = half_bits_to_f32((uint16_t)(sz[k] >> 16));
+      const int sh = 2 * pos_swap(k);
+      const bool salk = (hib >> k) & 1u;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        uint32_t X = (uint32_t)qcode(in_to_f32(half_of(v[i], k), BF), z, rr[k], 255.0f);
+        if (width <= 4) X = ers4(X);
+        if (width == 2 && !salk) X = ers2(X);
+        hwf[i] += (float)((X & 3u) << sh);
+        pw[0][i] |= ((X >> 2) & 3u) << sh;
+        pw[1][i] |= ((X >> 4) & 3u) << sh;
+        pw[2][i] |= (X >> 6) << sh;
+        if (bits4 && salk) hh[i] |= ((X >> 2) & 3u) << hish[k];
+      }
+      // the steps of the shrinks, each rounded once to fp16
+      uint32_t sb = sz[k] & 0xFFFFu;
+      if (width <= 4) sb = f32_to_half_bits(half_bits_to_f32((uint16_t)sb) * 17.0f);
+      if (width == 2 && !salk) sb = f32_to_half_bits(half_bits_to_f32((uint16_t)sb) * 5.0f);
+      sz[k] = (sz[k] & 0xFFFF0000u) | sb;
+    }
   }
 #pragma unroll
   for (int k = 0; k < 8; k++) {
+    if (width > 0) break;
     const float z = half_bits_to_f32((uint16_t)(sz[k] >> 16));
     const float mul = (float)(1u << (2 * pos_swap(k)));
     if (bits4 && __any(lv[k] == 15.0f)) {
@@ -350,8 +385,14 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const int T = i >> 2, r = 4 * tq + (i & 3);
-    ((uint16_t*)L.lo)[(((kq * 2 + u) * 2 + T) * 16 + r) * 2 + half] = (uint16_t)hw[i];
+    const int hx = (((kq * 2 + u) * 2 + T) * 16 + r) * 2 + half;
+    ((uint16_t*)L.lo)[hx] = (uint16_t)hw[i];
     if (bits4 && hh[i]) atomicOr(&L.hi[16 * T + r], hh[i]);
+    if (width >= 4) ((uint16_t*)L.pl[0])[hx] = (uint16_t)pw[0][i];
+    if (width == 8) {
+      ((uint16_t*)L.pl[1])[hx] = (uint16_t)pw[1][i];
+      ((uint16_t*)L.pl[2])[hx] = (uint16_t)pw[2][i];
+    }
   }
   if (raw16) {
 #pragma unroll
@@ -367,6 +408,11 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
   wave_lds_sync();
   ((uint4*)lo_out)[lane] = ((const uint4*)L.lo)[lane];
   if (lane < g.khi_bytes / 16) ((uint4*)hi_out)[lane] = ((const uint4*)L.hi)[lane];
+  if (width >= 4) ((uint4*)pl1)[lane] = ((const uint4*)L.pl[0])[lane];
+  if (width == 8) {
+    ((uint4*)pl23)[lane] = ((const uint4*)L.pl[1])[lane];
+    ((uint4*)pl23)[64 + lane] = ((const uint4*)L.pl[2])[lane];
+  }
   if (tq < 2) {
     uint32_t m[4];
 #pragma unroll
@@ -389,9 +435,12 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
 // slots below 8 n_vhi quantize at L = 2^bits_vhi - 1, and the high digits
 // of their codes go to vhi_out (the group's v_hi record) after its 8-word
 // order header, which the key side writes.
+// width > 0 (progressive precision, not with VHI): codes at 8 bits, shrunk
+// to `width` bits, digit planes 1..3 to pl1 / pl23, as for the keys.
 template <bool BF, bool CHMAJOR, bool VHI>
 __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint2 pos, uint32_t* vc_out,
-                                 uint16_t* meta_out, uint32_t* vhi_out) {
+                                 uint16_t* meta_out, uint32_t* vhi_out, int width = 0,
+                                 uint32_t* pl1 = nullptr, uint32_t* pl23 = nullptr) {
   const int lane = threadIdx.x & 63, cb = lane & 15, tq = lane >> 4, m = cb & 3, j = cb >> 2;
   auto pos_of = [&](int i) -> uint32_t {
     return ((i < 4 ? pos.x : pos.y) >> (8 * (i & 3))) & 0xFFu;
@@ -448,7 +497,7 @@ __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint2 pos, u
     }
   }
   const bool hiblk = VHI && tq < g.n_vhi;
-  const float Lv = hiblk ? (float)((1 << g.bits_vhi) - 1) : 3.0f;
+  const float Lv = width > 0 ? 255.0f : (hiblk ? (float)((1 << g.bits_vhi) - 1) : 3.0f);
   auto pick = [&](const float (&a)[8], int o) {
     return m == 0 ? a[o] : m == 1 ? a[2 + o] : m == 2 ? a[4 + o] : a[6 + o];
   };
@@ -468,10 +517,36 @@ __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint2 pos, u
   // (high-precision slots) split into a low digit here and a high digit in hh
   float hf[8], hhf[8];
   uint32_t h[8], hh[8];
+  uint32_t pw[3][8];  // progressive: digits 1..3 (half-words like h)
 #pragma unroll
-  for (int k = 0; k < 8; k++) hf[k] = hhf[k] = 0.0f;
+  for (int k = 0; k < 8; k++) {
+    hf[k] = hhf[k] = 0.0f;
+    pw[0][k] = pw[1][k] = pw[2][k] = 0;
+  }
+  if (width > 0) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float z = half_bits_to_f32((uint16_t)(sz[i] >> 16));
+      const int sh = 2 * pos_swap(i);
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        uint32_t X = (uint32_t)qcode(x(i, k), z, rr[i], 255.0f);
+        if (width <= 4) X = ers4(X);
+        if (width == 2) X = ers2(X);
+        hf[k] += (float)((X & 3u) << sh);
+        pw[0][k] |= ((X >> 2) & 3u) << sh;
+        pw[1][k] |= ((X >> 4) & 3u) << sh;
+        pw[2][k] |= (X >> 6) << sh;
+      }
+      uint32_t sb = sz[i] & 0xFFFFu;
+      if (width <= 4) sb = f32_to_half_bits(half_bits_to_f32((uint16_t)sb) * 17.0f);
+      if (width == 2) sb = f32_to_half_bits(half_bits_to_f32((uint16_t)sb) * 5.0f);
+      sz[i] = (sz[i] & 0xFFFF0000u) | sb;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 8; i++) {
+    if (width > 0) break;
     const float z = half_bits_to_f32((uint16_t)(sz[i] >> 16));
     const float mul = (float)(1u << (2 * pos_swap(i)));
 #pragma unroll
@@ -509,6 +584,16 @@ __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint2 pos, u
   words(h, wd);
   const int c0 = 8 * (m & 1) + 4 * (m >> 1);
   *(uint4*)(vc_out + (j * 4 + tq) * 16 + c0) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  if (width >= 4) {
+#pragma unroll
+    for (int d = 0; d < 3; d++) {
+      if (d > 0 && width < 8) break;
+      uint32_t wp[4];
+      words(pw[d], wp);
+      uint32_t* dst = d == 0 ? pl1 : pl23 + (d - 1) * GROUP_WORDS;
+      *(uint4*)(dst + (j * 4 + tq) * 16 + c0) = make_uint4(wp[0], wp[1], wp[2], wp[3]);
+    }
+  }
   if constexpr (VHI) {
     uint32_t wh[4];
     words(hh, wh);
@@ -525,6 +610,123 @@ __device__ void value_group_wave(const Geo& g, const uint16_t* src, uint2 pos, u
   }
 }
 
+// ----------------------------------------------------------- shrink step
+
+// Progressive precision: one shrink of a stored group, in place.  Each code
+// X (digit d of a code: (X >> 2d) & 3; digit 0 in the record, digit 1 in
+// plane pl1, digits 2 and 3 in pl23 and pl23 + 256 when from == 8) moves from
+// `from` bits (8 or 4) to `to` bits (4 or 2) by the equivalent right shift,
+// 8 -> 4 then 4 -> 2, and each step multiplies the scale by 17 or 5 (rounded
+// to fp16, zero point kept).  The new digit 0 goes back to the record and,
+// when to == 4, digit 1 back to pl1.  Word wi of a 256-word record covers 16
+// codes at bit positions 2p; `chan(wi, p)` names the key channel of
+// position p (salient channels stop at 4 bits) or -1 for values.  One wave;
+// every read of a word is consumed before any write (so a later write of
+// the same plane slot by the caller is ordered after the reads).
+template <typename Chan>
+__device__ inline void shrink_words(uint32_t* rec, uint32_t* pl1, const uint32_t* pl23, int from,
+                                    int to, Chan sal_of, uint32_t (&np1)[4]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t nlo[4];
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const int wi = lane + 64 * m;
+    const uint32_t w0 = rec[wi], w1 = pl1[wi];
+    const uint32_t w2 = from == 8 ? pl23[wi] : 0u, w3 = from == 8 ? pl23[GROUP_WORDS + wi] : 0u;
+    uint32_t a = 0, b = 0;
+#pragma unroll
+    for (int p = 0; p < 16; p++) {
+      uint32_t X = ((w0 >> (2 * p)) & 3u) | (((w1 >> (2 * p)) & 3u) << 2) |
+                   (((w2 >> (2 * p)) & 3u) << 4) | (((w3 >> (2 * p)) & 3u) << 6);
+      if (from == 8) X = ers4(X);
+      if (to == 2 && !sal_of(wi, p)) X = ers2(X);
+      a |= (X & 3u) << (2 * p);
+      b |= ((X >> 2) & 3u) << (2 * p);
+    }
+    nlo[m] = a;
+    np1[m] = b;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    rec[lane + 64 * m] = nlo[m];
+    if (to == 4) pl1[lane + 64 * m] = np1[m];
+  }
+}
+
+// The step of one quantizer after the shrink (fp16 bits).
+__device__ inline uint16_t shrunk_step(uint16_t sb, int from, int to, bool stop4) {
+  if (from == 8) sb = f32_to_half_bits(half_bits_to_f32(sb) * 17.0f);
+  if (to == 2 && !stop4) sb = f32_to_half_bits(half_bits_to_f32(sb) * 5.0f);
+  return sb;
+}
+
+// Key record of one group (lo, hi, meta) and its planes: channel 16 (wi / 32)
+// + pi(p) sits at position p of word wi.  From 8 bits, the salient channels'
+// new digit 1 is gathered into hi (word e: tile index e, the d-th salient
+// channel at position pi(d)) through the LDS.
+__device__ inline void shrink_key_group(const Geo& g, PairMasks pm, uint32_t* lo, uint8_t* hi,
+                                        uint16_t* meta, uint32_t* pl1, const uint32_t* pl23,
+                                        int from, int to, KeyLds& L) {
+  const int lane = threadIdx.x & 63;
+  auto sal_of = [&](int wi, int p) {
+    const int c = 16 * (wi >> 5) + pos_swap(p);
+    return ((pm.hi >> (c & (NPAIR - 1))) & 1ull) != 0;
+  };
+  uint32_t np1[4];
+  shrink_words(lo, pl1, pl23, from, to, sal_of, np1);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; h2++) {
+    const int ch = 2 * lane + h2;
+    uint16_t* sp = meta + (ch >> 4) * 32 + (ch & 15);
+    *sp = shrunk_step(*sp, from, to, ((pm.hi >> (ch & (NPAIR - 1))) & 1ull) != 0);
+  }
+  if (from == 8 && g.nh > 0 && g.bits_hi == 4) {
+#pragma unroll
+    for (int m = 0; m < 4; m++) L.pl[0][lane + 64 * m] = np1[m];
+    wave_lds_sync();
+    if (lane < GS) {
+      uint32_t hw = 0;
+      uint64_t mk = pm.hi;
+#pragma unroll
+      for (int d = 0; d < 8; d++) {
+        if (d >= g.n_hi) break;
+        const int pc = __builtin_ctzll(mk);
+        mk &= mk - 1;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) {  // channels pc (entry d) and pc + 64 (entry n_hi + d)
+          const int c = pc + NPAIR * h2, dd = d + g.n_hi * h2;
+          const uint32_t w = L.pl[0][(c >> 4) * 32 + lane];
+          hw |= ((w >> (2 * pos_swap(c & 15))) & 3u) << (2 * pos_swap(dd));
+        }
+      }
+      ((uint32_t*)hi)[lane] = hw;
+    }
+    wave_lds_sync();
+  }
+}
+
+// Value record of one group: every code shrinks (one precision for all).
+__device__ inline void shrink_value_group(uint32_t* vc, uint16_t* meta, uint32_t* pl1,
+                                          const uint32_t* pl23, int from, int to) {
+  const int lane = threadIdx.x & 63;
+  uint32_t np1[4];
+  shrink_words(vc, pl1, pl23, from, to, [](int, int) { return false; }, np1);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; h2++) {  // scales s[j][t] at j * 32 + t
+    uint16_t* sp = meta + 2 * lane + h2;
+    *sp = shrunk_step(*sp, from, to, false);
+  }
+}
+
+// Plane slots of group grp of (sequence, KV head) bh: digit 1 (slot grp mod
+// w4) and digits 2, 3 (slots w4 + 2 (grp mod w8) and the next).
+__device__ inline uint32_t* plane1(const Geo& g, uint32_t* base, int bh, int grp) {
+  return base + ((size_t)bh * g.npl + grp % g.w4) * GROUP_WORDS;
+}
+__device__ inline uint32_t* plane23(const Geo& g, uint32_t* base, int bh, int grp) {
+  return g.w8 > 0 ? base + ((size_t)bh * g.npl + g.w4 + 2 * (grp % g.w8)) * GROUP_WORDS : base;
+}
+
 // ------------------------------------------------------------ ring group
 
 // LDS of the two waves that pack a group from the ring.
@@ -538,6 +740,11 @@ struct PackLds {
 // wave; other threads must not call).  With two value precisions both waves
 // rank the group's tokens from the ring keys (the same integer sums, so the
 // same order) and the key wave writes the order to the v_hi header.
+// Progressive precision (g.w4 > 0): the new group enters at the width of
+// age 0, and first the group that reaches age w4 shrinks from 4 to 2 bits and
+// the one that reaches age w8 from 8 bits to the width of that age (in this
+// order, each wave for its side: the new group's planes take the slots these
+// two free).
 template <bool BF, bool VHI>
 __device__ void pack_ring_group(const Geo& g, kvq_cache& c, int bh, int nq0, int tid,
                                 PackLds& lds) {
@@ -546,11 +753,31 @@ __device__ void pack_ring_group(const Geo& g, kvq_cache& c, int bh, int nq0, int
   const int grp = nq0 / GS, s0 = nq0 % g.RS;
   const size_t rec = (size_t)bh * g.NG + grp;
   uint32_t* vhi = c.v_hi + rec * g.vhi_words;
+  const int width = g.w4 > 0 ? prog_width(0, g.w8, g.w4) : 0;
+  const int gA = grp - g.w4, gB = grp - g.w8;
+  const bool shrinkA = g.w4 > g.w8 && gA >= 0, shrinkB = g.w4 > 0 && g.w8 > 0 && gB >= 0;
+  const int toB = shrinkB ? prog_width(g.w8, g.w8, g.w4) : 0;
   if (tid < 64) {
-    key_group_wave<BF, VHI>(g, rk + (size_t)s0 * D, pair_masks(g, c.pairs + (size_t)bh * NPAIR),
+    const PairMasks pm = pair_masks(g, c.pairs + (size_t)bh * NPAIR);
+    uint32_t* kpl = c.k_pl;
+    if (shrinkA) {
+      const size_t ra = (size_t)bh * g.NG + gA;
+      shrink_key_group(g, pm, (uint32_t*)c.k_lo + ra * GROUP_WORDS, (uint8_t*)c.k_hi + ra * g.khi_bytes,
+                       (uint16_t*)c.k_meta + ra * 2 * D, plane1(g, kpl, bh, gA),
+                       plane23(g, kpl, bh, gA), 4, 2, lds.key);
+    }
+    if (shrinkB) {
+      const size_t rb = (size_t)bh * g.NG + gB;
+      shrink_key_group(g, pm, (uint32_t*)c.k_lo + rb * GROUP_WORDS, (uint8_t*)c.k_hi + rb * g.khi_bytes,
+                       (uint16_t*)c.k_meta + rb * 2 * D, plane1(g, kpl, bh, gB),
+                       plane23(g, kpl, bh, gB), 8, toB, lds.key);
+    }
+    key_group_wave<BF, VHI>(g, rk + (size_t)s0 * D, pm,
                             (uint32_t*)c.k_lo + rec * GROUP_WORDS,
                             (uint8_t*)c.k_hi + rec * g.khi_bytes,
-                            (uint16_t*)c.k_meta + rec * 2 * D, lds.key);
+                            (uint16_t*)c.k_meta + rec * 2 * D, lds.key, width,
+                            width ? plane1(g, kpl, bh, grp) : nullptr,
+                            width ? plane23(g, kpl, bh, grp) : nullptr);
     if constexpr (VHI)
       if (tid < 2) ((uint4*)vhi)[tid] = ((const uint4*)lds.key.ord)[tid];
   } else {
@@ -560,9 +787,22 @@ __device__ void pack_ring_group(const Geo& g, kvq_cache& c, int bh, int nq0, int
       wave_lds_sync();
       pos = ((const uint2*)lds.vord)[((tid & 63) >> 4)];
     }
+    uint32_t* vpl = c.v_pl;
+    if (shrinkA) {
+      const size_t ra = (size_t)bh * g.NG + gA;
+      shrink_value_group((uint32_t*)c.v_codes + ra * GROUP_WORDS, (uint16_t*)c.v_meta + ra * 2 * D,
+                         plane1(g, vpl, bh, gA), plane23(g, vpl, bh, gA), 4, 2);
+    }
+    if (shrinkB) {
+      const size_t rb = (size_t)bh * g.NG + gB;
+      shrink_value_group((uint32_t*)c.v_codes + rb * GROUP_WORDS, (uint16_t*)c.v_meta + rb * 2 * D,
+                         plane1(g, vpl, bh, gB), plane23(g, vpl, bh, gB), 8, toB);
+    }
     value_group_wave<BF, true, VHI>(g, rv + (size_t)(s0 / GS) * D * GS, pos,
                                     (uint32_t*)c.v_codes + rec * GROUP_WORDS,
-                                    (uint16_t*)c.v_meta + rec * 2 * D, vhi);
+                                    (uint16_t*)c.v_meta + rec * 2 * D, vhi, width,
+                                    width ? plane1(g, vpl, bh, grp) : nullptr,
+                                    width ? plane23(g, vpl, bh, grp) : nullptr);
   }
 }
 

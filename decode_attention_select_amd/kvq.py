@@ -18,9 +18,9 @@ LIB_PATH = os.path.join(_PKG, "libkvq.so")
 _lib = None
 
 KVQ_FP16, KVQ_BF16 = 0, 1
-NBUF = 12
+NBUF = 14
 BUF_NAMES = ["k_lo", "k_hi", "k_meta", "v_codes", "v_meta", "ring_k", "ring_v",
-             "pairs", "len", "sums", "err", "v_hi"]
+             "pairs", "len", "sums", "err", "v_hi", "k_pl", "v_pl"]
 
 
 class KvqError(RuntimeError):
@@ -33,7 +33,7 @@ class kvq_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "group", "n_pairs_hi",
         "bits_hi", "n_pairs_lo1", "bits_lo", "bits_v", "residual", "max_tokens",
-        "io_dtype", "n_vblk_hi", "bits_vhi")]
+        "io_dtype", "n_vblk_hi", "bits_vhi", "prog_w8", "prog_w4")]
 
 
 class kvq_cache(ctypes.Structure):
@@ -68,10 +68,12 @@ def use_stamps_library():
 
 def make_layout(batch, n_q_heads, n_kv_heads, *, n_pairs_hi=6, bits_hi=4,
                 residual=128, max_tokens, io_dtype="bf16", n_pairs_lo1=0,
-                bits_lo=2, bits_v=2, n_vblk_hi=0, bits_vhi=4) -> kvq_layout:
+                bits_lo=2, bits_v=2, n_vblk_hi=0, bits_vhi=4, prog_w8=0,
+                prog_w4=0) -> kvq_layout:
     return kvq_layout(batch, n_q_heads, n_kv_heads, 128, 32, n_pairs_hi, bits_hi,
                       n_pairs_lo1, bits_lo, bits_v, residual, max_tokens,
-                      KVQ_BF16 if io_dtype == "bf16" else KVQ_FP16, n_vblk_hi, bits_vhi)
+                      KVQ_BF16 if io_dtype == "bf16" else KVQ_FP16, n_vblk_hi, bits_vhi,
+                      prog_w8, prog_w4)
 
 
 def _stream(stream):

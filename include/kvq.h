@@ -89,6 +89,16 @@ typedef struct {
                           abstract: two precisions chosen per token; see
                           v_hi) */
   int32_t bits_vhi;    /* 3 or 4 when n_vblk_hi > 0 (ignored otherwise) */
+  int32_t prog_w8;     /* progressive precision ([PM-KVQ] review, lead and
+                          key_machinery: a cache held at 16 bits first and
+                          shrunk through 8, 4 and 2 bits as it ages): the
+                          newest prog_w8 quantized groups of a sequence are
+                          held at 8 bits, the newest prog_w4 at 4 bits or
+                          more, older groups at the widths above.
+                          0 <= prog_w8 <= prog_w4 <= 256; prog_w4 == 0
+                          turns it off.  Requires n_pairs_lo1 == 0 and
+                          n_vblk_hi == 0.  See k_pl. */
+  int32_t prog_w4;
 } kvq_layout;
 
 /* Device buffers of one cache, all caller-allocated with the sizes returned
@@ -136,6 +146,29 @@ typedef struct {
  *  err     [1] int32: sticky error word, 0 = none; bit 0 = an append found
  *          the cache full; bit 1 = an append found a negative len (a cache
  *          no prefill or zero-fill initialized).
+ *  k_pl    prog_w4 > 0: [B][Hkv][prog_w4 + 2 prog_w8][256] u32, the digit
+ *          planes of the groups held above 2 bits.  A progressive group g
+ *          of the ng = n_q(T)/32 quantized groups has age a = ng - 1 - g;
+ *          while a < prog_w8 its codes have 8 bits, while a < prog_w4 4
+ *          bits, then 2 (salient 4-bit channels stay at 4, 16-bit channels
+ *          raw).  Every group is quantized at 8 bits (L = 255) and each
+ *          shrink from 2b to b bits maps a code X to round(X / (2^b + 1))
+ *          (the equivalent right shift (241 (X + 8)) >> 12 for b = 4,
+ *          (13 (X + 2)) >> 6 for b = 2), keeps z and stores the step as
+ *          fp16(fp32(s) * (2^b + 1)).  Digit d of a code X is (X >> 2d) & 3:
+ *          k_lo holds digit 0 of every group and k_hi digit 1 of the
+ *          salient channels of every group; digit 1 of a group younger than
+ *          prog_w4 (every channel) is plane slot g mod prog_w4, digits 2
+ *          and 3 of a group younger than prog_w8 are slots prog_w4 +
+ *          2 (g mod prog_w8) and the slot after, each in the k_lo word
+ *          format.  A slot's bytes belong to the youngest group that maps
+ *          to it; the others are stale.  The planes are the only storage
+ *          above the 2-bit records, so a cache holds (prog_w4 + 2 prog_w8)
+ *          KiB of keys and as much of values beyond them per sequence and
+ *          KV head, whatever its length.
+ *  v_pl    prog_w4 > 0: the value digit planes, as k_pl in the v_codes word
+ *          format (value codes shrink with their group the same way; v_meta
+ *          holds the current steps).
  *  v_hi    n_vblk_hi > 0: [B][Hkv][NG][8 + 64 n_vblk_hi] u32.  Value
  *          precision by token ([SemKV] abstract: tokens ranked by a
  *          model-internal score get one of two adjacent precisions; the page
@@ -162,9 +195,10 @@ typedef struct {
   uint64_t *sums;
   int32_t *err;
   uint32_t *v_hi;
+  uint32_t *k_pl, *v_pl;
 } kvq_cache;
 
-#define KVQ_NBUF 12
+#define KVQ_NBUF 14
 
 /* Bytes of each cache buffer, in kvq_cache field order (host only, no GPU).
  * Returns KVQ_EINVAL / KVQ_ENOTSUP for a layout the library rejects. */
@@ -260,7 +294,11 @@ kvq_status kvq_quant_values(const kvq_layout *L, const void *v, int32_t T,
  * Otherwise writes k_new/v_new to ring slot T mod RS, sets len = T + 1, and
  * when n_q(T+1) > n_q(T) quantizes the group of positions [n_q(T),
  * n_q(T)+32) from the ring exactly as kvq_quant_keys / kvq_quant_values
- * would, with the prefill pair ranking.
+ * would, with the prefill pair ranking.  With progressive precision the new
+ * group enters at the width of age 0, and the groups that this makes reach
+ * age prog_w8 and age prog_w4 are shrunk in place to their new widths first
+ * (codes, steps, k_hi and planes), so that the cache always equals a
+ * prefill of the same tokens.
  *   k_new, v_new: [B][Hkv][128] io dtype. */
 kvq_status kvq_append(const kvq_layout *L, const void *k_new,
                       const void *v_new, kvq_cache *cache, void *stream);
@@ -275,7 +313,8 @@ kvq_status kvq_append(const kvq_layout *L, const void *k_new,
  * other channels are untouched; decoding needs no change.  This layout keeps
  * the 4-bit slots, so no bytes are freed.  A group must be shrunk at most once: the
  * caller keeps the boundary (typically the oldest groups, when memory
- * fills).  n_pairs_hi == 0 is a no-op; bits_hi == 16 returns KVQ_ENOTSUP;
+ * fills).  A progressive layout (prog_w4 > 0) shrinks inside kvq_append and
+ * returns KVQ_ENOTSUP here.  n_pairs_hi == 0 is a no-op; bits_hi == 16 returns KVQ_ENOTSUP;
  * g0 < 0 or g1 < g0 returns KVQ_EINVAL; g1 beyond the capacity is clamped. */
 kvq_status kvq_shrink(const kvq_layout *L, kvq_cache *cache, int32_t g0,
                       int32_t g1, void *stream);
@@ -296,6 +335,8 @@ kvq_status kvq_shrink(const kvq_layout *L, kvq_cache *cache, int32_t g0,
  * rounded (barring fp16 underflow of a remainder): the roundings left are
  * the softmax weights' (to fp16; numerator and denominator take the same
  * rounded weights) and fp32 accumulation, whatever the size of the logits.
+ * With progressive precision each group is dequantized at its current width
+ * (digits from k_lo / v_codes, k_hi and the planes, as k_pl describes).
  * Requires T >= 1 (T = 0 writes zeros); a
  * len outside [0, max_tokens] is clamped into it (the result is then
  * unspecified, but every read stays inside the cache).
@@ -321,8 +362,9 @@ kvq_status kvq_decode_attn(const kvq_layout *L, const void *q,
  * query is zero on the pruned channels).  The pruned runs' key codes and
  * key scale/zero are not read (the group copies wait for the query and the
  * choice); n_keep = 5 drops 37.5 % of the key channels.  n_keep = 8 is
- * kvq_decode_attn; n_keep outside 1..8 returns KVQ_EINVAL.  All other
- * arguments, limits and errors as for kvq_decode_attn. */
+ * kvq_decode_attn; n_keep outside 1..8 returns KVQ_EINVAL.  A progressive
+ * layout returns KVQ_ENOTSUP for n_keep < 8.  All other arguments, limits
+ * and errors as for kvq_decode_attn. */
 kvq_status kvq_decode_attn_pruned(const kvq_layout *L, const void *q,
                                   const kvq_cache *cache, float sm_scale,
                                   int32_t n_splits, int32_t n_keep,
@@ -344,7 +386,9 @@ kvq_status kvq_decode_attn_pruned(const kvq_layout *L, const void *q,
  *    kvq_decode_attn.
  *  - if T == max_tokens (T < 0): sets err bit 0 (bit 1), changes nothing,
  *    and decodes over the cache as it stands.
- * Saves the append's launch.  Pruned key chunks are not offered here.
+ * Saves the append's launch.  Pruned key chunks are not offered here, and a
+ * progressive layout returns KVQ_ENOTSUP (its append shrinks older groups:
+ * call kvq_append, then kvq_decode_attn).
  *   k_new, v_new: [B][Hkv][128] io dtype;  q, out: as for kvq_decode_attn.
  * Other arguments, limits and errors as for kvq_decode_attn. */
 kvq_status kvq_append_decode_attn(const kvq_layout *L, const void *k_new,
@@ -382,7 +426,8 @@ kvq_status kvq_decode_attn_noalloc(const kvq_layout *L, const void *q,
  * Reads cache as kvq_decode_attn does (len, ring, every quantized group of
  * each (b, kv head)); writes nothing but, for almost no data, one word of
  * `sink` (>= 4 bytes of device memory, 16-byte aligned).  n_splits limits
- * and errors as for kvq_decode_attn. */
+ * and errors as for kvq_decode_attn; a progressive layout returns
+ * KVQ_ENOTSUP. */
 kvq_status kvq_read_ceiling(const kvq_layout *L, const kvq_cache *cache,
                             int32_t n_splits, void *sink, void *stream);
 

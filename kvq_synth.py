@@ -54,6 +54,8 @@ class Workload:
     seed: int = 0
     n_vblk_hi: int = 0       # per group, 8 * n_vblk_hi tokens (largest keys) get bits_vhi-bit values
     bits_vhi: int = 4
+    prog_w8: int = 0         # progressive precision: newest groups held at 8 bits
+    prog_w4: int = 0         # ... and at 4 bits or more (0: off)
 
     @property
     def group_size(self) -> int:

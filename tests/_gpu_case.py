@@ -37,7 +37,8 @@ class Case:
                                       n_pairs_lo1=w.n_pairs_lo1,
                                       residual=w.residual, max_tokens=self.max_tokens,
                                       io_dtype=w.io_dtype, n_vblk_hi=w.n_vblk_hi,
-                                      bits_vhi=w.bits_vhi)
+                                      bits_vhi=w.bits_vhi, prog_w8=w.prog_w8,
+                                      prog_w4=w.prog_w4)
         self.cache = kvq.Cache(self.layout)
         self.NG = max(self.max_tokens - w.residual, 0) // 32
         # selection always looks at the workload's prefill (once, at prefill)
@@ -63,7 +64,8 @@ class Case:
                                residual=self.w.residual, n_pairs_hi=self.w.n_pairs_hi,
                                bits_hi=self.w.bits_hi, io_dtype=self.w.io_dtype,
                                ng=max(self.NG, 1), n_pairs_lo1=self.w.n_pairs_lo1,
-                               n_vblk_hi=self.w.n_vblk_hi, bits_vhi=self.w.bits_vhi)
+                               n_vblk_hi=self.w.n_vblk_hi, bits_vhi=self.w.bits_vhi,
+                               prog_w8=self.w.prog_w8, prog_w4=self.w.prog_w4)
 
     # -------------------------------------------------------------- GPU side
     def gpu_bytes(self) -> dict:
@@ -87,6 +89,10 @@ class Case:
         vw = 8 + 64 * self.w.n_vblk_hi if self.w.n_vblk_hi else 0
         out["v_hi"] = (host(c["v_hi"], np.uint32)[:B * H * NG * vw].reshape(B, H, NG, vw)
                        if vw and NG else np.zeros((B, H, NG, 0), np.uint32))
+        npl = self.w.prog_w4 + 2 * self.w.prog_w8 if NG else 0
+        for nm in ("k_pl", "v_pl"):
+            out[nm] = (host(c[nm], np.uint32).reshape(B, H, npl, 256) if npl
+                       else np.zeros((B, H, 0, 256), np.uint32))
         return out
 
     def decode_pruned(self, q_bits: np.ndarray, n_splits: int, n_keep: int):
@@ -201,6 +207,14 @@ def compare_cache(case: Case, qz, ng: int):
     if case.w.n_vblk_hi and ng:
         a, b = g["v_hi"][:, :, :ng], o["v_hi"][:, :, :ng]
         assert np.array_equal(a, b), "v_hi differs at %s" % np.argwhere(a != b)[:5]
+    if case.w.prog_w4 and ng:
+        # the digit planes of the live wide groups (other slots hold stale bytes)
+        assert ng == qz.nq // 32
+        for grp, sl in oracle.live_plane_slots(qz.T, qz.R, case.w.prog_w8, case.w.prog_w4):
+            for nm in ("k_pl", "v_pl"):
+                a, b = g[nm][:, :, sl], o[nm][:, :, sl]
+                assert np.array_equal(a, b), "%s slot %d (group %d) differs at %s" % (
+                    nm, sl, grp, np.argwhere(a != b)[:5])
     slots = oracle.live_ring_slots(qz.T, qz.R)
     assert np.array_equal(g["ring_k"][:, :, slots], o["ring_k"][:, :, slots])
     rv_g = g["ring_v"].reshape(*g["ring_v"].shape[:2], -1, 128, 32)

@@ -56,7 +56,7 @@ def test_cache_sizes_closed_form():
     s = kvq.kvq_cache_sizes(L32k())
     ng, bh = (32768 - 128) // 32, 8
     assert s == [bh * ng * 1024, bh * ng * 128, bh * ng * 512, bh * ng * 1024, bh * ng * 512,
-                 bh * 160 * 256, bh * 160 * 256, bh * 64 * 4, bh * 4, bh * 2 * 64 * 8, 4, 0]
+                 bh * 160 * 256, bh * 160 * 256, bh * 64 * 4, bh * 4, bh * 2 * 64 * 8, 4, 0, 0, 0]
     # two value precisions: 32 order bytes + 256 bytes per 8 high-precision tokens
     for n in (1, 2, 4):
         assert kvq.kvq_cache_sizes(L32k(n_vblk_hi=n, bits_vhi=3))[11] == bh * ng * (32 + 256 * n)
@@ -80,6 +80,8 @@ def status_of(name, *args):
     (dict(io_dtype=5), EINVAL), (dict(n_q_heads=30), EINVAL), (dict(n_q_heads=8 * 17), ENOTSUP),
     (dict(batch=0), EINVAL), (dict(n_vblk_hi=5), EINVAL), (dict(n_vblk_hi=-1), EINVAL),
     (dict(n_vblk_hi=2, bits_vhi=2), ENOTSUP), (dict(n_vblk_hi=1, bits_vhi=8), ENOTSUP),
+    (dict(prog_w8=-1), EINVAL), (dict(prog_w4=2, prog_w8=3), EINVAL), (dict(prog_w4=257), EINVAL),
+    (dict(prog_w4=4, n_pairs_lo1=2), ENOTSUP), (dict(prog_w4=4, n_vblk_hi=1), ENOTSUP),
 ])
 def test_layout_rejected(bad, want):
     L = L32k()
@@ -184,6 +186,43 @@ def test_prefill_and_append_validation():
     assert status_of("kvq_shrink", ctypes.byref(L), ctypes.byref(c), 5, 4, P(0)) == EINVAL
     L16 = L32k(bits_hi=16)
     assert status_of("kvq_shrink", ctypes.byref(L16), ctypes.byref(c), 0, 4, P(0)) == ENOTSUP
+
+
+def test_prog_plane_sizes():
+    # progressive precision: (w4 + 2 w8) KiB of key planes and as much of
+    # value planes per (sequence, KV head), whatever the length
+    bh = 1 * 8
+    for w8, w4 in ((0, 1), (4, 16), (256, 256)):
+        s = kvq.kvq_cache_sizes(L32k(prog_w8=w8, prog_w4=w4))
+        assert s[12] == s[13] == bh * (w4 + 2 * w8) * 1024
+        assert s[:12] == kvq.kvq_cache_sizes(L32k())[:12]
+    assert kvq.kvq_cache_sizes(L32k())[12:] == [0, 0]
+    assert kvq.kvq_cache_sizes(L32k(prog_w4=4, max_tokens=100))[12] == 0  # no groups
+
+
+@no_gpu
+def test_prog_calls_it_does_not_offer():
+    # pruned and one-launch decode, the explicit salient shrink and the read
+    # ceiling return ENOTSUP on a progressive layout, before any launch
+    L = L32k(prog_w8=2, prog_w4=8)
+    c = fake_cache()
+    ws = kvq.kvq_workspace_bytes(L, 8)
+    P = ctypes.c_void_p
+    assert status_of("kvq_decode_attn_pruned", ctypes.byref(L), P(FAKE), ctypes.byref(c),
+                     ctypes.c_float(0.088), 8, 5, P(FAKE), ctypes.c_size_t(ws), P(FAKE),
+                     P(0)) == ENOTSUP
+    assert status_of("kvq_append_decode_attn", ctypes.byref(L), P(FAKE), P(FAKE), P(FAKE),
+                     ctypes.byref(c), ctypes.c_float(0.088), 8, P(FAKE), ctypes.c_size_t(ws),
+                     P(FAKE), P(0)) == ENOTSUP
+    assert status_of("kvq_shrink", ctypes.byref(L), ctypes.byref(c), 0, 4, P(0)) == ENOTSUP
+    assert status_of("kvq_read_ceiling", ctypes.byref(L), ctypes.byref(c), 8, P(FAKE),
+                     P(0)) == ENOTSUP
+    # a plane buffer that is missing is an argument error
+    c0 = fake_cache()
+    c0.k_pl = None
+    assert status_of("kvq_decode_attn", ctypes.byref(L), P(FAKE), ctypes.byref(c0),
+                     ctypes.c_float(0.088), 8, P(FAKE), ctypes.c_size_t(ws), P(FAKE),
+                     P(0)) == EINVAL
 
 
 def test_bench_refuses_more_than_one_gpu():
