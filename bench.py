@@ -18,6 +18,7 @@ tokens at 256 B key + 256 B value, plus the query and the output.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -36,7 +37,7 @@ PEAK_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_traffic_llama3-8b-32k.md")
 # the decode kernel instance of the default workload: bf16, 4-bit salient
 # digits, quantized groups, unpruned, one value precision, no append, G <= 8
-DECODE_KERNEL = "_ZN3kvq13decode_kernelILb1ELi4ELb1ELi0ELb0ELb0ELb1E"
+DECODE_KERNEL = "_ZN3kvq13decode_kernelILb1ELi4ELb1ELi0ELb0ELb0ELb1ELb0EEEv"
 
 
 def kernel_code_hash(symbol_prefix: str = DECODE_KERNEL, lib_path: str = None):
@@ -152,12 +153,28 @@ def algorithmic_bytes(w, T: int, n_keep: int = 8) -> int:
         assert w.bits_hi == 4 and w.n_pairs_lo1 == 0
         per_tok = (2 * 16 * n_keep + 2 * n_hi_ch) / 8 + 2 * n_keep + 32 + 16
         return int(round(bh * (nq * per_tok + nr * (32 * n_keep + 256)) + qo))
+    raw = n_hi_ch if w.bits_hi == 16 else 0
+    k_meta = (128 - raw) * 4 / 32
+
+    def per_tok_at(width):
+        # progressive groups of `width` bits: every non-raw key channel and
+        # every value at that width (salient 4-bit channels never below 4)
+        kb = raw * 16 + (128 - raw) * width
+        return kb / 8 + k_meta + 128 * width / 8 + 16
+
+    if w.prog_w4 > 0:
+        ng = nq // 32
+        n8 = min(w.prog_w8, ng)
+        n4 = min(w.prog_w4, ng) - n8
+        tok = 32 * (n8 * per_tok_at(8) + n4 * per_tok_at(4))
+        w2 = dataclasses.replace(w, prog_w8=0, prog_w4=0)
+        rest = algorithmic_bytes(w2, 32 * (ng - n8 - n4) + R) - (
+            bh * R * 512 + qo)  # the 2-bit groups alone
+        return int(round(bh * (tok + nr * 512) + rest + qo))
     if w.bits_hi == 16:
         k_code_bits = n_hi_ch * 16 + n_two_ch * 2 + n_one_ch
-        k_meta = (128 - n_hi_ch) * 4 / 32
     else:
         k_code_bits = n_hi_ch * w.bits_hi + n_two_ch * 2 + n_one_ch
-        k_meta = 128 * 4 / 32
     per_tok = k_code_bits / 8 + k_meta + 32 + 16
     if w.n_vblk_hi:  # the high-precision tokens' extra value bits (decode skips the order bytes)
         per_tok += w.n_vblk_hi / 4 * (w.bits_vhi - 2) * 128 / 8
@@ -304,7 +321,7 @@ def streaming_leg(args, w):
     data = kvq_synth.generate(w)
     layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads, n_pairs_hi=w.n_pairs_hi,
                              bits_hi=w.bits_hi, residual=w.residual, max_tokens=T0 + n,
-                             io_dtype=w.io_dtype)
+                             io_dtype=w.io_dtype, prog_w8=w.prog_w8, prog_w4=w.prog_w4)
     pristine = kvq.Cache(layout)
     kvq.kvq_select_pairs(layout, dev(data["q_sel"]), w.n_qry, dev(data["k"][:, :, :T0]), T0,
                          pristine.struct)
@@ -379,10 +396,12 @@ def streaming_leg(args, w):
     restore()
     append_us = run(False)
     decode_us = step_us - append_us
-    restore()
-    fused_us = run_fused()
-    for c in layers:
-        assert kvq.kvq_check(c.struct) == 0
+    fused_us = None
+    if not w.prog_w4:  # a progressive append shrinks older groups: no one-launch step
+        restore()
+        fused_us = run_fused()
+        for c in layers:
+            assert kvq.kvq_check(c.struct) == 0
     alg = sum(algorithmic_bytes(w, T0 + i + 1) for i in range(n)) / n
     gbs = alg / (decode_us * 1e-6) / 1e9
     return {
@@ -396,7 +415,7 @@ def streaming_leg(args, w):
         "us_per_step": round(step_us, 3),
         "append_us_per_step": round(append_us, 3),
         "decode_us_per_step": round(decode_us, 3),
-        "fused_us_per_step": round(fused_us, 3),
+        "fused_us_per_step": round(fused_us, 3) if fused_us is not None else None,
         "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -415,27 +434,14 @@ def streaming_leg(args, w):
     }
 
 
-def pareto_leg(args, w):
-    """Bit-allocation sweep on one workload: for every point of
-    kvq_synth.PARETO_POINTS (key bits) and kvq_synth.VALUE_POINTS (two value
-    precisions on the 2.26-bit keys), the decode time and effective GB/s (cache
-    replicas beyond the Infinity Cache, as in the main leg) and the attention
-    error of the GPU output against plain softmax attention over the
-    unquantized 16-bit keys and values (fp64 on the host)."""
-    import dataclasses
-
+def unquantized_reference(w, data):
+    """fp64 softmax attention over the unquantized 16-bit keys and values,
+    every query head of the workload's first decode query."""
     import numpy as np
-    import torch
 
     import kvq_synth
-    from decode_attention_select_amd import kvq
-
-    T = w.tokens
-    data = kvq_synth.generate(w)
-    q_bits = data["q_dec"][:, :, 0]
-    # unquantized reference, every query head
-    qf = kvq_synth.bits_to_f64(q_bits, w.io_dtype)
-    G = w.group_size
+    T, G = w.tokens, w.group_size
+    qf = kvq_synth.bits_to_f64(data["q_dec"][:, :, 0], w.io_dtype)
     ref = np.zeros((w.batch, w.n_q_heads, 128))
     for b in range(w.batch):
         for kh in range(w.n_kv_heads):
@@ -444,82 +450,147 @@ def pareto_leg(args, w):
             lg = (qf[b, kh * G:(kh + 1) * G] @ K.T) * SM_SCALE
             p = np.exp(lg - lg.max(axis=1, keepdims=True))
             ref[b, kh * G:(kh + 1) * G] = (p / p.sum(axis=1, keepdims=True)) @ V
-    points = []
-    S = args.splits or w.n_splits or default_splits(w)
-    pts = [(label, n_hi, bits_hi, n_lo1, 0, 4)
-           for label, n_hi, bits_hi, n_lo1 in kvq_synth.PARETO_POINTS]
-    pts += [(label, 6, 4, 0, nvb, bvh) for label, nvb, bvh in kvq_synth.VALUE_POINTS]
-    for label, n_hi, bits_hi, n_lo1, nvb, bvh in pts:
-        wp = dataclasses.replace(w, n_pairs_hi=n_hi, bits_hi=bits_hi, n_pairs_lo1=n_lo1,
-                                 n_vblk_hi=nvb, bits_vhi=bvh)
-        layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads, n_pairs_hi=n_hi,
-                                 bits_hi=bits_hi, n_pairs_lo1=n_lo1, residual=w.residual,
-                                 max_tokens=T, io_dtype=w.io_dtype, n_vblk_hi=nvb,
-                                 bits_vhi=bvh)
-        base = kvq.Cache(layout)
-        kvq.kvq_select_pairs(layout, dev(data["q_sel"]), w.n_qry, dev(data["k"][:, :, :T]), T,
-                             base.struct)
-        kvq.kvq_quant_keys(layout, dev(data["k"][:, :, :T]), T, base.struct)
-        kvq.kvq_quant_values(layout, dev(data["v"][:, :, :T]), T, base.struct)
-        torch.cuda.synchronize()
-        n_rep = max(1, math.ceil(args.replica_mib * 2 ** 20 / base.nbytes()))
-        reps = [base]
-        for _ in range(n_rep - 1):
-            r = kvq.Cache.__new__(kvq.Cache)
-            r.layout, r.sizes = base.layout, base.sizes
-            r.bufs = {k: v.clone() for k, v in base.bufs.items()}
-            r.struct = kvq.kvq_cache(*[r.bufs[nm].data_ptr() for nm in kvq.BUF_NAMES])
-            reps.append(r)
-        q = dev(q_bits)
-        out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
-        ws = torch.zeros(kvq.kvq_workspace_bytes(layout, S), dtype=torch.uint8, device="cuda")
-        stream = torch.cuda.current_stream()
-        sc = float(np.float32(SM_SCALE))
-        for i in range(args.warmup):
-            kvq.kvq_decode_attn(layout, q, reps[i % n_rep].struct, sc, S, ws, out, stream=stream)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for i in range(args.steps):
-            kvq.kvq_decode_attn(layout, q, reps[i % n_rep].struct, sc, S, ws, out, stream=stream)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        us = ev0.elapsed_time(ev1) * 1e3 / args.steps
-        got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype)
-        err = np.abs(got - ref)
-        alg = algorithmic_bytes(wp, T)
-        points.append({"bits": label, "salient_pairs": n_hi, "salient_bits": bits_hi,
-                       "one_bit_pairs": n_lo1, "value_blocks_hi": nvb,
-                       "value_bits_hi": bvh if nvb else None, "us_per_step": round(us, 3),
-                       "GBs": round(alg / (us * 1e-6) / 1e9, 1),
-                       "algorithmic_bytes": alg, "layout_bytes": layout_bytes(base, wp, T),
-                       "max_abs_err_vs_unquantized": float(err.max()),
-                       "mean_abs_err_vs_unquantized": float(err.mean()),
-                       "rel_l2_err_vs_unquantized": float(np.linalg.norm(got - ref) /
-                                                          np.linalg.norm(ref))})
-        del reps, base
-        torch.cuda.empty_cache()
-    main_pt = [p for p in points if p["bits"] == "2.26"][0]
+    return ref
+
+
+def sweep_point(args, wp, data, S, ref):
+    """One layout of a sweep: prefill of the workload's T tokens, then the
+    decode time over cache replicas beyond the Infinity Cache (as in the main
+    leg), effective GB/s, the cache's bytes and the error of the GPU output
+    against `ref` (unquantized fp64 attention)."""
+    import numpy as np
+    import torch
+
+    import kvq_synth
+    from decode_attention_select_amd import kvq
+
+    T = wp.tokens
+    layout = kvq.make_layout(wp.batch, wp.n_q_heads, wp.n_kv_heads, n_pairs_hi=wp.n_pairs_hi,
+                             bits_hi=wp.bits_hi, n_pairs_lo1=wp.n_pairs_lo1, residual=wp.residual,
+                             max_tokens=T, io_dtype=wp.io_dtype, n_vblk_hi=wp.n_vblk_hi,
+                             bits_vhi=wp.bits_vhi, prog_w8=wp.prog_w8, prog_w4=wp.prog_w4)
+    base = kvq.Cache(layout)
+    kvq.kvq_select_pairs(layout, dev(data["q_sel"]), wp.n_qry, dev(data["k"][:, :, :T]), T,
+                         base.struct)
+    kvq.kvq_quant_keys(layout, dev(data["k"][:, :, :T]), T, base.struct)
+    kvq.kvq_quant_values(layout, dev(data["v"][:, :, :T]), T, base.struct)
+    torch.cuda.synchronize()
+    n_rep = max(1, math.ceil(args.replica_mib * 2 ** 20 / base.nbytes()))
+    reps = [base]
+    for _ in range(n_rep - 1):
+        r = kvq.Cache.__new__(kvq.Cache)
+        r.layout, r.sizes = base.layout, base.sizes
+        r.bufs = {k: v.clone() for k, v in base.bufs.items()}
+        r.struct = kvq.kvq_cache(*[r.bufs[nm].data_ptr() for nm in kvq.BUF_NAMES])
+        reps.append(r)
+    q = dev(data["q_dec"][:, :, 0])
+    out = torch.empty((wp.batch, wp.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    ws = torch.zeros(kvq.kvq_workspace_bytes(layout, S), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sc = float(np.float32(SM_SCALE))
+    for i in range(args.warmup):
+        kvq.kvq_decode_attn(layout, q, reps[i % n_rep].struct, sc, S, ws, out, stream=stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        kvq.kvq_decode_attn(layout, q, reps[i % n_rep].struct, sc, S, ws, out, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), wp.io_dtype)
+    err = np.abs(got - ref)
+    alg = algorithmic_bytes(wp, T)
+    pt = {"us_per_step": round(us, 3), "GBs": round(alg / (us * 1e-6) / 1e9, 1),
+          "algorithmic_bytes": alg, "cache_bytes": base.nbytes(),
+          "max_abs_err_vs_unquantized": float(err.max()),
+          "mean_abs_err_vs_unquantized": float(err.mean()),
+          "rel_l2_err_vs_unquantized": float(np.linalg.norm(got - ref) / np.linalg.norm(ref))}
+    if not wp.prog_w4:
+        pt["layout_bytes"] = layout_bytes(base, wp, T)
+    del reps, base
+    torch.cuda.empty_cache()
+    return pt
+
+
+def sweep_line(args, w, S, value_pt, key, points, note):
     return {
         "metric": METRIC,
-        "value": main_pt["GBs"],
+        "value": value_pt["GBs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(main_pt["us_per_step"] * 1e-3, 5),
+        "ms_per_step": round(value_pt["us_per_step"] * 1e-3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16 (MFMA) / f32 accumulate",
         "data": "synthetic (seeded N(0,1) + outlier key pairs, RoPE)",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads,
-                   "kv_heads": w.n_kv_heads, "context": T, "io_dtype": w.io_dtype,
+                   "kv_heads": w.n_kv_heads, "context": w.tokens, "io_dtype": w.io_dtype,
                    "residual": w.residual, "n_splits": S},
-        "pareto": points,
-        "note": "value = the 2.26-bit point; errors are against fp64 softmax attention over "
-                "the unquantized 16-bit K/V, all query heads",
+        key: points,
+        "note": note,
     }
+
+
+def pareto_leg(args, w):
+    """Bit-allocation sweep on one workload: for every point of
+    kvq_synth.PARETO_POINTS (key bits) and kvq_synth.VALUE_POINTS (two value
+    precisions on the 2.26-bit keys), the decode time and effective GB/s (cache
+    replicas beyond the Infinity Cache, as in the main leg) and the attention
+    error of the GPU output against plain softmax attention over the
+    unquantized 16-bit keys and values (fp64 on the host)."""
+    import kvq_synth
+
+    data = kvq_synth.generate(w)
+    ref = unquantized_reference(w, data)
+    S = args.splits or w.n_splits or default_splits(w)
+    pts = [(label, n_hi, bits_hi, n_lo1, 0, 4)
+           for label, n_hi, bits_hi, n_lo1 in kvq_synth.PARETO_POINTS]
+    pts += [(label, 6, 4, 0, nvb, bvh) for label, nvb, bvh in kvq_synth.VALUE_POINTS]
+    points = []
+    for label, n_hi, bits_hi, n_lo1, nvb, bvh in pts:
+        wp = dataclasses.replace(w, n_pairs_hi=n_hi, bits_hi=bits_hi, n_pairs_lo1=n_lo1,
+                                 n_vblk_hi=nvb, bits_vhi=bvh)
+        pt = {"bits": label, "salient_pairs": n_hi, "salient_bits": bits_hi,
+              "one_bit_pairs": n_lo1, "value_blocks_hi": nvb,
+              "value_bits_hi": bvh if nvb else None}
+        pt.update(sweep_point(args, wp, data, S, ref))
+        points.append(pt)
+    main_pt = [p for p in points if p["bits"] == "2.26"][0]
+    return sweep_line(args, w, S, main_pt, "pareto", points,
+                      "value = the 2.26-bit point; errors are against fp64 softmax attention "
+                      "over the unquantized 16-bit K/V, all query heads")
+
+
+def prog_leg(args, w):
+    """Progressive precision (PM-KVQ review: groups held at 8, then 4, then
+    2 bits as they age): for every window setting of kvq_synth.PROG_POINTS
+    (prog_w8, prog_w4: the newest groups held at 8 and at 4 bits or more) the
+    decode time, the bytes a step reads, the cache's whole footprint and the
+    error against unquantized attention.  The first point is the plain 2-bit
+    cache, the last every group (up to 256) at 8 bits: the cache before any
+    shrink."""
+    import kvq_synth
+
+    data = kvq_synth.generate(w)
+    ref = unquantized_reference(w, data)
+    S = args.splits or w.n_splits or default_splits(w)
+    points = []
+    for label, w8, w4 in kvq_synth.PROG_POINTS:
+        wp = dataclasses.replace(w, prog_w8=w8, prog_w4=w4)
+        pt = {"windows": label, "prog_w8": w8, "prog_w4": w4,
+              "groups_at_8": min(w8, (w.tokens - w.residual) // 32) if w4 else 0,
+              "groups_at_4": (min(w4, (w.tokens - w.residual) // 32) - min(w8, (w.tokens - w.residual) // 32)) if w4 else 0}
+        pt.update(sweep_point(args, wp, data, S, ref))
+        points.append(pt)
+    main_pt = [p for p in points if p["prog_w4"] == 16][0]
+    return sweep_line(args, w, S, main_pt, "progressive", points,
+                      "value = windows of 4 (8-bit) and 16 (>= 4-bit) groups; cache_bytes is "
+                      "the whole footprint at this capacity; errors against fp64 softmax "
+                      "attention over the unquantized 16-bit K/V")
 
 
 def prefill_leg(args, w):
@@ -749,6 +820,9 @@ def main():
     ap.add_argument("--value-hi", default="",
                     help="with --build: N:B, the N*8 tokens of largest key magnitude per group "
                          "get B-bit values (two value precisions)")
+    ap.add_argument("--prog", default="",
+                    help="W8:W4, progressive precision on the workload (the newest W8 groups "
+                         "held at 8 bits, the newest W4 at 4 bits or more)")
     ap.add_argument("--stamps", action="store_true",
                     help="phase timestamps of the decode kernel (libkvq_stamps.so)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -781,6 +855,9 @@ def main():
     if args.value_hi:
         nvb, bvh = (int(x) for x in args.value_hi.split(":"))
         w = w.replace(n_vblk_hi=nvb, bits_vhi=bvh)
+    if args.prog:
+        w8, w4 = (int(x) for x in args.prog.split(":"))
+        w = w.replace(prog_w8=w8, prog_w4=w4)
     if args.build:
         print(json.dumps(prefill_leg(args, w)), flush=True)
         return
@@ -793,12 +870,15 @@ def main():
     if w.name.startswith("pareto"):
         print(json.dumps(pareto_leg(args, w)), flush=True)
         return
+    if w.name.startswith("prog"):
+        print(json.dumps(prog_leg(args, w)), flush=True)
+        return
     S = args.splits or w.n_splits or default_splits(w)
     T = w.tokens
     data = kvq_synth.generate(w)
     layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads, n_pairs_hi=w.n_pairs_hi,
                              bits_hi=w.bits_hi, residual=w.residual, max_tokens=T,
-                             io_dtype=w.io_dtype)
+                             io_dtype=w.io_dtype, prog_w8=w.prog_w8, prog_w4=w.prog_w4)
     base = kvq.Cache(layout)
     kvq.kvq_select_pairs(layout, dev(data["q_sel"]), w.n_qry, dev(data["k"][:, :, :T]), T,
                          base.struct)
@@ -892,12 +972,16 @@ def main():
                    "residual": w.residual, "n_splits": S, "cache_replicas": n_rep,
                    **({"kept_key_runs": args.prune} if args.prune < 8 else {})},
         "algorithmic_bytes_per_step": alg,
-        "layout_bytes_per_step": layout_bytes(base, w, T),
+        "layout_bytes_per_step": layout_bytes(base, w, T) if not w.prog_w4 else None,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name) if args.prune == 8 else None},
+                     "traffic": (measured_traffic(w.name)
+                                 if args.prune == 8 and not w.prog_w4 else None)},
     }
-    if args.prune == 8:
+    if w.prog_w4:
+        res["config"].update(prog_w8=w.prog_w8, prog_w4=w.prog_w4)
+        res["cache_bytes"] = base.nbytes()
+    if args.prune == 8 and not w.prog_w4:
         cus = ceiling_us()
         cg = alg / (cus * 1e-6) / 1e9
         res["ceiling"] = {"us_per_step": round(cus, 3), "GBs": round(cg, 1),

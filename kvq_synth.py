@@ -84,6 +84,12 @@ WORKLOADS = [
              n_pairs_hi=6, residual=128, n_splits=32, seed=1004),
     # the 32K layer's cache with one query head per KV head (G = 1): the same
     # bytes, 1 of 16 MFMA head columns used
+    # progressive precision: 256 quantized groups (8192 tokens) plus the
+    # residual, so that the widest windows hold every group
+    Workload("prog-8k", 1, 32, 8, 8192 + 128, outliers="pct2x10",
+             n_pairs_hi=6, residual=128, seed=1006),
+    Workload("prog-32k", 1, 32, 8, 32768, outliers="pct2x10",
+             n_pairs_hi=6, residual=128, seed=1007),
     Workload("g1-32k", 1, 8, 8, 32768, outliers="pct2x10",
              n_pairs_hi=6, residual=128, seed=1005),
 ]
@@ -95,6 +101,11 @@ PARETO_POINTS = [("1.5", 0, 4, 32), ("2.0", 0, 4, 0), ("2.26", 6, 4, 0), ("3.0",
 # Value-precision points on the 2.26-bit keys: (label, kept 8-token value
 # blocks per 32-token group, their bits).
 VALUE_POINTS = [("2.26 v1@3", 1, 3), ("2.26 v1@4", 1, 4), ("2.26 v2@4", 2, 4)]
+# Progressive-precision windows (label, groups held at 8 bits, groups held
+# at 4 bits or more): the plain cache, a steady state, every group at 4 bits,
+# every group at 8 bits (up to 256 groups: the cache before any shrink).
+PROG_POINTS = [("2-bit", 0, 0), ("8/4/2 windows 4/16", 4, 16), ("4-bit, 256 groups", 0, 256),
+               ("8-bit, 256 groups", 256, 256)]
 
 
 def workload(name: str) -> Workload:
