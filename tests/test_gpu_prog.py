@@ -114,3 +114,103 @@ def test_prog_holds_less_than_an_eight_bit_cache():
     assert nb - n2 == 8 * (16 + 2 * 4) * 1024 * 2
     assert nw - n2 == 8 * (256 + 2 * 256) * 1024 * 2
     assert nb < nw
+
+
+def _random_prog_layouts(n, seed):
+    """Seeded draws over the progressive layouts the ABI accepts (small sizes)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2, 3]))
+        R = int(rng.choice([32, 64, 128]))
+        w4 = int(rng.integers(1, 14))
+        w8 = int(rng.integers(0, w4 + 1))
+        T = int(rng.integers(1, 900))
+        out.append(kvq_synth.Workload(
+            "prand%d" % i, int(rng.integers(1, 3)), G * Hkv, Hkv, T, n_qry=8, n_app=40,
+            io_dtype=str(rng.choice(["fp16", "bf16"])),
+            outliers=str(rng.choice(["none", "pairs4x8", "pct2x10"])),
+            n_pairs_hi=int(rng.integers(0, 9)), bits_hi=int(rng.choice([4, 16])), residual=R,
+            seed=400 + i, prog_w8=w8, prog_w4=w4))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_prog_layouts(10, 11), ids=_ids)
+def test_prog_random_layouts(w):
+    # prefill: every byte and the decode at a drawn split count; then 40
+    # appends (at least one pack): every byte and the decode again, and the
+    # no-allocation entry point equal to the plain one
+    print("case", w, flush=True)
+    rng = np.random.default_rng(w.seed)
+    case = Case(w, T=w.tokens, max_tokens=w.max_tokens)
+    pairs = case.oracle_select()[1]
+    q = case.d["q_dec"][:, :, 0]
+    qz = case.oracle_quant(pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
+    S = int(rng.integers(1, 12))
+    check_output(case.decode(q, S), oracle.attention(qz, q, SM_SCALE), w.io_dtype, ATOL)
+    kn = dev(np.ascontiguousarray(case.d["k"][:, :, w.tokens:]))
+    vn = dev(np.ascontiguousarray(case.d["v"][:, :, w.tokens:]))
+    for i in range(w.n_app):
+        kvq.kvq_append(case.layout, kn[:, :, i].contiguous(), vn[:, :, i].contiguous(),
+                       case.cache.struct)
+    torch.cuda.synchronize()
+    assert kvq.kvq_check(case.cache.struct) == 0
+    case.T = w.tokens + w.n_app
+    qz = case.oracle_quant(pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
+    S = int(rng.integers(1, 12))
+    got = case.decode(q, S)
+    check_output(got, oracle.attention(qz, q, SM_SCALE), w.io_dtype, ATOL)
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    kvq.kvq_decode_attn_noalloc(case.layout, dev(q), case.cache.struct, SM_SCALE, S, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype),
+                          got)
+
+
+def test_prog_guard_bands_survive():
+    # every cache section (the plane windows included), the workspace and the
+    # output between canary bands through prefill, appends that pack and
+    # shrink, and decode at several split counts
+    from tests.test_gpu_canary import Guarded
+    w = kvq_synth.Workload("prog-canary", 2, 8, 2, 32 * 9 + 64 + 7, n_qry=8, n_app=70,
+                           io_dtype="bf16", outliers="pct2x10", n_pairs_hi=6, residual=64,
+                           seed=67, prog_w8=2, prog_w4=4)
+    d = kvq_synth.generate(w)
+    T0 = w.tokens
+    layout = kvq.make_layout(w.batch, w.n_q_heads, w.n_kv_heads, n_pairs_hi=w.n_pairs_hi,
+                             residual=w.residual, max_tokens=T0 + w.n_app + 8,
+                             io_dtype=w.io_dtype, prog_w8=w.prog_w8, prog_w4=w.prog_w4)
+    sizes = kvq.kvq_cache_sizes(layout)
+    assert sizes[12] > 0 and sizes[13] > 0
+    bufs = [Guarded(n) for n in sizes]
+    cache = kvq.kvq_cache(*[b.ptr() for b in bufs])
+    q_sel = Guarded(d["q_sel"].nbytes, d["q_sel"])
+    k0 = Guarded(d["k"][:, :, :T0].nbytes, d["k"][:, :, :T0])
+    v0 = Guarded(d["v"][:, :, :T0].nbytes, d["v"][:, :, :T0])
+    q = Guarded(d["q_dec"][:, :, 0].nbytes, d["q_dec"][:, :, 0])
+    out = Guarded(w.batch * w.n_q_heads * 128 * 2)
+    S_list = [1, 3, 32]
+    ws = Guarded(max(kvq.kvq_workspace_bytes(layout, S) for S in S_list))
+    kvq.kvq_select_pairs(layout, q_sel.ptr(), w.n_qry, k0.ptr(), T0, cache)
+    kvq.kvq_quant_keys(layout, k0.ptr(), T0, cache)
+    kvq.kvq_quant_values(layout, v0.ptr(), T0, cache)
+    inputs = [q_sel, k0, v0, q]
+    for i in range(w.n_app):
+        kn = Guarded(d["k"][:, :, T0 + i].nbytes, d["k"][:, :, T0 + i])
+        vn = Guarded(d["v"][:, :, T0 + i].nbytes, d["v"][:, :, T0 + i])
+        kvq.kvq_append(layout, kn.ptr(), vn.ptr(), cache)
+        inputs += [kn, vn]
+        if i % 23 == 0:
+            for S in S_list:
+                kvq.kvq_decode_attn(layout, q.ptr(), cache, SM_SCALE, S, ws.ptr(), out.ptr(),
+                                    ws_bytes=ws.n)
+    kvq.kvq_decode_attn_noalloc(layout, q.ptr(), cache, SM_SCALE, 3, out.ptr())
+    torch.cuda.synchronize()
+    assert kvq.kvq_check(cache) == 0
+    bad = [kvq.BUF_NAMES[i] for i, b in enumerate(bufs) if not b.bands_intact()]
+    bad += [nm for nm, b in (("workspace", ws), ("out", out)) if not b.bands_intact()]
+    bad += ["input %d" % i for i, b in enumerate(inputs) if not b.bands_intact()]
+    assert not bad, "guard bands overwritten: %s" % bad
