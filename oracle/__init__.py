@@ -251,7 +251,7 @@ def pack(qz: Quantized) -> dict:
     lib = _load()
     B, Hkv, Tstride, _ = qz.k.shape
     NG = qz.NG
-    k_lo = np.zeros((B, Hkv, NG, 256), np.uint32)
+    k_lo = np.zeros((B, Hkv, NG, 192 if dense1(qz.n_hi, qz.n_lo1) else 256), np.uint32)
     k_hi = np.zeros((B, Hkv, NG, max(k_hi_words(qz.n_hi, qz.bits_hi), 1)), np.uint8)
     k_meta = np.zeros((B, Hkv, NG, 256), np.uint16)
     v_codes = np.zeros((B, Hkv, NG, 256), np.uint32)
@@ -298,6 +298,12 @@ def live_plane_slots(T: int, R: int, w8: int, w4: int):
         if ng - 1 - g < w8:
             out += [(g, w4 + 2 * (g % w8)), (g, w4 + 2 * (g % w8) + 1)]
     return out
+
+
+def dense1(n_pairs_hi: int, n_pairs_lo1: int) -> bool:
+    """The dense 1-bit layout (the 1.5-bit point): half of the pairs at one
+    bit, none salient; k_lo holds 768 bytes per group in plane order."""
+    return bool(_load().orc_dense1(int(n_pairs_hi), int(n_pairs_lo1)))
 
 
 def live_ring_slots(T: int, R: int) -> np.ndarray:

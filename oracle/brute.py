@@ -67,6 +67,41 @@ def _tile_index(t: int) -> int:
     return 16 * T + r
 
 
+def _bit1_pos(c: int) -> int:
+    # the bit of run channel c in a 1-bit half-word (include/kvq.h, k_lo)
+    return 4 * (c & 1) + ((c >> 1) & 1) + 8 * ((c >> 2) & 1) + 2 * (c >> 3)
+
+
+def unpack_keys_dense1(k_lo, k_meta, one_bit_pairs):
+    """One group record of the dense 1-bit layout -> (codes [128][32],
+    s_bits [128], z_bits [128]).  Plane order: the 2-bit channels ascending
+    (wl) and the 1-bit ones (ol), each a pair's first channel before the
+    second ones; chunk kq = 2-bit run wl[16kq ..] then 1-bit run ol[16kq ..]."""
+    one = set(int(p) for p in one_bit_pairs)
+    wl = [c for c in range(D) if c % 64 not in one]
+    ol = [c for c in range(D) if c % 64 in one]
+    assert len(wl) == len(ol) == 64
+    words = np.asarray(k_lo, np.uint32)
+    halves = np.frombuffer(words[128:192].tobytes(), np.uint16)
+    codes = np.zeros((D, GS), np.int64)
+    for t in range(GS):
+        T, r = divmod(_tile_index(t), 16)
+        for kq in range(4):
+            w = int(words[(kq * 2 + T) * 16 + r])
+            h = int(halves[(kq * 2 + T) * 16 + r])
+            for c in range(16):
+                codes[wl[16 * kq + c], t] = _code(w, _pos(c))
+                codes[ol[16 * kq + c], t] = (h >> _bit1_pos(c)) & 1
+    meta = np.asarray(k_meta, np.uint16).reshape(8, 2, 16)
+    s = np.zeros(D, np.uint16)
+    z = np.zeros(D, np.uint16)
+    for kq in range(4):
+        for c in range(16):
+            s[wl[16 * kq + c]], z[wl[16 * kq + c]] = meta[2 * kq, 0, c], meta[2 * kq, 1, c]
+            s[ol[16 * kq + c]], z[ol[16 * kq + c]] = meta[2 * kq + 1, 0, c], meta[2 * kq + 1, 1, c]
+    return codes, s, z
+
+
 def unpack_keys(k_lo, k_hi, k_meta, salient: list[int], bits_hi: int):
     """One group record -> (codes [128][32], raw16 [len(salient)][32] or None,
     s_bits [128], z_bits [128]).  `salient` = ascending salient channels."""

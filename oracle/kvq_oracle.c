@@ -529,9 +529,39 @@ static int tile_token(int e) {
 /* Position of element c inside its 4-aligned block: bits 0 and 1 swapped. */
 static int pos_swap(int c) { return (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1); }
 
+/* The dense 1-bit layout (PN-Mix, abstract: the cache degrades gracefully
+ * down to 1.5 bits; reading: with exactly half of the pairs at one bit and
+ * no salient pairs, the 1-bit codes take one bit each).  Channels go in
+ * "plane order": wl lists the 2-bit channels ascending, ol the 1-bit ones;
+ * chunk kq (0..3) is the 2-bit run wl[16 kq ..] (u = 0) then the 1-bit run
+ * ol[16 kq ..] (u = 1).  k_lo [..][NG][192] u32: words (kq*2 + T)*16 + r
+ * hold the 2-bit run kq of the token at tile index 16T + r, channel
+ * wl[16 kq + c] at position pos_swap(c); then (byte 512 on) u16 half-words
+ * (kq*2 + T)*16 + r hold the 1-bit run kq, channel ol[16 kq + c] at bit
+ * onebit_pos(c).  k_meta follows plane order: run 2 kq + u. */
+int orc_dense1(int n_hi, int n_lo1) { return n_hi == 0 && n_lo1 == NPAIR / 2; }
+
+/* Bit of the code of run channel c in a 1-bit half-word, chosen so that the
+ * four nibble masks (h >> i) & 0x1111 deliver the channels in order. */
+static int onebit_pos(int c) {
+  return 4 * (c & 1) + ((c >> 1) & 1) + 8 * ((c >> 2) & 1) + 2 * (c >> 3);
+}
+
+/* Plane lists of one (b, kv head): wl = 2-bit channels, ol = 1-bit ones,
+ * each ascending (the pairs' first channels, then their second ones). */
+static void orc_plane_lists(const int32_t *pr, int n_lo1, int *wl, int *ol) {
+  int one[NPAIR] = {0}, nw = 0, no = 0;
+  for (int r = NPAIR - n_lo1; r < NPAIR; r++) one[pr[r] & (NPAIR - 1)] = 1;
+  for (int c = 0; c < D; c++) {
+    if (one[c % NPAIR]) ol[no++] = c;
+    else wl[nw++] = c;
+  }
+}
+
 /* Packs the logical key codes of groups [0, ng) into the byte records.
- * k_lo [..][NG][256] u32, k_hi (4-bit: [..][NG][32] u32; 16-bit:
- * [..][NG][32][2*n_hi] u16 raw), k_meta [..][NG][8][2][16] u16. */
+ * k_lo [..][NG][256] u32 ([..][NG][192] in the dense 1-bit layout), k_hi
+ * (4-bit: [..][NG][32] u32; 16-bit: [..][NG][32][2*n_hi] u16 raw), k_meta
+ * [..][NG][8][2][16] u16. */
 /* Key records in the group's token order: tile index e holds the token at
  * slot tile_token(e), i.e. position order[tile_token(e)]. */
 int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
@@ -539,16 +569,42 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
                   const uint8_t *order, const uint8_t *codes, const uint16_t *s,
                   const uint16_t *z, uint32_t *k_lo, void *k_hi, uint16_t *k_meta) {
   int ng = orc_n_quant(T, R) / GS;
+  const int dense = orc_dense1(n_hi, n_lo1);
   for (int b = 0; b < B; b++)
     for (int kh = 0; kh < Hkv; kh++) {
       const int32_t *pr = pairs + (size_t)(b * Hkv + kh) * NPAIR;
       int hil[16], nh = 0; /* salient channels, ascending */
       for (int c = 0; c < D; c++)
         if (orc_is_salient(pr, n_hi, c)) hil[nh++] = c;
+      int wl[D], ol[D];
+      if (dense) orc_plane_lists(pr, n_lo1, wl, ol);
       for (int g = 0; g < ng; g++) {
         size_t grp = (size_t)(b * Hkv + kh) * NG + g;
         const uint8_t *cg = codes + grp * D * GS;
         const uint8_t *ord = order + grp * GS;
+        if (dense) {
+          uint32_t *lo = k_lo + grp * 192;
+          uint16_t *lo1 = (uint16_t *)(lo + 128);
+          memset(lo, 0, 192 * 4);
+          for (int e = 0; e < 32; e++) {
+            int t = ord[tile_token(e)], Tt = e / 16, r = e % 16;
+            for (int kq = 0; kq < 4; kq++)
+              for (int c = 0; c < 16; c++) {
+                int w_idx = (kq * 2 + Tt) * 16 + r;
+                lo[w_idx] |= (uint32_t)(cg[wl[16 * kq + c] * GS + t] & 3) << (2 * pos_swap(c));
+                lo1[w_idx] |= (uint16_t)((cg[ol[16 * kq + c] * GS + t] & 1) << onebit_pos(c));
+              }
+          }
+          uint16_t *meta = k_meta + grp * 256;
+          for (int kq = 0; kq < 4; kq++)
+            for (int c = 0; c < 16; c++) {
+              meta[(2 * kq) * 32 + c] = s[grp * D + wl[16 * kq + c]];
+              meta[(2 * kq) * 32 + 16 + c] = z[grp * D + wl[16 * kq + c]];
+              meta[(2 * kq + 1) * 32 + c] = s[grp * D + ol[16 * kq + c]];
+              meta[(2 * kq + 1) * 32 + 16 + c] = z[grp * D + ol[16 * kq + c]];
+            }
+          continue;
+        }
         uint32_t *lo = k_lo + grp * 256;
         memset(lo, 0, 256 * 4);
         for (int e = 0; e < 32; e++) {

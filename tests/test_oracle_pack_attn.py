@@ -41,6 +41,29 @@ VARIANTS = [
 ]
 
 
+def _unpack(w, pk, pairs, b, kh, g, sal):
+    """A key record read back bit by bit: the dense 1-bit layout (the
+    1.5-bit point) or the 2-bit slot layout."""
+    if oracle.dense1(w.n_pairs_hi, w.n_pairs_lo1):
+        codes, s, z = brute.unpack_keys_dense1(pk["k_lo"][b, kh, g], pk["k_meta"][b, kh, g],
+                                               pairs[b, kh, 64 - w.n_pairs_lo1:])
+        return codes, None, s, z
+    return brute.unpack_keys(pk["k_lo"][b, kh, g], pk["k_hi"][b, kh, g], pk["k_meta"][b, kh, g],
+                             sal, w.bits_hi)
+
+
+def test_dense_one_bit_layout_is_smaller():
+    # the 1.5-bit point stores one bit per 1-bit code: 768 bytes of key codes
+    # per group against 1024 for the 2.0-bit point; every bit position of a
+    # 1-bit half-word is used once
+    assert sorted(brute._bit1_pos(c) for c in range(16)) == list(range(16))
+    w2 = VARIANTS[-2].replace(n_pairs_lo1=0)
+    for w, words in ((VARIANTS[-2], 192), (w2, 256)):
+        d, pairs, qz = _setup(w)
+        assert oracle.pack(qz)["k_lo"].shape[-1] == words
+    assert oracle.dense1(0, 32) and not oracle.dense1(6, 32) and not oracle.dense1(0, 16)
+
+
 @pytest.mark.parametrize("w", VARIANTS, ids=lambda w: w.name)
 def test_pack_roundtrip(w):
     d, pairs, qz = _setup(w)
@@ -51,9 +74,7 @@ def test_pack_roundtrip(w):
         for kh in range(w.n_kv_heads):
             sal = _salient(pairs[b, kh], w.n_pairs_hi)
             for g in range(ng):
-                codes, raw, s, z = brute.unpack_keys(
-                    pk["k_lo"][b, kh, g], pk["k_hi"][b, kh, g], pk["k_meta"][b, kh, g],
-                    sal, w.bits_hi)
+                codes, raw, s, z = _unpack(w, pk, pairs, b, kh, g, sal)
                 assert np.array_equal(codes, qz.kcodes[b, kh, g])
                 assert np.array_equal(s, qz.ks[b, kh, g]) and np.array_equal(z, qz.kz[b, kh, g])
                 if raw is not None:
@@ -78,8 +99,7 @@ def _dequant_from_bytes(w, d, pairs, pk, b, kh, T):
     V = kvq_synth.bits_to_f64(d["v"][b, kh, :T], w.io_dtype).copy()
     sal = _salient(pairs[b, kh], w.n_pairs_hi)
     for g in range(nq // 32):
-        codes, raw, s, z = brute.unpack_keys(pk["k_lo"][b, kh, g], pk["k_hi"][b, kh, g],
-                                             pk["k_meta"][b, kh, g], sal, w.bits_hi)
+        codes, raw, s, z = _unpack(w, pk, pairs, b, kh, g, sal)
         for c in range(128):
             if w.bits_hi == 16 and c in sal:
                 continue
