@@ -37,7 +37,7 @@ PEAK_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_traffic_llama3-8b-32k.md")
 # the decode kernel instance of the default workload: bf16, 4-bit salient
 # digits, quantized groups, unpruned, one value precision, no append, G <= 8
-DECODE_KERNEL = "_ZN3kvq13decode_kernelILb1ELi4ELb1ELi0ELb0ELb0ELb1ELb0EEEv"
+DECODE_KERNEL = "_ZN3kvq13decode_kernelILb1ELi4ELb1ELi0ELb0ELb0ELb1ELb0ELb0EEEv"
 
 
 def kernel_code_hash(symbol_prefix: str = DECODE_KERNEL, lib_path: str = None):
@@ -188,9 +188,10 @@ def layout_bytes(cache, w, T: int) -> int:
     nr = T - nq
     ng = nq // 32
     bh = w.batch * w.n_kv_heads
+    klo = cache.sizes[0] // max(1, bh * cache_ng(cache, w))  # 768 in the dense 1-bit layout
     khi = cache.sizes[1] // max(1, bh * cache_ng(cache, w))
     vhi = cache.sizes[11] // max(1, bh * cache_ng(cache, w))
-    per_grp = 1024 + khi + 512 + 1024 + 512 + vhi
+    per_grp = klo + khi + 512 + 1024 + 512 + vhi
     return bh * (ng * per_grp + nr * 512) + 2 * w.batch * w.n_q_heads * 128 * 2
 
 

@@ -129,6 +129,8 @@ Geo make_geo(const kvq_layout* L) {
   g.w4 = L->prog_w4;
   g.w8 = g.w4 > 0 ? L->prog_w8 : 0;
   g.npl = g.w4 + 2 * g.w8;
+  g.dense1 = g.n_hi == 0 && g.n_lo1 == NPAIR / 2;
+  g.klo_bytes = g.dense1 ? 768 : GROUP_WORDS * 4;
   return g;
 }
 
@@ -172,7 +174,7 @@ kvq_status kvq_cache_sizes(const kvq_layout* L, size_t sizes[KVQ_NBUF]) {
   const Geo g = make_geo(L);
   const size_t bh = (size_t)g.B * g.Hkv, grp = bh * g.NG;
   const size_t el = 2;  // bytes of a 16-bit value
-  sizes[0] = grp * GROUP_WORDS * 4;  // k_lo
+  sizes[0] = grp * g.klo_bytes;      // k_lo
   // k_hi; raw 16-bit salient rows (2*nh bytes) are read 16 bytes at a time
   // from channel 0 or 8 of a row: the last row's read ends at most 32 - 2*nh
   // bytes past the record, so 32 bytes of tail slack keep it in the buffer
@@ -288,6 +290,7 @@ static kvq_status decode_common(const kvq_layout* L, const void* q, const kvq_ca
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_EINVAL;
   if (keep < 0 || keep > 8) return KVQ_EINVAL;
   if (g.w4 > 0 && keep != 8) return KVQ_ENOTSUP;
+  if (g.dense1 && keep >= 1 && keep < 8) return KVQ_ENOTSUP;
   if (kvq_status s = check_ptr(q)) return s;
   if (kvq_status s = check_ptr(out)) return s;
   if (kvq_status s = check_ptr(workspace)) return s;

@@ -17,7 +17,7 @@ namespace kvq {
 
 typedef uint32_t cu4 __attribute__((ext_vector_type(4)));
 
-template <int HIMODE, bool VHI>
+template <int HIMODE, bool VHI, bool DENSE1>
 __global__ __launch_bounds__(WG_THREADS) void ceiling_kernel(Geo g, kvq_cache c, int S,
                                                              uint32_t* sink) {
   using SC = SlotCfg<HIMODE, VHI>;
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(WG_THREADS) void ceiling_kernel(Geo g, kvq_cache c,
     if (g.NG > 0) {
 #pragma unroll
       for (int i = 0; i < NSLOT; i++)
-        issue_group<HIMODE, VHI, false>(c, rec0 + (size_t)min(gfirst + i * STR, g.NG - 1),
+        issue_group<HIMODE, VHI, false, DENSE1>(c, rec0 + (size_t)min(gfirst + i * STR, g.NG - 1),
                                         sl + i * SLOTB, lane, 0xFFu, 0, g.nh, g.n_vhi);
     }
   };
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(WG_THREADS) void ceiling_kernel(Geo g, kvq_cache c,
     if (issued < nmine) {
       wait_lgkmcnt0();  // the slot's read is done before its refill lands
       compiler_fence();
-      issue_group<HIMODE, VHI, false>(c, rec0 + gfirst + (size_t)issued * STR, slot, lane, 0xFFu,
+      issue_group<HIMODE, VHI, false, DENSE1>(c, rec0 + gfirst + (size_t)issued * STR, slot, lane, 0xFFu,
                                       0, g.nh, g.n_vhi);
       issued++;
     }
@@ -83,23 +83,24 @@ __global__ __launch_bounds__(WG_THREADS) void ceiling_kernel(Geo g, kvq_cache c,
   if (acc == 0x9E3779B9u) sink[0] = acc ^ (uint32_t)tid;
 }
 
-template <int HIMODE>
+template <int HIMODE, bool DENSE1>
 static void launch_ceiling_h(const Geo& g, const kvq_cache& c, int S, uint32_t* sink,
                              hipStream_t st) {
   const dim3 grid(g.B * g.Hkv * S);
   if (g.n_vhi > 0)
-    hipLaunchKernelGGL((ceiling_kernel<HIMODE, true>), grid, dim3(WG_THREADS), 0, st, g, c, S,
-                       sink);
+    hipLaunchKernelGGL((ceiling_kernel<HIMODE, true, DENSE1>), grid, dim3(WG_THREADS), 0, st, g,
+                       c, S, sink);
   else
-    hipLaunchKernelGGL((ceiling_kernel<HIMODE, false>), grid, dim3(WG_THREADS), 0, st, g, c, S,
-                       sink);
+    hipLaunchKernelGGL((ceiling_kernel<HIMODE, false, DENSE1>), grid, dim3(WG_THREADS), 0, st, g,
+                       c, S, sink);
 }
 
 hipError_t launch_ceiling(const Geo& g, const kvq_cache* c, int S, void* sink, hipStream_t st) {
   const int hm = g.n_hi == 0 ? 0 : g.bits_hi;
-  if (hm == 0) launch_ceiling_h<0>(g, *c, S, (uint32_t*)sink, st);
-  else if (hm == 4) launch_ceiling_h<4>(g, *c, S, (uint32_t*)sink, st);
-  else launch_ceiling_h<16>(g, *c, S, (uint32_t*)sink, st);
+  if (hm == 0 && g.dense1) launch_ceiling_h<0, true>(g, *c, S, (uint32_t*)sink, st);
+  else if (hm == 0) launch_ceiling_h<0, false>(g, *c, S, (uint32_t*)sink, st);
+  else if (hm == 4) launch_ceiling_h<4, false>(g, *c, S, (uint32_t*)sink, st);
+  else launch_ceiling_h<16, false>(g, *c, S, (uint32_t*)sink, st);
   return hipGetLastError();
 }
 

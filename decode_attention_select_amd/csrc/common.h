@@ -32,7 +32,16 @@ struct Geo {
   int w8, w4;          // progressive precision: groups younger than w8 at 8 bits,
                        // younger than w4 at 4 or more (w4 == 0: off)
   int npl;             // digit-plane slots per (b, kv head): w4 + 2 w8
+  int dense1;          // the dense 1-bit layout (n_hi == 0, n_lo1 == 32): k_lo in plane order
+  int klo_bytes;       // bytes of a group's k_lo record: 768 dense, else 1024
 };
+
+// Bit of run channel c (0..15) in a 1-bit word of the dense layout, tile
+// half 0 (half 1: + 16): the nibble masks (w >> i) & 0x11111111, i = 0..3,
+// then deliver the run's channels in order through the fp4 converts.
+__host__ __device__ inline int onebit_pos(int c) {
+  return 4 * (c & 1) + ((c >> 1) & 1) + 8 * ((c >> 2) & 1) + 2 * (c >> 3);
+}
 
 // Bits of a progressive group of age a (0 = the newest quantized group).
 __host__ __device__ inline int prog_width(int a, int w8, int w4) {

@@ -319,6 +319,8 @@ struct Lds {
   __align__(16) uint16_t q16[MAXG][D + 8];   // query as fp16 (scaled), every head
   __align__(16) uint16_t qraw[MAXG][D + 8];  // query in the io dtype, scaled (HIMODE 16)
   int hil[16];                               // salient channels, ascending
+  uint8_t plist[2][64];                      // DENSE1: the 2-bit (0) and 1-bit (1) channels, ascending
+  uint8_t pone[64];                          // DENSE1: pair j is a 1-bit pair
   uint16_t sal_s[NW][16];                    // per wave: salient scales of the group in work
   int mrank;                                 // -1: not the last split; 0/1: merge (1: all splits on this XCD)
 #ifdef KVQ_STAMPS
@@ -365,8 +367,13 @@ template <bool B>
 struct Wide {
   static constexpr bool value = B;
 };
+// DENSE1 (the dense 1-bit layout, no salient pairs): chunk kq of the keys is
+// the 2-bit run of plane channels wl[16 kq ..] and the 1-bit run ol[16 kq ..]
+// (k_lo words, then half-words); the query enters the group MFMAs in that
+// plane order, gathered once from its LDS copy, and the 1-bit run's codes
+// come from four nibble masks of its half-word.
 template <bool BF16, int HIMODE, bool HASQ, int KB, bool VHI, bool FUSED, bool LOCOL,
-          bool PROG = false>
+          bool PROG = false, bool DENSE1 = false>
 __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             kvq_cache c, float scale_log2, int S,
                                                             Ws ws, uint16_t* __restrict__ out,
@@ -378,6 +385,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   constexpr int NSLOT = SC::NSLOT, NLD = SC::NLD, SLOTB = SC::BYTES;
   static_assert(!PROG || (NSLOT >= 3 && SLOTB >= 3072 && !PRUNE && !VHI && !FUSED),
                 "a window group takes three slots: its record and three planes per side");
+  static_assert(!DENSE1 || (HIMODE == 0 && !PRUNE && !PROG), "dense 1-bit layout variants");
   __shared__ Lds<SLOTB, NSLOT> lds;
   // the wave index is wave-uniform: keeping it in a scalar register makes every
   // group address scalar (one 64-bit base per copy, no per-lane address math)
@@ -416,6 +424,11 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       const int row = min(4 * i + (lane >> 4), G - 1);
       dma16(qsrc + (size_t)row * (D * 2) + (lane & 15) * 16, &lds.qin[4 * i][0]);
     }
+    // DENSE1: the rank table (256 bytes, lanes past 16 repeat it) into the
+    // LDS the raw-salient query would use (unused without salient pairs),
+    // with the query: a load issued after the group copies would wait for them
+    if constexpr (DENSE1)
+      dma16((const uint8_t*)(c.pairs + (size_t)bh * NPAIR) + (lane & 15) * 16, &lds.qraw[0][0]);
   }
   const int RSB = g.RS / GS;        // physical ring blocks
   const int STR = S * NW;           // flat indices of one (sequence, KV head)
@@ -442,7 +455,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     if constexpr (HASQ) {
 #pragma unroll
       for (int i = 0; i < NSLOT; i++)
-        issue_group<HIMODE, VHI, PRUNE>(c, rec0 + (size_t)min(gfirst + i * STR, g.NG - 1),
+        issue_group<HIMODE, VHI, PRUNE, DENSE1>(c, rec0 + (size_t)min(gfirst + i * STR, g.NG - 1),
                                         slots + i * SLOTB, lane, kmask, kept0, g.nh, g.n_vhi);
       issued = NSLOT;
     }
@@ -565,12 +578,39 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // same on lo lanes and zero elsewhere, so that pk_fma(q, s, -q_m s) gives
   // the rounding hi of q*s on hi lanes and its residual lo on lo lanes
   uint32_t q16[16], qm[16];
+  // DENSE1: the group MFMAs take the query in plane order (k_lo layout):
+  // element 8i + 2e (+1) of chunk kq is wl[16 kq + 8i + 2e (+1)] for i < 2 and
+  // ol[16 kq + 8 (i - 2) + 2e (+1)] for i >= 2; the ring keeps channel order
+  u4 qg[4] = {qv[0], qv[1], qv[2], qv[3]};
+  if constexpr (DENSE1) {
+    // the 1-bit pairs (ranks 32 .. 63): rank lane's pair gets its flag (the
+    // ranks are a permutation, so every flag is written once)
+    lds.pone[((const int32_t*)&lds.qraw[0][0])[lane] & (NPAIR - 1)] = lane >= NPAIR / 2;
+    __builtin_amdgcn_wave_barrier();
+    compiler_fence();
+    const uint64_t one = __ballot(lds.pone[lane] != 0);
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const bool isone = (one >> lane) & 1ull;
+    const int rk = __popcll((isone ? one : ~one) & below);
+    // every wave writes the same lists and reads only after its own writes
+    lds.plist[isone][rk] = (uint8_t)lane;
+    lds.plist[isone][32 + rk] = (uint8_t)(lane + NPAIR);
+    __builtin_amdgcn_wave_barrier();
+    compiler_fence();
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const uint8_t* lst = &lds.plist[i >> 1][16 * kq + 8 * (i & 1) + 2 * e];
+        qg[i][e] = (uint32_t)lds.qin[hq][lst[0]] | ((uint32_t)lds.qin[hq][lst[1]] << 16);
+      }
+  }
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       float a, bb;
-      io_pair_f32<BF16>(qv[i][e], a, bb);
+      io_pair_f32<BF16>(qg[i][e], a, bb);
       q16[4 * i + e] = qvalid ? pk_rne(a * qsc, bb * qsc) : 0u;
       qm[4 * i + e] = lo_lane ? q16[4 * i + e] : 0u;
     }
@@ -782,6 +822,13 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         qshi[e] = kq < 2 ? hi : pk_fma_lo(qhi[e], spv[e], hi);
       }
     }
+    // DENSE1: the 1-bit run's word of tile row col (both halves), masked once
+    uint32_t X1b[4] = {0, 0, 0, 0};
+    if constexpr (DENSE1) {
+      const uint32_t w1 = ((const uint32_t*)(slot + SC::KLO + 512))[kqa * 16 + col];
+#pragma unroll
+      for (int i = 0; i < 4; i++) X1b[i] = (w1 >> i) & 0x11111111u;
+    }
     f4 C[2];
 #pragma unroll
     for (int TT = 0; TT < 2; TT++) {
@@ -799,6 +846,33 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
           acc = mma_f16(cd, u4{qs[4 * i], qs[4 * i + 1], qs[4 * i + 2], qs[4 * i + 3]}, acc);
           if constexpr (!LOCOL)
             acc = mma_f16(cd, u4{qsl[4 * i], qsl[4 * i + 1], qsl[4 * i + 2], qsl[4 * i + 3]}, acc);
+        }
+      } else if constexpr (DENSE1) {
+        // chunk kqa: its 2-bit run (u = 0) and its 1-bit run (u = 1; tile
+        // half TT in bytes 2 TT, 2 TT + 1 of the masks shared by both halves)
+        const uint32_t w2 = ((const uint32_t*)(slot + SC::KLO))[(kqa * 2 + TT) * 16 + col];
+        {
+          const uint32_t A = w2 & 0x33333333u, Bn = (w2 >> 2) & 0x33333333u;
+          const u4 c0 = u4{cvt2<0>(A), cvt2<0>(Bn), cvt2<1>(A), cvt2<1>(Bn)};
+          const u4 c1 = u4{cvt2<2>(A), cvt2<2>(Bn), cvt2<3>(A), cvt2<3>(Bn)};
+          acc = mma_f16(c0, u4{qs[0], qs[1], qs[2], qs[3]}, acc);
+          acc = mma_f16(c1, u4{qs[4], qs[5], qs[6], qs[7]}, acc);
+          if constexpr (!LOCOL) {
+            acc = mma_f16(c0, u4{qsl[0], qsl[1], qsl[2], qsl[3]}, acc);
+            acc = mma_f16(c1, u4{qsl[4], qsl[5], qsl[6], qsl[7]}, acc);
+          }
+        }
+        {
+          const u4 c0 = TT == 0 ? u4{cvt2<0>(X1b[0]), cvt2<0>(X1b[1]), cvt2<1>(X1b[0]), cvt2<1>(X1b[1])}
+                                : u4{cvt2<2>(X1b[0]), cvt2<2>(X1b[1]), cvt2<3>(X1b[0]), cvt2<3>(X1b[1])};
+          const u4 c1 = TT == 0 ? u4{cvt2<0>(X1b[2]), cvt2<0>(X1b[3]), cvt2<1>(X1b[2]), cvt2<1>(X1b[3])}
+                                : u4{cvt2<2>(X1b[2]), cvt2<2>(X1b[3]), cvt2<3>(X1b[2]), cvt2<3>(X1b[3])};
+          acc = mma_f16(c0, u4{qs[8], qs[9], qs[10], qs[11]}, acc);
+          acc = mma_f16(c1, u4{qs[12], qs[13], qs[14], qs[15]}, acc);
+          if constexpr (!LOCOL) {
+            acc = mma_f16(c0, u4{qsl[8], qsl[9], qsl[10], qsl[11]}, acc);
+            acc = mma_f16(c1, u4{qsl[12], qsl[13], qsl[14], qsl[15]}, acc);
+          }
         }
       } else {
         const uint32_t* kw0 = (const uint32_t*)(slot + SC::KLO) + (kqa * 4 + TT) * 16 + col;
@@ -1038,7 +1112,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
          it += STR) {
       const int age = it - RSB, gw = ngq - 1 - age;
       const int width = prog_width(age, g.w8, g.w4);
-      issue_group<HIMODE, VHI, false>(c, rec0 + gw, slots, lane, 0xFFu, 0, g.nh, g.n_vhi);
+      issue_group<HIMODE, VHI, false, DENSE1>(c, rec0 + gw, slots, lane, 0xFFu, 0, g.nh, g.n_vhi);
       const size_t p1 = ((size_t)bh * g.npl + gw % g.w4) * 1024 + lane * 16;
       dma16<CPOL_NT>((const uint8_t*)c.k_pl + p1, s1);
       dma16<CPOL_NT>((const uint8_t*)c.v_pl + p1, s2);
@@ -1073,7 +1147,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         // every read of this slot has returned before the copy overwrites it
         wait_lgkmcnt0();
         compiler_fence();
-        issue_group<HIMODE, VHI, PRUNE>(c, rec0 + gfirst + (size_t)issued * STR, slot, lane,
+        issue_group<HIMODE, VHI, PRUNE, DENSE1>(c, rec0 + gfirst + (size_t)issued * STR, slot, lane,
                                         kmask, kept0, g.nh, g.n_vhi);
         issued++;
       }
@@ -1345,6 +1419,14 @@ struct Launch {
 template <bool BF16, int HIMODE, int KB, bool VHI, bool FUSED, bool LOCOL>
 static void launch_cols(const Geo& g, int keep, const Launch& a) {
   const dim3 grid(g.B * g.Hkv * a.S), block(WG_THREADS);
+  if constexpr (HIMODE == 0 && KB == 0) {
+    if (g.NG > 0 && g.dense1) {
+      hipLaunchKernelGGL((decode_kernel<BF16, 0, true, 0, VHI, FUSED, LOCOL, false, true>), grid,
+                         block, 0, a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,
+                         (uint16_t*)a.out, (const uint16_t*)a.knew, (const uint16_t*)a.vnew, keep);
+      return;
+    }
+  }
   if constexpr (KB == 0 && !VHI && !FUSED) {
     if (g.NG > 0 && g.w4 > 0) {
       hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, 0, false, false, LOCOL, true>), grid,

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint1
   const int width = g.w4 > 0 ? prog_width(n_quant(T, g.R) / GS - 1 - grp, g.w8, g.w4) : 0;
   key_group_wave<BF, VHI>(g, k + ((size_t)bh * T + (size_t)grp * GS) * D,
                           pair_masks(g, c.pairs + (size_t)bh * NPAIR),
-                          (uint32_t*)c.k_lo + rec * GROUP_WORDS,
+                          (uint32_t*)((uint8_t*)c.k_lo + rec * g.klo_bytes),
                           (uint8_t*)c.k_hi + rec * g.khi_bytes, (uint16_t*)c.k_meta + rec * 2 * D,
                           lds[wave], width, width >= 4 ? plane1(g, c.k_pl, bh, grp) : nullptr,
                           width == 8 ? plane23(g, c.k_pl, bh, grp) : nullptr);
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * SHRINK_WAVES) void shrink_kernel(Geo g, kvq_ca
   const size_t rec = (size_t)bh * g.NG + grp;
   const int e = lane, T = e >> 4, r = e & 15;
   uint32_t* hi = (uint32_t*)c.k_hi + rec * 32;
-  uint32_t* lo = (uint32_t*)c.k_lo + rec * GROUP_WORDS;
+  uint32_t* lo = (uint32_t*)((uint8_t*)c.k_lo + rec * g.klo_bytes);
   uint2 lw[4];
 #pragma unroll
   for (int kq = 0; kq < 4; kq++)

@@ -323,6 +323,38 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
   // (digit * 4^position, below 2^16); the high digits of 4-bit channels as
   // integers, only for channel slots k where some lane holds a 4-bit channel
   refresh(v);
+  if (g.dense1 && width == 0) {
+    // the dense 1-bit layout: channel c goes to plane run 2 kq' + u (u = 1
+    // for a 1-bit pair), place cc = rank % 16, where rank counts the
+    // channels of its class below it (first channels, then second ones)
+    if (lane < 48) ((uint4*)L.lo)[lane] = make_uint4(0, 0, 0, 0);
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int c = 8 * cb + k, j = c & (NPAIR - 1);
+      const bool one = (pm.one >> j) & 1ull;
+      const uint64_t below = j ? (~0ull >> (64 - j)) : 0ull;
+      const int rank = 32 * (c >> 6) + __popcll((one ? pm.one : ~pm.one) & below);
+      const int kqp = rank >> 4, cc = rank & 15;
+      const float z = half_bits_to_f32((uint16_t)(sz[k] >> 16));
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint32_t code = (uint32_t)qcode(in_to_f32(half_of(v[i], k), BF), z, rr[k], lv[k]);
+        const int T = i >> 2, r = 4 * tq + (i & 3);
+        if (one) {  // word kq' * 16 + r, tile half T in bits 16 T ..
+          if (code) atomicOr(&L.lo[128 + kqp * 16 + r], code << (onebit_pos(cc) + 16 * T));
+        } else if (code) {
+          atomicOr(&L.lo[(kqp * 2 + T) * 16 + r], code << (2 * pos_swap(cc)));
+        }
+      }
+      if (tq < 2)  // run 2 kq' + u: 16 scales (tq 0), then 16 zeros (tq 1)
+        meta_out[(2 * kqp + (one ? 1 : 0)) * 32 + tq * 16 + cc] =
+            (uint16_t)(tq == 0 ? sz[k] & 0xFFFFu : sz[k] >> 16);
+    }
+    wave_lds_sync();
+    if (lane < 48) ((uint4*)lo_out)[lane] = ((const uint4*)L.lo)[lane];
+    return;
+  }
   float hwf[8];
   uint32_t hw[8], hh[8];
   uint32_t pw[3][8];  // progressive: digits 1..3 (half-words like hw)
@@ -773,7 +805,7 @@ __device__ void pack_ring_group(const Geo& g, kvq_cache& c, int bh, int nq0, int
                        plane23(g, kpl, bh, gB), 8, toB, lds.key);
     }
     key_group_wave<BF, VHI>(g, rk + (size_t)s0 * D, pm,
-                            (uint32_t*)c.k_lo + rec * GROUP_WORDS,
+                            (uint32_t*)((uint8_t*)c.k_lo + rec * g.klo_bytes),
                             (uint8_t*)c.k_hi + rec * g.khi_bytes,
                             (uint16_t*)c.k_meta + rec * 2 * D, lds.key, width,
                             width ? plane1(g, kpl, bh, grp) : nullptr,

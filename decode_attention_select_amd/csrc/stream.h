@@ -77,7 +77,9 @@ struct SlotCfg {
 // their key scale/zero) read the kept run kept0 instead, bytes the same
 // instruction fetches anyway, so the pruned runs' bytes are not read; what
 // those lanes write is never read.
-template <int HIMODE, bool VHI, bool PRUNE>
+// DENSE1: the dense 1-bit layout's 768-byte k_lo record (lanes 48..63
+// re-read bytes of the record into the slack after it).
+template <int HIMODE, bool VHI, bool PRUNE, bool DENSE1 = false>
 __device__ inline void issue_group(const kvq_cache& c, size_t rec, uint8_t* slot, int lane,
                                    uint32_t kmask, int kept0, int nh, int nvhi) {
   using C = SlotCfg<HIMODE, VHI>;
@@ -85,7 +87,11 @@ __device__ inline void issue_group(const kvq_cache& c, size_t rec, uint8_t* slot
   // (l / 4) % 2 of the 16-channel run l / 8 (128 bytes per run)
   int lk = lane;
   if (PRUNE && !((kmask >> (lane >> 3)) & 1u)) lk = (lane & 7) | (kept0 << 3);
-  dma16<CPOL_NT>((const uint8_t*)c.k_lo + rec * 1024 + lk * 16, slot + C::KLO);
+  if constexpr (DENSE1)
+    dma16<CPOL_NT>((const uint8_t*)c.k_lo + rec * 768 + (lane < 48 ? lane : lane - 16) * 16,
+                   slot + C::KLO);
+  else
+    dma16<CPOL_NT>((const uint8_t*)c.k_lo + rec * 1024 + lk * 16, slot + C::KLO);
   // metadata: lanes 0..31 k_meta (64 bytes per 16-channel run: lanes 4w,
   // 4w+1 its scales, 4w+2, 4w+3 its zeros), lanes 32..63 v_meta
   {

@@ -76,8 +76,9 @@ typedef struct {
   int32_t n_pairs_hi;  /* salient pairs, 0..8 (ranks 0 .. n_pairs_hi-1) */
   int32_t bits_hi;     /* 4 (4-bit codes) or 16 (raw 16-bit values) */
   int32_t n_pairs_lo1; /* pairs of the lowest ranks quantized at 1 bit
-                          (codes 0/1 kept in their 2-bit slots of k_lo);
-                          n_pairs_hi + n_pairs_lo1 <= 64 */
+                          (codes 0/1 kept in their 2-bit slots of k_lo,
+                          one bit each in the dense 1-bit layout: see
+                          k_lo); n_pairs_hi + n_pairs_lo1 <= 64 */
   int32_t bits_lo;     /* 2: bits of every non-salient key channel */
   int32_t bits_v;      /* 2: bits of every value */
   int32_t residual;    /* R: recent tokens kept at 16 bits; multiple of 32,
@@ -123,6 +124,17 @@ typedef struct {
  *          is the 2-bit code of a 2-bit channel, the code (0 or 1) of a
  *          1-bit channel, the low two bits of the code of a 4-bit channel,
  *          and 0 for a 16-bit channel.
+ *          Dense 1-bit layout (n_pairs_hi == 0 and n_pairs_lo1 == 32, the
+ *          1.5-bit point): [B][Hkv][NG][768] bytes in plane order.  Let wl
+ *          list the 64 channels of the 2-bit pairs ascending and ol those of
+ *          the 1-bit pairs (the 32 lowest ranks) ascending; 16-channel run
+ *          2kq + u (kq = 0..3) is wl[16kq ..] for u = 0 and ol[16kq ..] for
+ *          u = 1.  Bytes [0, 512): u32 words (kq*2 + T)*16 + r, for the token
+ *          at tile index 16T + r, channel wl[16kq + c] at position pi(c);
+ *          bytes [512, 768): u32 words kq*16 + r, for tile row r of both
+ *          halves, channel ol[16kq + c] at bit 16T + 4(c&1) + ((c>>1)&1) +
+ *          8((c>>2)&1) + 2(c>>3).
+ *          k_meta runs follow plane order (run 2kq + u).
  *  k_hi    bits_hi == 4: [B][Hkv][NG][32] u32: word 16T + r (token at tile
  *          index 16T+r) holds the high two bits (code >> 2) of the d-th
  *          salient channel (ascending channel order, d < 2*n_pairs_hi) at
@@ -363,7 +375,7 @@ kvq_status kvq_decode_attn(const kvq_layout *L, const void *q,
  * key scale/zero are not read (the group copies wait for the query and the
  * choice); n_keep = 5 drops 37.5 % of the key channels.  n_keep = 8 is
  * kvq_decode_attn; n_keep outside 1..8 returns KVQ_EINVAL.  A progressive
- * layout returns KVQ_ENOTSUP for n_keep < 8.  All other arguments, limits
+ * layout and the dense 1-bit layout return KVQ_ENOTSUP for n_keep < 8.  All other arguments, limits
  * and errors as for kvq_decode_attn. */
 kvq_status kvq_decode_attn_pruned(const kvq_layout *L, const void *q,
                                   const kvq_cache *cache, float sm_scale,

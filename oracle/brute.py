@@ -68,7 +68,8 @@ def _tile_index(t: int) -> int:
 
 
 def _bit1_pos(c: int) -> int:
-    # the bit of run channel c in a 1-bit half-word (include/kvq.h, k_lo)
+    # the bit of run channel c in a 1-bit word of the dense layout, tile half
+    # T = 0 (T = 1: the same + 16; include/kvq.h, k_lo)
     return 4 * (c & 1) + ((c >> 1) & 1) + 8 * ((c >> 2) & 1) + 2 * (c >> 3)
 
 
@@ -82,13 +83,12 @@ def unpack_keys_dense1(k_lo, k_meta, one_bit_pairs):
     ol = [c for c in range(D) if c % 64 in one]
     assert len(wl) == len(ol) == 64
     words = np.asarray(k_lo, np.uint32)
-    halves = np.frombuffer(words[128:192].tobytes(), np.uint16)
     codes = np.zeros((D, GS), np.int64)
     for t in range(GS):
         T, r = divmod(_tile_index(t), 16)
         for kq in range(4):
             w = int(words[(kq * 2 + T) * 16 + r])
-            h = int(halves[(kq * 2 + T) * 16 + r])
+            h = int(words[128 + kq * 16 + r]) >> (16 * T)
             for c in range(16):
                 codes[wl[16 * kq + c], t] = _code(w, _pos(c))
                 codes[ol[16 * kq + c], t] = (h >> _bit1_pos(c)) & 1

@@ -536,9 +536,10 @@ static int pos_swap(int c) { return (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1); 
  * chunk kq (0..3) is the 2-bit run wl[16 kq ..] (u = 0) then the 1-bit run
  * ol[16 kq ..] (u = 1).  k_lo [..][NG][192] u32: words (kq*2 + T)*16 + r
  * hold the 2-bit run kq of the token at tile index 16T + r, channel
- * wl[16 kq + c] at position pos_swap(c); then (byte 512 on) u16 half-words
- * (kq*2 + T)*16 + r hold the 1-bit run kq, channel ol[16 kq + c] at bit
- * onebit_pos(c).  k_meta follows plane order: run 2 kq + u. */
+ * wl[16 kq + c] at position pos_swap(c); then (byte 512 on) u32 words
+ * kq*16 + r hold the 1-bit run kq of tile row r for both tile halves,
+ * channel ol[16 kq + c] at bit onebit_pos(c) + 16 T.  k_meta follows plane
+ * order: run 2 kq + u. */
 int orc_dense1(int n_hi, int n_lo1) { return n_hi == 0 && n_lo1 == NPAIR / 2; }
 
 /* Bit of the code of run channel c in a 1-bit half-word, chosen so that the
@@ -584,7 +585,7 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
         const uint8_t *ord = order + grp * GS;
         if (dense) {
           uint32_t *lo = k_lo + grp * 192;
-          uint16_t *lo1 = (uint16_t *)(lo + 128);
+          uint32_t *lo1 = lo + 128;
           memset(lo, 0, 192 * 4);
           for (int e = 0; e < 32; e++) {
             int t = ord[tile_token(e)], Tt = e / 16, r = e % 16;
@@ -592,7 +593,8 @@ int orc_pack_keys(int B, int Hkv, const uint16_t *k, int Tstride, int T, int R,
               for (int c = 0; c < 16; c++) {
                 int w_idx = (kq * 2 + Tt) * 16 + r;
                 lo[w_idx] |= (uint32_t)(cg[wl[16 * kq + c] * GS + t] & 3) << (2 * pos_swap(c));
-                lo1[w_idx] |= (uint16_t)((cg[ol[16 * kq + c] * GS + t] & 1) << onebit_pos(c));
+                lo1[kq * 16 + r] |= (uint32_t)(cg[ol[16 * kq + c] * GS + t] & 1)
+                                    << (onebit_pos(c) + 16 * Tt);
               }
           }
           uint16_t *meta = k_meta + grp * 256;

@@ -74,7 +74,8 @@ class Case:
         RS = self.w.residual + 32
         khi = oracle.k_hi_words(self.w.n_pairs_hi, self.w.bits_hi) if NG else 0
         out = {
-            "k_lo": host(c["k_lo"], np.uint32).reshape(B, H, NG, 256),
+            "k_lo": host(c["k_lo"], np.uint32).reshape(
+                B, H, NG, 192 if oracle.dense1(self.w.n_pairs_hi, self.w.n_pairs_lo1) else 256),
             "k_hi": (host(c["k_hi"], np.uint8)[:B * H * NG * khi].reshape(B, H, NG, khi)
                      if khi else np.zeros((B, H, NG, 0), np.uint8)),
             "k_meta": host(c["k_meta"], np.uint16).reshape(B, H, NG, 256),
@@ -94,6 +95,20 @@ class Case:
             out[nm] = (host(c[nm], np.uint32).reshape(B, H, npl, 256) if npl
                        else np.zeros((B, H, 0, 256), np.uint32))
         return out
+
+    def pruned_unsupported(self, n_splits: int = 3, n_keep: int = 5) -> bool:
+        """True (after checking that the call returns KVQ_ENOTSUP) when the
+        layout offers no pruned decode: the dense 1-bit layout and
+        progressive layouts."""
+        w = self.w
+        if not (oracle.dense1(w.n_pairs_hi, w.n_pairs_lo1) or w.prog_w4):
+            return False
+        try:
+            self.decode_pruned(self.d["q_dec"][:, :, 0], n_splits, n_keep)
+        except kvq.KvqError as e:
+            assert e.status == -2, e
+            return True
+        raise AssertionError("pruned decode accepted on a layout that does not offer it")
 
     def decode_pruned(self, q_bits: np.ndarray, n_splits: int, n_keep: int):
         """kvq_decode_attn_pruned -> GPU output widened to fp64."""

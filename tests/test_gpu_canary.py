@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import kvq_synth
+import oracle
 from decode_attention_select_amd import kvq
 from _gpu_case import SM_SCALE
 
@@ -91,8 +92,9 @@ def test_guard_bands_survive_every_call(cfg):
         kvq.kvq_decode_attn(layout, q.ptr(), cache, SM_SCALE, S, ws.ptr(), out.ptr(),
                             ws_bytes=ws.n)
         kvq.kvq_read_ceiling(layout, cache, S, sink.ptr())
-    kvq.kvq_decode_attn_pruned(layout, q.ptr(), cache, SM_SCALE, 3, 5, ws.ptr(), out.ptr(),
-                               ws_bytes=ws.n)
+    if not oracle.dense1(w.n_pairs_hi, w.n_pairs_lo1):  # the dense 1-bit layout: ENOTSUP
+        kvq.kvq_decode_attn_pruned(layout, q.ptr(), cache, SM_SCALE, 3, 5, ws.ptr(), out.ptr(),
+                                   ws_bytes=ws.n)
     # appends across group boundaries, every other one fused with a decode
     for i in range(n_app):
         kn = Guarded(d["k"][:, :, T0 + i].nbytes, d["k"][:, :, T0 + i])
