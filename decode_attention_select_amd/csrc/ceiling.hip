@@ -45,7 +45,7 @@ __global__ __launch_bounds__(WG_THREADS) void ceiling_kernel(Geo g, kvq_cache c,
     }
   };
   if (!ring_owner) issue_first();
-  const int len = c.len[bh];
+  const int len = load_uniform(c.len + bh);
   const int T = min(max(len, 0), g.max_tokens);
   const int ngq = n_quant(T, g.R) / GS;
   // ring blocks rb = f, f + STR, ...: 32 slots of 256-byte key rows and the

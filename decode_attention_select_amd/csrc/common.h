@@ -43,6 +43,15 @@ __host__ __device__ inline int onebit_pos(int c) {
   return 4 * (c & 1) + ((c >> 1) & 1) + 8 * ((c >> 2) & 1) + 2 * (c >> 3);
 }
 
+// A uniform read of memory that nothing writes while the reading kernel
+// runs (lengths, rank tables), through the constant address space, so that
+// it becomes a scalar load: a vector load of it would be waited for (with a
+// vmcnt count) while the kernel's direct global->LDS copies are in flight,
+// and the compiler then waits for every copy.
+__device__ inline int32_t load_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 // Bits of a progressive group of age a (0 = the newest quantized group).
 __host__ __device__ inline int prog_width(int a, int w8, int w4) {
   return a < w8 ? 8 : (a < w4 ? 4 : 2);

@@ -413,10 +413,10 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // into LDS like the group records, so that no vector-register load is
   // waited for while copies are in flight (the compiler cannot count the two
   // kinds together and would wait for all of them).
-  const int len = c.len[bh];
+  const int len = load_uniform(c.len + bh);
   int top[8];
 #pragma unroll
-  for (int r = 0; r < 8; r++) top[r] = c.pairs[(size_t)bh * NPAIR + r];
+  for (int r = 0; r < 8; r++) top[r] = load_uniform(c.pairs + (size_t)bh * NPAIR + r);
   {
     const uint8_t* qsrc = (const uint8_t*)(q + ((size_t)b * g.Hq + kh * G) * D);
     for (int i = 0; i < (G + 3) / 4; i++) {
