@@ -1283,7 +1283,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         rv[((size_t)(slot / GS) * D + tid) * GS + slot % GS] = vnv;
       }
       if (n_quant(T, g.R) > nq && tid < 128)
-        pack_ring_group<BF16, VHI>(g, c, bh, nq, tid, lds.u.pack);
+        pack_ring_group<BF16, VHI, false, DENSE1>(g, c, bh, nq, tid, lds.u.pack);
     }
     __syncthreads();  // the packing's LDS is free again before the merge uses it
   }

@@ -199,7 +199,9 @@ __device__ void token_order_wave(const uint16_t* rows, uint32_t* ord) {
 // multiplied by 17, then 5, each product rounded to fp16; digit 0 goes to
 // lo_out, digit 1 of salient channels to hi_out, digit 1 of every channel to
 // pl1 (width >= 4) and digits 2, 3 to pl23 and pl23 + 256 (width 8).
-template <bool BF, bool VHI>
+// MAYDENSE false compiles the dense one-bit record out (callers that never
+// see that layout).
+template <bool BF, bool VHI, bool MAYDENSE = true>
 __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
                                uint32_t* lo_out, uint8_t* hi_out, uint16_t* meta_out,
                                KeyLds& L, int width = 0, uint32_t* pl1 = nullptr,
@@ -323,7 +325,7 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
   // (digit * 4^position, below 2^16); the high digits of 4-bit channels as
   // integers, only for channel slots k where some lane holds a 4-bit channel
   refresh(v);
-  if (g.dense1 && width == 0) {
+  if (MAYDENSE && g.dense1 && width == 0) {
     // the dense 1-bit layout: channel c goes to plane run 2 kq' + u (u = 1
     // for a 1-bit pair), place cc = rank % 16, where rank counts the
     // channels of its class below it (first channels, then second ones)
@@ -777,7 +779,9 @@ struct PackLds {
 // the one that reaches age w8 from 8 bits to the width of that age (in this
 // order, each wave for its side: the new group's planes take the slots these
 // two free).
-template <bool BF, bool VHI>
+// MAYPROG / MAYDENSE false compile progressive precision / the dense one-bit
+// record out, for callers the host never launches with that layout.
+template <bool BF, bool VHI, bool MAYPROG = true, bool MAYDENSE = true>
 __device__ void pack_ring_group(const Geo& g, kvq_cache& c, int bh, int nq0, int tid,
                                 PackLds& lds) {
   const uint16_t* rk = (const uint16_t*)c.ring_k + (size_t)bh * g.RS * D;
@@ -785,9 +789,10 @@ __device__ void pack_ring_group(const Geo& g, kvq_cache& c, int bh, int nq0, int
   const int grp = nq0 / GS, s0 = nq0 % g.RS;
   const size_t rec = (size_t)bh * g.NG + grp;
   uint32_t* vhi = c.v_hi + rec * g.vhi_words;
-  const int width = g.w4 > 0 ? prog_width(0, g.w8, g.w4) : 0;
+  const int width = MAYPROG && g.w4 > 0 ? prog_width(0, g.w8, g.w4) : 0;
   const int gA = grp - g.w4, gB = grp - g.w8;
-  const bool shrinkA = g.w4 > g.w8 && gA >= 0, shrinkB = g.w4 > 0 && g.w8 > 0 && gB >= 0;
+  const bool shrinkA = MAYPROG && g.w4 > g.w8 && gA >= 0;
+  const bool shrinkB = MAYPROG && g.w4 > 0 && g.w8 > 0 && gB >= 0;
   const int toB = shrinkB ? prog_width(g.w8, g.w8, g.w4) : 0;
   if (tid < 64) {
     const PairMasks pm = pair_masks(g, c.pairs + (size_t)bh * NPAIR);
@@ -804,7 +809,7 @@ __device__ void pack_ring_group(const Geo& g, kvq_cache& c, int bh, int nq0, int
                        (uint16_t*)c.k_meta + rb * 2 * D, plane1(g, kpl, bh, gB),
                        plane23(g, kpl, bh, gB), 8, toB, lds.key);
     }
-    key_group_wave<BF, VHI>(g, rk + (size_t)s0 * D, pm,
+    key_group_wave<BF, VHI, MAYDENSE>(g, rk + (size_t)s0 * D, pm,
                             (uint32_t*)((uint8_t*)c.k_lo + rec * g.klo_bytes),
                             (uint8_t*)c.k_hi + rec * g.khi_bytes,
                             (uint16_t*)c.k_meta + rec * 2 * D, lds.key, width,
