@@ -32,6 +32,54 @@ UNITS = [("api.hip", []), ("select.hip", []), ("quant.hip", []), ("ceiling.hip",
 
 
 STAMPS_LIB = os.path.join(PKG, "libkvq_stamps.so")
+# per-kernel registers, scratch and spills of libkvq.so, from the compiler's
+# resource-usage remarks (written by build(); not part of the library)
+RESOURCES = os.path.join(PKG, "kernel_resources.txt")
+
+
+def _resource_rows(text: str) -> list[tuple[str, dict]]:
+    """(kernel, {field: value}) from -Rpass-analysis=kernel-resource-usage
+    remarks, in the order the compiler printed them."""
+    rows: list[tuple[str, dict]] = []
+    for line in text.splitlines():
+        if "remark:" not in line or "kernel-resource-usage" not in line:
+            continue
+        body = line.split("remark:", 1)[1].rsplit("[-Rpass", 1)[0].strip()
+        key, _, val = body.partition(":")
+        if key == "Function Name":
+            rows.append((val.strip(), {}))
+        elif rows:
+            rows[-1][1][key.strip()] = val.strip()
+    return rows
+
+
+REPORT_KEYS = ("VGPRs", "AGPRs", "TotalSGPRs", "ScratchSize [bytes/lane]", "VGPRs Spill",
+               "SGPRs Spill", "LDS Size [bytes/block]", "Occupancy [waves/SIMD]")
+
+
+def write_resources(rows: list[tuple[str, dict]], path: str = RESOURCES) -> None:
+    with open(path, "w") as f:
+        f.write("# kernel | " + " | ".join(REPORT_KEYS) + "\n")
+        for name, r in rows:
+            f.write(" | ".join([name] + [r.get(k, "?") for k in REPORT_KEYS]) + "\n")
+
+
+def read_resources(path: str = RESOURCES) -> list[tuple[str, dict]]:
+    rows = []
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        cols = [c.strip() for c in line.split(" | ")]
+        rows.append((cols[0], dict(zip(REPORT_KEYS, cols[1:]))))
+    return rows
+
+
+def check_resources(rows: list[tuple[str, dict]]) -> list[str]:
+    """Kernels that use scratch memory or spill vector registers: every
+    kernel of the library keeps its state in registers and LDS (scalar
+    spills land in vector-register lanes, no memory, and are allowed)."""
+    return [name for name, f in rows
+            if any(int(f.get(k, "0")) for k in ("ScratchSize [bytes/lane]", "VGPRs Spill"))]
 
 
 def build(verbose: bool = False, stamps: bool = True) -> str:
@@ -45,16 +93,36 @@ def build(verbose: bool = False, stamps: bool = True) -> str:
         objs[lib] = []
         for i, (src, extra) in enumerate(UNITS):
             obj = os.path.join(PKG, "_unit%d%s.%s.o" % (i, "s" if vflags else "", tag))
-            cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + vflags + extra + \
+            remarks = [] if vflags else ["-Rpass-analysis=kernel-resource-usage"]
+            cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + vflags + extra + remarks + \
                   ["-c", "-o", obj, os.path.join(CSRC, src)]
             if verbose:
                 print(" ".join(cmd), flush=True)
             objs[lib].append(obj)
-            procs.append(subprocess.Popen(cmd))
+            err = open(obj + ".err", "w+")
+            procs.append((subprocess.Popen(cmd, stderr=err), err))
     try:
-        failed = [p.wait() for p in procs]
+        failed, text = [], []
+        for p, err in procs:
+            failed.append(p.wait())
+            err.seek(0)
+            out = err.read()
+            err.close()
+            os.remove(err.name)
+            text.append(out)
+            # compiler diagnostics other than the resource remarks pass through
+            rest = [ln for ln in out.splitlines() if "kernel-resource-usage" not in ln
+                    and not ln.lstrip().startswith(("|", "^")) and not ln[:6].strip().isdigit()]
+            if rest:
+                print("\n".join(rest), file=sys.stderr, flush=True)
         if any(failed):
             raise subprocess.CalledProcessError(max(failed), "hipcc")
+        rows = _resource_rows("\n".join(text))
+        write_resources(rows)
+        bad = check_resources(rows)
+        if bad:
+            raise RuntimeError("kernels with scratch memory or vector spills (%s): %s"
+                               % (RESOURCES, ", ".join(bad)))
         for lib, _ in variants:
             tmp = lib + ".tmp" + tag
             cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs[lib]
