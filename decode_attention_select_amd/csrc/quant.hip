@@ -55,11 +55,20 @@ __device__ void ring_fill(const Geo& g, const uint16_t* __restrict__ x, int T, i
   if (ry == 0 && tid == 0) c.len[bh] = T;
 }
 
+// Layout kinds of the quantize and append kernels: each variant compiles
+// only the record paths its layout can take (a path compiled in but never
+// taken still costs registers, and with them occupancy).
+constexpr int KIND_PLAIN = 0, KIND_DENSE1 = 1, KIND_PROG = 2;
+
+static int layout_kind(const Geo& g) {
+  return g.w4 > 0 ? KIND_PROG : (g.dense1 ? KIND_DENSE1 : KIND_PLAIN);
+}
+
 // grid (B * Hkv, qblocks + ring blocks): blocks below qblocks quantize
 // QWAVES groups, one per wave; the rest fill the ring.
 // VHI: each wave ranks its group's tokens, packs the keys in that order and
 // writes the order to the group's v_hi header.
-template <bool BF, bool VHI>
+template <bool BF, bool VHI, int KIND>
 __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint16_t* __restrict__ k,
                                                               int T, int qblocks, kvq_cache c) {
   if ((int)blockIdx.y >= qblocks) {
@@ -72,13 +81,14 @@ __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint1
   if (grp >= n_quant(T, g.R) / GS) return;
   const size_t rec = (size_t)bh * g.NG + grp;
   // progressive precision: the width of the group's age among n_q / 32
-  const int width = g.w4 > 0 ? prog_width(n_quant(T, g.R) / GS - 1 - grp, g.w8, g.w4) : 0;
-  key_group_wave<BF, VHI>(g, k + ((size_t)bh * T + (size_t)grp * GS) * D,
-                          pair_masks(g, c.pairs + (size_t)bh * NPAIR),
-                          (uint32_t*)((uint8_t*)c.k_lo + rec * g.klo_bytes),
-                          (uint8_t*)c.k_hi + rec * g.khi_bytes, (uint16_t*)c.k_meta + rec * 2 * D,
-                          lds[wave], width, width >= 4 ? plane1(g, c.k_pl, bh, grp) : nullptr,
-                          width == 8 ? plane23(g, c.k_pl, bh, grp) : nullptr);
+  const int width =
+      KIND == KIND_PROG ? prog_width(n_quant(T, g.R) / GS - 1 - grp, g.w8, g.w4) : 0;
+  key_group_wave<BF, VHI, KIND == KIND_DENSE1, KIND == KIND_PROG>(
+      g, k + ((size_t)bh * T + (size_t)grp * GS) * D, pair_masks(g, c.pairs + (size_t)bh * NPAIR),
+      (uint32_t*)((uint8_t*)c.k_lo + rec * g.klo_bytes), (uint8_t*)c.k_hi + rec * g.khi_bytes,
+      (uint16_t*)c.k_meta + rec * 2 * D, lds[wave], width,
+      width >= 4 ? plane1(g, c.k_pl, bh, grp) : nullptr,
+      width == 8 ? plane23(g, c.k_pl, bh, grp) : nullptr);
   if constexpr (VHI)
     if (lane < 2) ((uint4*)(c.v_hi + rec * g.vhi_words))[lane] = ((const uint4*)lds[wave].ord)[lane];
 }
@@ -87,7 +97,7 @@ __global__ __launch_bounds__(QTHREADS) void quant_keys_kernel(Geo g, const uint1
 // kernel wrote (an earlier launch on the same stream).  Its bytes are masked
 // to 0..31, so a header the key kernel never wrote cannot move a load out
 // of the group.
-template <bool BF, bool VHI>
+template <bool BF, bool VHI, bool PROG>
 __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uint16_t* __restrict__ v,
                                                                 int T, int qblocks, kvq_cache c) {
   if ((int)blockIdx.y >= qblocks) {
@@ -105,8 +115,8 @@ __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uin
     pos.x &= 0x1F1F1F1Fu;
     pos.y &= 0x1F1F1F1Fu;
   }
-  const int width = g.w4 > 0 ? prog_width(n_quant(T, g.R) / GS - 1 - grp, g.w8, g.w4) : 0;
-  value_group_wave<BF, false, VHI>(g, v + ((size_t)bh * T + (size_t)grp * GS) * D, pos,
+  const int width = PROG ? prog_width(n_quant(T, g.R) / GS - 1 - grp, g.w8, g.w4) : 0;
+  value_group_wave<BF, false, VHI, PROG>(g, v + ((size_t)bh * T + (size_t)grp * GS) * D, pos,
                                    (uint32_t*)c.v_codes + rec * GROUP_WORDS,
                                    (uint16_t*)c.v_meta + rec * 2 * D, vhi, width,
                                    width >= 4 ? plane1(g, c.v_pl, bh, grp) : nullptr,
@@ -120,7 +130,7 @@ __global__ __launch_bounds__(QTHREADS) void quant_values_kernel(Geo g, const uin
 // wave 1 its values (the new token is not in that group).  VHI: both waves
 // rank the group's tokens from the ring keys (the same integer sums, so the
 // same order); wave 0 also writes it to the v_hi header.
-template <bool BF, bool VHI>
+template <bool BF, bool VHI, int KIND>
 __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new,
                                                      kvq_cache c) {
@@ -137,9 +147,41 @@ __global__ __launch_bounds__(128) void append_kernel(Geo g, const uint16_t* __re
   rk[(size_t)slot * D + tid] = k_new[(size_t)bh * D + tid];
   rv[((size_t)(slot / GS) * D + tid) * GS + slot % GS] = v_new[(size_t)bh * D + tid];
   const int nq0 = n_quant(T, g.R);
-  if (n_quant(T + 1, g.R) > nq0) pack_ring_group<BF, VHI>(g, c, bh, nq0, tid, lds);
+  if (n_quant(T + 1, g.R) > nq0) pack_ring_group<BF, VHI, KIND == KIND_PROG, KIND == KIND_DENSE1>(g, c, bh, nq0, tid, lds);
   __syncthreads();
   if (tid == 0) c.len[bh] = T + 1;
+}
+
+// Progressive precision is never combined with two value precisions (the
+// host rejects that layout), so its variants exist without VHI only.
+template <bool BF>
+static auto keys_kernel(const Geo& g) -> decltype(&quant_keys_kernel<BF, false, KIND_PLAIN>) {
+  switch (layout_kind(g)) {
+    case KIND_PROG: return quant_keys_kernel<BF, false, KIND_PROG>;
+    case KIND_DENSE1:
+      return g.n_vhi ? quant_keys_kernel<BF, true, KIND_DENSE1>
+                     : quant_keys_kernel<BF, false, KIND_DENSE1>;
+    default:
+      return g.n_vhi ? quant_keys_kernel<BF, true, KIND_PLAIN>
+                     : quant_keys_kernel<BF, false, KIND_PLAIN>;
+  }
+}
+
+template <bool BF>
+static auto values_kernel(const Geo& g) -> decltype(&quant_values_kernel<BF, false, false>) {
+  if (layout_kind(g) == KIND_PROG) return quant_values_kernel<BF, false, true>;
+  return g.n_vhi ? quant_values_kernel<BF, true, false> : quant_values_kernel<BF, false, false>;
+}
+
+template <bool BF>
+static auto append_variant(const Geo& g) -> decltype(&append_kernel<BF, false, KIND_PLAIN>) {
+  switch (layout_kind(g)) {
+    case KIND_PROG: return append_kernel<BF, false, KIND_PROG>;
+    case KIND_DENSE1:
+      return g.n_vhi ? append_kernel<BF, true, KIND_DENSE1> : append_kernel<BF, false, KIND_DENSE1>;
+    default:
+      return g.n_vhi ? append_kernel<BF, true, KIND_PLAIN> : append_kernel<BF, false, KIND_PLAIN>;
+  }
 }
 
 static int ring_blocks(const Geo& g, int T) {
@@ -149,10 +191,7 @@ static int ring_blocks(const Geo& g, int T) {
 hipError_t launch_quant_keys(const Geo& g, const void* k, int T, kvq_cache* c, hipStream_t st) {
   const int qb = (n_quant(T, g.R) / GS + QWAVES - 1) / QWAVES;
   const dim3 grid(g.B * g.Hkv, qb + ring_blocks(g, T));
-  const auto kern = g.bf16 ? (g.n_vhi ? quant_keys_kernel<true, true>
-                                       : quant_keys_kernel<true, false>)
-                           : (g.n_vhi ? quant_keys_kernel<false, true>
-                                       : quant_keys_kernel<false, false>);
+  const auto kern = g.bf16 ? keys_kernel<true>(g) : keys_kernel<false>(g);
   hipLaunchKernelGGL(kern, grid, dim3(QTHREADS), 0, st, g, (const uint16_t*)k, T, qb, *c);
   return hipGetLastError();
 }
@@ -160,10 +199,7 @@ hipError_t launch_quant_keys(const Geo& g, const void* k, int T, kvq_cache* c, h
 hipError_t launch_quant_values(const Geo& g, const void* v, int T, kvq_cache* c, hipStream_t st) {
   const int qb = (n_quant(T, g.R) / GS + QWAVES - 1) / QWAVES;
   const dim3 grid(g.B * g.Hkv, qb + ring_blocks(g, T));
-  const auto kern = g.bf16 ? (g.n_vhi ? quant_values_kernel<true, true>
-                                       : quant_values_kernel<true, false>)
-                           : (g.n_vhi ? quant_values_kernel<false, true>
-                                       : quant_values_kernel<false, false>);
+  const auto kern = g.bf16 ? values_kernel<true>(g) : values_kernel<false>(g);
   hipLaunchKernelGGL(kern, grid, dim3(QTHREADS), 0, st, g, (const uint16_t*)v, T, qb, *c);
   return hipGetLastError();
 }
@@ -242,8 +278,7 @@ hipError_t launch_shrink(const Geo& g, kvq_cache* c, int g0, int g1, hipStream_t
 
 hipError_t launch_append(const Geo& g, const void* k_new, const void* v_new, kvq_cache* c,
                          hipStream_t st) {
-  const auto kern = g.bf16 ? (g.n_vhi ? append_kernel<true, true> : append_kernel<true, false>)
-                           : (g.n_vhi ? append_kernel<false, true> : append_kernel<false, false>);
+  const auto kern = g.bf16 ? append_variant<true>(g) : append_variant<false>(g);
   hipLaunchKernelGGL(kern, dim3(g.B * g.Hkv), dim3(128), 0, st, g, (const uint16_t*)k_new,
                      (const uint16_t*)v_new, *c);
   return hipGetLastError();

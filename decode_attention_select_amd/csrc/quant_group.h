@@ -174,7 +174,7 @@ __device__ inline void order_from_scores(uint32_t e, uint32_t* ord) {
 }
 
 template <bool BF>
-__device__ void token_order_wave(const uint16_t* rows, uint32_t* ord) {
+__device__ __forceinline__ void token_order_wave(const uint16_t* rows, uint32_t* ord) {
   const int lane = threadIdx.x & 63, t = lane >> 1, h = lane & 1;
   uint4 v[8];
 #pragma unroll
@@ -199,13 +199,15 @@ __device__ void token_order_wave(const uint16_t* rows, uint32_t* ord) {
 // multiplied by 17, then 5, each product rounded to fp16; digit 0 goes to
 // lo_out, digit 1 of salient channels to hi_out, digit 1 of every channel to
 // pl1 (width >= 4) and digits 2, 3 to pl23 and pl23 + 256 (width 8).
-// MAYDENSE false compiles the dense one-bit record out (callers that never
-// see that layout).
-template <bool BF, bool VHI, bool MAYDENSE = true>
-__device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
-                               uint32_t* lo_out, uint8_t* hi_out, uint16_t* meta_out,
-                               KeyLds& L, int width = 0, uint32_t* pl1 = nullptr,
-                               uint32_t* pl23 = nullptr) {
+// DENSE / PROG false compile the dense one-bit record / progressive
+// precision out (width is then taken as 0), for callers whose layouts never
+// take them.
+template <bool BF, bool VHI, bool DENSE, bool PROG>
+__device__ __forceinline__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
+                                               uint32_t* lo_out, uint8_t* hi_out,
+                                               uint16_t* meta_out, KeyLds& L, int width = 0,
+                                               uint32_t* pl1 = nullptr, uint32_t* pl23 = nullptr) {
+  if (!PROG) width = 0;
   const int lane = threadIdx.x & 63, cb = lane >> 2, tq = lane & 3;
   uint4 v[8];
 #pragma unroll
@@ -325,7 +327,7 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
   // (digit * 4^position, below 2^16); the high digits of 4-bit channels as
   // integers, only for channel slots k where some lane holds a 4-bit channel
   refresh(v);
-  if (MAYDENSE && g.dense1 && width == 0) {
+  if (DENSE && g.dense1 && width == 0) {
     // the dense 1-bit layout: channel c goes to plane run 2 kq' + u (u = 1
     // for a 1-bit pair), place cc = rank % 16, where rank counts the
     // channels of its class below it (first channels, then second ones)
@@ -470,11 +472,14 @@ __device__ void key_group_wave(const Geo& g, const uint16_t* rows, PairMasks pm,
 // of their codes go to vhi_out (the group's v_hi record) after its 8-word
 // order header, which the key side writes.
 // width > 0 (progressive precision, not with VHI): codes at 8 bits, shrunk
-// to `width` bits, digit planes 1..3 to pl1 / pl23, as for the keys.
-template <bool BF, bool CHMAJOR, bool VHI>
-__device__ void value_group_wave(const Geo& g, const uint16_t* src, uint2 pos, uint32_t* vc_out,
-                                 uint16_t* meta_out, uint32_t* vhi_out, int width = 0,
-                                 uint32_t* pl1 = nullptr, uint32_t* pl23 = nullptr) {
+// to `width` bits, digit planes 1..3 to pl1 / pl23, as for the keys (PROG
+// false compiles that out and takes width as 0).
+template <bool BF, bool CHMAJOR, bool VHI, bool PROG>
+__device__ __forceinline__ void value_group_wave(const Geo& g, const uint16_t* src, uint2 pos,
+                                                 uint32_t* vc_out, uint16_t* meta_out,
+                                                 uint32_t* vhi_out, int width = 0,
+                                                 uint32_t* pl1 = nullptr, uint32_t* pl23 = nullptr) {
+  if (!PROG) width = 0;
   const int lane = threadIdx.x & 63, cb = lane & 15, tq = lane >> 4, m = cb & 3, j = cb >> 2;
   auto pos_of = [&](int i) -> uint32_t {
     return ((i < 4 ? pos.x : pos.y) >> (8 * (i & 3))) & 0xFFu;
@@ -781,8 +786,8 @@ struct PackLds {
 // two free).
 // MAYPROG / MAYDENSE false compile progressive precision / the dense one-bit
 // record out, for callers the host never launches with that layout.
-template <bool BF, bool VHI, bool MAYPROG = true, bool MAYDENSE = true>
-__device__ void pack_ring_group(const Geo& g, kvq_cache& c, int bh, int nq0, int tid,
+template <bool BF, bool VHI, bool MAYPROG, bool MAYDENSE>
+__device__ __forceinline__ void pack_ring_group(const Geo& g, kvq_cache& c, int bh, int nq0, int tid,
                                 PackLds& lds) {
   const uint16_t* rk = (const uint16_t*)c.ring_k + (size_t)bh * g.RS * D;
   const uint16_t* rv = (const uint16_t*)c.ring_v + (size_t)bh * g.RS * D;
@@ -809,7 +814,7 @@ __device__ void pack_ring_group(const Geo& g, kvq_cache& c, int bh, int nq0, int
                        (uint16_t*)c.k_meta + rb * 2 * D, plane1(g, kpl, bh, gB),
                        plane23(g, kpl, bh, gB), 8, toB, lds.key);
     }
-    key_group_wave<BF, VHI, MAYDENSE>(g, rk + (size_t)s0 * D, pm,
+    key_group_wave<BF, VHI, MAYDENSE, MAYPROG>(g, rk + (size_t)s0 * D, pm,
                             (uint32_t*)((uint8_t*)c.k_lo + rec * g.klo_bytes),
                             (uint8_t*)c.k_hi + rec * g.khi_bytes,
                             (uint16_t*)c.k_meta + rec * 2 * D, lds.key, width,
@@ -835,7 +840,7 @@ __device__ void pack_ring_group(const Geo& g, kvq_cache& c, int bh, int nq0, int
       shrink_value_group((uint32_t*)c.v_codes + rb * GROUP_WORDS, (uint16_t*)c.v_meta + rb * 2 * D,
                          plane1(g, vpl, bh, gB), plane23(g, vpl, bh, gB), 8, toB);
     }
-    value_group_wave<BF, true, VHI>(g, rv + (size_t)(s0 / GS) * D * GS, pos,
+    value_group_wave<BF, true, VHI, MAYPROG>(g, rv + (size_t)(s0 / GS) * D * GS, pos,
                                     (uint32_t*)c.v_codes + rec * GROUP_WORDS,
                                     (uint16_t*)c.v_meta + rec * 2 * D, vhi, width,
                                     width ? plane1(g, vpl, bh, grp) : nullptr,
