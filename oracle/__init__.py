@@ -238,6 +238,26 @@ def attention_after_append(qz: Quantized, q, sm_scale: float, with_lse: bool = F
     return attention(Quantized(**kw), q, sm_scale, with_lse=with_lse)
 
 
+def attention_one_launch(qz_before: Quantized, q, sm_scale: float, with_lse: bool = False):
+    """Decode attention of a call that finds the cache as qz_before holds it
+    (qz_before.T tokens, every group at the width of its age then), appends
+    token qz_before.T from the inputs (present in qz_before.k / .v) and
+    decodes in the same step: the quantized prefix and its widths are the
+    ones from before the append, and every token past it, the new one
+    included, is attended at 16 bits (PM-KVQ, key_machinery: new tokens are
+    held at 16 bits first and quantized later).  With n_q(T+1, R+1) =
+    n_q(T, R) this is the attention above over T + 1 tokens with the
+    residual window one token longer.  Without progressive precision it
+    equals attention_after_append of the cache after the append; with it,
+    a step that packs a group also shrinks the groups crossing the window
+    edges, which this call still reads at their former widths."""
+    assert qz_before.k.shape[2] > qz_before.T, "the appended token must be in qz_before.k"
+    kw = dict(qz_before.__dict__)
+    kw["T"] = qz_before.T + 1
+    kw["R"] = qz_before.R + 1
+    return attention(Quantized(**kw), q, sm_scale, with_lse=with_lse)
+
+
 def k_hi_words(n_pairs_hi: int, bits_hi: int) -> int:
     """Bytes of the salient-key section of one group record."""
     if n_pairs_hi == 0:
