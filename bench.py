@@ -397,12 +397,10 @@ def streaming_leg(args, w):
     restore()
     append_us = run(False)
     decode_us = step_us - append_us
-    fused_us = None
-    if not w.prog_w4:  # a progressive append shrinks older groups: no one-launch step
-        restore()
-        fused_us = run_fused()
-        for c in layers:
-            assert kvq.kvq_check(c.struct) == 0
+    restore()
+    fused_us = run_fused()
+    for c in layers:
+        assert kvq.kvq_check(c.struct) == 0
     alg = sum(algorithmic_bytes(w, T0 + i + 1) for i in range(n)) / n
     gbs = alg / (decode_us * 1e-6) / 1e9
     return {

@@ -289,7 +289,7 @@ static kvq_status decode_common(const kvq_layout* L, const void* q, const kvq_ca
   if (ws_bytes < need) return KVQ_ECAPACITY;
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return KVQ_EINVAL;
   if (keep < 0 || keep > 8) return KVQ_EINVAL;
-  if (g.w4 > 0 && keep != 8) return KVQ_ENOTSUP;
+  if (g.w4 > 0 && keep != 8 && keep != 0) return KVQ_ENOTSUP;
   if (g.dense1 && keep >= 1 && keep < 8) return KVQ_ENOTSUP;
   if (kvq_status s = check_ptr(q)) return s;
   if (kvq_status s = check_ptr(out)) return s;

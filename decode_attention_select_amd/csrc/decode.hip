@@ -350,7 +350,9 @@ struct Lds {
 // from the ring at 16 bits in this call.  The first workgroup of the
 // (sequence, KV head) to take its ticket writes the token to its ring slot
 // and packs the completed group; the last merging workgroup, after every
-// workgroup has read the length, stores the new length.
+// workgroup has read the length, stores the new length.  With PROG the pack
+// also shrinks the groups that cross the window edges, which every split of
+// this call reads: the last workgroup packs, after its merge.
 // LOCOL (G <= 8): the exact pair (hi, lo) of every product q*s and p*s
 // enters one MFMA, hi in column h of head h and lo in the spare column
 // 15 - h; lane (col, kq) serves head col (col < G) or 15 - col (col >= 16 -
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   constexpr bool PRUNE = KB > 0;
   using SC = SlotCfg<HIMODE, VHI>;
   constexpr int NSLOT = SC::NSLOT, NLD = SC::NLD, SLOTB = SC::BYTES;
-  static_assert(!PROG || (NSLOT >= 3 && SLOTB >= 3072 && !PRUNE && !VHI && !FUSED),
+  static_assert(!PROG || (NSLOT >= 3 && SLOTB >= 3072 && !PRUNE && !VHI),
                 "a window group takes three slots: its record and three planes per side");
   static_assert(!DENSE1 || (HIMODE == 0 && !PRUNE && !PROG), "dense 1-bit layout variants");
   __shared__ Lds<SLOTB, NSLOT> lds;
@@ -1282,7 +1284,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         rk[(size_t)slot * D + tid] = knv;
         rv[((size_t)(slot / GS) * D + tid) * GS + slot % GS] = vnv;
       }
-      if (n_quant(T, g.R) > nq && tid < 128)
+      if (!PROG && n_quant(T, g.R) > nq && tid < 128)
         pack_ring_group<BF16, VHI, false, DENSE1>(g, c, bh, nq, tid, lds.u.pack);
     }
     __syncthreads();  // the packing's LDS is free again before the merge uses it
@@ -1393,6 +1395,15 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   KVQ_STAMP(tid == 0, 16);
 #endif
   KVQ_STAMP_FLUSH();
+  if constexpr (FUSED && PROG) {
+    // the pack of a progressive cache: every split of this (sequence, KV
+    // head) has read its window groups (its ticket followed its loads), and
+    // the merge's LDS is free once every thread is past the output
+    if (app && n_quant(T, g.R) > nq) {
+      __syncthreads();
+      if (tid < 128) pack_ring_group<BF16, VHI, true, false>(g, c, bh, nq, tid, lds.u.pack);
+    }
+  }
   if constexpr (FUSED) {
     // the append's length (or its error): every workgroup of this (sequence,
     // KV head) read the length before it took its ticket
@@ -1427,9 +1438,9 @@ static void launch_cols(const Geo& g, int keep, const Launch& a) {
       return;
     }
   }
-  if constexpr (KB == 0 && !VHI && !FUSED) {
+  if constexpr (KB == 0 && !VHI) {
     if (g.NG > 0 && g.w4 > 0) {
-      hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, 0, false, false, LOCOL, true>), grid,
+      hipLaunchKernelGGL((decode_kernel<BF16, HIMODE, true, 0, false, FUSED, LOCOL, true>), grid,
                          block, 0, a.st, g, (const uint16_t*)a.q, *a.c, a.scale_log2, a.S, a.ws,
                          (uint16_t*)a.out, (const uint16_t*)a.knew, (const uint16_t*)a.vnew, keep);
       return;

@@ -395,12 +395,13 @@ kvq_status kvq_decode_attn_pruned(const kvq_layout *L, const void *q,
  *    append, n_q(T): a group that this call packs is attended at 16 bits in
  *    this call (it is still in the ring) and quantized from the next call on.
  *    Where no group is packed the output equals kvq_append followed by
- *    kvq_decode_attn.
+ *    kvq_decode_attn.  With progressive precision the pack also shrinks the
+ *    groups reaching ages prog_w8 and prog_w4 (as kvq_append does); this
+ *    call attends them at the widths they had before it, and the shrinks
+ *    run after every split of the (b, kv head) has read them.
  *  - if T == max_tokens (T < 0): sets err bit 0 (bit 1), changes nothing,
  *    and decodes over the cache as it stands.
- * Saves the append's launch.  Pruned key chunks are not offered here, and a
- * progressive layout returns KVQ_ENOTSUP (its append shrinks older groups:
- * call kvq_append, then kvq_decode_attn).
+ * Saves the append's launch.  Pruned key chunks are not offered here.
  *   k_new, v_new: [B][Hkv][128] io dtype;  q, out: as for kvq_decode_attn.
  * Other arguments, limits and errors as for kvq_decode_attn. */
 kvq_status kvq_append_decode_attn(const kvq_layout *L, const void *k_new,

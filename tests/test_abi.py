@@ -202,8 +202,8 @@ def test_prog_plane_sizes():
 
 @no_gpu
 def test_prog_calls_it_does_not_offer():
-    # pruned and one-launch decode, the explicit salient shrink and the read
-    # ceiling return ENOTSUP on a progressive layout, before any launch
+    # pruned decode, the explicit salient shrink and the read ceiling return
+    # ENOTSUP on a progressive layout, before any launch
     L = L32k(prog_w8=2, prog_w4=8)
     c = fake_cache()
     ws = kvq.kvq_workspace_bytes(L, 8)
@@ -211,18 +211,21 @@ def test_prog_calls_it_does_not_offer():
     assert status_of("kvq_decode_attn_pruned", ctypes.byref(L), P(FAKE), ctypes.byref(c),
                      ctypes.c_float(0.088), 8, 5, P(FAKE), ctypes.c_size_t(ws), P(FAKE),
                      P(0)) == ENOTSUP
-    assert status_of("kvq_append_decode_attn", ctypes.byref(L), P(FAKE), P(FAKE), P(FAKE),
-                     ctypes.byref(c), ctypes.c_float(0.088), 8, P(FAKE), ctypes.c_size_t(ws),
-                     P(FAKE), P(0)) == ENOTSUP
     assert status_of("kvq_shrink", ctypes.byref(L), ctypes.byref(c), 0, 4, P(0)) == ENOTSUP
     assert status_of("kvq_read_ceiling", ctypes.byref(L), ctypes.byref(c), 8, P(FAKE),
                      P(0)) == ENOTSUP
-    # a plane buffer that is missing is an argument error
+    # a plane buffer that is missing is an argument error, for the plain and
+    # the one-launch decode (which is offered on progressive layouts)
     c0 = fake_cache()
     c0.k_pl = None
     assert status_of("kvq_decode_attn", ctypes.byref(L), P(FAKE), ctypes.byref(c0),
                      ctypes.c_float(0.088), 8, P(FAKE), ctypes.c_size_t(ws), P(FAKE),
                      P(0)) == EINVAL
+    c1 = fake_cache()
+    c1.v_pl = None
+    assert status_of("kvq_append_decode_attn", ctypes.byref(L), P(FAKE), P(FAKE), P(FAKE),
+                     ctypes.byref(c1), ctypes.c_float(0.088), 8, P(FAKE), ctypes.c_size_t(ws),
+                     P(FAKE), P(0)) == EINVAL
 
 
 def test_bench_refuses_more_than_one_gpu():

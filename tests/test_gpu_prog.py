@@ -12,6 +12,10 @@ ABI against the oracle on the same seeded inputs.
 * Decode: within 2e-3 of the oracle's fp64 attention over the current
   widths, at split counts where window groups fall to different waves and
   where one wave takes several; the one-split fp32 record as well.
+* Append and decode in one launch: every step within 2e-3 of the oracle's
+  attention from the cache the call found (window groups at their former
+  widths, the packed group and the new token at 16 bits), and after every
+  pack every byte equal to a prefill of the same tokens.
 """
 import numpy as np
 import pytest
@@ -101,6 +105,52 @@ def test_prog_appends_equal_prefill(w8, w4):
             check_output(case.decode(q, 5), oracle.attention(qz, q, SM_SCALE), w.io_dtype, ATOL)
     assert oracle.n_quant(w.tokens + w.n_app, w.residual) // 32 - ng0 == 4
     assert kvq.kvq_check(case.cache.struct) == 0
+
+
+FUSED_PROG = [
+    kvq_synth.Workload("fprog-2-5", 2, 8, 2, 32 * 6 + 64 + 20, n_qry=8, n_app=100,
+                       io_dtype="bf16", outliers="pct2x10", n_pairs_hi=6, residual=64, seed=68,
+                       prog_w8=2, prog_w4=5),
+    kvq_synth.Workload("fprog-0-2-g1", 1, 3, 3, 32 * 5 + 32 + 7, n_qry=8, n_app=100,
+                       io_dtype="fp16", n_pairs_hi=8, residual=32, seed=69, prog_w8=0,
+                       prog_w4=2),
+    kvq_synth.Workload("fprog-2-2-raw16", 1, 8, 2, 32 * 4 + 32 + 30, n_qry=8, n_app=100,
+                       io_dtype="bf16", n_pairs_hi=6, bits_hi=16, residual=32, seed=70,
+                       prog_w8=2, prog_w4=2),
+]
+
+
+@pytest.mark.parametrize("w", FUSED_PROG, ids=_ids)
+def test_prog_append_and_decode_in_one_launch(w):
+    # each step's output against the oracle's attention from the cache the
+    # call found; after each pack (its shrinks run once every split has read
+    # the window groups) every byte against the prefill of the same tokens
+    print("case", w.name, flush=True)
+    case = Case(w, T=w.tokens, max_tokens=w.max_tokens)
+    pairs = case.oracle_select()[1]
+    S = 5
+    ws = torch.zeros(kvq.kvq_workspace_bytes(case.layout, S), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    q_bits = case.d["q_dec"][:, :, 0]
+    q = dev(q_bits)
+    packs = 0
+    for i in range(w.n_app):
+        t = w.tokens + i
+        kvq.kvq_append_decode_attn(case.layout, dev(np.ascontiguousarray(case.d["k"][:, :, t])),
+                                   dev(np.ascontiguousarray(case.d["v"][:, :, t])), q,
+                                   case.cache.struct, SM_SCALE, S, ws, out)
+        before = case.oracle_quant(T=t, pairs=pairs)
+        got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype)
+        check_output(got, oracle.attention_one_launch(before, q_bits, SM_SCALE), w.io_dtype,
+                     ATOL)
+        if oracle.n_quant(t + 1, w.residual) > oracle.n_quant(t, w.residual):
+            packs += 1
+            qz = case.oracle_quant(T=t + 1, pairs=pairs)
+            compare_cache(case, qz, qz.nq // 32)
+    assert packs >= 3
+    assert kvq.kvq_check(case.cache.struct) == 0
+    qz = case.oracle_quant(T=w.tokens + w.n_app, pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
 
 
 def test_prog_holds_less_than_an_eight_bit_cache():
