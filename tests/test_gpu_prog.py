@@ -178,7 +178,7 @@ def _random_prog_layouts(n, seed):
         w8 = int(rng.integers(0, w4 + 1))
         T = int(rng.integers(1, 900))
         out.append(kvq_synth.Workload(
-            "prand%d" % i, int(rng.integers(1, 3)), G * Hkv, Hkv, T, n_qry=8, n_app=40,
+            "prand%d" % i, int(rng.integers(1, 3)), G * Hkv, Hkv, T, n_qry=8, n_app=64,
             io_dtype=str(rng.choice(["fp16", "bf16"])),
             outliers=str(rng.choice(["none", "pairs4x8", "pct2x10"])),
             n_pairs_hi=int(rng.integers(0, 9)), bits_hi=int(rng.choice([4, 16])), residual=R,
@@ -188,9 +188,11 @@ def _random_prog_layouts(n, seed):
 
 @pytest.mark.parametrize("w", _random_prog_layouts(10, 11), ids=_ids)
 def test_prog_random_layouts(w):
-    # prefill: every byte and the decode at a drawn split count; then 40
+    # prefill: every byte and the decode at a drawn split count; then 32
     # appends (at least one pack): every byte and the decode again, and the
-    # no-allocation entry point equal to the plain one
+    # no-allocation entry point equal to the plain one; then 32 one-launch
+    # steps at a drawn split count, each against the oracle's attention from
+    # the cache the call found, and every byte at the end
     print("case", w, flush=True)
     rng = np.random.default_rng(w.seed)
     case = Case(w, T=w.tokens, max_tokens=w.max_tokens)
@@ -202,12 +204,13 @@ def test_prog_random_layouts(w):
     check_output(case.decode(q, S), oracle.attention(qz, q, SM_SCALE), w.io_dtype, ATOL)
     kn = dev(np.ascontiguousarray(case.d["k"][:, :, w.tokens:]))
     vn = dev(np.ascontiguousarray(case.d["v"][:, :, w.tokens:]))
-    for i in range(w.n_app):
+    n1 = w.n_app // 2
+    for i in range(n1):
         kvq.kvq_append(case.layout, kn[:, :, i].contiguous(), vn[:, :, i].contiguous(),
                        case.cache.struct)
     torch.cuda.synchronize()
     assert kvq.kvq_check(case.cache.struct) == 0
-    case.T = w.tokens + w.n_app
+    case.T = w.tokens + n1
     qz = case.oracle_quant(pairs=pairs)
     compare_cache(case, qz, qz.nq // 32)
     S = int(rng.integers(1, 12))
@@ -218,6 +221,20 @@ def test_prog_random_layouts(w):
     torch.cuda.synchronize()
     assert np.array_equal(kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype),
                           got)
+    S = int(rng.integers(1, 12))
+    ws = torch.zeros(kvq.kvq_workspace_bytes(case.layout, S), dtype=torch.uint8, device="cuda")
+    qd = dev(q)
+    for i in range(n1, w.n_app):
+        t = w.tokens + i
+        kvq.kvq_append_decode_attn(case.layout, kn[:, :, i].contiguous(), vn[:, :, i].contiguous(),
+                                   qd, case.cache.struct, SM_SCALE, S, ws, out)
+        before = case.oracle_quant(T=t, pairs=pairs)
+        got = kvq_synth.bits_to_f64(out.cpu().numpy().view(np.uint16), w.io_dtype)
+        check_output(got, oracle.attention_one_launch(before, q, SM_SCALE), w.io_dtype, ATOL)
+    assert kvq.kvq_check(case.cache.struct) == 0
+    case.T = w.tokens + w.n_app
+    qz = case.oracle_quant(pairs=pairs)
+    compare_cache(case, qz, qz.nq // 32)
 
 
 def test_prog_guard_bands_survive():
