@@ -401,6 +401,37 @@ def streaming_leg(args, w):
     fused_us = run_fused()
     for c in layers:
         assert kvq.kvq_check(c.struct) == 0
+
+    def run_graph(fused):
+        # one HIP graph holds a token's step on every layer cache (a model's
+        # decode step), captured once with static inputs and replayed n times
+        restore()
+        kst, vst, qst = kn[0].clone(), vn[0].clone(), qd[0].clone()
+        a, b, qq = P(kst.data_ptr()), P(vst.data_ptr()), P(qst.data_ptr())
+        wsp, outp = P(ws.data_ptr()), P(out.data_ptr())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cst = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for cs in structs:
+                if fused:
+                    assert lib.kvq_append_decode_attn(L, a, b, qq, cs, scale, S, wsp, wsb, outp,
+                                                      cst) == 0
+                else:
+                    assert lib.kvq_append(L, a, b, cs, cst) == 0
+                    assert lib.kvq_decode_attn(L, qq, cs, scale, S, wsp, wsb, outp, cst) == 0
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(n):
+            g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        for c in layers:
+            assert kvq.kvq_check(c.struct) == 0
+        return ev0.elapsed_time(ev1) * 1e3 / (n * NL)
+
+    graph_us = run_graph(False)
+    graph_fused_us = run_graph(True)
     alg = sum(algorithmic_bytes(w, T0 + i + 1) for i in range(n)) / n
     gbs = alg / (decode_us * 1e-6) / 1e9
     return {
@@ -415,6 +446,8 @@ def streaming_leg(args, w):
         "append_us_per_step": round(append_us, 3),
         "decode_us_per_step": round(decode_us, 3),
         "fused_us_per_step": round(fused_us, 3) if fused_us is not None else None,
+        "graph_us_per_step": round(graph_us, 3),
+        "graph_fused_us_per_step": round(graph_fused_us, 3),
         "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -429,7 +462,9 @@ def streaming_leg(args, w):
         "algorithmic_bytes_per_step": int(alg),
         "note": "one step = kvq_append + kvq_decode_attn on one layer cache; value = "
                 "decode bytes / (step time - append time); fused_us_per_step: the same "
-                "steps as one kvq_append_decode_attn launch each",
+                "steps as one kvq_append_decode_attn launch each; graph_*: the two-call and "
+                "one-launch steps of every layer cache captured in one HIP graph per token "
+                "and replayed",
     }
 
 
