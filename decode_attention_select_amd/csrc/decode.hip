@@ -616,6 +616,11 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       q16[4 * i + e] = qvalid ? pk_rne(a * qsc, bb * qsc) : 0u;
       qm[4 * i + e] = lo_lane ? q16[4 * i + e] : 0u;
     }
+  // the query for the keys' zero-point bias: LOCOL zero on the lo lanes, so
+  // that the bias lands in the hi columns only (once per call, not per group)
+  uint32_t qh[16];
+#pragma unroll
+  for (int w = 0; w < 16; w++) qh[w] = LOCOL && lo_lane ? 0u : q16[w];
 
   const int T_old = min(max(len, 0), g.max_tokens);  // reads stay inside the cache
   // FUSED: whether this call appends (a full cache or a negative length is
@@ -630,6 +635,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const int nmine = (HASQ && gfirst < n2) ? (n2 - 1 - gfirst) / STR + 1 : 0;
 
   uint32_t qhi[4] = {0, 0, 0, 0};  // HIMODE 4: 4*q (fp16); HIMODE 16: raw q
+  uint32_t qhim[4] = {0, 0, 0, 0};  // HIMODE 4: qhi on K-lanes 16..31 (the residual lanes), else 0
   int sal_ch = 0;                  // HIMODE 4: salient channel whose scale lane%16 copies
   if constexpr (HIMODE != 0 || PRUNE) {
     // tables: every head's query rows (each wave writes the same values and
@@ -690,7 +696,10 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     if constexpr (HIMODE == 4) {
       // 4 q (exact in fp16)
 #pragma unroll
-      for (int e = 0; e < 4; e++) qhi[e] = h2u(u2h(qhi[e]) * u2h(0x44004400u));
+      for (int e = 0; e < 4; e++) {
+        qhi[e] = h2u(u2h(qhi[e]) * u2h(0x44004400u));
+        qhim[e] = kq < 2 ? 0u : qhi[e];
+      }
     }
     sal_ch = lds.hil[lane & 15] & (D - 1);
   }
@@ -798,12 +807,13 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
             qsl[4 * i + e] = pk_fma_lo(q16[4 * i + e], sv[e], qs[4 * i + e]);
           }
         }
-        const u4 qb = u4{q16[4 * i], q16[4 * i + 1], q16[4 * i + 2], q16[4 * i + 3]};
+        const u4 qb = u4{qh[4 * i], qh[4 * i + 1], qh[4 * i + 2], qh[4 * i + 3]};
         cb = mma_f16(zv, qb, cb);
       }
     }
-    if constexpr (LOCOL) {
-      // the bias enters the hi columns only
+    if constexpr (LOCOL && PRUNE) {
+      // the bias enters the hi columns only (the unpruned path's qh is zero
+      // on the lo lanes already)
 #pragma unroll
       for (int r = 0; r < 4; r++) cb[r] = lo_lane ? 0.0f : cb[r];
     }
@@ -819,9 +829,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         // 4*q*s as an exact fp16 pair: K-lanes 0..15 its rounding hi,
-        // K-lanes 16..31 the residual lo
-        const uint32_t hi = pk_mul(qhi[e], spv[e]);
-        qshi[e] = kq < 2 ? hi : pk_fma_lo(qhi[e], spv[e], hi);
+        // K-lanes 16..31 the residual lo (qhim is zero on the former, so
+        // the fma subtracts 0 there and the rounding hi elsewhere)
+        qshi[e] = pk_fma_lo(qhi[e], spv[e], pk_mul(qhim[e], spv[e]));
       }
     }
     // DENSE1: the 1-bit run's word of tile row col (both halves), masked once
@@ -947,9 +957,10 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
     // (non-negative fp16, so their bits order as integers)
     const u4 meta = ((const u4*)sm)[lane];
     const uint32_t vs2 = pk_max_u16(pk_max_u16(meta[0], meta[1]), pk_max_u16(meta[2], meta[3]));
-    const bool wide = lane >= 32 && lane < 48 && max(vs2 & 0xFFFFu, vs2 >> 16) > VSCALE_WIDE;
-    softmax_step(cr, sc_q, __builtin_amdgcn_ballot_w64(wide) ? RESCALE_SLACK_WIDE : RESCALE_SLACK,
-                 p);
+    const uint64_t wide =
+        __builtin_amdgcn_ballot_w64(max(vs2 & 0xFFFFu, vs2 >> 16) > VSCALE_WIDE) &
+        0x0000FFFF00000000ull;  // lanes 32..47
+    softmax_step(cr, sc_q, wide ? RESCALE_SLACK_WIDE : RESCALE_SLACK, p);
     const u4 P = u4{pk_rne(p[0], p[1]), pk_rne(p[2], p[3]), pk_rne(p[4], p[5]), pk_rne(p[6], p[7])};
     // LOCOL: the weights on lo lanes (zero elsewhere), as qm for the query
     u4 Pm;
