@@ -323,6 +323,7 @@ struct Lds {
   uint8_t pone[64];                          // DENSE1: pair j is a 1-bit pair
   uint16_t sal_s[NW][16];                    // per wave: salient scales of the group in work
   int mrank;                                 // -1: not the last split; 0/1: merge (1: all splits on this XCD)
+  int prog[NW];                              // per wave: quantized groups it has started
 #ifdef KVQ_STAMPS
   unsigned long long stamp[STAMP_SLOTS];
 #endif
@@ -409,6 +410,7 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   const bool qvalid = hvalid || lo_lane;          // the lane carries a query
   const int hq = hvalid ? col : (lo_lane ? 15 - col : 0);
   KVQ_STAMP(tid == 0, 0);
+  lds.prog[wave] = 0;
 
   // ---- entry.  The length and the leading ranks are scalar loads; the
   // query (every head of the group: G rows of 256 bytes) is copied straight
@@ -1150,6 +1152,21 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // is refilled with group i + NSLOT
   if constexpr (HASQ) {
     for (int i = 0; i < nmine; i++) {
+      // wave priority: the arbiter favours the older of a SIMD's two waves
+      // (waves w and w ^ 4 of the workgroup), which leaves the younger to
+      // finish its last groups alone, at a lower issue rate.  A wave that has
+      // started more groups than the other wave of its SIMD yields to it
+      // (advisory: a stale count only delays the balance).
+      {
+        const int other = __builtin_amdgcn_readfirstlane(lds.prog[wave ^ 4]);
+        lds.prog[wave] = i;
+        if (i > other)
+          __builtin_amdgcn_s_setprio(0);
+        else if (i < other)
+          __builtin_amdgcn_s_setprio(2);
+        else
+          __builtin_amdgcn_s_setprio(1);
+      }
       wait_slot<NLD, NSLOT>(issued - 1 - i);
       uint8_t* slot = slots + (i % NSLOT) * SLOTB;
       process_group(slot, Wide<false>{}, 2, nullptr, nullptr);
@@ -1165,6 +1182,8 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
         issued++;
       }
     }
+    lds.prog[wave] = 1 << 20;  // done: the other wave of the SIMD no longer yields to it
+    __builtin_amdgcn_s_setprio(0);
     // copies issued before the length was known, past the live groups: they
     // must land before the LDS is reused
     if (issued > nmine) {
