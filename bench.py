@@ -837,6 +837,58 @@ def stamps_leg(args, w):
                     "each), so the event time holds the launch"}
 
 
+# kvq_issue_probe's mixes: (name, instructions per loop iteration of one wave)
+PROBE_KINDS = [("int_valu", 32), ("cvt_pk_f16_fp4+xor", 32), ("pk_mul_f16", 16),
+               ("exp_f32+mul_f32", 32), ("mfma_16x16x32_f16", 4), ("mfma+int_valu", 36)]
+PROBE_ITERS = 256
+ENGINE_GHZ = 2.4
+
+
+def issue_probe_leg():
+    """Issue cost per SIMD of the decode loop's instruction kinds (one launch
+    of kvq_issue_probe per kind and occupancy, event-timed, mean of 10)."""
+    import torch
+    from decode_attention_select_amd import kvq
+
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    rows = []
+    for wps in (1, 2, 8):
+        nb = n_cu * wps
+        out = torch.empty(nb * 256, dtype=torch.int32, device="cuda")
+        us = []
+        for kind in range(len(PROBE_KINDS)):
+            for _ in range(3):
+                kvq.kvq_issue_probe(kind, nb, out, stream=stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                kvq.kvq_issue_probe(kind, nb, out, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3 / 10)
+        # cycles per loop iteration of one wave, per SIMD (all waves of a SIMD
+        # share its issue), at the engine clock
+        cyc = [u * 1e-6 * ENGINE_GHZ * 1e9 / (wps * PROBE_ITERS) for u in us]
+        per_int = cyc[0] / 32
+        rows.append({
+            "waves_per_simd": wps,
+            "us": {n: round(u, 3) for (n, _), u in zip(PROBE_KINDS, us)},
+            "cycles_per_instruction": {
+                "int_valu": round(per_int, 2),
+                "cvt_scalef32_pk_f16_fp4": round((cyc[1] - 16 * per_int) / 16, 2),
+                "pk_mul_f16": round(cyc[2] / 16, 2),
+                "exp_f32": round((cyc[3] - 16 * per_int) / 16, 2),
+                "mfma_16x16x32_f16": round(cyc[4] / 4, 2),
+            },
+            # 1: MFMA and VALU issue serialize on a SIMD; max/sum: they overlap
+            "mfma_valu_serial_fraction": round(us[5] / (us[4] + us[0]), 3),
+            "full_overlap_would_be": round(max(us[4], us[0]) / (us[4] + us[0]), 3),
+        })
+    return {"issue_probe": "gfx950", "compute_units": n_cu, "engine_ghz": ENGINE_GHZ,
+            "iterations_per_wave": PROBE_ITERS, "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -863,6 +915,9 @@ def main():
                     help="only run the copy-kernel calibration of this size")
     ap.add_argument("--ceiling", action="store_true",
                     help="time only kvq_read_ceiling (the decode's reads, no arithmetic)")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="time kvq_issue_probe: the issue cost per SIMD of the decode loop's "
+                         "instruction kinds, and whether MFMA overlaps VALU")
     ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
                     help="print the traffic record from four rocprofv3 --pmc output "
                          "directories: decode FETCH_SIZE, decode WRITE_SIZE, copy FETCH_SIZE, "
@@ -877,6 +932,9 @@ def main():
         sys.exit(2)
     if args.copy_mib:
         copy_calibration(args.copy_mib)
+        return
+    if args.issue_probe:
+        print(json.dumps(issue_probe_leg()), flush=True)
         return
 
     import numpy as np

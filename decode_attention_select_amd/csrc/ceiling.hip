@@ -104,4 +104,77 @@ hipError_t launch_ceiling(const Geo& g, const kvq_cache* c, int S, void* sink, h
   return hipGetLastError();
 }
 
+// ---- issue probe.  The decode loop is made of integer VALU (code masks),
+// v_cvt_scalef32_pk_f16_fp4 (codes to fp16), packed fp16 multiplies (the
+// exact q*s and p*s pairs), v_exp_f32 (softmax weights) and
+// v_mfma_f32_16x16x32_f16; this kernel runs each kind alone, and MFMA with
+// integer VALU in one loop, so that their issue cost per SIMD and whether a
+// SIMD overlaps MFMA with VALU can be read from the launch times.  Every
+// thread folds its registers into one word of `out` (which keeps every
+// instruction live).
+typedef _Float16 ph2 __attribute__((ext_vector_type(2)));
+typedef _Float16 ph8 __attribute__((ext_vector_type(8)));
+typedef float pf4 __attribute__((ext_vector_type(4)));
+
+template <int KIND>
+__global__ __launch_bounds__(PROBE_THREADS) void issue_probe_kernel(uint32_t* out) {
+  const uint32_t gid = blockIdx.x * PROBE_THREADS + threadIdx.x;
+  uint32_t x[16];
+  float fx[16];
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    x[i] = 0x9E3779B9u * (gid + 7u * i) + i;
+    fx[i] = (float)(x[i] & 255u) * 0.001f;
+  }
+  pf4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  const ph8 a = __builtin_bit_cast(ph8, cu4{x[0], x[1], x[2], x[3]});
+  for (int it = 0; it < PROBE_ITERS; it++) {
+    if constexpr (KIND == 4 || KIND == 5) {  // 4 MFMA, independent accumulators
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, a, acc[i], 0, 0, 0);
+    }
+    if constexpr (KIND == 0 || KIND == 5) {  // 16 v_add_u32 + 16 v_xor_b32
+#pragma unroll
+      for (int i = 0; i < 16; i++) x[i] = x[i] ^ (x[(i + 1) & 15] + (uint32_t)it);
+    } else if constexpr (KIND == 1) {  // 16 v_cvt_scalef32_pk_f16_fp4 + 16 v_xor_b32
+#define KVQ_PROBE_CVT(i, sel)                                                                \
+  x[i] ^= __builtin_bit_cast(uint32_t,                                                       \
+                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x[(i + 3) & 15], 2.0f, sel));
+      KVQ_PROBE_CVT(0, 0) KVQ_PROBE_CVT(1, 1) KVQ_PROBE_CVT(2, 2) KVQ_PROBE_CVT(3, 3)
+      KVQ_PROBE_CVT(4, 0) KVQ_PROBE_CVT(5, 1) KVQ_PROBE_CVT(6, 2) KVQ_PROBE_CVT(7, 3)
+      KVQ_PROBE_CVT(8, 0) KVQ_PROBE_CVT(9, 1) KVQ_PROBE_CVT(10, 2) KVQ_PROBE_CVT(11, 3)
+      KVQ_PROBE_CVT(12, 0) KVQ_PROBE_CVT(13, 1) KVQ_PROBE_CVT(14, 2) KVQ_PROBE_CVT(15, 3)
+#undef KVQ_PROBE_CVT
+    } else if constexpr (KIND == 2) {  // 16 v_pk_mul_f16
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        x[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(ph2, x[i]) *
+                                                __builtin_bit_cast(ph2, x[(i + 5) & 15]));
+    } else if constexpr (KIND == 3) {  // 16 v_exp_f32 + 16 v_mul_f32
+#pragma unroll
+      for (int i = 0; i < 16; i++) fx[i] = __builtin_amdgcn_exp2f(fx[(i + 1) & 15]) * 0.5f;
+    }
+  }
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) r ^= x[i] ^ __float_as_uint(fx[i]);
+#pragma unroll
+  for (int i = 0; i < 4; i++) r ^= __float_as_uint(acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3]);
+  out[gid] = r;
+}
+
+hipError_t launch_issue_probe(int kind, int n_blocks, void* out, hipStream_t st) {
+  const dim3 grid(n_blocks), block(PROBE_THREADS);
+  uint32_t* o = (uint32_t*)out;
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(issue_probe_kernel<0>, grid, block, 0, st, o); break;
+    case 1: hipLaunchKernelGGL(issue_probe_kernel<1>, grid, block, 0, st, o); break;
+    case 2: hipLaunchKernelGGL(issue_probe_kernel<2>, grid, block, 0, st, o); break;
+    case 3: hipLaunchKernelGGL(issue_probe_kernel<3>, grid, block, 0, st, o); break;
+    case 4: hipLaunchKernelGGL(issue_probe_kernel<4>, grid, block, 0, st, o); break;
+    default: hipLaunchKernelGGL(issue_probe_kernel<5>, grid, block, 0, st, o); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace kvq

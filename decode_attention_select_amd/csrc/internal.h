@@ -26,5 +26,9 @@ size_t decode_tick_bytes(int B, int Hkv);
 // the decode kernel's grid and group stream, reading only (ceiling.hip)
 hipError_t launch_ceiling(const Geo& g, const kvq_cache* c, int n_splits, void* sink,
                           hipStream_t st);
+// the issue probe (ceiling.hip): workgroups of PROBE_THREADS threads, each
+// wave PROBE_ITERS iterations of one instruction mix
+constexpr int PROBE_THREADS = 256, PROBE_ITERS = 256;
+hipError_t launch_issue_probe(int kind, int n_blocks, void* out, hipStream_t st);
 
 }  // namespace kvq

@@ -188,6 +188,11 @@ def kvq_read_ceiling(layout, cache: kvq_cache, n_splits, sink, stream=None):
           ctypes.c_int32(n_splits), _ptr(sink), _stream(stream))
 
 
+def kvq_issue_probe(kind, n_blocks, out, stream=None):
+    _call("kvq_issue_probe", ctypes.c_int32(kind), ctypes.c_int32(n_blocks), _ptr(out),
+          _stream(stream))
+
+
 def kvq_check(cache: kvq_cache, stream=None) -> int:
     err = ctypes.c_int32(0)
     _call("kvq_check", ctypes.byref(cache), ctypes.byref(err), _stream(stream))

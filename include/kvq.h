@@ -444,6 +444,22 @@ kvq_status kvq_decode_attn_noalloc(const kvq_layout *L, const void *q,
 kvq_status kvq_read_ceiling(const kvq_layout *L, const kvq_cache *cache,
                             int32_t n_splits, void *sink, void *stream);
 
+/* Measurement only: the issue cost of the instruction kinds the decode loop
+ * is made of, on this GPU.  One launch of n_blocks workgroups of 256 threads
+ * (4 waves; n_blocks = k x the compute-unit count puts k waves on every
+ * SIMD), each wave running 256 iterations of one mix:
+ *   kind 0: 16 v_add_u32 + 16 v_xor_b32 (integer VALU, as the code masks)
+ *   kind 1: 16 v_cvt_scalef32_pk_f16_fp4 + 16 v_xor_b32 (codes to fp16)
+ *   kind 2: 16 v_pk_mul_f16 (the exact q*s and p*s pairs)
+ *   kind 3: 16 v_exp_f32 + 16 v_mul_f32 (softmax weights)
+ *   kind 4: 4 v_mfma_f32_16x16x32_f16 on independent accumulators
+ *   kind 5: kinds 4 and 0 in one loop (whether a SIMD overlaps the two)
+ * Every thread writes one 32-bit word of `out` (device memory of at least
+ * n_blocks x 1024 bytes, 16-byte aligned); time the launch with events on
+ * `stream`.  KVQ_EINVAL for a kind outside 0..5 or n_blocks < 1, KVQ_EALIGN
+ * for a misaligned `out`. */
+kvq_status kvq_issue_probe(int32_t kind, int32_t n_blocks, void *out, void *stream);
+
 /* Synchronizes `stream`, then copies cache->err to *host_err (tests and
  * debugging only). */
 kvq_status kvq_check(const kvq_cache *cache, int32_t *host_err /*host*/,
