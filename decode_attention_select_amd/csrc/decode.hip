@@ -1156,8 +1156,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       // (waves w and w ^ 4 of the workgroup), which leaves the younger to
       // finish its last groups alone, at a lower issue rate.  A wave that has
       // started more groups than the other wave of its SIMD yields to it
-      // (advisory: a stale count only delays the balance).
-      {
+      // (advisory: a stale count only delays the balance).  Eight waves on
+      // four SIMDs only; other wave counts keep the arbiter's order.
+      if constexpr (NW == 8) {
         const int other = __builtin_amdgcn_readfirstlane(lds.prog[wave ^ 4]);
         lds.prog[wave] = i;
         if (i > other)
