@@ -839,7 +839,8 @@ def stamps_leg(args, w):
 
 # kvq_issue_probe's mixes: (name, instructions per loop iteration of one wave)
 PROBE_KINDS = [("int_valu", 32), ("cvt_pk_f16_fp4+xor", 32), ("pk_mul_f16", 16),
-               ("exp_f32+mul_f32", 32), ("mfma_16x16x32_f16", 4), ("mfma+int_valu", 36)]
+               ("exp_f32+mul_f32", 32), ("mfma_16x16x32_f16", 4), ("mfma+int_valu", 36),
+               ("mfma_16x16x16_f16", 4)]
 PROBE_ITERS = 256
 ENGINE_GHZ = 2.4
 
@@ -880,6 +881,7 @@ def issue_probe_leg():
                 "pk_mul_f16": round(cyc[2] / 16, 2),
                 "exp_f32": round((cyc[3] - 16 * per_int) / 16, 2),
                 "mfma_16x16x32_f16": round(cyc[4] / 4, 2),
+                "mfma_16x16x16_f16": round(cyc[6] / 4, 2),
             },
             # 1: MFMA and VALU issue serialize on a SIMD; max/sum: they overlap
             "mfma_valu_serial_fraction": round(us[5] / (us[4] + us[0]), 3),

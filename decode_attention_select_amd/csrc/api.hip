@@ -355,7 +355,7 @@ kvq_status kvq_read_ceiling(const kvq_layout* L, const kvq_cache* cache, int32_t
 }
 
 kvq_status kvq_issue_probe(int32_t kind, int32_t n_blocks, void* out, void* stream) {
-  if (kind < 0 || kind > 5 || n_blocks < 1) return KVQ_EINVAL;
+  if (kind < 0 || kind > 6 || n_blocks < 1) return KVQ_EINVAL;
   if (kvq_status s = check_ptr(out)) return s;
   return hip_status(launch_issue_probe(kind, n_blocks, out, (hipStream_t)stream));
 }

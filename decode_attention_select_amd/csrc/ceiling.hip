@@ -113,6 +113,7 @@ hipError_t launch_ceiling(const Geo& g, const kvq_cache* c, int S, void* sink, h
 // thread folds its registers into one word of `out` (which keeps every
 // instruction live).
 typedef _Float16 ph2 __attribute__((ext_vector_type(2)));
+typedef _Float16 ph4 __attribute__((ext_vector_type(4)));
 typedef _Float16 ph8 __attribute__((ext_vector_type(8)));
 typedef float pf4 __attribute__((ext_vector_type(4)));
 
@@ -132,6 +133,11 @@ __global__ __launch_bounds__(PROBE_THREADS) void issue_probe_kernel(uint32_t* ou
     if constexpr (KIND == 4 || KIND == 5) {  // 4 MFMA, independent accumulators
 #pragma unroll
       for (int i = 0; i < 4; i++) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, a, acc[i], 0, 0, 0);
+    }
+    if constexpr (KIND == 6) {  // 4 MFMA of half the contraction length (K = 16)
+      const ph4 a4 = __builtin_shufflevector(a, a, 0, 1, 2, 3);
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, a4, acc[i], 0, 0, 0);
     }
     if constexpr (KIND == 0 || KIND == 5) {  // 16 v_add_u32 + 16 v_xor_b32
 #pragma unroll
@@ -172,7 +178,8 @@ hipError_t launch_issue_probe(int kind, int n_blocks, void* out, hipStream_t st)
     case 2: hipLaunchKernelGGL(issue_probe_kernel<2>, grid, block, 0, st, o); break;
     case 3: hipLaunchKernelGGL(issue_probe_kernel<3>, grid, block, 0, st, o); break;
     case 4: hipLaunchKernelGGL(issue_probe_kernel<4>, grid, block, 0, st, o); break;
-    default: hipLaunchKernelGGL(issue_probe_kernel<5>, grid, block, 0, st, o); break;
+    case 5: hipLaunchKernelGGL(issue_probe_kernel<5>, grid, block, 0, st, o); break;
+    default: hipLaunchKernelGGL(issue_probe_kernel<6>, grid, block, 0, st, o); break;
   }
   return hipGetLastError();
 }

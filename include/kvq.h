@@ -454,9 +454,10 @@ kvq_status kvq_read_ceiling(const kvq_layout *L, const kvq_cache *cache,
  *   kind 3: 16 v_exp_f32 + 16 v_mul_f32 (softmax weights)
  *   kind 4: 4 v_mfma_f32_16x16x32_f16 on independent accumulators
  *   kind 5: kinds 4 and 0 in one loop (whether a SIMD overlaps the two)
+ *   kind 6: 4 v_mfma_f32_16x16x16_f16 (half the contraction length of kind 4)
  * Every thread writes one 32-bit word of `out` (device memory of at least
  * n_blocks x 1024 bytes, 16-byte aligned); time the launch with events on
- * `stream`.  KVQ_EINVAL for a kind outside 0..5 or n_blocks < 1, KVQ_EALIGN
+ * `stream`.  KVQ_EINVAL for a kind outside 0..6 or n_blocks < 1, KVQ_EALIGN
  * for a misaligned `out`. */
 kvq_status kvq_issue_probe(int32_t kind, int32_t n_blocks, void *out, void *stream);
 

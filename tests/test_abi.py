@@ -162,7 +162,7 @@ def test_decode_validation():
     assert ceil(S=0) == EINVAL and ceil(S=1025) == EINVAL
     # the issue probe: its kind, block count and output
     probe = lambda kind=0, nb=4, o=FAKE: status_of("kvq_issue_probe", kind, nb, P(o), P(0))
-    assert probe(kind=-1) == EINVAL and probe(kind=6) == EINVAL and probe(nb=0) == EINVAL
+    assert probe(kind=-1) == EINVAL and probe(kind=7) == EINVAL and probe(nb=0) == EINVAL
     assert probe(o=0) == EINVAL and probe(o=FAKE + 4) == EALIGN
 
 

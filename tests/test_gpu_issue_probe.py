@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 SENTINEL = 0x5A5A5A5A
 
 
-@pytest.mark.parametrize("kind", range(6))
+@pytest.mark.parametrize("kind", range(7))
 def test_issue_probe_writes_its_words_only(kind):
     nb = 4
     print("issue probe kind %d, %d blocks" % (kind, nb), flush=True)
