@@ -93,6 +93,17 @@ __device__ inline uint32_t to_f16_pair(uint32_t w) {
   return pk_rne(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
+// fp32 -> the io dtype, round to nearest even (bf16: finite values)
+template <bool BF16>
+__device__ inline uint16_t to_io_bits(float v) {
+  if constexpr (BF16) {
+    const uint32_t u = __float_as_uint(v);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  } else {
+    return f32_to_half_bits(v);
+  }
+}
+
 // Elementwise max of two u16 pairs.
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t pk_max_u16(uint32_t a, uint32_t b) {
@@ -1266,6 +1277,9 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
                          __HIP_MEMORY_SCOPE_AGENT);
       *(uint64_t*)&ws.mlL[rbh + (size_t)s * G + h] = mlv;
     }
+    // one split: its record is the attention output, stored at once (no
+    // split merge follows)
+    if (S == 1) out[((size_t)b * g.Hq + kh * G + h) * D + cc] = to_io_bits<BF16>(v);
   }
 
   // ---- ticket.  Every record store has completed (s_waitcnt) before the
@@ -1327,98 +1341,93 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   }
   const bool local = mr == 1;  // every split ran on this XCD: read the L2 copy
   if (tid == 0) __hip_atomic_store(tick, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // The last workgroup merges all splits.  Thread (chunk q, subset r): the
-  // 4 channels 4 (q % 32) .. of head q / 32, over splits r, r + NR, ...; the
-  // NR threads of a chunk are adjacent lanes and add up with shuffles.  The
-  // (m, l) of the first 64 splits and the records of up to 2 RB splits per
-  // thread are requested at once, in that order; meanwhile each head's
-  // weights w_i = 2^(m_i - M) l_i (M the largest running max) and 1 / L,
-  // L = sum w_i, are formed (one wave per head, lanes over splits).
-  const int NQ = G * (D / 4);
-  int NR = 1;
-  while (NR * 2 * NQ <= WG_THREADS) NR *= 2;
-  const int qc = tid / NR, r = tid % NR;
-  const bool act = qc < NQ;
-  const int h = act ? qc / (D / 4) : 0, c4 = act ? 4 * (qc % (D / 4)) : 0;
-  constexpr int RB = 8;
-  const int nk = (S - r + NR - 1) / NR;  // this thread's splits
-  const int nkmax = (S + NR - 1) / NR;   // the most any thread has
-  const __amdgpu_buffer_rsrc_t rs_mlL =
-      __builtin_amdgcn_make_buffer_rsrc(ws.mlL + rbh, 0, (int)(S * G * 8), BUF_RSRC_WORD3);
-  auto load_ml = [&](int i, int hh) -> uint64_t {
-    if (local) {
-      const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs_mlL, (i * G + hh) * 8, 0, CPOL_SC0);
-      return (uint64_t)x[0] | ((uint64_t)x[1] << 32);
-    }
-    return __hip_atomic_load((const uint64_t*)&ws.ml[rbh + (size_t)i * G + hh], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto load_batch = [&](u4 (&ov)[RB], int k0) {
-#pragma unroll
-    for (int k = 0; k < RB; k++) {
-      const int ooff = ((min(r + (k0 + k) * NR, S - 1) * G + h) * D + c4) * 4;  // past S: unused
-      ov[k] = local ? __builtin_amdgcn_raw_buffer_load_b128(rs_oL, ooff, 0, CPOL_SC0)
-                    : __builtin_amdgcn_raw_buffer_load_b128(rs_o, ooff, 0, CPOL_SC1);
-    }
-  };
-  const uint64_t ml0 = wave < G ? load_ml(min(lane, S - 1), wave) : 0ull;
-  u4 ova[RB], ovb[RB];
-  load_batch(ova, 0);
-  if (nkmax > RB) load_batch(ovb, RB);
-  KVQ_STAMP(tid == 0, 18);
-  for (int hh = wave; hh < G; hh += NW) {
-    float M = -INFINITY;
-    for (int i = lane; i < S; i += 64) {
-      const uint64_t mv = (hh == wave && i == lane) ? ml0 : load_ml(i, hh);
-      const float mi = __uint_as_float((uint32_t)mv);
-      lds.u.fin.ml[i * MAXG + hh] = f2{mi, __uint_as_float((uint32_t)(mv >> 32))};
-      M = fmaxf(M, mi);
-    }
-    M = wave_max64(M);
-    float L = 0.0f;
-    for (int i = lane; i < S; i += 64) {
-      const f2 x = lds.u.fin.ml[i * MAXG + hh];
-      const float w = x[0] == -INFINITY ? 0.0f : ex2(x[0] - M) * x[1];
-      lds.u.fin.ml[i * MAXG + hh][0] = w;
-      L += w;
-    }
-    L = wave_sum64(L);
-    if (lane == 0) lds.u.fin.inv[hh] = L > 0.0f ? 1.0f / L : 0.0f;
-  }
-  __syncthreads();
-  KVQ_STAMP(tid == 0, 19);
-  f4 acc = {0, 0, 0, 0};
-  auto accum = [&](const u4 (&ov)[RB], int k0) {
-#pragma unroll
-    for (int k = 0; k < RB; k++)
-      if (k0 + k < nk)
-        acc += lds.u.fin.ml[(r + (k0 + k) * NR) * MAXG + h][0] * __builtin_bit_cast(f4, ov[k]);
-  };
-  accum(ova, 0);
-  if (nkmax > RB) accum(ovb, RB);
-  for (int k0 = 2 * RB; k0 < nkmax; k0 += RB) {
-    load_batch(ova, k0);
-    accum(ova, k0);
-  }
-  for (int o = 1; o < NR; o <<= 1)
-#pragma unroll
-    for (int e = 0; e < 4; e++) acc[e] += __shfl_xor(acc[e], o);
-  KVQ_STAMP(tid == 0, 20);
-  if (act && r == 0) {
-    const float inv = lds.u.fin.inv[h];
-    uint16_t* op = out + ((size_t)b * g.Hq + kh * G + h) * D + c4;
-    uint16_t bits[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const float v = acc[e] * inv;
-      if constexpr (BF16) {
-        const uint32_t u = __float_as_uint(v);
-        bits[e] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-      } else {
-        bits[e] = f32_to_half_bits(v);
+  // with one split the workgroup merge wrote the output
+  if (S > 1) {
+    // The last workgroup merges all splits.  Thread (chunk q, subset r): the
+    // 4 channels 4 (q % 32) .. of head q / 32, over splits r, r + NR, ...; the
+    // NR threads of a chunk are adjacent lanes and add up with shuffles.  The
+    // (m, l) of the first 64 splits and the records of up to 2 RB splits per
+    // thread are requested at once, in that order; meanwhile each head's
+    // weights w_i = 2^(m_i - M) l_i (M the largest running max) and 1 / L,
+    // L = sum w_i, are formed (one wave per head, lanes over splits).
+    const int NQ = G * (D / 4);
+    int NR = 1;
+    while (NR * 2 * NQ <= WG_THREADS) NR *= 2;
+    const int qc = tid / NR, r = tid % NR;
+    const bool act = qc < NQ;
+    const int h = act ? qc / (D / 4) : 0, c4 = act ? 4 * (qc % (D / 4)) : 0;
+    constexpr int RB = 8;
+    const int nk = (S - r + NR - 1) / NR;  // this thread's splits
+    const int nkmax = (S + NR - 1) / NR;   // the most any thread has
+    const __amdgpu_buffer_rsrc_t rs_mlL =
+        __builtin_amdgcn_make_buffer_rsrc(ws.mlL + rbh, 0, (int)(S * G * 8), BUF_RSRC_WORD3);
+    auto load_ml = [&](int i, int hh) -> uint64_t {
+      if (local) {
+        const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs_mlL, (i * G + hh) * 8, 0, CPOL_SC0);
+        return (uint64_t)x[0] | ((uint64_t)x[1] << 32);
       }
+      return __hip_atomic_load((const uint64_t*)&ws.ml[rbh + (size_t)i * G + hh], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto load_batch = [&](u4 (&ov)[RB], int k0) {
+#pragma unroll
+      for (int k = 0; k < RB; k++) {
+        const int ooff = ((min(r + (k0 + k) * NR, S - 1) * G + h) * D + c4) * 4;  // past S: unused
+        ov[k] = local ? __builtin_amdgcn_raw_buffer_load_b128(rs_oL, ooff, 0, CPOL_SC0)
+                      : __builtin_amdgcn_raw_buffer_load_b128(rs_o, ooff, 0, CPOL_SC1);
+      }
+    };
+    const uint64_t ml0 = wave < G ? load_ml(min(lane, S - 1), wave) : 0ull;
+    u4 ova[RB], ovb[RB];
+    load_batch(ova, 0);
+    if (nkmax > RB) load_batch(ovb, RB);
+    KVQ_STAMP(tid == 0, 18);
+    for (int hh = wave; hh < G; hh += NW) {
+      float M = -INFINITY;
+      for (int i = lane; i < S; i += 64) {
+        const uint64_t mv = (hh == wave && i == lane) ? ml0 : load_ml(i, hh);
+        const float mi = __uint_as_float((uint32_t)mv);
+        lds.u.fin.ml[i * MAXG + hh] = f2{mi, __uint_as_float((uint32_t)(mv >> 32))};
+        M = fmaxf(M, mi);
+      }
+      M = wave_max64(M);
+      float L = 0.0f;
+      for (int i = lane; i < S; i += 64) {
+        const f2 x = lds.u.fin.ml[i * MAXG + hh];
+        const float w = x[0] == -INFINITY ? 0.0f : ex2(x[0] - M) * x[1];
+        lds.u.fin.ml[i * MAXG + hh][0] = w;
+        L += w;
+      }
+      L = wave_sum64(L);
+      if (lane == 0) lds.u.fin.inv[hh] = L > 0.0f ? 1.0f / L : 0.0f;
     }
-    *(u2*)op = u2{bits[0] | ((uint32_t)bits[1] << 16), bits[2] | ((uint32_t)bits[3] << 16)};
+    __syncthreads();
+    KVQ_STAMP(tid == 0, 19);
+    f4 acc = {0, 0, 0, 0};
+    auto accum = [&](const u4 (&ov)[RB], int k0) {
+#pragma unroll
+      for (int k = 0; k < RB; k++)
+        if (k0 + k < nk)
+          acc += lds.u.fin.ml[(r + (k0 + k) * NR) * MAXG + h][0] * __builtin_bit_cast(f4, ov[k]);
+    };
+    accum(ova, 0);
+    if (nkmax > RB) accum(ovb, RB);
+    for (int k0 = 2 * RB; k0 < nkmax; k0 += RB) {
+      load_batch(ova, k0);
+      accum(ova, k0);
+    }
+    for (int o = 1; o < NR; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; e++) acc[e] += __shfl_xor(acc[e], o);
+    KVQ_STAMP(tid == 0, 20);
+    if (act && r == 0) {
+      const float inv = lds.u.fin.inv[h];
+      uint16_t* op = out + ((size_t)b * g.Hq + kh * G + h) * D + c4;
+      uint16_t bits[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) bits[e] = to_io_bits<BF16>(acc[e] * inv);
+      *(u2*)op = u2{bits[0] | ((uint32_t)bits[1] << 16), bits[2] | ((uint32_t)bits[3] << 16)};
+    }
   }
   KVQ_STAMP(tid == 0, 15);
 #ifdef KVQ_STAMPS
