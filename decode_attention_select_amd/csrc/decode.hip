@@ -518,41 +518,32 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
   // kept key runs (PRUNE), a wave-uniform mask: E_s sums min(floor(4096 |q|),
   // 2^20) over run s's 16 channels and the G heads (at most 2^28, exact in 32
   // bits); lane (col, kq) holds runs 2kq (qv[0..1]) and 2kq + 1 (qv[2..3]),
-  // and the 16 lanes of row kq are DPP row kq
+  // whose query slices are zeroed when the runs are pruned
   uint32_t cmap = 0;  // kept runs in ascending order, three bits each
   if constexpr (PRUNE) {
-    uint32_t e[2] = {0, 0};
-    if (hvalid) {
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int w = 0; w < 4; w++) {
-          const uint32_t x = qv[i][w];  // 4096 |q| is exact; the conversion truncates
-          e[i >> 1] += (uint32_t)fminf(4096.0f * fabsf(in_to_f32((uint16_t)(x & 0xFFFF), BF16)),
-                                       1048576.0f);
-          e[i >> 1] += (uint32_t)fminf(4096.0f * fabsf(in_to_f32((uint16_t)(x >> 16), BF16)),
-                                       1048576.0f);
-        }
+    // run energies E_r: lane l sums min(floor(4096 |q|), 2^20) over
+    // channels 2l, 2l + 1 of every head (from the query's LDS copy; 4096 |q|
+    // is exact and the conversion truncates), the 8 lanes of run l / 8 add
+    // up (quad xor 1, xor 2, half-row mirror), and lane r < 8 ranks run r
+    // against the eight sums (ties to the lower run)
+    uint32_t e = 0;
+    for (int h = 0; h < G; h++) {
+      const uint32_t x = *(const uint32_t*)&lds.qin[h][2 * lane];
+      e += (uint32_t)fminf(4096.0f * fabsf(in_to_f32((uint16_t)(x & 0xFFFF), BF16)), 1048576.0f);
+      e += (uint32_t)fminf(4096.0f * fabsf(in_to_f32((uint16_t)(x >> 16), BF16)), 1048576.0f);
     }
-    uint32_t E[8];
+    e += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0xB1, 0xF, 0xF, false);
+    e += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x4E, 0xF, 0xF, false);
+    e += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x141, 0xF, 0xF, false);
+    const int rr = lane & 7;
+    const uint32_t Er = (uint32_t)__shfl((int)e, 8 * rr);
+    int rank = 0;
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
-      uint32_t x = e[h];
-      x += (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
-      x += (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x124, 0xF, 0xF, false);  // row_ror:4
-      x += (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x122, 0xF, 0xF, false);  // row_ror:2
-      x += (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x121, 0xF, 0xF, false);  // row_ror:1
-#pragma unroll
-      for (int m = 0; m < 4; m++) E[2 * m + h] = (uint32_t)__builtin_amdgcn_readlane((int)x, 16 * m);
+    for (int i = 0; i < 8; i++) {
+      const uint32_t Ei = (uint32_t)__builtin_amdgcn_readlane((int)e, 8 * i);
+      rank += (Ei > Er) || (Ei == Er && i < rr);
     }
-    kmask = 0;
-#pragma unroll
-    for (int r = 0; r < 8; r++) {
-      int rank = 0;
-#pragma unroll
-      for (int i = 0; i < 8; i++) rank += (E[i] > E[r]) || (E[i] == E[r] && i < r);
-      if (rank < nkeep) kmask |= 1u << r;
-    }
+    kmask = (uint32_t)(__ballot(rank < nkeep) & 0xFFull);
     kmask = __builtin_amdgcn_readfirstlane(kmask);
     kept0 = __builtin_ctz(kmask);
     int n = 0;
