@@ -1159,7 +1159,10 @@ __global__ __launch_bounds__(WG_THREADS) void decode_kernel(Geo g, const uint16_
       // finish its last groups alone, at a lower issue rate.  A wave that has
       // started more groups than the other wave of its SIMD yields to it
       // (advisory: a stale count only delays the balance).  Eight waves on
-      // four SIMDs only; other wave counts keep the arbiter's order.
+      // four SIMDs only; other wave counts keep the arbiter's order.  The
+      // counts are plain LDS words, read and written without ordering: an
+      // atomic access would make the compiler wait for every copy in flight
+      // (the group copies also write LDS) at each group.
       if constexpr (NW == 8) {
         const int other = __builtin_amdgcn_readfirstlane(lds.prog[wave ^ 4]);
         lds.prog[wave] = i;
