@@ -42,7 +42,7 @@ DECODE_KERNEL = "_ZN3kvq13decode_kernelILb1ELi4ELb1ELi0ELb0ELb0ELb1ELb0ELb0EEEv"
 
 def kernel_code_hash(symbol_prefix: str = DECODE_KERNEL, lib_path: str = None):
     """sha256 (16 hex digits) of a kernel's machine code in the gfx950 code
-    objects embedded in libkvq.so (this build's own library), or None."""
+    objects embedded in libkvq.so (the library compiled from these sources), or None."""
     import hashlib
     import struct
     if lib_path is None:
