@@ -306,6 +306,35 @@ def test_pruned_decode_matches_oracle(w, n_keep):
         print("%s keep=%d S=%d max|err| %.3g" % (w.name, n_keep, S, err))
 
 
+@pytest.mark.parametrize("w", [SMALL[1], SMALL[4], SMALL[6]], ids=_ids)
+def test_pruned_choice_ties_to_the_lower_run(w):
+    # runs 2 and 5 carry the same magnitudes (run 5 a permutation of run 2,
+    # both x8 above the other runs), so their energies tie exactly and a
+    # keep-1 decode must keep run 2, the lower one
+    case = Case(w)
+    if case.pruned_unsupported(3, 1):
+        return
+    qz = case.oracle_quant()
+    qf = kvq_synth.bits_to_f64(case.d["q_dec"][:, :, 0], w.io_dtype)
+    perm = np.random.default_rng(7).permutation(16)
+    qp = qf.copy()
+    qp[:, :, 32:48] *= 8
+    qp[:, :, 80:96] = qp[:, :, 32:48][:, :, perm]
+    q = kvq_synth.to_bits(qp, w.io_dtype)
+    keep = oracle.prune_chunks(q, w.n_kv_heads, w.io_dtype, 1)
+    assert keep[..., 2].all() and not keep[..., 5].any()
+    ref = oracle.attention_pruned(qz, q, SM_SCALE, 1)
+    # the output a choice of run 5 would give (the same query values, run 2
+    # not kept): far from ref, so a wrong tie order fails the check below
+    q5 = qp.copy()
+    q5[:, :, 32:48] = 0
+    wrong = oracle.attention_pruned(qz, kvq_synth.to_bits(q5, w.io_dtype), SM_SCALE, 1)
+    assert np.abs(wrong - ref).max() > 10 * ATOL
+    for S in (1, 3):
+        err = check_output(case.decode_pruned(q, S, 1), ref, w.io_dtype, ATOL)
+        print("%s tied runs S=%d max|err| %.3g" % (w.name, S, err))
+
+
 def test_pruned_keep_all_equals_unpruned():
     w = SMALL[1]
     case = Case(w)
